@@ -1,0 +1,223 @@
+"""Oracle: the prompt-prefill forward pass in fp64 (test infrastructure).
+
+What is computed is the plain definition: every prompt row through every
+layer, then the logits of the last row.  The pruned schedule is also here so
+that it can be checked against that definition; the llama.cpp Gemma 4 prefill
+page (section 1) states that KV-shared layers write no cache, so in those
+layers a row's output depends only on itself and on caches that are already
+final, and only the output row has to be kept (section 3: outputs identical).
+
+Model reading (the pages name a "Gemma-style" decoder without its layer
+math; the plainest pre-norm decoder is used):
+  x_t      = embd_scale * deq(tok_embd[id_t])
+  per layer il (own = il < n_layer_kv_from_start, src = kv source layer):
+    a      = rms(x, g_attn);  q = rope(Wq a)
+    own:     K[il][pos] = fp16(rope(Wk a)),  V[il][pos] = fp16(Wv a)
+    o      = causal attention of q over K[src], V[src] (fp16 cache values)
+    x     += Wo o
+    b      = rms(x, g_ffn);   x += Wd act(Wg b, Wu b)
+    ple_dim > 0:  c = rms(x, g_ple);  P = s_il * deq(ple_table[id_t])[il*E:(il+1)*E]
+                  x += Wple_up (gelu(Wple_gate c) * P)
+  logits   = W_out rms(x_last, g_out)   (W_out = tok_embd when tied), fp32
+All arithmetic is fp64; the only roundings are the fp16 cache store
+(round to nearest even) and the fp32 logits.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .model import OracleModel
+
+
+# ---------------------------------------------------------------- components
+
+def rms_norm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * g, over the last axis."""
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * g
+
+
+def rope(v: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
+    """Rotary embedding, half-split pairs (i, i + hd/2).
+
+    v: [rows, heads, hd]; pos: [rows] absolute positions.  The angle of pair i
+    at position p is p * base^(-2i/hd), in fp64.
+    """
+    hd = v.shape[-1]
+    half = hd // 2
+    i = np.arange(half, dtype=np.float64)
+    theta = base ** (-2.0 * i / hd)
+    ang = pos.astype(np.float64)[:, None] * theta[None, :]  # [rows, half]
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    a, b = v[..., :half], v[..., half:]
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
+
+
+def gelu_tanh(z: np.ndarray) -> np.ndarray:
+    return 0.5 * z * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (z + 0.044715 * z ** 3)))
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    return z / (1.0 + np.exp(-z))
+
+
+def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, pos: np.ndarray) -> np.ndarray:
+    """Causal softmax attention.
+
+    q: [rows, H, hd] fp64; K, V: [P, KVH, hd] (cache, any float dtype);
+    pos: [rows].  Row t attends to cache positions 0..pos[t].  Query head h
+    uses KV head h // (H / KVH).  Returns [rows, H*hd].
+    """
+    rows, H, hd = q.shape
+    KVH = K.shape[1]
+    grp = H // KVH
+    P = int(pos.max()) + 1
+    Kf = K[:P].astype(np.float64)
+    Vf = V[:P].astype(np.float64)
+    out = np.empty((rows, H, hd), dtype=np.float64)
+    scale = 1.0 / math.sqrt(hd)
+    j = np.arange(P)
+    chunk = max(1, (1 << 24) // max(P, 1))
+    for h in range(H):
+        g = h // grp
+        for s in range(0, rows, chunk):
+            e = min(rows, s + chunk)
+            sc = (q[s:e, h, :] @ Kf[:, g, :].T) * scale          # [r, P]
+            sc = np.where(j[None, :] <= pos[s:e, None], sc, -np.inf)
+            sc = sc - sc.max(axis=1, keepdims=True)
+            w = np.exp(sc)
+            w = w / w.sum(axis=1, keepdims=True)
+            out[s:e, h, :] = w @ Vf[:, g, :]
+    return out.reshape(rows, H * hd)
+
+
+# ---------------------------------------------------------------- KV state
+
+class KVState:
+    """fp16 K and V for the owning layers: [Ls][n_ctx][kv_dim] each."""
+
+    def __init__(self, m: OracleModel, n_ctx: int):
+        ls = m.n_layer_kv_from_start
+        self.n_ctx = n_ctx
+        self.K = np.zeros((ls, n_ctx, m.kv_dim), dtype=np.float16)
+        self.V = np.zeros((ls, n_ctx, m.kv_dim), dtype=np.float16)
+        self.n_pos = 0
+
+    def copy(self) -> "KVState":
+        c = KVState.__new__(KVState)
+        c.n_ctx, c.K, c.V, c.n_pos = self.n_ctx, self.K.copy(), self.V.copy(), self.n_pos
+        return c
+
+
+# ---------------------------------------------------------------- forward
+
+def embed_rows(m: OracleModel, tokens: np.ndarray) -> np.ndarray:
+    return m.embd_scale * m.q4("tok_embd", rows=tokens)
+
+
+def _layer(m: OracleModel, kv: KVState, il: int, x: np.ndarray, pos: np.ndarray,
+           toks: np.ndarray, W: dict) -> np.ndarray:
+    H, KVH, hd = m.n_head, m.n_kv_head, m.head_dim
+    own = il < m.n_layer_kv_from_start
+    src = il if own else m.kv_src[il]
+    r = x.shape[0]
+
+    a = rms_norm(x, W["attn_norm"], m.rms_eps)
+    q = rope((a @ W["wq"].T).reshape(r, H, hd), pos, m.rope_base)
+    if own:
+        k = rope((a @ W["wk"].T).reshape(r, KVH, hd), pos, m.rope_base)
+        v = a @ W["wv"].T
+        kv.K[il, pos] = k.reshape(r, KVH * hd).astype(np.float16)
+        kv.V[il, pos] = v.astype(np.float16)
+        Kc, Vc = kv.K[il], kv.V[il]
+    else:
+        # a shared layer only reads its source layer's cache
+        Kc, Vc = kv.K[src].view(), kv.V[src].view()
+        Kc.flags.writeable = False
+        Vc.flags.writeable = False
+    o = attention(q, Kc.reshape(-1, KVH, hd), Vc.reshape(-1, KVH, hd), pos)
+    x = x + o @ W["wo"].T
+
+    b = rms_norm(x, W["ffn_norm"], m.rms_eps)
+    gt = b @ W["ffn_gate"].T
+    up = b @ W["ffn_up"].T
+    hact = (gelu_tanh(gt) if m.act == 0 else silu(gt)) * up
+    x = x + hact @ W["ffn_down"].T
+
+    if m.ple_dim:
+        E = m.ple_dim
+        c = rms_norm(x, W["ple_norm"], m.rms_eps)
+        P = m.ple_scale[il] * m.q4("ple_table", rows=toks)[:, il * E:(il + 1) * E]
+        x = x + (gelu_tanh(c @ W["ple_gate"].T) * P) @ W["ple_up"].T
+    return x
+
+
+def _layer_weights(m: OracleModel, il: int) -> dict:
+    p = f"blk.{il}."
+    W = {}
+    for name, t in m.tensors.items():
+        if name.startswith(p):
+            key = name[len(p):]
+            W[key] = m.f32(name) if t.ttype == 0 else m.q4(name)
+    return W
+
+
+def head(m: OracleModel, x_last: np.ndarray, chunk: int = 16384) -> np.ndarray:
+    """fp32 logits of one row: W_out rms(x, g_out)."""
+    hn = rms_norm(x_last, m.f32("output_norm"), m.rms_eps)
+    name = "tok_embd" if m.tied else "output"
+    V = m.n_vocab
+    out = np.empty(V, dtype=np.float64)
+    for s in range(0, V, chunk):
+        e = min(V, s + chunk)
+        out[s:e] = m.q4(name, rows=np.arange(s, e)) @ hn
+    return out.astype(np.float32)
+
+
+def prefill(m: OracleModel, kv: KVState, tokens, prune: bool = False,
+            n_ubatch: int | None = None, trace: dict | None = None) -> np.ndarray:
+    """Run the prompt `tokens` from position kv.n_pos; return last-row logits.
+
+    prune=False is the plain definition: all rows through all layers.
+    prune=True keeps only the last row from the first KV-shared layer on (the
+    pages' schedule: intermediate ubatches stop before that layer, the last
+    ubatch carries one row through the remaining layers).
+
+    Layers are the outer loop.  Within a layer the rows are taken in ubatch
+    order (n_ubatch rows at a time, or all at once when None); each chunk
+    writes its K/V before it attends, so it sees exactly the cache the
+    ubatch-by-ubatch schedule would give it.  trace, if given, receives the
+    last row's hidden state after each layer.
+    """
+    tokens = np.asarray(tokens, dtype=np.int64)
+    n = int(tokens.shape[0])
+    if n < 1:
+        raise ValueError("empty prompt")
+    if tokens.min() < 0 or tokens.max() >= m.n_vocab:
+        raise ValueError("token id out of range")
+    p0 = kv.n_pos
+    if p0 + n > kv.n_ctx:
+        raise ValueError("context overflow")
+    ls, L = m.n_layer_kv_from_start, m.n_layer
+    ub = n if n_ubatch is None else int(n_ubatch)
+    pos = p0 + np.arange(n)
+    toks = tokens
+    x = embed_rows(m, toks)
+    for il in range(L):
+        if prune and il == ls and 0 < ls < L:
+            x, pos, toks = x[-1:], pos[-1:], toks[-1:]
+        W = _layer_weights(m, il)
+        parts = []
+        for s in range(0, x.shape[0], ub):
+            e = min(x.shape[0], s + ub)
+            parts.append(_layer(m, kv, il, x[s:e], pos[s:e], toks[s:e], W))
+        x = np.concatenate(parts, axis=0)
+        del W
+        if trace is not None:
+            trace[il] = x[-1].copy()
+    logits = head(m, x[-1])
+    kv.n_pos = p0 + n
+    return logits

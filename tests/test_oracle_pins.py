@@ -1,0 +1,309 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Closed forms, library special cases, hand-built fixtures under
+tests/golden/ (each with its citation), a scalar brute-force implementation
+(tests/brute.py) on micro shapes, and the invariants the pages fix:
+pruned == unpruned (llama.cpp Gemma 4 prefill page, section 3: identical
+outputs), KV-shared layers leave the cache untouched (section 1), and
+resuming after N cached positions equals a full prefill (PicoLM page,
+resume section).
+"""
+import json
+import math
+import os
+import struct
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle import forward as F
+from tests import brute
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+MICRO = synth.Config("micro", 90, n_layer=4, n_layer_kv_from_start=2, d_model=32, n_head=2,
+                     n_kv_head=1, head_dim=16, n_ff=64, n_vocab=40, ple_dim=32, act="geglu",
+                     tied=True, n_ubatch=2, seed=9090)
+MICRO_SW = synth.Config("micro_sw", 91, n_layer=3, n_layer_kv_from_start=3, d_model=32, n_head=4,
+                        n_kv_head=2, head_dim=8, n_ff=64, n_vocab=48, ple_dim=0, act="swiglu",
+                        tied=False, n_ubatch=3, seed=9191)
+
+
+# ------------------------------------------------------------------ Q4_0
+
+def test_deq_hand_built_blocks():
+    g = _gold("q4_0_blocks.json")
+    for blk in g["blocks"]:
+        raw = np.array(blk["bytes"], dtype=np.uint8).reshape(1, 18)
+        got = oracle.deq_q4_0(raw)[0]
+        assert got.tolist() == blk["values"], blk["what"]
+
+
+def test_deq_exhaustive_codes_and_scale_sweep():
+    # every code in both nibble positions, against scales decoded by struct
+    rng = np.random.default_rng(5)
+    bits = np.concatenate([np.arange(0, 0x7C00, 97), rng.integers(0x8000, 0xFC00, 200)]).astype(np.uint16)
+    for b in bits:
+        for c in range(16):
+            raw = np.zeros((1, 18), np.uint8)
+            raw[0, 0:2] = np.frombuffer(struct.pack("<H", int(b)), np.uint8)
+            raw[0, 2:] = c | ((15 - c) << 4)
+            (d,) = struct.unpack("<e", struct.pack("<H", int(b)))
+            got = oracle.deq_q4_0(raw)[0]
+            assert got[0] == d * (c - 8) and got[16] == d * (7 - c)
+
+
+def test_fp16_store_is_round_to_nearest_even():
+    # ties between fp16 neighbours of 1.0 (spacing 2^-10) round to the even one
+    one = 1.0
+    cases = {one + 2 ** -11: 1.0, one + 3 * 2 ** -11: 1.0 + 2 ** -9,
+             one + 2 ** -11 + 2 ** -30: 1.0 + 2 ** -10, -(one + 2 ** -11): -1.0,
+             65519.0: 65504.0, 2 ** -25: 0.0, 3 * 2 ** -26: 2 ** -24}
+    for v, want in cases.items():
+        assert float(np.float64(v).astype(np.float16)) == want, v
+
+
+# ------------------------------------------------------------------ elementwise
+
+def test_rms_norm_closed_form():
+    x = np.array([[3.0, 4.0]])
+    g = np.array([1.0, 2.0])
+    got = F.rms_norm(x, g, 0.0)
+    np.testing.assert_allclose(got, [[3 / math.sqrt(12.5), 8 / math.sqrt(12.5)]], rtol=1e-15)
+    # scale invariance and unit mean square when eps = 0 and g = 1
+    z = np.random.default_rng(1).standard_normal((5, 64))
+    np.testing.assert_allclose(F.rms_norm(7.5 * z, np.ones(64), 0.0), F.rms_norm(z, np.ones(64), 0.0),
+                               rtol=1e-13)
+    np.testing.assert_allclose((F.rms_norm(z, np.ones(64), 0.0) ** 2).mean(axis=1), 1.0, rtol=1e-13)
+    # eps enters under the root: a zero row stays zero, a constant row c gives c/sqrt(c^2+eps)
+    np.testing.assert_allclose(F.rms_norm(np.full((1, 4), 1e-3), np.ones(4), 1e-6),
+                               1e-3 / math.sqrt(1e-6 + 1e-6), rtol=1e-13)
+
+
+def test_gelu_tanh_against_library_and_identities():
+    z = np.linspace(-8, 8, 4001)
+    ref = torch.nn.functional.gelu(torch.from_numpy(z), approximate="tanh").numpy()
+    np.testing.assert_allclose(F.gelu_tanh(z), ref, rtol=1e-13, atol=1e-15)
+    # odd-part identity of x*Phi-like gates: g(z) - g(-z) = z
+    np.testing.assert_allclose(F.gelu_tanh(z) - F.gelu_tanh(-z), z, atol=1e-12)
+    # close to the erf form (within the approximation's known few-1e-4 error)
+    erf = torch.nn.functional.gelu(torch.from_numpy(z)).numpy()
+    assert np.abs(F.gelu_tanh(z) - erf).max() < 5e-4
+
+
+def test_silu_against_library_and_identity():
+    z = np.linspace(-30, 30, 3001)
+    np.testing.assert_allclose(F.silu(z), torch.nn.functional.silu(torch.from_numpy(z)).numpy(),
+                               rtol=1e-13, atol=1e-300)
+    np.testing.assert_allclose(F.silu(z) - F.silu(-z), z, atol=1e-12)
+
+
+def test_rope_special_cases():
+    rng = np.random.default_rng(2)
+    v = rng.standard_normal((3, 2, 16))
+    # position 0 is the identity
+    np.testing.assert_array_equal(F.rope(v, np.zeros(3, int), 10000.0), v)
+    # each (i, i + hd/2) pair keeps its norm
+    r = F.rope(v, np.array([5, 77, 32767]), 10000.0)
+    n0 = v[..., :8] ** 2 + v[..., 8:] ** 2
+    n1 = r[..., :8] ** 2 + r[..., 8:] ** 2
+    np.testing.assert_allclose(n1, n0, rtol=1e-12)
+    # explicit rotation: hd = 4, base 10000: pair (0,2) turns by p rad, pair (1,3) by p/100 rad
+    e = np.array([[[1.0, 1.0, 0.0, 0.0]]])
+    got = F.rope(e, np.array([1]), 10000.0)[0, 0]
+    np.testing.assert_allclose(got, [math.cos(1), math.cos(0.01), math.sin(1), math.sin(0.01)], rtol=1e-15)
+    # relative-position property: <rope(q,m), rope(k,n)> depends only on m - n
+    q = rng.standard_normal((1, 1, 64))
+    k = rng.standard_normal((1, 1, 64))
+    dots = [float((F.rope(q, np.array([m]), 1e4) * F.rope(k, np.array([m - 9]), 1e4)).sum())
+            for m in (9, 100, 4000)]
+    np.testing.assert_allclose(dots, dots[0], rtol=1e-10)
+
+
+# ------------------------------------------------------------------ attention
+
+def _attn_loops(q, K, V, pos):
+    rows, H, hd = q.shape
+    KVH = K.shape[1]
+    out = np.zeros((rows, H, hd))
+    for t in range(rows):
+        for h in range(H):
+            g = h * KVH // H
+            s = [sum(q[t, h, i] * float(K[j, g, i]) for i in range(hd)) / math.sqrt(hd)
+                 for j in range(pos[t] + 1)]
+            m = max(s)
+            w = [math.exp(x - m) for x in s]
+            tot = sum(w)
+            for i in range(hd):
+                out[t, h, i] = sum(w[j] / tot * float(V[j, g, i]) for j in range(pos[t] + 1))
+    return out.reshape(rows, H * hd)
+
+
+def test_attention_brute_force_gqa_causal_prefix():
+    rng = np.random.default_rng(3)
+    H, KVH, hd, P = 4, 2, 8, 9
+    K = rng.standard_normal((P, KVH, hd)).astype(np.float16)
+    V = rng.standard_normal((P, KVH, hd)).astype(np.float16)
+    pos = np.array([3, 4, 5, 8])  # queries after a 3-position prefix
+    q = rng.standard_normal((4, H, hd)) * 2
+    np.testing.assert_allclose(F.attention(q, K, V, pos), _attn_loops(q, K, V, pos), rtol=1e-12, atol=1e-13)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(4)
+    K = rng.standard_normal((6, 1, 8))
+    V = rng.standard_normal((6, 1, 8))
+    q = rng.standard_normal((1, 2, 8))
+    # one visible key -> its value
+    np.testing.assert_allclose(F.attention(q, K, V, np.array([0])).reshape(2, 8), np.repeat(V[0], 2, 0),
+                               rtol=1e-14)
+    # identical keys -> the mean of the visible values
+    Kc = np.repeat(K[:1], 6, 0)
+    np.testing.assert_allclose(F.attention(q, Kc, V, np.array([5])).reshape(2, 8),
+                               np.repeat(V.mean(0), 2, 0), rtol=1e-12)
+    # a far future key is masked out
+    K2 = K.copy(); V2 = V.copy()
+    K2[5] = 100 * q[0, 0]; V2[5] = 1e6
+    np.testing.assert_allclose(F.attention(q, K2, V2, np.array([4])), F.attention(q, K, V, np.array([4])),
+                               rtol=1e-14)
+
+
+# ------------------------------------------------------------------ whole model
+
+@pytest.mark.parametrize("cfg", [MICRO, MICRO_SW], ids=lambda c: c.name)
+def test_oracle_matches_scalar_brute_force(cfg):
+    buf = synth.build_model(cfg)
+    n = 5
+    toks = synth.prompt(cfg, n)
+    m = oracle.parse_model(buf)
+    kv = oracle.KVState(m, n)
+    lg = oracle.prefill(m, kv, toks)
+    bm = brute.BruteModel(buf.tobytes())
+    blg, bK, bV = brute.brute_prefill(bm, [int(t) for t in toks], n)
+    np.testing.assert_allclose(lg, np.array(blg, dtype=np.float32), rtol=2e-6, atol=1e-5)
+    np.testing.assert_array_equal(kv.K.astype(np.float64), brute.as_arrays(bK, n))
+    np.testing.assert_array_equal(kv.V.astype(np.float64), brute.as_arrays(bV, n))
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    buf = synth.build_model("tiny")
+    return oracle.parse_model(buf), synth.prompt("tiny", 64)
+
+
+@pytest.mark.parametrize("cfg", ["tiny", MICRO], ids=["tiny", "micro"])
+def test_pruned_equals_unpruned(cfg):
+    buf = synth.build_model(cfg)
+    m = oracle.parse_model(buf)
+    c = synth.CONFIGS[cfg] if isinstance(cfg, str) else cfg
+    toks = synth.prompt(c, 48)
+    a, b = oracle.KVState(m, 64), oracle.KVState(m, 64)
+    la = oracle.prefill(m, a, toks, prune=False)
+    lb = oracle.prefill(m, b, toks, prune=True, n_ubatch=16)
+    np.testing.assert_allclose(la, lb, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(a.K, b.K) and np.array_equal(a.V, b.V)
+
+
+def test_shared_layers_leave_cache_unchanged(tiny):
+    m, toks = tiny
+    full = oracle.KVState(m, 64)
+    oracle.prefill(m, full, toks)
+    # the same model cut after the owning layers writes the same cache
+    import copy
+    cut = copy.copy(m)
+    cut.n_layer = m.n_layer_kv_from_start
+    k2 = oracle.KVState(cut, 64)
+    oracle.prefill(cut, k2, toks)
+    assert np.array_equal(full.K, k2.K) and np.array_equal(full.V, k2.V)
+
+
+def test_resume_equals_full_prefill(tiny):
+    m, toks = tiny
+    full = oracle.KVState(m, 64)
+    lf = oracle.prefill(m, full, toks)
+    for N in (1, 25, 63):
+        kv = oracle.KVState(m, 64)
+        oracle.prefill(m, kv, toks[:N])
+        lr = oracle.prefill(m, kv, toks[N:], prune=True)
+        np.testing.assert_allclose(lr, lf, rtol=1e-12, atol=1e-12)
+        np.testing.assert_array_equal(kv.K, full.K)
+        np.testing.assert_array_equal(kv.V, full.V)
+
+
+def test_token_by_token_equals_prefill(tiny):
+    m, toks = tiny
+    full = oracle.KVState(m, 64)
+    lf = oracle.prefill(m, full, toks[:20])
+    kv = oracle.KVState(m, 64)
+    for t in toks[:20]:
+        lt = oracle.prefill(m, kv, [t])
+    np.testing.assert_allclose(lt, lf, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(kv.K[:, :20], full.K[:, :20])
+
+
+def test_ubatch_independence(tiny):
+    m, toks = tiny
+    outs = []
+    for ub in (None, 7, 16, 64):
+        kv = oracle.KVState(m, 64)
+        outs.append((oracle.prefill(m, kv, toks, n_ubatch=ub), kv.K.copy()))
+    for lg, K in outs[1:]:
+        np.testing.assert_allclose(lg, outs[0][0], rtol=1e-12, atol=1e-12)
+        assert np.array_equal(K, outs[0][1])
+
+
+def test_prefill_rejects_bad_input(tiny):
+    m, toks = tiny
+    kv = oracle.KVState(m, 16)
+    with pytest.raises(ValueError):
+        oracle.prefill(m, kv, [])
+    with pytest.raises(ValueError):
+        oracle.prefill(m, kv, [m.n_vocab])
+    with pytest.raises(ValueError):
+        oracle.prefill(m, kv, toks[:17])
+    assert kv.n_pos == 0
+
+
+# ------------------------------------------------------------------ predicate and snapshot
+
+def test_prune_predicate_truth_table():
+    g = _gold("prune_predicate.json")
+    for c in g["cases"]:
+        L = c["n_layer"]
+        inp = [False] * (L + 1)
+        for i in c["layer_inp_true"]:
+            inp[i] = True
+        got = oracle.prune_shared(L, c["n_layer_kv_from_start"], c["embeddings"], c["n_seq_max"], inp,
+                                  c["crop_before_nextn"])
+        assert got == c["expected"], c["note"]
+
+
+def test_kvcp_size_pin():
+    g = _gold("kvcp_tinyllama_25.json")
+    K = np.zeros((g["n_layers"], g["n_pos"], g["kv_dim"]), np.float16)
+    data = oracle.kvcp.dump(K, K, g["n_pos"])
+    assert len(data) - oracle.kvcp.HEADER == g["payload_bytes"] == 563200
+    assert round((len(data) - oracle.kvcp.HEADER) / 1024) == g["approx_kib"]
+
+
+def test_kvcp_round_trip_and_rejections():
+    rng = np.random.default_rng(6)
+    K = rng.standard_normal((3, 10, 16)).astype(np.float16)
+    V = rng.standard_normal((3, 10, 16)).astype(np.float16)
+    data = oracle.kvcp.dump(K, V, 10)
+    k2, v2 = oracle.kvcp.load(data, 3, 16, 4, 100)
+    assert np.array_equal(k2, K[:, :4]) and np.array_equal(v2, V[:, :4])
+    bad = [(b"XXXX" + data[4:], 3, 16, 4, 100), (data, 2, 16, 4, 100), (data, 3, 8, 4, 100),
+           (data[:-2], 3, 16, 4, 100), (data, 3, 16, 11, 100), (data, 3, 16, 4, 3), (data[:10], 3, 16, 1, 10)]
+    for args in bad:
+        with pytest.raises(oracle.kvcp.SnapshotError):
+            oracle.kvcp.load(*args)
