@@ -1,0 +1,170 @@
+"""Benchmark: E2B-like Q4_0 prompt prefill on one MI355X.
+
+One step = one ppx_prefill call from an empty cache (all ubatches, the
+pruned single-row phase and the head), inputs resident in HBM.  Prints one
+JSON line.  The metric is prefill tokens/s; `roofline` reports the MFMA GEMM
+phase (the dominant kernel) against the dense fp16 peak, from HIP events
+recorded around every GEMM launch in a separate, identical pass; the
+single-row phase's HBM rate and the attention phase's MFMA rate are given in
+`phases`.  `cpu_baseline` times the fp64 oracle on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP16_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="e2b")
+    ap.add_argument("--n", type=int, default=2048, help="prompt tokens")
+    ap.add_argument("--ubatch", type=int, default=0, help="0 = the config's ubatch")
+    ap.add_argument("--prune", default="auto", choices=["auto", "on", "off"])
+    ap.add_argument("--extra-n", default="512,8192", help="other prompt lengths to report (comma list, '' = none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=64, help="prompt tokens of the oracle sample")
+    return ap.parse_args()
+
+
+def timed_steps(mm, kv, toks, ub, prune, steps, warmup):
+    import torch
+    logits = torch.empty(mm.info["n_vocab"], dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        kv.clear()
+        mm.prefill(toks, kv, n_ubatch=ub, prune=prune, logits=logits)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(steps):
+        kv.clear()
+        t0.record()
+        mm.prefill(toks, kv, n_ubatch=ub, prune=prune, logits=logits)
+        t1.record()
+        t1.synchronize()
+        times.append(t0.elapsed_time(t1))
+    torch.cuda.synchronize()
+    return np.array(times), logits
+
+
+def phase_pass(ppx, mm, kv, toks, ub, prune, reps=3):
+    tm_sum = None
+    for _ in range(reps):
+        t = ppx.Timing()
+        kv.clear()
+        mm.prefill(toks, kv, n_ubatch=ub, prune=prune, timing=t)
+        d = t.as_dict()
+        if tm_sum is None:
+            tm_sum = d
+        else:
+            for k in d["ms"]:
+                tm_sum["ms"][k] += d["ms"][k]
+    for k in tm_sum["ms"]:
+        tm_sum["ms"][k] /= reps
+    return tm_sum
+
+
+def cpu_baseline(cfg, buf, toks, sample):
+    import oracle
+    m = oracle.parse_model(buf)
+    kv = oracle.KVState(m, sample)
+    t = time.perf_counter()
+    oracle.prefill(m, kv, toks[:sample], prune=True)
+    dt = time.perf_counter() - t
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    return {"value": sample / dt, "unit": "tokens/s", "cores": min(cores, threads), "kind": "oracle",
+            "sample": f"fp64 numpy oracle, first {sample} tokens of the same {cfg} prompt, pruned, "
+                      f"empty cache; {dt:.1f} s"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py: this engine runs on one GPU; --gpus {a.gpus} is not supported "
+              "(multi-GPU sharding is design-only)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import prompt_prefill_cross_amd as ppx
+    import synth
+
+    cfg = synth.CONFIGS[a.config]
+    ub = a.ubatch or cfg.n_ubatch
+    buf = synth.build_model(cfg)
+    mm = ppx.Model(buf)
+    lens = [a.n] + [int(x) for x in a.extra_n.split(",") if x.strip() and int(x) != a.n]
+    n_ctx = max(lens)
+    kv = ppx.KVCache(mm, n_ctx)
+    mm.workspace(ub, n_ctx)
+
+    results = {}
+    for n in lens:
+        toks = synth.prompt(cfg, n)
+        steps = a.steps if n == a.n else max(3, a.steps // 2)
+        times, _ = timed_steps(mm, kv, toks, ub, a.prune, steps, a.warmup if n == a.n else 1)
+        ph = phase_pass(ppx, mm, kv, toks, ub, a.prune)
+        results[n] = (times, ph)
+        print(f"# n={n}: {np.median(times):.3f} ms median, {n / np.median(times) * 1e3:.0f} tok/s; "
+              f"phases ms {ph['ms']}", file=sys.stderr, flush=True)
+
+    times, ph = results[a.n]
+    ms = float(np.mean(times))
+    gemm_tflops = ph["gemm_flop"] / (ph["ms"]["gemm"] * 1e-3) / 1e12 if ph["ms"]["gemm"] else 0.0
+    attn_tflops = ph["attn_flop"] / (ph["ms"]["attn"] * 1e-3) / 1e12 if ph["ms"]["attn"] else 0.0
+    row_gbs = ph["row_bytes"] / (ph["ms"]["row"] * 1e-3) / 1e9 if ph["ms"]["row"] else 0.0
+    launches = ph["launches"]["gemm"]
+    out = {
+        "metric": "prefill tokens/sec at 512/2048/8192 prompt (E2B-like Q4_0), % MFMA peak",
+        "value": a.n / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 MFMA (fp32 accumulate), Q4_0 weights, fp16 KV",
+        "data": "synthetic: seeded random Q4_0 weights and uniform-random token ids",
+        "config": {"workload": f"{cfg.name} prefill, {a.n}-token prompt, empty cache",
+                   "model": f"{cfg.name}: {cfg.n_layer} layers ({cfg.n_layer_kv_from_start} own KV), d {cfg.d_model}, "
+                            f"{cfg.n_head}x{cfg.head_dim} heads, {cfg.n_kv_head} KV head(s), FFN {cfg.n_ff}, "
+                            f"vocab {cfg.n_vocab}, PLE {cfg.ple_dim}",
+                   "global_batch": 1, "seq_len": a.n, "ubatch": ub, "prune": a.prune, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": "k_q4gemm (all GEMM launches of one prefill)",
+                     "achieved": gemm_tflops, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": gemm_tflops / PEAK_FP16_TFLOPS, "traffic": None,
+                     "launches": launches,
+                     "flop_per_launch": ph["gemm_flop"] / max(launches, 1),
+                     "avg_launch_us": ph["ms"]["gemm"] * 1e3 / max(launches, 1)},
+        "phases": {"ms": ph["ms"], "launches": ph["launches"],
+                   "attn_tflops": attn_tflops, "attn_frac_mfma": attn_tflops / PEAK_FP16_TFLOPS,
+                   "row_gbs": row_gbs, "row_frac_hbm": row_gbs / PEAK_HBM_GBS,
+                   "gemm_flop": ph["gemm_flop"], "attn_flop": ph["attn_flop"], "row_bytes": ph["row_bytes"]},
+        "other_lengths": {str(n): {"ms_median": float(np.median(t)), "tokens_per_s": n / float(np.median(t)) * 1e3}
+                          for n, (t, _) in results.items()},
+        "ms_median": float(np.median(times)),
+        "ms_std": float(np.std(times)),
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg.name, buf, synth.prompt(cfg, a.n), a.cpu_sample)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,218 @@
+/*
+ * ppx.h -- C ABI of the MI355X (gfx950) pruned prompt-prefill engine.
+ *
+ * The engine runs the prompt-prefill forward pass of a Gemma-style decoder
+ * whose layers from n_layer_kv_from_start on reuse, read-only, the KV cache
+ * of an earlier layer.  Before the first such layer every token row except
+ * the output row is pruned: an intermediate ubatch skips those layers and the
+ * last ubatch carries one row through them ("llama.cpp Gemma 4 prefill KV
+ * graph optimization", section 1).  A KV snapshot of the first N positions
+ * can be saved and loaded so that a repeated prompt prefix resumes at N
+ * ("PicoLM KV Cache persistence", sections on the cache flag, the file
+ * contents and the load check).
+ *
+ * Conventions for every call:
+ *  - Return value: PPX_OK (0) or a negative PPX_E_* status.  Nothing aborts
+ *    and nothing prints unless the environment variable PPX_LOG is set.
+ *  - Device pointers are HIP device memory of the current device; the caller
+ *    owns them (KV buffer, workspace, logits) unless a call says otherwise.
+ *  - hip_stream is a hipStream_t passed as void* (NULL = the null stream).
+ *    Calls are stream-ordered and asynchronous unless stated; argument
+ *    checks happen synchronously, before any work is queued.
+ *  - One sequence only (n_seq_max == 1), as the pages require for pruning.
+ */
+#ifndef PPX_H
+#define PPX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    PPX_OK = 0,
+    PPX_E_INVAL = -1,       /* bad argument (NULL, size, alignment, params) */
+    PPX_E_TOKEN = -2,       /* a token id outside [0, n_vocab)              */
+    PPX_E_CTX = -3,         /* positions would exceed n_ctx                 */
+    PPX_E_IO = -4,          /* file open/read/write failure                 */
+    PPX_E_FORMAT = -5,      /* bad magic, version, truncated or bad sizes   */
+    PPX_E_MISMATCH = -6,    /* snapshot layer count / kv dim != model       */
+    PPX_E_UNSUPPORTED = -7, /* shape or option the engine does not support  */
+    PPX_E_HIP = -8,         /* a HIP runtime call failed                    */
+    PPX_E_NOMEM = -9,       /* buffer too small or device allocation failed */
+    PPX_E_EMPTY = -10       /* n_tokens == 0: the last row must exist       */
+};
+
+typedef struct ppx_model ppx_model; /* library-owned: host state + device weights */
+typedef struct ppx_kv ppx_kv;       /* handle over a caller-owned device KV buffer */
+
+typedef struct {
+    int n_layer;               /* L                                           */
+    int n_layer_kv_from_start; /* Ls: layers [0, Ls) own KV, [Ls, L) share    */
+    int d_model, n_head, n_kv_head, head_dim, n_ff, n_vocab;
+    int ple_dim;               /* per-layer embedding width E (0 = none)      */
+    int kv_dim;                /* n_kv_head * head_dim                        */
+    int act;                   /* 0 GeGLU, 1 SwiGLU                           */
+} ppx_model_info;
+
+enum { PPX_PRUNE_AUTO = -1, PPX_PRUNE_OFF = 0, PPX_PRUNE_ON = 1 };
+
+/* Per-phase kernel timing of one prefill call (see ppx_prefill_params). */
+enum { PPX_PHASE_GEMM = 0,    /* Q4_0 MFMA GEMMs of the row-batched layers      */
+       PPX_PHASE_ATTN = 1,    /* causal prefill attention                        */
+       PPX_PHASE_ROW = 2,     /* single-row path: GEMVs, 1-row attention, norms  */
+       PPX_PHASE_OTHER = 3,   /* embedding gather, row norms, copies             */
+       PPX_N_PHASES = 4 };
+typedef struct {
+    double ms[PPX_N_PHASES];   /* summed event time around each phase's launches */
+    int launches[PPX_N_PHASES];
+    double gemm_flop;          /* algorithmic 2*M*N*K over the GEMM launches      */
+    double attn_flop;          /* 4*n_head*head_dim*(visible keys) over queries   */
+    double row_bytes;          /* Q4_0 weight bytes + KV bytes the row path reads */
+} ppx_timing;
+
+typedef struct {
+    int n_ubatch;   /* rows per ubatch, 1..PPX_MAX_UBATCH; must not exceed the
+                       n_ubatch given to ppx_workspace_bytes                    */
+    int prune;      /* PPX_PRUNE_AUTO: the predicate decides; OFF: every row
+                       through every layer; ON: PPX_E_UNSUPPORTED if the
+                       predicate is false                                       */
+    int embeddings; /* must be 0 (no embedding extraction in this engine)      */
+    int n_seq_max;  /* must be 1                                               */
+    float *debug_hidden; /* NULL, or device fp32 [n_layer][d_model]: receives
+                            the last row's hidden state after each layer       */
+    ppx_timing *timing;  /* NULL, or host struct filled with per-phase kernel
+                            times; HIP events are then recorded around every
+                            launch and the call synchronises the stream        */
+    float *debug_rows;   /* NULL, or device fp32 [n_layer][n_tokens][d_model]:
+                            receives the hidden state entering each layer for
+                            every row that layer processes (pruned layers: the
+                            last row only; other entries are left untouched)    */
+} ppx_prefill_params;
+
+#define PPX_MAX_UBATCH 4096
+
+/* ---------------------------------------------------------------- model */
+
+/* Load a "PPXM" v1 container (Q4_0 weights, fp32 norm gains; layout in the
+ * synthetic-input module's docstring) from host memory.  The bytes are read
+ * during the call only.  Weights are repacked for the kernels and uploaded
+ * into device memory the library allocates (freed by ppx_model_free).
+ * Errors: PPX_E_FORMAT (bad container), PPX_E_UNSUPPORTED (a dimension the
+ * kernels cannot tile: d_model, q_dim, n_ff, ple_dim not multiples of 64,
+ * head_dim not 64/128/256, n_head not a multiple of n_kv_head), PPX_E_HIP. */
+int ppx_model_load(const void *container, size_t bytes, void *hip_stream, ppx_model **out);
+/* Same, reading the container from a file (PPX_E_IO if it cannot be read). */
+int ppx_model_load_file(const char *path, void *hip_stream, ppx_model **out);
+void ppx_model_free(ppx_model *m);
+int ppx_model_get_info(const ppx_model *m, ppx_model_info *out);
+/* Device bytes the library holds for the model's weights and tables. */
+size_t ppx_model_device_bytes(const ppx_model *m);
+
+/* ---------------------------------------------------------------- KV cache */
+
+/* fp16 K and V of the Ls owning layers, [Ls][n_ctx][kv_dim] each, K first. */
+size_t ppx_kv_bytes(const ppx_model *m, int n_ctx);
+/* Wrap a caller-owned device buffer of >= ppx_kv_bytes bytes (256-byte
+ * aligned) as an empty cache (n_pos = 0).  The buffer must outlive the
+ * handle; ppx_kv_free releases the handle only.  Also builds the model's
+ * RoPE tables up to n_ctx if they are shorter (blocking). */
+int ppx_kv_init(ppx_model *m, void *kv_dev, size_t bytes, int n_ctx, ppx_kv **out);
+void ppx_kv_free(ppx_kv *kv);
+int ppx_kv_n_pos(const ppx_kv *kv);
+int ppx_kv_n_ctx(const ppx_kv *kv);
+/* Forget all positions (n_pos = 0); the buffer contents are left as is. */
+int ppx_kv_clear(ppx_kv *kv);
+
+/* KVCP snapshot ("PicoLM KV Cache persistence", file-content section):
+ * "KVCP", int32 n_pos, int32 n_layers (= Ls), int32 kv_dim, then K as
+ * [n_layers][n_pos][kv_dim] fp16, then V likewise; little-endian.
+ * kv_save writes the first n_pos (<= ppx_kv_n_pos) positions and
+ * synchronises hip_stream.  kv_load checks the file before touching the
+ * cache (magic, layer count, kv dim, exact size, n_pos <= file positions,
+ * n_pos <= n_ctx); on any failure it returns PPX_E_FORMAT / PPX_E_MISMATCH /
+ * PPX_E_CTX / PPX_E_IO and leaves the cache empty (n_pos = 0), so the caller
+ * falls back to a full prefill.  On success n_pos = the loaded count; it
+ * synchronises hip_stream.  The file stores no token ids: that the new
+ * prompt starts with the cached prefix is the caller's duty. */
+int ppx_kv_save(const ppx_kv *kv, const char *path, int n_pos, void *hip_stream);
+int ppx_kv_load(ppx_kv *kv, const char *path, int n_pos, void *hip_stream);
+/* Host-only check of a KVCP file against a model shape, the same check
+ * ppx_kv_load makes before touching the cache: PPX_OK if the file is a
+ * whole snapshot with n_layers layers of width kv_dim holding at least n_pos
+ * positions and n_pos <= n_ctx; *file_n_pos (if not NULL) receives the
+ * file's position count whenever the header could be read. */
+int ppx_kvfile_validate(const char *path, int n_layers, int kv_dim, int n_pos, int n_ctx, int *file_n_pos);
+
+/* ---------------------------------------------------------------- prefill */
+
+/* Device workspace bytes one prefill needs for ubatches of up to n_ubatch
+ * rows and prompts of up to n_ctx tokens. */
+size_t ppx_workspace_bytes(const ppx_model *m, int n_ubatch, int n_ctx);
+
+/* Run tokens_host[0..n_tokens) at positions n_pos .. n_pos+n_tokens-1 of kv
+ * and write the logits of the last token, fp32 [n_vocab], to logits_dev.
+ * KV-owning layers write their fp16 K/V at those positions; KV-shared layers
+ * read their source layer's cache and write nothing.  ws_dev (>=
+ * ppx_workspace_bytes, 256-byte aligned) is scratch for the call.  On
+ * success kv's n_pos advances by n_tokens.  Errors are reported before any
+ * work is queued and leave n_pos unchanged: PPX_E_EMPTY, PPX_E_TOKEN,
+ * PPX_E_CTX, PPX_E_INVAL, PPX_E_UNSUPPORTED (prune ON while the predicate
+ * is false, embeddings != 0, n_seq_max != 1), PPX_E_NOMEM (ws too small);
+ * PPX_E_HIP if a launch fails.  The host token array is copied during the
+ * call.  One call in flight per kv. */
+int ppx_prefill(ppx_model *m, ppx_kv *kv, const int32_t *tokens_host, int n_tokens,
+                const ppx_prefill_params *p, void *ws_dev, size_t ws_bytes, float *logits_dev,
+                void *hip_stream);
+
+/* The prune predicate printed on the llama.cpp Gemma 4 prefill page
+ * (section 1): 1 iff crop_before_nextn, 0 < n_layer_kv_from_start < n_layer,
+ * !embeddings, n_seq_max == 1 and no embeddings_layer_inp[il] is set for il
+ * in [n_layer_kv_from_start, n_layer] (n_layer + 1 flags; NULL = none). */
+int ppx_prune_predicate(int n_layer, int n_layer_kv_from_start, int embeddings, int n_seq_max,
+                        const uint8_t *embeddings_layer_inp, int crop_before_nextn);
+
+/* ---------------------------------------------------------------- kernel-level entry points
+ * These expose single kernels of the prefill path so that each can be
+ * checked against the oracle at full model shapes.  Tensors are named as in
+ * the container ("blk.3.ffn_down", "tok_embd", ...); fused tensors are
+ * addressed by their first member: "blk.3.wq" = Q rows in RoPE-pair order
+ * (16-row blocks alternate the two halves of each head), "blk.3.wk" = K
+ * rows in that order followed by V rows (owning layers), "blk.3.ffn_gate" =
+ * gate|up with 16-row blocks alternating gate and up. */
+
+/* Dequantise a whole Q4_0 tensor from the engine's repacked device layout
+ * into fp32 [rows][cols] row-major (exact). */
+int ppx_op_dequant(const ppx_model *m, const char *tensor, float *out_dev, void *hip_stream);
+/* C[M][N] (fp32, ldc = N) = A[M][K] (fp16, lda = K) x W^T on the MFMA GEMM
+ * path, W = the named container tensor [N][K]. */
+int ppx_op_gemm(const ppx_model *m, const char *tensor, const void *a_dev_f16, int M, float *c_dev,
+                void *hip_stream);
+/* The same on the exact-weight path used for the fused K|V weight
+ * ("blk.i.wk", owning layers): A = a_hi + a_lo (two fp16 [M][K] arrays),
+ * weights (code - 8) exactly with the fp32 block scale applied per 32-block. */
+int ppx_op_gemm_exact(const ppx_model *m, const char *tensor, const void *a_hi, const void *a_lo, int M,
+                      float *c_dev, void *hip_stream);
+/* y[N] (fp32) = W x on the single-row (GEMV) path; x fp32 [K]. */
+int ppx_op_gemv(const ppx_model *m, const char *tensor, const float *x_dev, float *y_dev,
+                void *hip_stream);
+/* Causal prefill attention: q fp16 [M][n_head][head_dim] at positions
+ * pos0..pos0+M-1 over k/v fp16 [>= pos0+M][n_kv_head][head_dim];
+ * o fp16 [M][n_head*head_dim]. */
+int ppx_op_attention(const ppx_model *m, const void *q_dev, const void *k_dev, const void *v_dev,
+                     int M, int pos0, void *o_dev, void *hip_stream);
+/* Single-query attention: q fp32 [n_head][head_dim] at position pos over the
+ * first pos+1 cache rows of k/v fp16; o fp32 [n_head*head_dim].  ws_dev is
+ * scratch of ppx_workspace_bytes(m, 1, pos+1) bytes. */
+int ppx_op_attention_1row(const ppx_model *m, const float *q_dev, const void *k_dev,
+                          const void *v_dev, int pos, float *o_dev, void *ws_dev, size_t ws_bytes,
+                          void *hip_stream);
+
+const char *ppx_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PPX_H */

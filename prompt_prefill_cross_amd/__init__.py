@@ -1,0 +1,318 @@
+"""Python binding of libppx (the MI355X pruned prompt-prefill engine).
+
+Argument marshalling only: every step of the prefill runs in the library's
+HIP kernels.  torch provides device memory and the current stream.  The
+names follow the C ABI in include/ppx.h.  If libppx.so has not been built,
+every entry point raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_float, c_int, c_size_t, c_uint8, c_void_p
+
+import numpy as np
+
+__all__ = ["PPXError", "lib", "Model", "KVCache", "prune_predicate", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libppx.so")
+
+PPX_OK = 0
+STATUS = {0: "PPX_OK", -1: "PPX_E_INVAL", -2: "PPX_E_TOKEN", -3: "PPX_E_CTX", -4: "PPX_E_IO",
+          -5: "PPX_E_FORMAT", -6: "PPX_E_MISMATCH", -7: "PPX_E_UNSUPPORTED", -8: "PPX_E_HIP",
+          -9: "PPX_E_NOMEM", -10: "PPX_E_EMPTY"}
+PRUNE = {"auto": -1, "off": 0, "on": 1}
+PPX_MAX_UBATCH = 4096
+
+
+class PPXError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        msg = lib().ppx_status_str(status).decode() if _LIB is not None else self.name
+        super().__init__(f"{what}: {self.name} ({msg})" if what else f"{self.name} ({msg})")
+
+
+class ModelInfo(ctypes.Structure):
+    _fields_ = [(n, c_int) for n in ("n_layer", "n_layer_kv_from_start", "d_model", "n_head", "n_kv_head",
+                                     "head_dim", "n_ff", "n_vocab", "ple_dim", "kv_dim", "act")]
+
+
+class Timing(ctypes.Structure):
+    _fields_ = [("ms", ctypes.c_double * 4), ("launches", c_int * 4), ("gemm_flop", ctypes.c_double),
+                ("attn_flop", ctypes.c_double), ("row_bytes", ctypes.c_double)]
+
+    def as_dict(self):
+        names = ("gemm", "attn", "row", "other")
+        return {"ms": dict(zip(names, list(self.ms))), "launches": dict(zip(names, list(self.launches))),
+                "gemm_flop": self.gemm_flop, "attn_flop": self.attn_flop, "row_bytes": self.row_bytes}
+
+
+class PrefillParams(ctypes.Structure):
+    _fields_ = [("n_ubatch", c_int), ("prune", c_int), ("embeddings", c_int), ("n_seq_max", c_int),
+                ("debug_hidden", c_void_p), ("timing", POINTER(Timing)), ("debug_rows", c_void_p)]
+
+
+# (name, restype, argtypes) of every symbol declared in include/ppx.h
+SIGNATURES = [
+    ("ppx_model_load", c_int, [c_void_p, c_size_t, c_void_p, POINTER(c_void_p)]),
+    ("ppx_model_load_file", c_int, [c_char_p, c_void_p, POINTER(c_void_p)]),
+    ("ppx_model_free", None, [c_void_p]),
+    ("ppx_model_get_info", c_int, [c_void_p, POINTER(ModelInfo)]),
+    ("ppx_model_device_bytes", c_size_t, [c_void_p]),
+    ("ppx_kv_bytes", c_size_t, [c_void_p, c_int]),
+    ("ppx_kv_init", c_int, [c_void_p, c_void_p, c_size_t, c_int, POINTER(c_void_p)]),
+    ("ppx_kv_free", None, [c_void_p]),
+    ("ppx_kv_n_pos", c_int, [c_void_p]),
+    ("ppx_kv_n_ctx", c_int, [c_void_p]),
+    ("ppx_kv_clear", c_int, [c_void_p]),
+    ("ppx_kv_save", c_int, [c_void_p, c_char_p, c_int, c_void_p]),
+    ("ppx_kv_load", c_int, [c_void_p, c_char_p, c_int, c_void_p]),
+    ("ppx_kvfile_validate", c_int, [c_char_p, c_int, c_int, c_int, c_int, POINTER(c_int)]),
+    ("ppx_workspace_bytes", c_size_t, [c_void_p, c_int, c_int]),
+    ("ppx_prefill", c_int, [c_void_p, c_void_p, c_void_p, c_int, POINTER(PrefillParams), c_void_p, c_size_t,
+                            c_void_p, c_void_p]),
+    ("ppx_prune_predicate", c_int, [c_int, c_int, c_int, c_int, POINTER(c_uint8), c_int]),
+    ("ppx_op_dequant", c_int, [c_void_p, c_char_p, c_void_p, c_void_p]),
+    ("ppx_op_gemm", c_int, [c_void_p, c_char_p, c_void_p, c_int, c_void_p, c_void_p]),
+    ("ppx_op_gemm_exact", c_int, [c_void_p, c_char_p, c_void_p, c_void_p, c_int, c_void_p, c_void_p]),
+    ("ppx_op_gemv", c_int, [c_void_p, c_char_p, c_void_p, c_void_p, c_void_p]),
+    ("ppx_op_attention", c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p]),
+    ("ppx_op_attention_1row", c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_void_p,
+                                      c_size_t, c_void_p]),
+    ("ppx_status_str", c_char_p, [c_int]),
+]
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libppx.so; raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m prompt_prefill_cross_amd.build` (no CPU fallback exists)")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, res, args in SIGNATURES:
+            f = getattr(h, name)
+            f.restype = res
+            f.argtypes = args
+        _LIB = h
+    return _LIB
+
+
+def _check(st: int, what: str):
+    if st != PPX_OK:
+        raise PPXError(st, what)
+
+
+def _stream(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return c_void_p(s.cuda_stream)
+
+
+def _ptr(t) -> c_void_p:
+    return c_void_p(t.data_ptr())
+
+
+def prune_predicate(n_layer, n_layer_kv_from_start, embeddings, n_seq_max, embeddings_layer_inp=None,
+                    crop_before_nextn=True) -> bool:
+    arr = None
+    if embeddings_layer_inp is not None:
+        a = np.ascontiguousarray(np.asarray(embeddings_layer_inp, dtype=np.uint8))
+        if a.shape[0] < n_layer + 1:
+            raise ValueError("embeddings_layer_inp needs n_layer + 1 flags")
+        arr = a.ctypes.data_as(POINTER(c_uint8))
+    return bool(lib().ppx_prune_predicate(n_layer, n_layer_kv_from_start, int(embeddings), n_seq_max, arr,
+                                          int(crop_before_nextn)))
+
+
+def kvfile_validate(path, n_layers: int, kv_dim: int, n_pos: int, n_ctx: int):
+    """(status, file_n_pos) of the host-only KVCP check."""
+    fp = c_int(-1)
+    st = lib().ppx_kvfile_validate(os.fsencode(path), n_layers, kv_dim, n_pos, n_ctx, ctypes.byref(fp))
+    return st, fp.value
+
+
+class Model:
+    """A loaded model: `Model(container)` with a numpy uint8 array / bytes, or a path."""
+
+    def __init__(self, src, stream=None):
+        self._h = c_void_p()
+        L = lib()
+        if isinstance(src, (str, os.PathLike)):
+            st = L.ppx_model_load_file(os.fsencode(src), _stream(stream), ctypes.byref(self._h))
+        else:
+            buf = np.ascontiguousarray(np.frombuffer(src, dtype=np.uint8) if not isinstance(src, np.ndarray)
+                                       else src.view(np.uint8).reshape(-1))
+            st = L.ppx_model_load(c_void_p(buf.ctypes.data), buf.nbytes, _stream(stream), ctypes.byref(self._h))
+        _check(st, "ppx_model_load")
+        info = ModelInfo()
+        _check(L.ppx_model_get_info(self._h, ctypes.byref(info)), "ppx_model_get_info")
+        self.info = {n: getattr(info, n) for n, _ in ModelInfo._fields_}
+        self._ws = None
+        self._ws_key = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    @property
+    def device_bytes(self) -> int:
+        return lib().ppx_model_device_bytes(self._h)
+
+    def close(self):
+        if self._h:
+            lib().ppx_model_free(self._h)
+            self._h = c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace(self, n_ubatch: int, n_ctx: int):
+        import torch
+        need = lib().ppx_workspace_bytes(self._h, n_ubatch, n_ctx)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        return self._ws
+
+    def prefill(self, tokens, kv: "KVCache", n_ubatch: int = 512, prune: str = "auto", logits=None,
+                debug_hidden=None, embeddings: int = 0, n_seq_max: int = 1, stream=None, timing=None,
+                debug_rows=None):
+        """Run `tokens` (int32) from kv.n_pos; return fp32 logits [n_vocab] of the last token."""
+        import torch
+        toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
+        if logits is None:
+            logits = torch.empty(self.info["n_vocab"], dtype=torch.float32, device="cuda")
+        ws = self.workspace(n_ubatch, kv.n_ctx) if n_ubatch >= 1 else torch.empty(256, dtype=torch.uint8,
+                                                                                  device="cuda")
+        p = PrefillParams(n_ubatch, PRUNE[prune] if isinstance(prune, str) else int(prune), embeddings,
+                          n_seq_max, c_void_p(debug_hidden.data_ptr()) if debug_hidden is not None else None,
+                          ctypes.pointer(timing) if timing is not None else None,
+                          c_void_p(debug_rows.data_ptr()) if debug_rows is not None else None)
+        st = lib().ppx_prefill(self._h, kv.handle, c_void_p(toks.ctypes.data), toks.shape[0], ctypes.byref(p),
+                               _ptr(ws), ws.numel(), _ptr(logits), _stream(stream))
+        _check(st, "ppx_prefill")
+        return logits
+
+    # ---- kernel-level entry points
+    def op_dequant(self, name: str):
+        import torch
+        rows, cols = self._shape(name)
+        out = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
+        _check(lib().ppx_op_dequant(self._h, name.encode(), _ptr(out), _stream()), "ppx_op_dequant")
+        return out
+
+    def op_gemm(self, name: str, a):
+        import torch
+        rows, cols = self._shape(name)
+        assert a.dtype == torch.float16 and a.is_contiguous() and a.shape[1] == cols
+        c = torch.empty((a.shape[0], rows), dtype=torch.float32, device="cuda")
+        _check(lib().ppx_op_gemm(self._h, name.encode(), _ptr(a), a.shape[0], _ptr(c), _stream()), "ppx_op_gemm")
+        return c
+
+    def op_gemm_exact(self, name: str, a_hi, a_lo):
+        import torch
+        rows, cols = self._shape(name)
+        assert a_hi.dtype == torch.float16 and a_lo.dtype == torch.float16 and a_hi.shape == a_lo.shape
+        assert a_hi.shape[1] == cols and a_hi.is_contiguous() and a_lo.is_contiguous()
+        c = torch.empty((a_hi.shape[0], rows), dtype=torch.float32, device="cuda")
+        _check(lib().ppx_op_gemm_exact(self._h, name.encode(), _ptr(a_hi), _ptr(a_lo), a_hi.shape[0], _ptr(c),
+                                       _stream()), "ppx_op_gemm_exact")
+        return c
+
+    def op_gemv(self, name: str, x):
+        import torch
+        rows, cols = self._shape(name)
+        assert x.dtype == torch.float32 and x.numel() == cols
+        y = torch.empty(rows, dtype=torch.float32, device="cuda")
+        _check(lib().ppx_op_gemv(self._h, name.encode(), _ptr(x), _ptr(y), _stream()), "ppx_op_gemv")
+        return y
+
+    def op_attention(self, q, k, v, pos0: int):
+        import torch
+        H, hd = self.info["n_head"], self.info["head_dim"]
+        M = q.shape[0]
+        o = torch.empty((M, H * hd), dtype=torch.float16, device="cuda")
+        _check(lib().ppx_op_attention(self._h, _ptr(q), _ptr(k), _ptr(v), M, pos0, _ptr(o), _stream()),
+               "ppx_op_attention")
+        return o
+
+    def op_attention_1row(self, q, k, v, pos: int):
+        import torch
+        H, hd = self.info["n_head"], self.info["head_dim"]
+        o = torch.empty(H * hd, dtype=torch.float32, device="cuda")
+        need = lib().ppx_workspace_bytes(self._h, 1, pos + 1)
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        _check(lib().ppx_op_attention_1row(self._h, _ptr(q), _ptr(k), _ptr(v), pos, _ptr(o), _ptr(ws), need,
+                                           _stream()), "ppx_op_attention_1row")
+        return o
+
+    def _shape(self, name):
+        I = self.info
+        d, qd, kvd, F, E, V = (I["d_model"], I["n_head"] * I["head_dim"], I["kv_dim"], I["n_ff"], I["ple_dim"],
+                               I["n_vocab"])
+        if name in ("tok_embd", "output"):
+            return V, d
+        il = int(name.split(".")[1])
+        kind = name.split(".", 2)[2]
+        own = il < I["n_layer_kv_from_start"]
+        return {"wq": (qd, d), "wk": (2 * kvd, d), "wo": (d, qd), "ffn_gate": (2 * F, d),
+                "ffn_down": (d, F), "ple_gate": (E, d), "ple_up": (d, E)}[kind]
+
+
+class KVCache:
+    """fp16 KV cache of the KV-owning layers in a caller-owned (torch) device buffer."""
+
+    def __init__(self, model: Model, n_ctx: int):
+        import torch
+        self.model = model
+        self.n_ctx = n_ctx
+        nbytes = lib().ppx_kv_bytes(model.handle, n_ctx)
+        self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+        self._h = c_void_p()
+        _check(lib().ppx_kv_init(model.handle, _ptr(self.buf), self.buf.numel(), n_ctx, ctypes.byref(self._h)),
+               "ppx_kv_init")
+
+    @property
+    def handle(self):
+        return self._h
+
+    @property
+    def n_pos(self) -> int:
+        return lib().ppx_kv_n_pos(self._h)
+
+    def clear(self):
+        _check(lib().ppx_kv_clear(self._h), "ppx_kv_clear")
+
+    def save(self, path, n_pos=None, stream=None):
+        n = self.n_pos if n_pos is None else n_pos
+        _check(lib().ppx_kv_save(self._h, os.fsencode(path), n, _stream(stream)), "ppx_kv_save")
+
+    def load(self, path, n_pos, stream=None):
+        _check(lib().ppx_kv_load(self._h, os.fsencode(path), n_pos, _stream(stream)), "ppx_kv_load")
+
+    def kv_tensors(self):
+        """(K, V) as torch fp16 views [Ls][n_ctx][kv_dim]."""
+        import torch
+        I = self.model.info
+        ls, kvd = I["n_layer_kv_from_start"], I["kv_dim"]
+        n = ls * self.n_ctx * kvd
+        h = self.buf[:4 * n].view(torch.float16)
+        return h[:n].view(ls, self.n_ctx, kvd), h[n:2 * n].view(ls, self.n_ctx, kvd)
+
+    def close(self):
+        if self._h:
+            lib().ppx_kv_free(self._h)
+            self._h = c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,734 @@
+// Prefill scheduler, KV store, KVCP snapshots and the extern "C" entry points.
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <fstream>
+#include <string>
+#include <vector>
+
+#include "ppx_internal.h"
+
+namespace ppx {
+bool log_enabled();
+int model_load(const uint8_t *b, size_t n, hipStream_t stream, ppx_model **out);
+int ensure_rope(ppx_model *m, int n_ctx);
+void model_free(ppx_model *m);
+
+namespace {
+
+#define PPX_TRY(x)                     \
+    do {                               \
+        const int st_ = (x);           \
+        if (st_ != PPX_OK) return st_; \
+    } while (0)
+
+inline size_t al(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace layout of one prefill (offsets from the workspace base).
+struct WsLayout {
+    size_t tok, x, a16, a16lo, q16, o16, h16, p16;
+    size_t xr, ar, qr, orow, hr, pr;
+    size_t gv_part, gv_cnt, at_part, at_cnt;
+    size_t total;
+    size_t gv_cnt_n, at_cnt_n;
+};
+
+WsLayout ws_layout(const ppx_model *m, int ub, int n_ctx) {
+    const ppx_model_info &I = m->info;
+    const int d = I.d_model, qd = I.n_head * I.head_dim, F = I.n_ff, E = I.ple_dim;
+    WsLayout w{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t r = o;
+        o += al(bytes);
+        return r;
+    };
+    w.tok = take(sizeof(int32_t) * (size_t)std::max(n_ctx, 1));
+    w.x = take(4ull * ub * d);
+    w.a16 = take(2ull * ub * std::max(d, 1));
+    w.a16lo = take(2ull * ub * std::max(d, 1));
+    w.q16 = take(2ull * ub * qd);
+    w.o16 = take(2ull * ub * qd);
+    w.h16 = take(2ull * ub * F);
+    w.p16 = take(2ull * ub * std::max(E, 1));
+    w.xr = take(4ull * d);
+    w.ar = take(4ull * d);
+    w.qr = take(4ull * qd);
+    w.orow = take(4ull * qd);
+    w.hr = take(4ull * F);
+    w.pr = take(4ull * std::max(E, 1));
+    // GEMV split-K scratch: the largest over the matrices the single-row path uses
+    size_t gvf = 0, gvc = 0;
+    auto gv = [&](int N, int K) {
+        if (N <= 0 || K <= 0) return;
+        gvf = std::max(gvf, gemv_scratch_floats(N, K));
+        gvc = std::max(gvc, (size_t)N / 32);
+    };
+    gv(qd, d);
+    gv(d, qd);
+    gv(2 * F, d);
+    gv(d, F);
+    gv(E, d);
+    gv(d, E);
+    gv(I.n_vocab, d);
+    w.gv_part = take(4 * gvf);
+    w.gv_cnt = take(4 * gvc);
+    w.gv_cnt_n = gvc;
+    w.at_part = take(4 * attn1_scratch_floats(I.n_head, I.head_dim, std::max(n_ctx, 1)));
+    w.at_cnt = take(4ull * I.n_kv_head);
+    w.at_cnt_n = I.n_kv_head;
+    w.total = o;
+    return w;
+}
+
+int predicate(int L, int Ls, int emb, int nseq, const uint8_t *inp, int crop) {
+    bool ok = crop && Ls > 0 && Ls < L && !emb && nseq == 1;
+    for (int il = Ls; ok && il <= L; ++il) ok = !(inp && inp[il]);
+    return ok ? 1 : 0;
+}
+
+struct Ctx {
+    ppx_model *m;
+    ppx_kv *kv;
+    hipStream_t s;
+    uint8_t *ws;
+    WsLayout L;
+    ppx_timing *tm = nullptr;  // per-phase timing requested
+    struct Rec { int phase; hipEvent_t a, b; };
+    std::vector<Rec> recs;
+    size_t next_ev = 0;
+    template <typename T>
+    T *at(size_t off) const { return reinterpret_cast<T *>(ws + off); }
+
+    hipEvent_t event() {
+        if (next_ev == m->events.size()) {
+            hipEvent_t e;
+            if (hipEventCreate(&e) != hipSuccess) return nullptr;
+            m->events.push_back(e);
+        }
+        return m->events[next_ev++];
+    }
+    hipEvent_t begin() {
+        if (!tm) return nullptr;
+        hipEvent_t e = event();
+        if (e) (void)hipEventRecord(e, s);
+        return e;
+    }
+    void end(int phase, hipEvent_t a) {
+        if (!tm || !a) return;
+        hipEvent_t b = event();
+        if (!b) return;
+        (void)hipEventRecord(b, s);
+        recs.push_back({phase, a, b});
+    }
+    int finish() {
+        if (!tm) return PPX_OK;
+        if (hipStreamSynchronize(s) != hipSuccess) return PPX_E_HIP;
+        for (const Rec &r : recs) {
+            float ms = 0.f;
+            if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return PPX_E_HIP;
+            tm->ms[r.phase] += ms;
+            tm->launches[r.phase] += 1;
+        }
+        return PPX_OK;
+    }
+};
+
+// Run one launch, timed under `phase` when timing was requested.
+#define PPX_LAUNCH(c, phase, expr)              \
+    do {                                        \
+        hipEvent_t ev0_ = (c).begin();          \
+        PPX_TRY(expr);                          \
+        (c).end((phase), ev0_);                 \
+    } while (0)
+
+inline double q4_bytes(const Q4R &w) { return (double)w.N * w.K * 18.0 / 32.0; }
+
+// One ubatch of M rows through layer il on the MFMA path.
+int layer_rows(Ctx &c, int il, int M, int row0, int pos0) {
+    const ppx_model *m = c.m;
+    const ppx_model_info &I = m->info;
+    const LayerW &w = m->layers[il];
+    const int d = I.d_model, hd = I.head_dim, qd = I.n_head * hd, kvd = I.kv_dim, F = I.n_ff;
+    float *x = c.at<float>(c.L.x);
+    __half *a16 = c.at<__half>(c.L.a16);
+    __half *q16 = c.at<__half>(c.L.q16);
+    __half *o16 = c.at<__half>(c.L.o16);
+    __half *h16 = c.at<__half>(c.L.h16);
+    const size_t lstride = (size_t)c.kv->n_ctx * kvd;
+
+    __half *a16lo = c.at<__half>(c.L.a16lo);
+    if (w.own)
+        PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_rmsnorm_split(x, w.attn_norm, m->eps, M, d, a16, a16lo, c.s));
+    else
+        PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_rmsnorm_f16(x, w.attn_norm, m->eps, M, d, a16, c.s));
+    GemmArgs g;
+    g.A = a16;
+    g.lda = d;
+    g.M = M;
+    g.W = w.wq;
+    g.epi = EPI_QKV;
+    g.out_f16 = q16;
+    g.qd = qd;
+    g.kvd = 0;
+    g.hd = hd;
+    g.pos0 = pos0;
+    g.rope = m->rope;
+    PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm(g, c.s));
+    if (w.own) {
+        // K and V on the exact-weight path, straight into this layer's cache rows
+        GemmArgs gk = g;
+        gk.A2 = a16lo;
+        gk.W = w.wkv;
+        gk.qd = 0;
+        gk.kvd = kvd;
+        gk.out_f16 = nullptr;
+        gk.kc = c.kv->k + il * lstride;
+        gk.vc = c.kv->v + il * lstride;
+        PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm_exact(gk, c.s));
+    }
+
+    AttnArgs at;
+    at.q = q16;
+    at.k = c.kv->k + (size_t)w.src * lstride;
+    at.v = c.kv->v + (size_t)w.src * lstride;
+    at.o = o16;
+    at.M = M;
+    at.H = I.n_head;
+    at.KVH = I.n_kv_head;
+    at.hd = hd;
+    at.pos0 = pos0;
+    PPX_LAUNCH(c, PPX_PHASE_ATTN, launch_attn_prefill(at, c.s));
+
+    GemmArgs go;
+    go.A = o16;
+    go.lda = qd;
+    go.M = M;
+    go.W = w.wo;
+    go.epi = EPI_ADD;
+    go.out_f32 = x;
+    PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm(go, c.s));
+
+    PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_rmsnorm_f16(x, w.ffn_norm, m->eps, M, d, a16, c.s));
+    GemmArgs gu;
+    gu.A = a16;
+    gu.lda = d;
+    gu.M = M;
+    gu.W = w.wgu;
+    gu.epi = EPI_GLU;
+    gu.out_f16 = h16;
+    gu.act = I.act;
+    PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm(gu, c.s));
+
+    GemmArgs gd;
+    gd.A = h16;
+    gd.lda = F;
+    gd.M = M;
+    gd.W = w.wdown;
+    gd.epi = EPI_ADD;
+    gd.out_f32 = x;
+    PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm(gd, c.s));
+
+    if (I.ple_dim) {
+        const int E = I.ple_dim;
+        __half *p16 = c.at<__half>(c.L.p16);
+        PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_rmsnorm_f16(x, w.ple_norm, m->eps, M, d, a16, c.s));
+        GemmArgs gp;
+        gp.A = a16;
+        gp.lda = d;
+        gp.M = M;
+        gp.W = w.wpg;
+        gp.epi = EPI_PLE;
+        gp.out_f16 = p16;
+        gp.ple_raw = m->ple_raw;
+        gp.tok = c.at<int32_t>(c.L.tok) + row0;
+        gp.ple_row_blocks = I.n_layer * E / 32;
+        gp.ple_col0 = il * E;
+        gp.ple_s = w.ple_s;
+        PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm(gp, c.s));
+        GemmArgs gq;
+        gq.A = p16;
+        gq.lda = E;
+        gq.M = M;
+        gq.W = w.wpu;
+        gq.epi = EPI_ADD;
+        gq.out_f32 = x;
+        PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm(gq, c.s));
+    }
+    if (c.tm) {
+        double nk = (double)w.wq.N * w.wq.K + (double)w.wo.N * w.wo.K + (double)w.wgu.N * w.wgu.K +
+                    (double)w.wdown.N * w.wdown.K;
+        if (w.own) nk += (double)w.wkv.N * w.wkv.K;
+        if (I.ple_dim) nk += (double)w.wpg.N * w.wpg.K + (double)w.wpu.N * w.wpu.K;
+        c.tm->gemm_flop += 2.0 * M * nk;
+        const double vis = (double)M * pos0 + 0.5 * (double)M * (M + 1);  // causal (query, key) pairs
+        c.tm->attn_flop += 4.0 * I.n_head * hd * vis;
+    }
+    return PPX_OK;
+}
+
+GemvArgs gemv_base(Ctx &c, const float *x, const Q4R &W, int epi, float *out) {
+    GemvArgs a;
+    a.x = x;
+    a.W = W;
+    a.epi = epi;
+    a.out = out;
+    a.partial = c.at<float>(c.L.gv_part);
+    a.counter = c.at<uint32_t>(c.L.gv_cnt);
+    return a;
+}
+
+// Layer il for the single output row (pruned KV-shared layers), fp32 throughout.
+int layer_row(Ctx &c, int il, int pos, int tok) {
+    const ppx_model *m = c.m;
+    const ppx_model_info &I = m->info;
+    const LayerW &w = m->layers[il];
+    const int d = I.d_model, hd = I.head_dim, kvd = I.kv_dim;
+    float *xr = c.at<float>(c.L.xr), *ar = c.at<float>(c.L.ar);
+    float *qr = c.at<float>(c.L.qr), *orow = c.at<float>(c.L.orow);
+    float *hr = c.at<float>(c.L.hr), *pr = c.at<float>(c.L.pr);
+    const size_t lstride = (size_t)c.kv->n_ctx * kvd;
+
+    PPX_LAUNCH(c, PPX_PHASE_ROW, launch_rmsnorm_f32(xr, w.attn_norm, m->eps, 1, d, ar, c.s));
+    GemvArgs gq = gemv_base(c, ar, w.wq, GV_QROPE, qr);
+    gq.hd = hd;
+    gq.pos = pos;
+    gq.rope = m->rope;
+    PPX_LAUNCH(c, PPX_PHASE_ROW, launch_gemv(gq, c.s));
+    Attn1Args at;
+    at.q = qr;
+    at.k = c.kv->k + (size_t)w.src * lstride;
+    at.v = c.kv->v + (size_t)w.src * lstride;
+    at.o = orow;
+    at.H = I.n_head;
+    at.KVH = I.n_kv_head;
+    at.hd = hd;
+    at.pos = pos;
+    at.partial = c.at<float>(c.L.at_part);
+    at.counter = c.at<uint32_t>(c.L.at_cnt);
+    PPX_LAUNCH(c, PPX_PHASE_ROW, launch_attn_1row(at, c.s));
+    PPX_LAUNCH(c, PPX_PHASE_ROW, launch_gemv(gemv_base(c, orow, w.wo, GV_ADD, xr), c.s));
+    PPX_LAUNCH(c, PPX_PHASE_ROW, launch_rmsnorm_f32(xr, w.ffn_norm, m->eps, 1, d, ar, c.s));
+    GemvArgs gg = gemv_base(c, ar, w.wgu, GV_GLU, hr);
+    gg.act = I.act;
+    PPX_LAUNCH(c, PPX_PHASE_ROW, launch_gemv(gg, c.s));
+    PPX_LAUNCH(c, PPX_PHASE_ROW, launch_gemv(gemv_base(c, hr, w.wdown, GV_ADD, xr), c.s));
+    if (c.tm) {
+        c.tm->row_bytes += q4_bytes(w.wq) + q4_bytes(w.wo) + q4_bytes(w.wgu) + q4_bytes(w.wdown) +
+                           4.0 * (pos + 1) * kvd;
+        if (I.ple_dim) c.tm->row_bytes += q4_bytes(w.wpg) + q4_bytes(w.wpu);
+    }
+    if (I.ple_dim) {
+        PPX_LAUNCH(c, PPX_PHASE_ROW, launch_rmsnorm_f32(xr, w.ple_norm, m->eps, 1, d, ar, c.s));
+        GemvArgs gp = gemv_base(c, ar, w.wpg, GV_PLE, pr);
+        gp.ple_raw = m->ple_raw;
+        gp.tok = tok;
+        gp.ple_row_blocks = I.n_layer * I.ple_dim / 32;
+        gp.ple_col0 = il * I.ple_dim;
+        gp.ple_s = w.ple_s;
+        PPX_LAUNCH(c, PPX_PHASE_ROW, launch_gemv(gp, c.s));
+        PPX_LAUNCH(c, PPX_PHASE_ROW, launch_gemv(gemv_base(c, pr, w.wpu, GV_ADD, xr), c.s));
+    }
+    return PPX_OK;
+}
+
+int head_row(Ctx &c, const float *x_last, float *logits) {
+    const ppx_model *m = c.m;
+    float *ar = c.at<float>(c.L.ar);
+    PPX_LAUNCH(c, PPX_PHASE_ROW, launch_rmsnorm_f32(x_last, m->out_norm, m->eps, 1, m->info.d_model, ar, c.s));
+    PPX_LAUNCH(c, PPX_PHASE_ROW, launch_gemv(gemv_base(c, ar, m->out, GV_F32, logits), c.s));
+    if (c.tm) c.tm->row_bytes += q4_bytes(m->out);
+    return PPX_OK;
+}
+
+int prefill(ppx_model *m, ppx_kv *kv, const int32_t *tokens, int n, const ppx_prefill_params *p, void *ws,
+            size_t ws_bytes, float *logits, hipStream_t s) {
+    if (!m || !kv || !p || !logits || !ws) return PPX_E_INVAL;
+    if (kv->m != m) return PPX_E_INVAL;
+    if (n <= 0) return PPX_E_EMPTY;
+    if (!tokens) return PPX_E_INVAL;
+    const ppx_model_info &I = m->info;
+    if (p->embeddings != 0 || p->n_seq_max != 1) return PPX_E_UNSUPPORTED;
+    if (p->n_ubatch < 1 || p->n_ubatch > PPX_MAX_UBATCH) return PPX_E_INVAL;
+    for (int i = 0; i < n; ++i)
+        if (tokens[i] < 0 || tokens[i] >= I.n_vocab) return PPX_E_TOKEN;
+    const int p0 = kv->n_pos;
+    if ((long)p0 + n > kv->n_ctx) return PPX_E_CTX;
+    if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return PPX_E_INVAL;
+    const int ub = p->n_ubatch;
+    Ctx c{m, kv, s, static_cast<uint8_t *>(ws), ws_layout(m, ub, kv->n_ctx)};
+    if (p->timing) {
+        std::memset(p->timing, 0, sizeof(*p->timing));
+        c.tm = p->timing;
+    }
+    if (ws_bytes < c.L.total) return PPX_E_NOMEM;
+    const int L = I.n_layer, Ls = I.n_layer_kv_from_start, d = I.d_model;
+    const int can = predicate(L, Ls, p->embeddings, p->n_seq_max, nullptr, 1);
+    bool prune;
+    if (p->prune == PPX_PRUNE_AUTO) prune = can;
+    else if (p->prune == PPX_PRUNE_OFF) prune = false;
+    else if (p->prune == PPX_PRUNE_ON) {
+        if (!can) return PPX_E_UNSUPPORTED;
+        prune = true;
+    } else return PPX_E_INVAL;
+
+    int32_t *tok_dev = c.at<int32_t>(c.L.tok);
+    if (hipMemcpyAsync(tok_dev, tokens, sizeof(int32_t) * n, hipMemcpyHostToDevice, s) != hipSuccess)
+        return PPX_E_HIP;
+    PPX_TRY(launch_fill_u32(c.at<uint32_t>(c.L.gv_cnt), 0u, c.L.gv_cnt_n, s));
+    PPX_TRY(launch_fill_u32(c.at<uint32_t>(c.L.at_cnt), 0u, c.L.at_cnt_n, s));
+    if (log_enabled())
+        std::fprintf(stderr, "[ppx] prefill %d tokens at position %d, ubatch %d, prune %s\n", n, p0, ub,
+                     prune ? "on" : "off");
+
+    float *x = c.at<float>(c.L.x);
+    for (int s0 = 0; s0 < n; s0 += ub) {
+        const int M = std::min(ub, n - s0);
+        const bool last = s0 + M == n;
+        const int pos0 = p0 + s0;
+        PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_embed(m->tok, tok_dev + s0, M, m->embd_scale, x, s));
+        const int full_layers = prune ? Ls : L;
+        for (int il = 0; il < full_layers; ++il) {
+            if (p->debug_rows)
+                PPX_TRY(launch_copy_f32(x, p->debug_rows + ((size_t)il * n + s0) * d, M * d, s));
+            PPX_TRY(layer_rows(c, il, M, s0, pos0));
+            if (last && p->debug_hidden)
+                PPX_TRY(launch_copy_f32(x + (size_t)(M - 1) * d, p->debug_hidden + (size_t)il * d, d, s));
+        }
+        if (!last) continue;
+        const float *x_last = x + (size_t)(M - 1) * d;
+        if (prune) {
+            float *xr = c.at<float>(c.L.xr);
+            PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_copy_f32(x_last, xr, d, s));  // the one row kept
+            const int pos = p0 + n - 1;
+            for (int il = Ls; il < L; ++il) {
+                if (p->debug_rows)
+                    PPX_TRY(launch_copy_f32(xr, p->debug_rows + ((size_t)il * n + n - 1) * d, d, s));
+                PPX_TRY(layer_row(c, il, pos, tokens[n - 1]));
+                if (p->debug_hidden) PPX_TRY(launch_copy_f32(xr, p->debug_hidden + (size_t)il * d, d, s));
+            }
+            x_last = xr;
+        }
+        PPX_TRY(head_row(c, x_last, logits));
+    }
+    PPX_TRY(c.finish());
+    kv->n_pos = p0 + n;
+    return PPX_OK;
+}
+
+// ------------------------------------------------------------------ KVCP snapshots
+
+int kv_save(const ppx_kv *kv, const char *path, int n_pos, hipStream_t s) {
+    if (!kv || !path) return PPX_E_INVAL;
+    if (n_pos < 0 || n_pos > kv->n_pos) return PPX_E_CTX;
+    const ppx_model_info &I = kv->m->info;
+    const int nl = I.n_layer_kv_from_start, kvd = I.kv_dim;
+    const size_t row = (size_t)n_pos * kvd;
+    std::vector<uint16_t> buf(2 * (size_t)nl * row);
+    if (hipStreamSynchronize(s) != hipSuccess) return PPX_E_HIP;
+    for (int il = 0; il < nl && row; ++il) {
+        const size_t src = (size_t)il * kv->n_ctx * kvd;
+        if (hipMemcpy(buf.data() + il * row, kv->k + src, row * 2, hipMemcpyDeviceToHost) != hipSuccess ||
+            hipMemcpy(buf.data() + (nl + il) * row, kv->v + src, row * 2, hipMemcpyDeviceToHost) != hipSuccess)
+            return PPX_E_HIP;
+    }
+    std::FILE *f = std::fopen(path, "wb");
+    if (!f) return PPX_E_IO;
+    const int32_t hdr[3] = {n_pos, nl, kvd};
+    bool ok = std::fwrite("KVCP", 1, 4, f) == 4 && std::fwrite(hdr, 4, 3, f) == 3 &&
+              std::fwrite(buf.data(), 2, buf.size(), f) == buf.size();
+    ok = (std::fclose(f) == 0) && ok;
+    return ok ? PPX_OK : PPX_E_IO;
+}
+
+// Validates a KVCP file; leaves *fpos = file positions when the header was read.
+int kvfile_check(const char *path, int nl, int kvd, int n_pos, int n_ctx, int *fpos) {
+    std::FILE *f = std::fopen(path, "rb");
+    if (!f) return PPX_E_IO;
+    char mg[4];
+    int32_t hdr[3];
+    int st = PPX_OK;
+    if (std::fread(mg, 1, 4, f) != 4 || std::memcmp(mg, "KVCP", 4) != 0 || std::fread(hdr, 4, 3, f) != 3) {
+        st = PPX_E_FORMAT;
+    } else {
+        if (fpos) *fpos = hdr[0];
+        if (hdr[1] != nl || hdr[2] != kvd) {
+            st = PPX_E_MISMATCH;
+        } else if (hdr[0] < 0) {
+            st = PPX_E_FORMAT;
+        } else {
+            std::fseek(f, 0, SEEK_END);
+            const long sz = std::ftell(f);
+            const long want = 16 + 4l * nl * hdr[0] * kvd;
+            if (sz != want) st = PPX_E_FORMAT;
+            else if (n_pos < 0 || n_pos > hdr[0]) st = PPX_E_FORMAT;
+            else if (n_pos > n_ctx) st = PPX_E_CTX;
+        }
+    }
+    std::fclose(f);
+    return st;
+}
+
+int kv_load(ppx_kv *kv, const char *path, int n_pos, hipStream_t s) {
+    if (!kv || !path) return PPX_E_INVAL;
+    kv->n_pos = 0;
+    const ppx_model_info &I = kv->m->info;
+    const int nl = I.n_layer_kv_from_start, kvd = I.kv_dim;
+    int fpos = 0;
+    int st = kvfile_check(path, nl, kvd, n_pos, kv->n_ctx, &fpos);
+    if (st) {
+        if (log_enabled()) std::fprintf(stderr, "[ppx] KV cache file %s rejected (%d)\n", path, st);
+        return st;
+    }
+    std::FILE *f = std::fopen(path, "rb");
+    if (!f) return PPX_E_IO;
+    const size_t frow = (size_t)fpos * kvd, row = (size_t)n_pos * kvd;
+    std::vector<uint16_t> buf(2 * (size_t)nl * row);
+    for (int part = 0; part < 2 && row; ++part)
+        for (int il = 0; il < nl; ++il) {
+            std::fseek(f, 16 + (long)(((size_t)part * nl + il) * frow * 2), SEEK_SET);
+            if (std::fread(buf.data() + ((size_t)part * nl + il) * row, 2, row, f) != row) st = PPX_E_IO;
+        }
+    std::fclose(f);
+    if (st) return st;
+    for (int il = 0; il < nl && row; ++il) {
+        const size_t dst = (size_t)il * kv->n_ctx * kvd;
+        if (hipMemcpyAsync(kv->k + dst, buf.data() + il * row, row * 2, hipMemcpyHostToDevice, s) != hipSuccess ||
+            hipMemcpyAsync(kv->v + dst, buf.data() + (nl + il) * row, row * 2, hipMemcpyHostToDevice, s) !=
+                hipSuccess)
+            return PPX_E_HIP;
+    }
+    if (hipStreamSynchronize(s) != hipSuccess) return PPX_E_HIP;
+    kv->n_pos = n_pos;
+    if (log_enabled()) {
+        std::fprintf(stderr, "KV cache loaded: %d positions from %s\n", n_pos, path);
+        std::fprintf(stderr, "Skipping %d cached prompt tokens\n", n_pos);
+    }
+    return PPX_OK;
+}
+
+const Q4R *find_q4(const ppx_model *m, const char *name, int *kind) {
+    if (!m || !name) return nullptr;
+    auto it = m->q4.find(name);
+    if (it == m->q4.end()) return nullptr;
+    auto k = m->q4_kind.find(name);
+    *kind = k == m->q4_kind.end() ? 0 : k->second;
+    return &it->second;
+}
+
+}  // namespace
+}  // namespace ppx
+
+using namespace ppx;
+
+// ====================================================================== C ABI
+
+extern "C" {
+
+int ppx_model_load(const void *container, size_t bytes, void *hip_stream, ppx_model **out) {
+    if (!container || !out) return PPX_E_INVAL;
+    *out = nullptr;
+    return model_load(static_cast<const uint8_t *>(container), bytes, (hipStream_t)hip_stream, out);
+}
+
+int ppx_model_load_file(const char *path, void *hip_stream, ppx_model **out) {
+    if (!path || !out) return PPX_E_INVAL;
+    *out = nullptr;
+    std::ifstream f(path, std::ios::binary | std::ios::ate);
+    if (!f) return PPX_E_IO;
+    const std::streamsize n = f.tellg();
+    if (n <= 0) return PPX_E_IO;
+    std::vector<uint8_t> buf((size_t)n);
+    f.seekg(0);
+    if (!f.read(reinterpret_cast<char *>(buf.data()), n)) return PPX_E_IO;
+    return model_load(buf.data(), buf.size(), (hipStream_t)hip_stream, out);
+}
+
+void ppx_model_free(ppx_model *m) { model_free(m); }
+
+int ppx_model_get_info(const ppx_model *m, ppx_model_info *out) {
+    if (!m || !out) return PPX_E_INVAL;
+    *out = m->info;
+    return PPX_OK;
+}
+
+size_t ppx_model_device_bytes(const ppx_model *m) { return m ? m->dev_bytes : 0; }
+
+size_t ppx_kv_bytes(const ppx_model *m, int n_ctx) {
+    if (!m || n_ctx <= 0) return 0;
+    return 2ull * m->info.n_layer_kv_from_start * (size_t)n_ctx * m->info.kv_dim * 2;
+}
+
+int ppx_kv_init(ppx_model *m, void *kv_dev, size_t bytes, int n_ctx, ppx_kv **out) {
+    if (!m || !out || n_ctx <= 0) return PPX_E_INVAL;
+    *out = nullptr;
+    const size_t need = ppx_kv_bytes(m, n_ctx);
+    if (need && !kv_dev) return PPX_E_INVAL;
+    if (bytes < need) return PPX_E_NOMEM;
+    if ((reinterpret_cast<uintptr_t>(kv_dev) & 255) != 0) return PPX_E_INVAL;
+    PPX_TRY(ensure_rope(m, n_ctx));
+    ppx_kv *kv = new ppx_kv();
+    kv->m = m;
+    kv->k = static_cast<__half *>(kv_dev);
+    kv->v = kv->k + need / 4;
+    kv->n_ctx = n_ctx;
+    *out = kv;
+    return PPX_OK;
+}
+
+void ppx_kv_free(ppx_kv *kv) { delete kv; }
+int ppx_kv_n_pos(const ppx_kv *kv) { return kv ? kv->n_pos : PPX_E_INVAL; }
+int ppx_kv_n_ctx(const ppx_kv *kv) { return kv ? kv->n_ctx : PPX_E_INVAL; }
+int ppx_kv_clear(ppx_kv *kv) {
+    if (!kv) return PPX_E_INVAL;
+    kv->n_pos = 0;
+    return PPX_OK;
+}
+
+int ppx_kv_save(const ppx_kv *kv, const char *path, int n_pos, void *hip_stream) {
+    return kv_save(kv, path, n_pos, (hipStream_t)hip_stream);
+}
+
+int ppx_kv_load(ppx_kv *kv, const char *path, int n_pos, void *hip_stream) {
+    return kv_load(kv, path, n_pos, (hipStream_t)hip_stream);
+}
+
+int ppx_kvfile_validate(const char *path, int n_layers, int kv_dim, int n_pos, int n_ctx, int *file_n_pos) {
+    if (!path) return PPX_E_INVAL;
+    return kvfile_check(path, n_layers, kv_dim, n_pos, n_ctx, file_n_pos);
+}
+
+size_t ppx_workspace_bytes(const ppx_model *m, int n_ubatch, int n_ctx) {
+    if (!m || n_ubatch < 1 || n_ctx < 1) return 0;
+    return ws_layout(m, n_ubatch, n_ctx).total;
+}
+
+int ppx_prefill(ppx_model *m, ppx_kv *kv, const int32_t *tokens_host, int n_tokens, const ppx_prefill_params *p,
+                void *ws_dev, size_t ws_bytes, float *logits_dev, void *hip_stream) {
+    return prefill(m, kv, tokens_host, n_tokens, p, ws_dev, ws_bytes, logits_dev, (hipStream_t)hip_stream);
+}
+
+int ppx_prune_predicate(int n_layer, int n_layer_kv_from_start, int embeddings, int n_seq_max,
+                        const uint8_t *embeddings_layer_inp, int crop_before_nextn) {
+    return predicate(n_layer, n_layer_kv_from_start, embeddings, n_seq_max, embeddings_layer_inp, crop_before_nextn);
+}
+
+int ppx_op_dequant(const ppx_model *m, const char *tensor, float *out_dev, void *hip_stream) {
+    int kind;
+    const Q4R *w = find_q4(m, tensor, &kind);
+    if (!w || !out_dev) return PPX_E_INVAL;
+    return launch_dequant(*w, out_dev, (hipStream_t)hip_stream);
+}
+
+int ppx_op_gemm(const ppx_model *m, const char *tensor, const void *a_dev_f16, int M, float *c_dev,
+                void *hip_stream) {
+    int kind;
+    const Q4R *w = find_q4(m, tensor, &kind);
+    if (!w || !a_dev_f16 || !c_dev || M < 0) return PPX_E_INVAL;
+    if (kind == 3) return PPX_E_INVAL;  // exact-weight tensors go through ppx_op_gemm_exact
+    GemmArgs g;
+    g.A = static_cast<const __half *>(a_dev_f16);
+    g.lda = w->K;
+    g.M = M;
+    g.W = *w;
+    g.epi = EPI_F32;
+    g.out_f32 = c_dev;
+    return launch_gemm(g, (hipStream_t)hip_stream);
+}
+
+int ppx_op_gemm_exact(const ppx_model *m, const char *tensor, const void *a_hi, const void *a_lo, int M,
+                      float *c_dev, void *hip_stream) {
+    int kind;
+    const Q4R *w = find_q4(m, tensor, &kind);
+    if (!w || !a_hi || !a_lo || !c_dev || M < 0) return PPX_E_INVAL;
+    GemmArgs g;
+    g.A = static_cast<const __half *>(a_hi);
+    g.A2 = static_cast<const __half *>(a_lo);
+    g.lda = w->K;
+    g.M = M;
+    g.W = *w;
+    g.epi = EPI_F32;
+    g.out_f32 = c_dev;
+    return launch_gemm_exact(g, (hipStream_t)hip_stream);
+}
+
+int ppx_op_gemv(const ppx_model *m, const char *tensor, const float *x_dev, float *y_dev, void *hip_stream) {
+    // split-K scratch: allocated per call (test entry point only)
+    int kind;
+    const Q4R *w = find_q4(m, tensor, &kind);
+    if (!w || !x_dev || !y_dev) return PPX_E_INVAL;
+    const size_t nf = gemv_scratch_floats(w->N, w->K), nc = (size_t)w->N / 32;
+    void *scratch = nullptr;
+    if (hipMalloc(&scratch, 4 * (nf + nc) + 256) != hipSuccess) return PPX_E_NOMEM;
+    GemvArgs a;
+    a.x = x_dev;
+    a.W = *w;
+    a.epi = GV_F32;
+    a.out = y_dev;
+    a.partial = static_cast<float *>(scratch);
+    a.counter = reinterpret_cast<uint32_t *>(static_cast<float *>(scratch) + nf);
+    hipStream_t s = (hipStream_t)hip_stream;
+    int st = launch_fill_u32(a.counter, 0u, nc, s);
+    if (!st) st = launch_gemv(a, s);
+    if (hipStreamSynchronize(s) != hipSuccess && !st) st = PPX_E_HIP;
+    (void)hipFree(scratch);
+    return st;
+}
+
+int ppx_op_attention(const ppx_model *m, const void *q_dev, const void *k_dev, const void *v_dev, int M, int pos0,
+                     void *o_dev, void *hip_stream) {
+    if (!m || !q_dev || !k_dev || !v_dev || !o_dev || M < 0 || pos0 < 0) return PPX_E_INVAL;
+    AttnArgs a;
+    a.q = static_cast<const __half *>(q_dev);
+    a.k = static_cast<const __half *>(k_dev);
+    a.v = static_cast<const __half *>(v_dev);
+    a.o = static_cast<__half *>(o_dev);
+    a.M = M;
+    a.H = m->info.n_head;
+    a.KVH = m->info.n_kv_head;
+    a.hd = m->info.head_dim;
+    a.pos0 = pos0;
+    return launch_attn_prefill(a, (hipStream_t)hip_stream);
+}
+
+int ppx_op_attention_1row(const ppx_model *m, const float *q_dev, const void *k_dev, const void *v_dev, int pos,
+                          float *o_dev, void *ws_dev, size_t ws_bytes, void *hip_stream) {
+    if (!m || !q_dev || !k_dev || !v_dev || !o_dev || !ws_dev || pos < 0) return PPX_E_INVAL;
+    const WsLayout L = ws_layout(m, 1, pos + 1);
+    if (ws_bytes < L.total) return PPX_E_NOMEM;
+    uint8_t *ws = static_cast<uint8_t *>(ws_dev);
+    hipStream_t s = (hipStream_t)hip_stream;
+    PPX_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(ws + L.at_cnt), 0u, L.at_cnt_n, s));
+    Attn1Args a;
+    a.q = q_dev;
+    a.k = static_cast<const __half *>(k_dev);
+    a.v = static_cast<const __half *>(v_dev);
+    a.o = o_dev;
+    a.H = m->info.n_head;
+    a.KVH = m->info.n_kv_head;
+    a.hd = m->info.head_dim;
+    a.pos = pos;
+    a.partial = reinterpret_cast<float *>(ws + L.at_part);
+    a.counter = reinterpret_cast<uint32_t *>(ws + L.at_cnt);
+    return launch_attn_1row(a, s);
+}
+
+const char *ppx_status_str(int st) {
+    switch (st) {
+    case PPX_OK: return "ok";
+    case PPX_E_INVAL: return "invalid argument";
+    case PPX_E_TOKEN: return "token id out of range";
+    case PPX_E_CTX: return "context length exceeded";
+    case PPX_E_IO: return "i/o error";
+    case PPX_E_FORMAT: return "bad file format";
+    case PPX_E_MISMATCH: return "snapshot does not match the model";
+    case PPX_E_UNSUPPORTED: return "unsupported shape or option";
+    case PPX_E_HIP: return "HIP runtime error";
+    case PPX_E_NOMEM: return "out of memory / buffer too small";
+    case PPX_E_EMPTY: return "empty prompt";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

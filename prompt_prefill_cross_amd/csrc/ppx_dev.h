@@ -1,0 +1,85 @@
+// Device-side helpers shared by the engine's kernels (gfx950, wave64).
+#pragma once
+
+#include "ppx_internal.h"
+
+namespace ppx {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f4 mfma16(const h8 &a, const h8 &b, const f4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Eight codes of one repacked word -> fp16 d*(code-8), rounded to nearest even.
+// (w >> 4i) & 0x000F000F | 0x6400_6400 is the fp16 pair (1024+q_{2i}, 1024+q_{2i+1});
+// subtracting 1032 is exact, the product with d rounds once.
+__device__ __forceinline__ h8 q4_word_to_h8(uint32_t w, _Float16 d) {
+    h8 r;
+    const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const h2 dd = {d, d};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t t = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
+        h2 v = __builtin_bit_cast(h2, t);
+        v = (v - bias) * dd;
+        r[2 * i] = v[0];
+        r[2 * i + 1] = v[1];
+    }
+    return r;
+}
+
+// Code of element e (0..7) in a repacked word.
+__device__ __forceinline__ int q4_word_code(uint32_t w, int e) {
+    int sh = (e & 1) ? (16 + 4 * (e >> 1)) : (4 * (e >> 1));
+    return (int)((w >> sh) & 15u);
+}
+
+// Exact fp32 weight W[n][k] of a repacked matrix.
+__device__ __forceinline__ float q4r_weight(const Q4R &w, int n, int k) {
+    const int kc = k >> 6, s = (k >> 5) & 1, g = (k >> 3) & 3, e = k & 7;
+    const int grp = n >> 4, col = n & 15;
+    const size_t base = (size_t)grp * (w.K >> 6) + kc;
+    const uint32_t word = w.nib[(base * 64 + g * 16 + col) * 2 + s];
+    const float d = __half2float(w.scl[(base * 16 + col) * 2 + s]);
+    return d * (float)(q4_word_code(word, e) - 8);
+}
+
+// Exact fp32 value of column c of a raw Q4_0 row (18-byte blocks).
+__device__ __forceinline__ float q4_raw_weight(const uint8_t *row, int c) {
+    const uint8_t *b = row + (size_t)(c >> 5) * 18;
+    const int j = c & 31;
+    const uint16_t dbits = (uint16_t)b[0] | ((uint16_t)b[1] << 8);
+    const float d = __half2float(__ushort_as_half(dbits));
+    const uint8_t byte = b[2 + (j & 15)];
+    const int q = (j < 16) ? (byte & 15) : (byte >> 4);
+    return d * (float)(q - 8);
+}
+
+__device__ __forceinline__ float gelu_tanh_f(float z) {
+    const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+    return 0.5f * z * (1.0f + tanhf(k0 * (z + 0.044715f * z * z * z)));
+}
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
+
+__device__ __forceinline__ float act_f(int act, float g) {
+    return act == ACT_GEGLU ? gelu_tanh_f(g) : silu_f(g);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+}  // namespace ppx

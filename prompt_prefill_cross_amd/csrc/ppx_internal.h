@@ -1,0 +1,178 @@
+// Internal declarations shared by the engine's host code and kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include <cstdint>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "../../include/ppx.h"
+
+namespace ppx {
+
+// Repacked Q4_0 matrix W[N][K] (N % 16 == 0, K % 64 == 0).
+//
+// The MFMA v_mfma_f32_16x16x32_f16 B operand gives lane l the column
+// n = l % 16 and eight consecutive k's of a 32-wide block, k = 8*(l/16)+0..7.
+// One Q4_0 block is exactly one such K step.  For every 16-column group and
+// every 64-wide K chunk (two blocks) the repacked layout stores, per lane, two
+// 32-bit words (block 0, block 1) holding that lane's eight 4-bit codes,
+// arranged so that (w >> 4i) & 0x000F000F yields the codes of k = 2i and
+// 2i+1 in the two 16-bit halves; and per column its two fp16 block scales.
+//   nib[((g * (K/64) + c) * 64 + lane) * 2 + s]   uint32
+//   scl[((g * (K/64) + c) * 16 + col) * 2 + s]    fp16
+// with g = n / 16, c = k / 64, s = (k / 32) % 2.  The decoded weight is
+// d * (code - 8), identical to the container's Q4_0 block.
+struct Q4R {
+    const uint32_t *nib = nullptr;
+    const __half *scl = nullptr;
+    int N = 0, K = 0;
+};
+
+enum Act { ACT_GEGLU = 0, ACT_SWIGLU = 1 };
+
+struct LayerW {
+    bool own = false;
+    int src = 0;        // KV source layer (own: itself)
+    float ple_s = 0.f;  // per-layer embedding scale
+    const float *attn_norm = nullptr, *ffn_norm = nullptr, *ple_norm = nullptr;
+    Q4R wq;    // [qd][d], rows in rope-pair order
+    Q4R wkv;   // own only: [2 kvd][d] rows K (rope-pair order) | V; run on the exact-weight path
+    Q4R wo;    // [d][qd]
+    Q4R wgu;   // [2F][d]: 16-row blocks alternate gate, up
+    Q4R wdown; // [d][F]
+    Q4R wpg;   // [E][d]
+    Q4R wpu;   // [d][E]
+};
+
+struct HostTensor {
+    int type;  // 0 f32, 1 q4_0
+    uint64_t rows, cols, offset;
+};
+
+}  // namespace ppx
+
+struct ppx_model {
+    ppx_model_info info{};
+    int tied = 1;
+    float eps = 1e-6f, rope_base = 10000.f, embd_scale = 1.f;
+    std::vector<ppx::LayerW> layers;
+    ppx::Q4R tok, out;  // out == tok when tied
+    const float *out_norm = nullptr;
+    const uint8_t *ple_raw = nullptr;  // raw Q4_0 blocks [V][L*E/32][18]
+    void *dev = nullptr;               // one allocation for all weights
+    size_t dev_bytes = 0;
+    float2 *rope = nullptr;            // [rope_n][head_dim/2] (cos, sin)
+    int rope_n = 0;
+    // named tensors for the kernel-level entry points
+    std::unordered_map<std::string, ppx::Q4R> q4;
+    std::unordered_map<std::string, int> q4_kind;  // 0 plain, 1 qkv, 2 gate|up
+    std::vector<hipEvent_t> events;                // reusable pool for per-phase timing
+};
+
+struct ppx_kv {
+    const ppx_model *m = nullptr;
+    __half *k = nullptr, *v = nullptr;  // [Ls][n_ctx][kv_dim]
+    int n_ctx = 0, n_pos = 0;
+};
+
+namespace ppx {
+
+// ---------------------------------------------------------------- launchers
+
+// GEMM epilogues
+enum GemmEpi {
+    EPI_F32 = 0,  // C -> fp32 out[M][N]
+    EPI_ADD = 1,  // resid[M][N] += C
+    EPI_QKV = 2,  // rope(Q) -> q16, rope(K), V -> fp16 cache rows
+    EPI_GLU = 3,  // act(gate) * up -> fp16 h[M][F]
+    EPI_PLE = 4,  // gelu(C) * s * deq(ple_table[tok]) -> fp16 [M][E]
+};
+
+struct GemmArgs {
+    const __half *A = nullptr;  // [M][K] fp16 (the high part on the exact-weight path)
+    const __half *A2 = nullptr; // [M][K] fp16 low part a - fp16(a) (exact-weight path only)
+    int lda = 0;
+    int M = 0;
+    Q4R W;
+    int epi = EPI_F32;
+    float *out_f32 = nullptr;   // EPI_F32 (ld = N), EPI_ADD residual (ld = N)
+    __half *out_f16 = nullptr;  // EPI_QKV q16 [M][qd]; EPI_GLU h [M][F]; EPI_PLE [M][E]
+    // rope / cache (EPI_QKV)
+    int qd = 0, kvd = 0, hd = 0;
+    int pos0 = 0;               // position of row 0
+    const float2 *rope = nullptr;
+    __half *kc = nullptr, *vc = nullptr;  // cache rows of this layer at position 0
+    int act = ACT_GEGLU;
+    // per-layer embedding (EPI_PLE)
+    const uint8_t *ple_raw = nullptr;
+    const int32_t *tok = nullptr;  // [M] token ids of the rows
+    int ple_row_blocks = 0;        // L*E/32
+    int ple_col0 = 0;              // il*E
+    float ple_s = 0.f;
+};
+int launch_gemm(const GemmArgs &a, hipStream_t s);
+// Exact-weight variant: B = (code - 8) exactly in fp16, A = A + A2 (split fp16),
+// block scales applied to each 32-wide partial in fp32.  Used for K and V.
+int launch_gemm_exact(const GemmArgs &a, hipStream_t s);
+
+enum GemvEpi {
+    GV_F32 = 0,   // y -> out[N]
+    GV_ADD = 1,   // resid[N] += y
+    GV_QROPE = 2, // rope(Q part) -> out fp32 [qd] (natural order), pos
+    GV_GLU = 3,   // act(gate)*up -> out fp32 [F]
+    GV_PLE = 4,   // gelu(y) * s * deq(ple row) -> out fp32 [E]
+};
+struct GemvArgs {
+    const float *x = nullptr;  // [K]
+    Q4R W;
+    int epi = GV_F32;
+    float *out = nullptr;
+    int hd = 0, pos = 0;
+    const float2 *rope = nullptr;
+    int act = ACT_GEGLU;
+    const uint8_t *ple_raw = nullptr;
+    int tok = 0, ple_row_blocks = 0, ple_col0 = 0;
+    float ple_s = 0.f;
+    float *partial = nullptr;    // scratch [ksplit][N]
+    uint32_t *counter = nullptr; // scratch [N/32], zero on entry, zero on exit
+    int ksplit = 1;
+};
+int launch_gemv(const GemvArgs &a, hipStream_t s);
+size_t gemv_scratch_floats(int N, int K);
+
+struct AttnArgs {
+    const __half *q = nullptr;  // [M][H][hd]
+    const __half *k = nullptr, *v = nullptr;  // cache [P][KVH][hd]
+    __half *o = nullptr;        // [M][H*hd]
+    int M = 0, H = 0, KVH = 0, hd = 0, pos0 = 0;
+};
+int launch_attn_prefill(const AttnArgs &a, hipStream_t s);
+
+struct Attn1Args {
+    const float *q = nullptr;  // [H][hd]
+    const __half *k = nullptr, *v = nullptr;
+    float *o = nullptr;        // [H*hd]
+    int H = 0, KVH = 0, hd = 0, pos = 0;
+    float *partial = nullptr;  // scratch
+    uint32_t *counter = nullptr;
+};
+int launch_attn_1row(const Attn1Args &a, hipStream_t s);
+size_t attn1_scratch_floats(int H, int hd, int n_pos);
+
+int launch_embed(const Q4R &tok, const int32_t *ids, int M, float scale, float *x, hipStream_t s);
+int launch_rmsnorm_f16(const float *x, const float *g, float eps, int M, int d, __half *out,
+                       hipStream_t s);
+// As launch_rmsnorm_f16, also writing lo = fp16(y - fp16(y)).
+int launch_rmsnorm_split(const float *x, const float *g, float eps, int M, int d, __half *hi, __half *lo,
+                         hipStream_t s);
+int launch_rmsnorm_f32(const float *x, const float *g, float eps, int M, int d, float *out,
+                       hipStream_t s);
+int launch_dequant(const Q4R &w, float *out, hipStream_t s);
+int launch_copy_f32(const float *src, float *dst, int n, hipStream_t s);
+int launch_fill_u32(uint32_t *p, uint32_t v, size_t n, hipStream_t s);
+
+}  // namespace ppx

@@ -1,0 +1,164 @@
+"""Kernel-level parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Each kernel entry point is run at the configs' real shapes (ragged M included)
+and compared element by element with the oracle's fp64 result on the same
+seeded inputs, to bounds derived from the kernel's arithmetic:
+  * dequantisation: bit-exact;
+  * MFMA GEMM: fp16 weights d*(q-8) rounded once (<= 2^-11 relative), exact
+    fp16 x fp16 products, fp32 accumulation over K terms:
+    |C - C64| <= (2^-11 + K 2^-24) sum_k |a_k w_k|  -> tested with 1e-3 sum|a w|;
+  * GEMV: exact fp32 weights, fp32 accumulation: <= K 2^-24 sum|w x|;
+  * prefill attention: probabilities rounded to fp16 before P.V and the
+    output rounded to fp16: |o - o64| <= 2e-3 max|V| + 1e-3 |o64|;
+  * single-row attention: fp32 throughout: 1e-5 max|V|.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_common import container, fused_reference, oracle_model
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ppx():
+    import prompt_prefill_cross_amd as p
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    p.lib()
+    return p
+
+
+_models = {}
+
+
+def engine_model(ppx, name):
+    if name not in _models:
+        _models.clear()
+        torch.cuda.synchronize()
+        _models[name] = ppx.Model(container(name))
+    return _models[name]
+
+
+TENSORS = {
+    "tiny": ["tok_embd", "blk.0.wq", "blk.1.wk", "blk.2.wq", "blk.1.wo", "blk.3.ffn_gate", "blk.0.ffn_down"],
+    "tinyllama": ["output", "blk.0.wq", "blk.7.wk", "blk.21.ffn_gate", "blk.5.ffn_down", "blk.3.wo"],
+    "e2b": ["blk.0.wq", "blk.14.wk", "blk.15.wq", "blk.14.ffn_gate", "blk.20.ffn_down", "blk.1.ple_gate",
+            "blk.1.ple_up", "blk.16.wo"],
+}
+
+
+@pytest.mark.parametrize("cfg", ["tiny", "tinyllama", "e2b"])
+def test_dequant_bit_exact(ppx, cfg):
+    mm = engine_model(ppx, cfg)
+    om = oracle_model(cfg)
+    for name in TENSORS[cfg]:
+        got = mm.op_dequant(name).cpu().numpy().astype(np.float64)
+        ref = fused_reference(om, name)
+        assert got.shape == ref.shape, name
+        assert np.array_equal(got, ref), name
+
+
+def test_dequant_token_table_e2b(ppx):
+    mm = engine_model(ppx, "e2b")
+    om = oracle_model("e2b")
+    got = mm.op_dequant("tok_embd")
+    rows = np.random.default_rng(11).integers(0, om.n_vocab, 4096)
+    g = got[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    assert np.array_equal(g, om.q4("tok_embd", rows=rows))
+
+
+@pytest.mark.parametrize("cfg,M", [("tiny", 64), ("tiny", 17), ("tinyllama", 512), ("tinyllama", 200),
+                                   ("e2b", 512), ("e2b", 333)])
+def test_gemm_vs_oracle(ppx, cfg, M):
+    mm = engine_model(ppx, cfg)
+    om = oracle_model(cfg)
+    rng = np.random.default_rng(M)
+    for name in TENSORS[cfg]:
+        if name in ("tok_embd", "output") or name.endswith(".wk"):
+            continue
+        W = fused_reference(om, name)
+        K = W.shape[1]
+        a = rng.standard_normal((M, K)).astype(np.float16)
+        c = mm.op_gemm(name, torch.from_numpy(a).cuda()).cpu().numpy().astype(np.float64)
+        a64 = a.astype(np.float64)
+        ref = a64 @ W.T
+        bound = 1e-3 * (np.abs(a64) @ np.abs(W).T) + 1e-6
+        err = np.abs(c - ref)
+        assert np.all(err <= bound), (name, float((err / bound).max()))
+
+
+@pytest.mark.parametrize("cfg,M", [("tiny", 64), ("tiny", 5), ("tinyllama", 512), ("e2b", 512), ("e2b", 77)])
+def test_gemm_exact_vs_oracle(ppx, cfg, M):
+    """K|V projection path: exact weights, split fp16 activations; only fp32
+    accumulation rounds (32-term block partials, then K/32 scaled adds):
+    |C - C64| <= 2 K 2^-24 sum|a w|."""
+    mm = engine_model(ppx, cfg)
+    om = oracle_model(cfg)
+    rng = np.random.default_rng(M + 1)
+    for name in TENSORS[cfg]:
+        if not name.endswith(".wk"):
+            continue
+        W = fused_reference(om, name)
+        K = W.shape[1]
+        a = rng.standard_normal((M, K)).astype(np.float32)
+        hi = a.astype(np.float16)
+        lo = (a - hi.astype(np.float32)).astype(np.float16)
+        c = mm.op_gemm_exact(name, torch.from_numpy(hi).cuda(), torch.from_numpy(lo).cuda())
+        c = c.cpu().numpy().astype(np.float64)
+        a64 = hi.astype(np.float64) + lo.astype(np.float64)
+        ref = a64 @ W.T
+        bound = (2 * K * 2.0 ** -24) * (np.abs(a64) @ np.abs(W).T) + 1e-7
+        err = np.abs(c - ref)
+        assert np.all(err <= bound), (name, float((err / bound).max()))
+
+
+@pytest.mark.parametrize("cfg", ["tiny", "tinyllama", "e2b"])
+def test_gemv_vs_oracle(ppx, cfg):
+    mm = engine_model(ppx, cfg)
+    om = oracle_model(cfg)
+    rng = np.random.default_rng(5)
+    for name in TENSORS[cfg]:
+        W = fused_reference(om, name) if name not in ("tok_embd", "output") else om.q4(name)
+        K = W.shape[1]
+        x = rng.standard_normal(K).astype(np.float32)
+        y = mm.op_gemv(name, torch.from_numpy(x).cuda()).cpu().numpy().astype(np.float64)
+        ref = W @ x.astype(np.float64)
+        bound = (K * 2.0 ** -24 + 1e-7) * (np.abs(W) @ np.abs(x.astype(np.float64))) + 1e-7
+        assert np.all(np.abs(y - ref) <= bound), name
+
+
+@pytest.mark.parametrize("cfg,M,pos0", [("tiny", 64, 0), ("tiny", 37, 21), ("tinyllama", 512, 0),
+                                        ("tinyllama", 100, 412), ("e2b", 512, 0), ("e2b", 200, 700)])
+def test_attention_prefill_vs_oracle(ppx, cfg, M, pos0):
+    mm = engine_model(ppx, cfg)
+    I = mm.info
+    H, KVH, hd = I["n_head"], I["n_kv_head"], I["head_dim"]
+    rng = np.random.default_rng(M + pos0)
+    P = pos0 + M
+    # magnitudes like the model's: q, k ~ N(0, 6^2), v ~ N(0, 6^2)
+    q = (6 * rng.standard_normal((M, H, hd))).astype(np.float16)
+    K = (6 * rng.standard_normal((P, KVH, hd))).astype(np.float16)
+    V = (6 * rng.standard_normal((P, KVH, hd))).astype(np.float16)
+    o = mm.op_attention(torch.from_numpy(q).cuda(), torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda(), pos0)
+    o = o.cpu().numpy().astype(np.float64)
+    ref = oracle.attention(q.astype(np.float64), K, V, pos0 + np.arange(M))
+    bound = 2e-3 * np.abs(V.astype(np.float64)).max() + 1e-3 * np.abs(ref)
+    assert np.all(np.abs(o - ref) <= bound), float(np.abs(o - ref).max())
+
+
+@pytest.mark.parametrize("cfg,pos", [("tiny", 0), ("tiny", 63), ("tinyllama", 511), ("e2b", 2047), ("e2b", 100)])
+def test_attention_1row_vs_oracle(ppx, cfg, pos):
+    mm = engine_model(ppx, cfg)
+    I = mm.info
+    H, KVH, hd = I["n_head"], I["n_kv_head"], I["head_dim"]
+    rng = np.random.default_rng(pos)
+    q = (6 * rng.standard_normal((H, hd))).astype(np.float32)
+    K = (6 * rng.standard_normal((pos + 1, KVH, hd))).astype(np.float16)
+    V = (6 * rng.standard_normal((pos + 1, KVH, hd))).astype(np.float16)
+    o = mm.op_attention_1row(torch.from_numpy(q).cuda(), torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda(),
+                             pos).cpu().numpy().astype(np.float64)
+    ref = oracle.attention(q.astype(np.float64)[None], K, V, np.array([pos]))[0]
+    assert np.all(np.abs(o - ref) <= 1e-5 * np.abs(V.astype(np.float64)).max() + 1e-5 * np.abs(ref))
