@@ -18,6 +18,9 @@ ARCH = "gfx950"
 
 CFLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # MFMA accumulators in VGPRs: avoids per-iteration AGPR<->VGPR copies of
+          # the accumulator tiles in the GEMM and attention loops
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-I", os.path.join(HERE, "..", "include")]
 
 

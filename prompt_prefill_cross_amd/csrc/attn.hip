@@ -146,25 +146,24 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnArgs a) {
         for (int r = 0; r < 4; ++r) o[d + r] = __float2half(oacc[i][r] * inv);
     }
 }
-
 // ------------------------------------------------------------------ single query
-// One query row (all heads) over cache positions 0..pos.  Grid: (chunks, KVH);
-// a workgroup scores CH keys against the G heads of its KV head and writes a
-// partial (max, sum, unnormalised output) per head; the last workgroup of a KV
-// head (integer counter) merges the chunks in chunk order.
+// One query row (all heads, fp32) over cache positions 0..pos, in two launches.
+// k_attn_1row: grid (chunks of CH keys, KVH); a workgroup stages its keys and
+// values in LDS with 16-byte loads, scores them against the G heads of its KV
+// head (one wave per head group of 64 keys), and writes per head the chunk's
+// max, exp-sum and unnormalised output.  k_attn_merge: one workgroup per head
+// combines the chunks in chunk order.
 constexpr int CH = 64;
 
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn_1row(Attn1Args a) {
-    constexpr int KLD = HD + 2;  // padded K rows (halves)
+    constexpr int KLD = HD + 2;  // padded K rows (halves): row r starts at bank r
     __shared__ _Float16 kl[CH * KLD];
     __shared__ _Float16 vl[CH * HD];
     __shared__ float ql[8 * HD];
-    __shared__ float sc[8 * CH];
-    __shared__ float mx[8], sm[8];
-    __shared__ int last;
+    __shared__ float pl[8 * CH];
 
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int G = a.H / a.KVH;  // <= 8
     const int kvh = blockIdx.y, chunk = blockIdx.x, nchunks = gridDim.x;
     const int k0 = chunk * CH;
@@ -181,72 +180,86 @@ __global__ __launch_bounds__(256) void k_attn_1row(Attn1Args a) {
             vv = *reinterpret_cast<const h8 *>(a.v + off);
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) kl[key * KLD + d8 * 8 + e] = kv[e];
+        for (int e = 0; e < 8; e += 2) *reinterpret_cast<h2 *>(kl + key * KLD + d8 * 8 + e) = h2{kv[e], kv[e + 1]};
         *reinterpret_cast<h8 *>(vl + key * HD + d8 * 8) = vv;
     }
     __syncthreads();
-    for (int u = tid; u < G * CH; u += 256) {
-        const int g = u / CH, j = u % CH;
+
+    // scores: wave w takes heads w, w+4; lane = key
+    for (int g = wave; g < G; g += 4) {
         float s = -INFINITY;
-        if (j < nk) {
-            float acc = 0.f;
-            const _Float16 *kr = kl + j * KLD;
+        if (lane < nk) {
+            const _Float16 *kr = kl + lane * KLD;
             const float *qr = ql + g * HD;
+            float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll 8
             for (int d = 0; d < HD; d += 2) {
                 const h2 kk = *reinterpret_cast<const h2 *>(kr + d);
-                acc += qr[d] * (float)kk[0] + qr[d + 1] * (float)kk[1];
+                acc0 += qr[d] * (float)kk[0];
+                acc1 += qr[d + 1] * (float)kk[1];
             }
-            s = acc * scale;
+            s = (acc0 + acc1) * scale;
         }
-        sc[u] = s;
+        const float m = wave_max(s);
+        const float p = lane < nk ? expf(s - m) : 0.f;
+        const float l = wave_sum(p);
+        pl[g * CH + lane] = p;
+        if (lane == 0) {
+            float *st = a.partial + ((size_t)(kvh * G + g) * nchunks + chunk) * 2;
+            st[0] = m;
+            st[1] = l;
+        }
     }
     __syncthreads();
-    if (tid < G) {
-        float m = -INFINITY;
-        for (int j = 0; j < nk; ++j) m = fmaxf(m, sc[tid * CH + j]);
-        float l = 0.f;
+    // unnormalised P.V: thread d (HD <= 256 threads), every head of the group
+    float *po = a.partial + (size_t)a.H * nchunks * 2;
+    for (int d = tid; d < HD; d += 256) {
+        float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int j = 0; j < nk; ++j) {
-            const float p = expf(sc[tid * CH + j] - m);
-            sc[tid * CH + j] = p;
-            l += p;
+            const float v = (float)vl[j * HD + d];
+#pragma unroll
+            for (int g = 0; g < 8; ++g)
+                if (g < G) o[g] += pl[g * CH + j] * v;
         }
-        mx[tid] = m;
-        sm[tid] = l;
+#pragma unroll
+        for (int g = 0; g < 8; ++g)
+            if (g < G) po[((size_t)(kvh * G + g) * nchunks + chunk) * HD + d] = o[g];
+    }
+}
+
+// o[h][d] = sum_c e^(m_c - M) o_c[d] / sum_c e^(m_c - M) l_c, chunks in order.
+__global__ __launch_bounds__(256) void k_attn_merge(Attn1Args a, int nchunks) {
+    __shared__ float wl[1024];
+    __shared__ float red[4];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const int hd = a.hd;
+    const float *st = a.partial + (size_t)h * nchunks * 2;
+    const float *po = a.partial + (size_t)a.H * nchunks * 2 + (size_t)h * nchunks * hd;
+    float M = -INFINITY;
+    for (int c = tid; c < nchunks; c += 256) M = fmaxf(M, st[2 * c]);
+    M = wave_max(M);
+    if ((tid & 63) == 0) red[tid >> 6] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float L = 0.f;
+    for (int c = tid; c < nchunks; c += 256) {
+        const float w = expf(st[2 * c] - M);
+        if (c < 1024) wl[c] = w;
+        L += w * st[2 * c + 1];
     }
     __syncthreads();
-    const size_t stride = (size_t)HD + 2;  // per head: o[HD], m, l
-    float *part = a.partial + ((size_t)kvh * nchunks + chunk) * G * stride;
-    for (int u = tid; u < G * HD; u += 256) {
-        const int g = u / HD, d = u % HD;
-        float acc = 0.f;
-        for (int j = 0; j < nk; ++j) acc += sc[g * CH + j] * (float)vl[j * HD + d];
-        part[g * stride + d] = acc;
-    }
-    if (tid < G) {
-        part[tid * stride + HD] = mx[tid];
-        part[tid * stride + HD + 1] = sm[tid];
-    }
-    __threadfence();
+    L = wave_sum(L);
+    if ((tid & 63) == 0) red[tid >> 6] = L;
     __syncthreads();
-    if (tid == 0) last = (atomicAdd(a.counter + kvh, 1u) == (uint32_t)(nchunks - 1));
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
-    const float *pb = a.partial + (size_t)kvh * nchunks * G * stride;
-    for (int u = tid; u < G * HD; u += 256) {
-        const int g = u / HD, d = u % HD;
-        float M = -INFINITY;
-        for (int c = 0; c < nchunks; ++c) M = fmaxf(M, __builtin_nontemporal_load(pb + ((size_t)c * G + g) * stride + HD));
-        float L = 0.f, O = 0.f;
+    L = red[0] + red[1] + red[2] + red[3];
+    for (int d = tid; d < hd; d += 256) {
+        float o = 0.f;
         for (int c = 0; c < nchunks; ++c) {
-            const float *pc = pb + ((size_t)c * G + g) * stride;
-            const float w = expf(__builtin_nontemporal_load(pc + HD) - M);
-            L += w * __builtin_nontemporal_load(pc + HD + 1);
-            O += w * __builtin_nontemporal_load(pc + d);
+            const float w = c < 1024 ? wl[c] : expf(st[2 * c] - M);
+            o += w * po[(size_t)c * hd + d];
         }
-        a.o[(size_t)(kvh * G + g) * HD + d] = O / L;
+        a.o[(size_t)h * hd + d] = o / L;
     }
-    if (tid == 0) a.counter[kvh] = 0u;
 }
 
 int ok() { return hipGetLastError() == hipSuccess ? PPX_OK : PPX_E_HIP; }
@@ -274,7 +287,7 @@ size_t attn1_scratch_floats(int H, int hd, int n_pos) {
 
 int launch_attn_1row(const Attn1Args &a, hipStream_t s) {
     const int G = a.H / a.KVH;
-    if (a.H % a.KVH || G > 8) return PPX_E_UNSUPPORTED;
+    if (a.H % a.KVH || G > 8 || a.pos < 0 || !a.partial) return PPX_E_UNSUPPORTED;
     const int chunks = (a.pos + 1 + CH - 1) / CH;
     dim3 grid(chunks, a.KVH);
     switch (a.hd) {
@@ -283,6 +296,8 @@ int launch_attn_1row(const Attn1Args &a, hipStream_t s) {
     case 256: hipLaunchKernelGGL(k_attn_1row<256>, grid, dim3(256), 0, s, a); break;
     default: return PPX_E_UNSUPPORTED;
     }
+    if (hipGetLastError() != hipSuccess) return PPX_E_HIP;
+    hipLaunchKernelGGL(k_attn_merge, dim3(a.H), dim3(256), 0, s, a, chunks);
     return ok();
 }
 

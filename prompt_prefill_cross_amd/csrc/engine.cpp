@@ -29,9 +29,8 @@ inline size_t al(size_t x) { return (x + 255) / 256 * 256; }
 struct WsLayout {
     size_t tok, x, a16, a16lo, q16, o16, h16, p16;
     size_t xr, ar, qr, orow, hr, pr;
-    size_t gv_part, gv_cnt, at_part, at_cnt;
+    size_t at_part;
     size_t total;
-    size_t gv_cnt_n, at_cnt_n;
 };
 
 WsLayout ws_layout(const ppx_model *m, int ub, int n_ctx) {
@@ -58,26 +57,7 @@ WsLayout ws_layout(const ppx_model *m, int ub, int n_ctx) {
     w.orow = take(4ull * qd);
     w.hr = take(4ull * F);
     w.pr = take(4ull * std::max(E, 1));
-    // GEMV split-K scratch: the largest over the matrices the single-row path uses
-    size_t gvf = 0, gvc = 0;
-    auto gv = [&](int N, int K) {
-        if (N <= 0 || K <= 0) return;
-        gvf = std::max(gvf, gemv_scratch_floats(N, K));
-        gvc = std::max(gvc, (size_t)N / 32);
-    };
-    gv(qd, d);
-    gv(d, qd);
-    gv(2 * F, d);
-    gv(d, F);
-    gv(E, d);
-    gv(d, E);
-    gv(I.n_vocab, d);
-    w.gv_part = take(4 * gvf);
-    w.gv_cnt = take(4 * gvc);
-    w.gv_cnt_n = gvc;
     w.at_part = take(4 * attn1_scratch_floats(I.n_head, I.head_dim, std::max(n_ctx, 1)));
-    w.at_cnt = take(4ull * I.n_kv_head);
-    w.at_cnt_n = I.n_kv_head;
     w.total = o;
     return w;
 }
@@ -274,8 +254,7 @@ GemvArgs gemv_base(Ctx &c, const float *x, const Q4R &W, int epi, float *out) {
     a.W = W;
     a.epi = epi;
     a.out = out;
-    a.partial = c.at<float>(c.L.gv_part);
-    a.counter = c.at<uint32_t>(c.L.gv_cnt);
+    (void)c;
     return a;
 }
 
@@ -306,7 +285,6 @@ int layer_row(Ctx &c, int il, int pos, int tok) {
     at.hd = hd;
     at.pos = pos;
     at.partial = c.at<float>(c.L.at_part);
-    at.counter = c.at<uint32_t>(c.L.at_cnt);
     PPX_LAUNCH(c, PPX_PHASE_ROW, launch_attn_1row(at, c.s));
     PPX_LAUNCH(c, PPX_PHASE_ROW, launch_gemv(gemv_base(c, orow, w.wo, GV_ADD, xr), c.s));
     PPX_LAUNCH(c, PPX_PHASE_ROW, launch_rmsnorm_f32(xr, w.ffn_norm, m->eps, 1, d, ar, c.s));
@@ -376,8 +354,6 @@ int prefill(ppx_model *m, ppx_kv *kv, const int32_t *tokens, int n, const ppx_pr
     int32_t *tok_dev = c.at<int32_t>(c.L.tok);
     if (hipMemcpyAsync(tok_dev, tokens, sizeof(int32_t) * n, hipMemcpyHostToDevice, s) != hipSuccess)
         return PPX_E_HIP;
-    PPX_TRY(launch_fill_u32(c.at<uint32_t>(c.L.gv_cnt), 0u, c.L.gv_cnt_n, s));
-    PPX_TRY(launch_fill_u32(c.at<uint32_t>(c.L.at_cnt), 0u, c.L.at_cnt_n, s));
     if (log_enabled())
         std::fprintf(stderr, "[ppx] prefill %d tokens at position %d, ubatch %d, prune %s\n", n, p0, ub,
                      prune ? "on" : "off");
@@ -654,26 +630,15 @@ int ppx_op_gemm_exact(const ppx_model *m, const char *tensor, const void *a_hi, 
 }
 
 int ppx_op_gemv(const ppx_model *m, const char *tensor, const float *x_dev, float *y_dev, void *hip_stream) {
-    // split-K scratch: allocated per call (test entry point only)
     int kind;
     const Q4R *w = find_q4(m, tensor, &kind);
     if (!w || !x_dev || !y_dev) return PPX_E_INVAL;
-    const size_t nf = gemv_scratch_floats(w->N, w->K), nc = (size_t)w->N / 32;
-    void *scratch = nullptr;
-    if (hipMalloc(&scratch, 4 * (nf + nc) + 256) != hipSuccess) return PPX_E_NOMEM;
     GemvArgs a;
     a.x = x_dev;
     a.W = *w;
     a.epi = GV_F32;
     a.out = y_dev;
-    a.partial = static_cast<float *>(scratch);
-    a.counter = reinterpret_cast<uint32_t *>(static_cast<float *>(scratch) + nf);
-    hipStream_t s = (hipStream_t)hip_stream;
-    int st = launch_fill_u32(a.counter, 0u, nc, s);
-    if (!st) st = launch_gemv(a, s);
-    if (hipStreamSynchronize(s) != hipSuccess && !st) st = PPX_E_HIP;
-    (void)hipFree(scratch);
-    return st;
+    return launch_gemv(a, (hipStream_t)hip_stream);
 }
 
 int ppx_op_attention(const ppx_model *m, const void *q_dev, const void *k_dev, const void *v_dev, int M, int pos0,
@@ -699,7 +664,6 @@ int ppx_op_attention_1row(const ppx_model *m, const float *q_dev, const void *k_
     if (ws_bytes < L.total) return PPX_E_NOMEM;
     uint8_t *ws = static_cast<uint8_t *>(ws_dev);
     hipStream_t s = (hipStream_t)hip_stream;
-    PPX_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(ws + L.at_cnt), 0u, L.at_cnt_n, s));
     Attn1Args a;
     a.q = q_dev;
     a.k = static_cast<const __half *>(k_dev);
@@ -710,7 +674,6 @@ int ppx_op_attention_1row(const ppx_model *m, const float *q_dev, const void *k_
     a.hd = m->info.head_dim;
     a.pos = pos;
     a.partial = reinterpret_cast<float *>(ws + L.at_part);
-    a.counter = reinterpret_cast<uint32_t *>(ws + L.at_cnt);
     return launch_attn_1row(a, s);
 }
 

@@ -2,10 +2,13 @@
 //
 //   C[M][N] = A[M][K] (fp16 activations) x W[N][K]^T (Q4_0), fp32 accumulate.
 //
-// A workgroup of four waves computes a BM x BN tile; the waves form a 2 x 2
-// grid of (BM/2) x (BN/2) wave tiles.  K advances 64 (two Q4_0 blocks) per
-// stage through double-buffered LDS.  A is staged as fp16 in the MFMA A
-// fragment order; W is read as repacked codes + fp16 block scales, decoded in
+// A workgroup of WGM x WGN waves computes a BM x BN tile, each wave a
+// (BM/WGM) x (BN/WGN) block of 16x16 MFMA tiles.  K advances 64 (two Q4_0
+// blocks) per stage through two LDS buffers; global loads run two stages ahead
+// of the MFMAs (two register sets, the loop unrolled by two), so a stage's
+// memory latency overlaps two stages of matrix work.  A is staged as fp16 in
+// the MFMA A fragment order -- one wave store fills one 1 KB fragment, lane by
+// lane -- and W is read as repacked codes + fp16 block scales, decoded in
 // registers and written to LDS in B fragment order, so a tile's weights are
 // decoded once per workgroup.  Epilogues work on the accumulator registers
 // directly; weights whose outputs are combined in pairs (RoPE halves,
@@ -27,161 +30,191 @@ namespace {
 
 constexpr int KSTEP = 64;
 
-template <int BM, int BN, bool EXACT>
-struct GemmShape {
-    static constexpr int WM = BM / 2, WN = BN / 2;
+template <int BM_, int BN_, int WGM_, int WGN_, bool EXACT_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
+    static constexpr bool EXACT = EXACT_;
+    static constexpr int NT = 64 * WGM * WGN;            // threads
+    static constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile
     static constexpr int TM = WM / 16, TN = WN / 16;
-    static constexpr int A_UNITS = 2 * (BM / 16) * 64;  // 16-byte units per stage (per A part)
+    static constexpr int A_UNITS = 2 * (BM / 16) * 64;   // 16-byte units per stage, per A part
     static constexpr int B_UNITS = 2 * (BN / 16) * 64;
     static constexpr int NA = EXACT ? 2 : 1;             // A parts staged
     static constexpr int S_FLOATS = EXACT ? 2 * BN : 0;  // block scales per stage
     static constexpr int STAGE_UNITS = NA * A_UNITS + B_UNITS + S_FLOATS / 4;
-    static constexpr int A_LOADS = BM * 8 / 256;         // A units per thread per stage
-    static constexpr int B_LOADS = BN * 4 / 256;         // B lane slots per thread per stage
-    static_assert(BM % 32 == 0 && BN % 64 == 0, "tile");
-    static_assert(A_LOADS >= 1 && B_LOADS >= 1, "tile too small for 256 threads");
+    static constexpr int A_LOADS = A_UNITS / NT;         // per thread, per part
+    static constexpr int B_SLOTS = (BN / 16) * 64 / NT;  // lane slots per thread
+    static_assert(TM >= 1 && TN >= 2 && TN % 2 == 0, "wave tile");
+    static_assert(A_UNITS % NT == 0 && A_LOADS >= 1, "A staging");
+    static_assert((BN / 16) * 64 % NT == 0 && B_SLOTS >= 1, "B staging");
 };
 
-// (code - 8) exactly, as fp16, for the eight codes of a repacked word.
-__device__ __forceinline__ h8 q4_word_to_h8_codes(uint32_t w) {
-    h8 r;
-    const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint32_t t = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
-        h2 v = __builtin_bit_cast(h2, t) - bias;
-        r[2 * i] = v[0];
-        r[2 * i + 1] = v[1];
-    }
-    return r;
-}
-
-template <int BM, int BN, bool EXACT>
+// One stage of operands held in registers between its global load and its LDS store.
+template <class C>
 struct Stage {
-    using S = GemmShape<BM, BN, EXACT>;
-    h8 ar[S::NA][S::A_LOADS];
-    uint2 br[S::B_LOADS];
-    uint32_t sr[S::B_LOADS];
+    h8 ar[C::NA][C::A_LOADS];
+    uint2 br[C::B_SLOTS];
+    uint32_t sr[C::B_SLOTS];
 
+    // Loads are branch-free (rows past M are clamped, then zeroed by a select),
+    // so the compiler can count outstanding loads exactly and keep the next
+    // stage's loads in flight across this stage's store.
     __device__ __forceinline__ void load(const GemmArgs &a, int m0, int n0, int kc) {
         const int tid = threadIdx.x;
 #pragma unroll
-        for (int i = 0; i < S::A_LOADS; ++i) {
-            const int u = tid + i * 256;
-            const int row = u >> 3, k8 = u & 7;
-            const int gr = m0 + row;
+        for (int i = 0; i < C::A_LOADS; ++i) {
+            // unit u = [kb][16-row subtile][lane]; lane l holds row 16*sub + l%16, k = 32*kb + 8*(l/16)
+            const int u = tid + i * C::NT;
+            const int kb = u / ((C::BM / 16) * 64), rem = u % ((C::BM / 16) * 64);
+            const int row = m0 + (rem >> 6) * 16 + (rem & 15);
+            const unsigned off = (unsigned)(min(row, a.M - 1) * a.lda + kc * KSTEP + kb * 32 + ((rem >> 4) & 3) * 8);
 #pragma unroll
-            for (int p = 0; p < S::NA; ++p) {
+            for (int p = 0; p < C::NA; ++p) {
                 const __half *src = p ? a.A2 : a.A;
-                if (gr < a.M)
-                    ar[p][i] = *reinterpret_cast<const h8 *>(src + (size_t)gr * a.lda + kc * KSTEP + k8 * 8);
-                else
-                    ar[p][i] = h8{0, 0, 0, 0, 0, 0, 0, 0};
+                ar[p][i] = *reinterpret_cast<const h8 *>(src + off);
             }
         }
-        const int kchunks = a.W.K >> 6;
+        const unsigned kchunks = (unsigned)a.W.K >> 6;
 #pragma unroll
-        for (int i = 0; i < S::B_LOADS; ++i) {
-            const int sl = tid + i * 256;
-            const int grp = sl >> 6, ln = sl & 63;
-            const size_t base = (size_t)((n0 >> 4) + grp) * kchunks + kc;
+        for (int i = 0; i < C::B_SLOTS; ++i) {
+            const unsigned sl = tid + i * C::NT;
+            const unsigned grp = sl >> 6, ln = sl & 63;
+            const unsigned base = (((unsigned)n0 >> 4) + grp) * kchunks + kc;
             br[i] = *reinterpret_cast<const uint2 *>(a.W.nib + (base * 64 + ln) * 2);
             sr[i] = *reinterpret_cast<const uint32_t *>(a.W.scl + (base * 16 + (ln & 15)) * 2);
         }
     }
 
-    __device__ __forceinline__ void store(h8 *lds) const {
+    __device__ __forceinline__ void store(h8 *lds, int m0, int M) const {
         const int tid = threadIdx.x;
+        if (m0 + C::BM <= M) {  // uniform: the whole tile is inside the matrix
 #pragma unroll
-        for (int i = 0; i < S::A_LOADS; ++i) {
-            const int u = tid + i * 256;
-            const int row = u >> 3, k8 = u & 7;
-            const int kb = k8 >> 2, g = k8 & 3;
+            for (int i = 0; i < C::A_LOADS; ++i)
 #pragma unroll
-            for (int p = 0; p < S::NA; ++p)
-                lds[p * S::A_UNITS + kb * (BM / 16) * 64 + (row >> 4) * 64 + g * 16 + (row & 15)] = ar[p][i];
+                for (int p = 0; p < C::NA; ++p) lds[p * C::A_UNITS + tid + i * C::NT] = ar[p][i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < C::A_LOADS; ++i) {
+                const int rem = (tid + i * C::NT) % ((C::BM / 16) * 64);
+                const bool valid = m0 + (rem >> 6) * 16 + (rem & 15) < M;  // rows past M were clamped
+#pragma unroll
+                for (int p = 0; p < C::NA; ++p)
+                    lds[p * C::A_UNITS + tid + i * C::NT] = valid ? ar[p][i] : h8{0, 0, 0, 0, 0, 0, 0, 0};
+            }
         }
-        h8 *lb = lds + S::NA * S::A_UNITS;
-        float *ls = reinterpret_cast<float *>(lb + S::B_UNITS);
+        h8 *lb = lds + C::NA * C::A_UNITS;
+        float *ls = reinterpret_cast<float *>(lb + C::B_UNITS);
 #pragma unroll
-        for (int i = 0; i < S::B_LOADS; ++i) {
-            const int sl = tid + i * 256;
+        for (int i = 0; i < C::B_SLOTS; ++i) {
+            const int sl = tid + i * C::NT;
             const int grp = sl >> 6, ln = sl & 63;
             const h2 d2 = __builtin_bit_cast(h2, sr[i]);
-            if constexpr (EXACT) {
-                lb[0 * (BN / 16) * 64 + grp * 64 + ln] = q4_word_to_h8_codes(br[i].x);
-                lb[1 * (BN / 16) * 64 + grp * 64 + ln] = q4_word_to_h8_codes(br[i].y);
+            if constexpr (C::EXACT) {
+                lb[0 * (C::BN / 16) * 64 + grp * 64 + ln] = q4_word_codes(br[i].x);
+                lb[1 * (C::BN / 16) * 64 + grp * 64 + ln] = q4_word_codes(br[i].y);
                 if (ln < 16) {
                     ls[grp * 16 + ln] = (float)d2[0];
-                    ls[BN + grp * 16 + ln] = (float)d2[1];
+                    ls[C::BN + grp * 16 + ln] = (float)d2[1];
                 }
             } else {
-                lb[0 * (BN / 16) * 64 + grp * 64 + ln] = q4_word_to_h8(br[i].x, d2[0]);
-                lb[1 * (BN / 16) * 64 + grp * 64 + ln] = q4_word_to_h8(br[i].y, d2[1]);
+                lb[0 * (C::BN / 16) * 64 + grp * 64 + ln] = q4_word_to_h8(br[i].x, d2[0]);
+                lb[1 * (C::BN / 16) * 64 + grp * 64 + ln] = q4_word_to_h8(br[i].y, d2[1]);
             }
         }
     }
 };
 
-template <int BM, int BN, bool EXACT>
-__global__ __launch_bounds__(256) void k_q4gemm(GemmArgs a) {
-    using S = GemmShape<BM, BN, EXACT>;
-    __shared__ h8 lds[2][S::STAGE_UNITS];
+// The fragments of one stage, read from LDS before the next stage is stored,
+// so that the MFMAs of this stage overlap the decode and LDS stores of the next.
+template <class C>
+struct Frags {
+    h8 af[2][C::TM], bf[2][C::TN];
+    h8 af2[2][C::EXACT ? C::TM : 1];
+    float dsc[2][C::EXACT ? C::TN : 1];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
-    const int wm = (wave >> 1) * S::WM, wn = (wave & 1) * S::WN;
-    const int lc = lane & 15, lr = (lane >> 4) * 4;
-
-    f4 acc[S::TM][S::TN];
-#pragma unroll
-    for (int i = 0; i < S::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < S::TN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
-
-    Stage<BM, BN, EXACT> st;
-    const int nk = a.W.K / KSTEP;
-    st.load(a, m0, n0, 0);
-    st.store(lds[0]);
-    __syncthreads();
-
-    for (int kc = 0; kc < nk; ++kc) {
-        const int cur = kc & 1;
-        if (kc + 1 < nk) st.load(a, m0, n0, kc + 1);
-        const h8 *la = lds[cur];
-        const h8 *lb = lds[cur] + S::NA * S::A_UNITS;
-        const float *ls = reinterpret_cast<const float *>(lb + S::B_UNITS);
+    __device__ __forceinline__ void read(const h8 *lds, int wm, int wn, int lane) {
+        const h8 *la = lds;
+        const h8 *lb = lds + C::NA * C::A_UNITS;
+        const float *ls = reinterpret_cast<const float *>(lb + C::B_UNITS);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            h8 af[S::TM], bf[S::TN];
 #pragma unroll
-            for (int i = 0; i < S::TM; ++i) af[i] = la[kb * (BM / 16) * 64 + ((wm >> 4) + i) * 64 + lane];
+            for (int i = 0; i < C::TM; ++i) af[kb][i] = la[kb * (C::BM / 16) * 64 + ((wm >> 4) + i) * 64 + lane];
 #pragma unroll
-            for (int j = 0; j < S::TN; ++j) bf[j] = lb[kb * (BN / 16) * 64 + ((wn >> 4) + j) * 64 + lane];
-            if constexpr (EXACT) {
-                h8 af2[S::TM];
+            for (int j = 0; j < C::TN; ++j) bf[kb][j] = lb[kb * (C::BN / 16) * 64 + ((wn >> 4) + j) * 64 + lane];
+            if constexpr (C::EXACT) {
 #pragma unroll
-                for (int i = 0; i < S::TM; ++i)
-                    af2[i] = la[S::A_UNITS + kb * (BM / 16) * 64 + ((wm >> 4) + i) * 64 + lane];
+                for (int i = 0; i < C::TM; ++i)
+                    af2[kb][i] = la[C::A_UNITS + kb * (C::BM / 16) * 64 + ((wm >> 4) + i) * 64 + lane];
 #pragma unroll
-                for (int j = 0; j < S::TN; ++j) {
-                    const float dsc = ls[kb * BN + wn + j * 16 + lc];
-#pragma unroll
-                    for (int i = 0; i < S::TM; ++i) {
-                        f4 p = mfma16(af[i], bf[j], f4{0.f, 0.f, 0.f, 0.f});
-                        p = mfma16(af2[i], bf[j], p);
-                        acc[i][j] += dsc * p;
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < S::TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < S::TN; ++j) acc[i][j] = mfma16(af[i], bf[j], acc[i][j]);
+                for (int j = 0; j < C::TN; ++j) dsc[kb][j] = ls[kb * C::BN + wn + j * 16 + (lane & 15)];
             }
         }
-        if (kc + 1 < nk) st.store(lds[cur ^ 1]);
+    }
+
+    __device__ __forceinline__ void mma(f4 (&acc)[C::TM][C::TN]) const {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            if constexpr (C::EXACT) {
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+                    for (int i = 0; i < C::TM; ++i) {
+                        f4 p = mfma16(af[kb][i], bf[kb][j], f4{0.f, 0.f, 0.f, 0.f});
+                        p = mfma16(af2[kb][i], bf[kb][j], p);
+                        acc[i][j] += dsc[kb][j] * p;
+                    }
+            } else {
+#pragma unroll
+                for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma16(af[kb][i], bf[kb][j], acc[i][j]);
+            }
+        }
+    }
+};
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void k_q4gemm(GemmArgs a) {
+    using S = C;
+    __shared__ h8 lds[2][C::STAGE_UNITS];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n0 = blockIdx.x * C::BN, m0 = blockIdx.y * C::BM;
+    const int wm = (wave / C::WGN) * C::WM, wn = (wave % C::WGN) * C::WN;
+    const int lc = lane & 15, lr = (lane >> 4) * 4;
+
+    f4 acc[C::TM][C::TN];
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+
+    // stage s lives in register set (s % 2) between its load and its store
+    Stage<C> r0, r1;
+    const int nk = a.W.K / KSTEP;
+    // nk is even (K % 128 == 0).  Every load, store and MFMA is unconditional:
+    // past the last stage the load index is clamped and the duplicate lands in
+    // a buffer that is not read again; no branch splits the accumulators'
+    // live ranges, so they stay in place across iterations.
+    const int last = nk - 1;
+    r0.load(a, m0, n0, 0);
+    r0.store(lds[0], m0, a.M);
+    r1.load(a, m0, n0, 1);
+    r0.load(a, m0, n0, min(2, last));
+    __syncthreads();
+    Frags<C> f;
+    for (int kc = 0; kc < nk; kc += 2) {
+        f.read(lds[0], wm, wn, lane);  // stage kc
+        r1.store(lds[1], m0, a.M);     // stage kc + 1 (lds[1] was last read before the previous barrier)
+        f.mma(acc);
         __syncthreads();
+        r1.load(a, m0, n0, min(kc + 3, last));
+        f.read(lds[1], wm, wn, lane);  // stage kc + 1
+        r0.store(lds[0], m0, a.M);     // stage kc + 2
+        f.mma(acc);
+        __syncthreads();
+        r0.load(a, m0, n0, min(kc + 4, last));
     }
 
     // ---------------------------------------------------------------- epilogue
@@ -266,28 +299,33 @@ __global__ __launch_bounds__(256) void k_q4gemm(GemmArgs a) {
     }
 }
 
-template <int BM, int BN, bool EXACT>
-int launch_tile(const GemmArgs &a, hipStream_t s) {
-    dim3 grid(a.W.N / BN, (a.M + BM - 1) / BM);
-    hipLaunchKernelGGL((k_q4gemm<BM, BN, EXACT>), grid, dim3(256), 0, s, a);
+template <class C>
+int launch_cfg(const GemmArgs &a, hipStream_t s) {
+    dim3 grid(a.W.N / C::BN, (a.M + C::BM - 1) / C::BM);
+    hipLaunchKernelGGL((k_q4gemm<C>), grid, dim3(C::NT), 0, s, a);
     return hipGetLastError() == hipSuccess ? PPX_OK : PPX_E_HIP;
+}
+
+long tiles(const GemmArgs &a, int bm, int bn) {
+    return a.W.N % bn ? 0 : (long)(a.W.N / bn) * ((a.M + bm - 1) / bm);
 }
 
 }  // namespace
 
 int launch_gemm(const GemmArgs &a, hipStream_t s) {
     if (a.M <= 0) return PPX_OK;
-    if (a.W.N % 64 || a.W.K % 64 || a.lda % 8 || !a.A) return PPX_E_UNSUPPORTED;
-    const long tiles128 = (long)(a.W.N / 128) * ((a.M + 127) / 128);
-    if (a.W.N % 128 == 0 && tiles128 >= 192) return launch_tile<128, 128, false>(a, s);
-    if (a.W.N % 128 == 0 && (long)(a.W.N / 128) * ((a.M + 63) / 64) >= 128) return launch_tile<64, 128, false>(a, s);
-    return launch_tile<64, 64, false>(a, s);
+    if (a.W.N % 64 || a.W.K % 128 || a.lda % 8 || !a.A) return PPX_E_UNSUPPORTED;
+    // measured on the E2B-like shapes at M = 512: wide outputs (gate|up) run best
+    // as 128x256 tiles of eight 64x64 wave tiles; everything narrower as 64x64
+    // tiles, which give the most workgroups
+    if (a.W.N >= 8192 && tiles(a, 128, 256) >= 128) return launch_cfg<Cfg<128, 256, 2, 4, false>>(a, s);
+    return launch_cfg<Cfg<64, 64, 2, 2, false>>(a, s);
 }
 
 int launch_gemm_exact(const GemmArgs &a, hipStream_t s) {
     if (a.M <= 0) return PPX_OK;
-    if (a.W.N % 64 || a.W.K % 64 || a.lda % 8 || !a.A || !a.A2) return PPX_E_UNSUPPORTED;
-    return launch_tile<64, 64, true>(a, s);
+    if (a.W.N % 64 || a.W.K % 128 || a.lda % 8 || !a.A || !a.A2) return PPX_E_UNSUPPORTED;
+    return launch_cfg<Cfg<64, 64, 2, 2, true>>(a, s);
 }
 
 }  // namespace ppx

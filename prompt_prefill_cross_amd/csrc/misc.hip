@@ -68,95 +68,67 @@ __global__ void k_copy_f32(const float *src, float *dst, int n) {
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) dst[i] = src[i];
 }
 
-// ------------------------------------------------------------------ GEMV
-// y[n] = sum_k W[n][k] x[k] for one fp32 row, weights decoded exactly in fp32.
-// Grid: (N/32 column pairs, ksplit).  A workgroup (4 waves) owns one pair of
-// 16-column groups and a contiguous range of 64-wide K chunks; lane l covers
-// column l%16 and the eight k's 8*(l/16)..+7 of each block.  Partial sums of
-// the ksplit workgroups of a pair go to scratch; the last one to arrive (an
-// integer counter) adds them in split order and applies the epilogue, so
-// the result does not depend on arrival order.
-__global__ __launch_bounds__(256) void k_q4gemv(GemvArgs a) {
-    __shared__ float red[4][2][16];
-    __shared__ int last;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int pair = blockIdx.x, split = blockIdx.y;
-    const int kch = a.W.K >> 6;
-    const int per = (kch + a.ksplit - 1) / a.ksplit;
-    const int c0 = split * per, c1 = min(kch, c0 + per);
-    const int col = lane & 15, g = lane >> 4;
+int ok() { return hipGetLastError() == hipSuccess ? PPX_OK : PPX_E_HIP; }
 
-    float acc0 = 0.f, acc1 = 0.f;
-    for (int kc = c0 + wave; kc < c1; kc += 4) {
-        const size_t b0 = (size_t)(2 * pair) * kch + kc;
-        const size_t b1 = (size_t)(2 * pair + 1) * kch + kc;
-        const uint2 w0 = *reinterpret_cast<const uint2 *>(a.W.nib + (b0 * 64 + lane) * 2);
-        const uint2 w1 = *reinterpret_cast<const uint2 *>(a.W.nib + (b1 * 64 + lane) * 2);
-        const h2 d0 = __builtin_bit_cast(h2, *reinterpret_cast<const uint32_t *>(a.W.scl + (b0 * 16 + col) * 2));
-        const h2 d1 = __builtin_bit_cast(h2, *reinterpret_cast<const uint32_t *>(a.W.scl + (b1 * 16 + col) * 2));
+// ------------------------------------------------------------------ GEMV
+// y[n] = sum_k W[n][k] x[k] for one fp32 row (the pruned layers and the head).
+// The row runs through the MFMA as two rows of the A operand: row 0 holds
+// fp16(x) and row 1 holds fp16(x - fp16(x)), so their sum carries x to ~22
+// bits; B holds (code - 8) exactly, and each block's partial is scaled by its
+// fp32 block scale -- only fp32 accumulation rounds.
+// A workgroup owns one pair of 16-row groups (RoPE and gate/up partners sit in
+// such a pair); KW waves per group split K, and their partial sums meet in LDS
+// in wave order, so the result is deterministic and no workgroup waits for
+// another.
+template <int KW>
+__global__ __launch_bounds__(128 * KW) void k_q4gemv(GemvArgs a) {
+    __shared__ float red[2][KW][16];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int half = wave / KW, kw = wave % KW;
+    const int grp = 2 * blockIdx.x + half;
+    const int kch = a.W.K >> 6;
+    const int per = (kch + KW - 1) / KW;
+    const int c0 = kw * per, c1 = min(kch, c0 + per);
+    const int col = lane & 15, g = lane >> 4;
+    const bool arow = col < 2;  // A rows 0 (hi) and 1 (lo) carry x
+
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    const uint2 *nib = reinterpret_cast<const uint2 *>(a.W.nib) + (size_t)grp * kch * 64 + lane;
+    const uint32_t *scl = reinterpret_cast<const uint32_t *>(a.W.scl) + (size_t)grp * kch * 16 + col;
+#pragma unroll 2
+    for (int kc = c0; kc < c1; ++kc) {
+        const uint2 w = nib[(size_t)kc * 64];
+        const h2 d = __builtin_bit_cast(h2, scl[(size_t)kc * 16]);
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const float *xv = a.x + kc * 64 + s * 32 + g * 8;
-            const float4 xa = *reinterpret_cast<const float4 *>(xv);
-            const float4 xb = *reinterpret_cast<const float4 *>(xv + 4);
-            const float xs[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-            const uint32_t u0 = s ? w0.y : w0.x, u1 = s ? w1.y : w1.x;
-            const float dd0 = (float)d0[s], dd1 = (float)d1[s];
-            float p0 = 0.f, p1 = 0.f;
+            h8 af = h8{0, 0, 0, 0, 0, 0, 0, 0};
+            if (arow) {
+                const float4 *xv = reinterpret_cast<const float4 *>(a.x + kc * 64 + s * 32 + g * 8);
+                const float4 x0 = xv[0], x1 = xv[1];
+                const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                p0 += (float)(q4_word_code(u0, e) - 8) * xs[e];
-                p1 += (float)(q4_word_code(u1, e) - 8) * xs[e];
+                for (int e = 0; e < 8; ++e) {
+                    const _Float16 hi = (_Float16)xs[e];
+                    af[e] = col == 0 ? hi : (_Float16)(xs[e] - (float)hi);
+                }
             }
-            acc0 += dd0 * p0;
-            acc1 += dd1 * p1;
+            const h8 bf = q4_word_codes(s ? w.y : w.x);
+            const f4 p = mfma16(af, bf, f4{0.f, 0.f, 0.f, 0.f});
+            acc += (float)d[s] * p;
         }
     }
-    acc0 += __shfl_xor(acc0, 16, 64);
-    acc0 += __shfl_xor(acc0, 32, 64);
-    acc1 += __shfl_xor(acc1, 16, 64);
-    acc1 += __shfl_xor(acc1, 32, 64);
-    if (lane < 16) {
-        red[wave][0][lane] = acc0;
-        red[wave][1][lane] = acc1;
-    }
+    // lanes 0..15 hold rows 0 and 1 (hi and lo parts) of column `col`
+    if (lane < 16) red[half][kw][lane] = acc[0] + acc[1];
     __syncthreads();
-    const int N = a.W.N;
-    const int n0 = pair * 32;
-    if (a.ksplit > 1) {
-        if (threadIdx.x < 32) {
-            const int t = threadIdx.x >> 4, c = threadIdx.x & 15;
-            const float v = red[0][t][c] + red[1][t][c] + red[2][t][c] + red[3][t][c];
-            a.partial[(size_t)split * N + n0 + t * 16 + c] = v;
-        }
-        __threadfence();
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            const uint32_t prev = atomicAdd(a.counter + pair, 1u);
-            last = (prev == (uint32_t)(a.ksplit - 1));
-        }
-        __syncthreads();
-        if (!last) return;
-        __threadfence();
-        if (threadIdx.x < 32) {
-            const int t = threadIdx.x >> 4, c = threadIdx.x & 15;
-            float v = 0.f;
-            for (int sp = 0; sp < a.ksplit; ++sp)
-                v += __builtin_nontemporal_load(a.partial + (size_t)sp * N + n0 + t * 16 + c);
-            red[0][t][c] = v;
-        }
-        if (threadIdx.x == 0) a.counter[pair] = 0u;
-        __syncthreads();
-    } else {
-        if (threadIdx.x < 32) {
-            const int t = threadIdx.x >> 4, c = threadIdx.x & 15;
-            red[0][t][c] = red[0][t][c] + red[1][t][c] + red[2][t][c] + red[3][t][c];
-        }
-        __syncthreads();
-    }
     if (threadIdx.x >= 16) return;
     const int c = threadIdx.x;
-    const float ya = red[0][0][c], yb = red[0][1][c];
+    float ya = 0.f, yb = 0.f;
+#pragma unroll
+    for (int i = 0; i < KW; ++i) {
+        ya += red[0][i][c];
+        yb += red[1][i][c];
+    }
+    const int n0 = blockIdx.x * 32;
     switch (a.epi) {
     case GV_F32:
         a.out[n0 + c] = ya;
@@ -167,16 +139,16 @@ __global__ __launch_bounds__(256) void k_q4gemv(GemvArgs a) {
         a.out[n0 + 16 + c] += yb;
         break;
     case GV_QROPE: {
-        const int hd = a.hd, half = hd >> 1;
+        const int hd = a.hd, hh = hd >> 1;
         const int h = n0 / hd, rr = n0 % hd;
         const int ii = (rr >> 5) * 16 + c;
-        const float2 cs = a.rope[(size_t)a.pos * half + ii];
+        const float2 cs = a.rope[(size_t)a.pos * hh + ii];
         a.out[h * hd + ii] = ya * cs.x - yb * cs.y;
-        a.out[h * hd + ii + half] = ya * cs.y + yb * cs.x;
+        a.out[h * hd + ii + hh] = ya * cs.y + yb * cs.x;
         break;
     }
     case GV_GLU:
-        a.out[pair * 16 + c] = act_f(a.act, ya) * yb;
+        a.out[blockIdx.x * 16 + c] = act_f(a.act, ya) * yb;
         break;
     case GV_PLE: {
         const uint8_t *prow = a.ple_raw + (size_t)a.tok * a.ple_row_blocks * 18;
@@ -187,25 +159,26 @@ __global__ __launch_bounds__(256) void k_q4gemv(GemvArgs a) {
     }
 }
 
-int ok() { return hipGetLastError() == hipSuccess ? PPX_OK : PPX_E_HIP; }
-
-int gemv_splits(int N, int K) {
-    const int pairs = N / 32, kch = K / 64;
-    int s = 1;
-    while (pairs * s < 1024 && s * 2 <= kch / 4) s *= 2;
-    return s;
+// waves per 16-row group: enough waves in flight to cover memory latency,
+// at least two 64-wide K chunks per wave
+int gemv_kw(int N, int K) {
+    const int groups = N / 16, kch = K / 64;
+    int kw = 1;
+    while (kw < 8 && groups * kw < 2048 && kch / (2 * kw) >= 2) kw *= 2;
+    return kw;
 }
 
 }  // namespace
 
-size_t gemv_scratch_floats(int N, int K) { return (size_t)gemv_splits(N, K) * N; }
-
-int launch_gemv(const GemvArgs &a0, hipStream_t s) {
-    GemvArgs a = a0;
-    if (a.W.N % 32 || a.W.K % 64) return PPX_E_UNSUPPORTED;
-    a.ksplit = gemv_splits(a.W.N, a.W.K);
-    if (a.ksplit > 1 && (!a.partial || !a.counter)) return PPX_E_INVAL;
-    hipLaunchKernelGGL(k_q4gemv, dim3(a.W.N / 32, a.ksplit), dim3(256), 0, s, a);
+int launch_gemv(const GemvArgs &a, hipStream_t s) {
+    if (a.W.N % 32 || a.W.K % 64 || !a.x || !a.out) return PPX_E_UNSUPPORTED;
+    const dim3 grid(a.W.N / 32);
+    switch (gemv_kw(a.W.N, a.W.K)) {
+    case 1: hipLaunchKernelGGL(k_q4gemv<1>, grid, dim3(128), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(k_q4gemv<2>, grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(k_q4gemv<4>, grid, dim3(512), 0, s, a); break;
+    default: hipLaunchKernelGGL(k_q4gemv<8>, grid, dim3(1024), 0, s, a); break;
+    }
     return ok();
 }
 

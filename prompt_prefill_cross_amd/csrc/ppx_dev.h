@@ -32,6 +32,20 @@ __device__ __forceinline__ h8 q4_word_to_h8(uint32_t w, _Float16 d) {
     return r;
 }
 
+// (code - 8) exactly, as fp16, for the eight codes of a repacked word.
+__device__ __forceinline__ h8 q4_word_codes(uint32_t w) {
+    h8 r;
+    const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t t = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
+        h2 v = __builtin_bit_cast(h2, t) - bias;
+        r[2 * i] = v[0];
+        r[2 * i + 1] = v[1];
+    }
+    return r;
+}
+
 // Code of element e (0..7) in a repacked word.
 __device__ __forceinline__ int q4_word_code(uint32_t w, int e) {
     int sh = (e & 1) ? (16 + 4 * (e >> 1)) : (4 * (e >> 1));

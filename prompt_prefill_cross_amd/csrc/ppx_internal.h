@@ -137,12 +137,8 @@ struct GemvArgs {
     const uint8_t *ple_raw = nullptr;
     int tok = 0, ple_row_blocks = 0, ple_col0 = 0;
     float ple_s = 0.f;
-    float *partial = nullptr;    // scratch [ksplit][N]
-    uint32_t *counter = nullptr; // scratch [N/32], zero on entry, zero on exit
-    int ksplit = 1;
 };
 int launch_gemv(const GemvArgs &a, hipStream_t s);
-size_t gemv_scratch_floats(int N, int K);
 
 struct AttnArgs {
     const __half *q = nullptr;  // [M][H][hd]
@@ -157,8 +153,7 @@ struct Attn1Args {
     const __half *k = nullptr, *v = nullptr;
     float *o = nullptr;        // [H*hd]
     int H = 0, KVH = 0, hd = 0, pos = 0;
-    float *partial = nullptr;  // scratch
-    uint32_t *counter = nullptr;
+    float *partial = nullptr;  // scratch of attn1_scratch_floats(H, hd, pos + 1) floats
 };
 int launch_attn_1row(const Attn1Args &a, hipStream_t s);
 size_t attn1_scratch_floats(int H, int hd, int n_pos);
