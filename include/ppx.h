@@ -113,7 +113,10 @@ size_t ppx_model_device_bytes(const ppx_model *m);
 
 /* ---------------------------------------------------------------- KV cache */
 
-/* fp16 K and V of the Ls owning layers, [Ls][n_ctx][kv_dim] each, K first. */
+/* fp16 K and V of the Ls owning layers: K as [Ls][n_ctx][kv_dim] first (its
+ * size rounded up to 256 bytes), then V transposed, [Ls][kv_dim][vld] with
+ * vld = n_ctx rounded up to a multiple of 64 (values of consecutive positions
+ * contiguous, as the attention kernels read them). */
 size_t ppx_kv_bytes(const ppx_model *m, int n_ctx);
 /* Wrap a caller-owned device buffer of >= ppx_kv_bytes bytes (256-byte
  * aligned) as an empty cache (n_pos = 0).  The buffer must outlive the
@@ -199,15 +202,18 @@ int ppx_op_gemm_exact(const ppx_model *m, const char *tensor, const void *a_hi, 
 int ppx_op_gemv(const ppx_model *m, const char *tensor, const float *x_dev, float *y_dev,
                 void *hip_stream);
 /* Causal prefill attention: q fp16 [M][n_head][head_dim] at positions
- * pos0..pos0+M-1 over k/v fp16 [>= pos0+M][n_kv_head][head_dim];
- * o fp16 [M][n_head*head_dim]. */
-int ppx_op_attention(const ppx_model *m, const void *q_dev, const void *k_dev, const void *v_dev,
-                     int M, int pos0, void *o_dev, void *hip_stream);
+ * pos0..pos0+M-1 over k fp16 [>= pos0+M][n_kv_head][head_dim] and the values
+ * in the cache's transposed layout, vt fp16 [n_kv_head][head_dim][vld]
+ * (vld a multiple of 64, >= pos0+M); o fp16 [M][n_head*head_dim].  ws_dev is
+ * scratch of ppx_workspace_bytes(m, M, pos0+M) bytes (1 <= M <= PPX_MAX_UBATCH). */
+int ppx_op_attention(const ppx_model *m, const void *q_dev, const void *k_dev, const void *vt_dev,
+                     int vld, int M, int pos0, void *o_dev, void *ws_dev, size_t ws_bytes, void *hip_stream);
 /* Single-query attention: q fp32 [n_head][head_dim] at position pos over the
- * first pos+1 cache rows of k/v fp16; o fp32 [n_head*head_dim].  ws_dev is
- * scratch of ppx_workspace_bytes(m, 1, pos+1) bytes. */
+ * first pos+1 cache positions (k as above, vt transposed with vld > pos, a
+ * multiple of 64); o fp32 [n_head*head_dim].  ws_dev is scratch of
+ * ppx_workspace_bytes(m, 1, pos+1) bytes. */
 int ppx_op_attention_1row(const ppx_model *m, const float *q_dev, const void *k_dev,
-                          const void *v_dev, int pos, float *o_dev, void *ws_dev, size_t ws_bytes,
+                          const void *vt_dev, int vld, int pos, float *o_dev, void *ws_dev, size_t ws_bytes,
                           void *hip_stream);
 
 const char *ppx_status_str(int status);

@@ -77,8 +77,9 @@ SIGNATURES = [
     ("ppx_op_gemm", c_int, [c_void_p, c_char_p, c_void_p, c_int, c_void_p, c_void_p]),
     ("ppx_op_gemm_exact", c_int, [c_void_p, c_char_p, c_void_p, c_void_p, c_int, c_void_p, c_void_p]),
     ("ppx_op_gemv", c_int, [c_void_p, c_char_p, c_void_p, c_void_p, c_void_p]),
-    ("ppx_op_attention", c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p]),
-    ("ppx_op_attention_1row", c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_void_p,
+    ("ppx_op_attention", c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p,
+                                 c_size_t, c_void_p]),
+    ("ppx_op_attention_1row", c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p,
                                       c_size_t, c_void_p]),
     ("ppx_status_str", c_char_p, [c_int]),
 ]
@@ -234,22 +235,37 @@ class Model:
         _check(lib().ppx_op_gemv(self._h, name.encode(), _ptr(x), _ptr(y), _stream()), "ppx_op_gemv")
         return y
 
+    @staticmethod
+    def _vt(v):
+        """[P][KVH][hd] values -> the cache's transposed layout [KVH][hd][vld], vld = P rounded up to 64."""
+        import torch
+        P, kvh, hd = v.shape
+        vld = (P + 63) // 64 * 64
+        vt = torch.zeros((kvh, hd, vld), dtype=v.dtype, device=v.device)
+        vt[:, :, :P] = v.permute(1, 2, 0)
+        return vt, vld
+
     def op_attention(self, q, k, v, pos0: int):
+        """q [M][H][hd], k/v [P][KVH][hd] (fp16); causal attention of rows at pos0.."""
         import torch
         H, hd = self.info["n_head"], self.info["head_dim"]
         M = q.shape[0]
+        vt, vld = self._vt(v)
         o = torch.empty((M, H * hd), dtype=torch.float16, device="cuda")
-        _check(lib().ppx_op_attention(self._h, _ptr(q), _ptr(k), _ptr(v), M, pos0, _ptr(o), _stream()),
-               "ppx_op_attention")
+        need = lib().ppx_workspace_bytes(self._h, M, pos0 + M)
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        _check(lib().ppx_op_attention(self._h, _ptr(q), _ptr(k), _ptr(vt), vld, M, pos0, _ptr(o), _ptr(ws), need,
+                                      _stream()), "ppx_op_attention")
         return o
 
     def op_attention_1row(self, q, k, v, pos: int):
         import torch
         H, hd = self.info["n_head"], self.info["head_dim"]
         o = torch.empty(H * hd, dtype=torch.float32, device="cuda")
+        vt, vld = self._vt(v)
         need = lib().ppx_workspace_bytes(self._h, 1, pos + 1)
         ws = torch.empty(need, dtype=torch.uint8, device="cuda")
-        _check(lib().ppx_op_attention_1row(self._h, _ptr(q), _ptr(k), _ptr(v), pos, _ptr(o), _ptr(ws), need,
+        _check(lib().ppx_op_attention_1row(self._h, _ptr(q), _ptr(k), _ptr(vt), vld, pos, _ptr(o), _ptr(ws), need,
                                            _stream()), "ppx_op_attention_1row")
         return o
 
@@ -298,13 +314,17 @@ class KVCache:
         _check(lib().ppx_kv_load(self._h, os.fsencode(path), n_pos, _stream(stream)), "ppx_kv_load")
 
     def kv_tensors(self):
-        """(K, V) as torch fp16 views [Ls][n_ctx][kv_dim]."""
+        """(K, V) as torch fp16 views [Ls][n_ctx][kv_dim] (V is a transposed view
+        of the cache's [Ls][kv_dim][vld] layout)."""
         import torch
         I = self.model.info
         ls, kvd = I["n_layer_kv_from_start"], I["kv_dim"]
         n = ls * self.n_ctx * kvd
-        h = self.buf[:4 * n].view(torch.float16)
-        return h[:n].view(ls, self.n_ctx, kvd), h[n:2 * n].view(ls, self.n_ctx, kvd)
+        kbytes = (2 * n + 255) // 256 * 256
+        vld = (self.n_ctx + 63) // 64 * 64
+        K = self.buf[:2 * n].view(torch.float16).view(ls, self.n_ctx, kvd)
+        VT = self.buf[kbytes:kbytes + 2 * ls * kvd * vld].view(torch.float16).view(ls, kvd, vld)
+        return K, VT[:, :, :self.n_ctx].transpose(1, 2)
 
     def close(self):
         if self._h:

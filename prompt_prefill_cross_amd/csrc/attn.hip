@@ -1,55 +1,109 @@
 // Causal prefill attention (MFMA, flash-style online softmax) and the
 // single-query attention of the pruned KV-shared layers.
 //
+// Cache layout: K is [pos][kv_head][head_dim]; V is kept transposed,
+// [kv_head][head_dim][vld] with vld >= n_ctx a multiple of 64, so that the
+// values of consecutive keys for one dimension are contiguous.
+//
 // Prefill: the query heads that share one KV head are packed together, so a
-// key/value tile read from the cache serves all of them (GQA/MQA).  A
-// workgroup owns 64 query columns -- (row, head-in-group) pairs -- of one KV
-// head; each of its four waves owns 16.  The kernel computes S^T = K Q^T so
-// that the 16x16 accumulator of a wave holds keys down and query columns
-// across; after the online-softmax update the probabilities in a lane are
-// exactly the B operand of O^T = V^T P^T for that lane (the MFMA pairs A and
-// B by lane group and element, so any common order of the 32 keys of a step
-// is valid).  V is staged transposed in LDS to serve as the A operand.
-// Tiles are aligned to absolute key positions, so a row's result does not
-// depend on how the prompt was split into ubatches.
+// key/value tile serves all of them (GQA/MQA).  A workgroup owns 64 query
+// columns -- (row, head-in-group) pairs -- of one KV head and one chunk of
+// keys; each of its four waves owns 16 columns.  The kernel computes
+// S^T = K Q^T, so the 16x16 accumulator of a wave holds keys down and query
+// columns across.  Inside each 32-key step the keys are taken in the order
+// that puts keys 8g..8g+7 of the step in lane group g of the accumulator;
+// then a lane's probabilities are exactly its B operand of O^T = V^T P^T, and
+// its V^T A operand is one 16-byte read of the transposed cache.  Tiles are
+// aligned to absolute key positions, so a row's result does not depend on
+// how the prompt was split into ubatches.  When the keys are split over
+// several workgroups, each writes (max, sum, unnormalised output) and a merge
+// kernel combines the chunks in chunk order.
 #include "ppx_dev.h"
 
 namespace ppx {
 
 namespace {
 
-constexpr int KT = 64;       // keys per tile
-constexpr int VT_LD = 68;    // LDS row stride (halves) of V^T
+constexpr int KT = 64;  // keys per tile
+
+template <int HD>
+struct AttnTile {
+    static constexpr int KB = HD / 32;            // 32-wide d steps of S
+    static constexpr int DT = HD / 16;            // 16-row d subtiles of O^T
+    static constexpr int KU = KB * 4 * 64 / 256;  // K units (16 B) per thread per tile
+    static constexpr int VU = DT * 2 * 64 / 256;  // V^T units per thread per tile
+    h8 kr[KU], vr[VU];
+
+    // Branch-free: keys past `pend` read the last valid K row (their scores
+    // are masked) and their values are zeroed when stored.
+    __device__ __forceinline__ void load(const AttnArgs &a, int kvh, int t0, int pend) {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < KU; ++i) {
+            const int u = tid + i * 256;
+            const int dk = u >> 8, j = (u >> 6) & 3, l = u & 63;
+            const int i16 = l & 15, g = l >> 4;
+            const int key = t0 + (j >> 1) * 32 + 8 * (i16 >> 2) + 4 * (j & 1) + (i16 & 3);
+            const unsigned off = (unsigned)((min(key, pend) * a.KVH + kvh) * HD + dk * 32 + g * 8);
+            kr[i] = *reinterpret_cast<const h8 *>(a.k + off);
+        }
+#pragma unroll
+        for (int i = 0; i < VU; ++i) {
+            const int u = tid + i * 256;
+            const int di = u >> 7, kb2 = (u >> 6) & 1, l = u & 63;
+            const int d = di * 16 + (l & 15);
+            const unsigned off = (unsigned)((kvh * HD + d) * a.vld + t0 + kb2 * 32 + 8 * (l >> 4));
+            vr[i] = *reinterpret_cast<const h8 *>(a.vt + off);
+        }
+    }
+
+    __device__ __forceinline__ void store(h8 *ks, h8 *vs, int t0, int pend) const {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < KU; ++i) ks[tid + i * 256] = kr[i];
+#pragma unroll
+        for (int i = 0; i < VU; ++i) {
+            const int u = tid + i * 256;
+            const int key0 = t0 + ((u >> 6) & 1) * 32 + 8 * ((u & 63) >> 4);
+            h8 v = vr[i];
+            if (key0 + 7 > pend) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (key0 + e > pend) v[e] = (_Float16)0.0f;
+            }
+            vs[u] = v;
+        }
+    }
+};
 
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn_prefill(AttnArgs a) {
-    constexpr int KB = HD / 32;  // 32-wide d steps
-    constexpr int DT = HD / 16;  // 16-row d subtiles of O^T
-    __shared__ h8 ks[KB * 4 * 64];             // K tile, A-fragment order [kb][key16][lane]
-    __shared__ _Float16 vt[HD * VT_LD];        // V^T tile [d][key]
+    using T = AttnTile<HD>;
+    constexpr int KB = T::KB, DT = T::DT;
+    __shared__ h8 ks[KB * 4 * 64];  // K fragments [d step][16-key block][lane]
+    __shared__ h8 vs[DT * 2 * 64];  // V^T fragments [d subtile][32-key step][lane]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int G = a.H / a.KVH;
-    const int kvh = blockIdx.y;
-    const int cbase = blockIdx.x * 64;
+    const int cb = blockIdx.x, ck = blockIdx.y, kvh = blockIdx.z;
     const int lc = lane & 15, lg = lane >> 4;
 
-    // this lane's query column
-    const int col = cbase + wave * 16 + lc;
+    const int tmax = min(a.M - 1, (cb * 64 + 63) / G);
+    const int pend = a.pos0 + tmax;  // last key any column here can see
+    const int kbeg = ck * a.kc;
+    if (kbeg > pend) return;
+    const int kend = min(kbeg + a.kc, pend + 1);
+
+    const int col = cb * 64 + wave * 16 + lc;
     const int t = col / G, hg = col % G;
     const bool valid = t < a.M;
     const int h = kvh * G + hg;
     const int qpos = a.pos0 + (valid ? t : 0);
 
-    // Q^T fragments (B operand): column = query, k = d
     h8 qf[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-        if (valid)
-            qf[kb] = *reinterpret_cast<const h8 *>(a.q + ((size_t)t * a.H + h) * HD + kb * 32 + lg * 8);
-        else
-            qf[kb] = h8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
+    for (int kb = 0; kb < KB; ++kb)
+        qf[kb] = *reinterpret_cast<const h8 *>(a.q + ((size_t)min(t, a.M - 1) * a.H + h) * HD + kb * 32 + lg * 8);
 
     f4 oacc[DT];
 #pragma unroll
@@ -57,31 +111,16 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnArgs a) {
     float mrun = -INFINITY, lrun = 0.f;
     const float sl2 = 1.4426950408889634f / sqrtf((float)HD);
 
-    // last position any column of this workgroup needs
-    const int tmax = min(a.M - 1, (cbase + 63) / G);
-    const int pend = a.pos0 + tmax;  // inclusive
-    const int ntiles = pend / KT + 1;
-
-    for (int tile = 0; tile < ntiles; ++tile) {
-        const int k0 = tile * KT;
-        // ---- stage K (fragment order) and V^T
-        for (int u = tid; u < KT * HD / 8; u += 256) {
-            const int key = u / (HD / 8), d8 = u % (HD / 8);
-            const int kp = k0 + key;
-            h8 kv = h8{0, 0, 0, 0, 0, 0, 0, 0}, vv = h8{0, 0, 0, 0, 0, 0, 0, 0};
-            if (kp <= pend) {
-                const size_t off = ((size_t)kp * a.KVH + kvh) * HD + d8 * 8;
-                kv = *reinterpret_cast<const h8 *>(a.k + off);
-                vv = *reinterpret_cast<const h8 *>(a.v + off);
-            }
-            const int kb = d8 >> 2, g = d8 & 3;
-            ks[(kb * 4 + (key >> 4)) * 64 + g * 16 + (key & 15)] = kv;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vt[(d8 * 8 + e) * VT_LD + key] = vv[e];
-        }
+    T tile;
+    const int ntiles = (kend - kbeg + KT - 1) / KT;
+    tile.load(a, kvh, kbeg, pend);
+    for (int it = 0; it < ntiles; ++it) {
+        const int t0 = kbeg + it * KT;
+        tile.store(ks, vs, t0, pend);
         __syncthreads();
+        tile.load(a, kvh, min(t0 + KT, kbeg + (ntiles - 1) * KT), pend);  // next tile (clamped)
 
-        // ---- S^T = K Q^T for 64 keys x 16 query columns
+        // S^T = K Q^T: s[j][r] is key t0 + 32(j/2) + 8 lg + 4(j%2) + r, query column lc
         f4 s[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -89,13 +128,12 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnArgs a) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) s[j] = mfma16(ks[(kb * 4 + j) * 64 + lane], qf[kb], s[j]);
         }
-        // ---- online softmax (per query column; a column lives in lanes lc, lc+16, lc+32, lc+48)
         float tmx = -INFINITY;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int kp = k0 + j * 16 + lg * 4 + r;
+                const int kp = t0 + (j >> 1) * 32 + 8 * lg + 4 * (j & 1) + r;
                 const float v = (kp <= qpos) ? s[j][r] * sl2 : -INFINITY;
                 s[j][r] = v;
                 tmx = fmaxf(tmx, v);
@@ -120,46 +158,71 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnArgs a) {
         mrun = mnew;
 #pragma unroll
         for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
-
-        // ---- O^T += V^T P^T; step kb2 covers keys 32kb2 + {4lg+r, 16+4lg+r}
+        // O^T += V^T P^T; step kb2 covers keys t0 + 32 kb2 + 8 lg + 0..7 in lane group lg
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
+        for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-            for (int i = 0; i < DT; ++i) {
-                const _Float16 *vr = vt + (i * 16 + lc) * VT_LD + kb2 * 32 + lg * 4;
-                const h4 lo = *reinterpret_cast<const h4 *>(vr);
-                const h4 hi = *reinterpret_cast<const h4 *>(vr + 16);
-                const h8 va = h8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                oacc[i] = mfma16(va, pf[kb2], oacc[i]);
-            }
-        }
+            for (int i = 0; i < DT; ++i) oacc[i] = mfma16(vs[(i * 2 + kb2) * 64 + lane], pf[kb2], oacc[i]);
         __syncthreads();
     }
 
     if (!valid) return;
-    const float inv = 1.0f / lrun;
-    __half *o = a.o + ((size_t)t * a.H + h) * HD;
+    if (a.nkc == 1) {
+        const float inv = 1.0f / lrun;
+        __half *o = a.o + ((size_t)t * a.H + h) * HD;
 #pragma unroll
-    for (int i = 0; i < DT; ++i) {
-        const int d = i * 16 + lg * 4;
+        for (int i = 0; i < DT; ++i) {
+            const int d = i * 16 + lg * 4;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[d + r] = __float2half(oacc[i][r] * inv);
+            for (int r = 0; r < 4; ++r) o[d + r] = __float2half(oacc[i][r] * inv);
+        }
+    } else {
+        const size_t slot = ((size_t)ck * a.M + t) * a.H + h;
+        float *po = a.part + slot * HD;
+#pragma unroll
+        for (int i = 0; i < DT; ++i) *reinterpret_cast<f4 *>(po + i * 16 + lg * 4) = oacc[i];
+        if (lg == 0) {
+            float *pm = a.part + (size_t)a.nkc * a.M * a.H * HD + slot * 2;
+            pm[0] = mrun;
+            pm[1] = lrun;
+        }
     }
 }
+
+// Combine the key chunks of row t, head h: chunks 0..floor(pos/kc) hold keys
+// the row can see.  Max-subtracted weights in the exp2 domain of the kernel.
+template <int HD>
+__global__ __launch_bounds__(HD) void k_attn_prefill_merge(AttnArgs a) {
+    const int t = blockIdx.x / a.H, h = blockIdx.x % a.H, d = threadIdx.x;
+    const int nch = (a.pos0 + t) / a.kc + 1;
+    const float *pm = a.part + (size_t)a.nkc * a.M * a.H * HD;
+    float M = -INFINITY;
+    for (int c = 0; c < nch; ++c) M = fmaxf(M, pm[(((size_t)c * a.M + t) * a.H + h) * 2]);
+    float L = 0.f, O = 0.f;
+    for (int c = 0; c < nch; ++c) {
+        const size_t slot = ((size_t)c * a.M + t) * a.H + h;
+        const float w = exp2f(pm[slot * 2] - M);
+        L += w * pm[slot * 2 + 1];
+        O += w * a.part[slot * HD + d];
+    }
+    a.o[((size_t)t * a.H + h) * HD + d] = __float2half(O / L);
+}
+
 // ------------------------------------------------------------------ single query
 // One query row (all heads, fp32) over cache positions 0..pos, in two launches.
 // k_attn_1row: grid (chunks of CH keys, KVH); a workgroup stages its keys and
-// values in LDS with 16-byte loads, scores them against the G heads of its KV
-// head (one wave per head group of 64 keys), and writes per head the chunk's
-// max, exp-sum and unnormalised output.  k_attn_merge: one workgroup per head
-// combines the chunks in chunk order.
+// transposed values in LDS with 16-byte loads, scores them against the G heads
+// of its KV head (a wave per head, lane = key), and writes per head the
+// chunk's max, exp-sum and unnormalised output.  k_attn_merge: one workgroup
+// per head combines the chunks in chunk order.
 constexpr int CH = 64;
 
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn_1row(Attn1Args a) {
     constexpr int KLD = HD + 2;  // padded K rows (halves): row r starts at bank r
+    constexpr int VLD = CH + 4;  // padded V^T rows (halves)
     __shared__ _Float16 kl[CH * KLD];
-    __shared__ _Float16 vl[CH * HD];
+    __shared__ _Float16 vl[HD * VLD];
     __shared__ float ql[8 * HD];
     __shared__ float pl[8 * CH];
 
@@ -173,15 +236,17 @@ __global__ __launch_bounds__(256) void k_attn_1row(Attn1Args a) {
     for (int u = tid; u < G * HD; u += 256) ql[u] = a.q[(size_t)kvh * G * HD + u];
     for (int u = tid; u < CH * HD / 8; u += 256) {
         const int key = u / (HD / 8), d8 = u % (HD / 8);
-        h8 kv = h8{0, 0, 0, 0, 0, 0, 0, 0}, vv = kv;
-        if (key < nk) {
-            const size_t off = ((size_t)(k0 + key) * a.KVH + kvh) * HD + d8 * 8;
-            kv = *reinterpret_cast<const h8 *>(a.k + off);
-            vv = *reinterpret_cast<const h8 *>(a.v + off);
-        }
+        const h8 kv = *reinterpret_cast<const h8 *>(a.k + ((size_t)(k0 + min(key, nk - 1)) * a.KVH + kvh) * HD + d8 * 8);
 #pragma unroll
         for (int e = 0; e < 8; e += 2) *reinterpret_cast<h2 *>(kl + key * KLD + d8 * 8 + e) = h2{kv[e], kv[e + 1]};
-        *reinterpret_cast<h8 *>(vl + key * HD + d8 * 8) = vv;
+        const int d = u / (CH / 8), k8 = u % (CH / 8);
+        h8 vv = *reinterpret_cast<const h8 *>(a.vt + ((size_t)kvh * HD + d) * a.vld + k0 + k8 * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (k8 * 8 + e >= nk) vv[e] = (_Float16)0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; e += 4)
+            *reinterpret_cast<h4 *>(vl + d * VLD + k8 * 8 + e) = h4{vv[e], vv[e + 1], vv[e + 2], vv[e + 3]};
     }
     __syncthreads();
 
@@ -211,12 +276,13 @@ __global__ __launch_bounds__(256) void k_attn_1row(Attn1Args a) {
         }
     }
     __syncthreads();
-    // unnormalised P.V: thread d (HD <= 256 threads), every head of the group
+    // unnormalised P.V: thread d, every head of the group
     float *po = a.partial + (size_t)a.H * nchunks * 2;
     for (int d = tid; d < HD; d += 256) {
         float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int j = 0; j < nk; ++j) {
-            const float v = (float)vl[j * HD + d];
+        const _Float16 *vrow = vl + d * VLD;
+        for (int j = 0; j < CH; ++j) {
+            const float v = (float)vrow[j];
 #pragma unroll
             for (int g = 0; g < 8; ++g)
                 if (g < G) o[g] += pl[g * CH + j] * v;
@@ -266,16 +332,47 @@ int ok() { return hipGetLastError() == hipSuccess ? PPX_OK : PPX_E_HIP; }
 
 }  // namespace
 
-int launch_attn_prefill(const AttnArgs &a, hipStream_t s) {
+AttnSplit attn_split(int M, int H, int KVH, int pos0) {
+    const int G = H / KVH;
+    const int colblocks = (M * G + 63) / 64;
+    const int P = pos0 + M;
+    int want = (256 + colblocks * KVH - 1) / (colblocks * KVH);
+    want = std::max(1, std::min(want, ATTN_MAX_CHUNKS));
+    int kc = (P + want - 1) / want;
+    kc = std::max(256, (kc + KT - 1) / KT * KT);
+    AttnSplit sp;
+    sp.kc = kc;
+    sp.nkc = (P + kc - 1) / kc;
+    return sp;
+}
+
+size_t attn_prefill_scratch_floats(int M, int H, int hd, int n_ctx) {
+    const int nkc = std::min(ATTN_MAX_CHUNKS, (n_ctx + 255) / 256);
+    return (size_t)nkc * M * H * (hd + 2);
+}
+
+int launch_attn_prefill(const AttnArgs &a0, hipStream_t s) {
+    AttnArgs a = a0;
     if (a.M <= 0) return PPX_OK;
     const int G = a.H / a.KVH;
-    if (a.H % a.KVH || 64 % G) return PPX_E_UNSUPPORTED;
-    dim3 grid((a.M * G + 63) / 64, a.KVH);
+    if (a.H % a.KVH || 64 % G || a.vld % 64 || a.pos0 + a.M > a.vld) return PPX_E_UNSUPPORTED;
+    const AttnSplit sp = attn_split(a.M, a.H, a.KVH, a.pos0);
+    a.kc = sp.kc;
+    a.nkc = sp.nkc;
+    if (a.nkc > 1 && !a.part) return PPX_E_INVAL;
+    dim3 grid((a.M * G + 63) / 64, a.nkc, a.KVH);
     switch (a.hd) {
     case 64: hipLaunchKernelGGL(k_attn_prefill<64>, grid, dim3(256), 0, s, a); break;
     case 128: hipLaunchKernelGGL(k_attn_prefill<128>, grid, dim3(256), 0, s, a); break;
     case 256: hipLaunchKernelGGL(k_attn_prefill<256>, grid, dim3(256), 0, s, a); break;
     default: return PPX_E_UNSUPPORTED;
+    }
+    if (a.nkc == 1) return ok();
+    if (hipGetLastError() != hipSuccess) return PPX_E_HIP;
+    switch (a.hd) {
+    case 64: hipLaunchKernelGGL(k_attn_prefill_merge<64>, dim3(a.M * a.H), dim3(64), 0, s, a); break;
+    case 128: hipLaunchKernelGGL(k_attn_prefill_merge<128>, dim3(a.M * a.H), dim3(128), 0, s, a); break;
+    default: hipLaunchKernelGGL(k_attn_prefill_merge<256>, dim3(a.M * a.H), dim3(256), 0, s, a); break;
     }
     return ok();
 }
@@ -287,7 +384,8 @@ size_t attn1_scratch_floats(int H, int hd, int n_pos) {
 
 int launch_attn_1row(const Attn1Args &a, hipStream_t s) {
     const int G = a.H / a.KVH;
-    if (a.H % a.KVH || G > 8 || a.pos < 0 || !a.partial) return PPX_E_UNSUPPORTED;
+    if (a.H % a.KVH || G > 8 || a.pos < 0 || !a.partial || a.vld % 64 || a.pos >= a.vld)
+        return PPX_E_UNSUPPORTED;
     const int chunks = (a.pos + 1 + CH - 1) / CH;
     dim3 grid(chunks, a.KVH);
     switch (a.hd) {

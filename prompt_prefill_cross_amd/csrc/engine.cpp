@@ -29,7 +29,7 @@ inline size_t al(size_t x) { return (x + 255) / 256 * 256; }
 struct WsLayout {
     size_t tok, x, a16, a16lo, q16, o16, h16, p16;
     size_t xr, ar, qr, orow, hr, pr;
-    size_t at_part;
+    size_t at_part, ap_part;
     size_t total;
 };
 
@@ -58,6 +58,7 @@ WsLayout ws_layout(const ppx_model *m, int ub, int n_ctx) {
     w.hr = take(4ull * F);
     w.pr = take(4ull * std::max(E, 1));
     w.at_part = take(4 * attn1_scratch_floats(I.n_head, I.head_dim, std::max(n_ctx, 1)));
+    w.ap_part = take(4 * attn_prefill_scratch_floats(ub, I.n_head, I.head_dim, std::max(n_ctx, 1)));
     w.total = o;
     return w;
 }
@@ -137,6 +138,7 @@ int layer_rows(Ctx &c, int il, int M, int row0, int pos0) {
     __half *o16 = c.at<__half>(c.L.o16);
     __half *h16 = c.at<__half>(c.L.h16);
     const size_t lstride = (size_t)c.kv->n_ctx * kvd;
+    const size_t vstride = (size_t)c.kv->vld * kvd;
 
     __half *a16lo = c.at<__half>(c.L.a16lo);
     if (w.own)
@@ -165,14 +167,17 @@ int layer_rows(Ctx &c, int il, int M, int row0, int pos0) {
         gk.kvd = kvd;
         gk.out_f16 = nullptr;
         gk.kc = c.kv->k + il * lstride;
-        gk.vc = c.kv->v + il * lstride;
+        gk.vc = c.kv->vt + il * vstride;
+        gk.vld = c.kv->vld;
         PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm_exact(gk, c.s));
     }
 
     AttnArgs at;
     at.q = q16;
     at.k = c.kv->k + (size_t)w.src * lstride;
-    at.v = c.kv->v + (size_t)w.src * lstride;
+    at.vt = c.kv->vt + (size_t)w.src * vstride;
+    at.vld = c.kv->vld;
+    at.part = c.at<float>(c.L.ap_part);
     at.o = o16;
     at.M = M;
     at.H = I.n_head;
@@ -278,7 +283,8 @@ int layer_row(Ctx &c, int il, int pos, int tok) {
     Attn1Args at;
     at.q = qr;
     at.k = c.kv->k + (size_t)w.src * lstride;
-    at.v = c.kv->v + (size_t)w.src * lstride;
+    at.vt = c.kv->vt + (size_t)w.src * c.kv->vld * kvd;
+    at.vld = c.kv->vld;
     at.o = orow;
     at.H = I.n_head;
     at.KVH = I.n_kv_head;
@@ -401,13 +407,19 @@ int kv_save(const ppx_kv *kv, const char *path, int n_pos, hipStream_t s) {
     const ppx_model_info &I = kv->m->info;
     const int nl = I.n_layer_kv_from_start, kvd = I.kv_dim;
     const size_t row = (size_t)n_pos * kvd;
-    std::vector<uint16_t> buf(2 * (size_t)nl * row);
+    std::vector<uint16_t> buf(2 * (size_t)nl * row), vt(row);
     if (hipStreamSynchronize(s) != hipSuccess) return PPX_E_HIP;
     for (int il = 0; il < nl && row; ++il) {
         const size_t src = (size_t)il * kv->n_ctx * kvd;
-        if (hipMemcpy(buf.data() + il * row, kv->k + src, row * 2, hipMemcpyDeviceToHost) != hipSuccess ||
-            hipMemcpy(buf.data() + (nl + il) * row, kv->v + src, row * 2, hipMemcpyDeviceToHost) != hipSuccess)
+        if (hipMemcpy(buf.data() + il * row, kv->k + src, row * 2, hipMemcpyDeviceToHost) != hipSuccess)
             return PPX_E_HIP;
+        // V is held transposed on the device: kvd rows of vld positions
+        if (hipMemcpy2D(vt.data(), (size_t)n_pos * 2, kv->vt + (size_t)il * kv->vld * kvd, (size_t)kv->vld * 2,
+                        (size_t)n_pos * 2, kvd, hipMemcpyDeviceToHost) != hipSuccess)
+            return PPX_E_HIP;
+        uint16_t *vdst = buf.data() + (nl + il) * row;
+        for (int dd = 0; dd < kvd; ++dd)
+            for (int p = 0; p < n_pos; ++p) vdst[(size_t)p * kvd + dd] = vt[(size_t)dd * n_pos + p];
     }
     std::FILE *f = std::fopen(path, "wb");
     if (!f) return PPX_E_IO;
@@ -468,11 +480,18 @@ int kv_load(ppx_kv *kv, const char *path, int n_pos, hipStream_t s) {
         }
     std::fclose(f);
     if (st) return st;
+    std::vector<uint16_t> vt((size_t)nl * row);
+    for (int il = 0; il < nl && row; ++il) {
+        const uint16_t *vsrc = buf.data() + (nl + il) * row;
+        uint16_t *vdst = vt.data() + il * row;
+        for (int p = 0; p < n_pos; ++p)
+            for (int dd = 0; dd < kvd; ++dd) vdst[(size_t)dd * n_pos + p] = vsrc[(size_t)p * kvd + dd];
+    }
     for (int il = 0; il < nl && row; ++il) {
         const size_t dst = (size_t)il * kv->n_ctx * kvd;
         if (hipMemcpyAsync(kv->k + dst, buf.data() + il * row, row * 2, hipMemcpyHostToDevice, s) != hipSuccess ||
-            hipMemcpyAsync(kv->v + dst, buf.data() + (nl + il) * row, row * 2, hipMemcpyHostToDevice, s) !=
-                hipSuccess)
+            hipMemcpy2DAsync(kv->vt + (size_t)il * kv->vld * kvd, (size_t)kv->vld * 2, vt.data() + il * row,
+                             (size_t)n_pos * 2, (size_t)n_pos * 2, kvd, hipMemcpyHostToDevice, s) != hipSuccess)
             return PPX_E_HIP;
     }
     if (hipStreamSynchronize(s) != hipSuccess) return PPX_E_HIP;
@@ -531,9 +550,13 @@ int ppx_model_get_info(const ppx_model *m, ppx_model_info *out) {
 
 size_t ppx_model_device_bytes(const ppx_model *m) { return m ? m->dev_bytes : 0; }
 
+static int kv_vld(int n_ctx) { return (n_ctx + 63) / 64 * 64; }
+
 size_t ppx_kv_bytes(const ppx_model *m, int n_ctx) {
     if (!m || n_ctx <= 0) return 0;
-    return 2ull * m->info.n_layer_kv_from_start * (size_t)n_ctx * m->info.kv_dim * 2;
+    const size_t ls = m->info.n_layer_kv_from_start, kvd = m->info.kv_dim;
+    const size_t kbytes = (ls * (size_t)n_ctx * kvd * 2 + 255) / 256 * 256;
+    return kbytes + ls * kvd * (size_t)kv_vld(n_ctx) * 2;
 }
 
 int ppx_kv_init(ppx_model *m, void *kv_dev, size_t bytes, int n_ctx, ppx_kv **out) {
@@ -546,8 +569,10 @@ int ppx_kv_init(ppx_model *m, void *kv_dev, size_t bytes, int n_ctx, ppx_kv **ou
     PPX_TRY(ensure_rope(m, n_ctx));
     ppx_kv *kv = new ppx_kv();
     kv->m = m;
+    const size_t kbytes = ((size_t)m->info.n_layer_kv_from_start * n_ctx * m->info.kv_dim * 2 + 255) / 256 * 256;
     kv->k = static_cast<__half *>(kv_dev);
-    kv->v = kv->k + need / 4;
+    kv->vt = reinterpret_cast<__half *>(static_cast<uint8_t *>(kv_dev) + kbytes);
+    kv->vld = kv_vld(n_ctx);
     kv->n_ctx = n_ctx;
     *out = kv;
     return PPX_OK;
@@ -641,25 +666,32 @@ int ppx_op_gemv(const ppx_model *m, const char *tensor, const float *x_dev, floa
     return launch_gemv(a, (hipStream_t)hip_stream);
 }
 
-int ppx_op_attention(const ppx_model *m, const void *q_dev, const void *k_dev, const void *v_dev, int M, int pos0,
-                     void *o_dev, void *hip_stream) {
-    if (!m || !q_dev || !k_dev || !v_dev || !o_dev || M < 0 || pos0 < 0) return PPX_E_INVAL;
+int ppx_op_attention(const ppx_model *m, const void *q_dev, const void *k_dev, const void *vt_dev, int vld, int M,
+                     int pos0, void *o_dev, void *ws_dev, size_t ws_bytes, void *hip_stream) {
+    if (!m || !q_dev || !k_dev || !vt_dev || !o_dev || !ws_dev || M < 1 || pos0 < 0 || M > PPX_MAX_UBATCH)
+        return PPX_E_INVAL;
+    if (vld % 64 || vld < pos0 + M) return PPX_E_INVAL;
+    const WsLayout L = ws_layout(m, M, pos0 + M);
+    if (ws_bytes < L.total) return PPX_E_NOMEM;
     AttnArgs a;
     a.q = static_cast<const __half *>(q_dev);
     a.k = static_cast<const __half *>(k_dev);
-    a.v = static_cast<const __half *>(v_dev);
+    a.vt = static_cast<const __half *>(vt_dev);
+    a.vld = vld;
     a.o = static_cast<__half *>(o_dev);
     a.M = M;
     a.H = m->info.n_head;
     a.KVH = m->info.n_kv_head;
     a.hd = m->info.head_dim;
     a.pos0 = pos0;
+    a.part = reinterpret_cast<float *>(static_cast<uint8_t *>(ws_dev) + L.ap_part);
     return launch_attn_prefill(a, (hipStream_t)hip_stream);
 }
 
-int ppx_op_attention_1row(const ppx_model *m, const float *q_dev, const void *k_dev, const void *v_dev, int pos,
-                          float *o_dev, void *ws_dev, size_t ws_bytes, void *hip_stream) {
-    if (!m || !q_dev || !k_dev || !v_dev || !o_dev || !ws_dev || pos < 0) return PPX_E_INVAL;
+int ppx_op_attention_1row(const ppx_model *m, const float *q_dev, const void *k_dev, const void *vt_dev, int vld,
+                          int pos, float *o_dev, void *ws_dev, size_t ws_bytes, void *hip_stream) {
+    if (!m || !q_dev || !k_dev || !vt_dev || !o_dev || !ws_dev || pos < 0) return PPX_E_INVAL;
+    if (vld % 64 || vld <= pos) return PPX_E_INVAL;
     const WsLayout L = ws_layout(m, 1, pos + 1);
     if (ws_bytes < L.total) return PPX_E_NOMEM;
     uint8_t *ws = static_cast<uint8_t *>(ws_dev);
@@ -667,7 +699,8 @@ int ppx_op_attention_1row(const ppx_model *m, const float *q_dev, const void *k_
     Attn1Args a;
     a.q = q_dev;
     a.k = static_cast<const __half *>(k_dev);
-    a.v = static_cast<const __half *>(v_dev);
+    a.vt = static_cast<const __half *>(vt_dev);
+    a.vld = vld;
     a.o = o_dev;
     a.H = m->info.n_head;
     a.KVH = m->info.n_kv_head;

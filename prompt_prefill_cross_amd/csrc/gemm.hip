@@ -289,9 +289,8 @@ __global__ __launch_bounds__(C::NT) void k_q4gemm(GemmArgs a) {
                             }
                         } else {
                             const int c = colA - a.qd - a.kvd;
-                            __half *v = a.vc + (size_t)pos * a.kvd;
-                            v[c] = __float2half(va);
-                            v[c + 16] = __float2half(vb);
+                            a.vc[(size_t)c * a.vld + pos] = __float2half(va);  // V^T
+                            a.vc[(size_t)(c + 16) * a.vld + pos] = __float2half(vb);
                         }
                     }
                 }

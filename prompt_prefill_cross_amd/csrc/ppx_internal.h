@@ -75,8 +75,10 @@ struct ppx_model {
 
 struct ppx_kv {
     const ppx_model *m = nullptr;
-    __half *k = nullptr, *v = nullptr;  // [Ls][n_ctx][kv_dim]
+    __half *k = nullptr;   // [Ls][n_ctx][kv_dim]
+    __half *vt = nullptr;  // [Ls][kv_dim][vld]: V transposed, row d = kv_head * head_dim + dim
     int n_ctx = 0, n_pos = 0;
+    int vld = 0;           // n_ctx rounded up to a multiple of 64
 };
 
 namespace ppx {
@@ -105,7 +107,9 @@ struct GemmArgs {
     int qd = 0, kvd = 0, hd = 0;
     int pos0 = 0;               // position of row 0
     const float2 *rope = nullptr;
-    __half *kc = nullptr, *vc = nullptr;  // cache rows of this layer at position 0
+    __half *kc = nullptr;       // K cache of this layer [n_ctx][kvd]
+    __half *vc = nullptr;       // V cache of this layer, transposed [kvd][vld]
+    int vld = 0;
     int act = ACT_GEGLU;
     // per-layer embedding (EPI_PLE)
     const uint8_t *ple_raw = nullptr;
@@ -140,17 +144,30 @@ struct GemvArgs {
 };
 int launch_gemv(const GemvArgs &a, hipStream_t s);
 
+constexpr int ATTN_MAX_CHUNKS = 16;
+struct AttnSplit {
+    int kc = 0, nkc = 1;  // keys per chunk (multiple of 64), chunks
+};
+AttnSplit attn_split(int M, int H, int KVH, int pos0);
+size_t attn_prefill_scratch_floats(int M, int H, int hd, int n_ctx);
+
 struct AttnArgs {
-    const __half *q = nullptr;  // [M][H][hd]
-    const __half *k = nullptr, *v = nullptr;  // cache [P][KVH][hd]
-    __half *o = nullptr;        // [M][H*hd]
+    const __half *q = nullptr;   // [M][H][hd]
+    const __half *k = nullptr;   // K cache of the source layer [P][KVH][hd]
+    const __half *vt = nullptr;  // V cache of the source layer, transposed [KVH][hd][vld]
+    int vld = 0;                 // multiple of 64, >= pos0 + M
+    __half *o = nullptr;         // [M][H*hd]
     int M = 0, H = 0, KVH = 0, hd = 0, pos0 = 0;
+    int kc = 0, nkc = 1;         // key split (set by the launcher)
+    float *part = nullptr;       // scratch of attn_prefill_scratch_floats(M, H, hd, pos0 + M) floats
 };
 int launch_attn_prefill(const AttnArgs &a, hipStream_t s);
 
 struct Attn1Args {
     const float *q = nullptr;  // [H][hd]
-    const __half *k = nullptr, *v = nullptr;
+    const __half *k = nullptr;   // [P][KVH][hd]
+    const __half *vt = nullptr;  // [KVH][hd][vld]
+    int vld = 0;
     float *o = nullptr;        // [H*hd]
     int H = 0, KVH = 0, hd = 0, pos = 0;
     float *partial = nullptr;  // scratch of attn1_scratch_floats(H, hd, pos + 1) floats

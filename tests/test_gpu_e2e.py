@@ -164,7 +164,16 @@ def test_tinyllama_full_and_resume(ppx, tmp_path):
         assert ok, (N, d)
         ok, d = logits_ok(lr, lg, atol=1e-3)
         assert ok, (N, d)
-        assert torch.equal(kv2.buf, kv.buf)
+        # The loaded prefix is the snapshot, bit for bit; positions computed
+        # after the resume match the uninterrupted run to rounding (the
+        # attention's key split follows the ubatch shape) and the oracle
+        # to the KV bound.
+        K1, V1 = kv.kv_tensors()
+        K2, V2 = kv2.kv_tensors()
+        assert torch.equal(K2[:, :N], K1[:, :N]) and torch.equal(V2[:, :N], V1[:, :N])
+        for got, want in ((K2, rkv.K), (V2, rkv.V)):
+            okk, dk = kv_within(got[:, :n].cpu().numpy(), want[:, :n])
+            assert okk, (N, dk)
 
 
 GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
