@@ -2,13 +2,23 @@
 
 One step = one ppx_prefill call from an empty cache (all ubatches, the
 pruned single-row phase and the head), inputs resident in HBM.  Prints one
-JSON line.  The metric is prefill tokens/s; `roofline` reports the MFMA GEMM
-phase (the dominant kernel) against the dense fp16 peak, from HIP events
-recorded around every GEMM launch in a separate, identical pass; the
-single-row phase's HBM rate and the attention phase's MFMA rate are given in
-`phases`.  `cpu_baseline` times the fp64 oracle on a bounded sample.
+JSON line.  The metric is prefill tokens/s.  `roofline` reports the dominant
+kernel, the gate|up GEMM of the row-batched layers (the largest single
+contraction of a layer), against the dense fp16 MFMA peak: its algorithmic
+FLOP per launch over its average launch time, from HIP events on the stream
+it runs on around back-to-back launches of the same kernel, shape and
+epilogue through ppx_op_gemm_glu (per-launch events inside a prefill add
+their own overhead; that figure is given beside it).  `phases` gives the
+whole GEMM phase, the attention phase (MFMA) and the single-row phase (HBM)
+from events around every launch in a separate, identical prefill pass.  `traffic` is read from the
+committed counter summary when it was taken on the current kernel source.
+`cpu_baseline` times the fp64 oracle on a bounded sample.
+
+--pmc-pass runs one prefill and one plain device copy of known size and
+exits: the command under which the HBM counters are collected.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -34,8 +44,42 @@ def parse():
     ap.add_argument("--prune", default="auto", choices=["auto", "on", "off"])
     ap.add_argument("--extra-n", default="512,8192", help="other prompt lengths to report (comma list, '' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=64, help="prompt tokens of the oracle sample")
+    ap.add_argument("--cpu-sample", type=int, default=0, help="prompt tokens of the oracle sample (0 = all)")
+    ap.add_argument("--pmc-pass", action="store_true", help="one prefill + one calibration copy, then exit")
     return ap.parse_args()
+
+
+# Sources of the GEMM kernel; counter-derived traffic is reported only while they are unchanged.
+GEMM_SOURCES = ("prompt_prefill_cross_amd/csrc/gemm.hip", "prompt_prefill_cross_amd/csrc/ppx_dev.h")
+TRAFFIC_FILE = "profiles/k_q4gemm_gate_up_e2b2048_traffic.txt"
+COPY_CAL_BYTES = 1 << 29  # calibration copy: 512 MiB read + 512 MiB written
+
+
+def gemm_source_sha():
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """Bytes per launch from the counter summary, or None when it is missing
+    or was taken on another version of the kernel."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != gemm_source_sha():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def timed_steps(mm, kv, toks, ub, prune, steps, warmup):
@@ -71,9 +115,41 @@ def phase_pass(ppx, mm, kv, toks, ub, prune, reps=3):
         else:
             for k in d["ms"]:
                 tm_sum["ms"][k] += d["ms"][k]
+            tm_sum["glu_ms"] += d["glu_ms"]
     for k in tm_sum["ms"]:
         tm_sum["ms"][k] /= reps
+    tm_sum["glu_ms"] /= reps
     return tm_sum
+
+
+def glu_kernel_us(mm, ub, reps=50, warmup=5):
+    """Average duration of the gate|up GEMM (layer 0's weights, ub rows)."""
+    import torch
+    I = mm.info
+    g = torch.Generator(device="cuda").manual_seed(7)
+    a = torch.randn((ub, I["d_model"]), generator=g, device="cuda").to(torch.float16)
+    h = torch.empty((ub, I["n_ff"]), dtype=torch.float16, device="cuda")
+    for _ in range(warmup):
+        mm.op_gemm_glu("blk.0.ffn_gate", a, out=h)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        mm.op_gemm_glu("blk.0.ffn_gate", a, out=h)
+    t1.record()
+    t1.synchronize()
+    return t0.elapsed_time(t1) * 1e3 / reps, reps
+
+
+def pmc_pass(mm, kv, toks, ub, prune):
+    import torch
+    kv.clear()
+    mm.prefill(toks, kv, n_ubatch=ub, prune=prune)
+    src = torch.ones(COPY_CAL_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"# pmc pass done: one prefill of {len(toks)} tokens, one {COPY_CAL_BYTES} B copy", flush=True)
 
 
 def cpu_baseline(cfg, buf, toks, sample):
@@ -112,6 +188,10 @@ def main():
     kv = ppx.KVCache(mm, n_ctx)
     mm.workspace(ub, n_ctx)
 
+    if a.pmc_pass:
+        pmc_pass(mm, kv, synth.prompt(cfg, a.n), ub, a.prune)
+        return
+
     results = {}
     for n in lens:
         toks = synth.prompt(cfg, n)
@@ -123,11 +203,15 @@ def main():
               f"phases ms {ph['ms']}", file=sys.stderr, flush=True)
 
     times, ph = results[a.n]
+    glu_us, glu_reps = glu_kernel_us(mm, ub)
     ms = float(np.mean(times))
     gemm_tflops = ph["gemm_flop"] / (ph["ms"]["gemm"] * 1e-3) / 1e12 if ph["ms"]["gemm"] else 0.0
     attn_tflops = ph["attn_flop"] / (ph["ms"]["attn"] * 1e-3) / 1e12 if ph["ms"]["attn"] else 0.0
     row_gbs = ph["row_bytes"] / (ph["ms"]["row"] * 1e-3) / 1e9 if ph["ms"]["row"] else 0.0
-    launches = ph["launches"]["gemm"]
+    glu_n = max(ph["glu_launches"], 1)
+    glu_flop = 2.0 * ub * (2 * cfg.n_ff) * cfg.d_model
+    assert abs(ph["glu_flop"] / glu_n - glu_flop) < 1.0, "gate|up launches of the prefill have another shape"
+    glu_tflops = glu_flop / (glu_us * 1e-6) / 1e12
     out = {
         "metric": "prefill tokens/sec at 512/2048/8192 prompt (E2B-like Q4_0), % MFMA peak",
         "value": a.n / (ms * 1e-3),
@@ -146,13 +230,15 @@ def main():
                             f"{cfg.n_head}x{cfg.head_dim} heads, {cfg.n_kv_head} KV head(s), FFN {cfg.n_ff}, "
                             f"vocab {cfg.n_vocab}, PLE {cfg.ple_dim}",
                    "global_batch": 1, "seq_len": a.n, "ubatch": ub, "prune": a.prune, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "kernel": "k_q4gemm (all GEMM launches of one prefill)",
-                     "achieved": gemm_tflops, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": gemm_tflops / PEAK_FP16_TFLOPS, "traffic": None,
-                     "launches": launches,
-                     "flop_per_launch": ph["gemm_flop"] / max(launches, 1),
-                     "avg_launch_us": ph["ms"]["gemm"] * 1e3 / max(launches, 1)},
+        "roofline": {"bound": "mfma", "kernel": f"k_q4gemm gate|up + GLU epilogue, M={ub} N={2 * cfg.n_ff} "
+                                                  f"K={cfg.d_model}",
+                     "achieved": glu_tflops, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": glu_tflops / PEAK_FP16_TFLOPS, "traffic": stored_traffic(),
+                     "flop_per_launch": glu_flop, "avg_launch_us": glu_us, "timed_launches": glu_reps,
+                     "in_prefill_avg_us_with_event_overhead": ph["glu_ms"] * 1e3 / glu_n,
+                     "in_prefill_launches": ph["glu_launches"]},
         "phases": {"ms": ph["ms"], "launches": ph["launches"],
+                   "gemm_tflops": gemm_tflops, "gemm_frac_mfma": gemm_tflops / PEAK_FP16_TFLOPS,
                    "attn_tflops": attn_tflops, "attn_frac_mfma": attn_tflops / PEAK_FP16_TFLOPS,
                    "row_gbs": row_gbs, "row_frac_hbm": row_gbs / PEAK_HBM_GBS,
                    "gemm_flop": ph["gemm_flop"], "attn_flop": ph["attn_flop"], "row_bytes": ph["row_bytes"]},
@@ -162,7 +248,7 @@ def main():
         "ms_std": float(np.std(times)),
     }
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg.name, buf, synth.prompt(cfg, a.n), a.cpu_sample)
+        out["cpu_baseline"] = cpu_baseline(cfg.name, buf, synth.prompt(cfg, a.n), a.cpu_sample or a.n)
     print(json.dumps(out), flush=True)
 
 

@@ -71,6 +71,9 @@ typedef struct {
     double gemm_flop;          /* algorithmic 2*M*N*K over the GEMM launches      */
     double attn_flop;          /* 4*n_head*head_dim*(visible keys) over queries   */
     double row_bytes;          /* Q4_0 weight bytes + KV bytes the row path reads */
+    double glu_ms;             /* the gate|up GEMM launches alone (also in GEMM)  */
+    int glu_launches;
+    double glu_flop;           /* their algorithmic 2*M*N*K                       */
 } ppx_timing;
 
 typedef struct {
@@ -193,6 +196,15 @@ int ppx_op_dequant(const ppx_model *m, const char *tensor, float *out_dev, void 
  * path, W = the named container tensor [N][K]. */
 int ppx_op_gemm(const ppx_model *m, const char *tensor, const void *a_dev_f16, int M, float *c_dev,
                 void *hip_stream);
+/* The gate|up GEMM of a layer with its fused activation epilogue, exactly
+ * as the prefill runs it for the row-batched layers (the GeGLU feed-forward
+ * of the Gemma-style decoder of "llama.cpp Gemma 4 prefill KV graph
+ * optimization"; SwiGLU for a model whose activation is SwiGLU):
+ * h[M][F] (fp16, ld = F) = act(A Wg^T) * (A Wu^T),
+ * A fp16 [M][K].  `tensor` must be a fused gate|up name ("blk.i.ffn_gate");
+ * PPX_E_INVAL otherwise.  Asynchronous on the stream. */
+int ppx_op_gemm_glu(const ppx_model *m, const char *tensor, const void *a_dev_f16, int M, void *h_dev_f16,
+                    void *hip_stream);
 /* The same on the exact-weight path used for the fused K|V weight
  * ("blk.i.wk", owning layers): A = a_hi + a_lo (two fp16 [M][K] arrays),
  * weights (code - 8) exactly with the fp32 block scale applied per 32-block. */

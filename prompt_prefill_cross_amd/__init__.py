@@ -40,12 +40,14 @@ class ModelInfo(ctypes.Structure):
 
 class Timing(ctypes.Structure):
     _fields_ = [("ms", ctypes.c_double * 4), ("launches", c_int * 4), ("gemm_flop", ctypes.c_double),
-                ("attn_flop", ctypes.c_double), ("row_bytes", ctypes.c_double)]
+                ("attn_flop", ctypes.c_double), ("row_bytes", ctypes.c_double), ("glu_ms", ctypes.c_double),
+                ("glu_launches", c_int), ("glu_flop", ctypes.c_double)]
 
     def as_dict(self):
         names = ("gemm", "attn", "row", "other")
         return {"ms": dict(zip(names, list(self.ms))), "launches": dict(zip(names, list(self.launches))),
-                "gemm_flop": self.gemm_flop, "attn_flop": self.attn_flop, "row_bytes": self.row_bytes}
+                "gemm_flop": self.gemm_flop, "attn_flop": self.attn_flop, "row_bytes": self.row_bytes,
+                "glu_ms": self.glu_ms, "glu_launches": self.glu_launches, "glu_flop": self.glu_flop}
 
 
 class PrefillParams(ctypes.Structure):
@@ -75,6 +77,7 @@ SIGNATURES = [
     ("ppx_prune_predicate", c_int, [c_int, c_int, c_int, c_int, POINTER(c_uint8), c_int]),
     ("ppx_op_dequant", c_int, [c_void_p, c_char_p, c_void_p, c_void_p]),
     ("ppx_op_gemm", c_int, [c_void_p, c_char_p, c_void_p, c_int, c_void_p, c_void_p]),
+    ("ppx_op_gemm_glu", c_int, [c_void_p, c_char_p, c_void_p, c_int, c_void_p, c_void_p]),
     ("ppx_op_gemm_exact", c_int, [c_void_p, c_char_p, c_void_p, c_void_p, c_int, c_void_p, c_void_p]),
     ("ppx_op_gemv", c_int, [c_void_p, c_char_p, c_void_p, c_void_p, c_void_p]),
     ("ppx_op_attention", c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p,
@@ -216,6 +219,18 @@ class Model:
         c = torch.empty((a.shape[0], rows), dtype=torch.float32, device="cuda")
         _check(lib().ppx_op_gemm(self._h, name.encode(), _ptr(a), a.shape[0], _ptr(c), _stream()), "ppx_op_gemm")
         return c
+
+    def op_gemm_glu(self, name: str, a, out=None):
+        """act(A Wg^T) * (A Wu^T) -> fp16 [M][F] for a fused gate|up tensor name."""
+        import torch
+        rows, cols = self._shape(name)
+        assert a.dtype == torch.float16 and a.is_contiguous() and a.shape[1] == cols
+        if out is None:
+            out = torch.empty((a.shape[0], rows // 2), dtype=torch.float16, device="cuda")
+        assert out.dtype == torch.float16 and out.is_contiguous() and out.shape == (a.shape[0], rows // 2)
+        _check(lib().ppx_op_gemm_glu(self._h, name.encode(), _ptr(a), a.shape[0], _ptr(out), _stream()),
+               "ppx_op_gemm_glu")
+        return out
 
     def op_gemm_exact(self, name: str, a_hi, a_lo):
         import torch

@@ -76,7 +76,7 @@ struct Ctx {
     uint8_t *ws;
     WsLayout L;
     ppx_timing *tm = nullptr;  // per-phase timing requested
-    struct Rec { int phase; hipEvent_t a, b; };
+    struct Rec { int phase; hipEvent_t a, b; bool glu; };
     std::vector<Rec> recs;
     size_t next_ev = 0;
     template <typename T>
@@ -96,12 +96,12 @@ struct Ctx {
         if (e) (void)hipEventRecord(e, s);
         return e;
     }
-    void end(int phase, hipEvent_t a) {
+    void end(int phase, hipEvent_t a, bool glu = false) {
         if (!tm || !a) return;
         hipEvent_t b = event();
         if (!b) return;
         (void)hipEventRecord(b, s);
-        recs.push_back({phase, a, b});
+        recs.push_back({phase, a, b, glu});
     }
     int finish() {
         if (!tm) return PPX_OK;
@@ -111,6 +111,10 @@ struct Ctx {
             if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return PPX_E_HIP;
             tm->ms[r.phase] += ms;
             tm->launches[r.phase] += 1;
+            if (r.glu) {
+                tm->glu_ms += ms;
+                tm->glu_launches += 1;
+            }
         }
         return PPX_OK;
     }
@@ -204,7 +208,11 @@ int layer_rows(Ctx &c, int il, int M, int row0, int pos0) {
     gu.epi = EPI_GLU;
     gu.out_f16 = h16;
     gu.act = I.act;
-    PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm(gu, c.s));
+    {
+        hipEvent_t ev0 = c.begin();
+        PPX_TRY(launch_gemm(gu, c.s));
+        c.end(PPX_PHASE_GEMM, ev0, true);
+    }
 
     GemmArgs gd;
     gd.A = h16;
@@ -247,6 +255,7 @@ int layer_rows(Ctx &c, int il, int M, int row0, int pos0) {
         if (w.own) nk += (double)w.wkv.N * w.wkv.K;
         if (I.ple_dim) nk += (double)w.wpg.N * w.wpg.K + (double)w.wpu.N * w.wpu.K;
         c.tm->gemm_flop += 2.0 * M * nk;
+        c.tm->glu_flop += 2.0 * M * w.wgu.N * w.wgu.K;
         const double vis = (double)M * pos0 + 0.5 * (double)M * (M + 1);  // causal (query, key) pairs
         c.tm->attn_flop += 4.0 * I.n_head * hd * vis;
     }
@@ -635,6 +644,22 @@ int ppx_op_gemm(const ppx_model *m, const char *tensor, const void *a_dev_f16, i
     g.W = *w;
     g.epi = EPI_F32;
     g.out_f32 = c_dev;
+    return launch_gemm(g, (hipStream_t)hip_stream);
+}
+
+int ppx_op_gemm_glu(const ppx_model *m, const char *tensor, const void *a_dev_f16, int M, void *h_dev_f16,
+                    void *hip_stream) {
+    int kind;
+    const Q4R *w = find_q4(m, tensor, &kind);
+    if (!w || kind != 2 || !a_dev_f16 || !h_dev_f16 || M < 0) return PPX_E_INVAL;
+    GemmArgs g;
+    g.A = static_cast<const __half *>(a_dev_f16);
+    g.lda = w->K;
+    g.M = M;
+    g.W = *w;
+    g.epi = EPI_GLU;
+    g.out_f16 = static_cast<__half *>(h_dev_f16);
+    g.act = m->info.act;
     return launch_gemm(g, (hipStream_t)hip_stream);
 }
 

@@ -90,6 +90,39 @@ def test_gemm_vs_oracle(ppx, cfg, M):
         assert np.all(err <= bound), (name, float((err / bound).max()))
 
 
+@pytest.mark.parametrize("cfg,M,layer", [("tiny", 64, 3), ("tiny", 9, 0), ("tinyllama", 512, 21), ("tinyllama", 131, 4),
+                                         ("e2b", 512, 14), ("e2b", 333, 30)])
+def test_gemm_glu_vs_oracle(ppx, cfg, M, layer):
+    """Fused gate|up GEMM + activation: g and u carry the GEMM bound
+    e = 1e-3 sum|a w| each; the activation's slope is below 1.2 for both GeGLU
+    and SiLU; the fp16 output adds half an ulp:
+    |h - h64| <= 1.2 |u| e_g + (|act(g)| + 1.2 e_g) e_u + ulp16(h64)/2."""
+    from tests.gpu_common import ulp16
+    mm = engine_model(ppx, cfg)
+    om = oracle_model(cfg)
+    rng = np.random.default_rng(1000 + M)
+    p = f"blk.{layer}."
+    Wg, Wu = om.q4(p + "ffn_gate"), om.q4(p + "ffn_up")
+    a = rng.standard_normal((M, Wg.shape[1])).astype(np.float16)
+    h = mm.op_gemm_glu(p + "ffn_gate", torch.from_numpy(a).cuda()).cpu().numpy().astype(np.float64)
+    a64 = a.astype(np.float64)
+    g, u = a64 @ Wg.T, a64 @ Wu.T
+    act = oracle.gelu_tanh(g) if om.act == 0 else oracle.silu(g)
+    ref = act * u
+    eg = 1e-3 * (np.abs(a64) @ np.abs(Wg).T) + 1e-6
+    eu = 1e-3 * (np.abs(a64) @ np.abs(Wu).T) + 1e-6
+    bound = 1.2 * np.abs(u) * eg + (np.abs(act) + 1.2 * eg) * eu + 0.5 * ulp16(ref)
+    err = np.abs(h - ref)
+    assert np.all(err <= bound), float((err / bound).max())
+
+
+def test_gemm_glu_rejects_plain_tensor(ppx):
+    mm = engine_model(ppx, "tiny")
+    a = torch.zeros((4, 256), dtype=torch.float16, device="cuda")
+    with pytest.raises(ppx.PPXError):
+        mm.op_gemm_glu("blk.0.wq", a, out=torch.empty((4, 128), dtype=torch.float16, device="cuda"))
+
+
 @pytest.mark.parametrize("cfg,M", [("tiny", 64), ("tiny", 5), ("tinyllama", 512), ("e2b", 512), ("e2b", 77)])
 def test_gemm_exact_vs_oracle(ppx, cfg, M):
     """K|V projection path: exact weights, split fp16 activations; only fp32
