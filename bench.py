@@ -127,15 +127,15 @@ def glu_kernel_us(mm, ub, reps=50, warmup=5):
     import torch
     I = mm.info
     g = torch.Generator(device="cuda").manual_seed(7)
-    a = torch.randn((ub, I["d_model"]), generator=g, device="cuda").to(torch.float16)
-    h = torch.empty((ub, I["n_ff"]), dtype=torch.float16, device="cuda")
+    a = mm.tile(torch.randn((ub, I["d_model"]), generator=g, device="cuda").to(torch.float16))
+    h = torch.empty(((ub + 15) // 16 * 16) * I["n_ff"], dtype=torch.float16, device="cuda")
     for _ in range(warmup):
-        mm.op_gemm_glu("blk.0.ffn_gate", a, out=h)
+        mm.op_gemm_glu("blk.0.ffn_gate", a, M=ub, out=h, raw=True)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
     for _ in range(reps):
-        mm.op_gemm_glu("blk.0.ffn_gate", a, out=h)
+        mm.op_gemm_glu("blk.0.ffn_gate", a, M=ub, out=h, raw=True)
     t1.record()
     t1.synchronize()
     return t0.elapsed_time(t1) * 1e3 / reps, reps

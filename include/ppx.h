@@ -104,7 +104,8 @@ typedef struct {
  * during the call only.  Weights are repacked for the kernels and uploaded
  * into device memory the library allocates (freed by ppx_model_free).
  * Errors: PPX_E_FORMAT (bad container), PPX_E_UNSUPPORTED (a dimension the
- * kernels cannot tile: d_model, q_dim, n_ff, ple_dim not multiples of 64,
+ * kernels cannot tile: d_model, q_dim, ple_dim not multiples of 128, n_ff
+ * not a multiple of 64,
  * head_dim not 64/128/256, n_head not a multiple of n_kv_head), PPX_E_HIP. */
 int ppx_model_load(const void *container, size_t bytes, void *hip_stream, ppx_model **out);
 /* Same, reading the container from a file (PPX_E_IO if it cannot be read). */
@@ -187,26 +188,38 @@ int ppx_prune_predicate(int n_layer, int n_layer_kv_from_start, int embeddings, 
  * addressed by their first member: "blk.3.wq" = Q rows in RoPE-pair order
  * (16-row blocks alternate the two halves of each head), "blk.3.wk" = K
  * rows in that order followed by V rows (owning layers), "blk.3.ffn_gate" =
- * gate|up with 16-row blocks alternating gate and up. */
+ * gate|up with 16-row blocks alternating gate and up.
+ *
+ * fp16 activations that feed a GEMM (and the prefill attention's output)
+ * use the engine's fragment-tiled layout: A[M][K] is cut into 16-row x
+ * 32-column tiles of 1 KB stored tile-row-major, and inside a tile element
+ * (r, k) sits at lane * 8 + k % 8 with lane = r % 16 + 16 * ((k % 32) / 8).
+ * A tiled [M][K] buffer holds ceil(M/16)*16 rows; ppx_op_tile_f16 converts
+ * from row-major. */
+
+/* Row-major fp16 [M][K] -> fragment-tiled (K % 32 == 0); dst holds
+ * ceil(M/16)*16 rows, of which the padding rows are left untouched. */
+int ppx_op_tile_f16(const void *src_dev, int M, int K, void *dst_dev, void *hip_stream);
 
 /* Dequantise a whole Q4_0 tensor from the engine's repacked device layout
  * into fp32 [rows][cols] row-major (exact). */
 int ppx_op_dequant(const ppx_model *m, const char *tensor, float *out_dev, void *hip_stream);
-/* C[M][N] (fp32, ldc = N) = A[M][K] (fp16, lda = K) x W^T on the MFMA GEMM
- * path, W = the named container tensor [N][K]. */
+/* C[M][N] (fp32, ldc = N) = A[M][K] (fp16, fragment-tiled) x W^T on the
+ * MFMA GEMM path, W = the named container tensor [N][K]. */
 int ppx_op_gemm(const ppx_model *m, const char *tensor, const void *a_dev_f16, int M, float *c_dev,
                 void *hip_stream);
 /* The gate|up GEMM of a layer with its fused activation epilogue, exactly
  * as the prefill runs it for the row-batched layers (the GeGLU feed-forward
  * of the Gemma-style decoder of "llama.cpp Gemma 4 prefill KV graph
  * optimization"; SwiGLU for a model whose activation is SwiGLU):
- * h[M][F] (fp16, ld = F) = act(A Wg^T) * (A Wu^T),
- * A fp16 [M][K].  `tensor` must be a fused gate|up name ("blk.i.ffn_gate");
+ * h[M][F] (fp16, fragment-tiled) = act(A Wg^T) * (A Wu^T), A fp16 [M][K]
+ * fragment-tiled.  `tensor` must be a fused gate|up name ("blk.i.ffn_gate");
  * PPX_E_INVAL otherwise.  Asynchronous on the stream. */
 int ppx_op_gemm_glu(const ppx_model *m, const char *tensor, const void *a_dev_f16, int M, void *h_dev_f16,
                     void *hip_stream);
 /* The same on the exact-weight path used for the fused K|V weight
- * ("blk.i.wk", owning layers): A = a_hi + a_lo (two fp16 [M][K] arrays),
+ * ("blk.i.wk", owning layers): A = a_hi + a_lo (two fp16 [M][K] arrays,
+ * fragment-tiled),
  * weights (code - 8) exactly with the fp32 block scale applied per 32-block. */
 int ppx_op_gemm_exact(const ppx_model *m, const char *tensor, const void *a_hi, const void *a_lo, int M,
                       float *c_dev, void *hip_stream);
@@ -216,7 +229,8 @@ int ppx_op_gemv(const ppx_model *m, const char *tensor, const float *x_dev, floa
 /* Causal prefill attention: q fp16 [M][n_head][head_dim] at positions
  * pos0..pos0+M-1 over k fp16 [>= pos0+M][n_kv_head][head_dim] and the values
  * in the cache's transposed layout, vt fp16 [n_kv_head][head_dim][vld]
- * (vld a multiple of 64, >= pos0+M); o fp16 [M][n_head*head_dim].  ws_dev is
+ * (vld a multiple of 64, >= pos0+M); o fp16 [M][n_head*head_dim]
+ * fragment-tiled (the O projection's operand).  ws_dev is
  * scratch of ppx_workspace_bytes(m, M, pos0+M) bytes (1 <= M <= PPX_MAX_UBATCH). */
 int ppx_op_attention(const ppx_model *m, const void *q_dev, const void *k_dev, const void *vt_dev,
                      int vld, int M, int pos0, void *o_dev, void *ws_dev, size_t ws_bytes, void *hip_stream);

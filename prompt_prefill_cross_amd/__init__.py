@@ -76,6 +76,7 @@ SIGNATURES = [
                             c_void_p, c_void_p]),
     ("ppx_prune_predicate", c_int, [c_int, c_int, c_int, c_int, POINTER(c_uint8), c_int]),
     ("ppx_op_dequant", c_int, [c_void_p, c_char_p, c_void_p, c_void_p]),
+    ("ppx_op_tile_f16", c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p]),
     ("ppx_op_gemm", c_int, [c_void_p, c_char_p, c_void_p, c_int, c_void_p, c_void_p]),
     ("ppx_op_gemm_glu", c_int, [c_void_p, c_char_p, c_void_p, c_int, c_void_p, c_void_p]),
     ("ppx_op_gemm_exact", c_int, [c_void_p, c_char_p, c_void_p, c_void_p, c_int, c_void_p, c_void_p]),
@@ -212,33 +213,59 @@ class Model:
         _check(lib().ppx_op_dequant(self._h, name.encode(), _ptr(out), _stream()), "ppx_op_dequant")
         return out
 
+    # fp16 GEMM operands travel in the engine's fragment-tiled layout (see
+    # include/ppx.h); these helpers convert on the device.
+    @staticmethod
+    def untile(t, M: int, K: int):
+        """fragment-tiled fp16 buffer -> row-major [M][K] (a torch view + copy)."""
+        Mp = (M + 15) // 16 * 16
+        return t[:Mp * K].view(Mp // 16, K // 32, 4, 16, 8).permute(0, 3, 1, 2, 4).reshape(Mp, K)[:M]
+
+    def tile(self, a):
+        """row-major fp16 [M][K] (device) -> fragment-tiled buffer of ceil(M/16)*16 rows."""
+        import torch
+        assert a.dtype == torch.float16 and a.is_contiguous() and a.dim() == 2
+        M, K = a.shape
+        t = torch.zeros(((M + 15) // 16 * 16) * K, dtype=torch.float16, device="cuda")
+        _check(lib().ppx_op_tile_f16(_ptr(a), M, K, _ptr(t), _stream()), "ppx_op_tile_f16")
+        return t
+
     def op_gemm(self, name: str, a):
+        """C = A W^T (fp32 [M][N]) for row-major fp16 A [M][K]."""
         import torch
         rows, cols = self._shape(name)
-        assert a.dtype == torch.float16 and a.is_contiguous() and a.shape[1] == cols
+        assert a.shape[1] == cols
         c = torch.empty((a.shape[0], rows), dtype=torch.float32, device="cuda")
-        _check(lib().ppx_op_gemm(self._h, name.encode(), _ptr(a), a.shape[0], _ptr(c), _stream()), "ppx_op_gemm")
+        at = self.tile(a)  # kept alive until the launch is queued
+        _check(lib().ppx_op_gemm(self._h, name.encode(), _ptr(at), a.shape[0], _ptr(c), _stream()), "ppx_op_gemm")
         return c
 
-    def op_gemm_glu(self, name: str, a, out=None):
-        """act(A Wg^T) * (A Wu^T) -> fp16 [M][F] for a fused gate|up tensor name."""
+    def op_gemm_glu(self, name: str, a, M: int = None, out=None, raw: bool = False):
+        """act(A Wg^T) * (A Wu^T) for a fused gate|up tensor name.  `a` is
+        row-major fp16 [M][K], or (with M given) an already tiled buffer; the
+        result is row-major fp16 [M][F], or the tiled buffer itself if raw."""
         import torch
         rows, cols = self._shape(name)
-        assert a.dtype == torch.float16 and a.is_contiguous() and a.shape[1] == cols
+        F = rows // 2
+        if M is None:
+            assert a.shape[1] == cols
+            M = a.shape[0]
+            a = self.tile(a)
+        Mp = (M + 15) // 16 * 16
         if out is None:
-            out = torch.empty((a.shape[0], rows // 2), dtype=torch.float16, device="cuda")
-        assert out.dtype == torch.float16 and out.is_contiguous() and out.shape == (a.shape[0], rows // 2)
-        _check(lib().ppx_op_gemm_glu(self._h, name.encode(), _ptr(a), a.shape[0], _ptr(out), _stream()),
-               "ppx_op_gemm_glu")
-        return out
+            out = torch.empty(Mp * F, dtype=torch.float16, device="cuda")
+        assert out.dtype == torch.float16 and out.numel() >= Mp * F
+        _check(lib().ppx_op_gemm_glu(self._h, name.encode(), _ptr(a), M, _ptr(out), _stream()), "ppx_op_gemm_glu")
+        return out if raw else self.untile(out, M, F)
 
     def op_gemm_exact(self, name: str, a_hi, a_lo):
         import torch
         rows, cols = self._shape(name)
         assert a_hi.dtype == torch.float16 and a_lo.dtype == torch.float16 and a_hi.shape == a_lo.shape
-        assert a_hi.shape[1] == cols and a_hi.is_contiguous() and a_lo.is_contiguous()
+        assert a_hi.shape[1] == cols
         c = torch.empty((a_hi.shape[0], rows), dtype=torch.float32, device="cuda")
-        _check(lib().ppx_op_gemm_exact(self._h, name.encode(), _ptr(a_hi), _ptr(a_lo), a_hi.shape[0], _ptr(c),
+        th, tl = self.tile(a_hi), self.tile(a_lo)  # both alive until the launch is queued
+        _check(lib().ppx_op_gemm_exact(self._h, name.encode(), _ptr(th), _ptr(tl), a_hi.shape[0], _ptr(c),
                                        _stream()), "ppx_op_gemm_exact")
         return c
 
@@ -266,12 +293,12 @@ class Model:
         H, hd = self.info["n_head"], self.info["head_dim"]
         M = q.shape[0]
         vt, vld = self._vt(v)
-        o = torch.empty((M, H * hd), dtype=torch.float16, device="cuda")
+        o = torch.empty(((M + 15) // 16 * 16) * H * hd, dtype=torch.float16, device="cuda")
         need = lib().ppx_workspace_bytes(self._h, M, pos0 + M)
         ws = torch.empty(need, dtype=torch.uint8, device="cuda")
         _check(lib().ppx_op_attention(self._h, _ptr(q), _ptr(k), _ptr(vt), vld, M, pos0, _ptr(o), _ptr(ws), need,
                                       _stream()), "ppx_op_attention")
-        return o
+        return self.untile(o, M, H * hd)
 
     def op_attention_1row(self, q, k, v, pos: int):
         import torch

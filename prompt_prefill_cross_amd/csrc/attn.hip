@@ -169,12 +169,14 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnArgs a) {
     if (!valid) return;
     if (a.nkc == 1) {
         const float inv = 1.0f / lrun;
-        __half *o = a.o + ((size_t)t * a.H + h) * HD;
+        const int od = a.H * HD;
 #pragma unroll
         for (int i = 0; i < DT; ++i) {
-            const int d = i * 16 + lg * 4;
+            const int d = i * 16 + lg * 4;  // four consecutive columns: 8 contiguous bytes of the tiled layout
+            h4 v;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) o[d + r] = __float2half(oacc[i][r] * inv);
+            for (int r = 0; r < 4; ++r) v[r] = (_Float16)(oacc[i][r] * inv);
+            *reinterpret_cast<h4 *>(a.o + tiled_index(t, h * HD + d, od)) = v;
         }
     } else {
         const size_t slot = ((size_t)ck * a.M + t) * a.H + h;
@@ -205,7 +207,7 @@ __global__ __launch_bounds__(HD) void k_attn_prefill_merge(AttnArgs a) {
         L += w * pm[slot * 2 + 1];
         O += w * a.part[slot * HD + d];
     }
-    a.o[((size_t)t * a.H + h) * HD + d] = __float2half(O / L);
+    a.o[tiled_index(t, h * HD + d, a.H * HD)] = __float2half(O / L);
 }
 
 // ------------------------------------------------------------------ single query

@@ -43,14 +43,15 @@ WsLayout ws_layout(const ppx_model *m, int ub, int n_ctx) {
         o += al(bytes);
         return r;
     };
+    const size_t ub16 = (size_t)(ub + 15) / 16 * 16;  // fragment-tiled buffers hold whole 16-row tiles
     w.tok = take(sizeof(int32_t) * (size_t)std::max(n_ctx, 1));
     w.x = take(4ull * ub * d);
-    w.a16 = take(2ull * ub * std::max(d, 1));
-    w.a16lo = take(2ull * ub * std::max(d, 1));
+    w.a16 = take(2ull * ub16 * std::max(d, 1));
+    w.a16lo = take(2ull * ub16 * std::max(d, 1));
     w.q16 = take(2ull * ub * qd);
-    w.o16 = take(2ull * ub * qd);
-    w.h16 = take(2ull * ub * F);
-    w.p16 = take(2ull * ub * std::max(E, 1));
+    w.o16 = take(2ull * ub16 * qd);
+    w.h16 = take(2ull * ub16 * F);
+    w.p16 = take(2ull * ub16 * std::max(E, 1));
     w.xr = take(4ull * d);
     w.ar = take(4ull * d);
     w.qr = take(4ull * qd);
@@ -661,6 +662,12 @@ int ppx_op_gemm_glu(const ppx_model *m, const char *tensor, const void *a_dev_f1
     g.out_f16 = static_cast<__half *>(h_dev_f16);
     g.act = m->info.act;
     return launch_gemm(g, (hipStream_t)hip_stream);
+}
+
+int ppx_op_tile_f16(const void *src_dev, int M, int K, void *dst_dev, void *hip_stream) {
+    if (!src_dev || !dst_dev || M < 0 || K <= 0) return PPX_E_INVAL;
+    return launch_tile_f16(static_cast<const __half *>(src_dev), M, K, static_cast<__half *>(dst_dev),
+                           (hipStream_t)hip_stream);
 }
 
 int ppx_op_gemm_exact(const ppx_model *m, const char *tensor, const void *a_hi, const void *a_lo, int M,

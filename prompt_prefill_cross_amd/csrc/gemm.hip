@@ -1,234 +1,103 @@
 // Q4_0 dequant-fused GEMM on CDNA4 MFMA (v_mfma_f32_16x16x32_f16).
 //
-//   C[M][N] = A[M][K] (fp16 activations) x W[N][K]^T (Q4_0), fp32 accumulate.
+//   C[M][N] = A[M][K] (fp16 activations, fragment-tiled) x W[N][K]^T (Q4_0),
+//   fp32 accumulate, with the layer's elementwise work fused into the epilogue.
 //
-// A workgroup of WGM x WGN waves computes a BM x BN tile, each wave a
-// (BM/WGM) x (BN/WGN) block of 16x16 MFMA tiles.  K advances 64 (two Q4_0
-// blocks) per stage through two LDS buffers; global loads run two stages ahead
-// of the MFMAs (two register sets, the loop unrolled by two), so a stage's
-// memory latency overlaps two stages of matrix work.  A is staged as fp16 in
-// the MFMA A fragment order -- one wave store fills one 1 KB fragment, lane by
-// lane -- and W is read as repacked codes + fp16 block scales, decoded in
-// registers and written to LDS in B fragment order, so a tile's weights are
-// decoded once per workgroup.  Epilogues work on the accumulator registers
-// directly; weights whose outputs are combined in pairs (RoPE halves,
-// gate/up) are stored with the two members of a pair in adjacent 16-column
-// groups, so both values of a pair sit in the same lane.
+// A workgroup holds NWN compute waves and one producer wave and computes a
+// BM x BN tile; compute wave w owns columns [w*WN, (w+1)*WN) for all BM rows
+// (TM x TN MFMA tiles of 16 x 16).  Operands reach LDS without passing through
+// registers: the producer wave fills a ring of DEPTH stages, one K step of 64
+// each, with global_load_lds DMA --
+//   * A: 1 KB fragments, contiguous in the fragment-tiled activation layout,
+//     one 16-byte piece per lane straight into A-operand order;
+//   * W: for every compute wave, its columns' repacked Q4_0 codes (16 bytes per
+//     lane = two lanes' words, two 16-column groups per instruction) and fp16
+//     block-scale pairs (4 bytes per lane, four groups per instruction).
+// The producer waits for a stage by counting its own outstanding DMA
+// instructions, then joins the workgroup barrier that hands the stage over;
+// compute waves only read LDS, decode weights in registers (a shift, a mask,
+// an OR with the fp16 exponent of 1024, a subtract and a multiply per pair)
+// and multiply.  Keeping the roles in different waves keeps the compiler from
+// making LDS reads wait on DMA aimed at other stages.
 //
-// Two arithmetic modes share the kernel:
+// Two arithmetic modes:
 //  * fast (EXACT = false): B = fp16(d * (code - 8)), one rounding per weight;
-//  * exact (EXACT = true): B = code - 8 (exact in fp16), A = hi + lo split in
-//    two fp16 operands, and each 32-wide block's partial sum is scaled by its
-//    fp32 block scale before it is added -- only fp32 accumulation rounds.
-//    The K and V projections use it, so the cache holds values accurate to
-//    the fp16 store itself.
+//  * exact (EXACT = true): B = code - 8 (exact in fp16), A = hi + lo (two
+//    fp16 arrays), each 32-wide block's partial scaled by its fp32 block scale
+//    before it is added -- only fp32 accumulation rounds.  The K|V projection
+//    uses it, so the cache holds values accurate to the fp16 store itself.
 #include "ppx_dev.h"
 
 namespace ppx {
 
 namespace {
 
-constexpr int KSTEP = 64;
+typedef __attribute__((address_space(3))) void lds_t;
 
-template <int BM_, int BN_, int WGM_, int WGN_, bool EXACT_>
+// DMA of 16 / 4 bytes per lane from global memory to LDS; lane l's bytes land
+// at dst + size * l (dst is wave-uniform).
+__device__ __forceinline__ void dma16(const void *src, h8 *dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_t *)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *src, h8 *dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_t *)dst, 4, 0, 0);
+}
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }
+
+// Workgroup barrier without the memory fences of __syncthreads (which would
+// drain every outstanding DMA); the empty asm statements keep memory accesses
+// on their side of it in the compiler.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N), expcnt and lgkmcnt untouched.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+}
+
+template <int TM_, int TN_, int NWN_, int DEPTH_, bool EXACT_>
 struct Cfg {
-    static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
+    static constexpr int TM = TM_, TN = TN_, NWN = NWN_, DEPTH = DEPTH_;
     static constexpr bool EXACT = EXACT_;
-    static constexpr int NT = 64 * WGM * WGN;            // threads
-    static constexpr int WM = BM / WGM, WN = BN / WGN;  // wave tile
-    static constexpr int TM = WM / 16, TN = WN / 16;
-    static constexpr int A_UNITS = 2 * (BM / 16) * 64;   // 16-byte units per stage, per A part
-    static constexpr int B_UNITS = 2 * (BN / 16) * 64;
-    static constexpr int NA = EXACT ? 2 : 1;             // A parts staged
-    static constexpr int S_FLOATS = EXACT ? 2 * BN : 0;  // block scales per stage
-    static constexpr int STAGE_UNITS = NA * A_UNITS + B_UNITS + S_FLOATS / 4;
-    static constexpr int A_LOADS = A_UNITS / NT;         // per thread, per part
-    static constexpr int B_SLOTS = (BN / 16) * 64 / NT;  // lane slots per thread
-    static_assert(TM >= 1 && TN >= 2 && TN % 2 == 0, "wave tile");
-    static_assert(A_UNITS % NT == 0 && A_LOADS >= 1, "A staging");
-    static_assert((BN / 16) * 64 % NT == 0 && B_SLOTS >= 1, "B staging");
+    static constexpr int NT = 64 * (NWN + 1);
+    static constexpr int BM = 16 * TM, WN = 16 * TN, BN = NWN * WN;
+    static constexpr int NA = EXACT ? 2 : 1;              // A parts (hi, lo)
+    static constexpr int AFR = 2 * TM * NA;                // 1 KB A fragments per stage
+    static constexpr int CPW = TN / 2;                     // code DMAs per compute wave
+    static constexpr int SPW = (TN + 3) / 4;               // scale DMAs per compute wave
+    static constexpr int DMAS = AFR + NWN * (CPW + SPW);   // producer instructions per stage
+    // LDS, in 16-byte units
+    static constexpr int A_UNITS = AFR * 64;
+    static constexpr int C_UNITS = TN * 32;                // codes: 512 B per group
+    static constexpr int S_UNITS = SPW * 16;               // scales: 256 B per four groups
+    static constexpr int W_UNITS = C_UNITS + S_UNITS;
+    static constexpr int STAGE_UNITS = A_UNITS + NWN * W_UNITS;
+    static_assert(TN % 2 == 0 && TN >= 2 && TN <= 4, "wave tile columns");
+    static_assert(DEPTH >= 2 && (DEPTH - 2) * DMAS <= 63, "vmcnt range");
+    static_assert(DEPTH * STAGE_UNITS * 16 <= 160 * 1024, "LDS");
 };
 
-// One stage of operands held in registers between its global load and its LDS store.
-template <class C>
-struct Stage {
-    h8 ar[C::NA][C::A_LOADS];
-    uint2 br[C::B_SLOTS];
-    uint32_t sr[C::B_SLOTS];
-
-    // Loads are branch-free (rows past M are clamped, then zeroed by a select),
-    // so the compiler can count outstanding loads exactly and keep the next
-    // stage's loads in flight across this stage's store.
-    __device__ __forceinline__ void load(const GemmArgs &a, int m0, int n0, int kc) {
-        const int tid = threadIdx.x;
-#pragma unroll
-        for (int i = 0; i < C::A_LOADS; ++i) {
-            // unit u = [kb][16-row subtile][lane]; lane l holds row 16*sub + l%16, k = 32*kb + 8*(l/16)
-            const int u = tid + i * C::NT;
-            const int kb = u / ((C::BM / 16) * 64), rem = u % ((C::BM / 16) * 64);
-            const int row = m0 + (rem >> 6) * 16 + (rem & 15);
-            const unsigned off = (unsigned)(min(row, a.M - 1) * a.lda + kc * KSTEP + kb * 32 + ((rem >> 4) & 3) * 8);
-#pragma unroll
-            for (int p = 0; p < C::NA; ++p) {
-                const __half *src = p ? a.A2 : a.A;
-                ar[p][i] = *reinterpret_cast<const h8 *>(src + off);
-            }
-        }
-        const unsigned kchunks = (unsigned)a.W.K >> 6;
-#pragma unroll
-        for (int i = 0; i < C::B_SLOTS; ++i) {
-            const unsigned sl = tid + i * C::NT;
-            const unsigned grp = sl >> 6, ln = sl & 63;
-            const unsigned base = (((unsigned)n0 >> 4) + grp) * kchunks + kc;
-            br[i] = *reinterpret_cast<const uint2 *>(a.W.nib + (base * 64 + ln) * 2);
-            sr[i] = *reinterpret_cast<const uint32_t *>(a.W.scl + (base * 16 + (ln & 15)) * 2);
-        }
-    }
-
-    __device__ __forceinline__ void store(h8 *lds, int m0, int M) const {
-        const int tid = threadIdx.x;
-        if (m0 + C::BM <= M) {  // uniform: the whole tile is inside the matrix
-#pragma unroll
-            for (int i = 0; i < C::A_LOADS; ++i)
-#pragma unroll
-                for (int p = 0; p < C::NA; ++p) lds[p * C::A_UNITS + tid + i * C::NT] = ar[p][i];
-        } else {
-#pragma unroll
-            for (int i = 0; i < C::A_LOADS; ++i) {
-                const int rem = (tid + i * C::NT) % ((C::BM / 16) * 64);
-                const bool valid = m0 + (rem >> 6) * 16 + (rem & 15) < M;  // rows past M were clamped
-#pragma unroll
-                for (int p = 0; p < C::NA; ++p)
-                    lds[p * C::A_UNITS + tid + i * C::NT] = valid ? ar[p][i] : h8{0, 0, 0, 0, 0, 0, 0, 0};
-            }
-        }
-        h8 *lb = lds + C::NA * C::A_UNITS;
-        float *ls = reinterpret_cast<float *>(lb + C::B_UNITS);
-#pragma unroll
-        for (int i = 0; i < C::B_SLOTS; ++i) {
-            const int sl = tid + i * C::NT;
-            const int grp = sl >> 6, ln = sl & 63;
-            const h2 d2 = __builtin_bit_cast(h2, sr[i]);
-            if constexpr (C::EXACT) {
-                lb[0 * (C::BN / 16) * 64 + grp * 64 + ln] = q4_word_codes(br[i].x);
-                lb[1 * (C::BN / 16) * 64 + grp * 64 + ln] = q4_word_codes(br[i].y);
-                if (ln < 16) {
-                    ls[grp * 16 + ln] = (float)d2[0];
-                    ls[C::BN + grp * 16 + ln] = (float)d2[1];
-                }
-            } else {
-                lb[0 * (C::BN / 16) * 64 + grp * 64 + ln] = q4_word_to_h8(br[i].x, d2[0]);
-                lb[1 * (C::BN / 16) * 64 + grp * 64 + ln] = q4_word_to_h8(br[i].y, d2[1]);
-            }
-        }
-    }
-};
-
-// The fragments of one stage, read from LDS before the next stage is stored,
-// so that the MFMAs of this stage overlap the decode and LDS stores of the next.
-template <class C>
-struct Frags {
-    h8 af[2][C::TM], bf[2][C::TN];
-    h8 af2[2][C::EXACT ? C::TM : 1];
-    float dsc[2][C::EXACT ? C::TN : 1];
-
-    __device__ __forceinline__ void read(const h8 *lds, int wm, int wn, int lane) {
-        const h8 *la = lds;
-        const h8 *lb = lds + C::NA * C::A_UNITS;
-        const float *ls = reinterpret_cast<const float *>(lb + C::B_UNITS);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int i = 0; i < C::TM; ++i) af[kb][i] = la[kb * (C::BM / 16) * 64 + ((wm >> 4) + i) * 64 + lane];
-#pragma unroll
-            for (int j = 0; j < C::TN; ++j) bf[kb][j] = lb[kb * (C::BN / 16) * 64 + ((wn >> 4) + j) * 64 + lane];
-            if constexpr (C::EXACT) {
-#pragma unroll
-                for (int i = 0; i < C::TM; ++i)
-                    af2[kb][i] = la[C::A_UNITS + kb * (C::BM / 16) * 64 + ((wm >> 4) + i) * 64 + lane];
-#pragma unroll
-                for (int j = 0; j < C::TN; ++j) dsc[kb][j] = ls[kb * C::BN + wn + j * 16 + (lane & 15)];
-            }
-        }
-    }
-
-    __device__ __forceinline__ void mma(f4 (&acc)[C::TM][C::TN]) const {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            if constexpr (C::EXACT) {
-#pragma unroll
-                for (int j = 0; j < C::TN; ++j)
-#pragma unroll
-                    for (int i = 0; i < C::TM; ++i) {
-                        f4 p = mfma16(af[kb][i], bf[kb][j], f4{0.f, 0.f, 0.f, 0.f});
-                        p = mfma16(af2[kb][i], bf[kb][j], p);
-                        acc[i][j] += dsc[kb][j] * p;
-                    }
-            } else {
-#pragma unroll
-                for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma16(af[kb][i], bf[kb][j], acc[i][j]);
-            }
-        }
-    }
-};
-
-template <class C>
-__global__ __launch_bounds__(C::NT) void k_q4gemm(GemmArgs a) {
-    using S = C;
-    __shared__ h8 lds[2][C::STAGE_UNITS];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n0 = blockIdx.x * C::BN, m0 = blockIdx.y * C::BM;
-    const int wm = (wave / C::WGN) * C::WM, wn = (wave % C::WGN) * C::WN;
+// Epilogue of one wave tile: acc[i][j][r] = C[r0 + 16i + 4(lane/16) + r][c0 + 16j + lane%16].
+template <int TM, int TN>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, const f4 (&acc)[TM][TN], int r0, int c0, int lane) {
     const int lc = lane & 15, lr = (lane >> 4) * 4;
-
-    f4 acc[C::TM][C::TN];
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
-
-    // stage s lives in register set (s % 2) between its load and its store
-    Stage<C> r0, r1;
-    const int nk = a.W.K / KSTEP;
-    // nk is even (K % 128 == 0).  Every load, store and MFMA is unconditional:
-    // past the last stage the load index is clamped and the duplicate lands in
-    // a buffer that is not read again; no branch splits the accumulators'
-    // live ranges, so they stay in place across iterations.
-    const int last = nk - 1;
-    r0.load(a, m0, n0, 0);
-    r0.store(lds[0], m0, a.M);
-    r1.load(a, m0, n0, 1);
-    r0.load(a, m0, n0, min(2, last));
-    __syncthreads();
-    Frags<C> f;
-    for (int kc = 0; kc < nk; kc += 2) {
-        f.read(lds[0], wm, wn, lane);  // stage kc
-        r1.store(lds[1], m0, a.M);     // stage kc + 1 (lds[1] was last read before the previous barrier)
-        f.mma(acc);
-        __syncthreads();
-        r1.load(a, m0, n0, min(kc + 3, last));
-        f.read(lds[1], wm, wn, lane);  // stage kc + 1
-        r0.store(lds[0], m0, a.M);     // stage kc + 2
-        f.mma(acc);
-        __syncthreads();
-        r0.load(a, m0, n0, min(kc + 4, last));
-    }
-
-    // ---------------------------------------------------------------- epilogue
-    // acc[i][j][r] = C[row][col], row = m0+wm+16i+4*(lane/16)+r, col = n0+wn+16j+lane%16
     const int N = a.W.N;
     if (a.epi == EPI_F32 || a.epi == EPI_ADD) {
 #pragma unroll
-        for (int i = 0; i < S::TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < S::TN; ++j)
+            for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int row = m0 + wm + i * 16 + lr + r;
-                    const int col = n0 + wn + j * 16 + lc;
+                    const int row = r0 + i * 16 + lr + r;
+                    const int col = c0 + j * 16 + lc;
                     if (row < a.M) {
                         float *p = a.out_f32 + (size_t)row * N + col;
                         if (a.epi == EPI_ADD) *p += acc[i][j][r];
@@ -236,37 +105,40 @@ __global__ __launch_bounds__(C::NT) void k_q4gemm(GemmArgs a) {
                     }
                 }
     } else if (a.epi == EPI_PLE) {
+        // gelu(C) * s * deq(ple_table[token][il*E + col]) -> fp16, fragment-tiled [M][E]
         const int E = N;
 #pragma unroll
-        for (int i = 0; i < S::TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = m0 + wm + i * 16 + lr + r;
+                const int row = r0 + i * 16 + lr + r;
                 if (row >= a.M) continue;
                 const uint8_t *prow = a.ple_raw + (size_t)a.tok[row] * a.ple_row_blocks * 18;
 #pragma unroll
-                for (int j = 0; j < S::TN; ++j) {
-                    const int col = n0 + wn + j * 16 + lc;
+                for (int j = 0; j < TN; ++j) {
+                    const int col = c0 + j * 16 + lc;
                     const float P = a.ple_s * q4_raw_weight(prow, a.ple_col0 + col);
-                    a.out_f16[(size_t)row * E + col] = (_Float16)(gelu_tanh_f(acc[i][j][r]) * P);
+                    a.out_f16[tiled_index(row, col, E)] = (_Float16)(gelu_tanh_f(acc[i][j][r]) * P);
                 }
             }
     } else {
-        // paired epilogues: subtiles (2p, 2p+1) of the wave tile
+        // paired epilogues: 16-column groups (2p, 2p+1) of the wave tile hold the
+        // two members of a pair (gate, up) or (first, second RoPE half)
 #pragma unroll
-        for (int p = 0; p < S::TN / 2; ++p) {
-            const int colA = n0 + wn + p * 32 + lc;  // first member; second = colA + 16
+        for (int p = 0; p < TN / 2; ++p) {
+            const int colA = c0 + p * 32 + lc;  // first member; second = colA + 16
 #pragma unroll
-            for (int i = 0; i < S::TM; ++i)
+            for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int row = m0 + wm + i * 16 + lr + r;
+                    const int row = r0 + i * 16 + lr + r;
                     if (row >= a.M) continue;
                     const float va = acc[i][2 * p][r], vb = acc[i][2 * p + 1][r];
                     if (a.epi == EPI_GLU) {
+                        // act(gate) * up -> fp16, fragment-tiled [M][F]
                         const int F = N >> 1;
                         const int f = (colA >> 5) * 16 + lc;
-                        a.out_f16[(size_t)row * F + f] = (_Float16)(act_f(a.act, va) * vb);
+                        a.out_f16[tiled_index(row, f, F)] = (_Float16)(act_f(a.act, va) * vb);
                     } else {  // EPI_QKV: columns [0,qd) Q, [qd,qd+kvd) K, [qd+kvd, qd+2kvd) V
                         const int hd = a.hd, half = hd >> 1;
                         const int pos = a.pos0 + row;
@@ -299,32 +171,155 @@ __global__ __launch_bounds__(C::NT) void k_q4gemm(GemmArgs a) {
 }
 
 template <class C>
+__global__ __launch_bounds__(C::NT) void k_q4gemm(GemmArgs a) {
+    __shared__ h8 ring[C::DEPTH * C::STAGE_UNITS];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id();
+    const int n0 = blockIdx.x * C::BN, m0 = blockIdx.y * C::BM;
+    const int kch = a.W.K >> 6;  // K steps of 64
+    const int ktiles = a.W.K >> 5;
+
+    if (wave == C::NWN) {
+        // ------------------------------------------------------ producer wave
+        // A fragment (part p, kb, i) of stage s: tile row m0/16 + i (clamped to
+        // the last tile row; rows past M are computed and discarded), tile
+        // column 2s + kb; stage layout [p][kb][i] x 1 KB
+        const int last_tr = (a.M - 1) >> 4;
+        const __half *asrc[C::AFR];
+#pragma unroll
+        for (int f = 0; f < C::AFR; ++f) {
+            const int p = f / (2 * C::TM), kb = (f / C::TM) & 1, i = f % C::TM;
+            const int tr = min((m0 >> 4) + i, last_tr);
+            asrc[f] = (p ? a.A2 : a.A) + (((size_t)tr * ktiles + kb) * 64 + lane) * 8;
+        }
+        const uint32_t *csrc[C::NWN][C::CPW];
+        const uint32_t *ssrc[C::NWN][C::SPW];
+#pragma unroll
+        for (int w = 0; w < C::NWN; ++w) {
+            const int g0 = (n0 >> 4) + w * C::TN;
+#pragma unroll
+            for (int p = 0; p < C::CPW; ++p)
+                csrc[w][p] = a.W.nib + ((size_t)(g0 + 2 * p + (lane >> 5)) * kch * 64 + (lane & 31) * 2) * 2;
+#pragma unroll
+            for (int q = 0; q < C::SPW; ++q) {
+                const int j = min(4 * q + (lane >> 4), C::TN - 1);
+                ssrc[w][q] = reinterpret_cast<const uint32_t *>(a.W.scl) + ((size_t)(g0 + j) * kch * 16 + (lane & 15));
+            }
+        }
+        // DMA of stage min(sb, kch-1) into the buffer of stage sb
+        auto issue = [&](int sb) {
+            h8 *st = ring + (sb % C::DEPTH) * C::STAGE_UNITS;
+            const int s = min(sb, kch - 1);
+#pragma unroll
+            for (int f = 0; f < C::AFR; ++f) dma16(asrc[f] + (size_t)s * 1024, st + f * 64);
+#pragma unroll
+            for (int w = 0; w < C::NWN; ++w) {
+                h8 *wst = st + C::A_UNITS + w * C::W_UNITS;
+#pragma unroll
+                for (int p = 0; p < C::CPW; ++p) dma16(csrc[w][p] + (size_t)s * 128, wst + p * 64);
+#pragma unroll
+                for (int q = 0; q < C::SPW; ++q) dma4(ssrc[w][q] + (size_t)s * 16, wst + C::C_UNITS + q * 16);
+            }
+        };
+        // Stages 0 .. DEPTH-2 up front; stage s + DEPTH - 1 right after the
+        // barrier that hands stage s over (every compute wave has then finished
+        // reading stage s - 1, whose buffer it refills).  Past the end the same
+        // number of instructions is issued -- reloads of the last stage into
+        // buffers of stages no one reads again -- so the count stays exact.
+#pragma unroll
+        for (int s = 0; s < C::DEPTH - 1; ++s) issue(s);
+        for (int s = 0; s < kch; ++s) {
+            wait_vm<(C::DEPTH - 2) * C::DMAS>();
+            lds_barrier();
+            issue(s + C::DEPTH - 1);
+        }
+        wait_vm<0>();
+        return;
+    }
+
+    // ---------------------------------------------------------- compute waves
+    f4 acc[C::TM][C::TN];
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+
+    for (int s = 0; s < kch; ++s) {
+        lds_barrier();
+        const h8 *st = ring + (s % C::DEPTH) * C::STAGE_UNITS;
+        const h8 *wst = st + C::A_UNITS + wave * C::W_UNITS;
+        const uint2 *codes = reinterpret_cast<const uint2 *>(wst);
+        const uint32_t *scales = reinterpret_cast<const uint32_t *>(wst + C::C_UNITS);
+        uint2 bw[C::TN];
+        h2 bs[C::TN];
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+            bw[j] = codes[j * 64 + lane];
+            bs[j] = __builtin_bit_cast(h2, scales[j * 16 + (lane & 15)]);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            h8 af[C::TM];
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i) af[i] = st[(kb * C::TM + i) * 64 + lane];
+            if constexpr (C::EXACT) {
+                h8 al[C::TM];
+#pragma unroll
+                for (int i = 0; i < C::TM; ++i) al[i] = st[((2 + kb) * C::TM + i) * 64 + lane];
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j) {
+                    const h8 bq = q4_word_codes(kb ? bw[j].y : bw[j].x);
+                    const float dj = (float)bs[j][kb];
+#pragma unroll
+                    for (int i = 0; i < C::TM; ++i) {
+                        f4 t = mfma16(af[i], bq, f4{0.f, 0.f, 0.f, 0.f});
+                        t = mfma16(al[i], bq, t);
+                        acc[i][j] += dj * t;
+                    }
+                }
+            } else {
+                h8 bf[C::TN];
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j) bf[j] = q4_word_to_h8(kb ? bw[j].y : bw[j].x, bs[j][kb]);
+#pragma unroll
+                for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma16(af[i], bf[j], acc[i][j]);
+            }
+        }
+    }
+    gemm_epilogue<C::TM, C::TN>(a, acc, m0, n0 + wave * C::WN, lane);
+}
+
+template <class C>
 int launch_cfg(const GemmArgs &a, hipStream_t s) {
+    if (a.W.N % C::BN) return PPX_E_UNSUPPORTED;
     dim3 grid(a.W.N / C::BN, (a.M + C::BM - 1) / C::BM);
     hipLaunchKernelGGL((k_q4gemm<C>), grid, dim3(C::NT), 0, s, a);
     return hipGetLastError() == hipSuccess ? PPX_OK : PPX_E_HIP;
 }
 
-long tiles(const GemmArgs &a, int bm, int bn) {
-    return a.W.N % bn ? 0 : (long)(a.W.N / bn) * ((a.M + bm - 1) / bm);
-}
-
 }  // namespace
 
+// Tile shapes measured on the E2B-like shapes at M = 512 (one MI355X):
+//  * wide outputs (gate|up, N >= 8192): 64 x 128 tiles, a three-stage ring
+//    (39 KB of LDS: four workgroups per CU);
+//  * narrow outputs (N <= 512): 32 x 64 tiles with two compute waves, for
+//    enough workgroups;
+//  * the rest (Q, O, down, PLE up): 32 x 128 tiles.
 int launch_gemm(const GemmArgs &a, hipStream_t s) {
     if (a.M <= 0) return PPX_OK;
-    if (a.W.N % 64 || a.W.K % 128 || a.lda % 8 || !a.A) return PPX_E_UNSUPPORTED;
-    // measured on the E2B-like shapes at M = 512: wide outputs (gate|up) run best
-    // as 128x256 tiles of eight 64x64 wave tiles; everything narrower as 64x64
-    // tiles, which give the most workgroups
-    if (a.W.N >= 8192 && tiles(a, 128, 256) >= 128) return launch_cfg<Cfg<128, 256, 2, 4, false>>(a, s);
-    return launch_cfg<Cfg<64, 64, 2, 2, false>>(a, s);
+    if (a.W.N % 128 || a.W.K % 64 || !a.A) return PPX_E_UNSUPPORTED;
+    if (a.W.N >= 8192) return launch_cfg<Cfg<4, 2, 4, 3, false>>(a, s);
+    if (a.W.N <= 512) return launch_cfg<Cfg<2, 2, 2, 4, false>>(a, s);
+    return launch_cfg<Cfg<2, 2, 4, 4, false>>(a, s);
 }
 
 int launch_gemm_exact(const GemmArgs &a, hipStream_t s) {
     if (a.M <= 0) return PPX_OK;
-    if (a.W.N % 64 || a.W.K % 128 || a.lda % 8 || !a.A || !a.A2) return PPX_E_UNSUPPORTED;
-    return launch_cfg<Cfg<64, 64, 2, 2, true>>(a, s);
+    if (a.W.N % 128 || a.W.K % 64 || !a.A || !a.A2) return PPX_E_UNSUPPORTED;
+    return launch_cfg<Cfg<1, 2, 4, 4, true>>(a, s);
 }
 
 }  // namespace ppx

@@ -34,21 +34,62 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float *x, const float *g,
     for (int k = threadIdx.x; k < d; k += 256) o[k] = (T)(xr[k] * r * g[k]);
 }
 
-// y = rmsnorm(x) split into hi = fp16(y) and lo = fp16(y - hi).
-__global__ __launch_bounds__(256) void k_rmsnorm_split(const float *x, const float *g, float eps, int d,
+// y = rmsnorm(x) -> fp16 in the fragment-tiled layout, one wave per row; with
+// LO, also lo = fp16(y - fp16(y)) (the split operand of the exact-weight
+// GEMM).  Lane l handles the 8-column chunks l, l+64, ... of its row, kept in
+// registers between the sum of squares and the scaling.
+constexpr int NORM_MAX_CHUNKS = 8;  // d <= 8 * 8 * 64 = 4096
+template <bool LO>
+__global__ __launch_bounds__(256) void k_rmsnorm_tiled(const float *x, const float *g, float eps, int M, int d,
                                                        __half *hi, __half *lo) {
-    __shared__ float red[4];
-    const float *xr = x + (size_t)blockIdx.x * d;
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;
+    const float *xr = x + (size_t)row * d;
+    const int nch = d >> 3;
+    float4 v[NORM_MAX_CHUNKS][2];
     float ss = 0.f;
-    for (int k = threadIdx.x; k < d; k += 256) ss += xr[k] * xr[k];
-    ss = block_sum_256(ss, red);
+#pragma unroll
+    for (int c = 0; c < NORM_MAX_CHUNKS; ++c) {
+        const int ch = lane + 64 * c;
+        if (ch < nch) {
+            v[c][0] = *reinterpret_cast<const float4 *>(xr + ch * 8);
+            v[c][1] = *reinterpret_cast<const float4 *>(xr + ch * 8 + 4);
+            ss += v[c][0].x * v[c][0].x + v[c][0].y * v[c][0].y + v[c][0].z * v[c][0].z + v[c][0].w * v[c][0].w;
+            ss += v[c][1].x * v[c][1].x + v[c][1].y * v[c][1].y + v[c][1].z * v[c][1].z + v[c][1].w * v[c][1].w;
+        }
+    }
+    ss = wave_sum(ss);
     const float r = 1.0f / sqrtf(ss / (float)d + eps);
-    const size_t o = (size_t)blockIdx.x * d;
-    for (int k = threadIdx.x; k < d; k += 256) {
-        const float y = xr[k] * r * g[k];
-        const __half h = __float2half(y);
-        hi[o + k] = h;
-        lo[o + k] = __float2half(y - __half2float(h));
+#pragma unroll
+    for (int c = 0; c < NORM_MAX_CHUNKS; ++c) {
+        const int ch = lane + 64 * c;
+        if (ch < nch) {
+            const float4 g0 = *reinterpret_cast<const float4 *>(g + ch * 8);
+            const float4 g1 = *reinterpret_cast<const float4 *>(g + ch * 8 + 4);
+            const float y[8] = {v[c][0].x * r * g0.x, v[c][0].y * r * g0.y, v[c][0].z * r * g0.z, v[c][0].w * r * g0.w,
+                                v[c][1].x * r * g1.x, v[c][1].y * r * g1.y, v[c][1].z * r * g1.z, v[c][1].w * r * g1.w};
+            h8 yh, yl;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                yh[e] = (_Float16)y[e];
+                if (LO) yl[e] = (_Float16)(y[e] - (float)yh[e]);
+            }
+            const size_t o = tiled_index(row, ch * 8, d);
+            *reinterpret_cast<h8 *>(hi + o) = yh;
+            if (LO) *reinterpret_cast<h8 *>(lo + o) = yl;
+        }
+    }
+}
+
+// Row-major fp16 [M][K] -> fragment-tiled.
+__global__ void k_tile_f16(const __half *src, int M, int K, __half *dst) {
+    const int nch = K >> 3;
+    const size_t total = (size_t)M * nch;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+        const int r = (int)(i / nch), ch = (int)(i % nch);
+        *reinterpret_cast<h8 *>(dst + tiled_index(r, ch * 8, K)) =
+            *reinterpret_cast<const h8 *>(src + (size_t)r * K + ch * 8);
     }
 }
 
@@ -190,14 +231,25 @@ int launch_embed(const Q4R &tok, const int32_t *ids, int M, float scale, float *
 
 int launch_rmsnorm_f16(const float *x, const float *g, float eps, int M, int d, __half *out, hipStream_t s) {
     if (M <= 0) return PPX_OK;
-    hipLaunchKernelGGL((k_rmsnorm<__half>), dim3(M), dim3(256), 0, s, x, g, eps, d, out);
+    if (d % 32 || d > NORM_MAX_CHUNKS * 8 * 64) return PPX_E_UNSUPPORTED;
+    hipLaunchKernelGGL((k_rmsnorm_tiled<false>), dim3((M + 3) / 4), dim3(256), 0, s, x, g, eps, M, d, out, nullptr);
     return ok();
 }
 
 int launch_rmsnorm_split(const float *x, const float *g, float eps, int M, int d, __half *hi, __half *lo,
                          hipStream_t s) {
     if (M <= 0) return PPX_OK;
-    hipLaunchKernelGGL(k_rmsnorm_split, dim3(M), dim3(256), 0, s, x, g, eps, d, hi, lo);
+    if (d % 32 || d > NORM_MAX_CHUNKS * 8 * 64) return PPX_E_UNSUPPORTED;
+    hipLaunchKernelGGL((k_rmsnorm_tiled<true>), dim3((M + 3) / 4), dim3(256), 0, s, x, g, eps, M, d, hi, lo);
+    return ok();
+}
+
+int launch_tile_f16(const __half *src, int M, int K, __half *dst, hipStream_t s) {
+    if (M <= 0) return PPX_OK;
+    if (K % 32) return PPX_E_UNSUPPORTED;
+    const size_t n = (size_t)M * (K >> 3);
+    hipLaunchKernelGGL(k_tile_f16, dim3((unsigned)std::min<size_t>((n + 255) / 256, 4096)), dim3(256), 0, s, src, M, K,
+                       dst);
     return ok();
 }
 

@@ -10,6 +10,17 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
+// Fragment-tiled fp16 activation layout, the A operand of every row-batched
+// GEMM.  A[M][K] is cut into 16-row x 32-column tiles of 1 KB, stored
+// tile-row-major; inside a tile, lane l = r % 16 + 16 * ((k % 32) / 8) holds
+// the eight consecutive k of its row (the v_mfma_f32_16x16x32_f16 A-operand
+// order), so one 16-byte load per lane fetches a whole fragment from 1 KB of
+// contiguous memory.  Rows are padded to a multiple of 16 in the allocation.
+__device__ __forceinline__ size_t tiled_index(int r, int k, int K) {
+    return (((size_t)(r >> 4) * (unsigned)(K >> 5) + (unsigned)(k >> 5)) * 64 + (r & 15) + 16 * ((k >> 3) & 3)) * 8 +
+           (k & 7);
+}
+
 __device__ __forceinline__ f4 mfma16(const h8 &a, const h8 &b, const f4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }

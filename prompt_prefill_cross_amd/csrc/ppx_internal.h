@@ -95,14 +95,14 @@ enum GemmEpi {
 };
 
 struct GemmArgs {
-    const __half *A = nullptr;  // [M][K] fp16 (the high part on the exact-weight path)
-    const __half *A2 = nullptr; // [M][K] fp16 low part a - fp16(a) (exact-weight path only)
-    int lda = 0;
+    const __half *A = nullptr;  // [M][K] fp16, fragment-tiled (the high part on the exact-weight path)
+    const __half *A2 = nullptr; // [M][K] fp16 low part a - fp16(a), tiled (exact-weight path only)
+    int lda = 0;                // unused: the tiled layout's row stride is K
     int M = 0;
     Q4R W;
     int epi = EPI_F32;
     float *out_f32 = nullptr;   // EPI_F32 (ld = N), EPI_ADD residual (ld = N)
-    __half *out_f16 = nullptr;  // EPI_QKV q16 [M][qd]; EPI_GLU h [M][F]; EPI_PLE [M][E]
+    __half *out_f16 = nullptr;  // EPI_QKV q16 [M][qd] row-major; EPI_GLU h [M][F], EPI_PLE [M][E] tiled
     // rope / cache (EPI_QKV)
     int qd = 0, kvd = 0, hd = 0;
     int pos0 = 0;               // position of row 0
@@ -156,7 +156,7 @@ struct AttnArgs {
     const __half *k = nullptr;   // K cache of the source layer [P][KVH][hd]
     const __half *vt = nullptr;  // V cache of the source layer, transposed [KVH][hd][vld]
     int vld = 0;                 // multiple of 64, >= pos0 + M
-    __half *o = nullptr;         // [M][H*hd]
+    __half *o = nullptr;         // [M][H*hd], fragment-tiled (the O projection's A operand)
     int M = 0, H = 0, KVH = 0, hd = 0, pos0 = 0;
     int kc = 0, nkc = 1;         // key split (set by the launcher)
     float *part = nullptr;       // scratch of attn_prefill_scratch_floats(M, H, hd, pos0 + M) floats
@@ -176,14 +176,17 @@ int launch_attn_1row(const Attn1Args &a, hipStream_t s);
 size_t attn1_scratch_floats(int H, int hd, int n_pos);
 
 int launch_embed(const Q4R &tok, const int32_t *ids, int M, float scale, float *x, hipStream_t s);
+// y = rmsnorm(x) * g -> fp16 in the fragment-tiled layout (the GEMM A operand).
 int launch_rmsnorm_f16(const float *x, const float *g, float eps, int M, int d, __half *out,
                        hipStream_t s);
-// As launch_rmsnorm_f16, also writing lo = fp16(y - fp16(y)).
+// As launch_rmsnorm_f16, also writing lo = fp16(y - fp16(y)), tiled the same way.
 int launch_rmsnorm_split(const float *x, const float *g, float eps, int M, int d, __half *hi, __half *lo,
                          hipStream_t s);
 int launch_rmsnorm_f32(const float *x, const float *g, float eps, int M, int d, float *out,
                        hipStream_t s);
 int launch_dequant(const Q4R &w, float *out, hipStream_t s);
+// Row-major fp16 [M][K] -> fragment-tiled (K % 32 == 0).
+int launch_tile_f16(const __half *src, int M, int K, __half *dst, hipStream_t s);
 int launch_copy_f32(const float *src, float *dst, int n, hipStream_t s);
 int launch_fill_u32(uint32_t *p, uint32_t v, size_t n, hipStream_t s);
 

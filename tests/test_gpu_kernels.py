@@ -120,7 +120,7 @@ def test_gemm_glu_rejects_plain_tensor(ppx):
     mm = engine_model(ppx, "tiny")
     a = torch.zeros((4, 256), dtype=torch.float16, device="cuda")
     with pytest.raises(ppx.PPXError):
-        mm.op_gemm_glu("blk.0.wq", a, out=torch.empty((4, 128), dtype=torch.float16, device="cuda"))
+        mm.op_gemm_glu("blk.0.wq", a)
 
 
 @pytest.mark.parametrize("cfg,M", [("tiny", 64), ("tiny", 5), ("tinyllama", 512), ("e2b", 512), ("e2b", 77)])
