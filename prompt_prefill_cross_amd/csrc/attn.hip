@@ -211,22 +211,22 @@ __global__ __launch_bounds__(HD) void k_attn_prefill_merge(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------ single query
-// One query row (all heads, fp32) over cache positions 0..pos, in two launches.
-// k_attn_1row: grid (chunks of CH keys, KVH); a workgroup stages its keys and
-// transposed values in LDS with 16-byte loads, scores them against the G heads
-// of its KV head (a wave per head, lane = key), and writes per head the
-// chunk's max, exp-sum and unnormalised output.  k_attn_merge: one workgroup
-// per head combines the chunks in chunk order.
-constexpr int CH = 64;
+// One query row (all heads) over cache positions 0..pos, in two launches.
+// k_attn_1row: grid (chunks of CH keys, KVH); the G <= 8 heads of a KV head
+// share a workgroup and both products run on MFMA at ~fp32 accuracy: the fp32
+// operand (q, then the probabilities) is split into fp16 hi and lo parts that
+// fill columns 0..7 and 8..15 of the B operand, against exact fp16 keys and
+// values, so a result is the sum of its two columns.
+//   scores  S[key][g] = K[key] . q_g         (A = 16 keys x 32 dims per step)
+//   softmax of the chunk per head (max, exp-sum)
+//   P.V     O[d][g] = sum_key V^T[d][key] P[g][key]   (A = 16 dims x 32 keys)
+// Each chunk writes per head its max, exp-sum and unnormalised output;
+// k_attn_merge combines the chunks in chunk order.
+constexpr int CH = 32;
 
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn_1row(Attn1Args a) {
-    constexpr int KLD = HD + 2;  // padded K rows (halves): row r starts at bank r
-    constexpr int VLD = CH + 4;  // padded V^T rows (halves)
-    __shared__ _Float16 kl[CH * KLD];
-    __shared__ _Float16 vl[HD * VLD];
-    __shared__ float ql[8 * HD];
-    __shared__ float pl[8 * CH];
+    __shared__ float sl[8][CH];  // scores, then probabilities
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int G = a.H / a.KVH;  // <= 8
@@ -234,64 +234,77 @@ __global__ __launch_bounds__(256) void k_attn_1row(Attn1Args a) {
     const int k0 = chunk * CH;
     const int nk = min(CH, a.pos + 1 - k0);
     const float scale = 1.0f / sqrtf((float)HD);
+    const int c = lane & 15, g = c & 7, lg = lane >> 4;
+    const bool lo = c >= 8;
 
-    for (int u = tid; u < G * HD; u += 256) ql[u] = a.q[(size_t)kvh * G * HD + u];
-    for (int u = tid; u < CH * HD / 8; u += 256) {
-        const int key = u / (HD / 8), d8 = u % (HD / 8);
-        const h8 kv = *reinterpret_cast<const h8 *>(a.k + ((size_t)(k0 + min(key, nk - 1)) * a.KVH + kvh) * HD + d8 * 8);
+    if (wave < CH / 16) {
+        const int key = wave * 16 + c;
+        const int kr = k0 + min(key, nk - 1);  // masked keys re-read a valid row
+        const __half *krow = a.k + ((size_t)kr * a.KVH + kvh) * HD + lg * 8;
+        const float *qrow = a.q + (size_t)(kvh * G + min(g, G - 1)) * HD + lg * 8;
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) *reinterpret_cast<h2 *>(kl + key * KLD + d8 * 8 + e) = h2{kv[e], kv[e + 1]};
-        const int d = u / (CH / 8), k8 = u % (CH / 8);
-        h8 vv = *reinterpret_cast<const h8 *>(a.vt + ((size_t)kvh * HD + d) * a.vld + k0 + k8 * 8);
+        for (int ks = 0; ks < HD / 32; ++ks) {
+            const h8 av = *reinterpret_cast<const h8 *>(krow + ks * 32);
+            const float4 q0 = *reinterpret_cast<const float4 *>(qrow + ks * 32);
+            const float4 q1 = *reinterpret_cast<const float4 *>(qrow + ks * 32 + 4);
+            const float qe[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+            h8 bv;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            if (k8 * 8 + e >= nk) vv[e] = (_Float16)0.0f;
+            for (int e = 0; e < 8; ++e) {
+                const _Float16 h = (_Float16)qe[e];
+                bv[e] = g < G ? (lo ? (_Float16)(qe[e] - (float)h) : h) : (_Float16)0.0f;
+            }
+            acc = mfma16(av, bv, acc);
+        }
+        // acc[r] = C[key 4*lg + r of the tile][column c]; S = column g + column g + 8
 #pragma unroll
-        for (int e = 0; e < 8; e += 4)
-            *reinterpret_cast<h4 *>(vl + d * VLD + k8 * 8 + e) = h4{vv[e], vv[e + 1], vv[e + 2], vv[e + 3]};
+        for (int r = 0; r < 4; ++r) {
+            const float v = acc[r] + __shfl_xor(acc[r], 8, 64);
+            const int kt = wave * 16 + 4 * lg + r;
+            if (c < G) sl[c][kt] = kt < nk ? v * scale : -INFINITY;
+        }
     }
     __syncthreads();
 
-    // scores: wave w takes heads w, w+4; lane = key
-    for (int g = wave; g < G; g += 4) {
-        float s = -INFINITY;
-        if (lane < nk) {
-            const _Float16 *kr = kl + lane * KLD;
-            const float *qr = ql + g * HD;
-            float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll 8
-            for (int d = 0; d < HD; d += 2) {
-                const h2 kk = *reinterpret_cast<const h2 *>(kr + d);
-                acc0 += qr[d] * (float)kk[0];
-                acc1 += qr[d + 1] * (float)kk[1];
-            }
-            s = (acc0 + acc1) * scale;
-        }
-        const float m = wave_max(s);
-        const float p = lane < nk ? expf(s - m) : 0.f;
+    // softmax of the chunk: wave w takes heads w, w+4; lane = key
+    for (int h = wave; h < G; h += 4) {
+        const float sc = lane < CH ? sl[h][lane] : -INFINITY;
+        const float m = wave_max(sc);
+        const float p = (lane < nk) ? expf(sc - m) : 0.f;
         const float l = wave_sum(p);
-        pl[g * CH + lane] = p;
+        if (lane < CH) sl[h][lane] = p;
         if (lane == 0) {
-            float *st = a.partial + ((size_t)(kvh * G + g) * nchunks + chunk) * 2;
+            float *st = a.partial + ((size_t)(kvh * G + h) * nchunks + chunk) * 2;
             st[0] = m;
             st[1] = l;
         }
     }
     __syncthreads();
-    // unnormalised P.V: thread d, every head of the group
+
+    // unnormalised P.V, 16 dimensions per MFMA tile; wave w takes tiles w, w+4, ...
     float *po = a.partial + (size_t)a.H * nchunks * 2;
-    for (int d = tid; d < HD; d += 256) {
-        float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        const _Float16 *vrow = vl + d * VLD;
-        for (int j = 0; j < CH; ++j) {
-            const float v = (float)vrow[j];
+    h8 bv;
 #pragma unroll
-            for (int g = 0; g < 8; ++g)
-                if (g < G) o[g] += pl[g * CH + j] * v;
+    for (int e = 0; e < 8; ++e) {
+        const int j = lg * 8 + e;
+        const float p = g < G ? sl[g][j] : 0.f;
+        const _Float16 h = (_Float16)p;
+        bv[e] = lo ? (_Float16)(p - (float)h) : h;
+    }
+    for (int t = wave; t < HD / 16; t += 4) {
+        const int d = t * 16 + c;
+        h8 av = *reinterpret_cast<const h8 *>(a.vt + ((size_t)kvh * HD + d) * a.vld + k0 + lg * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (lg * 8 + e >= nk) av[e] = (_Float16)0.0f;
+        const f4 acc = mfma16(av, bv, f4{0.f, 0.f, 0.f, 0.f});
+        // acc[r] = C[dimension t*16 + 4*lg + r][column c]
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float v = acc[r] + __shfl_xor(acc[r], 8, 64);
+            if (c < G) po[((size_t)(kvh * G + c) * nchunks + chunk) * HD + t * 16 + 4 * lg + r] = v;
         }
-#pragma unroll
-        for (int g = 0; g < 8; ++g)
-            if (g < G) po[((size_t)(kvh * G + g) * nchunks + chunk) * HD + d] = o[g];
     }
 }
 

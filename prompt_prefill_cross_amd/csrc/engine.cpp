@@ -278,14 +278,16 @@ int layer_row(Ctx &c, int il, int pos, int tok) {
     const ppx_model *m = c.m;
     const ppx_model_info &I = m->info;
     const LayerW &w = m->layers[il];
-    const int d = I.d_model, hd = I.head_dim, kvd = I.kv_dim;
-    float *xr = c.at<float>(c.L.xr), *ar = c.at<float>(c.L.ar);
+    const int hd = I.head_dim, kvd = I.kv_dim;
+    float *xr = c.at<float>(c.L.xr);
     float *qr = c.at<float>(c.L.qr), *orow = c.at<float>(c.L.orow);
     float *hr = c.at<float>(c.L.hr), *pr = c.at<float>(c.L.pr);
     const size_t lstride = (size_t)c.kv->n_ctx * kvd;
 
-    PPX_LAUNCH(c, PPX_PHASE_ROW, launch_rmsnorm_f32(xr, w.attn_norm, m->eps, 1, d, ar, c.s));
-    GemvArgs gq = gemv_base(c, ar, w.wq, GV_QROPE, qr);
+    // each projection that follows an RMSNorm normalises the row itself
+    GemvArgs gq = gemv_base(c, xr, w.wq, GV_QROPE, qr);
+    gq.norm_g = w.attn_norm;
+    gq.eps = m->eps;
     gq.hd = hd;
     gq.pos = pos;
     gq.rope = m->rope;
@@ -303,8 +305,9 @@ int layer_row(Ctx &c, int il, int pos, int tok) {
     at.partial = c.at<float>(c.L.at_part);
     PPX_LAUNCH(c, PPX_PHASE_ROW, launch_attn_1row(at, c.s));
     PPX_LAUNCH(c, PPX_PHASE_ROW, launch_gemv(gemv_base(c, orow, w.wo, GV_ADD, xr), c.s));
-    PPX_LAUNCH(c, PPX_PHASE_ROW, launch_rmsnorm_f32(xr, w.ffn_norm, m->eps, 1, d, ar, c.s));
-    GemvArgs gg = gemv_base(c, ar, w.wgu, GV_GLU, hr);
+    GemvArgs gg = gemv_base(c, xr, w.wgu, GV_GLU, hr);
+    gg.norm_g = w.ffn_norm;
+    gg.eps = m->eps;
     gg.act = I.act;
     PPX_LAUNCH(c, PPX_PHASE_ROW, launch_gemv(gg, c.s));
     PPX_LAUNCH(c, PPX_PHASE_ROW, launch_gemv(gemv_base(c, hr, w.wdown, GV_ADD, xr), c.s));
@@ -314,8 +317,9 @@ int layer_row(Ctx &c, int il, int pos, int tok) {
         if (I.ple_dim) c.tm->row_bytes += q4_bytes(w.wpg) + q4_bytes(w.wpu);
     }
     if (I.ple_dim) {
-        PPX_LAUNCH(c, PPX_PHASE_ROW, launch_rmsnorm_f32(xr, w.ple_norm, m->eps, 1, d, ar, c.s));
-        GemvArgs gp = gemv_base(c, ar, w.wpg, GV_PLE, pr);
+        GemvArgs gp = gemv_base(c, xr, w.wpg, GV_PLE, pr);
+        gp.norm_g = w.ple_norm;
+        gp.eps = m->eps;
         gp.ple_raw = m->ple_raw;
         gp.tok = tok;
         gp.ple_row_blocks = I.n_layer * I.ple_dim / 32;
@@ -329,9 +333,10 @@ int layer_row(Ctx &c, int il, int pos, int tok) {
 
 int head_row(Ctx &c, const float *x_last, float *logits) {
     const ppx_model *m = c.m;
-    float *ar = c.at<float>(c.L.ar);
-    PPX_LAUNCH(c, PPX_PHASE_ROW, launch_rmsnorm_f32(x_last, m->out_norm, m->eps, 1, m->info.d_model, ar, c.s));
-    PPX_LAUNCH(c, PPX_PHASE_ROW, launch_gemv(gemv_base(c, ar, m->out, GV_F32, logits), c.s));
+    GemvArgs gh = gemv_base(c, x_last, m->out, GV_F32, logits);
+    gh.norm_g = m->out_norm;
+    gh.eps = m->eps;
+    PPX_LAUNCH(c, PPX_PHASE_ROW, launch_gemv(gh, c.s));
     if (c.tm) c.tm->row_bytes += q4_bytes(m->out);
     return PPX_OK;
 }

@@ -112,100 +112,134 @@ __global__ void k_copy_f32(const float *src, float *dst, int n) {
 int ok() { return hipGetLastError() == hipSuccess ? PPX_OK : PPX_E_HIP; }
 
 // ------------------------------------------------------------------ GEMV
-// y[n] = sum_k W[n][k] x[k] for one fp32 row (the pruned layers and the head).
+// y[n] = sum_k W[n][k] v[k] for one fp32 row (the pruned layers and the head),
+// v = x, or v = x / sqrt(mean(x^2) + eps) * g when a norm gain is given (the
+// RMSNorm that precedes the projection, fused).
 // The row runs through the MFMA as two rows of the A operand: row 0 holds
-// fp16(x) and row 1 holds fp16(x - fp16(x)), so their sum carries x to ~22
+// fp16(v) and row 1 holds fp16(v - fp16(v)), so their sum carries v to ~22
 // bits; B holds (code - 8) exactly, and each block's partial is scaled by its
 // fp32 block scale -- only fp32 accumulation rounds.
-// A workgroup owns one pair of 16-row groups (RoPE and gate/up partners sit in
-// such a pair); KW waves per group split K, and their partial sums meet in LDS
-// in wave order, so the result is deterministic and no workgroup waits for
-// another.
-template <int KW>
-__global__ __launch_bounds__(128 * KW) void k_q4gemv(GemvArgs a) {
-    __shared__ float red[2][KW][16];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int half = wave / KW, kw = wave % KW;
-    const int grp = 2 * blockIdx.x + half;
-    const int kch = a.W.K >> 6;
-    const int per = (kch + KW - 1) / KW;
-    const int c0 = kw * per, c1 = min(kch, c0 + per);
-    const int col = lane & 15, g = lane >> 4;
-    const bool arow = col < 2;  // A rows 0 (hi) and 1 (lo) carry x
+// A workgroup owns G groups of 16 columns (G = 2 when the epilogue combines a
+// pair: RoPE halves, gate/up); KW waves per group take interleaved 64-wide K
+// chunks with UNR weight loads in flight.  v is staged once per workgroup in
+// LDS as hi/lo fp16 arrays, so a lane's A-operand piece is one 16-byte read.
+// Partial sums meet in LDS in wave order: the result is deterministic and no
+// workgroup waits for another.
+constexpr int GEMV_UNR = 4;
 
-    f4 acc = {0.f, 0.f, 0.f, 0.f};
+template <int KW, int G>
+__global__ __launch_bounds__(64 * KW * G) void k_q4gemv(GemvArgs a) {
+    extern __shared__ float gemv_lds[];  // red[G][KW][16] floats, then hi[K], lo[K] fp16
+    constexpr int NT = 64 * KW * G;
+    const int K = a.W.K, kch = K >> 6;
+    float *red = gemv_lds;
+    _Float16 *xh = reinterpret_cast<_Float16 *>(gemv_lds + G * KW * 16);
+    _Float16 *xl = xh + K;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int gi = wave / KW, kw = wave % KW;
+    const int grp = G * blockIdx.x + gi;
+
+    // stage v (normalised if asked) as hi / lo halves
+    float r = 1.f;
+    if (a.norm_g) {
+        float ss = 0.f;
+        for (int k = tid; k < K; k += NT) ss += a.x[k] * a.x[k];
+        ss = wave_sum(ss);
+        if (lane == 0) red[wave] = ss;
+        __syncthreads();
+        ss = 0.f;
+        for (int w = 0; w < NT / 64; ++w) ss += red[w];
+        r = 1.0f / sqrtf(ss / (float)K + a.eps);
+        __syncthreads();
+    }
+    for (int k = tid; k < K; k += NT) {
+        const float v = a.norm_g ? a.x[k] * r * a.norm_g[k] : a.x[k];
+        const _Float16 h = (_Float16)v;
+        xh[k] = h;
+        xl[k] = (_Float16)(v - (float)h);
+    }
+    __syncthreads();
+
+    const int col = lane & 15, g8 = (lane >> 4) * 8;
+    const _Float16 *xsrc = col == 0 ? xh : xl;  // rows 0 and 1 carry v; the others stay zero
+    const bool arow = col < 2;
     const uint2 *nib = reinterpret_cast<const uint2 *>(a.W.nib) + (size_t)grp * kch * 64 + lane;
     const uint32_t *scl = reinterpret_cast<const uint32_t *>(a.W.scl) + (size_t)grp * kch * 16 + col;
-#pragma unroll 2
-    for (int kc = c0; kc < c1; ++kc) {
-        const uint2 w = nib[(size_t)kc * 64];
-        const h2 d = __builtin_bit_cast(h2, scl[(size_t)kc * 16]);
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int base = kw; base < kch; base += KW * GEMV_UNR) {
+        uint2 w[GEMV_UNR];
+        uint32_t sc[GEMV_UNR];
+        // loads first (clamped, so they need no branch), then the arithmetic
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            h8 af = h8{0, 0, 0, 0, 0, 0, 0, 0};
-            if (arow) {
-                const float4 *xv = reinterpret_cast<const float4 *>(a.x + kc * 64 + s * 32 + g * 8);
-                const float4 x0 = xv[0], x1 = xv[1];
-                const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        for (int u = 0; u < GEMV_UNR; ++u) {
+            const int kc = min(base + u * KW, kch - 1);
+            w[u] = nib[(size_t)kc * 64];
+            sc[u] = scl[(size_t)kc * 16];
+        }
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const _Float16 hi = (_Float16)xs[e];
-                    af[e] = col == 0 ? hi : (_Float16)(xs[e] - (float)hi);
-                }
+        for (int u = 0; u < GEMV_UNR; ++u) {
+            const int kc = base + u * KW;
+            if (kc >= kch) break;  // uniform across the wave
+            const h2 d = __builtin_bit_cast(h2, sc[u]);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                h8 af = *reinterpret_cast<const h8 *>(xsrc + kc * 64 + s * 32 + g8);
+                if (!arow) af = h8{0, 0, 0, 0, 0, 0, 0, 0};
+                const f4 p = mfma16(af, q4_word_codes(s ? w[u].y : w[u].x), f4{0.f, 0.f, 0.f, 0.f});
+                acc += (float)d[s] * p;
             }
-            const h8 bf = q4_word_codes(s ? w.y : w.x);
-            const f4 p = mfma16(af, bf, f4{0.f, 0.f, 0.f, 0.f});
-            acc += (float)d[s] * p;
         }
     }
     // lanes 0..15 hold rows 0 and 1 (hi and lo parts) of column `col`
-    if (lane < 16) red[half][kw][lane] = acc[0] + acc[1];
+    if (lane < 16) red[(gi * KW + kw) * 16 + lane] = acc[0] + acc[1];
     __syncthreads();
-    if (threadIdx.x >= 16) return;
-    const int c = threadIdx.x;
-    float ya = 0.f, yb = 0.f;
+    if (tid >= 16) return;
+    const int c = tid;
+    float yv[G];
 #pragma unroll
-    for (int i = 0; i < KW; ++i) {
-        ya += red[0][i][c];
-        yb += red[1][i][c];
+    for (int q = 0; q < G; ++q) {
+        float y = 0.f;
+#pragma unroll
+        for (int i = 0; i < KW; ++i) y += red[(q * KW + i) * 16 + c];
+        yv[q] = y;
     }
-    const int n0 = blockIdx.x * 32;
+    const int n0 = blockIdx.x * 16 * G;
     switch (a.epi) {
     case GV_F32:
-        a.out[n0 + c] = ya;
-        a.out[n0 + 16 + c] = yb;
+#pragma unroll
+        for (int q = 0; q < G; ++q) a.out[n0 + 16 * q + c] = yv[q];
         break;
     case GV_ADD:
-        a.out[n0 + c] += ya;
-        a.out[n0 + 16 + c] += yb;
+#pragma unroll
+        for (int q = 0; q < G; ++q) a.out[n0 + 16 * q + c] += yv[q];
         break;
-    case GV_QROPE: {
-        const int hd = a.hd, hh = hd >> 1;
-        const int h = n0 / hd, rr = n0 % hd;
-        const int ii = (rr >> 5) * 16 + c;
-        const float2 cs = a.rope[(size_t)a.pos * hh + ii];
-        a.out[h * hd + ii] = ya * cs.x - yb * cs.y;
-        a.out[h * hd + ii + hh] = ya * cs.y + yb * cs.x;
+    case GV_QROPE:
+        if (G == 2) {
+            const int hd = a.hd, hh = hd >> 1;
+            const int h = n0 / hd, rr = n0 % hd;
+            const int ii = (rr >> 5) * 16 + c;
+            const float2 cs = a.rope[(size_t)a.pos * hh + ii];
+            a.out[h * hd + ii] = yv[0] * cs.x - yv[G - 1] * cs.y;
+            a.out[h * hd + ii + hh] = yv[0] * cs.y + yv[G - 1] * cs.x;
+        }
         break;
-    }
     case GV_GLU:
-        a.out[blockIdx.x * 16 + c] = act_f(a.act, ya) * yb;
+        if (G == 2) a.out[blockIdx.x * 16 + c] = act_f(a.act, yv[0]) * yv[G - 1];
         break;
     case GV_PLE: {
         const uint8_t *prow = a.ple_raw + (size_t)a.tok * a.ple_row_blocks * 18;
-        a.out[n0 + c] = gelu_tanh_f(ya) * (a.ple_s * q4_raw_weight(prow, a.ple_col0 + n0 + c));
-        a.out[n0 + 16 + c] = gelu_tanh_f(yb) * (a.ple_s * q4_raw_weight(prow, a.ple_col0 + n0 + 16 + c));
+#pragma unroll
+        for (int q = 0; q < G; ++q)
+            a.out[n0 + 16 * q + c] = gelu_tanh_f(yv[q]) * (a.ple_s * q4_raw_weight(prow, a.ple_col0 + n0 + 16 * q + c));
         break;
     }
     }
 }
 
-// waves per 16-row group: enough waves in flight to cover memory latency,
-// at least two 64-wide K chunks per wave
-int gemv_kw(int N, int K) {
-    const int groups = N / 16, kch = K / 64;
+// waves per group: aim for ~4096 waves in flight with >= 2 chunks per wave
+int gemv_kw(int groups, int kch) {
     int kw = 1;
-    while (kw < 8 && groups * kw < 2048 && kch / (2 * kw) >= 2) kw *= 2;
+    while (kw < 16 && groups * kw < 4096 && kch / (2 * kw) >= 2) kw *= 2;
     return kw;
 }
 
@@ -213,13 +247,30 @@ int gemv_kw(int N, int K) {
 
 int launch_gemv(const GemvArgs &a, hipStream_t s) {
     if (a.W.N % 32 || a.W.K % 64 || !a.x || !a.out) return PPX_E_UNSUPPORTED;
-    const dim3 grid(a.W.N / 32);
-    switch (gemv_kw(a.W.N, a.W.K)) {
-    case 1: hipLaunchKernelGGL(k_q4gemv<1>, grid, dim3(128), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(k_q4gemv<2>, grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(k_q4gemv<4>, grid, dim3(512), 0, s, a); break;
-    default: hipLaunchKernelGGL(k_q4gemv<8>, grid, dim3(1024), 0, s, a); break;
+    const bool paired = a.epi == GV_QROPE || a.epi == GV_GLU;
+    const int G = paired ? 2 : 1;
+    const int kw = std::min(gemv_kw(a.W.N / 16, a.W.K / 64), 16 / G);
+    const dim3 grid(a.W.N / (16 * G));
+    const size_t lds = sizeof(float) * G * kw * 16 + 4ull * a.W.K;
+    if (lds > 64 * 1024) return PPX_E_UNSUPPORTED;
+#define PPX_GEMV(KW_, G_) hipLaunchKernelGGL((k_q4gemv<KW_, G_>), grid, dim3(64 * KW_ * G_), lds, s, a)
+    if (G == 2) {
+        switch (kw) {
+        case 1: PPX_GEMV(1, 2); break;
+        case 2: PPX_GEMV(2, 2); break;
+        case 4: PPX_GEMV(4, 2); break;
+        default: PPX_GEMV(8, 2); break;
+        }
+    } else {
+        switch (kw) {
+        case 1: PPX_GEMV(1, 1); break;
+        case 2: PPX_GEMV(2, 1); break;
+        case 4: PPX_GEMV(4, 1); break;
+        case 8: PPX_GEMV(8, 1); break;
+        default: PPX_GEMV(16, 1); break;
+        }
     }
+#undef PPX_GEMV
     return ok();
 }
 

@@ -132,6 +132,8 @@ enum GemvEpi {
 };
 struct GemvArgs {
     const float *x = nullptr;  // [K]
+    const float *norm_g = nullptr;  // if set: x is RMS-normalised with this gain first
+    float eps = 0.f;
     Q4R W;
     int epi = GV_F32;
     float *out = nullptr;

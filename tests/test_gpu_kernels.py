@@ -10,7 +10,9 @@ seeded inputs, to bounds derived from the kernel's arithmetic:
   * GEMV: exact fp32 weights, fp32 accumulation: <= K 2^-24 sum|w x|;
   * prefill attention: probabilities rounded to fp16 before P.V and the
     output rounded to fp16: |o - o64| <= 2e-3 max|V| + 1e-3 |o64|;
-  * single-row attention: fp32 throughout: 1e-5 max|V|.
+  * single-row attention: q and the probabilities enter the MFMA as fp16
+    hi + lo pairs (about 22 significant bits) against exact fp16 keys and
+    values, with fp32 accumulation: 1e-5 max|V|.
 """
 import numpy as np
 import pytest
