@@ -104,8 +104,7 @@ typedef struct {
  * during the call only.  Weights are repacked for the kernels and uploaded
  * into device memory the library allocates (freed by ppx_model_free).
  * Errors: PPX_E_FORMAT (bad container), PPX_E_UNSUPPORTED (a dimension the
- * kernels cannot tile: d_model, q_dim, ple_dim not multiples of 128, n_ff
- * not a multiple of 64,
+ * kernels cannot tile: d_model, q_dim, n_ff, ple_dim not multiples of 256,
  * head_dim not 64/128/256, n_head not a multiple of n_kv_head), PPX_E_HIP. */
 int ppx_model_load(const void *container, size_t bytes, void *hip_stream, ppx_model **out);
 /* Same, reading the container from a file (PPX_E_IO if it cannot be read). */

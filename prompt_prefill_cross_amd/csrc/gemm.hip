@@ -3,22 +3,24 @@
 //   C[M][N] = A[M][K] (fp16 activations, fragment-tiled) x W[N][K]^T (Q4_0),
 //   fp32 accumulate, with the layer's elementwise work fused into the epilogue.
 //
-// A workgroup holds NWN compute waves and one producer wave and computes a
-// BM x BN tile; compute wave w owns columns [w*WN, (w+1)*WN) for all BM rows
-// (TM x TN MFMA tiles of 16 x 16).  Operands reach LDS without passing through
-// registers: the producer wave fills a ring of DEPTH stages, one K step of 64
-// each, with global_load_lds DMA --
-//   * A: 1 KB fragments, contiguous in the fragment-tiled activation layout,
-//     one 16-byte piece per lane straight into A-operand order;
-//   * W: for every compute wave, its columns' repacked Q4_0 codes (16 bytes per
-//     lane = two lanes' words, two 16-column groups per instruction) and fp16
-//     block-scale pairs (4 bytes per lane, four groups per instruction).
-// The producer waits for a stage by counting its own outstanding DMA
-// instructions, then joins the workgroup barrier that hands the stage over;
-// compute waves only read LDS, decode weights in registers (a shift, a mask,
-// an OR with the fp16 exponent of 1024, a subtract and a multiply per pair)
-// and multiply.  Keeping the roles in different waves keeps the compiler from
-// making LDS reads wait on DMA aimed at other stages.
+// A workgroup holds NWN x KS compute waves and one producer wave and computes
+// a BM x BN tile; compute wave (w, g) owns columns [w*WN, (w+1)*WN) for all BM
+// rows (TM x TN MFMA tiles of 16 x 16) over the g-th of KS equal slices of K;
+// the KS partial tiles meet in LDS, in slice order, before the epilogue.
+//   * A (shared by the compute waves) reaches LDS without passing through
+//     registers: the producer wave fills a ring of DEPTH stages, one 64-wide
+//     K step of every slice each, with global_load_lds DMA of 1 KB fragments -- contiguous in
+//     the fragment-tiled activation layout, one 16-byte piece per lane straight
+//     into A-operand order -- and hands a stage over with a workgroup barrier
+//     once its own outstanding-DMA count says the stage has landed.
+//   * W (private to each compute wave: its own columns) streams straight into
+//     registers, PB stages ahead: per lane and 64-wide K step one 8-byte word
+//     pair of repacked codes and one fp16 block-scale pair per 16-column group.
+//     Compute waves decode in registers (a shift, a mask, an OR with the fp16
+//     exponent of 1024, a subtract and a multiply per pair) and multiply.
+// Keeping DMA in its own wave keeps the compiler from making LDS reads wait on
+// DMA aimed at other stages.  The decode is paid once per wave for TM row
+// tiles, so taller wave tiles amortise it; LDS carries only A.
 //
 // Two arithmetic modes:
 //  * fast (EXACT = false): B = fp16(d * (code - 8)), one rounding per weight;
@@ -61,28 +63,6 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
     asm volatile("" ::: "memory");
 }
-
-template <int TM_, int TN_, int NWN_, int DEPTH_, bool EXACT_>
-struct Cfg {
-    static constexpr int TM = TM_, TN = TN_, NWN = NWN_, DEPTH = DEPTH_;
-    static constexpr bool EXACT = EXACT_;
-    static constexpr int NT = 64 * (NWN + 1);
-    static constexpr int BM = 16 * TM, WN = 16 * TN, BN = NWN * WN;
-    static constexpr int NA = EXACT ? 2 : 1;              // A parts (hi, lo)
-    static constexpr int AFR = 2 * TM * NA;                // 1 KB A fragments per stage
-    static constexpr int CPW = TN / 2;                     // code DMAs per compute wave
-    static constexpr int SPW = (TN + 3) / 4;               // scale DMAs per compute wave
-    static constexpr int DMAS = AFR + NWN * (CPW + SPW);   // producer instructions per stage
-    // LDS, in 16-byte units
-    static constexpr int A_UNITS = AFR * 64;
-    static constexpr int C_UNITS = TN * 32;                // codes: 512 B per group
-    static constexpr int S_UNITS = SPW * 16;               // scales: 256 B per four groups
-    static constexpr int W_UNITS = C_UNITS + S_UNITS;
-    static constexpr int STAGE_UNITS = A_UNITS + NWN * W_UNITS;
-    static_assert(TN % 2 == 0 && TN >= 2 && TN <= 4, "wave tile columns");
-    static_assert(DEPTH >= 2 && (DEPTH - 2) * DMAS <= 63, "vmcnt range");
-    static_assert(DEPTH * STAGE_UNITS * 16 <= 160 * 1024, "LDS");
-};
 
 // Epilogue of one wave tile: acc[i][j][r] = C[r0 + 16i + 4(lane/16) + r][c0 + 16j + lane%16].
 template <int TM, int TN>
@@ -170,21 +150,36 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, const f4 (&acc)
     }
 }
 
+template <int TM_, int TN_, int NWN_, int KS_, int DEPTH_, bool EXACT_>
+struct Cfg {
+    static constexpr int TM = TM_, TN = TN_, NWN = NWN_, KS = KS_, DEPTH = DEPTH_;
+    static constexpr bool EXACT = EXACT_;
+    static constexpr int NCW = NWN * KS;             // compute waves
+    static constexpr int NT = 64 * (NCW + 1);
+    static constexpr int BM = 16 * TM, WN = 16 * TN, BN = NWN * WN;
+    static constexpr int NA = EXACT ? 2 : 1;
+    static constexpr int AFR = 2 * TM * NA;          // fragments per chunk
+    static constexpr int DMAS = AFR * KS;            // per stage
+    static constexpr int STAGE_UNITS = DMAS * 64;
+    static constexpr int PB = 4;
+    static constexpr int RED_FLOATS = (KS - 1) * NWN * TM * TN * 4 * 64;
+    static_assert(NT <= 1024, "workgroup size");
+    static_assert(DEPTH >= 2 && (DEPTH - 2) * DMAS <= 63, "vmcnt range");
+    static_assert(DEPTH * STAGE_UNITS * 16 <= 160 * 1024, "LDS");
+    static_assert(RED_FLOATS * 4 <= DEPTH * STAGE_UNITS * 16, "reduction space");
+};
+
 template <class C>
 __global__ __launch_bounds__(C::NT) void k_q4gemm(GemmArgs a) {
     __shared__ h8 ring[C::DEPTH * C::STAGE_UNITS];
-
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
     const int n0 = blockIdx.x * C::BN, m0 = blockIdx.y * C::BM;
-    const int kch = a.W.K >> 6;  // K steps of 64
+    const int kch = a.W.K >> 6;
+    const int nkg = kch / C::KS;  // chunks per group
     const int ktiles = a.W.K >> 5;
 
-    if (wave == C::NWN) {
-        // ------------------------------------------------------ producer wave
-        // A fragment (part p, kb, i) of stage s: tile row m0/16 + i (clamped to
-        // the last tile row; rows past M are computed and discarded), tile
-        // column 2s + kb; stage layout [p][kb][i] x 1 KB
+    if (wave == C::NCW) {
         const int last_tr = (a.M - 1) >> 4;
         const __half *asrc[C::AFR];
 #pragma unroll
@@ -193,108 +188,126 @@ __global__ __launch_bounds__(C::NT) void k_q4gemm(GemmArgs a) {
             const int tr = min((m0 >> 4) + i, last_tr);
             asrc[f] = (p ? a.A2 : a.A) + (((size_t)tr * ktiles + kb) * 64 + lane) * 8;
         }
-        const uint32_t *csrc[C::NWN][C::CPW];
-        const uint32_t *ssrc[C::NWN][C::SPW];
-#pragma unroll
-        for (int w = 0; w < C::NWN; ++w) {
-            const int g0 = (n0 >> 4) + w * C::TN;
-#pragma unroll
-            for (int p = 0; p < C::CPW; ++p)
-                csrc[w][p] = a.W.nib + ((size_t)(g0 + 2 * p + (lane >> 5)) * kch * 64 + (lane & 31) * 2) * 2;
-#pragma unroll
-            for (int q = 0; q < C::SPW; ++q) {
-                const int j = min(4 * q + (lane >> 4), C::TN - 1);
-                ssrc[w][q] = reinterpret_cast<const uint32_t *>(a.W.scl) + ((size_t)(g0 + j) * kch * 16 + (lane & 15));
-            }
-        }
-        // DMA of stage min(sb, kch-1) into the buffer of stage sb
         auto issue = [&](int sb) {
             h8 *st = ring + (sb % C::DEPTH) * C::STAGE_UNITS;
-            const int s = min(sb, kch - 1);
+            const int s = min(sb, nkg - 1);
 #pragma unroll
-            for (int f = 0; f < C::AFR; ++f) dma16(asrc[f] + (size_t)s * 1024, st + f * 64);
+            for (int g = 0; g < C::KS; ++g)
 #pragma unroll
-            for (int w = 0; w < C::NWN; ++w) {
-                h8 *wst = st + C::A_UNITS + w * C::W_UNITS;
-#pragma unroll
-                for (int p = 0; p < C::CPW; ++p) dma16(csrc[w][p] + (size_t)s * 128, wst + p * 64);
-#pragma unroll
-                for (int q = 0; q < C::SPW; ++q) dma4(ssrc[w][q] + (size_t)s * 16, wst + C::C_UNITS + q * 16);
-            }
+                for (int f = 0; f < C::AFR; ++f)
+                    dma16(asrc[f] + (size_t)(g * nkg + s) * 1024, st + (g * C::AFR + f) * 64);
         };
-        // Stages 0 .. DEPTH-2 up front; stage s + DEPTH - 1 right after the
-        // barrier that hands stage s over (every compute wave has then finished
-        // reading stage s - 1, whose buffer it refills).  Past the end the same
-        // number of instructions is issued -- reloads of the last stage into
-        // buffers of stages no one reads again -- so the count stays exact.
 #pragma unroll
         for (int s = 0; s < C::DEPTH - 1; ++s) issue(s);
-        for (int s = 0; s < kch; ++s) {
+        for (int s = 0; s < nkg; ++s) {
             wait_vm<(C::DEPTH - 2) * C::DMAS>();
             lds_barrier();
             issue(s + C::DEPTH - 1);
         }
         wait_vm<0>();
+        if constexpr (C::KS > 1) lds_barrier();  // matches the compute waves' barrier before the reduction
         return;
     }
 
-    // ---------------------------------------------------------- compute waves
+    const int wn = wave % C::NWN, grp = wave / C::NWN;
+    const int g0 = (n0 >> 4) + wn * C::TN;
+    const int cbase = grp * nkg;
+    const uint2 *nib[C::TN];
+    const uint32_t *scl[C::TN];
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+        nib[j] = reinterpret_cast<const uint2 *>(a.W.nib) + ((size_t)(g0 + j) * kch + cbase) * 64 + lane;
+        scl[j] = reinterpret_cast<const uint32_t *>(a.W.scl) + ((size_t)(g0 + j) * kch + cbase) * 16 + (lane & 15);
+    }
+    uint2 bw[C::PB][C::TN];
+    uint32_t bs[C::PB][C::TN];
+    auto loadb = [&](int slot, int s) {
+        const int sc = min(s, nkg - 1);
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+            bw[slot][j] = nib[j][(size_t)sc * 64];
+            bs[slot][j] = scl[j][(size_t)sc * 16];
+        }
+    };
     f4 acc[C::TM][C::TN];
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
-
-    for (int s = 0; s < kch; ++s) {
-        lds_barrier();
-        const h8 *st = ring + (s % C::DEPTH) * C::STAGE_UNITS;
-        const h8 *wst = st + C::A_UNITS + wave * C::W_UNITS;
-        const uint2 *codes = reinterpret_cast<const uint2 *>(wst);
-        const uint32_t *scales = reinterpret_cast<const uint32_t *>(wst + C::C_UNITS);
-        uint2 bw[C::TN];
-        h2 bs[C::TN];
 #pragma unroll
-        for (int j = 0; j < C::TN; ++j) {
-            bw[j] = codes[j * 64 + lane];
-            bs[j] = __builtin_bit_cast(h2, scales[j * 16 + (lane & 15)]);
-        }
+    for (int p = 0; p < C::PB - 1; ++p) loadb(p, p);
+    for (int s0 = 0; s0 < nkg; s0 += C::PB) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            h8 af[C::TM];
+        for (int u = 0; u < C::PB; ++u) {
+            const int s = s0 + u;
+            loadb((u + C::PB - 1) % C::PB, s + C::PB - 1);
+            lds_barrier();
+            const h8 *st = ring + (s % C::DEPTH) * C::STAGE_UNITS + grp * C::AFR * 64;
 #pragma unroll
-            for (int i = 0; i < C::TM; ++i) af[i] = st[(kb * C::TM + i) * 64 + lane];
-            if constexpr (C::EXACT) {
-                h8 al[C::TM];
+            for (int kb = 0; kb < 2; ++kb) {
+                h8 af[C::TM];
 #pragma unroll
-                for (int i = 0; i < C::TM; ++i) al[i] = st[((2 + kb) * C::TM + i) * 64 + lane];
+                for (int i = 0; i < C::TM; ++i) af[i] = st[(kb * C::TM + i) * 64 + lane];
+                if constexpr (C::EXACT) {
+                    h8 al[C::TM];
 #pragma unroll
-                for (int j = 0; j < C::TN; ++j) {
-                    const h8 bq = q4_word_codes(kb ? bw[j].y : bw[j].x);
-                    const float dj = (float)bs[j][kb];
+                    for (int i = 0; i < C::TM; ++i) al[i] = st[((2 + kb) * C::TM + i) * 64 + lane];
 #pragma unroll
-                    for (int i = 0; i < C::TM; ++i) {
-                        f4 t = mfma16(af[i], bq, f4{0.f, 0.f, 0.f, 0.f});
-                        t = mfma16(al[i], bq, t);
-                        acc[i][j] += dj * t;
+                    for (int j = 0; j < C::TN; ++j) {
+                        const h8 bq = q4_word_codes(kb ? bw[u][j].y : bw[u][j].x);
+                        const float dj = (float)__builtin_bit_cast(h2, bs[u][j])[kb];
+#pragma unroll
+                        for (int i = 0; i < C::TM; ++i) {
+                            f4 t = mfma16(af[i], bq, f4{0.f, 0.f, 0.f, 0.f});
+                            t = mfma16(al[i], bq, t);
+                            acc[i][j] += dj * t;
+                        }
                     }
+                } else {
+                    h8 bf[C::TN];
+#pragma unroll
+                    for (int j = 0; j < C::TN; ++j)
+                        bf[j] = q4_word_to_h8(kb ? bw[u][j].y : bw[u][j].x, __builtin_bit_cast(h2, bs[u][j])[kb]);
+#pragma unroll
+                    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                        for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma16(af[i], bf[j], acc[i][j]);
                 }
-            } else {
-                h8 bf[C::TN];
-#pragma unroll
-                for (int j = 0; j < C::TN; ++j) bf[j] = q4_word_to_h8(kb ? bw[j].y : bw[j].x, bs[j][kb]);
-#pragma unroll
-                for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma16(af[i], bf[j], acc[i][j]);
             }
         }
     }
-    gemm_epilogue<C::TM, C::TN>(a, acc, m0, n0 + wave * C::WN, lane);
+    if constexpr (C::KS > 1) {
+        // every wave is past its last ring read once this barrier completes
+        lds_barrier();
+        float *red = reinterpret_cast<float *>(ring);
+        if (grp > 0) {
+            float *dst = red + ((size_t)((grp - 1) * C::NWN + wn) * C::TM * C::TN * 4) * 64;
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dst[((i * C::TN + j) * 4 + r) * 64 + lane] = acc[i][j][r];
+        }
+        __syncthreads();  // compute waves only: the producer has returned
+        if (grp > 0) return;
+#pragma unroll
+        for (int g = 1; g < C::KS; ++g) {
+            const float *src = red + ((size_t)((g - 1) * C::NWN + wn) * C::TM * C::TN * 4) * 64;
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[i][j][r] += src[((i * C::TN + j) * 4 + r) * 64 + lane];
+        }
+    }
+    gemm_epilogue<C::TM, C::TN>(a, acc, m0, n0 + wn * C::WN, lane);
 }
 
 template <class C>
 int launch_cfg(const GemmArgs &a, hipStream_t s) {
-    if (a.W.N % C::BN) return PPX_E_UNSUPPORTED;
+    if (a.W.N % C::BN || (a.W.K >> 6) % (C::PB * C::KS)) return PPX_E_UNSUPPORTED;
     dim3 grid(a.W.N / C::BN, (a.M + C::BM - 1) / C::BM);
     hipLaunchKernelGGL((k_q4gemm<C>), grid, dim3(C::NT), 0, s, a);
     return hipGetLastError() == hipSuccess ? PPX_OK : PPX_E_HIP;
@@ -303,23 +316,34 @@ int launch_cfg(const GemmArgs &a, hipStream_t s) {
 }  // namespace
 
 // Tile shapes measured on the E2B-like shapes at M = 512 (one MI355X):
-//  * wide outputs (gate|up, N >= 8192): 64 x 128 tiles, a three-stage ring
-//    (39 KB of LDS: four workgroups per CU);
-//  * narrow outputs (N <= 512): 32 x 64 tiles with two compute waves, for
-//    enough workgroups;
-//  * the rest (Q, O, down, PLE up): 32 x 128 tiles.
+//  * wide outputs (gate|up, N >= 8192): 64 x 128 tiles, four compute waves;
+//  * long K (down, K >= 4096): 64 x 64 tiles, K split over four wave groups;
+//  * narrow outputs (N <= 512): 16 x 128 tiles, K split over two groups;
+//  * the rest (Q, O, PLE up): 32 x 128 tiles, K split over two groups.
+// The exact-weight K|V projection: 16 x 64 tiles, K split over two groups.
+// A split needs K/64 to be a multiple of 4 x KS; narrower splits are used
+// where it is not.
+template <int TM, int TN, int NWN, int KS, int DEPTH, bool EXACT>
+int launch_split(const GemmArgs &a, hipStream_t s) {
+    if constexpr (KS > 1) {
+        if ((a.W.K >> 6) % (4 * KS)) return launch_split<TM, TN, NWN, KS / 2, DEPTH, EXACT>(a, s);
+    }
+    return launch_cfg<Cfg<TM, TN, NWN, KS, DEPTH, EXACT>>(a, s);
+}
+
 int launch_gemm(const GemmArgs &a, hipStream_t s) {
     if (a.M <= 0) return PPX_OK;
-    if (a.W.N % 128 || a.W.K % 64 || !a.A) return PPX_E_UNSUPPORTED;
-    if (a.W.N >= 8192) return launch_cfg<Cfg<4, 2, 4, 3, false>>(a, s);
-    if (a.W.N <= 512) return launch_cfg<Cfg<2, 2, 2, 4, false>>(a, s);
-    return launch_cfg<Cfg<2, 2, 4, 4, false>>(a, s);
+    if (a.W.N % 128 || a.W.K % 256 || !a.A) return PPX_E_UNSUPPORTED;
+    if (a.W.N >= 8192) return launch_split<4, 2, 4, 1, 4, false>(a, s);
+    if (a.W.K >= 4096) return launch_split<4, 2, 2, 4, 3, false>(a, s);
+    if (a.W.N <= 512) return launch_split<1, 2, 4, 2, 6, false>(a, s);
+    return launch_split<2, 2, 4, 2, 4, false>(a, s);
 }
 
 int launch_gemm_exact(const GemmArgs &a, hipStream_t s) {
     if (a.M <= 0) return PPX_OK;
-    if (a.W.N % 128 || a.W.K % 64 || !a.A || !a.A2) return PPX_E_UNSUPPORTED;
-    return launch_cfg<Cfg<1, 2, 4, 4, true>>(a, s);
+    if (a.W.N % 64 || a.W.K % 256 || !a.A || !a.A2) return PPX_E_UNSUPPORTED;
+    return launch_split<1, 2, 2, 2, 6, true>(a, s);
 }
 
 }  // namespace ppx

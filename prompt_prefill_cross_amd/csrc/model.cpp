@@ -160,7 +160,7 @@ int model_load(const uint8_t *b, size_t n, hipStream_t stream, ppx_model **out) 
     if (Ls < 0 || Ls > L || d <= 0 || I.n_head <= 0 || I.n_kv_head <= 0 || V <= 0 || F <= 0 || E < 0 ||
         I.act < 0 || I.act > 1)
         return PPX_E_FORMAT;
-    if (d % 128 || qd % 128 || F % 64 || E % 128 || (hd != 64 && hd != 128 && hd != 256) ||
+    if (d % 256 || qd % 256 || F % 256 || E % 256 || (hd != 64 && hd != 128 && hd != 256) ||
         I.n_head % I.n_kv_head || V % 32 || (I.n_head / I.n_kv_head) > 8 || kvd % 32)
         return PPX_E_UNSUPPORTED;
     for (int il = 0; il < L; ++il) {

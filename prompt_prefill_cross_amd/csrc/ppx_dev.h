@@ -25,6 +25,15 @@ __device__ __forceinline__ f4 mfma16(const h8 &a, const h8 &b, const f4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// (x & 0x000F000F) | 0x64006400 in one v_and_or_b32.  Both constants live in
+// VGPRs: gfx950's VOP3 encoding reads at most one scalar or literal operand,
+// so with two literals the compiler falls back to a separate AND and OR.
+__device__ __forceinline__ uint32_t q4_pair_bits(uint32_t x) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(0x000F000Fu), "v"(0x64006400u));
+    return r;
+}
+
 // Eight codes of one repacked word -> fp16 d*(code-8), rounded to nearest even.
 // (w >> 4i) & 0x000F000F | 0x6400_6400 is the fp16 pair (1024+q_{2i}, 1024+q_{2i+1});
 // subtracting 1032 is exact, the product with d rounds once.
@@ -34,8 +43,7 @@ __device__ __forceinline__ h8 q4_word_to_h8(uint32_t w, _Float16 d) {
     const h2 dd = {d, d};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        uint32_t t = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
-        h2 v = __builtin_bit_cast(h2, t);
+        h2 v = __builtin_bit_cast(h2, q4_pair_bits(w >> (4 * i)));
         v = (v - bias) * dd;
         r[2 * i] = v[0];
         r[2 * i + 1] = v[1];
@@ -49,8 +57,7 @@ __device__ __forceinline__ h8 q4_word_codes(uint32_t w) {
     const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        uint32_t t = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
-        h2 v = __builtin_bit_cast(h2, t) - bias;
+        h2 v = __builtin_bit_cast(h2, q4_pair_bits(w >> (4 * i))) - bias;
         r[2 * i] = v[0];
         r[2 * i + 1] = v[1];
     }
