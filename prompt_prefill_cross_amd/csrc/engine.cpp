@@ -274,7 +274,7 @@ GemvArgs gemv_base(Ctx &c, const float *x, const Q4R &W, int epi, float *out) {
 }
 
 // Layer il for the single output row (pruned KV-shared layers), fp32 throughout.
-int layer_row(Ctx &c, int il, int pos, int tok) {
+int layer_row(Ctx &c, int il, int pos, const int32_t *tok) {
     const ppx_model *m = c.m;
     const ppx_model_info &I = m->info;
     const LayerW &w = m->layers[il];
@@ -341,6 +341,111 @@ int head_row(Ctx &c, const float *x_last, float *logits) {
     return PPX_OK;
 }
 
+// The launch sequence of one prefill call (all ubatches, the pruned tail and
+// the head).  Token ids are read from tok_dev, so the sequence can be recorded
+// once and replayed for any prompt of the same shape.
+int enqueue_prefill(Ctx &c, const ppx_prefill_params *p, const int32_t *tok_dev, int n, int p0, int ub,
+                    bool prune, float *logits) {
+    ppx_model *m = c.m;
+    const ppx_model_info &I = m->info;
+    const int L = I.n_layer, Ls = I.n_layer_kv_from_start, d = I.d_model;
+    hipStream_t s = c.s;
+    float *x = c.at<float>(c.L.x);
+    for (int s0 = 0; s0 < n; s0 += ub) {
+        const int M = std::min(ub, n - s0);
+        const bool last = s0 + M == n;
+        const int pos0 = p0 + s0;
+        PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_embed(m->tok, tok_dev + s0, M, m->embd_scale, x, s));
+        const int full_layers = prune ? Ls : L;
+        for (int il = 0; il < full_layers; ++il) {
+            if (p->debug_rows)
+                PPX_TRY(launch_copy_f32(x, p->debug_rows + ((size_t)il * n + s0) * d, M * d, s));
+            PPX_TRY(layer_rows(c, il, M, s0, pos0));
+            if (last && p->debug_hidden)
+                PPX_TRY(launch_copy_f32(x + (size_t)(M - 1) * d, p->debug_hidden + (size_t)il * d, d, s));
+        }
+        if (!last) continue;
+        const float *x_last = x + (size_t)(M - 1) * d;
+        if (prune) {
+            float *xr = c.at<float>(c.L.xr);
+            PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_copy_f32(x_last, xr, d, s));  // the one row kept
+            const int pos = p0 + n - 1;
+            for (int il = Ls; il < L; ++il) {
+                if (p->debug_rows)
+                    PPX_TRY(launch_copy_f32(xr, p->debug_rows + ((size_t)il * n + n - 1) * d, d, s));
+                PPX_TRY(layer_row(c, il, pos, tok_dev + n - 1));
+                if (p->debug_hidden) PPX_TRY(launch_copy_f32(xr, p->debug_hidden + (size_t)il * d, d, s));
+            }
+            x_last = xr;
+        }
+        PPX_TRY(head_row(c, x_last, logits));
+    }
+    return PPX_OK;
+}
+
+bool graphs_enabled() {
+    static const bool on = [] {
+        const char *v = std::getenv("PPX_NO_GRAPH");
+        return !(v && *v && *v != '0');
+    }();
+    return on;
+}
+
+// Replay the recorded launch sequence for this call's shape and buffers, or
+// record it first (on a private stream: recording runs nothing).  At most
+// kMaxGraphs sequences are kept per model, least recently used first out.
+constexpr size_t kMaxGraphs = 8;
+int run_graph(Ctx &c, const ppx_prefill_params *p, const int32_t *tok_dev, int n, int p0, int ub, bool prune,
+              float *logits) {
+    ppx_model *m = c.m;
+    ppx_model::Graph key;
+    key.kv_k = c.kv->k;
+    key.kv_vt = c.kv->vt;
+    key.ws = c.ws;
+    key.logits = logits;
+    key.n_ctx = c.kv->n_ctx;
+    key.n = n;
+    key.p0 = p0;
+    key.ub = ub;
+    key.prune = prune;
+    for (auto &g : m->graphs) {
+        if (g.kv_k == key.kv_k && g.kv_vt == key.kv_vt && g.ws == key.ws && g.logits == key.logits &&
+            g.n_ctx == key.n_ctx && g.n == key.n && g.p0 == key.p0 && g.ub == key.ub && g.prune == key.prune) {
+            g.last_use = ++m->graph_clock;
+            return hipGraphLaunch(g.exec, c.s) == hipSuccess ? PPX_OK : PPX_E_HIP;
+        }
+    }
+    if (!m->capture_stream && hipStreamCreateWithFlags(&m->capture_stream, hipStreamNonBlocking) != hipSuccess)
+        return PPX_E_HIP;
+    Ctx rc = c;
+    rc.s = m->capture_stream;
+    if (hipStreamBeginCapture(rc.s, hipStreamCaptureModeThreadLocal) != hipSuccess) return PPX_E_HIP;
+    const int st = enqueue_prefill(rc, p, tok_dev, n, p0, ub, prune, logits);
+    hipGraph_t graph = nullptr;
+    const hipError_t ec = hipStreamEndCapture(rc.s, &graph);
+    if (st != PPX_OK) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return st;
+    }
+    if (ec != hipSuccess || !graph) return PPX_E_HIP;
+    hipGraphExec_t exec = nullptr;
+    const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (ei != hipSuccess) return PPX_E_HIP;
+    if (m->graphs.size() >= kMaxGraphs) {
+        auto old = std::min_element(m->graphs.begin(), m->graphs.end(),
+                                    [](const ppx_model::Graph &x, const ppx_model::Graph &y) {
+                                        return x.last_use < y.last_use;
+                                    });
+        (void)hipGraphExecDestroy(old->exec);
+        m->graphs.erase(old);
+    }
+    key.exec = exec;
+    key.last_use = ++m->graph_clock;
+    m->graphs.push_back(key);
+    return hipGraphLaunch(exec, c.s) == hipSuccess ? PPX_OK : PPX_E_HIP;
+}
+
 int prefill(ppx_model *m, ppx_kv *kv, const int32_t *tokens, int n, const ppx_prefill_params *p, void *ws,
             size_t ws_bytes, float *logits, hipStream_t s) {
     if (!m || !kv || !p || !logits || !ws) return PPX_E_INVAL;
@@ -379,35 +484,11 @@ int prefill(ppx_model *m, ppx_kv *kv, const int32_t *tokens, int n, const ppx_pr
         std::fprintf(stderr, "[ppx] prefill %d tokens at position %d, ubatch %d, prune %s\n", n, p0, ub,
                      prune ? "on" : "off");
 
-    float *x = c.at<float>(c.L.x);
-    for (int s0 = 0; s0 < n; s0 += ub) {
-        const int M = std::min(ub, n - s0);
-        const bool last = s0 + M == n;
-        const int pos0 = p0 + s0;
-        PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_embed(m->tok, tok_dev + s0, M, m->embd_scale, x, s));
-        const int full_layers = prune ? Ls : L;
-        for (int il = 0; il < full_layers; ++il) {
-            if (p->debug_rows)
-                PPX_TRY(launch_copy_f32(x, p->debug_rows + ((size_t)il * n + s0) * d, M * d, s));
-            PPX_TRY(layer_rows(c, il, M, s0, pos0));
-            if (last && p->debug_hidden)
-                PPX_TRY(launch_copy_f32(x + (size_t)(M - 1) * d, p->debug_hidden + (size_t)il * d, d, s));
-        }
-        if (!last) continue;
-        const float *x_last = x + (size_t)(M - 1) * d;
-        if (prune) {
-            float *xr = c.at<float>(c.L.xr);
-            PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_copy_f32(x_last, xr, d, s));  // the one row kept
-            const int pos = p0 + n - 1;
-            for (int il = Ls; il < L; ++il) {
-                if (p->debug_rows)
-                    PPX_TRY(launch_copy_f32(xr, p->debug_rows + ((size_t)il * n + n - 1) * d, d, s));
-                PPX_TRY(layer_row(c, il, pos, tokens[n - 1]));
-                if (p->debug_hidden) PPX_TRY(launch_copy_f32(xr, p->debug_hidden + (size_t)il * d, d, s));
-            }
-            x_last = xr;
-        }
-        PPX_TRY(head_row(c, x_last, logits));
+    const bool graphable = !c.tm && !p->debug_rows && !p->debug_hidden && graphs_enabled();
+    if (!graphable) {
+        PPX_TRY(enqueue_prefill(c, p, tok_dev, n, p0, ub, prune, logits));
+    } else {
+        PPX_TRY(run_graph(c, p, tok_dev, n, p0, ub, prune, logits));
     }
     PPX_TRY(c.finish());
     kv->n_pos = p0 + n;

@@ -227,7 +227,7 @@ __global__ __launch_bounds__(64 * KW * G) void k_q4gemv(GemvArgs a) {
         if (G == 2) a.out[blockIdx.x * 16 + c] = act_f(a.act, yv[0]) * yv[G - 1];
         break;
     case GV_PLE: {
-        const uint8_t *prow = a.ple_raw + (size_t)a.tok * a.ple_row_blocks * 18;
+        const uint8_t *prow = a.ple_raw + (size_t)a.tok[0] * a.ple_row_blocks * 18;
 #pragma unroll
         for (int q = 0; q < G; ++q)
             a.out[n0 + 16 * q + c] = gelu_tanh_f(yv[q]) * (a.ple_s * q4_raw_weight(prow, a.ple_col0 + n0 + 16 * q + c));

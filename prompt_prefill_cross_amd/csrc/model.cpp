@@ -365,6 +365,8 @@ void model_free(ppx_model *m) {
     if (m->dev) (void)hipFree(m->dev);
     if (m->rope) (void)hipFree(m->rope);
     for (hipEvent_t e : m->events) (void)hipEventDestroy(e);
+    for (auto &g : m->graphs) (void)hipGraphExecDestroy(g.exec);
+    if (m->capture_stream) (void)hipStreamDestroy(m->capture_stream);
     delete m;
 }
 

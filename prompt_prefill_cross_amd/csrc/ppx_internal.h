@@ -71,6 +71,17 @@ struct ppx_model {
     std::unordered_map<std::string, ppx::Q4R> q4;
     std::unordered_map<std::string, int> q4_kind;  // 0 plain, 1 qkv, 2 gate|up
     std::vector<hipEvent_t> events;                // reusable pool for per-phase timing
+    // Recorded prefill launch sequences (HIP graphs), keyed by everything the
+    // kernels' arguments depend on; token ids are read from device memory.
+    struct Graph {
+        const void *kv_k = nullptr, *kv_vt = nullptr, *ws = nullptr, *logits = nullptr;
+        int n_ctx = 0, n = 0, p0 = 0, ub = 0, prune = 0;
+        hipGraphExec_t exec = nullptr;
+        unsigned long long last_use = 0;
+    };
+    std::vector<Graph> graphs;
+    unsigned long long graph_clock = 0;
+    hipStream_t capture_stream = nullptr;  // recording only; graphs run on the caller's stream
 };
 
 struct ppx_kv {
@@ -141,7 +152,8 @@ struct GemvArgs {
     const float2 *rope = nullptr;
     int act = ACT_GEGLU;
     const uint8_t *ple_raw = nullptr;
-    int tok = 0, ple_row_blocks = 0, ple_col0 = 0;
+    const int32_t *tok = nullptr;  // device pointer to the row's token id
+    int ple_row_blocks = 0, ple_col0 = 0;
     float ple_s = 0.f;
 };
 int launch_gemv(const GemvArgs &a, hipStream_t s);

@@ -115,6 +115,30 @@ def test_tiny_invariants(ppx):
     assert np.array_equal(la, ld)
 
 
+def test_recorded_launches_replay_with_new_tokens(ppx):
+    """A prefill of a shape seen before replays its recorded launch sequence;
+    the replay must read the new prompt's tokens (embedding, per-layer
+    embedding of every row, and the pruned tail's row) and give exactly the
+    result of the direct launches (the timing mode never records)."""
+    mm = engine_model(ppx, "e2b")
+    n, ub = 96, 64
+    logits = torch.empty(mm.info["n_vocab"], dtype=torch.float32, device="cuda")
+    kv = ppx.KVCache(mm, n)
+    rng = np.random.default_rng(77)
+    prompts = [rng.integers(0, mm.info["n_vocab"], n).astype(np.int32) for _ in range(3)]
+    replayed = []
+    for toks in prompts:  # the first call records, the others replay
+        kv.clear()
+        replayed.append(mm.prefill(toks, kv, n_ubatch=ub, logits=logits).clone())
+    torch.cuda.synchronize()
+    for toks, got in zip(prompts, replayed):
+        kv.clear()
+        direct = mm.prefill(toks, kv, n_ubatch=ub, timing=ppx.Timing())
+        torch.cuda.synchronize()
+        assert torch.equal(got, direct)
+    assert not torch.equal(replayed[1], replayed[2])
+
+
 def test_tiny_error_paths(ppx):
     mm = engine_model(ppx, "tiny")
     kv = ppx.KVCache(mm, 32)
