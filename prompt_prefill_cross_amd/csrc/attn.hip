@@ -76,10 +76,11 @@ struct AttnTile {
     }
 };
 
-template <int HD>
+template <int HD, int CPW>
 __global__ __launch_bounds__(256) void k_attn_prefill(AttnArgs a) {
     using T = AttnTile<HD>;
     constexpr int KB = T::KB, DT = T::DT;
+    constexpr int CB = 64 * CPW;    // query columns per workgroup
     __shared__ h8 ks[KB * 4 * 64];  // K fragments [d step][16-key block][lane]
     __shared__ h8 vs[DT * 2 * 64];  // V^T fragments [d subtile][32-key step][lane]
 
@@ -88,27 +89,41 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnArgs a) {
     const int cb = blockIdx.x, ck = blockIdx.y, kvh = blockIdx.z;
     const int lc = lane & 15, lg = lane >> 4;
 
-    const int tmax = min(a.M - 1, (cb * 64 + 63) / G);
+    const int tmax = min(a.M - 1, (cb * CB + CB - 1) / G);
     const int pend = a.pos0 + tmax;  // last key any column here can see
     const int kbeg = ck * a.kc;
     if (kbeg > pend) return;
     const int kend = min(kbeg + a.kc, pend + 1);
 
-    const int col = cb * 64 + wave * 16 + lc;
-    const int t = col / G, hg = col % G;
-    const bool valid = t < a.M;
-    const int h = kvh * G + hg;
-    const int qpos = a.pos0 + (valid ? t : 0);
-
-    h8 qf[KB];
+    // a wave owns CPW groups of 16 query columns; every K / V^T fragment read
+    // from LDS feeds one MFMA per group
+    int t[CPW], h[CPW], qpos[CPW];
+    bool valid[CPW];
+    h8 qf[CPW][KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-        qf[kb] = *reinterpret_cast<const h8 *>(a.q + ((size_t)min(t, a.M - 1) * a.H + h) * HD + kb * 32 + lg * 8);
-
-    f4 oacc[DT];
+    for (int c = 0; c < CPW; ++c) {
+        const int col = cb * CB + wave * 16 * CPW + c * 16 + lc;
+        t[c] = col / G;
+        valid[c] = t[c] < a.M;
+        h[c] = kvh * G + col % G;
+        qpos[c] = a.pos0 + (valid[c] ? t[c] : 0);
 #pragma unroll
-    for (int i = 0; i < DT; ++i) oacc[i] = f4{0.f, 0.f, 0.f, 0.f};
-    float mrun = -INFINITY, lrun = 0.f;
+        for (int kb = 0; kb < KB; ++kb)
+            qf[c][kb] = *reinterpret_cast<const h8 *>(a.q + ((size_t)min(t[c], a.M - 1) * a.H + h[c]) * HD + kb * 32 +
+                                                      lg * 8);
+    }
+
+    f4 oacc[CPW][DT];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+        for (int i = 0; i < DT; ++i) oacc[c][i] = f4{0.f, 0.f, 0.f, 0.f};
+    float mrun[CPW], lrun[CPW];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+        mrun[c] = -INFINITY;
+        lrun[c] = 0.f;
+    }
     const float sl2 = 1.4426950408889634f / sqrtf((float)HD);
 
     T tile;
@@ -120,73 +135,88 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnArgs a) {
         __syncthreads();
         tile.load(a, kvh, min(t0 + KT, kbeg + (ntiles - 1) * KT), pend);  // next tile (clamped)
 
-        // S^T = K Q^T: s[j][r] is key t0 + 32(j/2) + 8 lg + 4(j%2) + r, query column lc
-        f4 s[4];
+        // S^T = K Q^T: s[c][j][r] is key t0 + 32(j/2) + 8 lg + 4(j%2) + r, query column lc of group c
+        f4 s[CPW][4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            s[j] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) s[j] = mfma16(ks[(kb * 4 + j) * 64 + lane], qf[kb], s[j]);
+            for (int c = 0; c < CPW; ++c) s[c][j] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const h8 kf = ks[(kb * 4 + j) * 64 + lane];
+#pragma unroll
+                for (int c = 0; c < CPW; ++c) s[c][j] = mfma16(kf, qf[c][kb], s[c][j]);
+            }
         }
-        float tmx = -INFINITY;
+        h8 pf[CPW][2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int c = 0; c < CPW; ++c) {
+            float tmx = -INFINITY;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int kp = t0 + (j >> 1) * 32 + 8 * lg + 4 * (j & 1) + r;
-                const float v = (kp <= qpos) ? s[j][r] * sl2 : -INFINITY;
-                s[j][r] = v;
-                tmx = fmaxf(tmx, v);
-            }
-        tmx = fmaxf(tmx, __shfl_xor(tmx, 16, 64));
-        tmx = fmaxf(tmx, __shfl_xor(tmx, 32, 64));
-        const float mnew = fmaxf(mrun, tmx);
-        const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(mrun - mnew);
-        float psum = 0.f;
-        h8 pf[2];
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+                for (int r = 0; r < 4; ++r) {
+                    const int kp = t0 + (j >> 1) * 32 + 8 * lg + 4 * (j & 1) + r;
+                    const float v = (kp <= qpos[c]) ? s[c][j][r] * sl2 : -INFINITY;
+                    s[c][j][r] = v;
+                    tmx = fmaxf(tmx, v);
+                }
+            tmx = fmaxf(tmx, __shfl_xor(tmx, 16, 64));
+            tmx = fmaxf(tmx, __shfl_xor(tmx, 32, 64));
+            const float mnew = fmaxf(mrun[c], tmx);
+            const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(mrun[c] - mnew);
+            float psum = 0.f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float p = (s[j][r] == -INFINITY) ? 0.f : exp2f(s[j][r] - mnew);
-                psum += p;
-                pf[j >> 1][(j & 1) * 4 + r] = (_Float16)p;
-            }
-        psum += __shfl_xor(psum, 16, 64);
-        psum += __shfl_xor(psum, 32, 64);
-        lrun = lrun * alpha + psum;
-        mrun = mnew;
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
+                for (int r = 0; r < 4; ++r) {
+                    const float p = (s[c][j][r] == -INFINITY) ? 0.f : exp2f(s[c][j][r] - mnew);
+                    psum += p;
+                    pf[c][j >> 1][(j & 1) * 4 + r] = (_Float16)p;
+                }
+            psum += __shfl_xor(psum, 16, 64);
+            psum += __shfl_xor(psum, 32, 64);
+            lrun[c] = lrun[c] * alpha + psum;
+            mrun[c] = mnew;
+#pragma unroll
+            for (int i = 0; i < DT; ++i) oacc[c][i] *= alpha;
+        }
         // O^T += V^T P^T; step kb2 covers keys t0 + 32 kb2 + 8 lg + 0..7 in lane group lg
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-            for (int i = 0; i < DT; ++i) oacc[i] = mfma16(vs[(i * 2 + kb2) * 64 + lane], pf[kb2], oacc[i]);
+            for (int i = 0; i < DT; ++i) {
+                const h8 vf = vs[(i * 2 + kb2) * 64 + lane];
+#pragma unroll
+                for (int c = 0; c < CPW; ++c) oacc[c][i] = mfma16(vf, pf[c][kb2], oacc[c][i]);
+            }
         __syncthreads();
     }
 
-    if (!valid) return;
-    if (a.nkc == 1) {
-        const float inv = 1.0f / lrun;
-        const int od = a.H * HD;
 #pragma unroll
-        for (int i = 0; i < DT; ++i) {
-            const int d = i * 16 + lg * 4;  // four consecutive columns: 8 contiguous bytes of the tiled layout
-            h4 v;
+    for (int c = 0; c < CPW; ++c) {
+        if (!valid[c]) continue;
+        if (a.nkc == 1) {
+            const float inv = 1.0f / lrun[c];
+            const int od = a.H * HD;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = (_Float16)(oacc[i][r] * inv);
-            *reinterpret_cast<h4 *>(a.o + tiled_index(t, h * HD + d, od)) = v;
-        }
-    } else {
-        const size_t slot = ((size_t)ck * a.M + t) * a.H + h;
-        float *po = a.part + slot * HD;
+            for (int i = 0; i < DT; ++i) {
+                const int d = i * 16 + lg * 4;  // four consecutive columns: 8 contiguous bytes of the tiled layout
+                h4 v;
 #pragma unroll
-        for (int i = 0; i < DT; ++i) *reinterpret_cast<f4 *>(po + i * 16 + lg * 4) = oacc[i];
-        if (lg == 0) {
-            float *pm = a.part + (size_t)a.nkc * a.M * a.H * HD + slot * 2;
-            pm[0] = mrun;
-            pm[1] = lrun;
+                for (int r = 0; r < 4; ++r) v[r] = (_Float16)(oacc[c][i][r] * inv);
+                *reinterpret_cast<h4 *>(a.o + tiled_index(t[c], h[c] * HD + d, od)) = v;
+            }
+        } else {
+            const size_t slot = ((size_t)ck * a.M + t[c]) * a.H + h[c];
+            float *po = a.part + slot * HD;
+#pragma unroll
+            for (int i = 0; i < DT; ++i) *reinterpret_cast<f4 *>(po + i * 16 + lg * 4) = oacc[c][i];
+            if (lg == 0) {
+                float *pm = a.part + (size_t)a.nkc * a.M * a.H * HD + slot * 2;
+                pm[0] = mrun[c];
+                pm[1] = lrun[c];
+            }
         }
     }
 }
@@ -347,9 +377,13 @@ int ok() { return hipGetLastError() == hipSuccess ? PPX_OK : PPX_E_HIP; }
 
 }  // namespace
 
+// Column groups of 16 per wave (64 query columns per group of four waves); two
+// groups halve the LDS reads per MFMA but spill at head_dim 256.
+constexpr int ATTN_CPW = 1;
+
 AttnSplit attn_split(int M, int H, int KVH, int pos0) {
     const int G = H / KVH;
-    const int colblocks = (M * G + 63) / 64;
+    const int colblocks = (M * G + 64 * ATTN_CPW - 1) / (64 * ATTN_CPW);
     const int P = pos0 + M;
     int want = (256 + colblocks * KVH - 1) / (colblocks * KVH);
     want = std::max(1, std::min(want, ATTN_MAX_CHUNKS));
@@ -375,11 +409,11 @@ int launch_attn_prefill(const AttnArgs &a0, hipStream_t s) {
     a.kc = sp.kc;
     a.nkc = sp.nkc;
     if (a.nkc > 1 && !a.part) return PPX_E_INVAL;
-    dim3 grid((a.M * G + 63) / 64, a.nkc, a.KVH);
+    dim3 grid((a.M * G + 64 * ATTN_CPW - 1) / (64 * ATTN_CPW), a.nkc, a.KVH);
     switch (a.hd) {
-    case 64: hipLaunchKernelGGL(k_attn_prefill<64>, grid, dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL(k_attn_prefill<128>, grid, dim3(256), 0, s, a); break;
-    case 256: hipLaunchKernelGGL(k_attn_prefill<256>, grid, dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((k_attn_prefill<64, ATTN_CPW>), grid, dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((k_attn_prefill<128, ATTN_CPW>), grid, dim3(256), 0, s, a); break;
+    case 256: hipLaunchKernelGGL((k_attn_prefill<256, ATTN_CPW>), grid, dim3(256), 0, s, a); break;
     default: return PPX_E_UNSUPPORTED;
     }
     if (a.nkc == 1) return ok();
