@@ -25,11 +25,23 @@ namespace {
 
 inline size_t al(size_t x) { return (x + 255) / 256 * 256; }
 
-// Workspace layout of one prefill (offsets from the workspace base).
+// Ubatches in flight at once: ubatch u runs on slot u % kSlots (its own
+// stream and its own activation buffers), and its attention waits only for
+// the earlier ubatches' K/V of that layer.  Measured on the E2B-like shapes
+// with two slots, kernels of the two streams overlapped in under 5% of the
+// launches (each launch already occupies every CU) and the prefill got
+// slower, so one slot is used: the schedule is then the plain serial one.
+constexpr int kSlots = 1;
+
+// Workspace layout of one prefill (offsets from the workspace base).  The
+// per-ubatch buffers (x .. ap_part) repeat once per slot, slot_stride apart.
 struct WsLayout {
-    size_t tok, x, a16, a16lo, q16, o16, h16, p16;
-    size_t xr, ar, qr, orow, hr, pr;
-    size_t at_part, ap_part;
+    size_t tok;
+    size_t x, a16, a16lo, q16, o16, h16, p16, ap_part;  // slot 0
+    size_t slot_stride;
+    int nslots;
+    size_t xr, qr, orow, hr, pr;
+    size_t at_part;
     size_t total;
 };
 
@@ -45,6 +57,7 @@ WsLayout ws_layout(const ppx_model *m, int ub, int n_ctx) {
     };
     const size_t ub16 = (size_t)(ub + 15) / 16 * 16;  // fragment-tiled buffers hold whole 16-row tiles
     w.tok = take(sizeof(int32_t) * (size_t)std::max(n_ctx, 1));
+    const size_t s0 = o;
     w.x = take(4ull * ub * d);
     w.a16 = take(2ull * ub16 * std::max(d, 1));
     w.a16lo = take(2ull * ub16 * std::max(d, 1));
@@ -52,14 +65,16 @@ WsLayout ws_layout(const ppx_model *m, int ub, int n_ctx) {
     w.o16 = take(2ull * ub16 * qd);
     w.h16 = take(2ull * ub16 * F);
     w.p16 = take(2ull * ub16 * std::max(E, 1));
+    w.ap_part = take(4 * attn_prefill_scratch_floats(ub, I.n_head, I.head_dim, std::max(n_ctx, 1)));
+    w.slot_stride = o - s0;
+    w.nslots = kSlots;
+    o += w.slot_stride * (kSlots - 1);
     w.xr = take(4ull * d);
-    w.ar = take(4ull * d);
     w.qr = take(4ull * qd);
     w.orow = take(4ull * qd);
     w.hr = take(4ull * F);
     w.pr = take(4ull * std::max(E, 1));
     w.at_part = take(4 * attn1_scratch_floats(I.n_head, I.head_dim, std::max(n_ctx, 1)));
-    w.ap_part = take(4 * attn_prefill_scratch_floats(ub, I.n_head, I.head_dim, std::max(n_ctx, 1)));
     w.total = o;
     return w;
 }
@@ -77,11 +92,20 @@ struct Ctx {
     uint8_t *ws;
     WsLayout L;
     ppx_timing *tm = nullptr;  // per-phase timing requested
+    int slot = 0;              // buffers of the ubatch being enqueued
+    // K/V ordering between ubatches on different streams: after writing layer
+    // l's K/V, kv_done[l] is recorded; before attention reads layer l's cache,
+    // kv_wait[l] (the previous ubatch's record, if on another stream) is
+    // waited for.  Null entries mean no ordering is needed.
+    std::vector<hipEvent_t> kv_done, kv_wait;
     struct Rec { int phase; hipEvent_t a, b; bool glu; };
     std::vector<Rec> recs;
     size_t next_ev = 0;
     template <typename T>
     T *at(size_t off) const { return reinterpret_cast<T *>(ws + off); }
+    // a per-ubatch buffer of the current slot
+    template <typename T>
+    T *sl(size_t off) const { return reinterpret_cast<T *>(ws + off + (size_t)slot * L.slot_stride); }
 
     hipEvent_t event() {
         if (next_ev == m->events.size()) {
@@ -137,15 +161,15 @@ int layer_rows(Ctx &c, int il, int M, int row0, int pos0) {
     const ppx_model_info &I = m->info;
     const LayerW &w = m->layers[il];
     const int d = I.d_model, hd = I.head_dim, qd = I.n_head * hd, kvd = I.kv_dim, F = I.n_ff;
-    float *x = c.at<float>(c.L.x);
-    __half *a16 = c.at<__half>(c.L.a16);
-    __half *q16 = c.at<__half>(c.L.q16);
-    __half *o16 = c.at<__half>(c.L.o16);
-    __half *h16 = c.at<__half>(c.L.h16);
+    float *x = c.sl<float>(c.L.x);
+    __half *a16 = c.sl<__half>(c.L.a16);
+    __half *q16 = c.sl<__half>(c.L.q16);
+    __half *o16 = c.sl<__half>(c.L.o16);
+    __half *h16 = c.sl<__half>(c.L.h16);
     const size_t lstride = (size_t)c.kv->n_ctx * kvd;
     const size_t vstride = (size_t)c.kv->vld * kvd;
 
-    __half *a16lo = c.at<__half>(c.L.a16lo);
+    __half *a16lo = c.sl<__half>(c.L.a16lo);
     if (w.own)
         PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_rmsnorm_split(x, w.attn_norm, m->eps, M, d, a16, a16lo, c.s));
     else
@@ -176,13 +200,18 @@ int layer_rows(Ctx &c, int il, int M, int row0, int pos0) {
         gk.vld = c.kv->vld;
         PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm_exact(gk, c.s));
     }
+    // earlier ubatches' K/V of the layer read here (owning: this layer; shared: its source)
+    if (!c.kv_wait.empty() && c.kv_wait[w.src] && hipStreamWaitEvent(c.s, c.kv_wait[w.src], 0) != hipSuccess)
+        return PPX_E_HIP;
+    if (w.own && !c.kv_done.empty() && c.kv_done[il] && hipEventRecord(c.kv_done[il], c.s) != hipSuccess)
+        return PPX_E_HIP;
 
     AttnArgs at;
     at.q = q16;
     at.k = c.kv->k + (size_t)w.src * lstride;
     at.vt = c.kv->vt + (size_t)w.src * vstride;
     at.vld = c.kv->vld;
-    at.part = c.at<float>(c.L.ap_part);
+    at.part = c.sl<float>(c.L.ap_part);
     at.o = o16;
     at.M = M;
     at.H = I.n_head;
@@ -226,7 +255,7 @@ int layer_rows(Ctx &c, int il, int M, int row0, int pos0) {
 
     if (I.ple_dim) {
         const int E = I.ple_dim;
-        __half *p16 = c.at<__half>(c.L.p16);
+        __half *p16 = c.sl<__half>(c.L.p16);
         PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_rmsnorm_f16(x, w.ple_norm, m->eps, M, d, a16, c.s));
         GemmArgs gp;
         gp.A = a16;
@@ -341,20 +370,57 @@ int head_row(Ctx &c, const float *x_last, float *logits) {
     return PPX_OK;
 }
 
+// Events for ordering work across streams, from a model-owned pool (reused
+// from call to call: every use is a record followed by waits in stream order).
+int sync_events(ppx_model *m, size_t n, std::vector<hipEvent_t> &out) {
+    while (m->sync_events.size() < n) {
+        hipEvent_t e;
+        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return PPX_E_HIP;
+        m->sync_events.push_back(e);
+    }
+    out.assign(m->sync_events.begin(), m->sync_events.begin() + n);
+    return PPX_OK;
+}
+
 // The launch sequence of one prefill call (all ubatches, the pruned tail and
 // the head).  Token ids are read from tok_dev, so the sequence can be recorded
-// once and replayed for any prompt of the same shape.
+// once and replayed for any prompt of the same shape.  With several streams,
+// ubatch u runs on streams[u % S] with slot u % S's buffers; the streams fork
+// from and join back into streams[0], and attention waits for the previous
+// ubatch's K/V of the layer it reads.
 int enqueue_prefill(Ctx &c, const ppx_prefill_params *p, const int32_t *tok_dev, int n, int p0, int ub,
-                    bool prune, float *logits) {
+                    bool prune, float *logits, hipStream_t *streams, int nstreams) {
     ppx_model *m = c.m;
     const ppx_model_info &I = m->info;
     const int L = I.n_layer, Ls = I.n_layer_kv_from_start, d = I.d_model;
-    hipStream_t s = c.s;
-    float *x = c.at<float>(c.L.x);
-    for (int s0 = 0; s0 < n; s0 += ub) {
+    const int nub = (n + ub - 1) / ub;
+    const int S = std::max(1, std::min({nstreams, nub, c.L.nslots}));
+    std::vector<hipEvent_t> ev;
+    if (S > 1) {
+        // [0] fork, [1..S-1] joins, then per ubatch the K/V record of every layer
+        PPX_TRY(sync_events(m, (size_t)S + (size_t)nub * L, ev));
+        if (hipEventRecord(ev[0], streams[0]) != hipSuccess) return PPX_E_HIP;
+        for (int k = 1; k < S; ++k)
+            if (hipStreamWaitEvent(streams[k], ev[0], 0) != hipSuccess) return PPX_E_HIP;
+    }
+    auto kv_ev = [&](int u, int l) { return ev[(size_t)S + (size_t)u * L + l]; };
+
+    for (int u = 0; u < nub; ++u) {
+        const int s0 = u * ub;
         const int M = std::min(ub, n - s0);
         const bool last = s0 + M == n;
         const int pos0 = p0 + s0;
+        c.slot = u % S;
+        c.s = streams[c.slot];
+        hipStream_t s = c.s;
+        c.kv_done.assign(S > 1 ? L : 0, nullptr);
+        c.kv_wait.assign(S > 1 ? L : 0, nullptr);
+        if (S > 1)
+            for (int l = 0; l < Ls; ++l) {
+                c.kv_done[l] = kv_ev(u, l);
+                if (u > 0) c.kv_wait[l] = kv_ev(u - 1, l);
+            }
+        float *x = c.sl<float>(c.L.x);
         PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_embed(m->tok, tok_dev + s0, M, m->embd_scale, x, s));
         const int full_layers = prune ? Ls : L;
         for (int il = 0; il < full_layers; ++il) {
@@ -380,6 +446,30 @@ int enqueue_prefill(Ctx &c, const ppx_prefill_params *p, const int32_t *tok_dev,
         }
         PPX_TRY(head_row(c, x_last, logits));
     }
+    if (S > 1) {
+        for (int k = 1; k < S; ++k) {
+            if (hipEventRecord(ev[k], streams[k]) != hipSuccess) return PPX_E_HIP;
+            if (hipStreamWaitEvent(streams[0], ev[k], 0) != hipSuccess) return PPX_E_HIP;
+        }
+    }
+    c.slot = 0;
+    c.s = streams[0];
+    c.kv_done.clear();
+    c.kv_wait.clear();
+    return PPX_OK;
+}
+
+// Streams for ubatches in flight: streams[0] is `main`, the others are
+// model-owned (separate sets for direct launches and for recording).
+int slot_streams(ppx_model *m, hipStream_t main, bool recording, hipStream_t *out) {
+    std::vector<hipStream_t> &pool = recording ? m->capture_aux : m->aux_streams;
+    while ((int)pool.size() < kSlots - 1) {
+        hipStream_t st;
+        if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return PPX_E_HIP;
+        pool.push_back(st);
+    }
+    out[0] = main;
+    for (int k = 1; k < kSlots; ++k) out[k] = pool[k - 1];
     return PPX_OK;
 }
 
@@ -419,8 +509,10 @@ int run_graph(Ctx &c, const ppx_prefill_params *p, const int32_t *tok_dev, int n
         return PPX_E_HIP;
     Ctx rc = c;
     rc.s = m->capture_stream;
+    hipStream_t streams[kSlots];
+    PPX_TRY(slot_streams(m, rc.s, true, streams));
     if (hipStreamBeginCapture(rc.s, hipStreamCaptureModeThreadLocal) != hipSuccess) return PPX_E_HIP;
-    const int st = enqueue_prefill(rc, p, tok_dev, n, p0, ub, prune, logits);
+    const int st = enqueue_prefill(rc, p, tok_dev, n, p0, ub, prune, logits, streams, kSlots);
     hipGraph_t graph = nullptr;
     const hipError_t ec = hipStreamEndCapture(rc.s, &graph);
     if (st != PPX_OK) {
@@ -486,7 +578,11 @@ int prefill(ppx_model *m, ppx_kv *kv, const int32_t *tokens, int n, const ppx_pr
 
     const bool graphable = !c.tm && !p->debug_rows && !p->debug_hidden && graphs_enabled();
     if (!graphable) {
-        PPX_TRY(enqueue_prefill(c, p, tok_dev, n, p0, ub, prune, logits));
+        // timing and debug outputs keep every launch on the caller's stream, in order
+        const bool serial = c.tm || p->debug_rows || p->debug_hidden;
+        hipStream_t streams[kSlots];
+        PPX_TRY(slot_streams(m, s, false, streams));
+        PPX_TRY(enqueue_prefill(c, p, tok_dev, n, p0, ub, prune, logits, streams, serial ? 1 : kSlots));
     } else {
         PPX_TRY(run_graph(c, p, tok_dev, n, p0, ub, prune, logits));
     }

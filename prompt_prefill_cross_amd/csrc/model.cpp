@@ -367,6 +367,9 @@ void model_free(ppx_model *m) {
     for (hipEvent_t e : m->events) (void)hipEventDestroy(e);
     for (auto &g : m->graphs) (void)hipGraphExecDestroy(g.exec);
     if (m->capture_stream) (void)hipStreamDestroy(m->capture_stream);
+    for (hipStream_t st : m->aux_streams) (void)hipStreamDestroy(st);
+    for (hipStream_t st : m->capture_aux) (void)hipStreamDestroy(st);
+    for (hipEvent_t e : m->sync_events) (void)hipEventDestroy(e);
     delete m;
 }
 

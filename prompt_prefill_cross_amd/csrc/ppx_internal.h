@@ -82,6 +82,9 @@ struct ppx_model {
     std::vector<Graph> graphs;
     unsigned long long graph_clock = 0;
     hipStream_t capture_stream = nullptr;  // recording only; graphs run on the caller's stream
+    std::vector<hipStream_t> aux_streams;  // ubatches in flight, direct launches
+    std::vector<hipStream_t> capture_aux;  // ubatches in flight, recording
+    std::vector<hipEvent_t> sync_events;   // cross-stream ordering inside one prefill
 };
 
 struct ppx_kv {
