@@ -203,19 +203,26 @@ int ppx_op_tile_f16(const void *src_dev, int M, int K, void *dst_dev, void *hip_
 /* Dequantise a whole Q4_0 tensor from the engine's repacked device layout
  * into fp32 [rows][cols] row-major (exact). */
 int ppx_op_dequant(const ppx_model *m, const char *tensor, float *out_dev, void *hip_stream);
+/* Bytes of scratch ppx_op_gemm / ppx_op_gemm_glu use for an M-row product
+ * with the named tensor when K is split over workgroups (fp32 partial tiles,
+ * summed in split order by a second kernel); 0 when that shape is not split. */
+size_t ppx_op_gemm_workspace_bytes(const ppx_model *m, const char *tensor, int M);
 /* C[M][N] (fp32, ldc = N) = A[M][K] (fp16, fragment-tiled) x W^T on the
- * MFMA GEMM path, W = the named container tensor [N][K]. */
+ * MFMA GEMM path, W = the named container tensor [N][K].  ws_dev: scratch of
+ * ppx_op_gemm_workspace_bytes bytes, or NULL (the product then runs without
+ * the split; results are equal up to the order of the fp32 sums). */
 int ppx_op_gemm(const ppx_model *m, const char *tensor, const void *a_dev_f16, int M, float *c_dev,
-                void *hip_stream);
+                void *ws_dev, size_t ws_bytes, void *hip_stream);
 /* The gate|up GEMM of a layer with its fused activation epilogue, exactly
  * as the prefill runs it for the row-batched layers (the GeGLU feed-forward
  * of the Gemma-style decoder of "llama.cpp Gemma 4 prefill KV graph
  * optimization"; SwiGLU for a model whose activation is SwiGLU):
  * h[M][F] (fp16, fragment-tiled) = act(A Wg^T) * (A Wu^T), A fp16 [M][K]
  * fragment-tiled.  `tensor` must be a fused gate|up name ("blk.i.ffn_gate");
- * PPX_E_INVAL otherwise.  Asynchronous on the stream. */
+ * PPX_E_INVAL otherwise.  ws_dev as for ppx_op_gemm.  Asynchronous on the
+ * stream. */
 int ppx_op_gemm_glu(const ppx_model *m, const char *tensor, const void *a_dev_f16, int M, void *h_dev_f16,
-                    void *hip_stream);
+                    void *ws_dev, size_t ws_bytes, void *hip_stream);
 /* The same on the exact-weight path used for the fused K|V weight
  * ("blk.i.wk", owning layers): A = a_hi + a_lo (two fp16 [M][K] arrays,
  * fragment-tiled),

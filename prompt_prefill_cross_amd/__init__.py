@@ -77,8 +77,9 @@ SIGNATURES = [
     ("ppx_prune_predicate", c_int, [c_int, c_int, c_int, c_int, POINTER(c_uint8), c_int]),
     ("ppx_op_dequant", c_int, [c_void_p, c_char_p, c_void_p, c_void_p]),
     ("ppx_op_tile_f16", c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p]),
-    ("ppx_op_gemm", c_int, [c_void_p, c_char_p, c_void_p, c_int, c_void_p, c_void_p]),
-    ("ppx_op_gemm_glu", c_int, [c_void_p, c_char_p, c_void_p, c_int, c_void_p, c_void_p]),
+    ("ppx_op_gemm_workspace_bytes", c_size_t, [c_void_p, c_char_p, c_int]),
+    ("ppx_op_gemm", c_int, [c_void_p, c_char_p, c_void_p, c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
+    ("ppx_op_gemm_glu", c_int, [c_void_p, c_char_p, c_void_p, c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
     ("ppx_op_gemm_exact", c_int, [c_void_p, c_char_p, c_void_p, c_void_p, c_int, c_void_p, c_void_p]),
     ("ppx_op_gemv", c_int, [c_void_p, c_char_p, c_void_p, c_void_p, c_void_p]),
     ("ppx_op_attention", c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p,
@@ -230,14 +231,26 @@ class Model:
         _check(lib().ppx_op_tile_f16(_ptr(a), M, K, _ptr(t), _stream()), "ppx_op_tile_f16")
         return t
 
-    def op_gemm(self, name: str, a):
-        """C = A W^T (fp32 [M][N]) for row-major fp16 A [M][K]."""
+    def _gemm_ws(self, name: str, M: int, split: bool):
+        """(tensor or None, bytes): scratch for a K split over workgroups."""
+        import torch
+        nb = lib().ppx_op_gemm_workspace_bytes(self._h, name.encode(), M) if split else 0
+        if not nb:
+            return None, 0
+        return torch.empty(nb, dtype=torch.uint8, device="cuda"), nb
+
+    def op_gemm(self, name: str, a, split: bool = True):
+        """C = A W^T (fp32 [M][N]) for row-major fp16 A [M][K].  split=False
+        runs shapes the engine splits over workgroups without the split."""
         import torch
         rows, cols = self._shape(name)
         assert a.shape[1] == cols
-        c = torch.empty((a.shape[0], rows), dtype=torch.float32, device="cuda")
+        M = a.shape[0]
+        c = torch.empty((M, rows), dtype=torch.float32, device="cuda")
         at = self.tile(a)  # kept alive until the launch is queued
-        _check(lib().ppx_op_gemm(self._h, name.encode(), _ptr(at), a.shape[0], _ptr(c), _stream()), "ppx_op_gemm")
+        ws, nb = self._gemm_ws(name, M, split)
+        _check(lib().ppx_op_gemm(self._h, name.encode(), _ptr(at), M, _ptr(c), _ptr(ws) if nb else None, nb,
+                                 _stream()), "ppx_op_gemm")
         return c
 
     def op_gemm_glu(self, name: str, a, M: int = None, out=None, raw: bool = False):
@@ -255,7 +268,9 @@ class Model:
         if out is None:
             out = torch.empty(Mp * F, dtype=torch.float16, device="cuda")
         assert out.dtype == torch.float16 and out.numel() >= Mp * F
-        _check(lib().ppx_op_gemm_glu(self._h, name.encode(), _ptr(a), M, _ptr(out), _stream()), "ppx_op_gemm_glu")
+        ws, nb = self._gemm_ws(name, M, True)
+        _check(lib().ppx_op_gemm_glu(self._h, name.encode(), _ptr(a), M, _ptr(out), _ptr(ws) if nb else None, nb,
+                                     _stream()), "ppx_op_gemm_glu")
         return out if raw else self.untile(out, M, F)
 
     def op_gemm_exact(self, name: str, a_hi, a_lo):

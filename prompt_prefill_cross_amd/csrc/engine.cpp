@@ -37,7 +37,8 @@ constexpr int kSlots = 1;
 // per-ubatch buffers (x .. ap_part) repeat once per slot, slot_stride apart.
 struct WsLayout {
     size_t tok;
-    size_t x, a16, a16lo, q16, o16, h16, p16, ap_part;  // slot 0
+    size_t x, a16, a16lo, q16, o16, h16, p16, ap_part, gpart;  // slot 0
+    size_t gpart_floats;                                       // split-K partials of one GEMM
     size_t slot_stride;
     int nslots;
     size_t xr, qr, orow, hr, pr;
@@ -66,6 +67,15 @@ WsLayout ws_layout(const ppx_model *m, int ub, int n_ctx) {
     w.h16 = take(2ull * ub16 * F);
     w.p16 = take(2ull * ub16 * std::max(E, 1));
     w.ap_part = take(4 * attn_prefill_scratch_floats(ub, I.n_head, I.head_dim, std::max(n_ctx, 1)));
+    {
+        const int kvd = I.kv_dim;
+        const int shapes[][2] = {{qd, d}, {2 * kvd, d}, {d, qd}, {2 * F, d}, {d, F}, {E, d}, {d, E}};
+        size_t pf = 0;
+        for (const auto &nk : shapes)
+            if (nk[0] > 0 && nk[1] > 0) pf = std::max(pf, gemm_part_floats(ub, nk[0], nk[1]));
+        w.gpart_floats = pf;
+        w.gpart = take(4 * std::max<size_t>(pf, 1));
+    }
     w.slot_stride = o - s0;
     w.nslots = kSlots;
     o += w.slot_stride * (kSlots - 1);
@@ -106,6 +116,13 @@ struct Ctx {
     // a per-ubatch buffer of the current slot
     template <typename T>
     T *sl(size_t off) const { return reinterpret_cast<T *>(ws + off + (size_t)slot * L.slot_stride); }
+    // a row-batched GEMM of the current slot, with the slot's split-K partial space
+    GemmArgs gemm() const {
+        GemmArgs g;
+        g.part = sl<float>(L.gpart);
+        g.part_floats = L.gpart_floats;
+        return g;
+    }
 
     hipEvent_t event() {
         if (next_ev == m->events.size()) {
@@ -174,7 +191,7 @@ int layer_rows(Ctx &c, int il, int M, int row0, int pos0) {
         PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_rmsnorm_split(x, w.attn_norm, m->eps, M, d, a16, a16lo, c.s));
     else
         PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_rmsnorm_f16(x, w.attn_norm, m->eps, M, d, a16, c.s));
-    GemmArgs g;
+    GemmArgs g = c.gemm();
     g.A = a16;
     g.lda = d;
     g.M = M;
@@ -220,7 +237,7 @@ int layer_rows(Ctx &c, int il, int M, int row0, int pos0) {
     at.pos0 = pos0;
     PPX_LAUNCH(c, PPX_PHASE_ATTN, launch_attn_prefill(at, c.s));
 
-    GemmArgs go;
+    GemmArgs go = c.gemm();
     go.A = o16;
     go.lda = qd;
     go.M = M;
@@ -230,7 +247,7 @@ int layer_rows(Ctx &c, int il, int M, int row0, int pos0) {
     PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm(go, c.s));
 
     PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_rmsnorm_f16(x, w.ffn_norm, m->eps, M, d, a16, c.s));
-    GemmArgs gu;
+    GemmArgs gu = c.gemm();
     gu.A = a16;
     gu.lda = d;
     gu.M = M;
@@ -244,7 +261,7 @@ int layer_rows(Ctx &c, int il, int M, int row0, int pos0) {
         c.end(PPX_PHASE_GEMM, ev0, true);
     }
 
-    GemmArgs gd;
+    GemmArgs gd = c.gemm();
     gd.A = h16;
     gd.lda = F;
     gd.M = M;
@@ -257,7 +274,7 @@ int layer_rows(Ctx &c, int il, int M, int row0, int pos0) {
         const int E = I.ple_dim;
         __half *p16 = c.sl<__half>(c.L.p16);
         PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_rmsnorm_f16(x, w.ple_norm, m->eps, M, d, a16, c.s));
-        GemmArgs gp;
+        GemmArgs gp = c.gemm();
         gp.A = a16;
         gp.lda = d;
         gp.M = M;
@@ -270,7 +287,7 @@ int layer_rows(Ctx &c, int il, int M, int row0, int pos0) {
         gp.ple_col0 = il * E;
         gp.ple_s = w.ple_s;
         PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm(gp, c.s));
-        GemmArgs gq;
+        GemmArgs gq = c.gemm();
         gq.A = p16;
         gq.lda = E;
         gq.M = M;
@@ -814,13 +831,22 @@ int ppx_op_dequant(const ppx_model *m, const char *tensor, float *out_dev, void 
     return launch_dequant(*w, out_dev, (hipStream_t)hip_stream);
 }
 
-int ppx_op_gemm(const ppx_model *m, const char *tensor, const void *a_dev_f16, int M, float *c_dev,
-                void *hip_stream) {
+size_t ppx_op_gemm_workspace_bytes(const ppx_model *m, const char *tensor, int M) {
+    int kind;
+    const Q4R *w = find_q4(m, tensor, &kind);
+    if (!w || M <= 0) return 0;
+    return 4 * gemm_part_floats(M, w->N, w->K);
+}
+
+int ppx_op_gemm(const ppx_model *m, const char *tensor, const void *a_dev_f16, int M, float *c_dev, void *ws_dev,
+                size_t ws_bytes, void *hip_stream) {
     int kind;
     const Q4R *w = find_q4(m, tensor, &kind);
     if (!w || !a_dev_f16 || !c_dev || M < 0) return PPX_E_INVAL;
     if (kind == 3) return PPX_E_INVAL;  // exact-weight tensors go through ppx_op_gemm_exact
     GemmArgs g;
+    g.part = static_cast<float *>(ws_dev);
+    g.part_floats = ws_dev ? ws_bytes / 4 : 0;
     g.A = static_cast<const __half *>(a_dev_f16);
     g.lda = w->K;
     g.M = M;
@@ -831,11 +857,13 @@ int ppx_op_gemm(const ppx_model *m, const char *tensor, const void *a_dev_f16, i
 }
 
 int ppx_op_gemm_glu(const ppx_model *m, const char *tensor, const void *a_dev_f16, int M, void *h_dev_f16,
-                    void *hip_stream) {
+                    void *ws_dev, size_t ws_bytes, void *hip_stream) {
     int kind;
     const Q4R *w = find_q4(m, tensor, &kind);
     if (!w || kind != 2 || !a_dev_f16 || !h_dev_f16 || M < 0) return PPX_E_INVAL;
     GemmArgs g;
+    g.part = static_cast<float *>(ws_dev);
+    g.part_floats = ws_dev ? ws_bytes / 4 : 0;
     g.A = static_cast<const __half *>(a_dev_f16);
     g.lda = w->K;
     g.M = M;

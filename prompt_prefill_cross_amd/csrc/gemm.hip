@@ -3,31 +3,40 @@
 //   C[M][N] = A[M][K] (fp16 activations, fragment-tiled) x W[N][K]^T (Q4_0),
 //   fp32 accumulate, with the layer's elementwise work fused into the epilogue.
 //
-// A workgroup holds NWN x KS compute waves and one producer wave and computes
-// a BM x BN tile; compute wave (w, g) owns columns [w*WN, (w+1)*WN) for all BM
-// rows (TM x TN MFMA tiles of 16 x 16) over the g-th of KS equal slices of K;
-// the KS partial tiles meet in LDS, in slice order, before the epilogue.
-//   * A (shared by the compute waves) reaches LDS without passing through
-//     registers: the producer wave fills a ring of DEPTH stages, one 64-wide
-//     K step of every slice each, with global_load_lds DMA of 1 KB fragments -- contiguous in
-//     the fragment-tiled activation layout, one 16-byte piece per lane straight
-//     into A-operand order -- and hands a stage over with a workgroup barrier
-//     once its own outstanding-DMA count says the stage has landed.
-//   * W (private to each compute wave: its own columns) streams straight into
-//     registers, PB stages ahead: per lane and 64-wide K step one 8-byte word
-//     pair of repacked codes and one fp16 block-scale pair per 16-column group.
-//     Compute waves decode in registers (a shift, a mask, an OR with the fp16
-//     exponent of 1024, a subtract and a multiply per pair) and multiply.
-// Keeping DMA in its own wave keeps the compiler from making LDS reads wait on
-// DMA aimed at other stages.  The decode is paid once per wave for TM row
-// tiles, so taller wave tiles amortise it; LDS carries only A.
+// Two kernels share the epilogue:
 //
-// Two arithmetic modes:
-//  * fast (EXACT = false): B = fp16(d * (code - 8)), one rounding per weight;
-//  * exact (EXACT = true): B = code - 8 (exact in fp16), A = hi + lo (two
-//    fp16 arrays), each 32-wide block's partial scaled by its fp32 block scale
-//    before it is added -- only fp32 accumulation rounds.  The K|V projection
-//    uses it, so the cache holds values accurate to the fp16 store itself.
+// k_q4gemm_p -- the row-batched projections (fast mode).  A workgroup holds
+// NWN x KS compute waves and one producer wave and computes a BM x BN tile
+// over a K range (the whole K, or one of S ranges when the K split goes
+// across workgroups).  Compute wave (w, g) owns columns [w*WN, (w+1)*WN) for
+// all BM rows (TM x TN MFMA tiles of 16 x 16) over the g-th of KS slices of
+// the range.
+//   * The producer wave streams everything a stage needs into a ring of DEPTH
+//     LDS stages with global_load_lds DMA: per K group one 64-wide K step of
+//     A (1 KB fragments, contiguous in the fragment-tiled layout, landing in
+//     A-operand order) and the repacked weight codes and block scales of the
+//     workgroup's columns.  It hands stage s over at barrier s once its own
+//     outstanding-DMA count says stages s and s+1 have landed.  (DMA lives in
+//     its own wave because the compiler makes any LDS read that follows an LDS
+//     DMA in the same wave wait for all DMA.)
+//   * Compute waves never touch global memory in the main loop: per stage they
+//     read A fragments and the NEXT stage's codes from LDS, and decode those
+//     codes (a shift, a mask, an OR with the fp16 exponent of 1024, a subtract
+//     and a multiply per pair) while the MFMAs of this stage run, so the VALU
+//     work of the decode overlaps the matrix work.
+//   * The KS partial tiles meet in LDS in slice order; the waves of up to KS
+//     groups then finish TM/KS row tiles each, spreading the epilogue.
+//   * With a K split across S workgroups, each writes its fp32 partial tile;
+//     k_gemm_reduce sums the S partials in split order and runs the epilogue.
+//   Every summation order is fixed, so results are deterministic.
+//
+// k_q4gemm -- the exact-weight mode (the K|V projection): B = code - 8
+// (exact in fp16), A = hi + lo (two fp16 arrays), each 32-wide block's partial
+// scaled by its fp32 block scale before it is added -- only fp32 accumulation
+// rounds, so the cache holds values accurate to the fp16 store itself.  Its
+// weights stream from global memory into registers, four K steps ahead.
+//
+// Fast-mode B = fp16(d * (code - 8)): one rounding per weight.
 #include "ppx_dev.h"
 
 namespace ppx {
@@ -62,6 +71,12 @@ __device__ __forceinline__ void wait_vm() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
     asm volatile("" ::: "memory");
+}
+
+// The value of lane (l + 8) mod 16 within each 16-lane row (DPP row rotate).
+__device__ __forceinline__ float row_swap8(float v) {
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
 }
 
 // Epilogue of one wave tile: acc[i][j][r] = C[r0 + 16i + 4(lane/16) + r][c0 + 16j + lane%16].
@@ -101,9 +116,35 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, const f4 (&acc)
                     a.out_f16[tiled_index(row, col, E)] = (_Float16)(gelu_tanh_f(acc[i][j][r]) * P);
                 }
             }
+    } else if (a.epi == EPI_GLU) {
+        // lane c < 8 of a 16-lane row holds gate f = 8t + c of 16-column group t,
+        // lane c + 8 the matching up: after a swap of the two halves of the row,
+        // lanes c < 8 finish the first two of the lane group's four rows and
+        // lanes c >= 8 the last two.
+        const int F = N >> 1;
+        const bool lo = lc < 8;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int f = ((c0 >> 4) + j) * 8 + (lc & 7);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const float v0 = acc[i][j][2 * h], v1 = acc[i][j][2 * h + 1];
+                    const float p0 = row_swap8(v0), p1 = row_swap8(v1);
+                    if (lo == (h == 0)) {
+                        const float g0 = lo ? v0 : p0, u0 = lo ? p0 : v0;
+                        const float g1 = lo ? v1 : p1, u1 = lo ? p1 : v1;
+                        const int row = r0 + i * 16 + lr + 2 * h;
+                        if (row < a.M) a.out_f16[tiled_index(row, f, F)] = (_Float16)(act_f(a.act, g0) * u0);
+                        if (row + 1 < a.M) a.out_f16[tiled_index(row + 1, f, F)] = (_Float16)(act_f(a.act, g1) * u1);
+                    }
+                }
+            }
     } else {
-        // paired epilogues: 16-column groups (2p, 2p+1) of the wave tile hold the
-        // two members of a pair (gate, up) or (first, second RoPE half)
+        // EPI_QKV: 16-column groups (2p, 2p+1) of the wave tile hold the first and
+        // second RoPE half of 16 dimensions.  Columns [0,qd) Q, [qd,qd+kvd) K,
+        // [qd+kvd, qd+2kvd) V.
 #pragma unroll
         for (int p = 0; p < TN / 2; ++p) {
             const int colA = c0 + p * 32 + lc;  // first member; second = colA + 16
@@ -114,51 +155,291 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, const f4 (&acc)
                     const int row = r0 + i * 16 + lr + r;
                     if (row >= a.M) continue;
                     const float va = acc[i][2 * p][r], vb = acc[i][2 * p + 1][r];
-                    if (a.epi == EPI_GLU) {
-                        // act(gate) * up -> fp16, fragment-tiled [M][F]
-                        const int F = N >> 1;
-                        const int f = (colA >> 5) * 16 + lc;
-                        a.out_f16[tiled_index(row, f, F)] = (_Float16)(act_f(a.act, va) * vb);
-                    } else {  // EPI_QKV: columns [0,qd) Q, [qd,qd+kvd) K, [qd+kvd, qd+2kvd) V
-                        const int hd = a.hd, half = hd >> 1;
-                        const int pos = a.pos0 + row;
-                        if (colA < a.qd + a.kvd) {
-                            const bool isq = colA < a.qd;
-                            const int c = isq ? colA : colA - a.qd;
-                            const int h = c / hd, rr = c % hd;
-                            const int ii = (rr >> 5) * 16 + lc;  // dimension in the first half
-                            const float2 cs = a.rope[(size_t)pos * half + ii];
-                            const float ra = va * cs.x - vb * cs.y;
-                            const float rb = va * cs.y + vb * cs.x;
-                            if (isq) {
-                                __half *q = a.out_f16 + (size_t)row * a.qd + h * hd;
-                                q[ii] = __float2half(ra);
-                                q[ii + half] = __float2half(rb);
-                            } else {
-                                __half *k = a.kc + (size_t)pos * a.kvd + h * hd;
-                                k[ii] = __float2half(ra);
-                                k[ii + half] = __float2half(rb);
-                            }
+                    const int hd = a.hd, half = hd >> 1;
+                    const int pos = a.pos0 + row;
+                    if (colA < a.qd + a.kvd) {
+                        const bool isq = colA < a.qd;
+                        const int c = isq ? colA : colA - a.qd;
+                        const int h = c / hd, rr = c % hd;
+                        const int ii = (rr >> 5) * 16 + lc;  // dimension in the first half
+                        const float2 cs = a.rope[(size_t)pos * half + ii];
+                        const float ra = va * cs.x - vb * cs.y;
+                        const float rb = va * cs.y + vb * cs.x;
+                        if (isq) {
+                            __half *q = a.out_f16 + (size_t)row * a.qd + h * hd;
+                            q[ii] = __float2half(ra);
+                            q[ii + half] = __float2half(rb);
                         } else {
-                            const int c = colA - a.qd - a.kvd;
-                            a.vc[(size_t)c * a.vld + pos] = __float2half(va);  // V^T
-                            a.vc[(size_t)(c + 16) * a.vld + pos] = __float2half(vb);
+                            __half *k = a.kc + (size_t)pos * a.kvd + h * hd;
+                            k[ii] = __float2half(ra);
+                            k[ii + half] = __float2half(rb);
                         }
+                    } else {
+                        const int c = colA - a.qd - a.kvd;
+                        a.vc[(size_t)c * a.vld + pos] = __float2half(va);  // V^T
+                        a.vc[(size_t)(c + 16) * a.vld + pos] = __float2half(vb);
                     }
                 }
         }
     }
 }
 
-template <int TM_, int TN_, int NWN_, int KS_, int DEPTH_, bool EXACT_>
-struct Cfg {
+// ------------------------------------------------------------ pipelined kernel
+
+template <int TM_, int TN_, int NWN_, int KS_, int DEPTH_>
+struct PCfg {
     static constexpr int TM = TM_, TN = TN_, NWN = NWN_, KS = KS_, DEPTH = DEPTH_;
-    static constexpr bool EXACT = EXACT_;
     static constexpr int NCW = NWN * KS;             // compute waves
     static constexpr int NT = 64 * (NCW + 1);
     static constexpr int BM = 16 * TM, WN = 16 * TN, BN = NWN * WN;
-    static constexpr int NA = EXACT ? 2 : 1;
-    static constexpr int AFR = 2 * TM * NA;          // fragments per chunk
+    static constexpr int AFR = 2 * TM;               // A fragments per K group and stage
+    static constexpr int NB = NWN * TN * KS;         // weight blocks (16 columns x 64 k) per stage
+    static constexpr int NBP = (NB + 1) / 2 * 2, NSP = (NB + 3) / 4 * 4;
+    static constexpr int A_UNITS = KS * AFR * 64;    // 16-byte units of a stage
+    static constexpr int B_UNITS = NBP * 32;         // 512 B of codes per block
+    static constexpr int S_UNITS = NSP * 4;          // 64 B of scales per block
+    static constexpr int STAGE_UNITS = A_UNITS + B_UNITS + S_UNITS;
+    static constexpr int DMA_STAGE = KS * AFR + NBP / 2 + NSP / 4;
+    // K groups that finish rows (NFG), TMS row tiles each
+    static constexpr int NFG = (TM % KS == 0) ? KS : 1;
+    static constexpr int TMS = TM / NFG;
+    static constexpr int SLOT_FLOATS = TMS * TN * 4 * 64;
+    static constexpr int XCH_FLOATS = (KS * NFG - NFG) * NWN * SLOT_FLOATS;
+    static_assert(NT <= 1024, "workgroup size");
+    static_assert(DEPTH >= 3 && (DEPTH - 3) * DMA_STAGE <= 63, "ring depth / vmcnt range");
+    static_assert(DEPTH * STAGE_UNITS * 16 <= 160 * 1024, "LDS");
+    static_assert(XCH_FLOATS * 4 <= DEPTH * STAGE_UNITS * 16, "exchange space");
+    // exchange slot of the rows K group gs hands to finishing group gd (gs != gd)
+    __device__ static constexpr int slot(int gs, int gd) {
+        return gs * NFG - (gs < NFG ? gs : NFG) + gd - ((gs < NFG && gd > gs) ? 1 : 0);
+    }
+};
+
+// Row tiles [G*TMS, (G+1)*TMS) of the wave's accumulators, summed over the K
+// groups in group order (the wave's own partial in its place), then finished:
+// the epilogue, or the fp32 partial of this workgroup's K range.
+template <class C, int G>
+__device__ __forceinline__ void finish_rows(const GemmArgs &a, const f4 (&acc)[C::TM][C::TN], const float *xch,
+                                            int wn, int m0, int n0, int lane) {
+    f4 sum[C::TMS][C::TN];
+#pragma unroll
+    for (int i = 0; i < C::TMS; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) sum[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int gs = 0; gs < C::KS; ++gs) {
+        if (gs == G) {
+#pragma unroll
+            for (int i = 0; i < C::TMS; ++i)
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j) sum[i][j] += acc[G * C::TMS + i][j];
+        } else {
+            const float *src = xch + (size_t)(C::slot(gs, G) * C::NWN + wn) * C::SLOT_FLOATS + lane;
+#pragma unroll
+            for (int i = 0; i < C::TMS; ++i)
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sum[i][j][r] += src[((i * C::TN + j) * 4 + r) * 64];
+        }
+    }
+    const int r0 = m0 + G * C::TMS * 16, c0 = n0 + wn * C::WN;
+    if (gridDim.z == 1) {
+        gemm_epilogue<C::TMS, C::TN>(a, sum, r0, c0, lane);
+    } else {
+        // partial tile layout: [split][row tile][16-column group][r][lane]
+        const int Mt = gridDim.y * C::TM, Nt = a.W.N >> 4;
+        float *dst = a.part + (size_t)blockIdx.z * Mt * Nt * 256;
+#pragma unroll
+        for (int i = 0; i < C::TMS; ++i)
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j) {
+                float *p = dst + ((size_t)((r0 >> 4) + i) * Nt + (c0 >> 4) + j) * 256 + lane;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) p[r * 64] = sum[i][j][r];
+            }
+    }
+}
+
+template <class C, int G>
+__device__ __forceinline__ void finish_group(const GemmArgs &a, const f4 (&acc)[C::TM][C::TN], const float *xch,
+                                             int g, int wn, int m0, int n0, int lane) {
+    if constexpr (G < C::NFG) {
+        if (g == G) finish_rows<C, G>(a, acc, xch, wn, m0, n0, lane);
+        else finish_group<C, G + 1>(a, acc, xch, g, wn, m0, n0, lane);
+    }
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void k_q4gemm_p(GemmArgs a) {
+    __shared__ h8 ring[C::DEPTH * C::STAGE_UNITS];
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id();
+    const int n0 = blockIdx.x * C::BN, m0 = blockIdx.y * C::BM;
+    const int kch = a.W.K >> 6;
+    const int nkg = kch / ((int)gridDim.z * C::KS);  // 64-wide K steps per K group
+    const int kz = blockIdx.z * C::KS * nkg;         // first K step of this workgroup
+    const int ktiles = a.W.K >> 5;
+
+    if (wave == C::NCW) {
+        // ---- producer
+        const int last_tr = (a.M - 1) >> 4;
+        const __half *asrc[C::AFR];
+#pragma unroll
+        for (int f = 0; f < C::AFR; ++f) {
+            const int kb = f / C::TM, i = f % C::TM;
+            const int tr = min((m0 >> 4) + i, last_tr);  // rows past M repeat the last tile
+            asrc[f] = a.A + (((size_t)tr * ktiles + 2 * kz + kb) * 64 + lane) * 8;
+        }
+        // weight block b = (K group gk, column group cg): b = gk * NWN * TN + cg;
+        // one 16-byte DMA carries two blocks' codes, one 4-byte DMA four blocks' scales
+        const int gbase = n0 >> 4;
+        const uint4 *bsrc[C::NBP / 2];
+        const uint32_t *ssrc[C::NSP / 4];
+#pragma unroll
+        for (int i = 0; i < C::NBP / 2; ++i) {
+            const int b = min(2 * i + (lane >> 5), C::NB - 1);
+            const int gk = b / (C::NWN * C::TN), cg = b % (C::NWN * C::TN);
+            bsrc[i] = reinterpret_cast<const uint4 *>(a.W.nib) + ((size_t)(gbase + cg) * kch + kz + gk * nkg) * 32 +
+                      (lane & 31);
+        }
+#pragma unroll
+        for (int i = 0; i < C::NSP / 4; ++i) {
+            const int b = min(4 * i + (lane >> 4), C::NB - 1);
+            const int gk = b / (C::NWN * C::TN), cg = b % (C::NWN * C::TN);
+            ssrc[i] = reinterpret_cast<const uint32_t *>(a.W.scl) + ((size_t)(gbase + cg) * kch + kz + gk * nkg) * 16 +
+                      (lane & 15);
+        }
+        auto issue = [&](int sb) {
+            h8 *st = ring + (sb % C::DEPTH) * C::STAGE_UNITS;
+            const int s = min(sb, nkg - 1);  // past the end: repeats keep the DMA count uniform
+#pragma unroll
+            for (int g = 0; g < C::KS; ++g)
+#pragma unroll
+                for (int f = 0; f < C::AFR; ++f)
+                    dma16(asrc[f] + (size_t)(g * nkg + s) * 1024, st + (g * C::AFR + f) * 64);
+#pragma unroll
+            for (int i = 0; i < C::NBP / 2; ++i) dma16(bsrc[i] + (size_t)s * 32, st + C::A_UNITS + i * 64);
+#pragma unroll
+            for (int i = 0; i < C::NSP / 4; ++i) dma4(ssrc[i] + (size_t)s * 16, st + C::A_UNITS + C::B_UNITS + i * 16);
+        };
+#pragma unroll
+        for (int s = 0; s < C::DEPTH - 1; ++s) issue(s);
+        for (int s = 0; s < nkg; ++s) {
+            wait_vm<(C::DEPTH - 3) * C::DMA_STAGE>();  // stages <= s + 1 have landed
+            lds_barrier();
+            issue(s + C::DEPTH - 1);  // into the buffer of stage s - 1, which nobody reads any more
+        }
+        wait_vm<0>();
+        lds_barrier();  // the ring is free once every DMA has landed
+        return;
+    }
+
+    // ---- compute waves
+    const int wn = wave % C::NWN, g = wave / C::NWN;
+    f4 acc[C::TM][C::TN];
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+    const int b0 = g * C::NWN * C::TN + wn * C::TN;
+    auto decode = [&](const h8 *st, h8 (&bf)[2][C::TN]) {
+        const uint2 *bws = reinterpret_cast<const uint2 *>(st + C::A_UNITS) + b0 * 64 + lane;
+        const uint32_t *bss =
+            reinterpret_cast<const uint32_t *>(st + C::A_UNITS + C::B_UNITS) + b0 * 16 + (lane & 15);
+        uint2 bw[C::TN];
+        uint32_t bs[C::TN];
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+            bw[j] = bws[j * 64];
+            bs[j] = bss[j * 16];
+        }
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+            const h2 d = __builtin_bit_cast(h2, bs[j]);
+            bf[0][j] = q4_word_to_h8(bw[j].x, d[0]);
+            bf[1][j] = q4_word_to_h8(bw[j].y, d[1]);
+        }
+    };
+    // stage s: MFMAs on the codes decoded one stage earlier (bc) while the next
+    // stage's codes are decoded (bn)
+    auto step = [&](int s, const h8 (&bc)[2][C::TN], h8 (&bn)[2][C::TN]) {
+        const h8 *st = ring + (s % C::DEPTH) * C::STAGE_UNITS;
+        const h8 *sn = ring + ((s + 1) % C::DEPTH) * C::STAGE_UNITS;
+        const h8 *as = st + g * C::AFR * 64 + lane;
+        h8 af[2][C::TM];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i) af[kb][i] = as[(kb * C::TM + i) * 64];
+        decode(sn, bn);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma16(af[kb][i], bc[kb][j], acc[i][j]);
+        if (s + 1 < nkg) lds_barrier();
+    };
+    h8 bA[2][C::TN], bB[2][C::TN];
+    lds_barrier();  // stages 0 and 1 have landed
+    decode(ring, bA);
+    for (int s = 0; s < nkg; s += 2) {
+        step(s, bA, bB);
+        if (s + 1 < nkg) step(s + 1, bB, bA);
+    }
+    lds_barrier();  // matches the producer's last barrier: the ring is free
+
+    float *xch = reinterpret_cast<float *>(ring);
+    if constexpr (C::KS > 1) {
+        // hand the row tiles of the other finishing groups over, then sum in group order
+#pragma unroll
+        for (int gd = 0; gd < C::NFG; ++gd) {
+            if (gd == g) continue;
+            float *dst = xch + (size_t)(C::slot(g, gd) * C::NWN + wn) * C::SLOT_FLOATS + lane;
+#pragma unroll
+            for (int i = 0; i < C::TMS; ++i)
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dst[((i * C::TN + j) * 4 + r) * 64] = acc[gd * C::TMS + i][j][r];
+        }
+        __syncthreads();  // compute waves only: the producer has returned
+    }
+    finish_group<C, 0>(a, acc, xch, g, wn, m0, n0, lane);
+}
+
+// Sum of the S split partials in split order, then the epilogue; one wave per
+// 16 rows x (16 * TNR) columns.
+template <int TNR>
+__global__ __launch_bounds__(256) void k_gemm_reduce(GemmArgs a, int S, int Mt) {
+    const int lane = threadIdx.x & 63;
+    const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int Nt = a.W.N >> 4, ncb = Nt / TNR;
+    const int rt = w / ncb, cb = w % ncb;
+    if (rt >= Mt || rt * 16 >= a.M) return;
+    f4 acc[1][TNR];
+#pragma unroll
+    for (int j = 0; j < TNR; ++j) acc[0][j] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int z = 0; z < S; ++z) {
+        const float *src = a.part + ((size_t)z * Mt * Nt + (size_t)rt * Nt + cb * TNR) * 256 + lane;
+#pragma unroll
+        for (int j = 0; j < TNR; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[0][j][r] += src[j * 256 + r * 64];
+    }
+    gemm_epilogue<1, TNR>(a, acc, rt * 16, cb * TNR * 16, lane);
+}
+
+// ------------------------------------------------------- exact-weight kernel
+
+template <int TM_, int TN_, int NWN_, int KS_, int DEPTH_>
+struct Cfg {
+    static constexpr int TM = TM_, TN = TN_, NWN = NWN_, KS = KS_, DEPTH = DEPTH_;
+    static constexpr int NCW = NWN * KS;             // compute waves
+    static constexpr int NT = 64 * (NCW + 1);
+    static constexpr int BM = 16 * TM, WN = 16 * TN, BN = NWN * WN;
+    static constexpr int AFR = 4 * TM;               // hi and lo fragments per chunk
     static constexpr int DMAS = AFR * KS;            // per stage
     static constexpr int STAGE_UNITS = DMAS * 64;
     static constexpr int PB = 4;
@@ -245,33 +526,22 @@ __global__ __launch_bounds__(C::NT) void k_q4gemm(GemmArgs a) {
             const h8 *st = ring + (s % C::DEPTH) * C::STAGE_UNITS + grp * C::AFR * 64;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                h8 af[C::TM];
+                h8 af[C::TM], al[C::TM];
 #pragma unroll
-                for (int i = 0; i < C::TM; ++i) af[i] = st[(kb * C::TM + i) * 64 + lane];
-                if constexpr (C::EXACT) {
-                    h8 al[C::TM];
+                for (int i = 0; i < C::TM; ++i) {
+                    af[i] = st[(kb * C::TM + i) * 64 + lane];
+                    al[i] = st[((2 + kb) * C::TM + i) * 64 + lane];
+                }
 #pragma unroll
-                    for (int i = 0; i < C::TM; ++i) al[i] = st[((2 + kb) * C::TM + i) * 64 + lane];
+                for (int j = 0; j < C::TN; ++j) {
+                    const h8 bq = q4_word_codes(kb ? bw[u][j].y : bw[u][j].x);
+                    const float dj = (float)__builtin_bit_cast(h2, bs[u][j])[kb];
 #pragma unroll
-                    for (int j = 0; j < C::TN; ++j) {
-                        const h8 bq = q4_word_codes(kb ? bw[u][j].y : bw[u][j].x);
-                        const float dj = (float)__builtin_bit_cast(h2, bs[u][j])[kb];
-#pragma unroll
-                        for (int i = 0; i < C::TM; ++i) {
-                            f4 t = mfma16(af[i], bq, f4{0.f, 0.f, 0.f, 0.f});
-                            t = mfma16(al[i], bq, t);
-                            acc[i][j] += dj * t;
-                        }
+                    for (int i = 0; i < C::TM; ++i) {
+                        f4 t = mfma16(af[i], bq, f4{0.f, 0.f, 0.f, 0.f});
+                        t = mfma16(al[i], bq, t);
+                        acc[i][j] += dj * t;
                     }
-                } else {
-                    h8 bf[C::TN];
-#pragma unroll
-                    for (int j = 0; j < C::TN; ++j)
-                        bf[j] = q4_word_to_h8(kb ? bw[u][j].y : bw[u][j].x, __builtin_bit_cast(h2, bs[u][j])[kb]);
-#pragma unroll
-                    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-                        for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma16(af[i], bf[j], acc[i][j]);
                 }
             }
         }
@@ -305,6 +575,26 @@ __global__ __launch_bounds__(C::NT) void k_q4gemm(GemmArgs a) {
     gemm_epilogue<C::TM, C::TN>(a, acc, m0, n0 + wn * C::WN, lane);
 }
 
+// ------------------------------------------------------------------ launchers
+
+template <class C>
+int launch_p(const GemmArgs &a, int S, hipStream_t s) {
+    const int kch = a.W.K >> 6;
+    if (S < 1 || a.W.N % C::BN || kch % (S * C::KS)) return PPX_E_UNSUPPORTED;
+    if (a.epi == EPI_QKV && C::TN % 2) return PPX_E_UNSUPPORTED;
+    const int mb = (a.M + C::BM - 1) / C::BM;
+    const int Mt = mb * C::TM;
+    if (S > 1 && (!a.part || (size_t)S * Mt * 16 * a.W.N > a.part_floats)) return PPX_E_UNSUPPORTED;
+    hipLaunchKernelGGL((k_q4gemm_p<C>), dim3(a.W.N / C::BN, mb, S), dim3(C::NT), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return PPX_E_HIP;
+    if (S > 1) {
+        const int waves = Mt * (a.W.N / 32);
+        hipLaunchKernelGGL((k_gemm_reduce<2>), dim3((waves + 3) / 4), dim3(256), 0, s, a, S, Mt);
+        if (hipGetLastError() != hipSuccess) return PPX_E_HIP;
+    }
+    return PPX_OK;
+}
+
 template <class C>
 int launch_cfg(const GemmArgs &a, hipStream_t s) {
     if (a.W.N % C::BN || (a.W.K >> 6) % (C::PB * C::KS)) return PPX_E_UNSUPPORTED;
@@ -313,37 +603,74 @@ int launch_cfg(const GemmArgs &a, hipStream_t s) {
     return hipGetLastError() == hipSuccess ? PPX_OK : PPX_E_HIP;
 }
 
+// Fast-mode configurations (workgroup tile; wave tile):
+//   0: 128 x 192, 4 column waves x 2 K groups (128 x 48)
+//   1: 128 x 128, 4 column waves x 2 K groups (128 x 32)
+//   2:  64 x 128, 4 column waves x 2 K groups ( 64 x 32)
+//   3:  32 x 128, 4 column waves x 2 K groups ( 32 x 32)
+//   4:  16 x 128, 4 column waves x 2 K groups ( 16 x 32)
+//   5:  64 x 192, 4 column waves x 2 K groups ( 64 x 48)
+//   6: 128 x 192, 4 column waves x 1 K group  (128 x 48)
+//   7:  32 x 128, 4 column waves x 1 K group  ( 32 x 32)
+int launch_plan(const GemmArgs &a, int cfg, int S, hipStream_t s) {
+    switch (cfg) {
+    case 0: return launch_p<PCfg<8, 3, 4, 2, 3>>(a, S, s);
+    case 1: return launch_p<PCfg<8, 2, 4, 2, 3>>(a, S, s);
+    case 2: return launch_p<PCfg<4, 2, 4, 2, 4>>(a, S, s);
+    case 3: return launch_p<PCfg<2, 2, 4, 2, 4>>(a, S, s);
+    case 4: return launch_p<PCfg<1, 2, 4, 2, 4>>(a, S, s);
+    case 5: return launch_p<PCfg<4, 3, 4, 2, 4>>(a, S, s);
+    case 6: return launch_p<PCfg<8, 3, 4, 1, 3>>(a, S, s);
+    case 7: return launch_p<PCfg<2, 2, 4, 1, 4>>(a, S, s);
+    default: return PPX_E_UNSUPPORTED;
+    }
+}
+
+int tile_rows(int cfg) {
+    static const int bm[] = {128, 128, 64, 32, 16, 64, 128, 32};
+    return cfg >= 0 && cfg < 8 ? bm[cfg] : 16;
+}
+
+struct Plan {
+    int cfg, S;
+};
+
+// Measured on the E2B-like shapes at M = 512 (one MI355X): wide outputs
+// (gate|up) use the tallest wave tiles; the long-K down projection splits K
+// four ways over workgroups; the rest use 32 x 128 tiles (16 x 128 when N is
+// small).
+Plan plan_for(int M, int N, int K) {
+    (void)M;
+    if (N >= 8192) return {N % 192 == 0 ? 0 : 1, 1};
+    if (K >= 4096) return {N % 192 == 0 ? 5 : 2, 4};
+    if (N <= 512) return {4, 1};
+    return {3, 1};
+}
+
 }  // namespace
 
-// Tile shapes measured on the E2B-like shapes at M = 512 (one MI355X):
-//  * wide outputs (gate|up, N >= 8192): 64 x 128 tiles, four compute waves;
-//  * long K (down, K >= 4096): 64 x 64 tiles, K split over four wave groups;
-//  * narrow outputs (N <= 512): 16 x 128 tiles, K split over two groups;
-//  * the rest (Q, O, PLE up): 32 x 128 tiles, K split over two groups.
-// The exact-weight K|V projection: 16 x 64 tiles, K split over two groups.
-// A split needs K/64 to be a multiple of 4 x KS; narrower splits are used
-// where it is not.
-template <int TM, int TN, int NWN, int KS, int DEPTH, bool EXACT>
-int launch_split(const GemmArgs &a, hipStream_t s) {
-    if constexpr (KS > 1) {
-        if ((a.W.K >> 6) % (4 * KS)) return launch_split<TM, TN, NWN, KS / 2, DEPTH, EXACT>(a, s);
-    }
-    return launch_cfg<Cfg<TM, TN, NWN, KS, DEPTH, EXACT>>(a, s);
+size_t gemm_part_floats(int M, int N, int K) {
+    const Plan p = plan_for(M, N, K);
+    if (p.S <= 1) return 0;
+    const int bm = tile_rows(p.cfg);
+    return (size_t)p.S * ((M + bm - 1) / bm * bm) * N;
 }
 
 int launch_gemm(const GemmArgs &a, hipStream_t s) {
     if (a.M <= 0) return PPX_OK;
     if (a.W.N % 128 || a.W.K % 256 || !a.A) return PPX_E_UNSUPPORTED;
-    if (a.W.N >= 8192) return launch_split<4, 2, 4, 1, 4, false>(a, s);
-    if (a.W.K >= 4096) return launch_split<4, 2, 2, 4, 3, false>(a, s);
-    if (a.W.N <= 512) return launch_split<1, 2, 4, 2, 6, false>(a, s);
-    return launch_split<2, 2, 4, 2, 4, false>(a, s);
+    const Plan p = plan_for(a.M, a.W.N, a.W.K);
+    int st = launch_plan(a, p.cfg, p.S, s);
+    if (st == PPX_E_UNSUPPORTED && p.S > 1) st = launch_plan(a, p.cfg, 1, s);  // no split workspace given
+    if (st == PPX_E_UNSUPPORTED) st = launch_plan(a, 3, 1, s);                 // N % 128, K % 256: always fits
+    return st;
 }
 
 int launch_gemm_exact(const GemmArgs &a, hipStream_t s) {
     if (a.M <= 0) return PPX_OK;
     if (a.W.N % 64 || a.W.K % 256 || !a.A || !a.A2) return PPX_E_UNSUPPORTED;
-    return launch_split<1, 2, 2, 2, 6, true>(a, s);
+    if ((a.W.K >> 6) % 8 == 0) return launch_cfg<Cfg<1, 2, 2, 2, 6>>(a, s);
+    return launch_cfg<Cfg<1, 2, 2, 1, 6>>(a, s);
 }
 
 }  // namespace ppx

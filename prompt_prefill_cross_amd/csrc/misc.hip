@@ -119,8 +119,8 @@ int ok() { return hipGetLastError() == hipSuccess ? PPX_OK : PPX_E_HIP; }
 // fp16(v) and row 1 holds fp16(v - fp16(v)), so their sum carries v to ~22
 // bits; B holds (code - 8) exactly, and each block's partial is scaled by its
 // fp32 block scale -- only fp32 accumulation rounds.
-// A workgroup owns G groups of 16 columns (G = 2 when the epilogue combines a
-// pair: RoPE halves, gate/up); KW waves per group take interleaved 64-wide K
+// A workgroup owns G groups of 16 columns (G = 2 when the epilogue combines
+// the two RoPE halves); KW waves per group take interleaved 64-wide K
 // chunks with UNR weight loads in flight.  v is staged once per workgroup in
 // LDS as hi/lo fp16 arrays, so a lane's A-operand piece is one 16-byte read.
 // Partial sums meet in LDS in wave order: the result is deterministic and no
@@ -224,7 +224,13 @@ __global__ __launch_bounds__(64 * KW * G) void k_q4gemv(GemvArgs a) {
         }
         break;
     case GV_GLU:
-        if (G == 2) a.out[blockIdx.x * 16 + c] = act_f(a.act, yv[0]) * yv[G - 1];
+        // columns 0-7 of the group are gate rows 8t..8t+7, columns 8-15 their up rows
+        if (c < 8) {
+            float u = 0.f;
+#pragma unroll
+            for (int i = 0; i < KW; ++i) u += red[i * 16 + c + 8];
+            a.out[blockIdx.x * 8 + c] = act_f(a.act, yv[0]) * u;
+        }
         break;
     case GV_PLE: {
         const uint8_t *prow = a.ple_raw + (size_t)a.tok[0] * a.ple_row_blocks * 18;
@@ -247,7 +253,7 @@ int gemv_kw(int groups, int kch) {
 
 int launch_gemv(const GemvArgs &a, hipStream_t s) {
     if (a.W.N % 32 || a.W.K % 64 || !a.x || !a.out) return PPX_E_UNSUPPORTED;
-    const bool paired = a.epi == GV_QROPE || a.epi == GV_GLU;
+    const bool paired = a.epi == GV_QROPE;
     const int G = paired ? 2 : 1;
     const int kw = std::min(gemv_kw(a.W.N / 16, a.W.K / 64), 16 / G);
     const dim3 grid(a.W.N / (16 * G));

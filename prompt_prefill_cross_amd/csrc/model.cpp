@@ -263,9 +263,10 @@ int model_load(const uint8_t *b, size_t n, hipStream_t stream, ppx_model **out) 
         RepackJob jg;
         jg.K = d;
         jg.N = 2 * F;
+        // every 16-row group: gate rows 8t..8t+7, then the matching up rows
         for (int r = 0; r < 2 * F; ++r) {
-            const int blk = r / 16, c = r % 16;
-            jg.rows.push_back(rowp((blk & 1) ? wu : wg, (blk >> 1) * 16 + c));
+            const int blk = r / 8, c = r % 8;
+            jg.rows.push_back(rowp((blk & 1) ? wu : wg, (blk >> 1) * 8 + c));
         }
         plan_q4(lw.wgu, std::move(jg));
         if ((st = plain(lw.wdown, need(pf + "ffn_down", 1, d, F)))) return st;

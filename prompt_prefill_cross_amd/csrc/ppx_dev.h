@@ -91,12 +91,21 @@ __device__ __forceinline__ float q4_raw_weight(const uint8_t *row, int c) {
     return d * (float)(q - 8);
 }
 
-__device__ __forceinline__ float gelu_tanh_f(float z) {
-    const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
-    return 0.5f * z * (1.0f + tanhf(k0 * (z + 0.044715f * z * z * z)));
+// z * sigmoid(t) with the hardware base-2 exponential and reciprocal (about
+// 1 ulp each): e^-t = 2^(-t log2 e).  For t -> -inf the exponential overflows
+// to +inf and the product goes to -0, the limit.
+__device__ __forceinline__ float mul_sigmoid(float z, float t) {
+    const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * t);
+    return z * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
+// GELU, tanh form: 0.5 z (1 + tanh(u)) = z * sigmoid(2u), u = sqrt(2/pi) (z + 0.044715 z^3).
+__device__ __forceinline__ float gelu_tanh_f(float z) {
+    const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+    return mul_sigmoid(z, 2.0f * k0 * (z + 0.044715f * z * z * z));
+}
+
+__device__ __forceinline__ float silu_f(float z) { return mul_sigmoid(z, z); }
 
 __device__ __forceinline__ float act_f(int act, float g) {
     return act == ACT_GEGLU ? gelu_tanh_f(g) : silu_f(g);

@@ -104,7 +104,8 @@ enum GemmEpi {
     EPI_F32 = 0,  // C -> fp32 out[M][N]
     EPI_ADD = 1,  // resid[M][N] += C
     EPI_QKV = 2,  // rope(Q) -> q16, rope(K), V -> fp16 cache rows
-    EPI_GLU = 3,  // act(gate) * up -> fp16 h[M][F]
+    EPI_GLU = 3,  // act(gate) * up -> fp16 h[M][F]; in every 16-column group of the fused
+                  // weight, columns 0-7 are gate rows 8t..8t+7 and columns 8-15 the up rows
     EPI_PLE = 4,  // gelu(C) * s * deq(ple_table[tok]) -> fp16 [M][E]
 };
 
@@ -131,8 +132,15 @@ struct GemmArgs {
     int ple_row_blocks = 0;        // L*E/32
     int ple_col0 = 0;              // il*E
     float ple_s = 0.f;
+    // K split over workgroups: fp32 partial tiles, summed in split order by a
+    // second kernel that applies the epilogue.  Null: no split.
+    float *part = nullptr;
+    size_t part_floats = 0;
 };
 int launch_gemm(const GemmArgs &a, hipStream_t s);
+// fp32 words of split-K partials launch_gemm would use for an M x N x K GEMM
+// (0: that shape is not split).
+size_t gemm_part_floats(int M, int N, int K);
 // Exact-weight variant: B = (code - 8) exactly in fp16, A = A + A2 (split fp16),
 // block scales applied to each 32-wide partial in fp32.  Used for K and V.
 int launch_gemm_exact(const GemmArgs &a, hipStream_t s);

@@ -50,8 +50,8 @@ def fused_reference(m, name):
         F = g.shape[0]
         rows = []
         for r in range(2 * F):
-            blk, c = divmod(r, 16)
-            rows.append((u if blk & 1 else g)[(blk >> 1) * 16 + c])
+            blk, c = divmod(r, 8)
+            rows.append((u if blk & 1 else g)[(blk >> 1) * 8 + c])
         return np.stack(rows)
     return m.q4(p + kind)
 
