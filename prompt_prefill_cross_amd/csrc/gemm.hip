@@ -6,19 +6,21 @@
 // Two kernels share the epilogue:
 //
 // k_q4gemm_p -- the row-batched projections (fast mode).  A workgroup holds
-// NWN x KS compute waves and one producer wave and computes a BM x BN tile
+// NWN x KS compute waves and NP producer waves and computes a BM x BN tile
 // over a K range (the whole K, or one of S ranges when the K split goes
 // across workgroups).  Compute wave (w, g) owns columns [w*WN, (w+1)*WN) for
 // all BM rows (TM x TN MFMA tiles of 16 x 16) over the g-th of KS slices of
 // the range.
-//   * The producer wave streams everything a stage needs into a ring of DEPTH
+//   * The producer waves stream everything a stage needs into a ring of DEPTH
 //     LDS stages with global_load_lds DMA: per K group one 64-wide K step of
 //     A (1 KB fragments, contiguous in the fragment-tiled layout, landing in
 //     A-operand order) and the repacked weight codes and block scales of the
-//     workgroup's columns.  It hands stage s over at barrier s once its own
-//     outstanding-DMA count says stages s and s+1 have landed.  (DMA lives in
-//     its own wave because the compiler makes any LDS read that follows an LDS
-//     DMA in the same wave wait for all DMA.)
+//     workgroup's columns, each wave an equal share.  Stage s is handed over at
+//     barrier s once every producer's outstanding-DMA count says its share of
+//     stages s and s+1 has landed.  (DMA lives in waves of its own because the
+//     compiler makes any LDS read that follows an LDS DMA in the same wave wait
+//     for all DMA; one wave issues DMA at only a fraction of what the CU can
+//     take in, so wide tiles use several.)
 //   * Compute waves never touch global memory in the main loop: per stage they
 //     read A fragments and the NEXT stage's codes from LDS, and decode those
 //     codes (a shift, a mask, an OR with the fp16 exponent of 1024, a subtract
@@ -186,11 +188,11 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, const f4 (&acc)
 
 // ------------------------------------------------------------ pipelined kernel
 
-template <int TM_, int TN_, int NWN_, int KS_, int DEPTH_>
+template <int TM_, int TN_, int NWN_, int KS_, int DEPTH_, int NP_ = 1>
 struct PCfg {
-    static constexpr int TM = TM_, TN = TN_, NWN = NWN_, KS = KS_, DEPTH = DEPTH_;
+    static constexpr int TM = TM_, TN = TN_, NWN = NWN_, KS = KS_, DEPTH = DEPTH_, NP = NP_;
     static constexpr int NCW = NWN * KS;             // compute waves
-    static constexpr int NT = 64 * (NCW + 1);
+    static constexpr int NT = 64 * (NCW + NP);
     static constexpr int BM = 16 * TM, WN = 16 * TN, BN = NWN * WN;
     static constexpr int AFR = 2 * TM;               // A fragments per K group and stage
     static constexpr int NB = NWN * TN * KS;         // weight blocks (16 columns x 64 k) per stage
@@ -199,14 +201,18 @@ struct PCfg {
     static constexpr int B_UNITS = NBP * 32;         // 512 B of codes per block
     static constexpr int S_UNITS = NSP * 4;          // 64 B of scales per block
     static constexpr int STAGE_UNITS = A_UNITS + B_UNITS + S_UNITS;
-    static constexpr int DMA_STAGE = KS * AFR + NBP / 2 + NSP / 4;
+    // DMAs of a stage: A fragments, code pairs, scale quads; each producer wave
+    // issues PER of them (the last one repeated where the count does not divide)
+    static constexpr int A_TOT = KS * AFR, B_TOT = NBP / 2, S_TOT = NSP / 4;
+    static constexpr int DMA_STAGE = A_TOT + B_TOT + S_TOT;
+    static constexpr int PER = (DMA_STAGE + NP - 1) / NP;
     // K groups that finish rows (NFG), TMS row tiles each
     static constexpr int NFG = (TM % KS == 0) ? KS : 1;
     static constexpr int TMS = TM / NFG;
     static constexpr int SLOT_FLOATS = TMS * TN * 4 * 64;
     static constexpr int XCH_FLOATS = (KS * NFG - NFG) * NWN * SLOT_FLOATS;
     static_assert(NT <= 1024, "workgroup size");
-    static_assert(DEPTH >= 3 && (DEPTH - 3) * DMA_STAGE <= 63, "ring depth / vmcnt range");
+    static_assert(DEPTH >= 3 && (DEPTH - 3) * PER <= 63, "ring depth / vmcnt range");
     static_assert(DEPTH * STAGE_UNITS * 16 <= 160 * 1024, "LDS");
     static_assert(XCH_FLOATS * 4 <= DEPTH * STAGE_UNITS * 16, "exchange space");
     // exchange slot of the rows K group gs hands to finishing group gd (gs != gd)
@@ -281,52 +287,60 @@ __global__ __launch_bounds__(C::NT) void k_q4gemm_p(GemmArgs a) {
     const int kz = blockIdx.z * C::KS * nkg;         // first K step of this workgroup
     const int ktiles = a.W.K >> 5;
 
-    if (wave == C::NCW) {
-        // ---- producer
+    if (wave >= C::NCW) {
+        // ---- producer waves: wave NCW + p issues DMAs p, p + NP, p + 2 NP, ... of
+        // each stage (A fragments, then code pairs, then scale quads)
+        const int pw = C::NP == 1 ? 0 : wave - C::NCW;
         const int last_tr = (a.M - 1) >> 4;
-        const __half *asrc[C::AFR];
-#pragma unroll
-        for (int f = 0; f < C::AFR; ++f) {
-            const int kb = f / C::TM, i = f % C::TM;
-            const int tr = min((m0 >> 4) + i, last_tr);  // rows past M repeat the last tile
-            asrc[f] = a.A + (((size_t)tr * ktiles + 2 * kz + kb) * 64 + lane) * 8;
-        }
-        // weight block b = (K group gk, column group cg): b = gk * NWN * TN + cg;
-        // one 16-byte DMA carries two blocks' codes, one 4-byte DMA four blocks' scales
         const int gbase = n0 >> 4;
-        const uint4 *bsrc[C::NBP / 2];
-        const uint32_t *ssrc[C::NSP / 4];
+        // the wave's t-th DMA of a stage: e = t * NP + pw (the last one repeated past the end)
+        auto entry = [&](int t) { return min(t * C::NP + pw, C::DMA_STAGE - 1); };
+        const char *src[C::PER];
 #pragma unroll
-        for (int i = 0; i < C::NBP / 2; ++i) {
-            const int b = min(2 * i + (lane >> 5), C::NB - 1);
-            const int gk = b / (C::NWN * C::TN), cg = b % (C::NWN * C::TN);
-            bsrc[i] = reinterpret_cast<const uint4 *>(a.W.nib) + ((size_t)(gbase + cg) * kch + kz + gk * nkg) * 32 +
-                      (lane & 31);
-        }
-#pragma unroll
-        for (int i = 0; i < C::NSP / 4; ++i) {
-            const int b = min(4 * i + (lane >> 4), C::NB - 1);
-            const int gk = b / (C::NWN * C::TN), cg = b % (C::NWN * C::TN);
-            ssrc[i] = reinterpret_cast<const uint32_t *>(a.W.scl) + ((size_t)(gbase + cg) * kch + kz + gk * nkg) * 16 +
-                      (lane & 15);
+        for (int t = 0; t < C::PER; ++t) {
+            const int e = entry(t);
+            if (e < C::A_TOT) {
+                // K group gk, fragment f = kb * TM + i: rows of tile i, the kb-th 32-wide half of the step
+                const int gk = e / C::AFR, f = e % C::AFR;
+                const int kb = f / C::TM, i = f % C::TM;
+                const int tr = min((m0 >> 4) + i, last_tr);  // rows past M repeat the last tile
+                src[t] = reinterpret_cast<const char *>(
+                    a.A + (((size_t)tr * ktiles + 2 * (kz + gk * nkg) + kb) * 64 + lane) * 8);
+            } else if (e < C::A_TOT + C::B_TOT) {
+                // codes of weight blocks 2i and 2i+1, block b = (K group gk, column group cg)
+                const int i = e - C::A_TOT;
+                const int b = min(2 * i + (lane >> 5), C::NB - 1);
+                const int gk = b / (C::NWN * C::TN), cg = b % (C::NWN * C::TN);
+                src[t] = reinterpret_cast<const char *>(reinterpret_cast<const uint4 *>(a.W.nib) +
+                                                        ((size_t)(gbase + cg) * kch + kz + gk * nkg) * 32 + (lane & 31));
+            } else {
+                // scales of weight blocks 4i .. 4i+3
+                const int i = e - C::A_TOT - C::B_TOT;
+                const int b = min(4 * i + (lane >> 4), C::NB - 1);
+                const int gk = b / (C::NWN * C::TN), cg = b % (C::NWN * C::TN);
+                src[t] = reinterpret_cast<const char *>(reinterpret_cast<const uint32_t *>(a.W.scl) +
+                                                        ((size_t)(gbase + cg) * kch + kz + gk * nkg) * 16 + (lane & 15));
+            }
         }
         auto issue = [&](int sb) {
             h8 *st = ring + (sb % C::DEPTH) * C::STAGE_UNITS;
-            const int s = min(sb, nkg - 1);  // past the end: repeats keep the DMA count uniform
+            const size_t s = (size_t)min(sb, nkg - 1);  // past the end: repeats keep the DMA count uniform
 #pragma unroll
-            for (int g = 0; g < C::KS; ++g)
-#pragma unroll
-                for (int f = 0; f < C::AFR; ++f)
-                    dma16(asrc[f] + (size_t)(g * nkg + s) * 1024, st + (g * C::AFR + f) * 64);
-#pragma unroll
-            for (int i = 0; i < C::NBP / 2; ++i) dma16(bsrc[i] + (size_t)s * 32, st + C::A_UNITS + i * 64);
-#pragma unroll
-            for (int i = 0; i < C::NSP / 4; ++i) dma4(ssrc[i] + (size_t)s * 16, st + C::A_UNITS + C::B_UNITS + i * 16);
+            for (int t = 0; t < C::PER; ++t) {
+                const int e = entry(t);
+                if (e < C::A_TOT) {
+                    dma16(src[t] + s * 2048, st + e * 64);
+                } else if (e < C::A_TOT + C::B_TOT) {
+                    dma16(src[t] + s * 512, st + C::A_UNITS + (e - C::A_TOT) * 64);
+                } else {
+                    dma4(src[t] + s * 64, st + C::A_UNITS + C::B_UNITS + (e - C::A_TOT - C::B_TOT) * 16);
+                }
+            }
         };
 #pragma unroll
         for (int s = 0; s < C::DEPTH - 1; ++s) issue(s);
         for (int s = 0; s < nkg; ++s) {
-            wait_vm<(C::DEPTH - 3) * C::DMA_STAGE>();  // stages <= s + 1 have landed
+            wait_vm<(C::DEPTH - 3) * C::PER>();  // this wave's share of stages <= s + 1 has landed
             lds_barrier();
             issue(s + C::DEPTH - 1);  // into the buffer of stage s - 1, which nobody reads any more
         }
@@ -404,7 +418,7 @@ __global__ __launch_bounds__(C::NT) void k_q4gemm_p(GemmArgs a) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) dst[((i * C::TN + j) * 4 + r) * 64] = acc[gd * C::TMS + i][j][r];
         }
-        __syncthreads();  // compute waves only: the producer has returned
+        __syncthreads();  // compute waves only: the producers have returned
     }
     finish_group<C, 0>(a, acc, xch, g, wn, m0, n0, lane);
 }
@@ -603,32 +617,37 @@ int launch_cfg(const GemmArgs &a, hipStream_t s) {
     return hipGetLastError() == hipSuccess ? PPX_OK : PPX_E_HIP;
 }
 
-// Fast-mode configurations (workgroup tile; wave tile):
-//   0: 128 x 192, 4 column waves x 2 K groups (128 x 48)
-//   1: 128 x 128, 4 column waves x 2 K groups (128 x 32)
-//   2:  64 x 128, 4 column waves x 2 K groups ( 64 x 32)
-//   3:  32 x 128, 4 column waves x 2 K groups ( 32 x 32)
-//   4:  16 x 128, 4 column waves x 2 K groups ( 16 x 32)
-//   5:  64 x 192, 4 column waves x 2 K groups ( 64 x 48)
-//   6: 128 x 192, 4 column waves x 1 K group  (128 x 48)
-//   7:  32 x 128, 4 column waves x 1 K group  ( 32 x 32)
+// Fast-mode configurations: id, TM, TN, NWN, KS, DEPTH, NP (producer waves);
+// workgroup tile (16 TM) x (16 TN NWN), K split over KS wave groups.
+#define PPX_GEMM_CONFIGS(X) \
+    X(0, 8, 3, 4, 2, 3, 1)  \
+    X(1, 8, 2, 4, 2, 3, 1)  \
+    X(2, 4, 3, 4, 2, 4, 4)  \
+    X(3, 4, 2, 4, 2, 4, 4)  \
+    X(4, 2, 2, 4, 2, 4, 4)  \
+    X(5, 2, 2, 4, 2, 4, 1)  \
+    X(6, 1, 2, 4, 2, 4, 4)
+
 int launch_plan(const GemmArgs &a, int cfg, int S, hipStream_t s) {
     switch (cfg) {
-    case 0: return launch_p<PCfg<8, 3, 4, 2, 3>>(a, S, s);
-    case 1: return launch_p<PCfg<8, 2, 4, 2, 3>>(a, S, s);
-    case 2: return launch_p<PCfg<4, 2, 4, 2, 4>>(a, S, s);
-    case 3: return launch_p<PCfg<2, 2, 4, 2, 4>>(a, S, s);
-    case 4: return launch_p<PCfg<1, 2, 4, 2, 4>>(a, S, s);
-    case 5: return launch_p<PCfg<4, 3, 4, 2, 4>>(a, S, s);
-    case 6: return launch_p<PCfg<8, 3, 4, 1, 3>>(a, S, s);
-    case 7: return launch_p<PCfg<2, 2, 4, 1, 4>>(a, S, s);
+#define PPX_CASE(id, tm, tn, nwn, ks, depth, np) \
+    case id:                                     \
+        return launch_p<PCfg<tm, tn, nwn, ks, depth, np>>(a, S, s);
+        PPX_GEMM_CONFIGS(PPX_CASE)
+#undef PPX_CASE
     default: return PPX_E_UNSUPPORTED;
     }
 }
 
 int tile_rows(int cfg) {
-    static const int bm[] = {128, 128, 64, 32, 16, 64, 128, 32};
-    return cfg >= 0 && cfg < 8 ? bm[cfg] : 16;
+    switch (cfg) {
+#define PPX_CASE(id, tm, tn, nwn, ks, depth, np) \
+    case id:                                     \
+        return 16 * tm;
+        PPX_GEMM_CONFIGS(PPX_CASE)
+#undef PPX_CASE
+    default: return 16;
+    }
 }
 
 struct Plan {
@@ -636,15 +655,17 @@ struct Plan {
 };
 
 // Measured on the E2B-like shapes at M = 512 (one MI355X): wide outputs
-// (gate|up) use the tallest wave tiles; the long-K down projection splits K
-// four ways over workgroups; the rest use 32 x 128 tiles (16 x 128 when N is
-// small).
+// (gate|up) take the tallest wave tiles; the long-K down projection splits K
+// four ways over workgroups; Q and O use 32-row tiles with four producer
+// waves, narrow outputs 16-row tiles, and K = 256 the single-producer 32-row
+// tiles.
 Plan plan_for(int M, int N, int K) {
     (void)M;
     if (N >= 8192) return {N % 192 == 0 ? 0 : 1, 1};
-    if (K >= 4096) return {N % 192 == 0 ? 5 : 2, 4};
-    if (N <= 512) return {4, 1};
-    return {3, 1};
+    if (K >= 4096) return {N % 192 == 0 ? 2 : 3, 4};
+    if (N <= 512) return {6, 1};
+    if (K <= 256) return {5, 1};
+    return {4, 1};
 }
 
 }  // namespace
@@ -662,7 +683,7 @@ int launch_gemm(const GemmArgs &a, hipStream_t s) {
     const Plan p = plan_for(a.M, a.W.N, a.W.K);
     int st = launch_plan(a, p.cfg, p.S, s);
     if (st == PPX_E_UNSUPPORTED && p.S > 1) st = launch_plan(a, p.cfg, 1, s);  // no split workspace given
-    if (st == PPX_E_UNSUPPORTED) st = launch_plan(a, 3, 1, s);                 // N % 128, K % 256: always fits
+    if (st == PPX_E_UNSUPPORTED) st = launch_plan(a, 5, 1, s);                 // N % 128, K % 256: always fits
     return st;
 }
 
