@@ -123,8 +123,8 @@ size_t ppx_model_device_bytes(const ppx_model *m);
 size_t ppx_kv_bytes(const ppx_model *m, int n_ctx);
 /* Wrap a caller-owned device buffer of >= ppx_kv_bytes bytes (256-byte
  * aligned) as an empty cache (n_pos = 0).  The buffer must outlive the
- * handle; ppx_kv_free releases the handle only.  Also builds the model's
- * RoPE tables up to n_ctx if they are shorter (blocking). */
+ * handle; ppx_kv_free releases the handle only.  Zeroes the buffer and
+ * builds the model's RoPE tables up to n_ctx if they are shorter (blocking). */
 int ppx_kv_init(ppx_model *m, void *kv_dev, size_t bytes, int n_ctx, ppx_kv **out);
 void ppx_kv_free(ppx_kv *kv);
 int ppx_kv_n_pos(const ppx_kv *kv);

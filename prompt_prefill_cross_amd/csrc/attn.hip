@@ -24,85 +24,124 @@ namespace ppx {
 
 namespace {
 
-constexpr int KT = 64;  // keys per tile
+constexpr int KT = 32;  // keys per pipeline stage
 
-template <int HD>
-struct AttnTile {
-    static constexpr int KB = HD / 32;            // 32-wide d steps of S
-    static constexpr int DT = HD / 16;            // 16-row d subtiles of O^T
-    static constexpr int KU = KB * 4 * 64 / 256;  // K units (16 B) per thread per tile
-    static constexpr int VU = DT * 2 * 64 / 256;  // V^T units per thread per tile
-    h8 kr[KU], vr[VU];
+typedef __attribute__((address_space(3))) void lds_t;
 
-    // Branch-free: keys past `pend` read the last valid K row (their scores
-    // are masked) and their values are zeroed when stored.
-    __device__ __forceinline__ void load(const AttnArgs &a, int kvh, int t0, int pend) {
-        const int tid = threadIdx.x;
-#pragma unroll
-        for (int i = 0; i < KU; ++i) {
-            const int u = tid + i * 256;
-            const int dk = u >> 8, j = (u >> 6) & 3, l = u & 63;
-            const int i16 = l & 15, g = l >> 4;
-            const int key = t0 + (j >> 1) * 32 + 8 * (i16 >> 2) + 4 * (j & 1) + (i16 & 3);
-            const unsigned off = (unsigned)((min(key, pend) * a.KVH + kvh) * HD + dk * 32 + g * 8);
-            kr[i] = *reinterpret_cast<const h8 *>(a.k + off);
-        }
-#pragma unroll
-        for (int i = 0; i < VU; ++i) {
-            const int u = tid + i * 256;
-            const int di = u >> 7, kb2 = (u >> 6) & 1, l = u & 63;
-            const int d = di * 16 + (l & 15);
-            const unsigned off = (unsigned)((kvh * HD + d) * a.vld + t0 + kb2 * 32 + 8 * (l >> 4));
-            vr[i] = *reinterpret_cast<const h8 *>(a.vt + off);
-        }
-    }
+__device__ __forceinline__ void adma16(const void *src, h8 *dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_t *)dst, 16, 0, 0);
+}
+__device__ __forceinline__ int attn_wave_id() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }
 
-    __device__ __forceinline__ void store(h8 *ks, h8 *vs, int t0, int pend) const {
-        const int tid = threadIdx.x;
-#pragma unroll
-        for (int i = 0; i < KU; ++i) ks[tid + i * 256] = kr[i];
-#pragma unroll
-        for (int i = 0; i < VU; ++i) {
-            const int u = tid + i * 256;
-            const int key0 = t0 + ((u >> 6) & 1) * 32 + 8 * ((u & 63) >> 4);
-            h8 v = vr[i];
-            if (key0 + 7 > pend) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (key0 + e > pend) v[e] = (_Float16)0.0f;
-            }
-            vs[u] = v;
-        }
-    }
+// Workgroup barrier without the fences of __syncthreads (which would drain
+// the producers' outstanding DMA).
+__device__ __forceinline__ void attn_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void attn_wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+}
+
+// Four compute waves of CPW groups of 16 query columns and NP producer waves;
+// a ring of DEPTH stages of KT keys each: the K fragments [d step][16-key
+// block][lane] and the V^T fragments [16-dim subtile][lane] of the stage.
+template <int HD_, int CPW_, int NP_, int DEPTH_>
+struct ACfg {
+    static constexpr int HD = HD_, CPW = CPW_, NP = NP_, DEPTH = DEPTH_;
+    static constexpr int KB = HD / 32;           // 32-wide d steps of S
+    static constexpr int DT = HD / 16;           // 16-row d subtiles of O^T
+    static constexpr int K_UNITS = KB * 2 * 64;  // 16-byte units
+    static constexpr int V_UNITS = DT * 64;
+    static constexpr int STAGE_UNITS = K_UNITS + V_UNITS;
+    static constexpr int DMA_STAGE = KB * 2 + DT;
+    static constexpr int PER = (DMA_STAGE + NP - 1) / NP;
+    static constexpr int NT = 64 * (4 + NP);
+    static constexpr int CB = 64 * CPW;          // query columns per workgroup
+    static_assert(DEPTH >= 2 && (DEPTH - 2) * PER <= 63, "vmcnt range");
+    static_assert(DEPTH * STAGE_UNITS * 16 <= 160 * 1024, "LDS");
 };
 
-template <int HD, int CPW>
-__global__ __launch_bounds__(256) void k_attn_prefill(AttnArgs a) {
-    using T = AttnTile<HD>;
-    constexpr int KB = T::KB, DT = T::DT;
-    constexpr int CB = 64 * CPW;    // query columns per workgroup
-    __shared__ h8 ks[KB * 4 * 64];  // K fragments [d step][16-key block][lane]
-    __shared__ h8 vs[DT * 2 * 64];  // V^T fragments [d subtile][32-key step][lane]
+template <class C>
+__global__ __launch_bounds__(C::NT) void k_attn_prefill(AttnArgs a) {
+    constexpr int HD = C::HD, KB = C::KB, DT = C::DT, CPW = C::CPW;
+    __shared__ h8 ring[C::DEPTH * C::STAGE_UNITS];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = attn_wave_id();
     const int G = a.H / a.KVH;
     const int cb = blockIdx.x, ck = blockIdx.y, kvh = blockIdx.z;
     const int lc = lane & 15, lg = lane >> 4;
 
-    const int tmax = min(a.M - 1, (cb * CB + CB - 1) / G);
+    const int tmax = min(a.M - 1, (cb * C::CB + C::CB - 1) / G);
     const int pend = a.pos0 + tmax;  // last key any column here can see
     const int kbeg = ck * a.kc;
-    if (kbeg > pend) return;
+    if (kbeg > pend) return;  // the whole workgroup
     const int kend = min(kbeg + a.kc, pend + 1);
+    const int nst = (kend - kbeg + KT - 1) / KT;
 
-    // a wave owns CPW groups of 16 query columns; every K / V^T fragment read
-    // from LDS feeds one MFMA per group
+    if (wave >= 4) {
+        // ---- producers: wave 4 + p issues DMAs p, p + NP, ... of every stage.
+        // K rows past the last written position repeat it (their scores are
+        // masked); V^T reads stay inside the row (vld is a multiple of 64).
+        const int pw = C::NP == 1 ? 0 : wave - 4;
+        const int plast = a.pos0 + a.M - 1;
+        auto entry = [&](int t) { return min(t * C::NP + pw, C::DMA_STAGE - 1); };
+        int koff[C::PER];  // K: key within the stage; V^T: element offset within the row block
+#pragma unroll
+        for (int t = 0; t < C::PER; ++t) {
+            const int e = entry(t);
+            if (e < 2 * KB) {
+                // fragment (d step kb, key block j): lane l holds the key of accumulator row
+                // 8 (r / 4) + 4 j + r % 4, r = l % 16, and dims kb*32 + 8 (l / 16) ..
+                const int j = e & 1;
+                koff[t] = 8 * ((lane & 15) >> 2) + 4 * j + (lane & 3);
+            } else {
+                // V^T subtile i: lane l holds dim 16 i + l % 16, keys 8 (l / 16) .. + 7
+                const int i = e - 2 * KB;
+                koff[t] = (kvh * HD + i * 16 + (lane & 15)) * a.vld + 8 * (lane >> 4);
+            }
+        }
+        auto issue = [&](int sb) {
+            h8 *st = ring + (sb % C::DEPTH) * C::STAGE_UNITS;
+            const int t0 = kbeg + min(sb, nst - 1) * KT;  // past the end: repeats keep the count uniform
+#pragma unroll
+            for (int t = 0; t < C::PER; ++t) {
+                const int e = entry(t);
+                if (e < 2 * KB) {
+                    const int kb = e >> 1;
+                    const int key = min(t0 + koff[t], plast);
+                    adma16(a.k + ((size_t)key * a.KVH + kvh) * HD + kb * 32 + 8 * (lane >> 4), st + e * 64);
+                } else {
+                    adma16(a.vt + (size_t)koff[t] + t0, st + C::K_UNITS + (e - 2 * KB) * 64);
+                }
+            }
+        };
+#pragma unroll
+        for (int s = 0; s < C::DEPTH - 1; ++s) issue(s);
+        for (int s = 0; s < nst; ++s) {
+            attn_wait_vm<(C::DEPTH - 2) * C::PER>();  // this wave's share of stage s has landed
+            attn_barrier();
+            issue(s + C::DEPTH - 1);  // into the buffer of stage s - 1, already consumed
+        }
+        attn_wait_vm<0>();
+        attn_barrier();
+        return;
+    }
+
+    // ---- compute waves: CPW groups of 16 query columns; every K / V^T
+    // fragment read from LDS feeds one MFMA per group
     int t[CPW], h[CPW], qpos[CPW];
     bool valid[CPW];
     h8 qf[CPW][KB];
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
-        const int col = cb * CB + wave * 16 * CPW + c * 16 + lc;
+        const int col = cb * C::CB + wave * 16 * CPW + c * 16 + lc;
         t[c] = col / G;
         valid[c] = t[c] < a.M;
         h[c] = kvh * G + col % G;
@@ -126,72 +165,72 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnArgs a) {
     }
     const float sl2 = 1.4426950408889634f / sqrtf((float)HD);
 
-    T tile;
-    const int ntiles = (kend - kbeg + KT - 1) / KT;
-    tile.load(a, kvh, kbeg, pend);
-    for (int it = 0; it < ntiles; ++it) {
+    for (int it = 0; it < nst; ++it) {
+        attn_barrier();  // stage it has landed
         const int t0 = kbeg + it * KT;
-        tile.store(ks, vs, t0, pend);
-        __syncthreads();
-        tile.load(a, kvh, min(t0 + KT, kbeg + (ntiles - 1) * KT), pend);  // next tile (clamped)
+        const h8 *st = ring + (it % C::DEPTH) * C::STAGE_UNITS + lane;
 
-        // S^T = K Q^T: s[c][j][r] is key t0 + 32(j/2) + 8 lg + 4(j%2) + r, query column lc of group c
-        f4 s[CPW][4];
+        // S^T = K Q^T: s[c][j][r] is key t0 + 8 lg + 4 j + r, query column lc of group c
+        f4 s[CPW][2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 2; ++j) {
 #pragma unroll
             for (int c = 0; c < CPW; ++c) s[c][j] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                const h8 kf = ks[(kb * 4 + j) * 64 + lane];
+                const h8 kf = st[(kb * 2 + j) * 64];
 #pragma unroll
                 for (int c = 0; c < CPW; ++c) s[c][j] = mfma16(kf, qf[c][kb], s[c][j]);
             }
         }
-        h8 pf[CPW][2];
+        h8 pf[CPW];
 #pragma unroll
         for (int c = 0; c < CPW; ++c) {
             float tmx = -INFINITY;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int kp = t0 + (j >> 1) * 32 + 8 * lg + 4 * (j & 1) + r;
+                    const int kp = t0 + 8 * lg + 4 * j + r;
                     const float v = (kp <= qpos[c]) ? s[c][j][r] * sl2 : -INFINITY;
                     s[c][j][r] = v;
                     tmx = fmaxf(tmx, v);
                 }
             tmx = fmaxf(tmx, __shfl_xor(tmx, 16, 64));
             tmx = fmaxf(tmx, __shfl_xor(tmx, 32, 64));
+            // hardware 2^x: 2^-inf = 0 covers masked keys; a column with no
+            // visible key yet keeps max -inf and subtracts 0 instead
             const float mnew = fmaxf(mrun[c], tmx);
-            const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(mrun[c] - mnew);
+            const float msub = mnew == -INFINITY ? 0.f : mnew;
+            const float alpha = __builtin_amdgcn_exp2f(mrun[c] - msub);
             float psum = 0.f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float p = (s[c][j][r] == -INFINITY) ? 0.f : exp2f(s[c][j][r] - mnew);
+                    const float p = __builtin_amdgcn_exp2f(s[c][j][r] - msub);
                     psum += p;
-                    pf[c][j >> 1][(j & 1) * 4 + r] = (_Float16)p;
+                    pf[c][4 * j + r] = (_Float16)p;
                 }
             psum += __shfl_xor(psum, 16, 64);
             psum += __shfl_xor(psum, 32, 64);
             lrun[c] = lrun[c] * alpha + psum;
             mrun[c] = mnew;
+            // rescale the output only when some column's max moved this stage
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-            for (int i = 0; i < DT; ++i) oacc[c][i] *= alpha;
-        }
-        // O^T += V^T P^T; step kb2 covers keys t0 + 32 kb2 + 8 lg + 0..7 in lane group lg
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int i = 0; i < DT; ++i) {
-                const h8 vf = vs[(i * 2 + kb2) * 64 + lane];
-#pragma unroll
-                for (int c = 0; c < CPW; ++c) oacc[c][i] = mfma16(vf, pf[c][kb2], oacc[c][i]);
+                for (int i = 0; i < DT; ++i) oacc[c][i] *= alpha;
             }
-        __syncthreads();
+        }
+        // O^T += V^T P^T over the stage's 32 keys (8 lg .. 8 lg + 7 in lane group lg)
+#pragma unroll
+        for (int i = 0; i < DT; ++i) {
+            const h8 vf = st[C::K_UNITS + i * 64];
+#pragma unroll
+            for (int c = 0; c < CPW; ++c) oacc[c][i] = mfma16(vf, pf[c], oacc[c][i]);
+        }
     }
+    attn_barrier();  // matches the producers' last barrier
 
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
@@ -223,21 +262,44 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnArgs a) {
 
 // Combine the key chunks of row t, head h: chunks 0..floor(pos/kc) hold keys
 // the row can see.  Max-subtracted weights in the exp2 domain of the kernel.
+// One wave per (row, head): lane l owns dims 4l .. 4l+3 of each 256-dim slice;
+// the chunks are summed in chunk order.
 template <int HD>
-__global__ __launch_bounds__(HD) void k_attn_prefill_merge(AttnArgs a) {
-    const int t = blockIdx.x / a.H, h = blockIdx.x % a.H, d = threadIdx.x;
+__global__ __launch_bounds__(256) void k_attn_prefill_merge(AttnArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (w >= a.M * a.H) return;
+    const int t = w / a.H, h = w % a.H;
     const int nch = (a.pos0 + t) / a.kc + 1;
     const float *pm = a.part + (size_t)a.nkc * a.M * a.H * HD;
     float M = -INFINITY;
     for (int c = 0; c < nch; ++c) M = fmaxf(M, pm[(((size_t)c * a.M + t) * a.H + h) * 2]);
-    float L = 0.f, O = 0.f;
+    constexpr int NV = (HD + 255) / 256;  // float4 per lane
+    f4 O[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) O[v] = f4{0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
     for (int c = 0; c < nch; ++c) {
         const size_t slot = ((size_t)c * a.M + t) * a.H + h;
-        const float w = exp2f(pm[slot * 2] - M);
-        L += w * pm[slot * 2 + 1];
-        O += w * a.part[slot * HD + d];
+        const float wgt = exp2f(pm[slot * 2] - M);
+        L += wgt * pm[slot * 2 + 1];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int d = v * 256 + lane * 4;
+            if (d < HD) O[v] += wgt * *reinterpret_cast<const f4 *>(a.part + slot * HD + d);
+        }
     }
-    a.o[tiled_index(t, h * HD + d, a.H * HD)] = __float2half(O / L);
+    const float inv = 1.0f / L;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int d = v * 256 + lane * 4;
+        if (d >= HD) continue;
+        h4 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = (_Float16)(O[v][e] * inv);
+        // four consecutive dims: 8 contiguous bytes of the tiled layout
+        *reinterpret_cast<h4 *>(a.o + tiled_index(t, h * HD + d, a.H * HD)) = r;
+    }
 }
 
 // ------------------------------------------------------------------ single query
@@ -377,9 +439,8 @@ int ok() { return hipGetLastError() == hipSuccess ? PPX_OK : PPX_E_HIP; }
 
 }  // namespace
 
-// Column groups of 16 per wave (64 query columns per group of four waves); two
-// groups halve the LDS reads per MFMA but spill at head_dim 256.
-constexpr int ATTN_CPW = 1;
+// Two groups of 16 query columns per compute wave: 128 columns per workgroup.
+constexpr int ATTN_CPW = 2;
 
 AttnSplit attn_split(int M, int H, int KVH, int pos0) {
     const int G = H / KVH;
@@ -388,7 +449,7 @@ AttnSplit attn_split(int M, int H, int KVH, int pos0) {
     int want = (256 + colblocks * KVH - 1) / (colblocks * KVH);
     want = std::max(1, std::min(want, ATTN_MAX_CHUNKS));
     int kc = (P + want - 1) / want;
-    kc = std::max(256, (kc + KT - 1) / KT * KT);
+    kc = std::max(256, (kc + 63) / 64 * 64);
     AttnSplit sp;
     sp.kc = kc;
     sp.nkc = (P + kc - 1) / kc;
@@ -411,17 +472,24 @@ int launch_attn_prefill(const AttnArgs &a0, hipStream_t s) {
     if (a.nkc > 1 && !a.part) return PPX_E_INVAL;
     dim3 grid((a.M * G + 64 * ATTN_CPW - 1) / (64 * ATTN_CPW), a.nkc, a.KVH);
     switch (a.hd) {
-    case 64: hipLaunchKernelGGL((k_attn_prefill<64, ATTN_CPW>), grid, dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((k_attn_prefill<128, ATTN_CPW>), grid, dim3(256), 0, s, a); break;
-    case 256: hipLaunchKernelGGL((k_attn_prefill<256, ATTN_CPW>), grid, dim3(256), 0, s, a); break;
+#define PPX_ATTN(hd_, np_, depth_)                                                                   \
+    case hd_: {                                                                                      \
+        using C = ACfg<hd_, ATTN_CPW, np_, depth_>;                                                  \
+        hipLaunchKernelGGL((k_attn_prefill<C>), grid, dim3(C::NT), 0, s, a);                         \
+        break;                                                                                       \
+    }
+        PPX_ATTN(64, 1, 8)
+        PPX_ATTN(128, 2, 6)
+        PPX_ATTN(256, 2, 4)
+#undef PPX_ATTN
     default: return PPX_E_UNSUPPORTED;
     }
     if (a.nkc == 1) return ok();
     if (hipGetLastError() != hipSuccess) return PPX_E_HIP;
     switch (a.hd) {
-    case 64: hipLaunchKernelGGL(k_attn_prefill_merge<64>, dim3(a.M * a.H), dim3(64), 0, s, a); break;
-    case 128: hipLaunchKernelGGL(k_attn_prefill_merge<128>, dim3(a.M * a.H), dim3(128), 0, s, a); break;
-    default: hipLaunchKernelGGL(k_attn_prefill_merge<256>, dim3(a.M * a.H), dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL(k_attn_prefill_merge<64>, dim3((a.M * a.H + 3) / 4), dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL(k_attn_prefill_merge<128>, dim3((a.M * a.H + 3) / 4), dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL(k_attn_prefill_merge<256>, dim3((a.M * a.H + 3) / 4), dim3(256), 0, s, a); break;
     }
     return ok();
 }

@@ -776,6 +776,9 @@ int ppx_kv_init(ppx_model *m, void *kv_dev, size_t bytes, int n_ctx, ppx_kv **ou
     if (bytes < need) return PPX_E_NOMEM;
     if ((reinterpret_cast<uintptr_t>(kv_dev) & 255) != 0) return PPX_E_INVAL;
     PPX_TRY(ensure_rope(m, n_ctx));
+    // positions never written read as zero: attention tiles that run past the
+    // last written position multiply those values by zero probabilities
+    if (need && hipMemset(kv_dev, 0, need) != hipSuccess) return PPX_E_HIP;
     ppx_kv *kv = new ppx_kv();
     kv->m = m;
     const size_t kbytes = ((size_t)m->info.n_layer_kv_from_start * n_ctx * m->info.kv_dim * 2 + 255) / 256 * 256;
