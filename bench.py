@@ -230,7 +230,7 @@ def main():
                             f"{cfg.n_head}x{cfg.head_dim} heads, {cfg.n_kv_head} KV head(s), FFN {cfg.n_ff}, "
                             f"vocab {cfg.n_vocab}, PLE {cfg.ple_dim}",
                    "global_batch": 1, "seq_len": a.n, "ubatch": ub, "prune": a.prune, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "kernel": f"k_q4gemm gate|up + GLU epilogue, M={ub} N={2 * cfg.n_ff} "
+        "roofline": {"bound": "mfma", "kernel": f"k_q4gemm_p gate|up + GLU epilogue, M={ub} N={2 * cfg.n_ff} "
                                                   f"K={cfg.d_model}",
                      "achieved": glu_tflops, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                      "frac": glu_tflops / PEAK_FP16_TFLOPS, "traffic": stored_traffic(),
