@@ -173,6 +173,21 @@ int ppx_prefill(ppx_model *m, ppx_kv *kv, const int32_t *tokens_host, int n_toke
                 const ppx_prefill_params *p, void *ws_dev, size_t ws_bytes, float *logits_dev,
                 void *hip_stream);
 
+/* One generation step after a prefill: the row of `token` at position n_pos
+ * runs through every layer on the single-row (GEMV) path -- KV-owning layers
+ * append its fp16 K and V at n_pos, KV-shared layers read their source
+ * layer's cache -- and the logits of that row, fp32 [n_vocab], go to
+ * logits_dev.  The result is that of ppx_prefill of the one token (the
+ * pages' text-generation runs, "tg128", reuse the same cache after a
+ * prefill).  ws_dev: >= ppx_workspace_bytes(m, 1, n_ctx) bytes (a prefill's
+ * workspace for the same n_ctx is large enough), 256-byte aligned.  On
+ * success n_pos advances by one.  Errors are reported before any work is
+ * queued and leave n_pos unchanged: PPX_E_TOKEN, PPX_E_CTX (cache full),
+ * PPX_E_INVAL, PPX_E_NOMEM; PPX_E_HIP if a launch fails.  Asynchronous on
+ * the stream; one call in flight per kv. */
+int ppx_decode(ppx_model *m, ppx_kv *kv, int32_t token, void *ws_dev, size_t ws_bytes, float *logits_dev,
+               void *hip_stream);
+
 /* The prune predicate printed on the llama.cpp Gemma 4 prefill page
  * (section 1): 1 iff crop_before_nextn, 0 < n_layer_kv_from_start < n_layer,
  * !embeddings, n_seq_max == 1 and no embeddings_layer_inp[il] is set for il
@@ -187,7 +202,7 @@ int ppx_prune_predicate(int n_layer, int n_layer_kv_from_start, int embeddings, 
  * addressed by their first member: "blk.3.wq" = Q rows in RoPE-pair order
  * (16-row blocks alternate the two halves of each head), "blk.3.wk" = K
  * rows in that order followed by V rows (owning layers), "blk.3.ffn_gate" =
- * gate|up with 16-row blocks alternating gate and up.
+ * gate|up with 8-row blocks alternating gate and up.
  *
  * fp16 activations that feed a GEMM (and the prefill attention's output)
  * use the engine's fragment-tiled layout: A[M][K] is cut into 16-row x

@@ -72,6 +72,7 @@ SIGNATURES = [
     ("ppx_kv_load", c_int, [c_void_p, c_char_p, c_int, c_void_p]),
     ("ppx_kvfile_validate", c_int, [c_char_p, c_int, c_int, c_int, c_int, POINTER(c_int)]),
     ("ppx_workspace_bytes", c_size_t, [c_void_p, c_int, c_int]),
+    ("ppx_decode", c_int, [c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_void_p, c_void_p]),
     ("ppx_prefill", c_int, [c_void_p, c_void_p, c_void_p, c_int, POINTER(PrefillParams), c_void_p, c_size_t,
                             c_void_p, c_void_p]),
     ("ppx_prune_predicate", c_int, [c_int, c_int, c_int, c_int, POINTER(c_uint8), c_int]),
@@ -204,6 +205,17 @@ class Model:
         st = lib().ppx_prefill(self._h, kv.handle, c_void_p(toks.ctypes.data), toks.shape[0], ctypes.byref(p),
                                _ptr(ws), ws.numel(), _ptr(logits), _stream(stream))
         _check(st, "ppx_prefill")
+        return logits
+
+    def decode(self, token: int, kv: "KVCache", logits=None, stream=None):
+        """One generation step: `token` at kv.n_pos through every layer on the
+        single-row path (owning layers append its K/V); return its fp32 logits."""
+        import torch
+        if logits is None:
+            logits = torch.empty(self.info["n_vocab"], dtype=torch.float32, device="cuda")
+        ws = self.workspace(1, kv.n_ctx)
+        _check(lib().ppx_decode(self._h, kv.handle, int(token), _ptr(ws), ws.numel(), _ptr(logits), _stream(stream)),
+               "ppx_decode")
         return logits
 
     # ---- kernel-level entry points

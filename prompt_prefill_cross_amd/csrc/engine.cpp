@@ -319,8 +319,10 @@ GemvArgs gemv_base(Ctx &c, const float *x, const Q4R &W, int epi, float *out) {
     return a;
 }
 
-// Layer il for the single output row (pruned KV-shared layers), fp32 throughout.
-int layer_row(Ctx &c, int il, int pos, const int32_t *tok) {
+// Layer il for one row at position pos, fp32 throughout: the pruned KV-shared
+// layers of a prefill, and every layer of a decode step (where an owning layer
+// first writes the row's K and V at pos).
+int layer_row(Ctx &c, int il, int pos, const int32_t *tok, bool write_kv = false) {
     const ppx_model *m = c.m;
     const ppx_model_info &I = m->info;
     const LayerW &w = m->layers[il];
@@ -338,6 +340,20 @@ int layer_row(Ctx &c, int il, int pos, const int32_t *tok) {
     gq.pos = pos;
     gq.rope = m->rope;
     PPX_LAUNCH(c, PPX_PHASE_ROW, launch_gemv(gq, c.s));
+    if (write_kv && w.own) {
+        GemvArgs gk = gemv_base(c, xr, w.wkv, GV_KV, nullptr);
+        gk.norm_g = w.attn_norm;
+        gk.eps = m->eps;
+        gk.hd = hd;
+        gk.pos = pos;
+        gk.rope = m->rope;
+        gk.kc = c.kv->k + (size_t)il * lstride;
+        gk.vt = c.kv->vt + (size_t)il * c.kv->vld * kvd;
+        gk.kvd = kvd;
+        gk.vld = c.kv->vld;
+        PPX_LAUNCH(c, PPX_PHASE_ROW, launch_gemv(gk, c.s));
+        if (c.tm) c.tm->row_bytes += q4_bytes(w.wkv);
+    }
     Attn1Args at;
     at.q = qr;
     at.k = c.kv->k + (size_t)w.src * lstride;
@@ -608,6 +624,30 @@ int prefill(ppx_model *m, ppx_kv *kv, const int32_t *tokens, int n, const ppx_pr
     return PPX_OK;
 }
 
+// One generated token: the row at position n_pos through every layer on the
+// single-row path (owning layers append its K and V), then the head.  The
+// same computation as a prefill of that one token.
+int decode(ppx_model *m, ppx_kv *kv, int32_t token, void *ws, size_t ws_bytes, float *logits, hipStream_t s) {
+    if (!m || !kv || !logits || !ws) return PPX_E_INVAL;
+    if (kv->m != m) return PPX_E_INVAL;
+    const ppx_model_info &I = m->info;
+    if (token < 0 || token >= I.n_vocab) return PPX_E_TOKEN;
+    const int pos = kv->n_pos;
+    if (pos + 1 > kv->n_ctx) return PPX_E_CTX;
+    if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return PPX_E_INVAL;
+    Ctx c{m, kv, s, static_cast<uint8_t *>(ws), ws_layout(m, 1, kv->n_ctx)};
+    if (ws_bytes < c.L.total) return PPX_E_NOMEM;
+    int32_t *tok_dev = c.at<int32_t>(c.L.tok);
+    PPX_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(tok_dev), (uint32_t)token, 1, s));  // by value: no host buffer to outlive
+    float *xr = c.at<float>(c.L.xr);
+    PPX_TRY(launch_embed(m->tok, tok_dev, 1, m->embd_scale, xr, s));
+    for (int il = 0; il < I.n_layer; ++il) PPX_TRY(layer_row(c, il, pos, tok_dev, true));
+    PPX_TRY(head_row(c, xr, logits));
+    PPX_TRY(c.finish());
+    kv->n_pos = pos + 1;
+    return PPX_OK;
+}
+
 // ------------------------------------------------------------------ KVCP snapshots
 
 int kv_save(const ppx_kv *kv, const char *path, int n_pos, hipStream_t s) {
@@ -820,6 +860,11 @@ size_t ppx_workspace_bytes(const ppx_model *m, int n_ubatch, int n_ctx) {
 int ppx_prefill(ppx_model *m, ppx_kv *kv, const int32_t *tokens_host, int n_tokens, const ppx_prefill_params *p,
                 void *ws_dev, size_t ws_bytes, float *logits_dev, void *hip_stream) {
     return prefill(m, kv, tokens_host, n_tokens, p, ws_dev, ws_bytes, logits_dev, (hipStream_t)hip_stream);
+}
+
+int ppx_decode(ppx_model *m, ppx_kv *kv, int32_t token, void *ws_dev, size_t ws_bytes, float *logits_dev,
+               void *hip_stream) {
+    return decode(m, kv, token, ws_dev, ws_bytes, logits_dev, (hipStream_t)hip_stream);
 }
 
 int ppx_prune_predicate(int n_layer, int n_layer_kv_from_start, int embeddings, int n_seq_max,

@@ -120,7 +120,7 @@ int ok() { return hipGetLastError() == hipSuccess ? PPX_OK : PPX_E_HIP; }
 // bits; B holds (code - 8) exactly, and each block's partial is scaled by its
 // fp32 block scale -- only fp32 accumulation rounds.
 // A workgroup owns G groups of 16 columns (G = 2 when the epilogue combines
-// the two RoPE halves); KW waves per group take interleaved 64-wide K
+// the two RoPE halves of Q or K); KW waves per group take interleaved 64-wide K
 // chunks with UNR weight loads in flight.  v is staged once per workgroup in
 // LDS as hi/lo fp16 arrays, so a lane's A-operand piece is one 16-byte read.
 // Partial sums meet in LDS in wave order: the result is deterministic and no
@@ -223,6 +223,24 @@ __global__ __launch_bounds__(64 * KW * G) void k_q4gemv(GemvArgs a) {
             a.out[h * hd + ii + hh] = yv[0] * cs.y + yv[G - 1] * cs.x;
         }
         break;
+    case GV_KV:
+        if (G == 2) {
+            if (n0 < a.kvd) {
+                // K: groups (2p, 2p+1) hold the first and second RoPE half of 16 dims
+                const int hd = a.hd, hh = hd >> 1;
+                const int h = n0 / hd, rr = n0 % hd;
+                const int ii = (rr >> 5) * 16 + c;
+                const float2 cs = a.rope[(size_t)a.pos * hh + ii];
+                __half *k = a.kc + (size_t)a.pos * a.kvd + h * hd;
+                k[ii] = __float2half(yv[0] * cs.x - yv[G - 1] * cs.y);
+                k[ii + hh] = __float2half(yv[0] * cs.y + yv[G - 1] * cs.x);
+            } else {
+#pragma unroll
+                for (int q = 0; q < G; ++q)
+                    a.vt[(size_t)(n0 - a.kvd + 16 * q + c) * a.vld + a.pos] = __float2half(yv[q]);
+            }
+        }
+        break;
     case GV_GLU:
         // columns 0-7 of the group are gate rows 8t..8t+7, columns 8-15 their up rows
         if (c < 8) {
@@ -252,8 +270,9 @@ int gemv_kw(int groups, int kch) {
 }  // namespace
 
 int launch_gemv(const GemvArgs &a, hipStream_t s) {
-    if (a.W.N % 32 || a.W.K % 64 || !a.x || !a.out) return PPX_E_UNSUPPORTED;
-    const bool paired = a.epi == GV_QROPE;
+    if (a.W.N % 32 || a.W.K % 64 || !a.x) return PPX_E_UNSUPPORTED;
+    if (a.epi == GV_KV ? (!a.kc || !a.vt || a.kvd % 32 || 2 * a.kvd != a.W.N) : !a.out) return PPX_E_UNSUPPORTED;
+    const bool paired = a.epi == GV_QROPE || a.epi == GV_KV;
     const int G = paired ? 2 : 1;
     const int kw = std::min(gemv_kw(a.W.N / 16, a.W.K / 64), 16 / G);
     const dim3 grid(a.W.N / (16 * G));

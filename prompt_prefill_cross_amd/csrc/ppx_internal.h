@@ -42,7 +42,7 @@ struct LayerW {
     Q4R wq;    // [qd][d], rows in rope-pair order
     Q4R wkv;   // own only: [2 kvd][d] rows K (rope-pair order) | V; run on the exact-weight path
     Q4R wo;    // [d][qd]
-    Q4R wgu;   // [2F][d]: 16-row blocks alternate gate, up
+    Q4R wgu;   // [2F][d]: 8-row blocks alternate gate, up
     Q4R wdown; // [d][F]
     Q4R wpg;   // [E][d]
     Q4R wpu;   // [d][E]
@@ -151,6 +151,7 @@ enum GemvEpi {
     GV_QROPE = 2, // rope(Q part) -> out fp32 [qd] (natural order), pos
     GV_GLU = 3,   // act(gate)*up -> out fp32 [F]
     GV_PLE = 4,   // gelu(y) * s * deq(ple row) -> out fp32 [E]
+    GV_KV = 5,    // fused K|V weight: rope(K) and V -> fp16 cache at pos (K rows, V^T columns)
 };
 struct GemvArgs {
     const float *x = nullptr;  // [K]
@@ -166,6 +167,9 @@ struct GemvArgs {
     const int32_t *tok = nullptr;  // device pointer to the row's token id
     int ple_row_blocks = 0, ple_col0 = 0;
     float ple_s = 0.f;
+    __half *kc = nullptr;   // GV_KV: K cache of the layer [n_ctx][kvd]
+    __half *vt = nullptr;   // GV_KV: V cache of the layer, transposed [kvd][vld]
+    int kvd = 0, vld = 0;
 };
 int launch_gemv(const GemvArgs &a, hipStream_t s);
 
