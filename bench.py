@@ -43,6 +43,7 @@ def parse():
     ap.add_argument("--ubatch", type=int, default=0, help="0 = the config's ubatch")
     ap.add_argument("--prune", default="auto", choices=["auto", "on", "off"])
     ap.add_argument("--extra-n", default="512,8192", help="other prompt lengths to report (comma list, '' = none)")
+    ap.add_argument("--decode", type=int, default=32, help="tokens decoded after the main prompt (0 = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="prompt tokens of the oracle sample (0 = all)")
     ap.add_argument("--pmc-pass", action="store_true", help="one prefill + one calibration copy, then exit")
@@ -141,6 +142,42 @@ def glu_kernel_us(mm, ub, reps=50, warmup=5):
     return t0.elapsed_time(t1) * 1e3 / reps, reps
 
 
+def decode_bytes(I, pos):
+    """HBM bytes one decode step at position pos reads: every layer's Q4_0
+    weights, the head, its per-layer embedding row and the K/V of positions
+    0..pos of each layer's cache."""
+    q4 = lambda n, k: n * k * 18 / 32
+    d, qd, kvd, F, E = I["d_model"], I["n_head"] * I["head_dim"], I["kv_dim"], I["n_ff"], I["ple_dim"]
+    per = q4(qd, d) + q4(d, qd) + q4(2 * F, d) + q4(d, F) + (q4(E, d) + q4(d, E) if E else 0)
+    b = I["n_layer"] * (per + (pos + 1) * kvd * 2 * 2) + I["n_layer_kv_from_start"] * q4(2 * kvd, d)
+    return b + q4(I["n_vocab"], d) + I["n_layer"] * E * 18 / 32
+
+
+def decode_pass(mm, kv, toks, ub, n_dec, warmup=2):
+    """Prefill toks[:-n_dec-warmup], then time n_dec single-token decode steps."""
+    import torch
+    n0 = len(toks) - n_dec - warmup
+    logits = torch.empty(mm.info["n_vocab"], dtype=torch.float32, device="cuda")
+    kv.clear()
+    mm.prefill(toks[:n0], kv, n_ubatch=ub, logits=logits)
+    for i in range(warmup):
+        mm.decode(int(toks[n0 + i]), kv, logits=logits)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    p0 = kv.n_pos
+    t0.record()
+    for i in range(n_dec):
+        mm.decode(int(toks[p0 + i]), kv, logits=logits)
+    t1.record()
+    t1.synchronize()
+    ms = t0.elapsed_time(t1) / n_dec
+    byts = float(np.mean([decode_bytes(mm.info, p0 + i) for i in range(n_dec)]))
+    return {"after_prompt": p0, "tokens": n_dec, "ms_per_token": ms, "tokens_per_s": 1e3 / ms,
+            "hbm_bytes_per_token": byts, "gbs": byts / (ms * 1e-3) / 1e9,
+            "frac_hbm": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
 def pmc_pass(mm, kv, toks, ub, prune):
     import torch
     kv.clear()
@@ -184,7 +221,7 @@ def main():
     buf = synth.build_model(cfg)
     mm = ppx.Model(buf)
     lens = [a.n] + [int(x) for x in a.extra_n.split(",") if x.strip() and int(x) != a.n]
-    n_ctx = max(lens)
+    n_ctx = max(max(lens), a.n + a.decode + 2)
     kv = ppx.KVCache(mm, n_ctx)
     mm.workspace(ub, n_ctx)
 
@@ -201,6 +238,12 @@ def main():
         results[n] = (times, ph)
         print(f"# n={n}: {np.median(times):.3f} ms median, {n / np.median(times) * 1e3:.0f} tok/s; "
               f"phases ms {ph['ms']}", file=sys.stderr, flush=True)
+
+    dec = None
+    if a.decode:
+        dec = decode_pass(mm, kv, synth.prompt(cfg, a.n + a.decode + 2), ub, a.decode)
+        print(f"# decode after {dec['after_prompt']}: {dec['ms_per_token']:.3f} ms/token, "
+              f"{dec['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
 
     times, ph = results[a.n]
     glu_us, glu_reps = glu_kernel_us(mm, ub)
@@ -244,6 +287,7 @@ def main():
                    "gemm_flop": ph["gemm_flop"], "attn_flop": ph["attn_flop"], "row_bytes": ph["row_bytes"]},
         "other_lengths": {str(n): {"ms_median": float(np.median(t)), "tokens_per_s": n / float(np.median(t)) * 1e3}
                           for n, (t, _) in results.items()},
+        "decode": dec,
         "ms_median": float(np.median(times)),
         "ms_std": float(np.std(times)),
     }

@@ -83,7 +83,8 @@ __device__ __forceinline__ float row_swap8(float v) {
 
 // Epilogue of one wave tile: acc[i][j][r] = C[r0 + 16i + 4(lane/16) + r][c0 + 16j + lane%16].
 template <int TM, int TN>
-__device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, const f4 (&acc)[TM][TN], int r0, int c0, int lane) {
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, const f4 (&acc)[TM][TN], int r0, int c0, int lane,
+                                              _Float16 *stage = nullptr) {
     const int lc = lane & 15, lr = (lane >> 4) * 4;
     const int N = a.W.N;
     if (a.epi == EPI_F32 || a.epi == EPI_ADD) {
@@ -125,6 +126,35 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, const f4 (&acc)
         // lanes c >= 8 the last two.
         const int F = N >> 1;
         const bool lo = lc < 8;
+        if (stage) {
+            // through this wave's LDS staging area (TM x TN x 16 units of 16 bytes:
+            // eight consecutive f of one row), so that the tiled output is written
+            // one 16-byte unit per lane
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const float v0 = acc[i][j][2 * h], v1 = acc[i][j][2 * h + 1];
+                        const float p0 = row_swap8(v0), p1 = row_swap8(v1);
+                        if (lo == (h == 0)) {
+                            const float g0 = lo ? v0 : p0, u0 = lo ? p0 : v0;
+                            const float g1 = lo ? v1 : p1, u1 = lo ? p1 : v1;
+                            _Float16 *u = stage + ((i * TN + j) * 16 + lr + 2 * h) * 8 + (lc & 7);
+                            u[0] = (_Float16)(act_f(a.act, g0) * u0);
+                            u[8] = (_Float16)(act_f(a.act, g1) * u1);
+                        }
+                    }
+#pragma unroll
+            for (int u = lane; u < TM * TN * 16; u += 64) {
+                const int i = u / (TN * 16), j = (u / 16) % TN, rr = u % 16;
+                const int row = r0 + i * 16 + rr;
+                const h8 v = *reinterpret_cast<const h8 *>(stage + u * 8);
+                if (row < a.M) *reinterpret_cast<h8 *>(a.out_f16 + tiled_index(row, ((c0 >> 4) + j) * 8, F)) = v;
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -211,10 +241,11 @@ struct PCfg {
     static constexpr int TMS = TM / NFG;
     static constexpr int SLOT_FLOATS = TMS * TN * 4 * 64;
     static constexpr int XCH_FLOATS = (KS * NFG - NFG) * NWN * SLOT_FLOATS;
+    static constexpr int STAGE_HALVES = TMS * TN * 16 * 8;  // epilogue staging per compute wave
     static_assert(NT <= 1024, "workgroup size");
     static_assert(DEPTH >= 3 && (DEPTH - 3) * PER <= 63, "ring depth / vmcnt range");
     static_assert(DEPTH * STAGE_UNITS * 16 <= 160 * 1024, "LDS");
-    static_assert(XCH_FLOATS * 4 <= DEPTH * STAGE_UNITS * 16, "exchange space");
+    static_assert(XCH_FLOATS * 4 + NCW * STAGE_HALVES * 2 <= DEPTH * STAGE_UNITS * 16, "exchange + staging space");
     // exchange slot of the rows K group gs hands to finishing group gd (gs != gd)
     __device__ static constexpr int slot(int gs, int gd) {
         return gs * NFG - (gs < NFG ? gs : NFG) + gd - ((gs < NFG && gd > gs) ? 1 : 0);
@@ -226,7 +257,7 @@ struct PCfg {
 // the epilogue, or the fp32 partial of this workgroup's K range.
 template <class C, int G>
 __device__ __forceinline__ void finish_rows(const GemmArgs &a, const f4 (&acc)[C::TM][C::TN], const float *xch,
-                                            int wn, int m0, int n0, int lane) {
+                                            int wn, int m0, int n0, int lane, _Float16 *stage) {
     f4 sum[C::TMS][C::TN];
 #pragma unroll
     for (int i = 0; i < C::TMS; ++i)
@@ -251,7 +282,7 @@ __device__ __forceinline__ void finish_rows(const GemmArgs &a, const f4 (&acc)[C
     }
     const int r0 = m0 + G * C::TMS * 16, c0 = n0 + wn * C::WN;
     if (gridDim.z == 1) {
-        gemm_epilogue<C::TMS, C::TN>(a, sum, r0, c0, lane);
+        gemm_epilogue<C::TMS, C::TN>(a, sum, r0, c0, lane, stage);
     } else {
         // partial tile layout: [split][row tile][16-column group][r][lane]
         const int Mt = gridDim.y * C::TM, Nt = a.W.N >> 4;
@@ -269,10 +300,10 @@ __device__ __forceinline__ void finish_rows(const GemmArgs &a, const f4 (&acc)[C
 
 template <class C, int G>
 __device__ __forceinline__ void finish_group(const GemmArgs &a, const f4 (&acc)[C::TM][C::TN], const float *xch,
-                                             int g, int wn, int m0, int n0, int lane) {
+                                             int g, int wn, int m0, int n0, int lane, _Float16 *stage) {
     if constexpr (G < C::NFG) {
-        if (g == G) finish_rows<C, G>(a, acc, xch, wn, m0, n0, lane);
-        else finish_group<C, G + 1>(a, acc, xch, g, wn, m0, n0, lane);
+        if (g == G) finish_rows<C, G>(a, acc, xch, wn, m0, n0, lane, stage);
+        else finish_group<C, G + 1>(a, acc, xch, g, wn, m0, n0, lane, stage);
     }
 }
 
@@ -420,7 +451,9 @@ __global__ __launch_bounds__(C::NT) void k_q4gemm_p(GemmArgs a) {
         }
         __syncthreads();  // compute waves only: the producers have returned
     }
-    finish_group<C, 0>(a, acc, xch, g, wn, m0, n0, lane);
+    // each compute wave's epilogue staging area follows the exchange space
+    _Float16 *stage = reinterpret_cast<_Float16 *>(xch + C::XCH_FLOATS) + (size_t)wave * C::STAGE_HALVES;
+    finish_group<C, 0>(a, acc, xch, g, wn, m0, n0, lane, stage);
 }
 
 // Sum of the S split partials in split order, then the epilogue; one wave per
