@@ -247,12 +247,23 @@ __global__ __launch_bounds__(C::NT) void k_attn_prefill(AttnArgs a) {
                 *reinterpret_cast<h4 *>(a.o + tiled_index(t[c], h[c] * HD + d, od)) = v;
             }
         } else {
+            // the chunk's own normalised output in fp16 (a convex combination of
+            // value rows, so bounded by them), its max and exp-sum in fp32; a
+            // row that sees no key of the chunk writes zeros, never read
             const size_t slot = ((size_t)ck * a.M + t[c]) * a.H + h[c];
-            float *po = a.part + slot * HD;
+            const float inv = lrun[c] > 0.f ? 1.0f / lrun[c] : 0.f;
+            _Float16 *po = reinterpret_cast<_Float16 *>(a.part) + slot * HD;
 #pragma unroll
-            for (int i = 0; i < DT; ++i) *reinterpret_cast<f4 *>(po + i * 16 + lg * 4) = oacc[c][i];
+            for (int i = 0; i < DT; ++i) {
+                h4 v;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = (_Float16)(oacc[c][i][r] * inv);
+                *reinterpret_cast<h4 *>(po + i * 16 + lg * 4) = v;
+            }
             if (lg == 0) {
-                float *pm = a.part + (size_t)a.nkc * a.M * a.H * HD + slot * 2;
+                // (max, sum) pairs of one (row, head) are contiguous over the chunks
+                float *pm = a.part + (size_t)a.nkc * a.M * a.H * (HD / 2) +
+                            (((size_t)t[c] * a.H + h[c]) * a.nkc + ck) * 2;
                 pm[0] = mrun[c];
                 pm[1] = lrun[c];
             }
@@ -261,32 +272,51 @@ __global__ __launch_bounds__(C::NT) void k_attn_prefill(AttnArgs a) {
 }
 
 // Combine the key chunks of row t, head h: chunks 0..floor(pos/kc) hold keys
-// the row can see.  Max-subtracted weights in the exp2 domain of the kernel.
-// One wave per (row, head): lane l owns dims 4l .. 4l+3 of each 256-dim slice;
+// the row can see.  Chunk c contributes its normalised output with weight
+// l_c 2^(m_c - M) (max-subtracted, in the exp2 domain of the kernel).  One
+// wave per (row, head): lane l owns dims 4l .. 4l+3 of each 256-dim slice;
 // the chunks are summed in chunk order.
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn_prefill_merge(AttnArgs a) {
+    static_assert(ATTN_MAX_CHUNKS <= 64, "one chunk per lane");
     const int lane = threadIdx.x & 63;
-    const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
     if (w >= a.M * a.H) return;
     const int t = w / a.H, h = w % a.H;
     const int nch = (a.pos0 + t) / a.kc + 1;
-    const float *pm = a.part + (size_t)a.nkc * a.M * a.H * HD;
-    float M = -INFINITY;
-    for (int c = 0; c < nch; ++c) M = fmaxf(M, pm[(((size_t)c * a.M + t) * a.H + h) * 2]);
-    constexpr int NV = (HD + 255) / 256;  // float4 per lane
+    const _Float16 *po = reinterpret_cast<const _Float16 *>(a.part);
+    const float *pm = a.part + (size_t)a.nkc * a.M * a.H * (HD / 2) + (size_t)w * a.nkc * 2;
+    // lane c holds chunk c's weight l_c 2^(m_c - M)
+    const bool own = lane < nch;
+    const float mc = own ? pm[2 * lane] : -INFINITY;
+    const float lc = own ? pm[2 * lane + 1] : 0.f;
+    const float M = wave_max(mc);
+    const float wl = own ? exp2f(mc - M) * lc : 0.f;
+    constexpr int NV = (HD + 255) / 256;  // four dims per lane per slice
+    const size_t cstride = (size_t)a.M * a.H * HD;  // fp16 elements per chunk
+    const _Float16 *base = po + (size_t)w * HD;
     f4 O[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) O[v] = f4{0.f, 0.f, 0.f, 0.f};
     float L = 0.f;
-    for (int c = 0; c < nch; ++c) {
-        const size_t slot = ((size_t)c * a.M + t) * a.H + h;
-        const float wgt = exp2f(pm[slot * 2] - M);
-        L += wgt * pm[slot * 2 + 1];
+    // eight chunks' loads in flight at a time; the sums stay in chunk order
+    for (int c0 = 0; c0 < nch; c0 += 8) {
+        h4 x[8][NV];
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            const int d = v * 256 + lane * 4;
-            if (d < HD) O[v] += wgt * *reinterpret_cast<const f4 *>(a.part + slot * HD + d);
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+                x[u][v] = *reinterpret_cast<const h4 *>(base + (size_t)min(c0 + u, nch - 1) * cstride +
+                                                        min(v * 256 + lane * 4, HD - 4));
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            // chunks past the last repeat it with weight 0 (no branch, so every load above issues at once)
+            const float wg = c0 + u < nch ? __shfl(wl, c0 + u, 64) : 0.f;
+            L += wg;
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) O[v][e] += wg * (float)x[u][v][e];
         }
     }
     const float inv = 1.0f / L;
@@ -458,7 +488,7 @@ AttnSplit attn_split(int M, int H, int KVH, int pos0) {
 
 size_t attn_prefill_scratch_floats(int M, int H, int hd, int n_ctx) {
     const int nkc = std::min(ATTN_MAX_CHUNKS, (n_ctx + 255) / 256);
-    return (size_t)nkc * M * H * (hd + 2);
+    return (size_t)nkc * M * H * (hd / 2 + 2);  // fp16 chunk outputs, then fp32 (max, sum) pairs
 }
 
 int launch_attn_prefill(const AttnArgs &a0, hipStream_t s) {
