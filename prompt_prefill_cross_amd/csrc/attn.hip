@@ -430,18 +430,22 @@ __global__ __launch_bounds__(256) void k_attn_1row(Attn1Args a) {
     }
 }
 
-// o[h][d] = sum_c e^(m_c - M) o_c[d] / sum_c e^(m_c - M) l_c, chunks in order.
+// o[h][d] = sum_c e^(m_c - M) o_c[d] / sum_c e^(m_c - M) l_c.  One workgroup
+// per head: thread (s, q) owns dims 4q .. 4q+3 and the chunks c = s (mod NS),
+// NS = 1024 / hd subsets, four chunks' loads in flight at a time; the subsets
+// are then added in subset order, so the result is deterministic.
 __global__ __launch_bounds__(256) void k_attn_merge(Attn1Args a, int nchunks) {
     __shared__ float wl[1024];
-    __shared__ float red[4];
-    const int h = blockIdx.x, tid = threadIdx.x;
-    const int hd = a.hd;
+    __shared__ float red[8];
+    __shared__ f4 part[256];
+    const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hd = a.hd, nq = hd >> 2, ns = 256 / nq;
     const float *st = a.partial + (size_t)h * nchunks * 2;
     const float *po = a.partial + (size_t)a.H * nchunks * 2 + (size_t)h * nchunks * hd;
     float M = -INFINITY;
     for (int c = tid; c < nchunks; c += 256) M = fmaxf(M, st[2 * c]);
     M = wave_max(M);
-    if ((tid & 63) == 0) red[tid >> 6] = M;
+    if (lane == 0) red[wave] = M;
     __syncthreads();
     M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     float L = 0.f;
@@ -450,18 +454,33 @@ __global__ __launch_bounds__(256) void k_attn_merge(Attn1Args a, int nchunks) {
         if (c < 1024) wl[c] = w;
         L += w * st[2 * c + 1];
     }
-    __syncthreads();
     L = wave_sum(L);
-    if ((tid & 63) == 0) red[tid >> 6] = L;
+    if (lane == 0) red[4 + wave] = L;
     __syncthreads();
-    L = red[0] + red[1] + red[2] + red[3];
-    for (int d = tid; d < hd; d += 256) {
-        float o = 0.f;
-        for (int c = 0; c < nchunks; ++c) {
-            const float w = c < 1024 ? wl[c] : expf(st[2 * c] - M);
-            o += w * po[(size_t)c * hd + d];
+    L = red[4] + red[5] + red[6] + red[7];
+    const int q = tid % nq, sub = tid / nq;
+    f4 o = {0.f, 0.f, 0.f, 0.f};
+    if (sub < ns) {
+        for (int c0 = sub; c0 < nchunks; c0 += 4 * ns) {
+            f4 x[4];
+            float w[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = min(c0 + u * ns, nchunks - 1);
+                x[u] = *reinterpret_cast<const f4 *>(po + (size_t)c * hd + 4 * q);
+                w[u] = c0 + u * ns < nchunks ? (c < 1024 ? wl[c] : expf(st[2 * c] - M)) : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) o += w[u] * x[u];
         }
-        a.o[(size_t)h * hd + d] = o / L;
+    }
+    part[tid] = o;
+    __syncthreads();
+    if (tid < nq) {
+        f4 r = part[tid];
+        for (int s2 = 1; s2 < ns; ++s2) r += part[s2 * nq + tid];
+        const float inv = 1.0f / L;
+        *reinterpret_cast<f4 *>(a.o + (size_t)h * hd + 4 * tid) = r * inv;
     }
 }
 
