@@ -127,74 +127,10 @@ int ok() { return hipGetLastError() == hipSuccess ? PPX_OK : PPX_E_HIP; }
 // workgroup waits for another.
 constexpr int GEMV_UNR = 4;
 
+// The finished unit: thread c < 16 sums column c of each group over the KW
+// waves (in wave order) and applies the epilogue.
 template <int KW, int G>
-__global__ __launch_bounds__(64 * KW * G) void k_q4gemv(GemvArgs a) {
-    extern __shared__ float gemv_lds[];  // red[G][KW][16] floats, then hi[K], lo[K] fp16
-    constexpr int NT = 64 * KW * G;
-    const int K = a.W.K, kch = K >> 6;
-    float *red = gemv_lds;
-    _Float16 *xh = reinterpret_cast<_Float16 *>(gemv_lds + G * KW * 16);
-    _Float16 *xl = xh + K;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int gi = wave / KW, kw = wave % KW;
-    const int grp = G * blockIdx.x + gi;
-
-    // stage v (normalised if asked) as hi / lo halves
-    float r = 1.f;
-    if (a.norm_g) {
-        float ss = 0.f;
-        for (int k = tid; k < K; k += NT) ss += a.x[k] * a.x[k];
-        ss = wave_sum(ss);
-        if (lane == 0) red[wave] = ss;
-        __syncthreads();
-        ss = 0.f;
-        for (int w = 0; w < NT / 64; ++w) ss += red[w];
-        r = 1.0f / sqrtf(ss / (float)K + a.eps);
-        __syncthreads();
-    }
-    for (int k = tid; k < K; k += NT) {
-        const float v = a.norm_g ? a.x[k] * r * a.norm_g[k] : a.x[k];
-        const _Float16 h = (_Float16)v;
-        xh[k] = h;
-        xl[k] = (_Float16)(v - (float)h);
-    }
-    __syncthreads();
-
-    const int col = lane & 15, g8 = (lane >> 4) * 8;
-    const _Float16 *xsrc = col == 0 ? xh : xl;  // rows 0 and 1 carry v; the others stay zero
-    const bool arow = col < 2;
-    const uint2 *nib = reinterpret_cast<const uint2 *>(a.W.nib) + (size_t)grp * kch * 64 + lane;
-    const uint32_t *scl = reinterpret_cast<const uint32_t *>(a.W.scl) + (size_t)grp * kch * 16 + col;
-    f4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int base = kw; base < kch; base += KW * GEMV_UNR) {
-        uint2 w[GEMV_UNR];
-        uint32_t sc[GEMV_UNR];
-        // loads first (clamped, so they need no branch), then the arithmetic
-#pragma unroll
-        for (int u = 0; u < GEMV_UNR; ++u) {
-            const int kc = min(base + u * KW, kch - 1);
-            w[u] = nib[(size_t)kc * 64];
-            sc[u] = scl[(size_t)kc * 16];
-        }
-#pragma unroll
-        for (int u = 0; u < GEMV_UNR; ++u) {
-            const int kc = base + u * KW;
-            if (kc >= kch) break;  // uniform across the wave
-            const h2 d = __builtin_bit_cast(h2, sc[u]);
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                h8 af = *reinterpret_cast<const h8 *>(xsrc + kc * 64 + s * 32 + g8);
-                if (!arow) af = h8{0, 0, 0, 0, 0, 0, 0, 0};
-                const f4 p = mfma16(af, q4_word_codes(s ? w[u].y : w[u].x), f4{0.f, 0.f, 0.f, 0.f});
-                acc += (float)d[s] * p;
-            }
-        }
-    }
-    // lanes 0..15 hold rows 0 and 1 (hi and lo parts) of column `col`
-    if (lane < 16) red[(gi * KW + kw) * 16 + lane] = acc[0] + acc[1];
-    __syncthreads();
-    if (tid >= 16) return;
-    const int c = tid;
+__device__ __forceinline__ void gemv_epilogue(const GemvArgs &a, const float *red, int unit, int c) {
     float yv[G];
 #pragma unroll
     for (int q = 0; q < G; ++q) {
@@ -203,7 +139,7 @@ __global__ __launch_bounds__(64 * KW * G) void k_q4gemv(GemvArgs a) {
         for (int i = 0; i < KW; ++i) y += red[(q * KW + i) * 16 + c];
         yv[q] = y;
     }
-    const int n0 = blockIdx.x * 16 * G;
+    const int n0 = unit * 16 * G;
     switch (a.epi) {
     case GV_F32:
 #pragma unroll
@@ -247,7 +183,7 @@ __global__ __launch_bounds__(64 * KW * G) void k_q4gemv(GemvArgs a) {
             float u = 0.f;
 #pragma unroll
             for (int i = 0; i < KW; ++i) u += red[i * 16 + c + 8];
-            a.out[blockIdx.x * 8 + c] = act_f(a.act, yv[0]) * u;
+            a.out[unit * 8 + c] = act_f(a.act, yv[0]) * u;
         }
         break;
     case GV_PLE: {
@@ -259,6 +195,98 @@ __global__ __launch_bounds__(64 * KW * G) void k_q4gemv(GemvArgs a) {
     }
     }
 }
+
+template <int KW, int G>
+__global__ __launch_bounds__(64 * KW * G) void k_q4gemv(GemvArgs a) {
+    extern __shared__ float gemv_lds[];  // red[G][KW][16] floats, then hi[K], lo[K] fp16
+    constexpr int NT = 64 * KW * G;
+    const int K = a.W.K, kch = K >> 6;
+    const int nunits = a.W.N / (16 * G);  // a unit: the G groups of one workgroup pass
+    float *red = gemv_lds;
+    _Float16 *xh = reinterpret_cast<_Float16 *>(gemv_lds + G * KW * 16);
+    _Float16 *xl = xh + K;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int gi = wave / KW, kw = wave % KW;
+    const int col = lane & 15, g8 = (lane >> 4) * 8;
+
+    // weight batches: UNR chunks kc = base + u KW of group G unit + gi (clamped, so no branch)
+    const uint2 *nib0 = reinterpret_cast<const uint2 *>(a.W.nib) + lane;
+    const uint32_t *scl0 = reinterpret_cast<const uint32_t *>(a.W.scl) + col;
+    uint2 w[GEMV_UNR];
+    uint32_t sc[GEMV_UNR];
+    auto load = [&](int unit, int base, uint2 (&wd)[GEMV_UNR], uint32_t (&sd)[GEMV_UNR]) {
+        const size_t grp = (size_t)(G * unit + gi) * kch;
+#pragma unroll
+        for (int u = 0; u < GEMV_UNR; ++u) {
+            const size_t kc = grp + min(base + u * KW, kch - 1);
+            wd[u] = nib0[kc * 64];
+            sd[u] = scl0[kc * 16];
+        }
+    };
+    // the first batch does not depend on v: it is in flight during the norm and staging
+    int unit = blockIdx.x;
+    load(unit, kw, w, sc);
+
+    // stage v (normalised if asked) as hi / lo halves
+    float r = 1.f;
+    if (a.norm_g) {
+        float ss = 0.f;
+        for (int k = tid; k < K; k += NT) ss += a.x[k] * a.x[k];
+        ss = wave_sum(ss);
+        if (lane == 0) red[wave] = ss;
+        __syncthreads();
+        ss = 0.f;
+        for (int i = 0; i < NT / 64; ++i) ss += red[i];
+        r = 1.0f / sqrtf(ss / (float)K + a.eps);
+        __syncthreads();
+    }
+    for (int k = tid; k < K; k += NT) {
+        const float v = a.norm_g ? a.x[k] * r * a.norm_g[k] : a.x[k];
+        const _Float16 h = (_Float16)v;
+        xh[k] = h;
+        xl[k] = (_Float16)(v - (float)h);
+    }
+    __syncthreads();
+
+    const _Float16 *xsrc = col == 0 ? xh : xl;  // rows 0 and 1 carry v; the others stay zero
+    const bool arow = col < 2;
+    for (; unit < nunits; unit += gridDim.x) {
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int base = kw; base < kch; base += KW * GEMV_UNR) {
+            // the next batch (this unit's, else the next unit's first) while this one is used
+            uint2 wn[GEMV_UNR];
+            uint32_t sn[GEMV_UNR];
+            const int nb = base + KW * GEMV_UNR;
+            const int nu = nb < kch ? unit : unit + gridDim.x;
+            if (nu < nunits) load(nu, nb < kch ? nb : kw, wn, sn);
+#pragma unroll
+            for (int u = 0; u < GEMV_UNR; ++u) {
+                const int kc = base + u * KW;
+                if (kc >= kch) break;  // uniform across the wave
+                const h2 d = __builtin_bit_cast(h2, sc[u]);
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    h8 af = *reinterpret_cast<const h8 *>(xsrc + kc * 64 + s * 32 + g8);
+                    if (!arow) af = h8{0, 0, 0, 0, 0, 0, 0, 0};
+                    const f4 p = mfma16(af, q4_word_codes(s ? w[u].y : w[u].x), f4{0.f, 0.f, 0.f, 0.f});
+                    acc += (float)d[s] * p;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < GEMV_UNR; ++u) {
+                w[u] = wn[u];
+                sc[u] = sn[u];
+            }
+        }
+        // lanes 0..15 hold rows 0 and 1 (hi and lo parts) of column `col`
+        if (lane < 16) red[(gi * KW + kw) * 16 + lane] = acc[0] + acc[1];
+        __syncthreads();
+        if (tid < 16) gemv_epilogue<KW, G>(a, red, unit, tid);
+        __syncthreads();  // red is reused by the next unit
+    }
+}
+
+constexpr int kGemvMaxGrid = 2048;
 
 // waves per group: aim for ~4096 waves in flight with >= 2 chunks per wave
 int gemv_kw(int groups, int kch) {
@@ -274,8 +302,12 @@ int launch_gemv(const GemvArgs &a, hipStream_t s) {
     if (a.epi == GV_KV ? (!a.kc || !a.vt || a.kvd % 32 || 2 * a.kvd != a.W.N) : !a.out) return PPX_E_UNSUPPORTED;
     const bool paired = a.epi == GV_QROPE || a.epi == GV_KV;
     const int G = paired ? 2 : 1;
-    const int kw = std::min(gemv_kw(a.W.N / 16, a.W.K / 64), 16 / G);
-    const dim3 grid(a.W.N / (16 * G));
+    const int units = a.W.N / (16 * G);
+    // wide outputs (the vocabulary head): a capped grid of workgroups that each
+    // stage v once and loop over their units, four waves per unit
+    const bool looped = units > kGemvMaxGrid;
+    const int kw = looped ? 4 : std::min(gemv_kw(a.W.N / 16, a.W.K / 64), 16 / G);
+    const dim3 grid(looped ? kGemvMaxGrid : units);
     const size_t lds = sizeof(float) * G * kw * 16 + 4ull * a.W.K;
     if (lds > 64 * 1024) return PPX_E_UNSUPPORTED;
 #define PPX_GEMV(KW_, G_) hipLaunchKernelGGL((k_q4gemv<KW_, G_>), grid, dim3(64 * KW_ * G_), lds, s, a)
