@@ -268,12 +268,17 @@ int layer_rows(Ctx &c, int il, int M, int row0, int pos0) {
     gd.W = w.wdown;
     gd.epi = EPI_ADD;
     gd.out_f32 = x;
+    if (I.ple_dim) {
+        // the per-layer-embedding block's RMSNorm of the updated rows rides on the down projection
+        gd.norm_g = w.ple_norm;
+        gd.norm_eps = m->eps;
+        gd.norm_out = a16;
+    }
     PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm(gd, c.s));
 
     if (I.ple_dim) {
         const int E = I.ple_dim;
         __half *p16 = c.sl<__half>(c.L.p16);
-        PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_rmsnorm_f16(x, w.ple_norm, m->eps, M, d, a16, c.s));
         GemmArgs gp = c.gemm();
         gp.A = a16;
         gp.lda = d;

@@ -478,6 +478,63 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(GemmArgs a, int S, int Mt) 
     gemm_epilogue<1, TNR>(a, acc, rt * 16, cb * TNR * 16, lane);
 }
 
+// x[row] += the S split partials of its tile (summed in split order, as
+// k_gemm_reduce does), then the RMSNorm of the updated row with gain g into
+// the fp16 fragment-tiled `out` (as the standalone norm kernel computes it:
+// lane l owns the eight-float chunks l, l + 64, ...).  One wave per row.
+constexpr int RAN_MAX_CHUNKS = 8;  // d <= 8 * 8 * 64
+__global__ __launch_bounds__(256) void k_reduce_add_norm(GemmArgs a, int S, int Mt) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= a.M) return;
+    const int d = a.W.N, Nt = d >> 4, nch = d >> 3;
+    const int rt = row >> 4, rr = row & 15;
+    const int sub = (rr & 3) * 64 + (rr >> 2) * 16;  // r * 64 + lane group * 16 in the partial tile
+    float *xr = a.out_f32 + (size_t)row * d;
+    float4 v[RAN_MAX_CHUNKS][2];
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < RAN_MAX_CHUNKS; ++c) {
+        const int ch = lane + 64 * c;
+        if (ch < nch) {
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int z = 0; z < S; ++z) {
+                const float *src = a.part + (((size_t)z * Mt + rt) * Nt + (ch >> 1)) * 256 + sub + (ch & 1) * 8;
+                const float4 p0 = *reinterpret_cast<const float4 *>(src);
+                const float4 p1 = *reinterpret_cast<const float4 *>(src + 4);
+                acc[0] += p0.x; acc[1] += p0.y; acc[2] += p0.z; acc[3] += p0.w;
+                acc[4] += p1.x; acc[5] += p1.y; acc[6] += p1.z; acc[7] += p1.w;
+            }
+            float4 x0 = *reinterpret_cast<const float4 *>(xr + ch * 8);
+            float4 x1 = *reinterpret_cast<const float4 *>(xr + ch * 8 + 4);
+            x0.x += acc[0]; x0.y += acc[1]; x0.z += acc[2]; x0.w += acc[3];
+            x1.x += acc[4]; x1.y += acc[5]; x1.z += acc[6]; x1.w += acc[7];
+            *reinterpret_cast<float4 *>(xr + ch * 8) = x0;
+            *reinterpret_cast<float4 *>(xr + ch * 8 + 4) = x1;
+            v[c][0] = x0;
+            v[c][1] = x1;
+            ss += x0.x * x0.x + x0.y * x0.y + x0.z * x0.z + x0.w * x0.w;
+            ss += x1.x * x1.x + x1.y * x1.y + x1.z * x1.z + x1.w * x1.w;
+        }
+    }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)d + a.norm_eps);
+#pragma unroll
+    for (int c = 0; c < RAN_MAX_CHUNKS; ++c) {
+        const int ch = lane + 64 * c;
+        if (ch < nch) {
+            const float4 g0 = *reinterpret_cast<const float4 *>(a.norm_g + ch * 8);
+            const float4 g1 = *reinterpret_cast<const float4 *>(a.norm_g + ch * 8 + 4);
+            const float y[8] = {v[c][0].x * r * g0.x, v[c][0].y * r * g0.y, v[c][0].z * r * g0.z, v[c][0].w * r * g0.w,
+                                v[c][1].x * r * g1.x, v[c][1].y * r * g1.y, v[c][1].z * r * g1.z, v[c][1].w * r * g1.w};
+            h8 yh;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) yh[e] = (_Float16)y[e];
+            *reinterpret_cast<h8 *>(a.norm_out + tiled_index(row, ch * 8, d)) = yh;
+        }
+    }
+}
+
 // ------------------------------------------------------- exact-weight kernel
 
 template <int TM_, int TN_, int NWN_, int KS_, int DEPTH_>
@@ -635,8 +692,12 @@ int launch_p(const GemmArgs &a, int S, hipStream_t s) {
     hipLaunchKernelGGL((k_q4gemm_p<C>), dim3(a.W.N / C::BN, mb, S), dim3(C::NT), 0, s, a);
     if (hipGetLastError() != hipSuccess) return PPX_E_HIP;
     if (S > 1) {
-        const int waves = Mt * (a.W.N / 32);
-        hipLaunchKernelGGL((k_gemm_reduce<2>), dim3((waves + 3) / 4), dim3(256), 0, s, a, S, Mt);
+        if (a.norm_out) {
+            hipLaunchKernelGGL(k_reduce_add_norm, dim3((a.M + 3) / 4), dim3(256), 0, s, a, S, Mt);
+        } else {
+            const int waves = Mt * (a.W.N / 32);
+            hipLaunchKernelGGL((k_gemm_reduce<2>), dim3((waves + 3) / 4), dim3(256), 0, s, a, S, Mt);
+        }
         if (hipGetLastError() != hipSuccess) return PPX_E_HIP;
     }
     return PPX_OK;
@@ -713,10 +774,14 @@ size_t gemm_part_floats(int M, int N, int K) {
 int launch_gemm(const GemmArgs &a, hipStream_t s) {
     if (a.M <= 0) return PPX_OK;
     if (a.W.N % 128 || a.W.K % 256 || !a.A) return PPX_E_UNSUPPORTED;
+    if (a.norm_out && (a.epi != EPI_ADD || !a.norm_g || a.W.N > RAN_MAX_CHUNKS * 8 * 64)) return PPX_E_UNSUPPORTED;
     const Plan p = plan_for(a.M, a.W.N, a.W.K);
     int st = launch_plan(a, p.cfg, p.S, s);
+    bool normed = st == PPX_OK && p.S > 1 && a.norm_out;  // the split's reduction normalised too
     if (st == PPX_E_UNSUPPORTED && p.S > 1) st = launch_plan(a, p.cfg, 1, s);  // no split workspace given
     if (st == PPX_E_UNSUPPORTED) st = launch_plan(a, 5, 1, s);                 // N % 128, K % 256: always fits
+    if (st == PPX_OK && a.norm_out && !normed)
+        st = launch_rmsnorm_f16(a.out_f32, a.norm_g, a.norm_eps, a.M, a.W.N, a.norm_out, s);
     return st;
 }
 

@@ -136,6 +136,12 @@ struct GemmArgs {
     // second kernel that applies the epilogue.  Null: no split.
     float *part = nullptr;
     size_t part_floats = 0;
+    // EPI_ADD only: after the residual update, RMS-normalise the updated rows with
+    // gain norm_g into norm_out (fp16, fragment-tiled) -- fused into the split-K
+    // reduction when the K split is used, a separate pass otherwise.  Null: none.
+    const float *norm_g = nullptr;
+    float norm_eps = 0.f;
+    __half *norm_out = nullptr;
 };
 int launch_gemm(const GemmArgs &a, hipStream_t s);
 // fp32 words of split-K partials launch_gemm would use for an M x N x K GEMM
