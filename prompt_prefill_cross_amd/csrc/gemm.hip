@@ -480,13 +480,14 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(GemmArgs a, int S, int Mt) 
 
 // x[row] += the S split partials of its tile (summed in split order, as
 // k_gemm_reduce does), then the RMSNorm of the updated row with gain g into
-// the fp16 fragment-tiled `out` (as the standalone norm kernel computes it:
-// lane l owns the eight-float chunks l, l + 64, ...).  One wave per row.
-constexpr int RAN_MAX_CHUNKS = 8;  // d <= 8 * 8 * 64
+// the fp16 fragment-tiled norm_out.  One workgroup per row; thread t owns the
+// eight-float chunks t, t + 256, ...; every split's loads issue together.
+constexpr int RAN_MAX_CHUNKS = 2;  // d <= 2 * 8 * 256
+constexpr int RAN_MAX_SPLIT = 8;
 __global__ __launch_bounds__(256) void k_reduce_add_norm(GemmArgs a, int S, int Mt) {
-    const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= a.M) return;
+    __shared__ float red[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = blockIdx.x;
     const int d = a.W.N, Nt = d >> 4, nch = d >> 3;
     const int rt = row >> 4, rr = row & 15;
     const int sub = (rr & 3) * 64 + (rr >> 2) * 16;  // r * 64 + lane group * 16 in the partial tile
@@ -495,20 +496,29 @@ __global__ __launch_bounds__(256) void k_reduce_add_norm(GemmArgs a, int S, int 
     float ss = 0.f;
 #pragma unroll
     for (int c = 0; c < RAN_MAX_CHUNKS; ++c) {
-        const int ch = lane + 64 * c;
+        const int ch = tid + 256 * c;
         if (ch < nch) {
-            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            for (int z = 0; z < S; ++z) {
-                const float *src = a.part + (((size_t)z * Mt + rt) * Nt + (ch >> 1)) * 256 + sub + (ch & 1) * 8;
-                const float4 p0 = *reinterpret_cast<const float4 *>(src);
-                const float4 p1 = *reinterpret_cast<const float4 *>(src + 4);
-                acc[0] += p0.x; acc[1] += p0.y; acc[2] += p0.z; acc[3] += p0.w;
-                acc[4] += p1.x; acc[5] += p1.y; acc[6] += p1.z; acc[7] += p1.w;
+            float4 p[RAN_MAX_SPLIT][2];
+#pragma unroll
+            for (int z = 0; z < RAN_MAX_SPLIT; ++z) {
+                if (z < S) {
+                    const float *src = a.part + (((size_t)z * Mt + rt) * Nt + (ch >> 1)) * 256 + sub + (ch & 1) * 8;
+                    p[z][0] = *reinterpret_cast<const float4 *>(src);
+                    p[z][1] = *reinterpret_cast<const float4 *>(src + 4);
+                }
             }
             float4 x0 = *reinterpret_cast<const float4 *>(xr + ch * 8);
             float4 x1 = *reinterpret_cast<const float4 *>(xr + ch * 8 + 4);
-            x0.x += acc[0]; x0.y += acc[1]; x0.z += acc[2]; x0.w += acc[3];
-            x1.x += acc[4]; x1.y += acc[5]; x1.z += acc[6]; x1.w += acc[7];
+            float4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int z = 0; z < RAN_MAX_SPLIT; ++z) {
+                if (z < S) {
+                    s0.x += p[z][0].x; s0.y += p[z][0].y; s0.z += p[z][0].z; s0.w += p[z][0].w;
+                    s1.x += p[z][1].x; s1.y += p[z][1].y; s1.z += p[z][1].z; s1.w += p[z][1].w;
+                }
+            }
+            x0.x += s0.x; x0.y += s0.y; x0.z += s0.z; x0.w += s0.w;
+            x1.x += s1.x; x1.y += s1.y; x1.z += s1.z; x1.w += s1.w;
             *reinterpret_cast<float4 *>(xr + ch * 8) = x0;
             *reinterpret_cast<float4 *>(xr + ch * 8 + 4) = x1;
             v[c][0] = x0;
@@ -518,10 +528,13 @@ __global__ __launch_bounds__(256) void k_reduce_add_norm(GemmArgs a, int S, int 
         }
     }
     ss = wave_sum(ss);
+    if (lane == 0) red[wave] = ss;
+    __syncthreads();
+    ss = red[0] + red[1] + red[2] + red[3];
     const float r = 1.0f / sqrtf(ss / (float)d + a.norm_eps);
 #pragma unroll
     for (int c = 0; c < RAN_MAX_CHUNKS; ++c) {
-        const int ch = lane + 64 * c;
+        const int ch = tid + 256 * c;
         if (ch < nch) {
             const float4 g0 = *reinterpret_cast<const float4 *>(a.norm_g + ch * 8);
             const float4 g1 = *reinterpret_cast<const float4 *>(a.norm_g + ch * 8 + 4);
@@ -692,8 +705,8 @@ int launch_p(const GemmArgs &a, int S, hipStream_t s) {
     hipLaunchKernelGGL((k_q4gemm_p<C>), dim3(a.W.N / C::BN, mb, S), dim3(C::NT), 0, s, a);
     if (hipGetLastError() != hipSuccess) return PPX_E_HIP;
     if (S > 1) {
-        if (a.norm_out) {
-            hipLaunchKernelGGL(k_reduce_add_norm, dim3((a.M + 3) / 4), dim3(256), 0, s, a, S, Mt);
+        if (a.norm_out && S <= RAN_MAX_SPLIT) {
+            hipLaunchKernelGGL(k_reduce_add_norm, dim3(a.M), dim3(256), 0, s, a, S, Mt);
         } else {
             const int waves = Mt * (a.W.N / 32);
             hipLaunchKernelGGL((k_gemm_reduce<2>), dim3((waves + 3) / 4), dim3(256), 0, s, a, S, Mt);
@@ -774,10 +787,10 @@ size_t gemm_part_floats(int M, int N, int K) {
 int launch_gemm(const GemmArgs &a, hipStream_t s) {
     if (a.M <= 0) return PPX_OK;
     if (a.W.N % 128 || a.W.K % 256 || !a.A) return PPX_E_UNSUPPORTED;
-    if (a.norm_out && (a.epi != EPI_ADD || !a.norm_g || a.W.N > RAN_MAX_CHUNKS * 8 * 64)) return PPX_E_UNSUPPORTED;
+    if (a.norm_out && (a.epi != EPI_ADD || !a.norm_g || a.W.N > RAN_MAX_CHUNKS * 8 * 256)) return PPX_E_UNSUPPORTED;
     const Plan p = plan_for(a.M, a.W.N, a.W.K);
     int st = launch_plan(a, p.cfg, p.S, s);
-    bool normed = st == PPX_OK && p.S > 1 && a.norm_out;  // the split's reduction normalised too
+    bool normed = st == PPX_OK && p.S > 1 && p.S <= RAN_MAX_SPLIT && a.norm_out;  // the split's reduction normalised too
     if (st == PPX_E_UNSUPPORTED && p.S > 1) st = launch_plan(a, p.cfg, 1, s);  // no split workspace given
     if (st == PPX_E_UNSUPPORTED) st = launch_plan(a, 5, 1, s);                 // N % 128, K % 256: always fits
     if (st == PPX_OK && a.norm_out && !normed)
