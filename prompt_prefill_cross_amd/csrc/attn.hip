@@ -49,12 +49,12 @@ __device__ __forceinline__ void attn_wait_vm() {
     asm volatile("" ::: "memory");
 }
 
-// Four compute waves of CPW groups of 16 query columns and NP producer waves;
+// NC compute waves of CPW groups of 16 query columns and NP producer waves;
 // a ring of DEPTH stages of KT keys each: the K fragments [d step][16-key
 // block][lane] and the V^T fragments [16-dim subtile][lane] of the stage.
-template <int HD_, int CPW_, int NP_, int DEPTH_>
+template <int HD_, int CPW_, int NC_, int NP_, int DEPTH_>
 struct ACfg {
-    static constexpr int HD = HD_, CPW = CPW_, NP = NP_, DEPTH = DEPTH_;
+    static constexpr int HD = HD_, CPW = CPW_, NC = NC_, NP = NP_, DEPTH = DEPTH_;
     static constexpr int KB = HD / 32;           // 32-wide d steps of S
     static constexpr int DT = HD / 16;           // 16-row d subtiles of O^T
     static constexpr int K_UNITS = KB * 2 * 64;  // 16-byte units
@@ -62,8 +62,8 @@ struct ACfg {
     static constexpr int STAGE_UNITS = K_UNITS + V_UNITS;
     static constexpr int DMA_STAGE = KB * 2 + DT;
     static constexpr int PER = (DMA_STAGE + NP - 1) / NP;
-    static constexpr int NT = 64 * (4 + NP);
-    static constexpr int CB = 64 * CPW;          // query columns per workgroup
+    static constexpr int NT = 64 * (NC + NP);
+    static constexpr int CB = 16 * CPW * NC;     // query columns per workgroup
     static_assert(DEPTH >= 2 && (DEPTH - 2) * PER <= 63, "vmcnt range");
     static_assert(DEPTH * STAGE_UNITS * 16 <= 160 * 1024, "LDS");
 };
@@ -85,11 +85,11 @@ __global__ __launch_bounds__(C::NT) void k_attn_prefill(AttnArgs a) {
     const int kend = min(kbeg + a.kc, pend + 1);
     const int nst = (kend - kbeg + KT - 1) / KT;
 
-    if (wave >= 4) {
-        // ---- producers: wave 4 + p issues DMAs p, p + NP, ... of every stage.
+    if (wave >= C::NC) {
+        // ---- producers: wave NC + p issues DMAs p, p + NP, ... of every stage.
         // K rows past the last written position repeat it (their scores are
         // masked); V^T reads stay inside the row (vld is a multiple of 64).
-        const int pw = C::NP == 1 ? 0 : wave - 4;
+        const int pw = C::NP == 1 ? 0 : wave - C::NC;
         const int plast = a.pos0 + a.M - 1;
         auto entry = [&](int t) { return min(t * C::NP + pw, C::DMA_STAGE - 1); };
         int koff[C::PER];  // K: key within the stage; V^T: element offset within the row block
@@ -488,12 +488,13 @@ int ok() { return hipGetLastError() == hipSuccess ? PPX_OK : PPX_E_HIP; }
 
 }  // namespace
 
-// Two groups of 16 query columns per compute wave: 128 columns per workgroup.
-constexpr int ATTN_CPW = 2;
+// Eight compute waves of one group of 16 query columns: 128 columns per
+// workgroup, two compute waves per SIMD.
+constexpr int ATTN_CPW = 1, ATTN_NC = 8, ATTN_CB = 16 * ATTN_CPW * ATTN_NC;
 
 AttnSplit attn_split(int M, int H, int KVH, int pos0) {
     const int G = H / KVH;
-    const int colblocks = (M * G + 64 * ATTN_CPW - 1) / (64 * ATTN_CPW);
+    const int colblocks = (M * G + ATTN_CB - 1) / ATTN_CB;
     const int P = pos0 + M;
     int want = (256 + colblocks * KVH - 1) / (colblocks * KVH);
     want = std::max(1, std::min(want, ATTN_MAX_CHUNKS));
@@ -519,11 +520,11 @@ int launch_attn_prefill(const AttnArgs &a0, hipStream_t s) {
     a.kc = sp.kc;
     a.nkc = sp.nkc;
     if (a.nkc > 1 && !a.part) return PPX_E_INVAL;
-    dim3 grid((a.M * G + 64 * ATTN_CPW - 1) / (64 * ATTN_CPW), a.nkc, a.KVH);
+    dim3 grid((a.M * G + ATTN_CB - 1) / ATTN_CB, a.nkc, a.KVH);
     switch (a.hd) {
 #define PPX_ATTN(hd_, np_, depth_)                                                                   \
     case hd_: {                                                                                      \
-        using C = ACfg<hd_, ATTN_CPW, np_, depth_>;                                                  \
+        using C = ACfg<hd_, ATTN_CPW, ATTN_NC, np_, depth_>;                                         \
         hipLaunchKernelGGL((k_attn_prefill<C>), grid, dim3(C::NT), 0, s, a);                         \
         break;                                                                                       \
     }
