@@ -733,7 +733,8 @@ int launch_cfg(const GemmArgs &a, hipStream_t s) {
     X(3, 4, 2, 4, 2, 4, 4)  \
     X(4, 2, 2, 4, 2, 4, 4)  \
     X(5, 2, 2, 4, 2, 4, 1)  \
-    X(6, 1, 2, 4, 2, 4, 4)
+    X(6, 1, 2, 4, 2, 4, 4)  \
+    X(7, 1, 1, 1, 4, 4, 1)
 
 int launch_plan(const GemmArgs &a, int cfg, int S, hipStream_t s) {
     switch (cfg) {
@@ -764,13 +765,14 @@ struct Plan {
 // Measured on the E2B-like shapes at M = 512 (one MI355X): wide outputs
 // (gate|up) take the tallest wave tiles; the long-K down projection splits K
 // four ways over workgroups; Q and O use 32-row tiles with four producer
-// waves, narrow outputs 16-row tiles, and K = 256 the single-producer 32-row
-// tiles.
+// waves; narrow outputs (N <= 512) single 16 x 16 tiles with K split four
+// ways inside the workgroup, so that 512 short chains run instead of 64 long
+// ones; K = 256 the single-producer 32-row tiles.
 Plan plan_for(int M, int N, int K) {
     (void)M;
     if (N >= 8192) return {N % 192 == 0 ? 0 : 1, 1};
     if (K >= 4096) return {N % 192 == 0 ? 2 : 3, 4};
-    if (N <= 512) return {6, 1};
+    if (N <= 512) return {7, 1};
     if (K <= 256) return {5, 1};
     return {4, 1};
 }
