@@ -719,6 +719,7 @@ int launch_p(const GemmArgs &a, int S, hipStream_t s) {
 template <class C>
 int launch_cfg(const GemmArgs &a, hipStream_t s) {
     if (a.W.N % C::BN || (a.W.K >> 6) % (C::PB * C::KS)) return PPX_E_UNSUPPORTED;
+    if (a.epi == EPI_QKV && C::TN % 2) return PPX_E_UNSUPPORTED;  // RoPE pairs are adjacent groups of one wave
     dim3 grid(a.W.N / C::BN, (a.M + C::BM - 1) / C::BM);
     hipLaunchKernelGGL((k_q4gemm<C>), grid, dim3(C::NT), 0, s, a);
     return hipGetLastError() == hipSuccess ? PPX_OK : PPX_E_HIP;
@@ -767,13 +768,13 @@ struct Plan {
 // four ways over workgroups; Q and O use 32-row tiles with four producer
 // waves; narrow outputs (N <= 512) single 16 x 16 tiles with K split four
 // ways inside the workgroup, so that 512 short chains run instead of 64 long
-// ones; K = 256 the single-producer 32-row tiles.
+// ones; K = 256 the 32-row tiles of Q and O.
 Plan plan_for(int M, int N, int K) {
     (void)M;
     if (N >= 8192) return {N % 192 == 0 ? 0 : 1, 1};
     if (K >= 4096) return {N % 192 == 0 ? 2 : 3, 4};
     if (N <= 512) return {7, 1};
-    if (K <= 256) return {5, 1};
+    if (K <= 256) return {4, 1};
     return {4, 1};
 }
 
