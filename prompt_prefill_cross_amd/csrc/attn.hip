@@ -491,6 +491,7 @@ int ok() { return hipGetLastError() == hipSuccess ? PPX_OK : PPX_E_HIP; }
 // Eight compute waves of one group of 16 query columns: 128 columns per
 // workgroup, two compute waves per SIMD.
 constexpr int ATTN_CPW = 1, ATTN_NC = 8, ATTN_CB = 16 * ATTN_CPW * ATTN_NC;
+constexpr int ATTN_MIN_KC = 128;  // keys per chunk at least (early ubatches get more workgroups)
 
 AttnSplit attn_split(int M, int H, int KVH, int pos0) {
     const int G = H / KVH;
@@ -499,7 +500,7 @@ AttnSplit attn_split(int M, int H, int KVH, int pos0) {
     int want = (256 + colblocks * KVH - 1) / (colblocks * KVH);
     want = std::max(1, std::min(want, ATTN_MAX_CHUNKS));
     int kc = (P + want - 1) / want;
-    kc = std::max(256, (kc + 63) / 64 * 64);
+    kc = std::max(ATTN_MIN_KC, (kc + 63) / 64 * 64);
     AttnSplit sp;
     sp.kc = kc;
     sp.nkc = (P + kc - 1) / kc;
@@ -507,7 +508,7 @@ AttnSplit attn_split(int M, int H, int KVH, int pos0) {
 }
 
 size_t attn_prefill_scratch_floats(int M, int H, int hd, int n_ctx) {
-    const int nkc = std::min(ATTN_MAX_CHUNKS, (n_ctx + 255) / 256);
+    const int nkc = std::min(ATTN_MAX_CHUNKS, (n_ctx + ATTN_MIN_KC - 1) / ATTN_MIN_KC);
     return (size_t)nkc * M * H * (hd / 2 + 2);  // fp16 chunk outputs, then fp32 (max, sum) pairs
 }
 
