@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--prune", default="auto", choices=["auto", "on", "off"])
     ap.add_argument("--extra-n", default="512,8192", help="other prompt lengths to report (comma list, '' = none)")
     ap.add_argument("--decode", type=int, default=32, help="tokens decoded after the main prompt (0 = none)")
+    ap.add_argument("--no-reuse", dest="reuse", action="store_false",
+                    help="skip the token-verified prefix-reuse timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="prompt tokens of the oracle sample (0 = all)")
     ap.add_argument("--pmc-pass", action="store_true", help="one prefill + one calibration copy, then exit")
@@ -178,6 +180,42 @@ def decode_pass(mm, kv, toks, ub, n_dec, warmup=2):
             "frac_hbm": byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
 
+def prefix_reuse_pass(mm, kv, toks, ub, keep, reps=3):
+    """Token-verified prefix reuse: a snapshot of the prompt, then a prompt
+    that shares its first `keep` tokens; times loading that prefix (file read
+    and upload) plus the prefill of the rest, against the full prefill."""
+    import tempfile
+    import torch
+    V = mm.info["n_vocab"]
+    n = len(toks)
+    new = np.concatenate([toks[:keep], (toks[keep:] + 1) % V]).astype(np.int32)
+    logits = torch.empty(V, dtype=torch.float32, device="cuda")
+    kv.clear()
+    mm.prefill(toks, kv, n_ubatch=ub, logits=logits)
+    with tempfile.TemporaryDirectory() as d:
+        snap = os.path.join(d, "prefix.kvc")
+        kv.save_tokens(snap, toks)
+        loads, rests = [], []
+        for _ in range(reps):
+            kv.clear()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            L = kv.load_prefix(snap, new)
+            t1 = time.perf_counter()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            mm.prefill(new[L:], kv, n_ubatch=ub, logits=logits)
+            e1.record()
+            e1.synchronize()
+            loads.append((t1 - t0) * 1e3)
+            rests.append(e0.elapsed_time(e1))
+        size = os.path.getsize(snap)
+    return {"prompt": n, "reused": int(L), "snapshot_bytes": size, "load_ms": float(np.median(loads)),
+            "prefill_rest_ms": float(np.median(rests)),
+            "total_ms": float(np.median(loads) + np.median(rests))}
+
+
 def pmc_pass(mm, kv, toks, ub, prune):
     import torch
     kv.clear()
@@ -239,6 +277,10 @@ def main():
         print(f"# n={n}: {np.median(times):.3f} ms median, {n / np.median(times) * 1e3:.0f} tok/s; "
               f"phases ms {ph['ms']}", file=sys.stderr, flush=True)
 
+    reuse = prefix_reuse_pass(mm, kv, synth.prompt(cfg, a.n), ub, a.n * 3 // 4) if a.reuse else None
+    if reuse:
+        print(f"# prefix reuse: {reuse['reused']} of {reuse['prompt']} cached; load {reuse['load_ms']:.1f} ms + "
+              f"prefill {reuse['prefill_rest_ms']:.2f} ms", file=sys.stderr, flush=True)
     dec = None
     if a.decode:
         dec = decode_pass(mm, kv, synth.prompt(cfg, a.n + a.decode + 2), ub, a.decode)
@@ -288,6 +330,7 @@ def main():
         "other_lengths": {str(n): {"ms_median": float(np.median(t)), "tokens_per_s": n / float(np.median(t)) * 1e3}
                           for n, (t, _) in results.items()},
         "decode": dec,
+        "prefix_reuse": reuse,
         "ms_median": float(np.median(times)),
         "ms_std": float(np.std(times)),
     }

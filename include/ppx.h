@@ -137,14 +137,35 @@ int ppx_kv_clear(ppx_kv *kv);
  * [n_layers][n_pos][kv_dim] fp16, then V likewise; little-endian.
  * kv_save writes the first n_pos (<= ppx_kv_n_pos) positions and
  * synchronises hip_stream.  kv_load checks the file before touching the
- * cache (magic, layer count, kv dim, exact size, n_pos <= file positions,
+ * cache (magic, layer count, kv dim, exact size -- the KVCP body, or the body
+ * and a token section as written by ppx_kv_save_tokens --, n_pos <= file positions,
  * n_pos <= n_ctx); on any failure it returns PPX_E_FORMAT / PPX_E_MISMATCH /
  * PPX_E_CTX / PPX_E_IO and leaves the cache empty (n_pos = 0), so the caller
  * falls back to a full prefill.  On success n_pos = the loaded count; it
  * synchronises hip_stream.  The file stores no token ids: that the new
- * prompt starts with the cached prefix is the caller's duty. */
+ * prompt starts with the cached prefix is the caller's duty (see
+ * ppx_kv_save_tokens / ppx_kv_load_prefix for a checked variant). */
 int ppx_kv_save(const ppx_kv *kv, const char *path, int n_pos, void *hip_stream);
 int ppx_kv_load(ppx_kv *kv, const char *path, int n_pos, void *hip_stream);
+
+/* Token-verified prefix reuse (an extension outside the KVCP layout of the
+ * PicoLM page, whose invalidation rules leave prefix checking to the
+ * caller).  ppx_kv_save_tokens writes the same KVCP body as ppx_kv_save and
+ * then a token section: "KVTK", int32 count (= n_pos), and the n_pos int32
+ * token ids (host array) of the cached positions.  ppx_kv_load and
+ * ppx_kvfile_validate accept such a file (the body is unchanged).
+ * ppx_kv_load_prefix reads a file with a token section, takes the longest
+ * common prefix L of its ids and tokens_host[0..n_tokens), capped at
+ * n_tokens - 1 (so at least one token is left to prefill, which yields the
+ * logits) and at n_ctx, loads the first L positions as ppx_kv_load(kv, path,
+ * L) does, and stores L in *n_reused; the caller then prefills
+ * tokens_host[L..n_tokens).  L = 0 loads nothing and returns PPX_OK.  Errors
+ * leave the cache empty (n_pos = 0) and *n_reused = 0: PPX_E_FORMAT (no
+ * token section, or the checks of ppx_kv_load), PPX_E_MISMATCH, PPX_E_IO,
+ * PPX_E_INVAL (null arguments). */
+int ppx_kv_save_tokens(const ppx_kv *kv, const char *path, int n_pos, const int32_t *tokens_host, void *hip_stream);
+int ppx_kv_load_prefix(ppx_kv *kv, const char *path, const int32_t *tokens_host, int n_tokens, int *n_reused,
+                       void *hip_stream);
 /* Host-only check of a KVCP file against a model shape, the same check
  * ppx_kv_load makes before touching the cache: PPX_OK if the file is a
  * whole snapshot with n_layers layers of width kv_dim holding at least n_pos

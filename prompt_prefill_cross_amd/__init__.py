@@ -70,6 +70,8 @@ SIGNATURES = [
     ("ppx_kv_clear", c_int, [c_void_p]),
     ("ppx_kv_save", c_int, [c_void_p, c_char_p, c_int, c_void_p]),
     ("ppx_kv_load", c_int, [c_void_p, c_char_p, c_int, c_void_p]),
+    ("ppx_kv_save_tokens", c_int, [c_void_p, c_char_p, c_int, c_void_p, c_void_p]),
+    ("ppx_kv_load_prefix", c_int, [c_void_p, c_char_p, c_void_p, c_int, c_void_p, c_void_p]),
     ("ppx_kvfile_validate", c_int, [c_char_p, c_int, c_int, c_int, c_int, POINTER(c_int)]),
     ("ppx_workspace_bytes", c_size_t, [c_void_p, c_int, c_int]),
     ("ppx_decode", c_int, [c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_void_p, c_void_p]),
@@ -381,6 +383,25 @@ class KVCache:
 
     def load(self, path, n_pos, stream=None):
         _check(lib().ppx_kv_load(self._h, os.fsencode(path), n_pos, _stream(stream)), "ppx_kv_load")
+
+    def save_tokens(self, path, tokens, n_pos=None, stream=None):
+        """Snapshot with the token ids of the cached positions (tokens[:n_pos])."""
+        import numpy as np
+        n = self.n_pos if n_pos is None else n_pos
+        ids = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32)[:n])
+        if ids.size != n:
+            raise ValueError("need one token id per saved position")
+        _check(lib().ppx_kv_save_tokens(self._h, os.fsencode(path), n, ids.ctypes.data, _stream(stream)),
+               "ppx_kv_save_tokens")
+
+    def load_prefix(self, path, tokens, stream=None):
+        """Load the longest cached prefix of `tokens` (at most len - 1); returns its length."""
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        out = ctypes.c_int(0)
+        _check(lib().ppx_kv_load_prefix(self._h, os.fsencode(path), ids.ctypes.data, int(ids.size),
+                                        ctypes.byref(out), _stream(stream)), "ppx_kv_load_prefix")
+        return out.value
 
     def kv_tensors(self):
         """(K, V) as torch fp16 views [Ls][n_ctx][kv_dim] (V is a transposed view

@@ -655,7 +655,9 @@ int decode(ppx_model *m, ppx_kv *kv, int32_t token, void *ws, size_t ws_bytes, f
 
 // ------------------------------------------------------------------ KVCP snapshots
 
-int kv_save(const ppx_kv *kv, const char *path, int n_pos, hipStream_t s) {
+// With tokens: the KVCP body is followed by a token section, "KVTK", int32
+// count (= n_pos), then the count int32 token ids of the cached positions.
+int kv_save(const ppx_kv *kv, const char *path, int n_pos, hipStream_t s, const int32_t *tokens = nullptr) {
     if (!kv || !path) return PPX_E_INVAL;
     if (n_pos < 0 || n_pos > kv->n_pos) return PPX_E_CTX;
     const ppx_model_info &I = kv->m->info;
@@ -680,12 +682,21 @@ int kv_save(const ppx_kv *kv, const char *path, int n_pos, hipStream_t s) {
     const int32_t hdr[3] = {n_pos, nl, kvd};
     bool ok = std::fwrite("KVCP", 1, 4, f) == 4 && std::fwrite(hdr, 4, 3, f) == 3 &&
               std::fwrite(buf.data(), 2, buf.size(), f) == buf.size();
+    if (ok && tokens) {
+        const int32_t cnt = n_pos;
+        ok = std::fwrite("KVTK", 1, 4, f) == 4 && std::fwrite(&cnt, 4, 1, f) == 1 &&
+             std::fwrite(tokens, 4, (size_t)n_pos, f) == (size_t)n_pos;
+    }
     ok = (std::fclose(f) == 0) && ok;
     return ok ? PPX_OK : PPX_E_IO;
 }
 
-// Validates a KVCP file; leaves *fpos = file positions when the header was read.
-int kvfile_check(const char *path, int nl, int kvd, int n_pos, int n_ctx, int *fpos) {
+// Validates a KVCP file; leaves *fpos = file positions when the header was read
+// and *has_tokens = whether a token section follows the body.  The file is
+// exactly the KVCP body, or the body and a token section of one id per
+// cached position.
+int kvfile_check(const char *path, int nl, int kvd, int n_pos, int n_ctx, int *fpos, bool *has_tokens = nullptr) {
+    if (has_tokens) *has_tokens = false;
     std::FILE *f = std::fopen(path, "rb");
     if (!f) return PPX_E_IO;
     char mg[4];
@@ -703,7 +714,16 @@ int kvfile_check(const char *path, int nl, int kvd, int n_pos, int n_ctx, int *f
             std::fseek(f, 0, SEEK_END);
             const long sz = std::ftell(f);
             const long want = 16 + 4l * nl * hdr[0] * kvd;
-            if (sz != want) st = PPX_E_FORMAT;
+            bool tok = false;
+            if (sz == want + 8 + 4l * hdr[0]) {
+                char tm[4];
+                int32_t cnt = -1;
+                std::fseek(f, want, SEEK_SET);
+                tok = std::fread(tm, 1, 4, f) == 4 && std::memcmp(tm, "KVTK", 4) == 0 &&
+                      std::fread(&cnt, 4, 1, f) == 1 && cnt == hdr[0];
+            }
+            if (has_tokens) *has_tokens = tok;
+            if (sz != want && !tok) st = PPX_E_FORMAT;
             else if (n_pos < 0 || n_pos > hdr[0]) st = PPX_E_FORMAT;
             else if (n_pos > n_ctx) st = PPX_E_CTX;
         }
@@ -754,6 +774,36 @@ int kv_load(ppx_kv *kv, const char *path, int n_pos, hipStream_t s) {
         std::fprintf(stderr, "KV cache loaded: %d positions from %s\n", n_pos, path);
         std::fprintf(stderr, "Skipping %d cached prompt tokens\n", n_pos);
     }
+    return PPX_OK;
+}
+
+// Token-verified prefix reuse: the longest common prefix of the snapshot's
+// token ids and the new prompt, at most n_tokens - 1 positions (one token is
+// left to prefill, which gives the logits), is loaded into the cache.
+int kv_load_prefix(ppx_kv *kv, const char *path, const int32_t *tokens, int n_tokens, int *n_reused, hipStream_t s) {
+    if (!kv || !path || !n_reused || (n_tokens > 0 && !tokens)) return PPX_E_INVAL;
+    *n_reused = 0;
+    kv->n_pos = 0;
+    const ppx_model_info &I = kv->m->info;
+    const int nl = I.n_layer_kv_from_start, kvd = I.kv_dim;
+    int fpos = 0;
+    bool has_tokens = false;
+    const int st = kvfile_check(path, nl, kvd, 0, kv->n_ctx, &fpos, &has_tokens);
+    if (st) return st;
+    if (!has_tokens) return PPX_E_FORMAT;  // nothing to verify the prefix against
+    std::vector<int32_t> ids((size_t)fpos);
+    std::FILE *f = std::fopen(path, "rb");
+    if (!f) return PPX_E_IO;
+    std::fseek(f, 16 + 4l * nl * fpos * kvd + 8, SEEK_SET);
+    const bool rd = std::fread(ids.data(), 4, (size_t)fpos, f) == (size_t)fpos;
+    std::fclose(f);
+    if (!rd) return PPX_E_IO;
+    const int cap = std::min({fpos, n_tokens - 1, kv->n_ctx});
+    int L = 0;
+    while (L < cap && ids[(size_t)L] == tokens[L]) ++L;
+    if (L == 0) return PPX_OK;
+    PPX_TRY(kv_load(kv, path, L, s));
+    *n_reused = L;
     return PPX_OK;
 }
 
@@ -850,6 +900,16 @@ int ppx_kv_save(const ppx_kv *kv, const char *path, int n_pos, void *hip_stream)
 
 int ppx_kv_load(ppx_kv *kv, const char *path, int n_pos, void *hip_stream) {
     return kv_load(kv, path, n_pos, (hipStream_t)hip_stream);
+}
+
+int ppx_kv_save_tokens(const ppx_kv *kv, const char *path, int n_pos, const int32_t *tokens_host, void *hip_stream) {
+    if (!tokens_host && n_pos > 0) return PPX_E_INVAL;
+    return kv_save(kv, path, n_pos, (hipStream_t)hip_stream, tokens_host ? tokens_host : reinterpret_cast<const int32_t *>(""));
+}
+
+int ppx_kv_load_prefix(ppx_kv *kv, const char *path, const int32_t *tokens_host, int n_tokens, int *n_reused,
+                       void *hip_stream) {
+    return kv_load_prefix(kv, path, tokens_host, n_tokens, n_reused, (hipStream_t)hip_stream);
 }
 
 int ppx_kvfile_validate(const char *path, int n_layers, int kv_dim, int n_pos, int n_ctx, int *file_n_pos) {

@@ -102,3 +102,44 @@ def test_kvcp_size_pin_via_engine_rule(tmp_path):
     p.write_bytes(oracle.kvcp.dump(K, K, 25))
     assert os.path.getsize(p) - 16 == g["payload_bytes"]
     assert ppx.kvfile_validate(str(p), 22, 256, 25, 2048)[0] == 0
+
+
+def test_kvfile_with_token_section_matches_oracle(tmp_path):
+    """A snapshot may end with a token section ("KVTK", int32 count = n_pos,
+    the ids); the engine's check and the oracle's reader accept and reject
+    the same files."""
+    rng = np.random.default_rng(11)
+    K = rng.standard_normal((3, 6, 64)).astype(np.float16)
+    V = rng.standard_normal((3, 6, 64)).astype(np.float16)
+    ids = [5, 9, 9, 2, 7, 1]
+    good = tmp_path / "tok.kvc"
+    good.write_bytes(oracle.kvcp.dump_tokens(K, V, 6, ids))
+    st, ok, fpos = _statuses(str(good), 3, 64, 6, 32)
+    assert st == 0 and ok and fpos == 6
+    assert oracle.kvcp.stored_tokens(good.read_bytes()) == ids
+    body = len(oracle.kvcp.dump(K, V, 6))
+    data = good.read_bytes()
+    cases = {
+        "bad_token_magic": data[:body] + b"KVTX" + data[body + 4:],
+        "count_mismatch": data[:body + 4] + np.int32(5).tobytes() + data[body + 8:],
+        "missing_id": data[:-4],
+        "extra_bytes": data + b"\0\0\0\0",
+    }
+    for name, d in cases.items():
+        p = tmp_path / f"{name}.kvc"
+        p.write_bytes(d)
+        st, ok, _ = _statuses(str(p), 3, 64, 6, 32)
+        assert st == -5 and not ok, name
+
+
+def test_reusable_prefix_rule_brute_force():
+    """oracle.kvcp.reusable_prefix against a direct search: the longest l with
+    equal first l ids, at most len(prompt) - 1 and n_ctx."""
+    rng = np.random.default_rng(3)
+    for _ in range(2000):
+        stored = list(rng.integers(0, 3, rng.integers(0, 7)))
+        prompt = list(rng.integers(0, 3, rng.integers(1, 8)))
+        n_ctx = int(rng.integers(1, 9))
+        cap = min(len(stored), len(prompt) - 1, n_ctx)
+        want = max(l for l in range(cap + 1) if stored[:l] == prompt[:l])
+        assert oracle.kvcp.reusable_prefix(stored, prompt, n_ctx) == want
