@@ -663,20 +663,27 @@ int kv_save(const ppx_kv *kv, const char *path, int n_pos, hipStream_t s, const 
     const ppx_model_info &I = kv->m->info;
     const int nl = I.n_layer_kv_from_start, kvd = I.kv_dim;
     const size_t row = (size_t)n_pos * kvd;
-    std::vector<uint16_t> buf(2 * (size_t)nl * row), vt(row);
+    std::vector<uint16_t> buf(2 * (size_t)nl * row);
     if (hipStreamSynchronize(s) != hipSuccess) return PPX_E_HIP;
-    for (int il = 0; il < nl && row; ++il) {
+    // V is held transposed on the device ([kvd][vld] per layer): back to
+    // position-major rows in a temporary device buffer, then one copy
+    uint16_t *vpos = nullptr;
+    if (row && hipMalloc(&vpos, (size_t)nl * row * 2) != hipSuccess) return PPX_E_NOMEM;
+    int st = PPX_OK;
+    for (int il = 0; il < nl && row && st == PPX_OK; ++il) {
         const size_t src = (size_t)il * kv->n_ctx * kvd;
         if (hipMemcpy(buf.data() + il * row, kv->k + src, row * 2, hipMemcpyDeviceToHost) != hipSuccess)
-            return PPX_E_HIP;
-        // V is held transposed on the device: kvd rows of vld positions
-        if (hipMemcpy2D(vt.data(), (size_t)n_pos * 2, kv->vt + (size_t)il * kv->vld * kvd, (size_t)kv->vld * 2,
-                        (size_t)n_pos * 2, kvd, hipMemcpyDeviceToHost) != hipSuccess)
-            return PPX_E_HIP;
-        uint16_t *vdst = buf.data() + (nl + il) * row;
-        for (int dd = 0; dd < kvd; ++dd)
-            for (int p = 0; p < n_pos; ++p) vdst[(size_t)p * kvd + dd] = vt[(size_t)dd * n_pos + p];
+            st = PPX_E_HIP;
+        else
+            st = launch_transpose_u16(reinterpret_cast<const uint16_t *>(kv->vt) + (size_t)il * kv->vld * kvd, kvd,
+                                      n_pos, (size_t)kv->vld, vpos + (size_t)il * row, (size_t)kvd, s);
     }
+    if (st == PPX_OK && row &&
+        (hipStreamSynchronize(s) != hipSuccess ||
+         hipMemcpy(buf.data() + (size_t)nl * row, vpos, (size_t)nl * row * 2, hipMemcpyDeviceToHost) != hipSuccess))
+        st = PPX_E_HIP;
+    if (vpos) (void)hipFree(vpos);
+    if (st) return st;
     std::FILE *f = std::fopen(path, "wb");
     if (!f) return PPX_E_IO;
     const int32_t hdr[3] = {n_pos, nl, kvd};
@@ -754,21 +761,25 @@ int kv_load(ppx_kv *kv, const char *path, int n_pos, hipStream_t s) {
         }
     std::fclose(f);
     if (st) return st;
-    std::vector<uint16_t> vt((size_t)nl * row);
-    for (int il = 0; il < nl && row; ++il) {
-        const uint16_t *vsrc = buf.data() + (nl + il) * row;
-        uint16_t *vdst = vt.data() + il * row;
-        for (int p = 0; p < n_pos; ++p)
-            for (int dd = 0; dd < kvd; ++dd) vdst[(size_t)dd * n_pos + p] = vsrc[(size_t)p * kvd + dd];
-    }
-    for (int il = 0; il < nl && row; ++il) {
+    // V rows go up position-major into a temporary device buffer and are
+    // transposed there into the cache's [kvd][vld] layout
+    uint16_t *vpos = nullptr;
+    if (row && hipMalloc(&vpos, (size_t)nl * row * 2) != hipSuccess) return PPX_E_NOMEM;
+    if (row && hipMemcpyAsync(vpos, buf.data() + (size_t)nl * row, (size_t)nl * row * 2, hipMemcpyHostToDevice, s) !=
+                   hipSuccess)
+        st = PPX_E_HIP;
+    for (int il = 0; il < nl && row && st == PPX_OK; ++il) {
         const size_t dst = (size_t)il * kv->n_ctx * kvd;
-        if (hipMemcpyAsync(kv->k + dst, buf.data() + il * row, row * 2, hipMemcpyHostToDevice, s) != hipSuccess ||
-            hipMemcpy2DAsync(kv->vt + (size_t)il * kv->vld * kvd, (size_t)kv->vld * 2, vt.data() + il * row,
-                             (size_t)n_pos * 2, (size_t)n_pos * 2, kvd, hipMemcpyHostToDevice, s) != hipSuccess)
-            return PPX_E_HIP;
+        if (hipMemcpyAsync(kv->k + dst, buf.data() + il * row, row * 2, hipMemcpyHostToDevice, s) != hipSuccess)
+            st = PPX_E_HIP;
+        else
+            st = launch_transpose_u16(vpos + (size_t)il * row, n_pos, kvd, (size_t)kvd,
+                                      reinterpret_cast<uint16_t *>(kv->vt) + (size_t)il * kv->vld * kvd,
+                                      (size_t)kv->vld, s);
     }
-    if (hipStreamSynchronize(s) != hipSuccess) return PPX_E_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess && st == PPX_OK) st = PPX_E_HIP;
+    if (vpos) (void)hipFree(vpos);
+    if (st) return st;
     kv->n_pos = n_pos;
     if (log_enabled()) {
         std::fprintf(stderr, "KV cache loaded: %d positions from %s\n", n_pos, path);

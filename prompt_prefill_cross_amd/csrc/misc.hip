@@ -38,35 +38,41 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float *x, const float *g,
 // LO, also lo = fp16(y - fp16(y)) (the split operand of the exact-weight
 // GEMM).  Lane l handles the 8-column chunks l, l+64, ... of its row, kept in
 // registers between the sum of squares and the scaling.
-constexpr int NORM_MAX_CHUNKS = 8;  // d <= 8 * 8 * 64 = 4096
+constexpr int NORM_MAX_CHUNKS = 2;  // d <= 2 * 8 * 256
+// One workgroup per row: thread t owns the eight-float chunks t, t + 256;
+// the gain is loaded before the row's reduction, which it does not need.
 template <bool LO>
 __global__ __launch_bounds__(256) void k_rmsnorm_tiled(const float *x, const float *g, float eps, int M, int d,
                                                        __half *hi, __half *lo) {
-    const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= M) return;
+    __shared__ float red[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = blockIdx.x;
     const float *xr = x + (size_t)row * d;
     const int nch = d >> 3;
-    float4 v[NORM_MAX_CHUNKS][2];
+    float4 v[NORM_MAX_CHUNKS][2], gv[NORM_MAX_CHUNKS][2];
     float ss = 0.f;
 #pragma unroll
     for (int c = 0; c < NORM_MAX_CHUNKS; ++c) {
-        const int ch = lane + 64 * c;
+        const int ch = tid + 256 * c;
         if (ch < nch) {
             v[c][0] = *reinterpret_cast<const float4 *>(xr + ch * 8);
             v[c][1] = *reinterpret_cast<const float4 *>(xr + ch * 8 + 4);
+            gv[c][0] = *reinterpret_cast<const float4 *>(g + ch * 8);
+            gv[c][1] = *reinterpret_cast<const float4 *>(g + ch * 8 + 4);
             ss += v[c][0].x * v[c][0].x + v[c][0].y * v[c][0].y + v[c][0].z * v[c][0].z + v[c][0].w * v[c][0].w;
             ss += v[c][1].x * v[c][1].x + v[c][1].y * v[c][1].y + v[c][1].z * v[c][1].z + v[c][1].w * v[c][1].w;
         }
     }
     ss = wave_sum(ss);
+    if (lane == 0) red[wave] = ss;
+    __syncthreads();
+    ss = red[0] + red[1] + red[2] + red[3];
     const float r = 1.0f / sqrtf(ss / (float)d + eps);
 #pragma unroll
     for (int c = 0; c < NORM_MAX_CHUNKS; ++c) {
-        const int ch = lane + 64 * c;
+        const int ch = tid + 256 * c;
         if (ch < nch) {
-            const float4 g0 = *reinterpret_cast<const float4 *>(g + ch * 8);
-            const float4 g1 = *reinterpret_cast<const float4 *>(g + ch * 8 + 4);
+            const float4 g0 = gv[c][0], g1 = gv[c][1];
             const float y[8] = {v[c][0].x * r * g0.x, v[c][0].y * r * g0.y, v[c][0].z * r * g0.z, v[c][0].w * r * g0.w,
                                 v[c][1].x * r * g1.x, v[c][1].y * r * g1.y, v[c][1].z * r * g1.z, v[c][1].w * r * g1.w};
             h8 yh, yl;
@@ -90,6 +96,24 @@ __global__ void k_tile_f16(const __half *src, int M, int K, __half *dst) {
         const int r = (int)(i / nch), ch = (int)(i % nch);
         *reinterpret_cast<h8 *>(dst + tiled_index(r, ch * 8, K)) =
             *reinterpret_cast<const h8 *>(src + (size_t)r * K + ch * 8);
+    }
+}
+
+// dst[c * ld + r] = src[r * lds + c] for a rows x cols array of 16-bit
+// values, through 32 x 32 LDS tiles (both sides touch memory in rows).
+__global__ __launch_bounds__(256) void k_transpose_u16(const uint16_t *src, int rows, int cols, size_t lds,
+                                                      uint16_t *dst, size_t ld) {
+    __shared__ uint16_t t[32][33];
+    const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+    for (int i = ty; i < 32; i += 8) {
+        const int r = r0 + i, c = c0 + tx;
+        if (r < rows && c < cols) t[i][tx] = src[(size_t)r * lds + c];
+    }
+    __syncthreads();
+    for (int i = ty; i < 32; i += 8) {
+        const int c = c0 + i, r = r0 + tx;
+        if (r < rows && c < cols) dst[(size_t)c * ld + r] = t[tx][i];
     }
 }
 
@@ -339,16 +363,16 @@ int launch_embed(const Q4R &tok, const int32_t *ids, int M, float scale, float *
 
 int launch_rmsnorm_f16(const float *x, const float *g, float eps, int M, int d, __half *out, hipStream_t s) {
     if (M <= 0) return PPX_OK;
-    if (d % 32 || d > NORM_MAX_CHUNKS * 8 * 64) return PPX_E_UNSUPPORTED;
-    hipLaunchKernelGGL((k_rmsnorm_tiled<false>), dim3((M + 3) / 4), dim3(256), 0, s, x, g, eps, M, d, out, nullptr);
+    if (d % 32 || d > NORM_MAX_CHUNKS * 8 * 256) return PPX_E_UNSUPPORTED;
+    hipLaunchKernelGGL((k_rmsnorm_tiled<false>), dim3(M), dim3(256), 0, s, x, g, eps, M, d, out, nullptr);
     return ok();
 }
 
 int launch_rmsnorm_split(const float *x, const float *g, float eps, int M, int d, __half *hi, __half *lo,
                          hipStream_t s) {
     if (M <= 0) return PPX_OK;
-    if (d % 32 || d > NORM_MAX_CHUNKS * 8 * 64) return PPX_E_UNSUPPORTED;
-    hipLaunchKernelGGL((k_rmsnorm_tiled<true>), dim3((M + 3) / 4), dim3(256), 0, s, x, g, eps, M, d, hi, lo);
+    if (d % 32 || d > NORM_MAX_CHUNKS * 8 * 256) return PPX_E_UNSUPPORTED;
+    hipLaunchKernelGGL((k_rmsnorm_tiled<true>), dim3(M), dim3(256), 0, s, x, g, eps, M, d, hi, lo);
     return ok();
 }
 
@@ -364,6 +388,14 @@ int launch_tile_f16(const __half *src, int M, int K, __half *dst, hipStream_t s)
 int launch_rmsnorm_f32(const float *x, const float *g, float eps, int M, int d, float *out, hipStream_t s) {
     if (M <= 0) return PPX_OK;
     hipLaunchKernelGGL((k_rmsnorm<float>), dim3(M), dim3(256), 0, s, x, g, eps, d, out);
+    return ok();
+}
+
+int launch_transpose_u16(const uint16_t *src, int rows, int cols, size_t lds, uint16_t *dst, size_t ld,
+                         hipStream_t s) {
+    if (rows <= 0 || cols <= 0) return PPX_OK;
+    hipLaunchKernelGGL(k_transpose_u16, dim3((cols + 31) / 32, (rows + 31) / 32), dim3(256), 0, s, src, rows, cols,
+                       lds, dst, ld);
     return ok();
 }
 

@@ -224,5 +224,8 @@ int launch_dequant(const Q4R &w, float *out, hipStream_t s);
 int launch_tile_f16(const __half *src, int M, int K, __half *dst, hipStream_t s);
 int launch_copy_f32(const float *src, float *dst, int n, hipStream_t s);
 int launch_fill_u32(uint32_t *p, uint32_t v, size_t n, hipStream_t s);
+// dst[c * ld + r] = src[r * lds + c] (16-bit values, rows x cols).
+int launch_transpose_u16(const uint16_t *src, int rows, int cols, size_t lds, uint16_t *dst, size_t ld,
+                         hipStream_t s);
 
 }  // namespace ppx
