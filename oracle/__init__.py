@@ -23,7 +23,7 @@ Modules:
   predicate -- the prune predicate
 """
 from .model import OracleModel, parse_model, deq_q4_0  # noqa: F401
-from .forward import (KVState, prefill, rms_norm, rope, gelu_tanh, silu,  # noqa: F401
+from .forward import (KVState, prefill, prefill_multi, rms_norm, rope, gelu_tanh, silu,  # noqa: F401
                       attention, embed_rows)
 from .predicate import prune_shared  # noqa: F401
 from . import kvcp  # noqa: F401

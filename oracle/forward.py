@@ -118,8 +118,13 @@ def embed_rows(m: OracleModel, tokens: np.ndarray) -> np.ndarray:
     return m.embd_scale * m.q4("tok_embd", rows=tokens)
 
 
-def _layer(m: OracleModel, kv: KVState, il: int, x: np.ndarray, pos: np.ndarray,
-           toks: np.ndarray, W: dict) -> np.ndarray:
+def _layer(m: OracleModel, kvs: list, il: int, x: np.ndarray, pos: np.ndarray,
+           toks: np.ndarray, seq: np.ndarray, W: dict) -> np.ndarray:
+    """Layer il for rows x of sequences seq (row t belongs to kvs[seq[t]]).
+
+    Every row's K/V goes into its own sequence's cache before any row
+    attends, and a row attends only to its own sequence's cache.
+    """
     H, KVH, hd = m.n_head, m.n_kv_head, m.head_dim
     own = il < m.n_layer_kv_from_start
     src = il if own else m.kv_src[il]
@@ -127,18 +132,24 @@ def _layer(m: OracleModel, kv: KVState, il: int, x: np.ndarray, pos: np.ndarray,
 
     a = rms_norm(x, W["attn_norm"], m.rms_eps)
     q = rope((a @ W["wq"].T).reshape(r, H, hd), pos, m.rope_base)
+    groups = [(int(s), np.nonzero(seq == s)[0]) for s in np.unique(seq)]
     if own:
-        k = rope((a @ W["wk"].T).reshape(r, KVH, hd), pos, m.rope_base)
+        k = rope((a @ W["wk"].T).reshape(r, KVH, hd), pos, m.rope_base).reshape(r, KVH * hd)
         v = a @ W["wv"].T
-        kv.K[il, pos] = k.reshape(r, KVH * hd).astype(np.float16)
-        kv.V[il, pos] = v.astype(np.float16)
-        Kc, Vc = kv.K[il], kv.V[il]
-    else:
-        # a shared layer only reads its source layer's cache
-        Kc, Vc = kv.K[src].view(), kv.V[src].view()
-        Kc.flags.writeable = False
-        Vc.flags.writeable = False
-    o = attention(q, Kc.reshape(-1, KVH, hd), Vc.reshape(-1, KVH, hd), pos)
+        for s, rows in groups:
+            kvs[s].K[il, pos[rows]] = k[rows].astype(np.float16)
+            kvs[s].V[il, pos[rows]] = v[rows].astype(np.float16)
+    o = np.empty((r, H * hd), dtype=np.float64)
+    for s, rows in groups:
+        kv = kvs[s]
+        if own:
+            Kc, Vc = kv.K[il], kv.V[il]
+        else:
+            # a shared layer only reads its source layer's cache
+            Kc, Vc = kv.K[src].view(), kv.V[src].view()
+            Kc.flags.writeable = False
+            Vc.flags.writeable = False
+        o[rows] = attention(q[rows], Kc.reshape(-1, KVH, hd), Vc.reshape(-1, KVH, hd), pos[rows])
     x = x + o @ W["wo"].T
 
     b = rms_norm(x, W["ffn_norm"], m.rms_eps)
@@ -177,6 +188,51 @@ def head(m: OracleModel, x_last: np.ndarray, chunk: int = 16384) -> np.ndarray:
     return out.astype(np.float32)
 
 
+def _check_prompt(m: OracleModel, kv: KVState, tokens: np.ndarray) -> None:
+    n = int(tokens.shape[0])
+    if n < 1:
+        raise ValueError("empty prompt")
+    if tokens.min() < 0 or tokens.max() >= m.n_vocab:
+        raise ValueError("token id out of range")
+    if kv.n_pos + n > kv.n_ctx:
+        raise ValueError("context overflow")
+
+
+def _run(m: OracleModel, kvs: list, prompts: list, prune: bool, n_ubatch: int | None,
+         trace: dict | None) -> np.ndarray:
+    """The forward pass over the rows of all prompts, laid end to end in
+    prompt order; returns the logits of each prompt's last row."""
+    if len({id(kv) for kv in kvs}) != len(kvs):
+        raise ValueError("each sequence needs its own cache")
+    prompts = [np.asarray(t, dtype=np.int64) for t in prompts]
+    for kv, t in zip(kvs, prompts):
+        _check_prompt(m, kv, t)
+    ls, L = m.n_layer_kv_from_start, m.n_layer
+    toks = np.concatenate(prompts)
+    seq = np.concatenate([np.full(len(t), s, dtype=np.int64) for s, t in enumerate(prompts)])
+    pos = np.concatenate([kv.n_pos + np.arange(len(t)) for kv, t in zip(kvs, prompts)])
+    last = np.cumsum([len(t) for t in prompts]) - 1  # each prompt's output row
+    ub = toks.shape[0] if n_ubatch is None else int(n_ubatch)
+    x = embed_rows(m, toks)
+    for il in range(L):
+        if prune and il == ls and 0 < ls < L:
+            x, pos, toks, seq = x[last], pos[last], toks[last], seq[last]
+            last = np.arange(len(prompts))
+        W = _layer_weights(m, il)
+        parts = []
+        for s in range(0, x.shape[0], ub):
+            e = min(x.shape[0], s + ub)
+            parts.append(_layer(m, kvs, il, x[s:e], pos[s:e], toks[s:e], seq[s:e], W))
+        x = np.concatenate(parts, axis=0)
+        del W
+        if trace is not None:
+            trace[il] = x[last[-1]].copy()
+    logits = np.stack([head(m, x[r]) for r in last])
+    for kv, t in zip(kvs, prompts):
+        kv.n_pos += len(t)
+    return logits
+
+
 def prefill(m: OracleModel, kv: KVState, tokens, prune: bool = False,
             n_ubatch: int | None = None, trace: dict | None = None) -> np.ndarray:
     """Run the prompt `tokens` from position kv.n_pos; return last-row logits.
@@ -192,32 +248,24 @@ def prefill(m: OracleModel, kv: KVState, tokens, prune: bool = False,
     ubatch-by-ubatch schedule would give it.  trace, if given, receives the
     last row's hidden state after each layer.
     """
-    tokens = np.asarray(tokens, dtype=np.int64)
-    n = int(tokens.shape[0])
-    if n < 1:
-        raise ValueError("empty prompt")
-    if tokens.min() < 0 or tokens.max() >= m.n_vocab:
-        raise ValueError("token id out of range")
-    p0 = kv.n_pos
-    if p0 + n > kv.n_ctx:
-        raise ValueError("context overflow")
-    ls, L = m.n_layer_kv_from_start, m.n_layer
-    ub = n if n_ubatch is None else int(n_ubatch)
-    pos = p0 + np.arange(n)
-    toks = tokens
-    x = embed_rows(m, toks)
-    for il in range(L):
-        if prune and il == ls and 0 < ls < L:
-            x, pos, toks = x[-1:], pos[-1:], toks[-1:]
-        W = _layer_weights(m, il)
-        parts = []
-        for s in range(0, x.shape[0], ub):
-            e = min(x.shape[0], s + ub)
-            parts.append(_layer(m, kv, il, x[s:e], pos[s:e], toks[s:e], W))
-        x = np.concatenate(parts, axis=0)
-        del W
-        if trace is not None:
-            trace[il] = x[-1].copy()
-    logits = head(m, x[-1])
-    kv.n_pos = p0 + n
-    return logits
+    return _run(m, [kv], [tokens], prune, n_ubatch, trace)[0]
+
+
+def prefill_multi(m: OracleModel, kvs: list, prompts: list, prune: bool = False,
+                  n_ubatch: int | None = None) -> np.ndarray:
+    """Several independent prompts in one pass: prompt s runs from
+    kvs[s].n_pos in its own cache, and its last row's logits are row s of
+    the result ([n_seq][n_vocab], fp32).
+
+    The rows of all prompts are laid end to end and cut into ubatches of
+    n_ubatch rows, so one ubatch can hold the end of one prompt and the start
+    of the next; a row attends only to keys of its own sequence.  prune=True
+    generalises the pages' single-sequence prune to one output row per
+    sequence: before the first KV-shared layer the last row of every prompt
+    is gathered, and those rows alone run the KV-shared layers, each reading
+    its own sequence's source-layer cache.  By definition the result equals
+    running each prompt alone, which is what the pins check.
+    """
+    if len(prompts) < 1 or len(prompts) != len(kvs):
+        raise ValueError("one cache per prompt, at least one prompt")
+    return _run(m, list(kvs), list(prompts), prune, n_ubatch, None)

@@ -6,7 +6,8 @@ tests/golden/ (each with its citation), a scalar brute-force implementation
 pruned == unpruned (llama.cpp Gemma 4 prefill page, section 3: identical
 outputs), KV-shared layers leave the cache untouched (section 1), and
 resuming after N cached positions equals a full prefill (PicoLM page,
-resume section).
+resume section).  Several prompts in one pass are pinned to the same brute
+force run on each prompt alone.
 """
 import json
 import math
@@ -270,6 +271,75 @@ def test_prefill_rejects_bad_input(tiny):
         oracle.prefill(m, kv, [m.n_vocab])
     with pytest.raises(ValueError):
         oracle.prefill(m, kv, toks[:17])
+    assert kv.n_pos == 0
+
+
+# ------------------------------------------------------------------ several sequences
+
+@pytest.mark.parametrize("prune", [False, True])
+def test_multi_sequence_matches_scalar_brute_force(prune):
+    """Two prompts in one pass (rows laid end to end, n_ubatch 3 cuts inside
+    both) against the scalar brute force run on each prompt alone."""
+    buf = synth.build_model(MICRO)
+    m = oracle.parse_model(buf)
+    bm = brute.BruteModel(buf.tobytes())
+    prompts = [synth.prompt(MICRO, 5), synth.prompt(MICRO, 9)[4:8]]
+    kvs = [oracle.KVState(m, 5), oracle.KVState(m, 6)]
+    lg = oracle.prefill_multi(m, kvs, prompts, prune=prune, n_ubatch=3)
+    assert lg.shape == (2, m.n_vocab) and lg.dtype == np.float32
+    for s, t in enumerate(prompts):
+        blg, bK, bV = brute.brute_prefill(bm, [int(v) for v in t], kvs[s].n_ctx)
+        np.testing.assert_allclose(lg[s], np.array(blg, dtype=np.float32), rtol=2e-6, atol=1e-5)
+        n = len(t)
+        np.testing.assert_array_equal(kvs[s].K[:, :n].astype(np.float64), brute.as_arrays(bK, n)[:, :n])
+        np.testing.assert_array_equal(kvs[s].V[:, :n].astype(np.float64), brute.as_arrays(bV, n)[:, :n])
+        assert kvs[s].n_pos == n
+
+
+def test_multi_sequence_equals_separate_prefills(tiny):
+    """Prompts of different lengths, one resuming from cached positions, cut
+    into ubatches that straddle sequences: each sequence's logits and cache
+    equal those of its own prefill (sequences are independent), pruned or
+    not."""
+    m, toks = tiny
+    lens, starts = (13, 1, 30, 7), (0, 5, 0, 20)
+    prompts = [toks[3 * s:3 * s + n] for s, n in enumerate(lens)]
+
+    def fresh():
+        kvs = []
+        for s, p0 in enumerate(starts):
+            kv = oracle.KVState(m, 64)
+            if p0:
+                oracle.prefill(m, kv, toks[40:40 + p0])
+            kvs.append(kv)
+        return kvs
+
+    ref_kvs = fresh()
+    ref = [oracle.prefill(m, kv, p, prune=False) for kv, p in zip(ref_kvs, prompts)]
+    for prune, ub in ((False, None), (True, 8), (True, 64), (False, 5)):
+        kvs = fresh()
+        lg = oracle.prefill_multi(m, kvs, prompts, prune=prune, n_ubatch=ub)
+        for s in range(len(lens)):
+            np.testing.assert_allclose(lg[s], ref[s], rtol=1e-12, atol=1e-12)
+            np.testing.assert_array_equal(kvs[s].K, ref_kvs[s].K)
+            np.testing.assert_array_equal(kvs[s].V, ref_kvs[s].V)
+            assert kvs[s].n_pos == starts[s] + lens[s]
+
+
+def test_multi_sequence_identical_prompts_and_rejections(tiny):
+    m, toks = tiny
+    kvs = [oracle.KVState(m, 32) for _ in range(3)]
+    lg = oracle.prefill_multi(m, kvs, [toks[:11]] * 3, prune=True, n_ubatch=4)
+    assert np.array_equal(lg[0], lg[1]) and np.array_equal(lg[1], lg[2])
+    kv = oracle.KVState(m, 32)
+    with pytest.raises(ValueError):
+        oracle.prefill_multi(m, [kv, kv], [toks[:3], toks[:4]])  # one cache for two sequences
+    with pytest.raises(ValueError):
+        oracle.prefill_multi(m, [kv], [toks[:3], toks[:4]])
+    with pytest.raises(ValueError):
+        oracle.prefill_multi(m, [kv, oracle.KVState(m, 32)], [toks[:3], []])
+    with pytest.raises(ValueError):
+        oracle.prefill_multi(m, [kv, oracle.KVState(m, 2)], [toks[:3], toks[:3]])
     assert kv.n_pos == 0
 
 
