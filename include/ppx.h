@@ -19,7 +19,9 @@
  *  - hip_stream is a hipStream_t passed as void* (NULL = the null stream).
  *    Calls are stream-ordered and asynchronous unless stated; argument
  *    checks happen synchronously, before any work is queued.
- *  - One sequence only (n_seq_max == 1), as the pages require for pruning.
+ *  - ppx_prefill runs one sequence (n_seq_max == 1), the case the pages
+ *    prune; ppx_prefill_multi runs several, each in its own cache, with the
+ *    prune generalised to one output row per sequence.
  */
 #ifndef PPX_H
 #define PPX_H
@@ -83,7 +85,7 @@ typedef struct {
                        through every layer; ON: PPX_E_UNSUPPORTED if the
                        predicate is false                                       */
     int embeddings; /* must be 0 (no embedding extraction in this engine)      */
-    int n_seq_max;  /* must be 1                                               */
+    int n_seq_max;  /* ppx_prefill: must be 1; ppx_prefill_multi: >= n_seq    */
     float *debug_hidden; /* NULL, or device fp32 [n_layer][d_model]: receives
                             the last row's hidden state after each layer       */
     ppx_timing *timing;  /* NULL, or host struct filled with per-phase kernel
@@ -96,6 +98,7 @@ typedef struct {
 } ppx_prefill_params;
 
 #define PPX_MAX_UBATCH 4096
+#define PPX_MAX_SEQ 64
 
 /* ---------------------------------------------------------------- model */
 
@@ -193,6 +196,44 @@ size_t ppx_workspace_bytes(const ppx_model *m, int n_ubatch, int n_ctx);
 int ppx_prefill(ppx_model *m, ppx_kv *kv, const int32_t *tokens_host, int n_tokens,
                 const ppx_prefill_params *p, void *ws_dev, size_t ws_bytes, float *logits_dev,
                 void *hip_stream);
+
+/* One prompt of a multi-sequence prefill: tokens_host[0..n_tokens) run at
+ * positions kv->n_pos .. in kv, a cache no other sequence of the call uses. */
+typedef struct {
+    ppx_kv *kv;
+    const int32_t *tokens_host;
+    int n_tokens;
+} ppx_seq;
+
+/* Device workspace bytes of a ppx_prefill_multi call over n_seq prompts of
+ * n_tokens_total tokens together, in caches of up to n_ctx_max positions;
+ * 0 for arguments out of range. */
+size_t ppx_workspace_bytes_multi(const ppx_model *m, int n_ubatch, int n_seq, long n_tokens_total, int n_ctx_max);
+
+/* Several independent prompts in one pass (1 <= n_seq <= PPX_MAX_SEQ,
+ * n_seq <= p->n_seq_max); row s of logits_dev (fp32 [n_seq][n_vocab])
+ * receives the logits of prompt s's last token, and each sequence's result
+ * is that of ppx_prefill of its prompt alone.  The rows of all prompts are
+ * laid end to end and cut into ubatches of p->n_ubatch rows, so short
+ * prompts share the row-batched GEMMs; each row writes K/V into, and attends
+ * over, its own sequence's cache.  Pruning (the llama.cpp Gemma 4 prefill
+ * page, section 1, excludes several sequences at merge time; this is the
+ * generalisation to one output row per sequence): before the first KV-shared
+ * layer the last row of every prompt is gathered, and those n_seq rows alone
+ * run the KV-shared layers, each reading its own sequence's source-layer
+ * cache, and the head.  p->prune AUTO / ON apply the predicate with the
+ * sequence-count clause taken per sequence.  n_seq == 1 is ppx_prefill.
+ * ws_dev: >= ppx_workspace_bytes_multi bytes, 256-byte aligned.  On success
+ * every kv's n_pos advances by its n_tokens.  Errors are reported before any
+ * work is queued and leave every n_pos unchanged: PPX_E_EMPTY (a prompt of
+ * no tokens), PPX_E_TOKEN, PPX_E_CTX, PPX_E_INVAL (NULL arguments, a cache
+ * used twice or built for another model, n_seq out of range), PPX_E_UNSUPPORTED
+ * (embeddings, debug outputs, prune ON while the predicate is false),
+ * PPX_E_NOMEM; PPX_E_HIP if a launch fails.  The host token arrays are read
+ * during the call; the call may wait for the previous multi-sequence call of
+ * the same model to have copied its tables.  One call in flight per kv. */
+int ppx_prefill_multi(ppx_model *m, const ppx_seq *seqs, int n_seq, const ppx_prefill_params *p, void *ws_dev,
+                      size_t ws_bytes, float *logits_dev, void *hip_stream);
 
 /* One generation step after a prefill: the row of `token` at position n_pos
  * runs through every layer on the single-row (GEMV) path -- KV-owning layers

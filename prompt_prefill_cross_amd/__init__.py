@@ -55,6 +55,10 @@ class PrefillParams(ctypes.Structure):
                 ("debug_hidden", c_void_p), ("timing", POINTER(Timing)), ("debug_rows", c_void_p)]
 
 
+class Seq(ctypes.Structure):
+    _fields_ = [("kv", c_void_p), ("tokens_host", c_void_p), ("n_tokens", c_int)]
+
+
 # (name, restype, argtypes) of every symbol declared in include/ppx.h
 SIGNATURES = [
     ("ppx_model_load", c_int, [c_void_p, c_size_t, c_void_p, POINTER(c_void_p)]),
@@ -74,6 +78,9 @@ SIGNATURES = [
     ("ppx_kv_load_prefix", c_int, [c_void_p, c_char_p, c_void_p, c_int, c_void_p, c_void_p]),
     ("ppx_kvfile_validate", c_int, [c_char_p, c_int, c_int, c_int, c_int, POINTER(c_int)]),
     ("ppx_workspace_bytes", c_size_t, [c_void_p, c_int, c_int]),
+    ("ppx_workspace_bytes_multi", c_size_t, [c_void_p, c_int, c_int, ctypes.c_long, c_int]),
+    ("ppx_prefill_multi", c_int, [c_void_p, POINTER(Seq), c_int, POINTER(PrefillParams), c_void_p, c_size_t,
+                                  c_void_p, c_void_p]),
     ("ppx_decode", c_int, [c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_void_p, c_void_p]),
     ("ppx_prefill", c_int, [c_void_p, c_void_p, c_void_p, c_int, POINTER(PrefillParams), c_void_p, c_size_t,
                             c_void_p, c_void_p]),
@@ -207,6 +214,34 @@ class Model:
         st = lib().ppx_prefill(self._h, kv.handle, c_void_p(toks.ctypes.data), toks.shape[0], ctypes.byref(p),
                                _ptr(ws), ws.numel(), _ptr(logits), _stream(stream))
         _check(st, "ppx_prefill")
+        return logits
+
+    def prefill_multi(self, prompts, kvs, n_ubatch: int = 512, prune: str = "auto", logits=None,
+                      n_seq_max: int | None = None, stream=None, timing=None):
+        """Several prompts in one pass, prompt s from kvs[s].n_pos in its own
+        cache; return fp32 logits [n_seq][n_vocab] of each prompt's last token."""
+        import torch
+        toks = [np.ascontiguousarray(np.asarray(t, dtype=np.int32).reshape(-1)) for t in prompts]
+        k = len(toks)
+        if k != len(kvs):
+            raise ValueError("one cache per prompt")
+        seqs = (Seq * max(k, 1))()
+        for i, (t, kv) in enumerate(zip(toks, kvs)):
+            seqs[i] = Seq(kv.handle, t.ctypes.data if t.size else None, int(t.shape[0]))
+        if logits is None:
+            logits = torch.empty((max(k, 1), self.info["n_vocab"]), dtype=torch.float32, device="cuda")
+        total = max(1, sum(int(t.shape[0]) for t in toks))
+        n_ctx = max([kv.n_ctx for kv in kvs] or [1])
+        need = lib().ppx_workspace_bytes_multi(self._h, max(n_ubatch, 1), max(min(k, 64), 1), total, n_ctx)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+        ws = self._ws
+        p = PrefillParams(n_ubatch, PRUNE[prune] if isinstance(prune, str) else int(prune), 0,
+                          k if n_seq_max is None else n_seq_max, None,
+                          ctypes.pointer(timing) if timing is not None else None, None)
+        st = lib().ppx_prefill_multi(self._h, seqs, k, ctypes.byref(p), _ptr(ws), ws.numel(), _ptr(logits),
+                                     _stream(stream))
+        _check(st, "ppx_prefill_multi")
         return logits
 
     def decode(self, token: int, kv: "KVCache", logits=None, stream=None):

@@ -75,11 +75,26 @@ __global__ __launch_bounds__(C::NT) void k_attn_prefill(AttnArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = attn_wave_id();
     const int G = a.H / a.KVH;
-    const int cb = blockIdx.x, ck = blockIdx.y, kvh = blockIdx.z;
+    const int ck = blockIdx.y, kvh = blockIdx.z;
     const int lc = lane & 15, lg = lane >> 4;
+    // the workgroup's rows: [row0, row0 + M) of the launch, one sequence's
+    // positions pos0 .. pos0 + M - 1, read against that sequence's cache
+    int cb = blockIdx.x, M = a.M, pos0 = a.pos0, row0 = 0, vld = a.vld;
+    const __half *kp = a.k, *vtp = a.vt;
+    if (a.wg) {
+        const AttnWg &d = a.wg[blockIdx.x];
+        cb = d.cb;
+        M = d.M;
+        pos0 = d.pos0;
+        row0 = d.row0;
+        const KVRef &ref = a.seq_kv[d.seq];
+        kp = ref.k;
+        vtp = ref.vt;
+        vld = ref.vld;
+    }
 
-    const int tmax = min(a.M - 1, (cb * C::CB + C::CB - 1) / G);
-    const int pend = a.pos0 + tmax;  // last key any column here can see
+    const int tmax = min(M - 1, (cb * C::CB + C::CB - 1) / G);
+    const int pend = pos0 + tmax;  // last key any column here can see
     const int kbeg = ck * a.kc;
     if (kbeg > pend) return;  // the whole workgroup
     const int kend = min(kbeg + a.kc, pend + 1);
@@ -90,7 +105,7 @@ __global__ __launch_bounds__(C::NT) void k_attn_prefill(AttnArgs a) {
         // K rows past the last written position repeat it (their scores are
         // masked); V^T reads stay inside the row (vld is a multiple of 64).
         const int pw = C::NP == 1 ? 0 : wave - C::NC;
-        const int plast = a.pos0 + a.M - 1;
+        const int plast = pos0 + M - 1;
         auto entry = [&](int t) { return min(t * C::NP + pw, C::DMA_STAGE - 1); };
         int koff[C::PER];  // K: key within the stage; V^T: element offset within the row block
 #pragma unroll
@@ -104,7 +119,7 @@ __global__ __launch_bounds__(C::NT) void k_attn_prefill(AttnArgs a) {
             } else {
                 // V^T subtile i: lane l holds dim 16 i + l % 16, keys 8 (l / 16) .. + 7
                 const int i = e - 2 * KB;
-                koff[t] = (kvh * HD + i * 16 + (lane & 15)) * a.vld + 8 * (lane >> 4);
+                koff[t] = (kvh * HD + i * 16 + (lane & 15)) * vld + 8 * (lane >> 4);
             }
         }
         auto issue = [&](int sb) {
@@ -116,9 +131,9 @@ __global__ __launch_bounds__(C::NT) void k_attn_prefill(AttnArgs a) {
                 if (e < 2 * KB) {
                     const int kb = e >> 1;
                     const int key = min(t0 + koff[t], plast);
-                    adma16(a.k + ((size_t)key * a.KVH + kvh) * HD + kb * 32 + 8 * (lane >> 4), st + e * 64);
+                    adma16(kp + ((size_t)key * a.KVH + kvh) * HD + kb * 32 + 8 * (lane >> 4), st + e * 64);
                 } else {
-                    adma16(a.vt + (size_t)koff[t] + t0, st + C::K_UNITS + (e - 2 * KB) * 64);
+                    adma16(vtp + (size_t)koff[t] + t0, st + C::K_UNITS + (e - 2 * KB) * 64);
                 }
             }
         };
@@ -143,13 +158,13 @@ __global__ __launch_bounds__(C::NT) void k_attn_prefill(AttnArgs a) {
     for (int c = 0; c < CPW; ++c) {
         const int col = cb * C::CB + wave * 16 * CPW + c * 16 + lc;
         t[c] = col / G;
-        valid[c] = t[c] < a.M;
+        valid[c] = t[c] < M;
         h[c] = kvh * G + col % G;
-        qpos[c] = a.pos0 + (valid[c] ? t[c] : 0);
+        qpos[c] = pos0 + (valid[c] ? t[c] : 0);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
-            qf[c][kb] = *reinterpret_cast<const h8 *>(a.q + ((size_t)min(t[c], a.M - 1) * a.H + h[c]) * HD + kb * 32 +
-                                                      lg * 8);
+            qf[c][kb] = *reinterpret_cast<const h8 *>(a.q + ((size_t)(row0 + min(t[c], M - 1)) * a.H + h[c]) * HD +
+                                                      kb * 32 + lg * 8);
     }
 
     f4 oacc[CPW][DT];
@@ -244,13 +259,13 @@ __global__ __launch_bounds__(C::NT) void k_attn_prefill(AttnArgs a) {
                 h4 v;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) v[r] = (_Float16)(oacc[c][i][r] * inv);
-                *reinterpret_cast<h4 *>(a.o + tiled_index(t[c], h[c] * HD + d, od)) = v;
+                *reinterpret_cast<h4 *>(a.o + tiled_index(row0 + t[c], h[c] * HD + d, od)) = v;
             }
         } else {
             // the chunk's own normalised output in fp16 (a convex combination of
             // value rows, so bounded by them), its max and exp-sum in fp32; a
             // row that sees no key of the chunk writes zeros, never read
-            const size_t slot = ((size_t)ck * a.M + t[c]) * a.H + h[c];
+            const size_t slot = ((size_t)ck * a.M + row0 + t[c]) * a.H + h[c];
             const float inv = lrun[c] > 0.f ? 1.0f / lrun[c] : 0.f;
             _Float16 *po = reinterpret_cast<_Float16 *>(a.part) + slot * HD;
 #pragma unroll
@@ -263,7 +278,7 @@ __global__ __launch_bounds__(C::NT) void k_attn_prefill(AttnArgs a) {
             if (lg == 0) {
                 // (max, sum) pairs of one (row, head) are contiguous over the chunks
                 float *pm = a.part + (size_t)a.nkc * a.M * a.H * (HD / 2) +
-                            (((size_t)t[c] * a.H + h[c]) * a.nkc + ck) * 2;
+                            (((size_t)(row0 + t[c]) * a.H + h[c]) * a.nkc + ck) * 2;
                 pm[0] = mrun[c];
                 pm[1] = lrun[c];
             }
@@ -283,7 +298,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_merge(AttnArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
     if (w >= a.M * a.H) return;
     const int t = w / a.H, h = w % a.H;
-    const int nch = (a.pos0 + t) / a.kc + 1;
+    const int nch = (a.row_pos ? a.row_pos[t] : a.pos0 + t) / a.kc + 1;
     const _Float16 *po = reinterpret_cast<const _Float16 *>(a.part);
     const float *pm = a.part + (size_t)a.nkc * a.M * a.H * (HD / 2) + (size_t)w * a.nkc * 2;
     // lane c holds chunk c's weight l_c 2^(m_c - M)
@@ -495,8 +510,9 @@ constexpr int ATTN_MIN_KC = 128;  // keys per chunk at least (early ubatches get
 
 AttnSplit attn_split(int M, int H, int KVH, int pos0) {
     const int G = H / KVH;
-    const int colblocks = (M * G + ATTN_CB - 1) / ATTN_CB;
-    const int P = pos0 + M;
+    return attn_split_cols((M * G + ATTN_CB - 1) / ATTN_CB, KVH, pos0 + M);
+}
+AttnSplit attn_split_cols(int colblocks, int KVH, int P) {
     int want = (256 + colblocks * KVH - 1) / (colblocks * KVH);
     want = std::max(1, std::min(want, ATTN_MAX_CHUNKS));
     int kc = (P + want - 1) / want;
@@ -507,6 +523,10 @@ AttnSplit attn_split(int M, int H, int KVH, int pos0) {
     return sp;
 }
 
+int attn_prefill_cols_per_wg(int hd) {
+    (void)hd;
+    return ATTN_CB;
+}
 size_t attn_prefill_scratch_floats(int M, int H, int hd, int n_ctx) {
     const int nkc = std::min(ATTN_MAX_CHUNKS, (n_ctx + ATTN_MIN_KC - 1) / ATTN_MIN_KC);
     return (size_t)nkc * M * H * (hd / 2 + 2);  // fp16 chunk outputs, then fp32 (max, sum) pairs
@@ -516,12 +536,23 @@ int launch_attn_prefill(const AttnArgs &a0, hipStream_t s) {
     AttnArgs a = a0;
     if (a.M <= 0) return PPX_OK;
     const int G = a.H / a.KVH;
-    if (a.H % a.KVH || 64 % G || a.vld % 64 || a.pos0 + a.M > a.vld) return PPX_E_UNSUPPORTED;
-    const AttnSplit sp = attn_split(a.M, a.H, a.KVH, a.pos0);
-    a.kc = sp.kc;
-    a.nkc = sp.nkc;
+    if (a.H % a.KVH || 64 % G) return PPX_E_UNSUPPORTED;
+    int nx;
+    if (a.wg) {
+        // several sequences: the caller built the workgroup table and the split
+        if (a.nwg < 1 || !a.seq_kv || !a.row_pos || a.kc < ATTN_MIN_KC || a.kc % 64 || a.nkc < 1 ||
+            a.nkc > ATTN_MAX_CHUNKS)
+            return PPX_E_INVAL;
+        nx = a.nwg;
+    } else {
+        if (a.vld % 64 || a.pos0 + a.M > a.vld) return PPX_E_UNSUPPORTED;
+        const AttnSplit sp = attn_split(a.M, a.H, a.KVH, a.pos0);
+        a.kc = sp.kc;
+        a.nkc = sp.nkc;
+        nx = (a.M * G + ATTN_CB - 1) / ATTN_CB;
+    }
     if (a.nkc > 1 && !a.part) return PPX_E_INVAL;
-    dim3 grid((a.M * G + ATTN_CB - 1) / ATTN_CB, a.nkc, a.KVH);
+    dim3 grid(nx, a.nkc, a.KVH);
     switch (a.hd) {
 #define PPX_ATTN(hd_, np_, depth_)                                                                   \
     case hd_: {                                                                                      \

@@ -103,6 +103,18 @@ struct Ctx {
     WsLayout L;
     ppx_timing *tm = nullptr;  // per-phase timing requested
     int slot = 0;              // buffers of the ubatch being enqueued
+    // A row batch spanning several sequences, each with its own cache (null:
+    // the rows are one sequence's consecutive positions, in kv).
+    struct Rows {
+        const int32_t *tok = nullptr, *pos = nullptr, *seq = nullptr;  // device, per row
+        const KVRef *kv = nullptr;  // device, [Ls][nseq]: sequence s's cache of owning layer l at l * nseq + s
+        int nseq = 0;
+        const AttnWg *wg = nullptr;  // device: the attention workgroups of the batch
+        int nwg = 0;
+        AttnSplit split;
+        double vis = 0;  // causal (query, key) pairs of the batch (timing only)
+    };
+    const Rows *rows = nullptr;
     // K/V ordering between ubatches on different streams: after writing layer
     // l's K/V, kv_done[l] is recorded; before attention reads layer l's cache,
     // kv_wait[l] (the previous ubatch's record, if on another stream) is
@@ -183,8 +195,9 @@ int layer_rows(Ctx &c, int il, int M, int row0, int pos0) {
     __half *q16 = c.sl<__half>(c.L.q16);
     __half *o16 = c.sl<__half>(c.L.o16);
     __half *h16 = c.sl<__half>(c.L.h16);
-    const size_t lstride = (size_t)c.kv->n_ctx * kvd;
-    const size_t vstride = (size_t)c.kv->vld * kvd;
+    const Ctx::Rows *R = c.rows;
+    const size_t lstride = R ? 0 : (size_t)c.kv->n_ctx * kvd;
+    const size_t vstride = R ? 0 : (size_t)c.kv->vld * kvd;
 
     __half *a16lo = c.sl<__half>(c.L.a16lo);
     if (w.own)
@@ -203,6 +216,7 @@ int layer_rows(Ctx &c, int il, int M, int row0, int pos0) {
     g.hd = hd;
     g.pos0 = pos0;
     g.rope = m->rope;
+    if (R) g.row_pos = R->pos;
     PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm(g, c.s));
     if (w.own) {
         // K and V on the exact-weight path, straight into this layer's cache rows
@@ -212,9 +226,14 @@ int layer_rows(Ctx &c, int il, int M, int row0, int pos0) {
         gk.qd = 0;
         gk.kvd = kvd;
         gk.out_f16 = nullptr;
-        gk.kc = c.kv->k + il * lstride;
-        gk.vc = c.kv->vt + il * vstride;
-        gk.vld = c.kv->vld;
+        if (R) {
+            gk.row_seq = R->seq;
+            gk.seq_kv = R->kv + (size_t)il * R->nseq;
+        } else {
+            gk.kc = c.kv->k + il * lstride;
+            gk.vc = c.kv->vt + il * vstride;
+            gk.vld = c.kv->vld;
+        }
         PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm_exact(gk, c.s));
     }
     // earlier ubatches' K/V of the layer read here (owning: this layer; shared: its source)
@@ -225,9 +244,18 @@ int layer_rows(Ctx &c, int il, int M, int row0, int pos0) {
 
     AttnArgs at;
     at.q = q16;
-    at.k = c.kv->k + (size_t)w.src * lstride;
-    at.vt = c.kv->vt + (size_t)w.src * vstride;
-    at.vld = c.kv->vld;
+    if (R) {
+        at.wg = R->wg;
+        at.nwg = R->nwg;
+        at.seq_kv = R->kv + (size_t)w.src * R->nseq;
+        at.row_pos = R->pos;
+        at.kc = R->split.kc;
+        at.nkc = R->split.nkc;
+    } else {
+        at.k = c.kv->k + (size_t)w.src * lstride;
+        at.vt = c.kv->vt + (size_t)w.src * vstride;
+        at.vld = c.kv->vld;
+    }
     at.part = c.sl<float>(c.L.ap_part);
     at.o = o16;
     at.M = M;
@@ -287,7 +315,7 @@ int layer_rows(Ctx &c, int il, int M, int row0, int pos0) {
         gp.epi = EPI_PLE;
         gp.out_f16 = p16;
         gp.ple_raw = m->ple_raw;
-        gp.tok = c.at<int32_t>(c.L.tok) + row0;
+        gp.tok = R ? R->tok : c.at<int32_t>(c.L.tok) + row0;
         gp.ple_row_blocks = I.n_layer * E / 32;
         gp.ple_col0 = il * E;
         gp.ple_s = w.ple_s;
@@ -308,7 +336,7 @@ int layer_rows(Ctx &c, int il, int M, int row0, int pos0) {
         if (I.ple_dim) nk += (double)w.wpg.N * w.wpg.K + (double)w.wpu.N * w.wpu.K;
         c.tm->gemm_flop += 2.0 * M * nk;
         c.tm->glu_flop += 2.0 * M * w.wgu.N * w.wgu.K;
-        const double vis = (double)M * pos0 + 0.5 * (double)M * (M + 1);  // causal (query, key) pairs
+        const double vis = R ? R->vis : (double)M * pos0 + 0.5 * (double)M * (M + 1);  // causal (query, key) pairs
         c.tm->attn_flop += 4.0 * I.n_head * hd * vis;
     }
     return PPX_OK;
@@ -653,6 +681,316 @@ int decode(ppx_model *m, ppx_kv *kv, int32_t token, void *ws, size_t ws_bytes, f
     return PPX_OK;
 }
 
+// ------------------------------------------------------------------ several sequences
+
+// Workspace of a multi-sequence prefill: the single-sequence buffers sized for
+// max(n_ubatch, n_seq) rows (every ubatch and the gathered output rows use
+// them in turn), the gathered rows, then the per-row tables, copied from the
+// host in one transfer.
+struct MultiLayout {
+    WsLayout w;
+    size_t xk;                  // fp32 [k][d]: each sequence's output row
+    size_t blob;                // start of the tables (everything below is relative to it)
+    size_t tok, pos, seq;       // int32 [T] over the rows laid end to end
+    size_t ttok, tpos, tseq;    // int32 [k] of the gathered rows
+    size_t kv;                  // KVRef [Ls][k]
+    size_t wg;                  // AttnWg [max_wg]: every ubatch's workgroups, then the tail's
+    size_t pairs;               // int2 [k]: (row in its ubatch, sequence) of each output row
+    size_t blob_bytes;
+    size_t max_wg;
+    size_t total;
+};
+
+MultiLayout multi_layout(const ppx_model *m, int ub, int k, long T, int n_ctx_max) {
+    const ppx_model_info &I = m->info;
+    MultiLayout L{};
+    L.w = ws_layout(m, std::max(ub, k), n_ctx_max);
+    size_t o = L.w.total;
+    L.xk = o;
+    o += al(4ull * k * I.d_model);
+    L.blob = o;
+    size_t b = 0;
+    auto take = [&](size_t bytes) {
+        const size_t r = b;
+        b += al(bytes);
+        return r;
+    };
+    const int G = I.n_head / std::max(I.n_kv_head, 1);
+    const int cb = attn_prefill_cols_per_wg(I.head_dim);
+    const long nub = (T + ub - 1) / ub;
+    // per ubatch: its rows' column blocks, plus one partial block per sequence boundary
+    L.max_wg = (size_t)nub * ((ub * (size_t)G + cb - 1) / cb + 1) + 2 * (size_t)k;
+    L.tok = take(4ull * T);
+    L.pos = take(4ull * T);
+    L.seq = take(4ull * T);
+    L.ttok = take(4ull * k);
+    L.tpos = take(4ull * k);
+    L.tseq = take(4ull * k);
+    L.kv = take(sizeof(KVRef) * (size_t)std::max(I.n_layer_kv_from_start, 1) * k);
+    L.wg = take(sizeof(AttnWg) * L.max_wg);
+    L.pairs = take(sizeof(int2) * (size_t)k);
+    L.blob_bytes = b;
+    L.total = L.blob + b;
+    return L;
+}
+
+// Pinned staging for the tables: the previous copy out of it must be done
+// before it is rewritten (the caller's stream may still be behind).
+int stage_tables(ppx_model *m, size_t bytes, uint8_t **out) {
+    if (m->stage_event && hipEventSynchronize(m->stage_event) != hipSuccess) return PPX_E_HIP;
+    if (m->stage_bytes < bytes) {
+        if (m->stage_host) (void)hipHostFree(m->stage_host);
+        m->stage_host = nullptr;
+        m->stage_bytes = 0;
+        if (hipHostMalloc(&m->stage_host, bytes, hipHostMallocDefault) != hipSuccess) return PPX_E_NOMEM;
+        m->stage_bytes = bytes;
+    }
+    if (!m->stage_event && hipEventCreateWithFlags(&m->stage_event, hipEventDisableTiming) != hipSuccess)
+        return PPX_E_HIP;
+    *out = static_cast<uint8_t *>(m->stage_host);
+    return PPX_OK;
+}
+
+// Several prompts, each in its own cache, in one pass.  Their rows are laid
+// end to end and cut into ubatches of n_ubatch rows; a ubatch row carries its
+// own position and sequence, so the K|V projection writes each row into its
+// own cache and attention reads each row's own cache.  Pruning generalises
+// the single-sequence rule to one output row per sequence: the ubatch that
+// holds a prompt's last row gathers it after the owning layers, and the k
+// gathered rows alone run the KV-shared layers (each against its own
+// sequence's source-layer cache) and the head.  Without pruning they are
+// gathered after the last layer.  logits: fp32 [k][n_vocab].
+int prefill_multi(ppx_model *m, const ppx_seq *seqs, int k, const ppx_prefill_params *p, void *ws, size_t ws_bytes,
+                  float *logits, hipStream_t s) {
+    if (!m || !seqs || !p || !logits || !ws) return PPX_E_INVAL;
+    if (k < 1 || k > PPX_MAX_SEQ) return PPX_E_INVAL;
+    const ppx_model_info &I = m->info;
+    if (p->embeddings != 0) return PPX_E_UNSUPPORTED;
+    if (p->debug_rows || p->debug_hidden) return PPX_E_UNSUPPORTED;
+    if (p->n_seq_max < k) return PPX_E_INVAL;
+    if (p->n_ubatch < 1 || p->n_ubatch > PPX_MAX_UBATCH) return PPX_E_INVAL;
+    long T = 0;
+    int nctx_max = 1;
+    for (int q = 0; q < k; ++q) {
+        const ppx_seq &sq = seqs[q];
+        if (!sq.kv || sq.kv->m != m) return PPX_E_INVAL;
+        for (int r = 0; r < q; ++r)
+            if (seqs[r].kv == sq.kv) return PPX_E_INVAL;  // each sequence needs its own cache
+        if (sq.n_tokens <= 0) return PPX_E_EMPTY;
+        if (!sq.tokens_host) return PPX_E_INVAL;
+        for (int i = 0; i < sq.n_tokens; ++i)
+            if (sq.tokens_host[i] < 0 || sq.tokens_host[i] >= I.n_vocab) return PPX_E_TOKEN;
+        if ((long)sq.kv->n_pos + sq.n_tokens > sq.kv->n_ctx) return PPX_E_CTX;
+        T += sq.n_tokens;
+        nctx_max = std::max(nctx_max, sq.kv->n_ctx);
+    }
+    if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return PPX_E_INVAL;
+    if (k == 1) {
+        // one sequence: exactly the single-sequence prefill
+        ppx_prefill_params q1 = *p;
+        q1.n_seq_max = 1;
+        return prefill(m, seqs[0].kv, seqs[0].tokens_host, seqs[0].n_tokens, &q1, ws, ws_bytes, logits, s);
+    }
+    const int L = I.n_layer, Ls = I.n_layer_kv_from_start, d = I.d_model, kvd = I.kv_dim;
+    // one output row per sequence: the single-sequence predicate holds per sequence
+    const int can = predicate(L, Ls, p->embeddings, 1, nullptr, 1);
+    bool prune;
+    if (p->prune == PPX_PRUNE_AUTO) prune = can;
+    else if (p->prune == PPX_PRUNE_OFF) prune = false;
+    else if (p->prune == PPX_PRUNE_ON) {
+        if (!can) return PPX_E_UNSUPPORTED;
+        prune = true;
+    } else return PPX_E_INVAL;
+
+    const int ub = p->n_ubatch;
+    const MultiLayout ML = multi_layout(m, ub, k, T, nctx_max);
+    if (ws_bytes < ML.total) return PPX_E_NOMEM;
+    const int G = I.n_head / I.n_kv_head;
+    const int cbw = attn_prefill_cols_per_wg(I.head_dim);
+    if (G > cbw) return PPX_E_UNSUPPORTED;  // a one-row segment fits one column block
+
+    // ---- the tables, built on the host
+    uint8_t *hb = nullptr;
+    PPX_TRY(stage_tables(m, ML.blob_bytes, &hb));
+    auto H32 = [&](size_t off) { return reinterpret_cast<int32_t *>(hb + off); };
+    int32_t *tok = H32(ML.tok), *pos = H32(ML.pos), *seq = H32(ML.seq);
+    int32_t *ttok = H32(ML.ttok), *tpos = H32(ML.tpos), *tseq = H32(ML.tseq);
+    std::vector<long> last(k);
+    {
+        long r = 0;
+        for (int q = 0; q < k; ++q) {
+            const ppx_seq &sq = seqs[q];
+            for (int i = 0; i < sq.n_tokens; ++i, ++r) {
+                tok[r] = sq.tokens_host[i];
+                pos[r] = sq.kv->n_pos + i;
+                seq[r] = q;
+            }
+            last[q] = r - 1;
+            ttok[q] = sq.tokens_host[sq.n_tokens - 1];
+            tpos[q] = sq.kv->n_pos + sq.n_tokens - 1;
+            tseq[q] = q;
+        }
+    }
+    KVRef *kvt = reinterpret_cast<KVRef *>(hb + ML.kv);
+    for (int l = 0; l < Ls; ++l)
+        for (int q = 0; q < k; ++q) {
+            const ppx_kv *kv = seqs[q].kv;
+            KVRef &ref = kvt[(size_t)l * k + q];
+            ref.k = kv->k + (size_t)l * kv->n_ctx * kvd;
+            ref.vt = kv->vt + (size_t)l * kv->vld * kvd;
+            ref.vld = kv->vld;
+            ref.pad = 0;
+        }
+    AttnWg *wgt = reinterpret_cast<AttnWg *>(hb + ML.wg);
+    int2 *pairs = reinterpret_cast<int2 *>(hb + ML.pairs);
+    struct Ub {
+        long u0;
+        int M;
+        size_t wg0;
+        int nwg;
+        AttnSplit split;
+        double vis;
+        int pair0, npairs;
+    };
+    std::vector<Ub> ubs;
+    size_t nw = 0;
+    int np = 0;
+    bool over = false;
+    auto add_segment = [&](int row0, int Ms, int pos0, int q) {
+        const int nb = (Ms * G + cbw - 1) / cbw;
+        for (int b = 0; b < nb; ++b) {
+            if (nw >= ML.max_wg) {
+                over = true;
+                return;
+            }
+            wgt[nw++] = AttnWg{row0, Ms, pos0, q, b, {0, 0, 0}};
+        }
+    };
+    for (long u0 = 0; u0 < T; u0 += ub) {
+        Ub U{};
+        U.u0 = u0;
+        U.M = (int)std::min<long>(ub, T - u0);
+        U.wg0 = nw;
+        U.pair0 = np;
+        int P = 1;
+        for (int r = 0; r < U.M;) {
+            const int q = seq[u0 + r];
+            int e = r + 1;
+            while (e < U.M && seq[u0 + e] == q) ++e;
+            const int Ms = e - r, p0 = pos[u0 + r];
+            add_segment(r, Ms, p0, q);
+            P = std::max(P, p0 + Ms);
+            U.vis += (double)Ms * p0 + 0.5 * (double)Ms * (Ms + 1);
+            if (last[q] < u0 + e) {
+                if (np < k) pairs[np] = int2{(int)(last[q] - u0), q};
+                ++np;
+            }
+            r = e;
+        }
+        U.nwg = (int)(nw - U.wg0);
+        U.npairs = np - U.pair0;
+        U.split = attn_split_cols(U.nwg, I.n_kv_head, P);
+        ubs.push_back(U);
+    }
+    Ub tail{};
+    tail.M = k;
+    tail.wg0 = nw;
+    {
+        int P = 1;
+        for (int q = 0; q < k; ++q) {
+            add_segment(q, 1, tpos[q], q);
+            P = std::max(P, tpos[q] + 1);
+            tail.vis += tpos[q] + 1.0;
+        }
+        tail.nwg = (int)(nw - tail.wg0);
+        tail.split = attn_split_cols(tail.nwg, I.n_kv_head, P);
+    }
+    if (over || np != k) return PPX_E_INVAL;  // cannot happen: the layout's bounds hold for any lengths
+
+    uint8_t *wsb = static_cast<uint8_t *>(ws);
+    uint8_t *dblob = wsb + ML.blob;
+    if (hipMemcpyAsync(dblob, hb, ML.blob_bytes, hipMemcpyHostToDevice, s) != hipSuccess) return PPX_E_HIP;
+    if (hipEventRecord(m->stage_event, s) != hipSuccess) return PPX_E_HIP;
+    auto D32 = [&](size_t off) { return reinterpret_cast<const int32_t *>(dblob + off); };
+    const KVRef *dkv = reinterpret_cast<const KVRef *>(dblob + ML.kv);
+    const AttnWg *dwg = reinterpret_cast<const AttnWg *>(dblob + ML.wg);
+    const int2 *dpairs = reinterpret_cast<const int2 *>(dblob + ML.pairs);
+    float *xk = reinterpret_cast<float *>(wsb + ML.xk);
+
+    Ctx c{m, nullptr, s, wsb, ML.w};
+    if (p->timing) {
+        std::memset(p->timing, 0, sizeof(*p->timing));
+        c.tm = p->timing;
+    }
+    if (log_enabled())
+        std::fprintf(stderr, "[ppx] prefill of %d sequences, %ld rows, ubatch %d, prune %s\n", k, T, ub,
+                     prune ? "on" : "off");
+    float *x = c.sl<float>(c.L.x);
+    const int full_layers = prune ? Ls : L;
+    for (const Ub &U : ubs) {
+        Ctx::Rows R;
+        R.tok = D32(ML.tok) + U.u0;
+        R.pos = D32(ML.pos) + U.u0;
+        R.seq = D32(ML.seq) + U.u0;
+        R.kv = dkv;
+        R.nseq = k;
+        R.wg = dwg + U.wg0;
+        R.nwg = U.nwg;
+        R.split = U.split;
+        R.vis = U.vis;
+        c.rows = &R;
+        PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_embed(m->tok, R.tok, U.M, m->embd_scale, x, s));
+        for (int il = 0; il < full_layers; ++il) PPX_TRY(layer_rows(c, il, U.M, 0, 0));
+        if (U.npairs) PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_gather_rows(x, d, dpairs + U.pair0, U.npairs, xk, s));
+    }
+    PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_copy_f32(xk, x, k * d, s));
+    Ctx::Rows R;
+    R.tok = D32(ML.ttok);
+    R.pos = D32(ML.tpos);
+    R.seq = D32(ML.tseq);
+    R.kv = dkv;
+    R.nseq = k;
+    R.wg = dwg + tail.wg0;
+    R.nwg = tail.nwg;
+    R.split = tail.split;
+    R.vis = tail.vis;
+    c.rows = &R;
+    if (prune)
+        for (int il = Ls; il < L; ++il) PPX_TRY(layer_rows(c, il, k, 0, 0));
+    // the head of the k rows as one GEMM (the output matrix is read once)
+    __half *a16 = c.sl<__half>(c.L.a16);
+    PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_rmsnorm_f16(x, m->out_norm, m->eps, k, d, a16, s));
+    GemmArgs gh = c.gemm();
+    gh.A = a16;
+    gh.lda = d;
+    gh.M = k;
+    gh.W = m->out;
+    gh.epi = EPI_F32;
+    gh.out_f32 = logits;
+    int st = PPX_OK;
+    {
+        hipEvent_t ev0 = c.begin();
+        st = launch_gemm(gh, s);
+        if (st == PPX_E_UNSUPPORTED) {
+            // an output width the MFMA tiles do not divide: one fp32 row at a time
+            st = PPX_OK;
+            for (int q = 0; q < k && st == PPX_OK; ++q) {
+                GemvArgs gv = gemv_base(c, x + (size_t)q * d, m->out, GV_F32, logits + (size_t)q * I.n_vocab);
+                gv.norm_g = m->out_norm;
+                gv.eps = m->eps;
+                st = launch_gemv(gv, s);
+            }
+        }
+        PPX_TRY(st);
+        c.end(PPX_PHASE_GEMM, ev0);
+    }
+    if (c.tm) c.tm->gemm_flop += 2.0 * k * (double)m->out.N * m->out.K;
+    c.rows = nullptr;
+    PPX_TRY(c.finish());
+    for (int q = 0; q < k; ++q) seqs[q].kv->n_pos += seqs[q].n_tokens;
+    return PPX_OK;
+}
+
 // ------------------------------------------------------------------ KVCP snapshots
 
 // With tokens: the KVCP body is followed by a token section, "KVTK", int32
@@ -936,6 +1274,17 @@ size_t ppx_workspace_bytes(const ppx_model *m, int n_ubatch, int n_ctx) {
 int ppx_prefill(ppx_model *m, ppx_kv *kv, const int32_t *tokens_host, int n_tokens, const ppx_prefill_params *p,
                 void *ws_dev, size_t ws_bytes, float *logits_dev, void *hip_stream) {
     return prefill(m, kv, tokens_host, n_tokens, p, ws_dev, ws_bytes, logits_dev, (hipStream_t)hip_stream);
+}
+
+size_t ppx_workspace_bytes_multi(const ppx_model *m, int n_ubatch, int n_seq, long n_tokens_total, int n_ctx_max) {
+    if (!m || n_ubatch < 1 || n_seq < 1 || n_seq > PPX_MAX_SEQ || n_tokens_total < 1 || n_ctx_max < 1) return 0;
+    const size_t one = ws_layout(m, n_ubatch, n_ctx_max).total;
+    return std::max(one, multi_layout(m, n_ubatch, n_seq, n_tokens_total, n_ctx_max).total);
+}
+
+int ppx_prefill_multi(ppx_model *m, const ppx_seq *seqs, int n_seq, const ppx_prefill_params *p, void *ws_dev,
+                      size_t ws_bytes, float *logits_dev, void *hip_stream) {
+    return prefill_multi(m, seqs, n_seq, p, ws_dev, ws_bytes, logits_dev, (hipStream_t)hip_stream);
 }
 
 int ppx_decode(ppx_model *m, ppx_kv *kv, int32_t token, void *ws_dev, size_t ws_bytes, float *logits_dev,

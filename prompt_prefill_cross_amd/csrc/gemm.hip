@@ -176,7 +176,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, const f4 (&acc)
     } else {
         // EPI_QKV: 16-column groups (2p, 2p+1) of the wave tile hold the first and
         // second RoPE half of 16 dimensions.  Columns [0,qd) Q, [qd,qd+kvd) K,
-        // [qd+kvd, qd+2kvd) V.
+        // [qd+kvd, qd+2kvd) V.  Rows of several sequences take their position
+        // and their sequence's cache from the per-row tables.
 #pragma unroll
         for (int p = 0; p < TN / 2; ++p) {
             const int colA = c0 + p * 32 + lc;  // first member; second = colA + 16
@@ -188,7 +189,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, const f4 (&acc)
                     if (row >= a.M) continue;
                     const float va = acc[i][2 * p][r], vb = acc[i][2 * p + 1][r];
                     const int hd = a.hd, half = hd >> 1;
-                    const int pos = a.pos0 + row;
+                    const int pos = a.row_pos ? a.row_pos[row] : a.pos0 + row;
                     if (colA < a.qd + a.kvd) {
                         const bool isq = colA < a.qd;
                         const int c = isq ? colA : colA - a.qd;
@@ -202,14 +203,22 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, const f4 (&acc)
                             q[ii] = __float2half(ra);
                             q[ii + half] = __float2half(rb);
                         } else {
-                            __half *k = a.kc + (size_t)pos * a.kvd + h * hd;
+                            __half *kc = a.seq_kv ? a.seq_kv[a.row_seq[row]].k : a.kc;
+                            __half *k = kc + (size_t)pos * a.kvd + h * hd;
                             k[ii] = __float2half(ra);
                             k[ii + half] = __float2half(rb);
                         }
                     } else {
                         const int c = colA - a.qd - a.kvd;
-                        a.vc[(size_t)c * a.vld + pos] = __float2half(va);  // V^T
-                        a.vc[(size_t)(c + 16) * a.vld + pos] = __float2half(vb);
+                        __half *vc = a.vc;
+                        int vld = a.vld;
+                        if (a.seq_kv) {
+                            const KVRef &ref = a.seq_kv[a.row_seq[row]];
+                            vc = ref.vt;
+                            vld = ref.vld;
+                        }
+                        vc[(size_t)c * vld + pos] = __float2half(va);  // V^T
+                        vc[(size_t)(c + 16) * vld + pos] = __float2half(vb);
                     }
                 }
         }
@@ -768,9 +777,11 @@ struct Plan {
 // four ways over workgroups; Q and O use 32-row tiles with four producer
 // waves; narrow outputs (N <= 512) single 16 x 16 tiles with K split four
 // ways inside the workgroup, so that 512 short chains run instead of 64 long
-// ones; K = 256 the 32-row tiles of Q and O.
+// ones; K = 256 the 32-row tiles of Q and O.  At most 16 rows of a wide
+// output (the logits of a few sequences) take the single 16 x 16 tiles, so
+// the weights stream once with no idle tile rows.
 Plan plan_for(int M, int N, int K) {
-    (void)M;
+    if (N >= 8192 && M <= 16) return {7, 1};  // a few rows (the head of several sequences): one 16-row tile
     if (N >= 8192) return {N % 192 == 0 ? 0 : 1, 1};
     if (K >= 4096) return {N % 192 == 0 ? 2 : 3, 4};
     if (N <= 512) return {7, 1};

@@ -133,6 +133,15 @@ __global__ void k_copy_f32(const float *src, float *dst, int n) {
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) dst[i] = src[i];
 }
 
+// One workgroup per pair: dst row pairs[i].y = src row pairs[i].x (the
+// output rows of several sequences, gathered before the KV-shared layers).
+__global__ __launch_bounds__(256) void k_gather_rows(const float *src, int d, const int2 *pairs, float *dst) {
+    const int2 pr = pairs[blockIdx.x];
+    const float *x = src + (size_t)pr.x * d;
+    float *y = dst + (size_t)pr.y * d;
+    for (int i = threadIdx.x; i < d; i += 256) y[i] = x[i];
+}
+
 int ok() { return hipGetLastError() == hipSuccess ? PPX_OK : PPX_E_HIP; }
 
 // ------------------------------------------------------------------ GEMV
@@ -415,6 +424,13 @@ int launch_copy_f32(const float *src, float *dst, int n, hipStream_t s) {
     if (n <= 0) return PPX_OK;
     hipLaunchKernelGGL(k_copy_f32, dim3((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024), dim3(256), 0, s, src,
                        dst, n);
+    return ok();
+}
+
+int launch_gather_rows(const float *src, int d, const int2 *pairs, int n, float *dst, hipStream_t s) {
+    if (n <= 0) return PPX_OK;
+    if (!src || !pairs || !dst || d <= 0) return PPX_E_INVAL;
+    hipLaunchKernelGGL(k_gather_rows, dim3(n), dim3(256), 0, s, src, d, pairs, dst);
     return ok();
 }
 

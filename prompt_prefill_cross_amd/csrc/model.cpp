@@ -371,6 +371,8 @@ void model_free(ppx_model *m) {
     for (hipStream_t st : m->aux_streams) (void)hipStreamDestroy(st);
     for (hipStream_t st : m->capture_aux) (void)hipStreamDestroy(st);
     for (hipEvent_t e : m->sync_events) (void)hipEventDestroy(e);
+    if (m->stage_host) (void)hipHostFree(m->stage_host);
+    if (m->stage_event) (void)hipEventDestroy(m->stage_event);
     delete m;
 }
 

@@ -85,6 +85,11 @@ struct ppx_model {
     std::vector<hipStream_t> aux_streams;  // ubatches in flight, direct launches
     std::vector<hipStream_t> capture_aux;  // ubatches in flight, recording
     std::vector<hipEvent_t> sync_events;   // cross-stream ordering inside one prefill
+    // pinned host staging of the per-row tables of a multi-sequence prefill;
+    // stage_event marks the end of the last copy out of it
+    void *stage_host = nullptr;
+    size_t stage_bytes = 0;
+    hipEvent_t stage_event = nullptr;
 };
 
 struct ppx_kv {
@@ -107,6 +112,15 @@ enum GemmEpi {
     EPI_GLU = 3,  // act(gate) * up -> fp16 h[M][F]; in every 16-column group of the fused
                   // weight, columns 0-7 are gate rows 8t..8t+7 and columns 8-15 the up rows
     EPI_PLE = 4,  // gelu(C) * s * deq(ple_table[tok]) -> fp16 [M][E]
+};
+
+// One sequence's cache of one layer, for row batches that span several
+// sequences (each with its own cache).
+struct KVRef {
+    __half *k = nullptr;   // [n_ctx][kv_dim]
+    __half *vt = nullptr;  // [kv_dim][vld]
+    int vld = 0;
+    int pad = 0;
 };
 
 struct GemmArgs {
@@ -132,6 +146,12 @@ struct GemmArgs {
     int ple_row_blocks = 0;        // L*E/32
     int ple_col0 = 0;              // il*E
     float ple_s = 0.f;
+    // EPI_QKV rows of several sequences (null: one sequence, row r at pos0 + r
+    // in kc / vc): row r's position, and for the K|V projection its sequence,
+    // whose cache of this layer is seq_kv[row_seq[r]].
+    const int32_t *row_pos = nullptr;
+    const int32_t *row_seq = nullptr;
+    const KVRef *seq_kv = nullptr;
     // K split over workgroups: fp32 partial tiles, summed in split order by a
     // second kernel that applies the epilogue.  Null: no split.
     float *part = nullptr;
@@ -184,6 +204,19 @@ struct AttnSplit {
     int kc = 0, nkc = 1;  // keys per chunk (multiple of 64), chunks
 };
 AttnSplit attn_split(int M, int H, int KVH, int pos0);
+// The same rule for a launch of `colblocks` workgroup column blocks per KV
+// head whose longest sequence segment ends at position P - 1.
+AttnSplit attn_split_cols(int colblocks, int KVH, int P);
+// Query columns ((row, head-in-group) pairs) one prefill attention workgroup owns.
+int attn_prefill_cols_per_wg(int hd);
+
+// A workgroup of a row-batched attention launch over several sequences: rows
+// [row0, row0 + M) of the launch are one sequence's positions pos0 .. pos0+M-1,
+// and the workgroup owns column block cb of them.
+struct AttnWg {
+    int row0, M, pos0, seq, cb;
+    int pad[3];
+};
 size_t attn_prefill_scratch_floats(int M, int H, int hd, int n_ctx);
 
 struct AttnArgs {
@@ -195,6 +228,14 @@ struct AttnArgs {
     int M = 0, H = 0, KVH = 0, hd = 0, pos0 = 0;
     int kc = 0, nkc = 1;         // key split (set by the launcher)
     float *part = nullptr;       // scratch of attn_prefill_scratch_floats(M, H, hd, pos0 + M) floats
+    // Rows of several sequences (null wg: one sequence, k / vt / pos0 above):
+    // workgroup x of the launch is wg[x]; sequence s reads the cache seq_kv[s];
+    // row r is at position row_pos[r].  kc / nkc are then set by the caller
+    // (attn_split_cols), every segment satisfies pos0 + M <= its vld.
+    const AttnWg *wg = nullptr;
+    int nwg = 0;
+    const KVRef *seq_kv = nullptr;
+    const int32_t *row_pos = nullptr;
 };
 int launch_attn_prefill(const AttnArgs &a, hipStream_t s);
 
@@ -224,6 +265,8 @@ int launch_dequant(const Q4R &w, float *out, hipStream_t s);
 int launch_tile_f16(const __half *src, int M, int K, __half *dst, hipStream_t s);
 int launch_copy_f32(const float *src, float *dst, int n, hipStream_t s);
 int launch_fill_u32(uint32_t *p, uint32_t v, size_t n, hipStream_t s);
+// dst row pairs[i].y = src row pairs[i].x (fp32 rows of d values), i < n.
+int launch_gather_rows(const float *src, int d, const int2 *pairs, int n, float *dst, hipStream_t s);
 // dst[c * ld + r] = src[r * lds + c] (16-bit values, rows x cols).
 int launch_transpose_u16(const uint16_t *src, int rows, int cols, size_t lds, uint16_t *dst, size_t ld,
                          hipStream_t s);

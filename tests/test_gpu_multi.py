@@ -1,0 +1,251 @@
+"""Several prompts in one prefill (ppx_prefill_multi), each in its own cache.
+
+Each sequence's result is, by definition, that of its prompt run alone, and
+the pruned schedule generalises to one output row per sequence.  Checks:
+  * per-sequence logits vs the fp64 oracle's multi-sequence pass (itself
+    pinned to the scalar brute force per prompt): max-abs 2e-2, same top-1;
+  * K/V vs the oracle (|d| <= 1e-2 + one fp16 ulp) where the cache entry
+    depends on the row's own input (layer 0, every config; every layer of the
+    TinyLlama-shaped model, as in the single-prompt tests);
+  * rows land in their own cache only: layer 0's K/V are bit-identical to a
+    single-prompt prefill of the same prompt, and positions past each
+    prompt stay untouched;
+  * full E2B-like shapes: prompts of 512 and 2048 tokens in one call against
+    the stored oracle results of those prompts;
+  * one sequence is exactly ppx_prefill; argument errors change no cache.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_common import container, kv_within, logits_ok, oracle_model
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.fixture(scope="module")
+def ppx():
+    import prompt_prefill_cross_amd as p
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    p.lib()
+    return p
+
+
+_models = {}
+
+
+def engine_model(ppx, name):
+    if name not in _models:
+        _models.clear()
+        torch.cuda.synchronize()
+        _models[name] = ppx.Model(container(name))
+    return _models[name]
+
+
+def case(cfg, lens, starts, seed_off=0):
+    """Prompts of the given lengths cut from one long seeded prompt, and the
+    tokens that fill each cache before the call (positions 0 .. start-1)."""
+    base = synth.prompt(cfg, sum(lens) + sum(starts) + seed_off + 8)
+    prompts, pre, o = [], [], seed_off
+    for n, p0 in zip(lens, starts):
+        pre.append(base[o:o + p0])
+        o += p0
+        prompts.append(base[o:o + n])
+        o += n
+    return prompts, pre
+
+
+def engine_caches(ppx, mm, pre, n_ctx):
+    kvs = []
+    for t in pre:
+        kv = ppx.KVCache(mm, n_ctx)
+        if len(t):
+            mm.prefill(t, kv, n_ubatch=512)
+        kvs.append(kv)
+    return kvs
+
+
+def oracle_multi(cfg, prompts, pre, n_ctx, prune):
+    om = oracle_model(cfg)
+    okvs = []
+    for t in pre:
+        kv = oracle.KVState(om, n_ctx)
+        if len(t):
+            oracle.prefill(om, kv, t, prune=True)
+        okvs.append(kv)
+    lg = oracle.prefill_multi(om, okvs, prompts, prune=prune)
+    return lg, okvs
+
+
+def check_untouched(kv, end):
+    K, V = kv.kv_tensors()
+    if end < kv.n_ctx:
+        assert not torch.any(K[:, end:] != 0) and not torch.any(V[:, end:] != 0), "write past the prompt"
+
+
+@pytest.mark.parametrize("ub,prune", [(16, "auto"), (64, "auto"), (7, "off"), (512, "auto")])
+def test_tiny_multi_vs_oracle(ppx, ub, prune):
+    cfg, n_ctx = "tiny", 64
+    lens, starts = (13, 1, 30, 7), (0, 5, 0, 20)
+    prompts, pre = case(cfg, lens, starts)
+    ref, okvs = oracle_multi(cfg, prompts, pre, n_ctx, prune != "off")
+    mm = engine_model(ppx, cfg)
+    kvs = engine_caches(ppx, mm, pre, n_ctx)
+    lg = mm.prefill_multi(prompts, kvs, n_ubatch=ub, prune=prune).cpu().numpy()
+    torch.cuda.synchronize()
+    for s in range(len(lens)):
+        ok, d = logits_ok(lg[s], ref[s])
+        print(f"tiny multi ub={ub} prune={prune} seq {s}: logits max-abs {d:.3e}")
+        assert ok, (s, d)
+        end = starts[s] + lens[s]
+        assert kvs[s].n_pos == end
+        K, V = kvs[s].kv_tensors()
+        for got, want in ((K[0, :end], okvs[s].K[0, :end]), (V[0, :end], okvs[s].V[0, :end])):
+            okk, dk = kv_within(got.cpu().numpy(), want)
+            assert okk, (s, dk)
+        check_untouched(kvs[s], end)
+
+
+def test_tinyllama_multi_vs_oracle(ppx):
+    """No KV-shared layers (nothing to prune), eight query heads per KV head;
+    every layer's cache against the oracle."""
+    cfg, n_ctx = "tinyllama", 256
+    lens, starts = (100, 37, 200, 1), (0, 50, 0, 9)
+    prompts, pre = case(cfg, lens, starts)
+    ref, okvs = oracle_multi(cfg, prompts, pre, n_ctx, False)
+    mm = engine_model(ppx, cfg)
+    kvs = engine_caches(ppx, mm, pre, n_ctx)
+    lg = mm.prefill_multi(prompts, kvs, n_ubatch=128).cpu().numpy()
+    torch.cuda.synchronize()
+    for s in range(len(lens)):
+        ok, d = logits_ok(lg[s], ref[s])
+        print(f"tinyllama multi seq {s}: logits max-abs {d:.3e}")
+        assert ok, (s, d)
+        end = starts[s] + lens[s]
+        K, V = kvs[s].kv_tensors()
+        for got, want in ((K[:, :end], okvs[s].K[:, :end]), (V[:, :end], okvs[s].V[:, :end])):
+            okk, dk = kv_within(got.cpu().numpy(), want)
+            assert okk, (s, dk)
+        check_untouched(kvs[s], end)
+
+
+def test_e2b_multi_small_vs_oracle(ppx):
+    """E2B-like model (MQA, 20 KV-shared layers, per-layer embeddings): three
+    short prompts, one resuming at position 40, pruned to three rows."""
+    cfg, n_ctx = "e2b", 128
+    lens, starts = (37, 5, 1), (0, 40, 0)
+    prompts, pre = case(cfg, lens, starts)
+    ref, okvs = oracle_multi(cfg, prompts, pre, n_ctx, True)
+    mm = engine_model(ppx, cfg)
+    kvs = engine_caches(ppx, mm, pre, n_ctx)
+    lg = mm.prefill_multi(prompts, kvs, n_ubatch=512).cpu().numpy()
+    torch.cuda.synchronize()
+    for s in range(len(lens)):
+        ok, d = logits_ok(lg[s], ref[s])
+        print(f"e2b multi seq {s}: logits max-abs {d:.3e}")
+        assert ok, (s, d)
+        end = starts[s] + lens[s]
+        K, V = kvs[s].kv_tensors()
+        for got, want in ((K[0, :end], okvs[s].K[0, :end]), (V[0, :end], okvs[s].V[0, :end])):
+            okk, dk = kv_within(got.cpu().numpy(), want)
+            assert okk, (s, dk)
+
+
+def load_golden(name):
+    import json
+    path = os.path.join(GOLD, f"oracle_{name}.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"no stored oracle result {path} (tests/golden/make_goldens.py writes it)")
+    g = np.load(path)
+    return g, json.loads(str(g["meta"]))
+
+
+def test_e2b_multi_full_size_vs_stored_oracle(ppx):
+    """The stored oracle prompts of 512 and 2048 tokens in one call (ubatch
+    512: the rows of both share no ubatch here, the tail holds two rows)."""
+    gs = [load_golden("e2b_512"), load_golden("e2b_2048")]
+    mm = engine_model(ppx, "e2b")
+    prompts = [synth.prompt(meta["config"], meta["n"]) for _, meta in gs]
+    kvs = [ppx.KVCache(mm, meta["n"]) for _, meta in gs]
+    lg = mm.prefill_multi(prompts, kvs, n_ubatch=512).cpu().numpy()
+    torch.cuda.synchronize()
+    for s, (g, meta) in enumerate(gs):
+        ok, d = logits_ok(lg[s], g["logits"])
+        print(f"e2b multi {meta['n']}-token prompt: logits max-abs {d:.3e}")
+        assert ok, (s, d)
+        K, V = kvs[s].kv_tensors()
+        layers = torch.from_numpy(g["kv_layers"]).cuda()
+        pos = torch.from_numpy(g["kv_pos"]).cuda()
+        for got, want in ((K, g["K"]), (V, g["V"])):
+            okk, dk = kv_within(got[layers][:, pos].cpu().numpy(), want)
+            assert okk, (s, dk)
+
+
+def test_e2b_multi_matches_single_prompts(ppx):
+    """Eight prompts of mixed lengths sharing ubatches: every sequence's
+    logits agree with its own ppx_prefill, and layer 0's K/V (a function of
+    the row's embedding alone) are the same bytes."""
+    cfg = "e2b"
+    lens = (1, 17, 128, 255, 256, 300, 513, 64)
+    prompts, _ = case(cfg, lens, (0,) * len(lens))
+    n_ctx = 600
+    mm = engine_model(ppx, cfg)
+    kvs = [ppx.KVCache(mm, n_ctx) for _ in lens]
+    lg = mm.prefill_multi(prompts, kvs, n_ubatch=512).cpu().numpy()
+    torch.cuda.synchronize()
+    for s, t in enumerate(prompts):
+        kv1 = ppx.KVCache(mm, n_ctx)
+        l1 = mm.prefill(t, kv1, n_ubatch=512).cpu().numpy()
+        torch.cuda.synchronize()
+        ok, d = logits_ok(lg[s], l1)
+        print(f"e2b multi vs single, {lens[s]}-token prompt: logits max-abs {d:.3e}")
+        assert ok, (s, d)
+        Ka, Va = kvs[s].kv_tensors()
+        Kb, Vb = kv1.kv_tensors()
+        n = lens[s]
+        assert torch.equal(Ka[0, :n], Kb[0, :n]) and torch.equal(Va[0, :n], Vb[0, :n])
+        for got, want in ((Ka[:, :n], Kb[:, :n]), (Va[:, :n], Vb[:, :n])):
+            okk, dk = kv_within(got.cpu().numpy(), want.cpu().numpy())
+            assert okk, (s, dk)
+        check_untouched(kvs[s], n)
+        del kv1
+
+
+def test_multi_one_sequence_is_prefill(ppx):
+    mm = engine_model(ppx, "tiny")
+    toks = synth.prompt("tiny", 40)
+    kva, kvb = ppx.KVCache(mm, 64), ppx.KVCache(mm, 64)
+    la = mm.prefill(toks, kva, n_ubatch=16).clone()
+    lb = mm.prefill_multi([toks], [kvb], n_ubatch=16)[0]
+    torch.cuda.synchronize()
+    assert torch.equal(la, lb) and torch.equal(kva.buf, kvb.buf)
+
+
+def test_multi_errors_change_nothing(ppx):
+    mm = engine_model(ppx, "tiny")
+    kv1, kv2 = ppx.KVCache(mm, 16), ppx.KVCache(mm, 16)
+    mm.prefill([1, 2, 3], kv1)
+    before = (kv1.buf.clone(), kv2.buf.clone())
+    cases = [
+        (([[1, 2], [3]], [kv1, kv1]), {}, -1),         # one cache for two sequences
+        (([[1, 2], []], [kv1, kv2]), {}, -10),         # an empty prompt
+        (([[1, 2], [2048]], [kv1, kv2]), {}, -2),      # token out of range
+        (([[1] * 14, [3]], [kv1, kv2]), {}, -3),       # kv1 holds 3 positions: 3 + 14 > 16
+        (([[1, 2], [3]], [kv1, kv2]), {"n_seq_max": 1}, -1),
+    ]
+    for (prompts, kvs), kw, status in cases:
+        with pytest.raises(ppx.PPXError) as e:
+            mm.prefill_multi(prompts, kvs, n_ubatch=8, **kw)
+        assert e.value.status == status, (prompts, kw)
+    torch.cuda.synchronize()
+    assert kv1.n_pos == 3 and kv2.n_pos == 0
+    assert torch.equal(kv1.buf, before[0]) and torch.equal(kv2.buf, before[1])
+    lg = mm.prefill_multi([[4, 5], [6]], [kv1, kv2], n_ubatch=8)
+    torch.cuda.synchronize()
+    assert lg.shape == (2, mm.info["n_vocab"]) and kv1.n_pos == 5 and kv2.n_pos == 1
