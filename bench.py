@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--decode", type=int, default=32, help="tokens decoded after the main prompt (0 = none)")
     ap.add_argument("--no-reuse", dest="reuse", action="store_false",
                     help="skip the token-verified prefix-reuse timing")
+    ap.add_argument("--multi", default="16x128,8x256,4x512",
+                    help="multi-sequence prefills to report, KxN = K prompts of N tokens ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="prompt tokens of the oracle sample (0 = all)")
     ap.add_argument("--pmc-pass", action="store_true", help="one prefill + one calibration copy, then exit")
@@ -216,6 +218,53 @@ def prefix_reuse_pass(mm, kv, toks, ub, keep, reps=3):
             "total_ms": float(np.median(loads) + np.median(rests))}
 
 
+def multi_pass(ppx, mm, cfg, ub, shapes, reps=5):
+    """k prompts of n tokens in one ppx_prefill_multi call against the same k
+    prompts run one ppx_prefill after another (same stream, one timed region
+    each way)."""
+    import torch
+    import synth
+    V = mm.info["n_vocab"]
+    out = {}
+    for k, n in shapes:
+        base = synth.prompt(cfg, k * n)
+        prompts = [base[i * n:(i + 1) * n] for i in range(k)]
+        kvs = [ppx.KVCache(mm, n) for _ in range(k)]
+        lg_multi = torch.empty((k, V), dtype=torch.float32, device="cuda")
+        lg_one = torch.empty(V, dtype=torch.float32, device="cuda")
+
+        def run_multi():
+            for kv in kvs:
+                kv.clear()
+            mm.prefill_multi(prompts, kvs, n_ubatch=ub, logits=lg_multi)
+
+        def run_single():
+            for kv, t in zip(kvs, prompts):
+                kv.clear()
+                mm.prefill(t, kv, n_ubatch=ub, logits=lg_one)
+
+        res = {}
+        for name, fn in (("multi", run_multi), ("one_by_one", run_single)):
+            fn()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(reps):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                e1.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            res[name] = float(np.median(ts))
+        out[f"{k}x{n}"] = {"sequences": k, "tokens_each": n, "multi_ms": res["multi"],
+                           "one_by_one_ms": res["one_by_one"],
+                           "multi_tokens_per_s": k * n / res["multi"] * 1e3,
+                           "one_by_one_tokens_per_s": k * n / res["one_by_one"] * 1e3}
+        del kvs
+    return out
+
+
 def pmc_pass(mm, kv, toks, ub, prune):
     import torch
     kv.clear()
@@ -281,6 +330,14 @@ def main():
     if reuse:
         print(f"# prefix reuse: {reuse['reused']} of {reuse['prompt']} cached; load {reuse['load_ms']:.1f} ms + "
               f"prefill {reuse['prefill_rest_ms']:.2f} ms", file=sys.stderr, flush=True)
+    multi = None
+    if a.multi.strip():
+        shapes = [tuple(int(v) for v in x.split("x")) for x in a.multi.split(",") if x.strip()]
+        multi = multi_pass(ppx, mm, cfg, ub, shapes)
+        for key, r in multi.items():
+            print(f"# multi {key}: {r['multi_ms']:.2f} ms ({r['multi_tokens_per_s']:.0f} tok/s) vs one by one "
+                  f"{r['one_by_one_ms']:.2f} ms ({r['one_by_one_tokens_per_s']:.0f} tok/s)", file=sys.stderr,
+                  flush=True)
     dec = None
     if a.decode:
         dec = decode_pass(mm, kv, synth.prompt(cfg, a.n + a.decode + 2), ub, a.decode)
@@ -331,6 +388,7 @@ def main():
                           for n, (t, _) in results.items()},
         "decode": dec,
         "prefix_reuse": reuse,
+        "multi_sequence": multi,
         "ms_median": float(np.median(times)),
         "ms_std": float(np.std(times)),
     }
