@@ -199,15 +199,29 @@ def _check_prompt(m: OracleModel, kv: KVState, tokens: np.ndarray) -> None:
 
 
 def _run(m: OracleModel, kvs: list, prompts: list, prune: bool, n_ubatch: int | None,
-         trace: dict | None) -> np.ndarray:
+         trace: dict | None, layer_inp: dict | None = None, embeddings: list | None = None) -> np.ndarray:
     """The forward pass over the rows of all prompts, laid end to end in
-    prompt order; returns the logits of each prompt's last row."""
+    prompt order; returns the logits of each prompt's last row.
+
+    layer_inp: keys are layer indices il in [0, n_layer]; each value becomes
+    the hidden state entering layer il for every row ([rows][d], fp64;
+    il = n_layer is the final hidden state before the output norm).
+    embeddings: receives every row's output-normed final hidden state.  Both
+    need every row, so a pruned run may request only layers before the first
+    KV-shared one (the llama.cpp Gemma 4 prefill page, section 1: the
+    predicate forbids pruning when a layer from there on, or the embeddings,
+    are extracted)."""
     if len({id(kv) for kv in kvs}) != len(kvs):
         raise ValueError("each sequence needs its own cache")
     prompts = [np.asarray(t, dtype=np.int64) for t in prompts]
     for kv, t in zip(kvs, prompts):
         _check_prompt(m, kv, t)
     ls, L = m.n_layer_kv_from_start, m.n_layer
+    want = sorted(layer_inp) if layer_inp is not None else []
+    if any(il < 0 or il > L for il in want):
+        raise ValueError("layer index out of range")
+    if prune and 0 < ls < L and (embeddings is not None or any(il >= ls for il in want)):
+        raise ValueError("extraction from pruned layers needs every row")
     toks = np.concatenate(prompts)
     seq = np.concatenate([np.full(len(t), s, dtype=np.int64) for s, t in enumerate(prompts)])
     pos = np.concatenate([kv.n_pos + np.arange(len(t)) for kv, t in zip(kvs, prompts)])
@@ -218,6 +232,8 @@ def _run(m: OracleModel, kvs: list, prompts: list, prune: bool, n_ubatch: int | 
         if prune and il == ls and 0 < ls < L:
             x, pos, toks, seq = x[last], pos[last], toks[last], seq[last]
             last = np.arange(len(prompts))
+        if il in want:
+            layer_inp[il] = x.copy()
         W = _layer_weights(m, il)
         parts = []
         for s in range(0, x.shape[0], ub):
@@ -227,6 +243,10 @@ def _run(m: OracleModel, kvs: list, prompts: list, prune: bool, n_ubatch: int | 
         del W
         if trace is not None:
             trace[il] = x[last[-1]].copy()
+    if L in want:
+        layer_inp[L] = x.copy()
+    if embeddings is not None:
+        embeddings.append(rms_norm(x, m.f32("output_norm"), m.rms_eps))
     logits = np.stack([head(m, x[r]) for r in last])
     for kv, t in zip(kvs, prompts):
         kv.n_pos += len(t)
@@ -234,7 +254,8 @@ def _run(m: OracleModel, kvs: list, prompts: list, prune: bool, n_ubatch: int | 
 
 
 def prefill(m: OracleModel, kv: KVState, tokens, prune: bool = False,
-            n_ubatch: int | None = None, trace: dict | None = None) -> np.ndarray:
+            n_ubatch: int | None = None, trace: dict | None = None,
+            layer_inp: dict | None = None, embeddings: list | None = None) -> np.ndarray:
     """Run the prompt `tokens` from position kv.n_pos; return last-row logits.
 
     prune=False is the plain definition: all rows through all layers.
@@ -246,9 +267,10 @@ def prefill(m: OracleModel, kv: KVState, tokens, prune: bool = False,
     order (n_ubatch rows at a time, or all at once when None); each chunk
     writes its K/V before it attends, so it sees exactly the cache the
     ubatch-by-ubatch schedule would give it.  trace, if given, receives the
-    last row's hidden state after each layer.
+    last row's hidden state after each layer.  layer_inp / embeddings: the
+    extraction outputs described at _run.
     """
-    return _run(m, [kv], [tokens], prune, n_ubatch, trace)[0]
+    return _run(m, [kv], [tokens], prune, n_ubatch, trace, layer_inp, embeddings)[0]
 
 
 def prefill_multi(m: OracleModel, kvs: list, prompts: list, prune: bool = False,

@@ -80,15 +80,20 @@ def _silu(z):
     return z / (1.0 + math.exp(-z))
 
 
-def brute_prefill(M: BruteModel, tokens, n_ctx: int):
-    """Returns (logits list, K, V) with K[il][pos] = list of kv_dim floats."""
+def brute_prefill(M: BruteModel, tokens, n_ctx: int, hidden: dict | None = None):
+    """Returns (logits list, K, V) with K[il][pos] = list of kv_dim floats.
+
+    hidden, if given, receives "inp": the rows entering each layer il (index
+    L: the final rows), and "embd": every final row after the output norm."""
     L, Ls, H, KVH, hd = M.L, M.Ls, M.H, M.KVH, M.hd
     K = [[None] * n_ctx for _ in range(Ls)]
     V = [[None] * n_ctx for _ in range(Ls)]
     xs = []
     for t, tok in enumerate(tokens):
         xs.append([M.escale * w for w in M.t["tok_embd"][tok]])
+    inp = []
     for il in range(L):
+        inp.append([list(x) for x in xs])
         p = f"blk.{il}."
         g = M.t
         own = il < Ls
@@ -136,6 +141,9 @@ def brute_prefill(M: BruteModel, tokens, n_ctx: int):
                 x = [a + b for a, b in zip(x, _mv(g[p + "ple_up"], gg))]
             new.append(x)
         xs = new
+    if hidden is not None:
+        hidden["inp"] = inp + [[list(x) for x in xs]]
+        hidden["embd"] = [_rms(x, M.t["output_norm"][0], M.eps) for x in xs]
     hn = _rms(xs[-1], M.t["output_norm"][0], M.eps)
     Wout = M.t["tok_embd"] if M.tied else M.t["output"]
     logits = _mv(Wout, hn)

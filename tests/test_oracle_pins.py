@@ -274,6 +274,55 @@ def test_prefill_rejects_bad_input(tiny):
     assert kv.n_pos == 0
 
 
+# ------------------------------------------------------------------ extraction
+
+@pytest.mark.parametrize("cfg", [MICRO, MICRO_SW], ids=lambda c: c.name)
+def test_extraction_matches_scalar_brute_force(cfg):
+    """Every row's input to every layer (index L: the final rows) and every
+    row's output-normed final state, against the scalar brute force."""
+    buf = synth.build_model(cfg)
+    m = oracle.parse_model(buf)
+    n = 5
+    toks = synth.prompt(cfg, n)
+    inp = {il: None for il in range(m.n_layer + 1)}
+    emb = []
+    oracle.prefill(m, oracle.KVState(m, n), toks, n_ubatch=2, layer_inp=inp, embeddings=emb)
+    hb = {}
+    brute.brute_prefill(brute.BruteModel(buf.tobytes()), [int(t) for t in toks], n, hidden=hb)
+    for il in range(m.n_layer + 1):
+        np.testing.assert_allclose(inp[il], np.array(hb["inp"][il]), rtol=1e-9, atol=1e-9)
+    np.testing.assert_allclose(emb[0], np.array(hb["embd"]), rtol=1e-9, atol=1e-9)
+
+
+def test_extraction_invariants(tiny):
+    """Layer 0's input is the embedding; row r's final state is the last row
+    of the prompt's first r + 1 tokens (causality); the logits are the head
+    matrix times the last embedding; a pruned run extracts the owning layers'
+    inputs unchanged and refuses layers from the first shared one on."""
+    m, toks = tiny
+    n, L, ls = 24, m.n_layer, m.n_layer_kv_from_start
+    inp = {0: None, 1: None, L: None}
+    emb = []
+    lg = oracle.prefill(m, oracle.KVState(m, n), toks[:n], layer_inp=inp, embeddings=emb)
+    np.testing.assert_array_equal(inp[0], m.embd_scale * m.q4("tok_embd", rows=toks[:n]))
+    for r in (0, 9, n - 1):
+        tr = {}
+        oracle.prefill(m, oracle.KVState(m, n), toks[:r + 1], trace=tr)
+        np.testing.assert_allclose(inp[L][r], tr[L - 1], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(emb[0][r], F.rms_norm(tr[L - 1], m.f32("output_norm"), m.rms_eps),
+                                   rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lg, (m.q4("tok_embd") @ emb[0][-1]).astype(np.float32), rtol=1e-6, atol=1e-6)
+    own = {il: None for il in range(ls)}
+    oracle.prefill(m, oracle.KVState(m, n), toks[:n], prune=True, layer_inp=own)
+    assert ls == 2
+    np.testing.assert_array_equal(own[0], inp[0])
+    np.testing.assert_array_equal(own[1], inp[1])
+    with pytest.raises(ValueError):
+        oracle.prefill(m, oracle.KVState(m, n), toks[:n], prune=True, layer_inp={ls: None})
+    with pytest.raises(ValueError):
+        oracle.prefill(m, oracle.KVState(m, n), toks[:n], prune=True, embeddings=[])
+
+
 # ------------------------------------------------------------------ several sequences
 
 @pytest.mark.parametrize("prune", [False, True])
