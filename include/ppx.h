@@ -84,7 +84,8 @@ typedef struct {
     int prune;      /* PPX_PRUNE_AUTO: the predicate decides; OFF: every row
                        through every layer; ON: PPX_E_UNSUPPORTED if the
                        predicate is false                                       */
-    int embeddings; /* must be 0 (no embedding extraction in this engine)      */
+    int embeddings; /* 1: write every row's output-normed final hidden state to
+                       embd_out (the predicate then forbids pruning)            */
     int n_seq_max;  /* ppx_prefill: must be 1; ppx_prefill_multi: >= n_seq    */
     float *debug_hidden; /* NULL, or device fp32 [n_layer][d_model]: receives
                             the last row's hidden state after each layer       */
@@ -95,6 +96,17 @@ typedef struct {
                             receives the hidden state entering each layer for
                             every row that layer processes (pruned layers: the
                             last row only; other entries are left untouched)    */
+    const uint8_t *embeddings_layer_inp; /* NULL (none), or host flags
+                            [n_layer + 1]: flag il requests every row's hidden
+                            state entering layer il (il = n_layer: the final
+                            hidden state before the output norm); the
+                            predicate forbids pruning when a flag at
+                            il >= n_layer_kv_from_start is set              */
+    float *layer_inp_out; /* device fp32 [n_flagged][n_tokens][d_model]: the
+                            flagged layers' inputs in increasing layer order;
+                            required when any flag is set                    */
+    float *embd_out;     /* device fp32 [n_tokens][d_model]: required when
+                            embeddings != 0                                  */
 } ppx_prefill_params;
 
 #define PPX_MAX_UBATCH 4096
@@ -189,10 +201,15 @@ size_t ppx_workspace_bytes(const ppx_model *m, int n_ubatch, int n_ctx);
  * ppx_workspace_bytes, 256-byte aligned) is scratch for the call.  On
  * success kv's n_pos advances by n_tokens.  Errors are reported before any
  * work is queued and leave n_pos unchanged: PPX_E_EMPTY, PPX_E_TOKEN,
- * PPX_E_CTX, PPX_E_INVAL, PPX_E_UNSUPPORTED (prune ON while the predicate
- * is false, embeddings != 0, n_seq_max != 1), PPX_E_NOMEM (ws too small);
- * PPX_E_HIP if a launch fails.  The host token array is copied during the
- * call.  One call in flight per kv. */
+ * PPX_E_CTX, PPX_E_INVAL (also: an extraction without its output buffer),
+ * PPX_E_UNSUPPORTED (prune ON while the predicate is false, n_seq_max !=
+ * 1), PPX_E_NOMEM (ws too small); PPX_E_HIP if a launch fails.
+ * Extraction (embeddings, embeddings_layer_inp): the prune predicate of the
+ * llama.cpp Gemma 4 prefill page, section 1, is evaluated with the call's
+ * flags, so extracting the embeddings or a layer from the first KV-shared
+ * one on runs every row through every layer, while extracting only earlier
+ * layers keeps the prune.  The host token array is copied during the call.
+ * One call in flight per kv. */
 int ppx_prefill(ppx_model *m, ppx_kv *kv, const int32_t *tokens_host, int n_tokens,
                 const ppx_prefill_params *p, void *ws_dev, size_t ws_bytes, float *logits_dev,
                 void *hip_stream);
@@ -228,7 +245,7 @@ size_t ppx_workspace_bytes_multi(const ppx_model *m, int n_ubatch, int n_seq, lo
  * work is queued and leave every n_pos unchanged: PPX_E_EMPTY (a prompt of
  * no tokens), PPX_E_TOKEN, PPX_E_CTX, PPX_E_INVAL (NULL arguments, a cache
  * used twice or built for another model, n_seq out of range), PPX_E_UNSUPPORTED
- * (embeddings, debug outputs, prune ON while the predicate is false),
+ * (extraction, debug outputs, prune ON while the predicate is false),
  * PPX_E_NOMEM; PPX_E_HIP if a launch fails.  The host token arrays are read
  * during the call; the call may wait for the previous multi-sequence call of
  * the same model to have copied its tables.  One call in flight per kv. */

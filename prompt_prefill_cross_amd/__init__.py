@@ -52,7 +52,8 @@ class Timing(ctypes.Structure):
 
 class PrefillParams(ctypes.Structure):
     _fields_ = [("n_ubatch", c_int), ("prune", c_int), ("embeddings", c_int), ("n_seq_max", c_int),
-                ("debug_hidden", c_void_p), ("timing", POINTER(Timing)), ("debug_rows", c_void_p)]
+                ("debug_hidden", c_void_p), ("timing", POINTER(Timing)), ("debug_rows", c_void_p),
+                ("embeddings_layer_inp", c_void_p), ("layer_inp_out", c_void_p), ("embd_out", c_void_p)]
 
 
 class Seq(ctypes.Structure):
@@ -199,22 +200,49 @@ class Model:
 
     def prefill(self, tokens, kv: "KVCache", n_ubatch: int = 512, prune: str = "auto", logits=None,
                 debug_hidden=None, embeddings: int = 0, n_seq_max: int = 1, stream=None, timing=None,
-                debug_rows=None):
-        """Run `tokens` (int32) from kv.n_pos; return fp32 logits [n_vocab] of the last token."""
+                debug_rows=None, layer_flags=None, layer_inp_out=None, embd_out=None):
+        """Run `tokens` (int32) from kv.n_pos; return fp32 logits [n_vocab] of the last token.
+
+        layer_flags (n_layer + 1 truth values) / layer_inp_out and embeddings /
+        embd_out are the extraction outputs of ppx_prefill_params."""
         import torch
         toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
         if logits is None:
             logits = torch.empty(self.info["n_vocab"], dtype=torch.float32, device="cuda")
         ws = self.workspace(n_ubatch, kv.n_ctx) if n_ubatch >= 1 else torch.empty(256, dtype=torch.uint8,
                                                                                   device="cuda")
+        flags = None
+        if layer_flags is not None:
+            flags = np.ascontiguousarray(np.asarray(layer_flags, dtype=np.uint8).reshape(-1))
+            if flags.size != self.info["n_layer"] + 1:
+                raise ValueError("layer_flags needs n_layer + 1 entries")
         p = PrefillParams(n_ubatch, PRUNE[prune] if isinstance(prune, str) else int(prune), embeddings,
                           n_seq_max, c_void_p(debug_hidden.data_ptr()) if debug_hidden is not None else None,
                           ctypes.pointer(timing) if timing is not None else None,
-                          c_void_p(debug_rows.data_ptr()) if debug_rows is not None else None)
+                          c_void_p(debug_rows.data_ptr()) if debug_rows is not None else None,
+                          c_void_p(flags.ctypes.data) if flags is not None else None,
+                          c_void_p(layer_inp_out.data_ptr()) if layer_inp_out is not None else None,
+                          c_void_p(embd_out.data_ptr()) if embd_out is not None else None)
         st = lib().ppx_prefill(self._h, kv.handle, c_void_p(toks.ctypes.data), toks.shape[0], ctypes.byref(p),
                                _ptr(ws), ws.numel(), _ptr(logits), _stream(stream))
         _check(st, "ppx_prefill")
         return logits
+
+    def extract(self, tokens, kv: "KVCache", layers=(), embeddings: bool = False, n_ubatch: int = 512,
+                prune: str = "auto"):
+        """Prefill with extraction: returns (logits, {il: fp32 [n][d] input of
+        layer il for every row}, fp32 [n][d] output-normed final rows or None)."""
+        import torch
+        n = int(np.asarray(tokens).reshape(-1).shape[0])
+        L, d = self.info["n_layer"], self.info["d_model"]
+        want = sorted(set(int(il) for il in layers))
+        flags = np.zeros(L + 1, np.uint8)
+        flags[want] = 1
+        inp = torch.empty((max(len(want), 1), n, d), dtype=torch.float32, device="cuda")
+        emb = torch.empty((n, d), dtype=torch.float32, device="cuda") if embeddings else None
+        lg = self.prefill(tokens, kv, n_ubatch=n_ubatch, prune=prune, embeddings=int(bool(embeddings)),
+                          layer_flags=flags, layer_inp_out=inp if want else None, embd_out=emb)
+        return lg, {il: inp[j] for j, il in enumerate(want)}, emb
 
     def prefill_multi(self, prompts, kvs, n_ubatch: int = 512, prune: str = "auto", logits=None,
                       n_seq_max: int | None = None, stream=None, timing=None):

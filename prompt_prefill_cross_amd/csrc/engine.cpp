@@ -470,6 +470,16 @@ int enqueue_prefill(Ctx &c, const ppx_prefill_params *p, const int32_t *tok_dev,
             if (hipStreamWaitEvent(streams[k], ev[0], 0) != hipSuccess) return PPX_E_HIP;
     }
     auto kv_ev = [&](int u, int l) { return ev[(size_t)S + (size_t)u * L + l]; };
+    // extraction: the flagged layers' inputs, each in its own [n][d] slab
+    std::vector<int> slab(L + 1, -1);
+    int nslab = 0;
+    if (p->embeddings_layer_inp)
+        for (int il = 0; il <= L; ++il)
+            if (p->embeddings_layer_inp[il]) slab[il] = nslab++;
+    auto extract = [&](int il, const float *x, int M, int s0, hipStream_t s) -> int {
+        if (slab[il] < 0) return PPX_OK;
+        return launch_copy_f32(x, p->layer_inp_out + ((size_t)slab[il] * n + s0) * d, M * d, s);
+    };
 
     for (int u = 0; u < nub; ++u) {
         const int s0 = u * ub;
@@ -492,9 +502,16 @@ int enqueue_prefill(Ctx &c, const ppx_prefill_params *p, const int32_t *tok_dev,
         for (int il = 0; il < full_layers; ++il) {
             if (p->debug_rows)
                 PPX_TRY(launch_copy_f32(x, p->debug_rows + ((size_t)il * n + s0) * d, M * d, s));
+            PPX_TRY(extract(il, x, M, s0, s));
             PPX_TRY(layer_rows(c, il, M, s0, pos0));
             if (last && p->debug_hidden)
                 PPX_TRY(launch_copy_f32(x + (size_t)(M - 1) * d, p->debug_hidden + (size_t)il * d, d, s));
+        }
+        if (full_layers == L) {
+            // every row reached the end (the predicate keeps these off pruned runs)
+            PPX_TRY(extract(L, x, M, s0, s));
+            if (p->embeddings)
+                PPX_TRY(launch_rmsnorm_f32(x, m->out_norm, m->eps, M, d, p->embd_out + (size_t)s0 * d, s));
         }
         if (!last) continue;
         const float *x_last = x + (size_t)(M - 1) * d;
@@ -611,7 +628,11 @@ int prefill(ppx_model *m, ppx_kv *kv, const int32_t *tokens, int n, const ppx_pr
     if (n <= 0) return PPX_E_EMPTY;
     if (!tokens) return PPX_E_INVAL;
     const ppx_model_info &I = m->info;
-    if (p->embeddings != 0 || p->n_seq_max != 1) return PPX_E_UNSUPPORTED;
+    if (p->n_seq_max != 1) return PPX_E_UNSUPPORTED;
+    if (p->embeddings && !p->embd_out) return PPX_E_INVAL;
+    if (p->embeddings_layer_inp && !p->layer_inp_out)
+        for (int il = 0; il <= I.n_layer; ++il)
+            if (p->embeddings_layer_inp[il]) return PPX_E_INVAL;
     if (p->n_ubatch < 1 || p->n_ubatch > PPX_MAX_UBATCH) return PPX_E_INVAL;
     for (int i = 0; i < n; ++i)
         if (tokens[i] < 0 || tokens[i] >= I.n_vocab) return PPX_E_TOKEN;
@@ -626,7 +647,7 @@ int prefill(ppx_model *m, ppx_kv *kv, const int32_t *tokens, int n, const ppx_pr
     }
     if (ws_bytes < c.L.total) return PPX_E_NOMEM;
     const int L = I.n_layer, Ls = I.n_layer_kv_from_start, d = I.d_model;
-    const int can = predicate(L, Ls, p->embeddings, p->n_seq_max, nullptr, 1);
+    const int can = predicate(L, Ls, p->embeddings, p->n_seq_max, p->embeddings_layer_inp, 1);
     bool prune;
     if (p->prune == PPX_PRUNE_AUTO) prune = can;
     else if (p->prune == PPX_PRUNE_OFF) prune = false;
@@ -642,10 +663,13 @@ int prefill(ppx_model *m, ppx_kv *kv, const int32_t *tokens, int n, const ppx_pr
         std::fprintf(stderr, "[ppx] prefill %d tokens at position %d, ubatch %d, prune %s\n", n, p0, ub,
                      prune ? "on" : "off");
 
-    const bool graphable = !c.tm && !p->debug_rows && !p->debug_hidden && graphs_enabled();
+    bool extract = p->embeddings != 0;
+    if (p->embeddings_layer_inp)
+        for (int il = 0; il <= L; ++il) extract = extract || p->embeddings_layer_inp[il];
+    const bool graphable = !c.tm && !p->debug_rows && !p->debug_hidden && !extract && graphs_enabled();
     if (!graphable) {
-        // timing and debug outputs keep every launch on the caller's stream, in order
-        const bool serial = c.tm || p->debug_rows || p->debug_hidden;
+        // timing, debug and extraction outputs keep every launch on the caller's stream, in order
+        const bool serial = c.tm || p->debug_rows || p->debug_hidden || extract;
         hipStream_t streams[kSlots];
         PPX_TRY(slot_streams(m, s, false, streams));
         PPX_TRY(enqueue_prefill(c, p, tok_dev, n, p0, ub, prune, logits, streams, serial ? 1 : kSlots));
@@ -765,7 +789,7 @@ int prefill_multi(ppx_model *m, const ppx_seq *seqs, int k, const ppx_prefill_pa
     if (!m || !seqs || !p || !logits || !ws) return PPX_E_INVAL;
     if (k < 1 || k > PPX_MAX_SEQ) return PPX_E_INVAL;
     const ppx_model_info &I = m->info;
-    if (p->embeddings != 0) return PPX_E_UNSUPPORTED;
+    if (p->embeddings != 0 || p->embeddings_layer_inp) return PPX_E_UNSUPPORTED;
     if (p->debug_rows || p->debug_hidden) return PPX_E_UNSUPPORTED;
     if (p->n_seq_max < k) return PPX_E_INVAL;
     if (p->n_ubatch < 1 || p->n_ubatch > PPX_MAX_UBATCH) return PPX_E_INVAL;

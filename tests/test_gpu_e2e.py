@@ -152,7 +152,11 @@ def test_tiny_error_paths(ppx):
         mm.prefill(np.zeros(33, np.int32), kv)
     assert e.value.status == -3
     with pytest.raises(ppx.PPXError) as e:
-        mm.prefill([1, 2], kv, embeddings=1)
+        mm.prefill([1, 2], kv, embeddings=1)  # no output buffer for the embeddings
+    assert e.value.status == -1
+    with pytest.raises(ppx.PPXError) as e:
+        mm.prefill([1, 2], kv, embeddings=1, prune="on",
+                   embd_out=torch.empty((2, mm.info["d_model"]), device="cuda"))  # predicate false
     assert e.value.status == -7
     with pytest.raises(ppx.PPXError) as e:
         mm.prefill([1, 2], kv, n_seq_max=2)
