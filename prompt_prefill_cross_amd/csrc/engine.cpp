@@ -621,6 +621,46 @@ int run_graph(Ctx &c, const ppx_prefill_params *p, const int32_t *tok_dev, int n
     return hipGraphLaunch(exec, c.s) == hipSuccess ? PPX_OK : PPX_E_HIP;
 }
 
+// Replay the launch sequence recorded under `key` (everything the launches'
+// arguments depend on), or record it first on the model's private stream.
+// Up to kMaxGraphs such sequences are kept, least recently used first out.
+template <class F>
+int run_keyed_graph(Ctx &c, std::vector<long long> key, F &&enqueue) {
+    ppx_model *m = c.m;
+    for (auto &g : m->keyed_graphs)
+        if (g.key == key) {
+            g.last_use = ++m->graph_clock;
+            return hipGraphLaunch(g.exec, c.s) == hipSuccess ? PPX_OK : PPX_E_HIP;
+        }
+    if (!m->capture_stream && hipStreamCreateWithFlags(&m->capture_stream, hipStreamNonBlocking) != hipSuccess)
+        return PPX_E_HIP;
+    Ctx rc = c;
+    rc.s = m->capture_stream;
+    if (hipStreamBeginCapture(rc.s, hipStreamCaptureModeThreadLocal) != hipSuccess) return PPX_E_HIP;
+    const int st = enqueue(rc);
+    hipGraph_t graph = nullptr;
+    const hipError_t ec = hipStreamEndCapture(rc.s, &graph);
+    if (st != PPX_OK) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return st;
+    }
+    if (ec != hipSuccess || !graph) return PPX_E_HIP;
+    hipGraphExec_t exec = nullptr;
+    const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (ei != hipSuccess) return PPX_E_HIP;
+    if (m->keyed_graphs.size() >= kMaxGraphs) {
+        auto old = std::min_element(m->keyed_graphs.begin(), m->keyed_graphs.end(),
+                                    [](const ppx_model::KeyedGraph &x, const ppx_model::KeyedGraph &y) {
+                                        return x.last_use < y.last_use;
+                                    });
+        (void)hipGraphExecDestroy(old->exec);
+        m->keyed_graphs.erase(old);
+    }
+    m->keyed_graphs.push_back({std::move(key), exec, ++m->graph_clock});
+    return hipGraphLaunch(exec, c.s) == hipSuccess ? PPX_OK : PPX_E_HIP;
+}
+
 int prefill(ppx_model *m, ppx_kv *kv, const int32_t *tokens, int n, const ppx_prefill_params *p, void *ws,
             size_t ws_bytes, float *logits, hipStream_t s) {
     if (!m || !kv || !p || !logits || !ws) return PPX_E_INVAL;
@@ -949,67 +989,83 @@ int prefill_multi(ppx_model *m, const ppx_seq *seqs, int k, const ppx_prefill_pa
     if (log_enabled())
         std::fprintf(stderr, "[ppx] prefill of %d sequences, %ld rows, ubatch %d, prune %s\n", k, T, ub,
                      prune ? "on" : "off");
-    float *x = c.sl<float>(c.L.x);
-    const int full_layers = prune ? Ls : L;
-    for (const Ub &U : ubs) {
+    // the launches (tables and tokens are already in device memory, so a
+    // recorded sequence serves any prompts of the same shape)
+    auto enqueue = [&](Ctx &c) -> int {
+        float *x = c.sl<float>(c.L.x);
+        const int full_layers = prune ? Ls : L;
+        for (const Ub &U : ubs) {
+            Ctx::Rows R;
+            R.tok = D32(ML.tok) + U.u0;
+            R.pos = D32(ML.pos) + U.u0;
+            R.seq = D32(ML.seq) + U.u0;
+            R.kv = dkv;
+            R.nseq = k;
+            R.wg = dwg + U.wg0;
+            R.nwg = U.nwg;
+            R.split = U.split;
+            R.vis = U.vis;
+            c.rows = &R;
+            PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_embed(m->tok, R.tok, U.M, m->embd_scale, x, c.s));
+            for (int il = 0; il < full_layers; ++il) PPX_TRY(layer_rows(c, il, U.M, 0, 0));
+            if (U.npairs) PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_gather_rows(x, d, dpairs + U.pair0, U.npairs, xk, c.s));
+        }
+        PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_copy_f32(xk, x, k * d, c.s));
         Ctx::Rows R;
-        R.tok = D32(ML.tok) + U.u0;
-        R.pos = D32(ML.pos) + U.u0;
-        R.seq = D32(ML.seq) + U.u0;
+        R.tok = D32(ML.ttok);
+        R.pos = D32(ML.tpos);
+        R.seq = D32(ML.tseq);
         R.kv = dkv;
         R.nseq = k;
-        R.wg = dwg + U.wg0;
-        R.nwg = U.nwg;
-        R.split = U.split;
-        R.vis = U.vis;
+        R.wg = dwg + tail.wg0;
+        R.nwg = tail.nwg;
+        R.split = tail.split;
+        R.vis = tail.vis;
         c.rows = &R;
-        PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_embed(m->tok, R.tok, U.M, m->embd_scale, x, s));
-        for (int il = 0; il < full_layers; ++il) PPX_TRY(layer_rows(c, il, U.M, 0, 0));
-        if (U.npairs) PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_gather_rows(x, d, dpairs + U.pair0, U.npairs, xk, s));
-    }
-    PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_copy_f32(xk, x, k * d, s));
-    Ctx::Rows R;
-    R.tok = D32(ML.ttok);
-    R.pos = D32(ML.tpos);
-    R.seq = D32(ML.tseq);
-    R.kv = dkv;
-    R.nseq = k;
-    R.wg = dwg + tail.wg0;
-    R.nwg = tail.nwg;
-    R.split = tail.split;
-    R.vis = tail.vis;
-    c.rows = &R;
-    if (prune)
-        for (int il = Ls; il < L; ++il) PPX_TRY(layer_rows(c, il, k, 0, 0));
-    // the head of the k rows as one GEMM (the output matrix is read once)
-    __half *a16 = c.sl<__half>(c.L.a16);
-    PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_rmsnorm_f16(x, m->out_norm, m->eps, k, d, a16, s));
-    GemmArgs gh = c.gemm();
-    gh.A = a16;
-    gh.lda = d;
-    gh.M = k;
-    gh.W = m->out;
-    gh.epi = EPI_F32;
-    gh.out_f32 = logits;
-    int st = PPX_OK;
-    {
-        hipEvent_t ev0 = c.begin();
-        st = launch_gemm(gh, s);
-        if (st == PPX_E_UNSUPPORTED) {
-            // an output width the MFMA tiles do not divide: one fp32 row at a time
-            st = PPX_OK;
-            for (int q = 0; q < k && st == PPX_OK; ++q) {
-                GemvArgs gv = gemv_base(c, x + (size_t)q * d, m->out, GV_F32, logits + (size_t)q * I.n_vocab);
-                gv.norm_g = m->out_norm;
-                gv.eps = m->eps;
-                st = launch_gemv(gv, s);
+        if (prune)
+            for (int il = Ls; il < L; ++il) PPX_TRY(layer_rows(c, il, k, 0, 0));
+        // the head of the k rows as one GEMM (the output matrix is read once)
+        __half *a16 = c.sl<__half>(c.L.a16);
+        PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_rmsnorm_f16(x, m->out_norm, m->eps, k, d, a16, c.s));
+        GemmArgs gh = c.gemm();
+        gh.A = a16;
+        gh.lda = d;
+        gh.M = k;
+        gh.W = m->out;
+        gh.epi = EPI_F32;
+        gh.out_f32 = logits;
+        int st = PPX_OK;
+        {
+            hipEvent_t ev0 = c.begin();
+            st = launch_gemm(gh, c.s);
+            if (st == PPX_E_UNSUPPORTED) {
+                // an output width the MFMA tiles do not divide: one fp32 row at a time
+                st = PPX_OK;
+                for (int q = 0; q < k && st == PPX_OK; ++q) {
+                    GemvArgs gv = gemv_base(c, x + (size_t)q * d, m->out, GV_F32, logits + (size_t)q * I.n_vocab);
+                    gv.norm_g = m->out_norm;
+                    gv.eps = m->eps;
+                    st = launch_gemv(gv, c.s);
+                }
             }
+            PPX_TRY(st);
+            c.end(PPX_PHASE_GEMM, ev0);
         }
-        PPX_TRY(st);
-        c.end(PPX_PHASE_GEMM, ev0);
+        c.rows = nullptr;
+        return PPX_OK;
+    };
+    if (!c.tm && graphs_enabled()) {
+        std::vector<long long> key = {(long long)(uintptr_t)wsb, (long long)(uintptr_t)logits, T, ub, k, prune,
+                                      nctx_max, (long long)ubs.size(), tail.nwg, tail.split.kc, tail.split.nkc};
+        for (const Ub &U : ubs) {
+            const long long v[] = {U.M, (long long)U.wg0, U.nwg, U.split.kc, U.split.nkc, U.pair0, U.npairs};
+            key.insert(key.end(), v, v + 7);
+        }
+        PPX_TRY(run_keyed_graph(c, std::move(key), enqueue));
+    } else {
+        PPX_TRY(enqueue(c));
     }
     if (c.tm) c.tm->gemm_flop += 2.0 * k * (double)m->out.N * m->out.K;
-    c.rows = nullptr;
     PPX_TRY(c.finish());
     for (int q = 0; q < k; ++q) seqs[q].kv->n_pos += seqs[q].n_tokens;
     return PPX_OK;

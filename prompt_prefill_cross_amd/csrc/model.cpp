@@ -367,6 +367,7 @@ void model_free(ppx_model *m) {
     if (m->rope) (void)hipFree(m->rope);
     for (hipEvent_t e : m->events) (void)hipEventDestroy(e);
     for (auto &g : m->graphs) (void)hipGraphExecDestroy(g.exec);
+    for (auto &g : m->keyed_graphs) (void)hipGraphExecDestroy(g.exec);
     if (m->capture_stream) (void)hipStreamDestroy(m->capture_stream);
     for (hipStream_t st : m->aux_streams) (void)hipStreamDestroy(st);
     for (hipStream_t st : m->capture_aux) (void)hipStreamDestroy(st);

@@ -80,6 +80,13 @@ struct ppx_model {
         unsigned long long last_use = 0;
     };
     std::vector<Graph> graphs;
+    // recorded multi-sequence launch sequences, keyed by their shape
+    struct KeyedGraph {
+        std::vector<long long> key;
+        hipGraphExec_t exec = nullptr;
+        unsigned long long last_use = 0;
+    };
+    std::vector<KeyedGraph> keyed_graphs;
     unsigned long long graph_clock = 0;
     hipStream_t capture_stream = nullptr;  // recording only; graphs run on the caller's stream
     std::vector<hipStream_t> aux_streams;  // ubatches in flight, direct launches

@@ -217,6 +217,34 @@ def test_e2b_multi_matches_single_prompts(ppx):
         del kv1
 
 
+def test_multi_replay_with_new_prompts_and_caches(ppx):
+    """The first call of a shape records its launches and later calls replay
+    them; every replay must read its own prompts and its own caches (they
+    reach the kernels through device tables) and equal direct launches
+    (timing mode never records) bit for bit."""
+    mm = engine_model(ppx, "e2b")
+    V = mm.info["n_vocab"]
+    lens, ub = (40, 17, 90), 64
+    rng = np.random.default_rng(5)
+    sets = [[rng.integers(0, V, n).astype(np.int32) for n in lens] for _ in range(3)]
+    caches = [[ppx.KVCache(mm, 128) for _ in lens] for _ in sets]
+    logits = torch.empty((len(lens), V), dtype=torch.float32, device="cuda")
+    replayed = []
+    for prompts, kvs in zip(sets, caches):
+        lg = mm.prefill_multi(prompts, kvs, n_ubatch=ub, logits=logits).clone()
+        replayed.append((lg, [kv.buf.clone() for kv in kvs]))
+    torch.cuda.synchronize()
+    for prompts, kvs, (got, bufs) in zip(sets, caches, replayed):
+        for kv in kvs:
+            kv.clear()
+        direct = mm.prefill_multi(prompts, kvs, n_ubatch=ub, timing=ppx.Timing())
+        torch.cuda.synchronize()
+        assert torch.equal(got, direct)
+        for kv, b in zip(kvs, bufs):
+            assert torch.equal(kv.buf, b)
+    assert not torch.equal(replayed[1][0], replayed[2][0])
+
+
 def test_multi_one_sequence_is_prefill(ppx):
     mm = engine_model(ppx, "tiny")
     toks = synth.prompt("tiny", 40)
