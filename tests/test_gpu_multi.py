@@ -245,6 +245,44 @@ def test_multi_replay_with_new_prompts_and_caches(ppx):
     assert not torch.equal(replayed[1][0], replayed[2][0])
 
 
+@pytest.mark.parametrize("ub", [16, 1])
+def test_tiny_multi_most_sequences(ppx, ub):
+    """PPX_MAX_SEQ (64) prompts of 1-5 tokens: the gathered tail is wider than
+    the ubatch (16) or every ubatch is one row (1), and 64 rows exceed the
+    head's one-tile path.  Every sequence's logits vs its own single-prompt
+    ppx_prefill (the logit bound), its layer-0 K/V vs the oracle; 65 prompts
+    fail.  (The logits are not held to the oracle here: on this model prompts
+    of two tokens are ill-conditioned for fp16 operands, see
+    test_conditioning.py, and the single-prompt path misses the bound by the
+    same amount.)"""
+    cfg, n_ctx = "tiny", 8
+    rng = np.random.default_rng(64)
+    lens = tuple(int(v) for v in rng.integers(1, 6, 64))
+    prompts, pre = case(cfg, lens, (0,) * 64)
+    ref, okvs = oracle_multi(cfg, prompts, pre, n_ctx, True)
+    mm = engine_model(ppx, cfg)
+    kvs = [ppx.KVCache(mm, n_ctx) for _ in lens]
+    lg = mm.prefill_multi(prompts, kvs, n_ubatch=ub).cpu().numpy()
+    torch.cuda.synchronize()
+    worst = worst_oracle = 0.0
+    for s, n in enumerate(lens):
+        one = mm.prefill(prompts[s], ppx.KVCache(mm, n_ctx), n_ubatch=16).cpu().numpy()
+        ok, d = logits_ok(lg[s], one)
+        worst = max(worst, d)
+        worst_oracle = max(worst_oracle, float(np.abs(lg[s] - ref[s]).max()))
+        assert ok, (s, d)
+        assert kvs[s].n_pos == n
+        K, V = kvs[s].kv_tensors()
+        for got, want in ((K[0, :n], okvs[s].K[0, :n]), (V[0, :n], okvs[s].V[0, :n])):
+            okk, dk = kv_within(got.cpu().numpy(), want)
+            assert okk, (s, dk)
+    print(f"64 tiny prompts, ubatch {ub}: worst logits max-abs vs single prompts {worst:.3e}, "
+          f"vs the oracle {worst_oracle:.3e}")
+    with pytest.raises(ppx.PPXError) as e:
+        mm.prefill_multi([[1]] * 65, [ppx.KVCache(mm, 4) for _ in range(65)], n_ubatch=ub)
+    assert e.value.status == -1
+
+
 def test_multi_one_sequence_is_prefill(ppx):
     mm = engine_model(ppx, "tiny")
     toks = synth.prompt("tiny", 40)
