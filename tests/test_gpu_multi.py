@@ -305,6 +305,10 @@ def test_multi_errors_change_nothing(ppx):
         (([[1] * 14, [3]], [kv1, kv2]), {}, -3),       # kv1 holds 3 positions: 3 + 14 > 16
         (([[1, 2], [3]], [kv1, kv2]), {"n_seq_max": 1}, -1),
     ]
+    lib, h = ppx.lib(), mm.handle
+    assert lib.ppx_workspace_bytes_multi(h, 8, 2, 10, 16) >= lib.ppx_workspace_bytes(h, 8, 16) > 0
+    for args in ((0, 2, 10, 16), (8, 0, 10, 16), (8, 65, 10, 16), (8, 2, 0, 16), (8, 2, 10, 0)):
+        assert lib.ppx_workspace_bytes_multi(h, *args) == 0, args
     for (prompts, kvs), kw, status in cases:
         with pytest.raises(ppx.PPXError) as e:
             mm.prefill_multi(prompts, kvs, n_ubatch=8, **kw)
