@@ -420,19 +420,30 @@ __global__ __launch_bounds__(C::NT) void k_q4gemm_p(GemmArgs a) {
     auto step = [&](int s, const h8 (&bc)[2][C::TN], h8 (&bn)[2][C::TN]) {
         const h8 *st = ring + (s % C::DEPTH) * C::STAGE_UNITS;
         const h8 *sn = ring + ((s + 1) % C::DEPTH) * C::STAGE_UNITS;
+        // the A fragments of the two 32-wide halves in turn: the second half's
+        // reads are in flight during the first half's MFMAs, and only one half
+        // is held at a time (with both, the 8 x 3 wave tile spills registers)
         const h8 *as = st + g * C::AFR * 64 + lane;
-        h8 af[2][C::TM];
+        h8 af[C::TM];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < C::TM; ++i) af[kb][i] = as[(kb * C::TM + i) * 64];
+        for (int i = 0; i < C::TM; ++i) af[i] = as[i * 64];
         decode(sn, bn);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb) {
+            h8 an[C::TM];
+            if (kb == 0) {
+#pragma unroll
+                for (int i = 0; i < C::TM; ++i) an[i] = as[(C::TM + i) * 64];
+            }
 #pragma unroll
             for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-                for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma16(af[kb][i], bc[kb][j], acc[i][j]);
+                for (int j = 0; j < C::TN; ++j) acc[i][j] = mfma16(af[i], bc[kb][j], acc[i][j]);
+            if (kb == 0) {
+#pragma unroll
+                for (int i = 0; i < C::TM; ++i) af[i] = an[i];
+            }
+        }
         if (s + 1 < nkg) lds_barrier();
     };
     h8 bA[2][C::TN], bB[2][C::TN];
