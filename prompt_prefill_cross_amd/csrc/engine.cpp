@@ -113,6 +113,7 @@ struct Ctx {
         int nwg = 0;
         AttnSplit split;
         double vis = 0;  // causal (query, key) pairs of the batch (timing only)
+        bool gathered = false;  // the sequences' output rows, one each
     };
     const Rows *rows = nullptr;
     // K/V ordering between ubatches on different streams: after writing layer
@@ -133,6 +134,7 @@ struct Ctx {
         GemmArgs g;
         g.part = sl<float>(L.gpart);
         g.part_floats = L.gpart_floats;
+        g.few_rows = rows && rows->gathered;
         return g;
     }
 
@@ -1021,6 +1023,7 @@ int prefill_multi(ppx_model *m, const ppx_seq *seqs, int k, const ppx_prefill_pa
         R.nwg = tail.nwg;
         R.split = tail.split;
         R.vis = tail.vis;
+        R.gathered = true;
         c.rows = &R;
         if (prune)
             for (int il = Ls; il < L; ++il) PPX_TRY(layer_rows(c, il, k, 0, 0));

@@ -159,6 +159,9 @@ struct GemmArgs {
     const int32_t *row_pos = nullptr;
     const int32_t *row_seq = nullptr;
     const KVRef *seq_kv = nullptr;
+    // the gathered output rows of several sequences: tiles chosen by row count
+    // (other calls use plans that do not depend on M)
+    bool few_rows = false;
     // K split over workgroups: fp32 partial tiles, summed in split order by a
     // second kernel that applies the epilogue.  Null: no split.
     float *part = nullptr;
