@@ -791,14 +791,14 @@ struct Plan {
 // ways inside the workgroup, so that 512 short chains run instead of 64 long
 // ones; K = 256 the 32-row tiles of Q and O.  Otherwise the plan does not
 // depend on M, so a row's result does not depend on the ubatch size.  The
-// gathered output rows of several sequences (at most 16, GemmArgs::few_rows)
+// gathered output rows of several sequences (at most 64, GemmArgs::few_rows)
 // take the single 16 x 16 tiles whatever the shape (16 x 32 where the RoPE
-// epilogue needs column pairs), so the weights stream once over N / 16
-// workgroups instead of a few dozen tall tiles with idle rows; measured
-// 0.4 ms faster on the multi-sequence prefills (4 x 512, 16 x 128 and
-// 2 x 1024 tokens).
+// epilogue needs column pairs), so the weights stream over N / 16 workgroups
+// per 16 rows instead of a few dozen tall tiles with idle rows; measured
+// 0.4-0.5 ms faster on multi-sequence prefills of 2048 tokens in 2 to 32
+// prompts.
 Plan plan_for(int M, int N, int K, bool few = false) {
-    if (few && M <= 16) return {7, K >= 4096 ? 4 : 1};  // a few gathered rows: 16-row tiles, many workgroups
+    if (few && M <= 64) return {7, K >= 4096 ? 4 : 1};  // a few gathered rows: 16-row tiles, many workgroups
     if (N >= 8192) return {N % 192 == 0 ? 0 : 1, 1};
     if (K >= 4096) return {N % 192 == 0 ? 2 : 3, 4};
     if (N <= 512) return {7, 1};
@@ -820,7 +820,7 @@ int launch_gemm(const GemmArgs &a, hipStream_t s) {
     if (a.W.N % 128 || a.W.K % 256 || !a.A) return PPX_E_UNSUPPORTED;
     if (a.norm_out && (a.epi != EPI_ADD || !a.norm_g || a.W.N > RAN_MAX_CHUNKS * 8 * 256)) return PPX_E_UNSUPPORTED;
     Plan p = plan_for(a.M, a.W.N, a.W.K, a.few_rows);
-    if (a.few_rows && a.M <= 16 && a.epi == EPI_QKV) p = {8, 1};  // RoPE pairs need two column groups per wave
+    if (a.few_rows && a.M <= 64 && a.epi == EPI_QKV) p = {8, 1};  // RoPE pairs need two column groups per wave
     int st = launch_plan(a, p.cfg, p.S, s);
     bool normed = st == PPX_OK && p.S > 1 && p.S <= RAN_MAX_SPLIT && a.norm_out;  // the split's reduction normalised too
     if (st == PPX_E_UNSUPPORTED && p.S > 1) st = launch_plan(a, p.cfg, 1, s);  // no split workspace given
