@@ -124,9 +124,22 @@ typedef struct {
 int ppx_model_load(const void *container, size_t bytes, void *hip_stream, ppx_model **out);
 /* Same, reading the container from a file (PPX_E_IO if it cannot be read). */
 int ppx_model_load_file(const char *path, void *hip_stream, ppx_model **out);
+/* Device bytes the repacked weights of a container need (host only: the
+ * container is parsed and laid out, nothing touches the GPU); 0 if the
+ * container is invalid or unsupported. */
+size_t ppx_model_weight_bytes(const void *container, size_t bytes);
+/* As ppx_model_load, with the repacked weights placed in caller-owned device
+ * memory (a torch tensor, say): weights_dev 256-byte aligned, weights_bytes
+ * >= ppx_model_weight_bytes.  The buffer must outlive the model and is not
+ * freed by ppx_model_free; the library still allocates the small RoPE table
+ * of each context length it meets.  Errors: those of ppx_model_load, and
+ * PPX_E_INVAL (NULL or misaligned weights_dev), PPX_E_NOMEM (too small). */
+int ppx_model_load_into(const void *container, size_t bytes, void *weights_dev, size_t weights_bytes,
+                        void *hip_stream, ppx_model **out);
 void ppx_model_free(ppx_model *m);
 int ppx_model_get_info(const ppx_model *m, ppx_model_info *out);
-/* Device bytes the library holds for the model's weights and tables. */
+/* Device bytes of the model's repacked weights (the library's allocation, or
+ * the part of the caller's buffer in use after ppx_model_load_into). */
 size_t ppx_model_device_bytes(const ppx_model *m);
 
 /* ---------------------------------------------------------------- KV cache */

@@ -64,6 +64,8 @@ class Seq(ctypes.Structure):
 SIGNATURES = [
     ("ppx_model_load", c_int, [c_void_p, c_size_t, c_void_p, POINTER(c_void_p)]),
     ("ppx_model_load_file", c_int, [c_char_p, c_void_p, POINTER(c_void_p)]),
+    ("ppx_model_weight_bytes", c_size_t, [c_void_p, c_size_t]),
+    ("ppx_model_load_into", c_int, [c_void_p, c_size_t, c_void_p, c_size_t, c_void_p, POINTER(c_void_p)]),
     ("ppx_model_free", None, [c_void_p]),
     ("ppx_model_get_info", c_int, [c_void_p, POINTER(ModelInfo)]),
     ("ppx_model_device_bytes", c_size_t, [c_void_p]),
@@ -156,15 +158,31 @@ def kvfile_validate(path, n_layers: int, kv_dim: int, n_pos: int, n_ctx: int):
 class Model:
     """A loaded model: `Model(container)` with a numpy uint8 array / bytes, or a path."""
 
-    def __init__(self, src, stream=None):
+    def __init__(self, src, stream=None, torch_weights: bool = False):
+        """torch_weights: place the repacked weights in a torch uint8 tensor
+        (ppx_model_load_into) instead of library-allocated device memory."""
         self._h = c_void_p()
+        self._weights = None
         L = lib()
         if isinstance(src, (str, os.PathLike)):
-            st = L.ppx_model_load_file(os.fsencode(src), _stream(stream), ctypes.byref(self._h))
-        else:
+            if torch_weights:
+                with open(src, "rb") as f:
+                    src = f.read()
+            else:
+                st = L.ppx_model_load_file(os.fsencode(src), _stream(stream), ctypes.byref(self._h))
+        if not isinstance(src, (str, os.PathLike)):
             buf = np.ascontiguousarray(np.frombuffer(src, dtype=np.uint8) if not isinstance(src, np.ndarray)
                                        else src.view(np.uint8).reshape(-1))
-            st = L.ppx_model_load(c_void_p(buf.ctypes.data), buf.nbytes, _stream(stream), ctypes.byref(self._h))
+            if torch_weights:
+                import torch
+                need = L.ppx_model_weight_bytes(c_void_p(buf.ctypes.data), buf.nbytes)
+                if need == 0:
+                    raise PPXError(-5, "ppx_model_weight_bytes: invalid container")
+                self._weights = torch.empty(need, dtype=torch.uint8, device="cuda")
+                st = L.ppx_model_load_into(c_void_p(buf.ctypes.data), buf.nbytes, _ptr(self._weights), need,
+                                           _stream(stream), ctypes.byref(self._h))
+            else:
+                st = L.ppx_model_load(c_void_p(buf.ctypes.data), buf.nbytes, _stream(stream), ctypes.byref(self._h))
         _check(st, "ppx_model_load")
         info = ModelInfo()
         _check(L.ppx_model_get_info(self._h, ctypes.byref(info)), "ppx_model_get_info")

@@ -11,7 +11,8 @@
 
 namespace ppx {
 bool log_enabled();
-int model_load(const uint8_t *b, size_t n, hipStream_t stream, ppx_model **out);
+int model_load(const uint8_t *b, size_t n, hipStream_t stream, void *weights_dev, size_t weights_bytes,
+               size_t *need_bytes, ppx_model **out);
 int ensure_rope(ppx_model *m, int n_ctx);
 void model_free(ppx_model *m);
 
@@ -1260,7 +1261,24 @@ extern "C" {
 int ppx_model_load(const void *container, size_t bytes, void *hip_stream, ppx_model **out) {
     if (!container || !out) return PPX_E_INVAL;
     *out = nullptr;
-    return model_load(static_cast<const uint8_t *>(container), bytes, (hipStream_t)hip_stream, out);
+    return model_load(static_cast<const uint8_t *>(container), bytes, (hipStream_t)hip_stream, nullptr, 0, nullptr,
+                      out);
+}
+
+size_t ppx_model_weight_bytes(const void *container, size_t bytes) {
+    if (!container) return 0;
+    size_t need = 0;
+    if (model_load(static_cast<const uint8_t *>(container), bytes, nullptr, nullptr, 0, &need, nullptr) != PPX_OK)
+        return 0;
+    return need;
+}
+
+int ppx_model_load_into(const void *container, size_t bytes, void *weights_dev, size_t weights_bytes,
+                        void *hip_stream, ppx_model **out) {
+    if (!container || !out || !weights_dev) return PPX_E_INVAL;
+    *out = nullptr;
+    return model_load(static_cast<const uint8_t *>(container), bytes, (hipStream_t)hip_stream, weights_dev,
+                      weights_bytes, nullptr, out);
 }
 
 int ppx_model_load_file(const char *path, void *hip_stream, ppx_model **out) {
@@ -1273,7 +1291,7 @@ int ppx_model_load_file(const char *path, void *hip_stream, ppx_model **out) {
     std::vector<uint8_t> buf((size_t)n);
     f.seekg(0);
     if (!f.read(reinterpret_cast<char *>(buf.data()), n)) return PPX_E_IO;
-    return model_load(buf.data(), buf.size(), (hipStream_t)hip_stream, out);
+    return model_load(buf.data(), buf.size(), (hipStream_t)hip_stream, nullptr, 0, nullptr, out);
 }
 
 void ppx_model_free(ppx_model *m) { model_free(m); }

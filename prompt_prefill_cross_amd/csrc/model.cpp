@@ -134,7 +134,12 @@ void repack_rows(const RepackJob &j, uint8_t *host) {
 
 }  // namespace
 
-int model_load(const uint8_t *b, size_t n, hipStream_t stream, ppx_model **out) {
+// weights_dev: caller-owned device memory of weights_bytes bytes for the
+// repacked weights (null: the library allocates it).  With out == null only
+// the layout is planned and *need_bytes receives its size; nothing touches
+// the GPU.
+int model_load(const uint8_t *b, size_t n, hipStream_t stream, void *weights_dev, size_t weights_bytes,
+               size_t *need_bytes, ppx_model **out) {
     Parsed p;
     int st = parse(b, n, p);
     if (st) return st;
@@ -277,20 +282,32 @@ int model_load(const uint8_t *b, size_t n, hipStream_t stream, ppx_model **out) 
         }
     }
 
+    if (need_bytes) *need_bytes = ar.used;
+    if (!out) return PPX_OK;
+    if (weights_dev && ((reinterpret_cast<uintptr_t>(weights_dev) & 255) != 0)) return PPX_E_INVAL;
+    if (weights_dev && weights_bytes < ar.used) return PPX_E_NOMEM;
+
     // ---- build the host image and upload it
     std::vector<uint8_t> host(ar.used);
     for (const RepackJob &j : jobs) repack_rows(j, host.data());
     for (auto &f : f32s) std::memcpy(host.data() + f.off, b + f.t->offset, f.t->cols * 4);
     if (E) std::memcpy(host.data() + ple_off, b + ple->offset, (size_t)V * (L * E / 32) * 18);
 
-    if (hipMalloc(&m->dev, ar.used) != hipSuccess) {
-        (void)hipGetLastError();
-        return PPX_E_NOMEM;
+    if (weights_dev) {
+        m->dev = weights_dev;
+        m->dev_owned = false;
+    } else {
+        if (hipMalloc(&m->dev, ar.used) != hipSuccess) {
+            (void)hipGetLastError();
+            return PPX_E_NOMEM;
+        }
+        m->dev_owned = true;
     }
     m->dev_bytes = ar.used;
     if (hipMemcpyAsync(m->dev, host.data(), ar.used, hipMemcpyHostToDevice, stream) != hipSuccess ||
         hipStreamSynchronize(stream) != hipSuccess) {
-        (void)hipFree(m->dev);
+        if (m->dev_owned) (void)hipFree(m->dev);
+        m->dev = nullptr;
         return PPX_E_HIP;
     }
     uint8_t *dev = static_cast<uint8_t *>(m->dev);
@@ -363,7 +380,7 @@ int ensure_rope(ppx_model *m, int n_ctx) {
 void model_free(ppx_model *m) {
     if (!m) return;
     (void)hipDeviceSynchronize();
-    if (m->dev) (void)hipFree(m->dev);
+    if (m->dev && m->dev_owned) (void)hipFree(m->dev);
     if (m->rope) (void)hipFree(m->rope);
     for (hipEvent_t e : m->events) (void)hipEventDestroy(e);
     for (auto &g : m->graphs) (void)hipGraphExecDestroy(g.exec);

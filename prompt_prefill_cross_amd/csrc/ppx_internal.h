@@ -65,6 +65,7 @@ struct ppx_model {
     const uint8_t *ple_raw = nullptr;  // raw Q4_0 blocks [V][L*E/32][18]
     void *dev = nullptr;               // one allocation for all weights
     size_t dev_bytes = 0;
+    bool dev_owned = true;             // false: the caller's memory (ppx_model_load_into)
     float2 *rope = nullptr;            // [rope_n][head_dim/2] (cos, sin)
     int rope_n = 0;
     // named tensors for the kernel-level entry points

@@ -271,3 +271,37 @@ def test_snapshot_rejections_leave_cache_empty(ppx, tmp_path):
             kv2.load(str(path), n)
         assert e.value.status == want
         assert kv2.n_pos == 0
+
+
+def test_torch_owned_weights(ppx):
+    """ppx_model_load_into: the repacked weights in a torch tensor give the
+    same bits as the library's own allocation; the tensor outlives the model
+    and is not freed with it; a short or misaligned buffer is refused."""
+    import ctypes
+    buf = container("tiny")
+    toks = synth.prompt("tiny", 40)
+    ma = ppx.Model(buf)
+    mb = ppx.Model(buf, torch_weights=True)
+    need = ppx.lib().ppx_model_weight_bytes(ctypes.c_void_p(buf.ctypes.data), buf.nbytes)
+    assert mb._weights.numel() == need == mb.device_bytes == ma.device_bytes
+    la = ma.prefill(toks, ppx.KVCache(ma, 64), n_ubatch=16).clone()
+    kvb = ppx.KVCache(mb, 64)
+    lb = mb.prefill(toks, kvb, n_ubatch=16)
+    torch.cuda.synchronize()
+    assert torch.equal(la, lb)
+    w = mb._weights
+    kvb.close()
+    mb.close()
+    w.zero_()  # still the caller's memory
+    torch.cuda.synchronize()
+    L = ppx.lib()
+    h = ctypes.c_void_p()
+    small = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    st = L.ppx_model_load_into(ctypes.c_void_p(buf.ctypes.data), buf.nbytes, ctypes.c_void_p(small.data_ptr()),
+                               small.numel(), None, ctypes.byref(h))
+    assert st == -9 and not h.value
+    big = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
+    st = L.ppx_model_load_into(ctypes.c_void_p(buf.ctypes.data), buf.nbytes, ctypes.c_void_p(big.data_ptr() + 1),
+                               need, None, ctypes.byref(h))
+    assert st == -1 and not h.value
+

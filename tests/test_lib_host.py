@@ -143,3 +143,27 @@ def test_reusable_prefix_rule_brute_force():
         cap = min(len(stored), len(prompt) - 1, n_ctx)
         want = max(l for l in range(cap + 1) if stored[:l] == prompt[:l])
         assert oracle.kvcp.reusable_prefix(stored, prompt, n_ctx) == want
+
+
+def test_model_weight_bytes_host_only():
+    """ppx_model_weight_bytes lays a container out without a GPU: the repacked
+    weights take the container's tensor bytes (Q4_0 18 B per 32 weights, fp32
+    gains and the raw per-layer-embedding table) plus 256-byte alignment per
+    array; a damaged container gives 0."""
+    import ctypes
+    import synth
+    L = ppx.lib()
+    for name in ("tiny", "tinyllama"):
+        buf = synth.build_model(name)
+        m = oracle.parse_model(buf)
+        tensor_bytes = sum(t.rows * t.cols * (4 if t.ttype == 0 else 18 // 2) // (1 if t.ttype == 0 else 16)
+                           for t in m.tensors.values())
+        need = L.ppx_model_weight_bytes(ctypes.c_void_p(buf.ctypes.data), buf.nbytes)
+        assert tensor_bytes <= need <= tensor_bytes + 2 * 256 * (len(m.tensors) + 1), (name, need, tensor_bytes)
+        assert need == L.ppx_model_weight_bytes(ctypes.c_void_p(buf.ctypes.data), buf.nbytes)
+    bad = buf.copy()
+    bad[:4] = 0
+    assert L.ppx_model_weight_bytes(ctypes.c_void_p(bad.ctypes.data), bad.nbytes) == 0
+    assert L.ppx_model_weight_bytes(ctypes.c_void_p(buf.ctypes.data), 100) == 0
+    assert L.ppx_model_weight_bytes(None, 0) == 0
+
