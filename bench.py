@@ -48,6 +48,8 @@ def parse():
                     help="skip the token-verified prefix-reuse timing")
     ap.add_argument("--multi", default="16x128,8x256,4x512",
                     help="multi-sequence prefills to report, KxN = K prompts of N tokens ('' = none)")
+    ap.add_argument("--table", action="store_true",
+                    help="also time every config's full shapes, pruned and unpruned (builds 3 more models)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="prompt tokens of the oracle sample (0 = all)")
     ap.add_argument("--pmc-pass", action="store_true", help="one prefill + one calibration copy, then exit")
@@ -265,6 +267,47 @@ def multi_pass(ppx, mm, cfg, ub, shapes, reps=5):
     return out
 
 
+def table_pass(ppx, main_cfg, main_model):
+    """The configs' full matrix: E2B-like and E4B-like at 512/2048/8192
+    tokens pruned and unpruned, the long E2B-like prompts (16384, 32768;
+    ubatch 1024) and the no-sharing control at 8192 (pruned vs unpruned
+    should time the same there).  5 timed runs after 2 warm-ups each."""
+    import torch
+    import synth
+    plan = [("e2b", (512, 2048, 8192), ("auto", "off")), ("e4b", (512, 2048, 8192), ("auto", "off")),
+            ("e2b_long", (16384, 32768), ("auto",)), ("e2b_ctrl", (8192,), ("auto", "off"))]
+    rows = []
+    for name, lens, prunes in plan:
+        cfg = synth.CONFIGS[name]
+        ub = cfg.n_ubatch
+        if name == main_cfg.name:
+            mm = main_model
+        else:
+            mm = ppx.Model(synth.build_model(cfg))
+        kv = ppx.KVCache(mm, max(lens))
+        for n in lens:
+            toks = synth.prompt(cfg, n)
+            for pr in prunes:
+                times, _ = timed_steps(mm, kv, toks, ub, pr, 5, 2)
+                ph = phase_pass(ppx, mm, kv, toks, ub, pr, reps=1)
+                med = float(np.median(times))
+                gemm = ph["gemm_flop"] / (ph["ms"]["gemm"] * 1e-3) / 1e12 if ph["ms"]["gemm"] else 0.0
+                attn = ph["attn_flop"] / (ph["ms"]["attn"] * 1e-3) / 1e12 if ph["ms"]["attn"] else 0.0
+                rows.append({"config": name, "n": n, "prune": pr, "ubatch": ub, "ms_median": med,
+                             "tokens_per_s": n / med * 1e3, "gemm_frac_mfma": gemm / PEAK_FP16_TFLOPS,
+                             "attn_frac_mfma": attn / PEAK_FP16_TFLOPS, "phases_ms": ph["ms"]})
+                print(f"# table {name} n={n} prune={pr}: {med:.2f} ms, {n / med * 1e3:.0f} tok/s, GEMM phase "
+                      f"{gemm / PEAK_FP16_TFLOPS:.2f} / attention {attn / PEAK_FP16_TFLOPS:.2f} of MFMA peak",
+                      file=sys.stderr, flush=True)
+        del kv
+        if mm is not main_model:
+            mm.close()
+            del mm
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return rows
+
+
 def pmc_pass(mm, kv, toks, ub, prune):
     import torch
     kv.clear()
@@ -344,6 +387,7 @@ def main():
         print(f"# decode after {dec['after_prompt']}: {dec['ms_per_token']:.3f} ms/token, "
               f"{dec['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
 
+    table = table_pass(ppx, cfg, mm) if a.table else None
     times, ph = results[a.n]
     glu_us, glu_reps = glu_kernel_us(mm, ub)
     ms = float(np.mean(times))
@@ -389,6 +433,7 @@ def main():
         "decode": dec,
         "prefix_reuse": reuse,
         "multi_sequence": multi,
+        "config_table": table,
         "ms_median": float(np.median(times)),
         "ms_std": float(np.std(times)),
     }
