@@ -375,21 +375,18 @@ int layer_row(Ctx &c, int il, int pos, const int32_t *tok, bool write_kv = false
     gq.hd = hd;
     gq.pos = pos;
     gq.rope = m->rope;
-    PPX_LAUNCH(c, PPX_PHASE_ROW, launch_gemv(gq, c.s));
     if (write_kv && w.own) {
-        GemvArgs gk = gemv_base(c, xr, w.wkv, GV_KV, nullptr);
-        gk.norm_g = w.attn_norm;
-        gk.eps = m->eps;
-        gk.hd = hd;
-        gk.pos = pos;
-        gk.rope = m->rope;
-        gk.kc = c.kv->k + (size_t)il * lstride;
-        gk.vt = c.kv->vt + (size_t)il * c.kv->vld * kvd;
-        gk.kvd = kvd;
-        gk.vld = c.kv->vld;
-        PPX_LAUNCH(c, PPX_PHASE_ROW, launch_gemv(gk, c.s));
+        // the K|V projection of the same normalised row, in the same launch:
+        // the roped K row and the V^T column at pos
+        gq.W2 = w.wkv;
+        gq.epi2 = GV_KV;
+        gq.kc = c.kv->k + (size_t)il * lstride;
+        gq.vt = c.kv->vt + (size_t)il * c.kv->vld * kvd;
+        gq.kvd = kvd;
+        gq.vld = c.kv->vld;
         if (c.tm) c.tm->row_bytes += q4_bytes(w.wkv);
     }
+    PPX_LAUNCH(c, PPX_PHASE_ROW, launch_gemv(gq, c.s));
     Attn1Args at;
     at.q = qr;
     at.k = c.kv->k + (size_t)w.src * lstride;

@@ -163,7 +163,7 @@ constexpr int GEMV_UNR = 4;
 // The finished unit: thread c < 16 sums column c of each group over the KW
 // waves (in wave order) and applies the epilogue.
 template <int KW, int G>
-__device__ __forceinline__ void gemv_epilogue(const GemvArgs &a, const float *red, int unit, int c) {
+__device__ __forceinline__ void gemv_epilogue(const GemvArgs &a, const float *red, int unit, int c, int epi) {
     float yv[G];
 #pragma unroll
     for (int q = 0; q < G; ++q) {
@@ -173,7 +173,7 @@ __device__ __forceinline__ void gemv_epilogue(const GemvArgs &a, const float *re
         yv[q] = y;
     }
     const int n0 = unit * 16 * G;
-    switch (a.epi) {
+    switch (epi) {
     case GV_F32:
 #pragma unroll
         for (int q = 0; q < G; ++q) a.out[n0 + 16 * q + c] = yv[q];
@@ -234,7 +234,8 @@ __global__ __launch_bounds__(64 * KW * G) void k_q4gemv(GemvArgs a) {
     extern __shared__ float gemv_lds[];  // red[G][KW][16] floats, then hi[K], lo[K] fp16
     constexpr int NT = 64 * KW * G;
     const int K = a.W.K, kch = K >> 6;
-    const int nunits = a.W.N / (16 * G);  // a unit: the G groups of one workgroup pass
+    const int n1 = a.W.N / (16 * G);       // a unit: the G groups of one workgroup pass
+    const int nunits = n1 + a.W2.N / (16 * G);  // then the second matrix's units
     float *red = gemv_lds;
     _Float16 *xh = reinterpret_cast<_Float16 *>(gemv_lds + G * KW * 16);
     _Float16 *xl = xh + K;
@@ -243,12 +244,13 @@ __global__ __launch_bounds__(64 * KW * G) void k_q4gemv(GemvArgs a) {
     const int col = lane & 15, g8 = (lane >> 4) * 8;
 
     // weight batches: UNR chunks kc = base + u KW of group G unit + gi (clamped, so no branch)
-    const uint2 *nib0 = reinterpret_cast<const uint2 *>(a.W.nib) + lane;
-    const uint32_t *scl0 = reinterpret_cast<const uint32_t *>(a.W.scl) + col;
     uint2 w[GEMV_UNR];
     uint32_t sc[GEMV_UNR];
     auto load = [&](int unit, int base, uint2 (&wd)[GEMV_UNR], uint32_t (&sd)[GEMV_UNR]) {
-        const size_t grp = (size_t)(G * unit + gi) * kch;
+        const bool sec = unit >= n1;
+        const uint2 *nib0 = reinterpret_cast<const uint2 *>(sec ? a.W2.nib : a.W.nib) + lane;
+        const uint32_t *scl0 = reinterpret_cast<const uint32_t *>(sec ? a.W2.scl : a.W.scl) + col;
+        const size_t grp = (size_t)(G * (sec ? unit - n1 : unit) + gi) * kch;
 #pragma unroll
         for (int u = 0; u < GEMV_UNR; ++u) {
             const size_t kc = grp + min(base + u * KW, kch - 1);
@@ -314,7 +316,10 @@ __global__ __launch_bounds__(64 * KW * G) void k_q4gemv(GemvArgs a) {
         // lanes 0..15 hold rows 0 and 1 (hi and lo parts) of column `col`
         if (lane < 16) red[(gi * KW + kw) * 16 + lane] = acc[0] + acc[1];
         __syncthreads();
-        if (tid < 16) gemv_epilogue<KW, G>(a, red, unit, tid);
+        if (tid < 16) {
+            if (unit < n1) gemv_epilogue<KW, G>(a, red, unit, tid, a.epi);
+            else gemv_epilogue<KW, G>(a, red, unit - n1, tid, a.epi2);
+        }
         __syncthreads();  // red is reused by the next unit
     }
 }
@@ -332,14 +337,21 @@ int gemv_kw(int groups, int kch) {
 
 int launch_gemv(const GemvArgs &a, hipStream_t s) {
     if (a.W.N % 32 || a.W.K % 64 || !a.x) return PPX_E_UNSUPPORTED;
-    if (a.epi == GV_KV ? (!a.kc || !a.vt || a.kvd % 32 || 2 * a.kvd != a.W.N) : !a.out) return PPX_E_UNSUPPORTED;
+    auto bad_epi = [&](int epi, const Q4R &W) {
+        return epi == GV_KV ? (!a.kc || !a.vt || a.kvd % 32 || 2 * a.kvd != W.N) : !a.out;
+    };
+    if (bad_epi(a.epi, a.W)) return PPX_E_UNSUPPORTED;
     const bool paired = a.epi == GV_QROPE || a.epi == GV_KV;
+    if (a.W2.N) {
+        const bool paired2 = a.epi2 == GV_QROPE || a.epi2 == GV_KV;
+        if (a.W2.K != a.W.K || a.W2.N % 32 || paired2 != paired || bad_epi(a.epi2, a.W2)) return PPX_E_UNSUPPORTED;
+    }
     const int G = paired ? 2 : 1;
-    const int units = a.W.N / (16 * G);
+    const int units = (a.W.N + a.W2.N) / (16 * G);
     // wide outputs (the vocabulary head): a capped grid of workgroups that each
     // stage v once and loop over their units, four waves per unit
     const bool looped = units > kGemvMaxGrid;
-    const int kw = looped ? 4 : std::min(gemv_kw(a.W.N / 16, a.W.K / 64), 16 / G);
+    const int kw = looped ? 4 : std::min(gemv_kw((a.W.N + a.W2.N) / 16, a.W.K / 64), 16 / G);
     const dim3 grid(looped ? kGemvMaxGrid : units);
     const size_t lds = sizeof(float) * G * kw * 16 + 4ull * a.W.K;
     if (lds > 64 * 1024) return PPX_E_UNSUPPORTED;

@@ -207,6 +207,11 @@ struct GemvArgs {
     __half *kc = nullptr;   // GV_KV: K cache of the layer [n_ctx][kvd]
     __half *vt = nullptr;   // GV_KV: V cache of the layer, transposed [kvd][vld]
     int kvd = 0, vld = 0;
+    // Optional second matrix over the same (normalised) row, finished with
+    // epi2 (the K|V projection beside Q in one launch): its units follow W's.
+    // Both epilogues must take the same column pairing.  W2.N == 0: none.
+    Q4R W2;
+    int epi2 = GV_F32;
 };
 int launch_gemv(const GemvArgs &a, hipStream_t s);
 
