@@ -22,6 +22,10 @@
  *  - ppx_prefill runs one sequence (n_seq_max == 1), the case the pages
  *    prune; ppx_prefill_multi runs several, each in its own cache, with the
  *    prune generalised to one output row per sequence.
+ *  - Host threads: a model keeps per-model state that its calls update (the
+ *    recorded launch sequences, event pools, the tables' staging buffer), so
+ *    calls on one model, or on caches of one model, come from one host
+ *    thread at a time.  Different models are independent.
  */
 #ifndef PPX_H
 #define PPX_H
