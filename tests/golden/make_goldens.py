@@ -2,7 +2,8 @@
 
 Calls only the fp64 oracle (oracle/) on the seeded inputs of `synth`; the
 GPU parity tests compare the HIP path against these files instead of
-re-running the oracle on the GPU machine.  Each file holds the last-row logits
+re-running the oracle (minutes to hours at these sizes) inside the test.
+Each file holds the last-row logits
 (fp32, all n_vocab), the fp16 K and V rows of 16 sampled positions (first
 and last included) in up to six evenly spaced KV-owning layers, and the
 run's metadata.
