@@ -61,7 +61,10 @@ int parse(const uint8_t *b, size_t n, Parsed &p) {
         ht.type = (int)tt;
         if (tt > 1) return PPX_E_FORMAT;
         if (tt == 1 && ht.cols % 32) return PPX_E_FORMAT;
-        const uint64_t nb = tt == 0 ? ht.rows * ht.cols * 4 : ht.rows * (ht.cols / 32) * 18;
+        // sizes in 64 bits without wrapping: a tensor must lie inside the container
+        uint64_t nb = 0;
+        const uint64_t per = tt == 0 ? 4 : 18, units = tt == 0 ? ht.cols : ht.cols / 32;
+        if (__builtin_mul_overflow(ht.rows, units, &nb) || __builtin_mul_overflow(nb, per, &nb)) return PPX_E_FORMAT;
         if (ht.offset > n || nb > n - ht.offset) return PPX_E_FORMAT;
         p.t[name] = ht;
     }
@@ -155,6 +158,12 @@ int model_load(const uint8_t *b, size_t n, hipStream_t stream, void *weights_dev
     I.n_vocab = p.h[7];
     I.ple_dim = p.h[8];
     I.act = p.h[9];
+    // every dimension is bounded before any product of them is formed
+    for (int k = 1; k <= 8; ++k)
+        if (p.h[k] < 0 || p.h[k] > (1 << 20)) return PPX_E_FORMAT;
+    if ((int64_t)p.h[3] * p.h[5] > (1 << 24) || (int64_t)p.h[4] * p.h[5] > (1 << 24) ||
+        (int64_t)p.h[0] * p.h[8] > (1 << 24))
+        return PPX_E_FORMAT;
     I.kv_dim = I.n_kv_head * I.head_dim;
     m->tied = p.h[10];
     m->eps = p.eps;
@@ -348,6 +357,13 @@ int model_load(const uint8_t *b, size_t n, hipStream_t stream, void *weights_dev
     return PPX_OK;
 }
 
+void drop_graphs(ppx_model *m) {
+    for (auto &g : m->graphs) (void)hipGraphExecDestroy(g.exec);
+    for (auto &g : m->keyed_graphs) (void)hipGraphExecDestroy(g.exec);
+    m->graphs.clear();
+    m->keyed_graphs.clear();
+}
+
 int ensure_rope(ppx_model *m, int n_ctx) {
     if (m->rope_n >= n_ctx) return PPX_OK;
     const int half = m->info.head_dim / 2, hd = m->info.head_dim;
@@ -369,7 +385,10 @@ int ensure_rope(ppx_model *m, int n_ctx) {
         return PPX_E_HIP;
     }
     if (m->rope) {
+        // Recorded launch sequences hold the old table's address in their RoPE
+        // epilogues: they are dropped with it and recorded again on next use.
         (void)hipDeviceSynchronize();
+        drop_graphs(m);
         (void)hipFree(m->rope);
     }
     m->rope = dev;
@@ -383,8 +402,7 @@ void model_free(ppx_model *m) {
     if (m->dev && m->dev_owned) (void)hipFree(m->dev);
     if (m->rope) (void)hipFree(m->rope);
     for (hipEvent_t e : m->events) (void)hipEventDestroy(e);
-    for (auto &g : m->graphs) (void)hipGraphExecDestroy(g.exec);
-    for (auto &g : m->keyed_graphs) (void)hipGraphExecDestroy(g.exec);
+    drop_graphs(m);
     if (m->capture_stream) (void)hipStreamDestroy(m->capture_stream);
     for (hipStream_t st : m->aux_streams) (void)hipStreamDestroy(st);
     for (hipStream_t st : m->capture_aux) (void)hipStreamDestroy(st);
