@@ -95,6 +95,7 @@ __global__ __launch_bounds__(C::NT) void k_attn_prefill(AttnArgs a) {
 
     const int tmax = min(M - 1, (cb * C::CB + C::CB - 1) / G);
     const int pend = pos0 + tmax;  // last key any column here can see
+    const int plast = pos0 + M - 1;  // last key written before this launch reads the cache
     const int kbeg = ck * a.kc;
     if (kbeg > pend) return;  // the whole workgroup
     const int kend = min(kbeg + a.kc, pend + 1);
@@ -105,7 +106,6 @@ __global__ __launch_bounds__(C::NT) void k_attn_prefill(AttnArgs a) {
         // K rows past the last written position repeat it (their scores are
         // masked); V^T reads stay inside the row (vld is a multiple of 64).
         const int pw = C::NP == 1 ? 0 : wave - C::NC;
-        const int plast = pos0 + M - 1;
         auto entry = [&](int t) { return min(t * C::NP + pw, C::DMA_STAGE - 1); };
         int koff[C::PER];  // K: key within the stage; V^T: element offset within the row block
 #pragma unroll
@@ -237,10 +237,20 @@ __global__ __launch_bounds__(C::NT) void k_attn_prefill(AttnArgs a) {
                 for (int i = 0; i < DT; ++i) oacc[c][i] *= alpha;
             }
         }
-        // O^T += V^T P^T over the stage's 32 keys (8 lg .. 8 lg + 7 in lane group lg)
+        // O^T += V^T P^T over the stage's 32 keys (8 lg .. 8 lg + 7 in lane group lg).
+        // Values of keys past the last written position may be stale (a cache
+        // cleared or reloaded to fewer positions keeps its old contents): they
+        // are zeroed, so a non-finite stale value cannot meet a zero weight.
+        const int vlim = plast - (t0 + 8 * lg);  // elements e <= vlim are written keys
+        const bool tail = t0 + KT - 1 > plast;   // uniform over the workgroup
 #pragma unroll
         for (int i = 0; i < DT; ++i) {
-            const h8 vf = st[C::K_UNITS + i * 64];
+            h8 vf = st[C::K_UNITS + i * 64];
+            if (tail) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (e > vlim) vf[e] = (_Float16)0.0f;
+            }
 #pragma unroll
             for (int c = 0; c < CPW; ++c) oacc[c][i] = mfma16(vf, pf[c], oacc[c][i]);
         }

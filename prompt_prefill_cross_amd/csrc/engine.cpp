@@ -1132,16 +1132,22 @@ int kvfile_check(const char *path, int nl, int kvd, int n_pos, int n_ctx, int *f
         st = PPX_E_FORMAT;
     } else {
         if (fpos) *fpos = hdr[0];
+        // the body size in 64 bits without wrapping (the layer count and
+        // width come from the model, the position count from the file)
+        int64_t body = 0;
+        const bool huge = nl <= 0 || kvd <= 0 || hdr[0] < 0 ||
+                          __builtin_mul_overflow((int64_t)4 * nl, (int64_t)kvd, &body) ||
+                          __builtin_mul_overflow(body, (int64_t)hdr[0], &body) || body > (int64_t)1 << 50;
         if (hdr[1] != nl || hdr[2] != kvd) {
             st = PPX_E_MISMATCH;
-        } else if (hdr[0] < 0) {
+        } else if (huge) {
             st = PPX_E_FORMAT;
         } else {
             std::fseek(f, 0, SEEK_END);
-            const long sz = std::ftell(f);
-            const long want = 16 + 4l * nl * hdr[0] * kvd;
+            const int64_t sz = std::ftell(f);
+            const int64_t want = 16 + body;
             bool tok = false;
-            if (sz == want + 8 + 4l * hdr[0]) {
+            if (sz == want + 8 + 4ll * hdr[0]) {
                 char tm[4];
                 int32_t cnt = -1;
                 std::fseek(f, want, SEEK_SET);
@@ -1200,10 +1206,9 @@ int kv_load(ppx_kv *kv, const char *path, int n_pos, hipStream_t s) {
     if (vpos) (void)hipFree(vpos);
     if (st) return st;
     kv->n_pos = n_pos;
-    if (log_enabled()) {
-        std::fprintf(stderr, "KV cache loaded: %d positions from %s\n", n_pos, path);
-        std::fprintf(stderr, "Skipping %d cached prompt tokens\n", n_pos);
-    }
+    if (log_enabled())
+        std::fprintf(stderr, "[ppx] snapshot %s: %d positions restored; the prefill resumes at position %d\n", path,
+                     n_pos, n_pos);
     return PPX_OK;
 }
 
@@ -1318,8 +1323,9 @@ int ppx_kv_init(ppx_model *m, void *kv_dev, size_t bytes, int n_ctx, ppx_kv **ou
     if (bytes < need) return PPX_E_NOMEM;
     if ((reinterpret_cast<uintptr_t>(kv_dev) & 255) != 0) return PPX_E_INVAL;
     PPX_TRY(ensure_rope(m, n_ctx));
-    // positions never written read as zero: attention tiles that run past the
-    // last written position multiply those values by zero probabilities
+    // a fresh cache holds zeros; the attention kernels never use a value
+    // past the last written position (after kv_clear or a shorter kv_load the
+    // old contents stay, and are masked or zeroed in the kernels)
     if (need && hipMemset(kv_dev, 0, need) != hipSuccess) return PPX_E_HIP;
     ppx_kv *kv = new ppx_kv();
     kv->m = m;
