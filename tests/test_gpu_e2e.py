@@ -139,6 +139,38 @@ def test_recorded_launches_replay_with_new_tokens(ppx):
     assert not torch.equal(replayed[1], replayed[2])
 
 
+def test_replay_after_the_rope_table_grows(ppx):
+    """A recorded launch sequence holds the RoPE table's address.  Creating a
+    cache with a longer context replaces the table; a later prefill of a shape
+    recorded before must not replay against the freed one.  Order: record on
+    cache A, create the longer cache B, prefill A again with the same shape
+    (and a new prompt), check against the oracle and the direct launches."""
+    mm = ppx.Model(container("tiny"))  # a fresh model: its table covers only what this test creates
+    n = 48
+    kva = ppx.KVCache(mm, 64)
+    t1 = synth.prompt("tiny", n)
+    first = mm.prefill(t1, kva, n_ubatch=16).clone()
+    kvb = ppx.KVCache(mm, 4096)  # grows the table
+    scratch = torch.full((1 << 22,), float("nan"), device="cuda")  # reuses freed memory, if any
+    rng = np.random.default_rng(48)
+    t2 = rng.integers(0, mm.info["n_vocab"], n).astype(np.int32)
+    kva.clear()
+    again = mm.prefill(t2, kva, n_ubatch=16).clone()
+    kva.clear()
+    direct = mm.prefill(t2, kva, n_ubatch=16, timing=ppx.Timing())
+    torch.cuda.synchronize()
+    assert torch.equal(again, direct)
+    om = oracle_model("tiny")
+    ref = oracle.prefill(om, oracle.KVState(om, 64), t2, prune=True)
+    ok, d = logits_ok(again.cpu().numpy(), ref)
+    assert ok, d
+    ok, d = logits_ok(first.cpu().numpy(), oracle.prefill(om, oracle.KVState(om, 64), t1, prune=True))
+    assert ok, d
+    del scratch, kvb
+    kva.close()
+    mm.close()
+
+
 def test_tiny_error_paths(ppx):
     mm = engine_model(ppx, "tiny")
     kv = ppx.KVCache(mm, 32)
@@ -181,6 +213,17 @@ def test_tinyllama_full_and_resume(ppx, tmp_path):
     path = tmp_path / "prompt.kvc"
     kv.save(str(path), n)
     assert os.path.getsize(path) == 16 + 2 * 22 * n * 256 * 2
+    # the PicoLM page's order: magic, positions (512 = 0x200), layers (22),
+    # KV dim (256 = 0x100), typed out byte by byte; then K, then V, each
+    # [layer][position][dim] fp16 (offsets computed by hand)
+    raw = path.read_bytes()
+    assert raw[:16] == bytes([0x4B, 0x56, 0x43, 0x50, 0, 2, 0, 0, 22, 0, 0, 0, 0, 1, 0, 0])
+    K1, V1 = kv.kv_tensors()
+    for il, p_, c in ((0, 0, 0), (5, 17, 3), (21, 511, 255)):
+        ko = 16 + 2 * ((il * n + p_) * 256 + c)
+        vo = 16 + 2 * 22 * n * 256 + 2 * ((il * n + p_) * 256 + c)
+        assert np.frombuffer(raw[ko:ko + 2], "<f2")[0] == K1[il, p_, c].item()
+        assert np.frombuffer(raw[vo:vo + 2], "<f2")[0] == V1[il, p_, c].item()
     mm = engine_model(ppx, cfg)
     for N in (25, 500):
         kv2 = ppx.KVCache(mm, n)
@@ -214,6 +257,10 @@ GOLDEN_RUNS = [
     ("e2b_8192", 512, "auto"), ("e4b_2048", 512, "auto"),
     ("e2b_ctrl_8192", 1024, "auto"), ("e2b_long_16384", 1024, "auto"),
     ("e4b_8192", 512, "auto"), ("e2b_long_32768", 1024, "auto"),
+    # unpruned at the larger sizes: the stored results serve both modes, since
+    # the oracle's pruned and unpruned passes are bit-identical
+    ("e2b_8192", 512, "off"), ("e4b_2048", 512, "off"), ("e4b_8192", 512, "off"),
+    ("e2b_long_16384", 1024, "off"),
 ]
 
 

@@ -426,3 +426,32 @@ def test_kvcp_round_trip_and_rejections():
     for args in bad:
         with pytest.raises(oracle.kvcp.SnapshotError):
             oracle.kvcp.load(*args)
+
+
+def test_kvcp_header_and_body_order_against_hand_written_bytes():
+    """The PicoLM page's file contents, in its order: the magic, then the
+    cached positions, the layer count and the KV dimension, then K, then V.
+    The expected header is typed out byte by byte here (25 positions, 22
+    layers, KV dim 256 -- the page's TinyLlama example), so a swap of two
+    header fields in both the writer and the reader fails; the body offsets
+    are computed by hand from [layer][position][dim] order."""
+    nl, npos, kvd = 22, 25, 256
+    K = np.zeros((nl, npos, kvd), np.float16)
+    V = np.zeros((nl, npos, kvd), np.float16)
+    K[3, 7, 5] = 1.5     # fp16 0x3E00
+    V[21, 24, 255] = -2.0  # fp16 0xC000
+    data = oracle.kvcp.dump(K, V, npos)
+    assert data[:16] == bytes([0x4B, 0x56, 0x43, 0x50, 25, 0, 0, 0, 22, 0, 0, 0, 0, 1, 0, 0])
+    k_off = 16 + 2 * ((3 * npos + 7) * kvd + 5)
+    assert data[k_off:k_off + 2] == bytes([0x00, 0x3E])
+    v_off = 16 + 2 * nl * npos * kvd + 2 * ((21 * npos + 24) * kvd + 255)
+    assert data[v_off:v_off + 2] == bytes([0x00, 0xC0])
+    assert v_off + 2 == len(data)
+    assert sum(1 for b in data[16:] if b) == 2  # the two high bytes above; nothing else is set
+    # a header typed with the layer count and the position count swapped is
+    # refused by the reader (the layer count no longer matches the model)
+    swapped = bytes([0x4B, 0x56, 0x43, 0x50, 22, 0, 0, 0, 25, 0, 0, 0, 0, 1, 0, 0]) + data[16:]
+    with pytest.raises(oracle.kvcp.SnapshotError):
+        oracle.kvcp.load(swapped, nl, kvd, 1, 100)
+    k2, v2 = oracle.kvcp.load(data, nl, kvd, npos, 100)
+    assert k2[3, 7, 5] == 1.5 and v2[21, 24, 255] == -2.0
