@@ -111,7 +111,23 @@ typedef struct {
                             required when any flag is set                    */
     float *embd_out;     /* device fp32 [n_tokens][d_model]: required when
                             embeddings != 0                                  */
+    int precision;       /* PPX_PRECISION_FAST (0, the default) or
+                            PPX_PRECISION_EXACT; see below                   */
 } ppx_prefill_params;
+
+/* Arithmetic of the row-batched layers (the single-row path and the head
+ * are fp32-class in both):
+ *  - FAST: fp16 MFMA operands with fp32 accumulation -- activations, the
+ *    attention query, probabilities and output rounded to fp16, weights
+ *    entering the products as fp16(d * (code - 8)); the K|V projection
+ *    alone uses exact weights and split activations.
+ *  - EXACT: every product at ~fp32 accuracy -- each fp32 operand split into
+ *    fp16 high and low parts against exact (code - 8) weights, each 32-wide
+ *    block's partial scaled by its fp32 block scale; attention of every row
+ *    in fp32 (online softmax over 32-key chunks, both products split the same
+ *    way).  Several times slower; for models whose activations amplify fp16
+ *    rounding beyond the tolerance a comparison needs. */
+enum { PPX_PRECISION_FAST = 0, PPX_PRECISION_EXACT = 1 };
 
 #define PPX_MAX_UBATCH 4096
 #define PPX_MAX_SEQ 64

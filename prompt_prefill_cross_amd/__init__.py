@@ -22,6 +22,7 @@ STATUS = {0: "PPX_OK", -1: "PPX_E_INVAL", -2: "PPX_E_TOKEN", -3: "PPX_E_CTX", -4
           -5: "PPX_E_FORMAT", -6: "PPX_E_MISMATCH", -7: "PPX_E_UNSUPPORTED", -8: "PPX_E_HIP",
           -9: "PPX_E_NOMEM", -10: "PPX_E_EMPTY"}
 PRUNE = {"auto": -1, "off": 0, "on": 1}
+PRECISION = {"fast": 0, "exact": 1}
 PPX_MAX_UBATCH = 4096
 
 
@@ -53,7 +54,8 @@ class Timing(ctypes.Structure):
 class PrefillParams(ctypes.Structure):
     _fields_ = [("n_ubatch", c_int), ("prune", c_int), ("embeddings", c_int), ("n_seq_max", c_int),
                 ("debug_hidden", c_void_p), ("timing", POINTER(Timing)), ("debug_rows", c_void_p),
-                ("embeddings_layer_inp", c_void_p), ("layer_inp_out", c_void_p), ("embd_out", c_void_p)]
+                ("embeddings_layer_inp", c_void_p), ("layer_inp_out", c_void_p), ("embd_out", c_void_p),
+                ("precision", c_int)]
 
 
 class Seq(ctypes.Structure):
@@ -218,7 +220,7 @@ class Model:
 
     def prefill(self, tokens, kv: "KVCache", n_ubatch: int = 512, prune: str = "auto", logits=None,
                 debug_hidden=None, embeddings: int = 0, n_seq_max: int = 1, stream=None, timing=None,
-                debug_rows=None, layer_flags=None, layer_inp_out=None, embd_out=None):
+                debug_rows=None, layer_flags=None, layer_inp_out=None, embd_out=None, precision: str = "fast"):
         """Run `tokens` (int32) from kv.n_pos; return fp32 logits [n_vocab] of the last token.
 
         layer_flags (n_layer + 1 truth values) / layer_inp_out and embeddings /
@@ -240,7 +242,8 @@ class Model:
                           c_void_p(debug_rows.data_ptr()) if debug_rows is not None else None,
                           c_void_p(flags.ctypes.data) if flags is not None else None,
                           c_void_p(layer_inp_out.data_ptr()) if layer_inp_out is not None else None,
-                          c_void_p(embd_out.data_ptr()) if embd_out is not None else None)
+                          c_void_p(embd_out.data_ptr()) if embd_out is not None else None,
+                          PRECISION[precision])
         st = lib().ppx_prefill(self._h, kv.handle, c_void_p(toks.ctypes.data), toks.shape[0], ctypes.byref(p),
                                _ptr(ws), ws.numel(), _ptr(logits), _stream(stream))
         _check(st, "ppx_prefill")
@@ -263,7 +266,7 @@ class Model:
         return lg, {il: inp[j] for j, il in enumerate(want)}, emb
 
     def prefill_multi(self, prompts, kvs, n_ubatch: int = 512, prune: str = "auto", logits=None,
-                      n_seq_max: int | None = None, stream=None, timing=None):
+                      n_seq_max: int | None = None, stream=None, timing=None, precision: str = "fast"):
         """Several prompts in one pass, prompt s from kvs[s].n_pos in its own
         cache; return fp32 logits [n_seq][n_vocab] of each prompt's last token."""
         import torch
@@ -284,7 +287,8 @@ class Model:
         ws = self._ws
         p = PrefillParams(n_ubatch, PRUNE[prune] if isinstance(prune, str) else int(prune), 0,
                           k if n_seq_max is None else n_seq_max, None,
-                          ctypes.pointer(timing) if timing is not None else None, None)
+                          ctypes.pointer(timing) if timing is not None else None, None, None, None, None,
+                          PRECISION[precision])
         st = lib().ppx_prefill_multi(self._h, seqs, k, ctypes.byref(p), _ptr(ws), ws.numel(), _ptr(logits),
                                      _stream(stream))
         _check(st, "ppx_prefill_multi")

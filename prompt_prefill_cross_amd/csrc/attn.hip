@@ -509,6 +509,128 @@ __global__ __launch_bounds__(256) void k_attn_merge(Attn1Args a, int nchunks) {
     }
 }
 
+// ------------------------------------------------------------------ exact rows
+// Causal attention of M rows at ~fp32 accuracy.  Workgroup (row r, KV head):
+// the G <= 8 query heads of the KV head take columns 0..7 (high part) and
+// 8..15 (low part) of the MFMA B operand, as in the single-query kernel, and
+// the keys 0..pos are taken 32 at a time with an online softmax in fp32:
+//   scores  S[key][g] = K[key] . q_g          (waves 0, 1: 16 keys each)
+//   softmax update per head: running max m, sum l, rescale factor alpha
+//   O[d][g] = alpha O[d][g] + sum_key V^T[d][key] p[g][key]  (all waves)
+// The output o = O / l leaves as fp16 high and low parts, fragment-tiled.
+template <int HD>
+__global__ __launch_bounds__(256) void k_attn_rows_exact(AttnArgs a) {
+    constexpr int NJ = HD / 64;  // 16-dim output tiles per wave
+    __shared__ float sl[8][CH];
+    __shared__ float mrun[8], lrun[8], alf[8];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = blockIdx.x, kvh = blockIdx.y;
+    const int G = a.H / a.KVH;
+    const int pos = a.row_pos ? a.row_pos[r] : a.pos0 + r;
+    const __half *kp = a.k, *vtp = a.vt;
+    int vld = a.vld;
+    if (a.seq_kv) {
+        const KVRef &ref = a.seq_kv[a.row_seq[r]];
+        kp = ref.k;
+        vtp = ref.vt;
+        vld = ref.vld;
+    }
+    const int c = lane & 15, g = c & 7, lg = lane >> 4;
+    const bool lo = c >= 8;
+    const float scale = 1.0f / sqrtf((float)HD);
+    // the B operand of the scores: q of head g (high or low part), dims ks*32 + 8 lg ..
+    h8 qb[HD / 32];
+    {
+        const float *qrow = a.q32 + ((size_t)r * a.H + kvh * G + min(g, G - 1)) * HD + lg * 8;
+#pragma unroll
+        for (int ks = 0; ks < HD / 32; ++ks) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v = qrow[ks * 32 + e];
+                const _Float16 h = (_Float16)v;
+                qb[ks][e] = g < G ? (lo ? (_Float16)(v - (float)h) : h) : (_Float16)0.0f;
+            }
+        }
+    }
+    if (tid < 8) {
+        mrun[tid] = -INFINITY;
+        lrun[tid] = 0.f;
+    }
+    f4 oacc[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) oacc[j] = f4{0.f, 0.f, 0.f, 0.f};
+    const int nch = (pos + CH) / CH;
+    for (int ch = 0; ch < nch; ++ch) {
+        const int k0 = ch * CH, nk = min(CH, pos + 1 - k0);
+        if (wave < CH / 16) {
+            const int kt = wave * 16 + c;
+            const int kr = k0 + min(kt, nk - 1);  // masked keys re-read a valid row
+            const __half *krow = kp + ((size_t)kr * a.KVH + kvh) * HD + lg * 8;
+            f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < HD / 32; ++ks)
+                acc = mfma16(*reinterpret_cast<const h8 *>(krow + ks * 32), qb[ks], acc);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float v = acc[q] + __shfl_xor(acc[q], 8, 64);
+                const int kk = wave * 16 + 4 * lg + q;
+                if (c < G) sl[c][kk] = kk < nk ? v * scale : -INFINITY;
+            }
+        }
+        __syncthreads();
+        for (int h = wave; h < G; h += 4) {
+            const float sc = lane < CH ? sl[h][lane] : -INFINITY;
+            const float mx = wave_max(sc);
+            const float mold = mrun[h];
+            const float mnew = fmaxf(mold, mx);
+            const float p = lane < nk ? expf(sc - mnew) : 0.f;
+            const float l = wave_sum(p);
+            if (lane < CH) sl[h][lane] = p;
+            if (lane == 0) {
+                const float al = expf(mold - mnew);  // 0 for the first chunk (mold = -inf)
+                alf[h] = al;
+                lrun[h] = lrun[h] * al + l;
+                mrun[h] = mnew;
+            }
+        }
+        __syncthreads();
+        h8 bv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float p = g < G ? sl[g][lg * 8 + e] : 0.f;
+            const _Float16 h = (_Float16)p;
+            bv[e] = lo ? (_Float16)(p - (float)h) : h;
+        }
+        const float al = g < G ? alf[g] : 1.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int d = (wave + 4 * j) * 16 + c;
+            h8 av = *reinterpret_cast<const h8 *>(vtp + ((size_t)kvh * HD + d) * vld + k0 + lg * 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (lg * 8 + e >= nk) av[e] = (_Float16)0.0f;
+            oacc[j] = mfma16(av, bv, oacc[j] * al);
+        }
+        __syncthreads();  // sl and alf are rewritten by the next chunk
+    }
+    const int od = a.H * HD;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float v = oacc[j][q] + __shfl_xor(oacc[j][q], 8, 64);
+            if (c < G) {
+                const int h = kvh * G + c, d = (wave + 4 * j) * 16 + 4 * lg + q;
+                const float o = v / lrun[c];
+                const _Float16 hv = (_Float16)o;
+                const size_t idx = tiled_index(r, h * HD + d, od);
+                a.o[idx] = hv;
+                a.o_lo[idx] = (_Float16)(o - (float)hv);
+            }
+        }
+    }
+}
+
 int ok() { return hipGetLastError() == hipSuccess ? PPX_OK : PPX_E_HIP; }
 
 }  // namespace
@@ -582,6 +704,22 @@ int launch_attn_prefill(const AttnArgs &a0, hipStream_t s) {
     case 64: hipLaunchKernelGGL(k_attn_prefill_merge<64>, dim3((a.M * a.H + 3) / 4), dim3(256), 0, s, a); break;
     case 128: hipLaunchKernelGGL(k_attn_prefill_merge<128>, dim3((a.M * a.H + 3) / 4), dim3(256), 0, s, a); break;
     default: hipLaunchKernelGGL(k_attn_prefill_merge<256>, dim3((a.M * a.H + 3) / 4), dim3(256), 0, s, a); break;
+    }
+    return ok();
+}
+
+int launch_attn_rows_exact(const AttnArgs &a, hipStream_t s) {
+    if (a.M <= 0) return PPX_OK;
+    const int G = a.KVH > 0 ? a.H / a.KVH : 0;
+    if (!a.q32 || !a.o || !a.o_lo || G < 1 || G > 8 || a.H % a.KVH) return PPX_E_UNSUPPORTED;
+    if (a.seq_kv ? (!a.row_pos || !a.row_seq) : (!a.k || !a.vt || a.vld % 64 || a.pos0 + a.M > a.vld))
+        return PPX_E_UNSUPPORTED;
+    dim3 grid(a.M, a.KVH);
+    switch (a.hd) {
+    case 64: hipLaunchKernelGGL(k_attn_rows_exact<64>, grid, dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL(k_attn_rows_exact<128>, grid, dim3(256), 0, s, a); break;
+    case 256: hipLaunchKernelGGL(k_attn_rows_exact<256>, grid, dim3(256), 0, s, a); break;
+    default: return PPX_E_UNSUPPORTED;
     }
     return ok();
 }

@@ -39,6 +39,7 @@ constexpr int kSlots = 1;
 struct WsLayout {
     size_t tok;
     size_t x, a16, a16lo, q16, o16, h16, p16, ap_part, gpart;  // slot 0
+    size_t q32, o16lo, h16lo, p16lo;                           // exact precision only (slot 0)
     size_t gpart_floats;                                       // split-K partials of one GEMM
     size_t slot_stride;
     int nslots;
@@ -80,6 +81,11 @@ WsLayout ws_layout(const ppx_model *m, int ub, int n_ctx) {
     w.slot_stride = o - s0;
     w.nslots = kSlots;
     o += w.slot_stride * (kSlots - 1);
+    // exact precision: fp32 queries and the low parts of the split operands
+    w.q32 = take(4ull * ub * qd);
+    w.o16lo = take(2ull * ub16 * qd);
+    w.h16lo = take(2ull * ub16 * F);
+    w.p16lo = take(2ull * ub16 * std::max(E, 1));
     w.xr = take(4ull * d);
     w.qr = take(4ull * qd);
     w.orow = take(4ull * qd);
@@ -104,6 +110,7 @@ struct Ctx {
     WsLayout L;
     ppx_timing *tm = nullptr;  // per-phase timing requested
     int slot = 0;              // buffers of the ubatch being enqueued
+    bool exact = false;        // PPX_PRECISION_EXACT: the row-batched layers at ~fp32 accuracy
     // A row batch spanning several sequences, each with its own cache (null:
     // the rows are one sequence's consecutive positions, in kv).
     struct Rows {
@@ -187,8 +194,123 @@ struct Ctx {
 
 inline double q4_bytes(const Q4R &w) { return (double)w.N * w.K * 18.0 / 32.0; }
 
+// Layer il for M rows at ~fp32 accuracy (PPX_PRECISION_EXACT): every GEMM on
+// the exact-weight kernel with split activations (norms write high and low
+// parts; the epilogues of Q, GLU and PLE keep fp32 or write both parts), and
+// attention of each row in fp32.  Slot 0's buffers only (one ubatch at a time).
+int layer_rows_exact(Ctx &c, int il, int M, int row0, int pos0) {
+    const ppx_model *m = c.m;
+    const ppx_model_info &I = m->info;
+    const LayerW &w = m->layers[il];
+    const int d = I.d_model, hd = I.head_dim, qd = I.n_head * hd, kvd = I.kv_dim;
+    float *x = c.sl<float>(c.L.x);
+    __half *a16 = c.sl<__half>(c.L.a16), *a16lo = c.sl<__half>(c.L.a16lo);
+    __half *o16 = c.sl<__half>(c.L.o16), *o16lo = c.at<__half>(c.L.o16lo);
+    __half *h16 = c.sl<__half>(c.L.h16), *h16lo = c.at<__half>(c.L.h16lo);
+    float *q32 = c.at<float>(c.L.q32);
+    const Ctx::Rows *R = c.rows;
+    const size_t lstride = R ? 0 : (size_t)c.kv->n_ctx * kvd;
+    const size_t vstride = R ? 0 : (size_t)c.kv->vld * kvd;
+    auto gemm = [&](const __half *A, const __half *A2, const Q4R &W, int epi) {
+        GemmArgs g;
+        g.A = A;
+        g.A2 = A2;
+        g.M = M;
+        g.W = W;
+        g.epi = epi;
+        return g;
+    };
+
+    PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_rmsnorm_split(x, w.attn_norm, m->eps, M, d, a16, a16lo, c.s));
+    GemmArgs g = gemm(a16, a16lo, w.wq, EPI_QKV);
+    g.q32 = q32;
+    g.qd = qd;
+    g.kvd = 0;
+    g.hd = hd;
+    g.pos0 = pos0;
+    g.rope = m->rope;
+    if (R) g.row_pos = R->pos;
+    PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm_exact(g, c.s));
+    if (w.own) {
+        GemmArgs gk = g;
+        gk.W = w.wkv;
+        gk.q32 = nullptr;
+        gk.qd = 0;
+        gk.kvd = kvd;
+        if (R) {
+            gk.row_seq = R->seq;
+            gk.seq_kv = R->kv + (size_t)il * R->nseq;
+        } else {
+            gk.kc = c.kv->k + il * lstride;
+            gk.vc = c.kv->vt + il * vstride;
+            gk.vld = c.kv->vld;
+        }
+        PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm_exact(gk, c.s));
+    }
+    AttnArgs at;
+    at.q32 = q32;
+    at.o = o16;
+    at.o_lo = o16lo;
+    if (R) {
+        at.seq_kv = R->kv + (size_t)w.src * R->nseq;
+        at.row_pos = R->pos;
+        at.row_seq = R->seq;
+    } else {
+        at.k = c.kv->k + (size_t)w.src * lstride;
+        at.vt = c.kv->vt + (size_t)w.src * vstride;
+        at.vld = c.kv->vld;
+    }
+    at.M = M;
+    at.H = I.n_head;
+    at.KVH = I.n_kv_head;
+    at.hd = hd;
+    at.pos0 = pos0;
+    PPX_LAUNCH(c, PPX_PHASE_ATTN, launch_attn_rows_exact(at, c.s));
+    GemmArgs go = gemm(o16, o16lo, w.wo, EPI_ADD);
+    go.out_f32 = x;
+    PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm_exact(go, c.s));
+
+    PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_rmsnorm_split(x, w.ffn_norm, m->eps, M, d, a16, a16lo, c.s));
+    GemmArgs gu = gemm(a16, a16lo, w.wgu, EPI_GLU);
+    gu.out_f16 = h16;
+    gu.out_lo = h16lo;
+    gu.act = I.act;
+    PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm_exact(gu, c.s));
+    GemmArgs gd = gemm(h16, h16lo, w.wdown, EPI_ADD);
+    gd.out_f32 = x;
+    PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm_exact(gd, c.s));
+    if (I.ple_dim) {
+        const int E = I.ple_dim;
+        __half *p16 = c.sl<__half>(c.L.p16), *p16lo = c.at<__half>(c.L.p16lo);
+        PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_rmsnorm_split(x, w.ple_norm, m->eps, M, d, a16, a16lo, c.s));
+        GemmArgs gp = gemm(a16, a16lo, w.wpg, EPI_PLE);
+        gp.out_f16 = p16;
+        gp.out_lo = p16lo;
+        gp.ple_raw = m->ple_raw;
+        gp.tok = R ? R->tok : c.at<int32_t>(c.L.tok) + row0;
+        gp.ple_row_blocks = I.n_layer * E / 32;
+        gp.ple_col0 = il * E;
+        gp.ple_s = w.ple_s;
+        PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm_exact(gp, c.s));
+        GemmArgs gq = gemm(p16, p16lo, w.wpu, EPI_ADD);
+        gq.out_f32 = x;
+        PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm_exact(gq, c.s));
+    }
+    if (c.tm) {
+        double nk = (double)w.wq.N * w.wq.K + (double)w.wo.N * w.wo.K + (double)w.wgu.N * w.wgu.K +
+                    (double)w.wdown.N * w.wdown.K;
+        if (w.own) nk += (double)w.wkv.N * w.wkv.K;
+        if (I.ple_dim) nk += (double)w.wpg.N * w.wpg.K + (double)w.wpu.N * w.wpu.K;
+        c.tm->gemm_flop += 2.0 * M * nk;
+        const double vis = R ? R->vis : (double)M * pos0 + 0.5 * (double)M * (M + 1);
+        c.tm->attn_flop += 4.0 * I.n_head * hd * vis;
+    }
+    return PPX_OK;
+}
+
 // One ubatch of M rows through layer il on the MFMA path.
 int layer_rows(Ctx &c, int il, int M, int row0, int pos0) {
+    if (c.exact) return layer_rows_exact(c, il, M, row0, pos0);
     const ppx_model *m = c.m;
     const ppx_model_info &I = m->info;
     const LayerW &w = m->layers[il];
@@ -581,9 +703,11 @@ int run_graph(Ctx &c, const ppx_prefill_params *p, const int32_t *tok_dev, int n
     key.p0 = p0;
     key.ub = ub;
     key.prune = prune;
+    key.exact = c.exact;
     for (auto &g : m->graphs) {
         if (g.kv_k == key.kv_k && g.kv_vt == key.kv_vt && g.ws == key.ws && g.logits == key.logits &&
-            g.n_ctx == key.n_ctx && g.n == key.n && g.p0 == key.p0 && g.ub == key.ub && g.prune == key.prune) {
+            g.n_ctx == key.n_ctx && g.n == key.n && g.p0 == key.p0 && g.ub == key.ub && g.prune == key.prune &&
+            g.exact == key.exact) {
             g.last_use = ++m->graph_clock;
             return hipGraphLaunch(g.exec, c.s) == hipSuccess ? PPX_OK : PPX_E_HIP;
         }
@@ -686,6 +810,8 @@ int prefill(ppx_model *m, ppx_kv *kv, const int32_t *tokens, int n, const ppx_pr
         c.tm = p->timing;
     }
     if (ws_bytes < c.L.total) return PPX_E_NOMEM;
+    if (p->precision != PPX_PRECISION_FAST && p->precision != PPX_PRECISION_EXACT) return PPX_E_INVAL;
+    c.exact = p->precision == PPX_PRECISION_EXACT;
     const int L = I.n_layer, Ls = I.n_layer_kv_from_start, d = I.d_model;
     const int can = predicate(L, Ls, p->embeddings, p->n_seq_max, p->embeddings_layer_inp, 1);
     bool prune;
@@ -833,6 +959,7 @@ int prefill_multi(ppx_model *m, const ppx_seq *seqs, int k, const ppx_prefill_pa
     if (p->debug_rows || p->debug_hidden) return PPX_E_UNSUPPORTED;
     if (p->n_seq_max < k) return PPX_E_INVAL;
     if (p->n_ubatch < 1 || p->n_ubatch > PPX_MAX_UBATCH) return PPX_E_INVAL;
+    if (p->precision != PPX_PRECISION_FAST && p->precision != PPX_PRECISION_EXACT) return PPX_E_INVAL;
     long T = 0;
     int nctx_max = 1;
     for (int q = 0; q < k; ++q) {
@@ -982,6 +1109,7 @@ int prefill_multi(ppx_model *m, const ppx_seq *seqs, int k, const ppx_prefill_pa
     float *xk = reinterpret_cast<float *>(wsb + ML.xk);
 
     Ctx c{m, nullptr, s, wsb, ML.w};
+    c.exact = p->precision == PPX_PRECISION_EXACT;
     if (p->timing) {
         std::memset(p->timing, 0, sizeof(*p->timing));
         c.tm = p->timing;
@@ -1038,7 +1166,8 @@ int prefill_multi(ppx_model *m, const ppx_seq *seqs, int k, const ppx_prefill_pa
         int st = PPX_OK;
         {
             hipEvent_t ev0 = c.begin();
-            st = launch_gemm(gh, c.s);
+            // exact precision keeps the head on the fp32-class single-row path
+            st = c.exact ? PPX_E_UNSUPPORTED : launch_gemm(gh, c.s);
             if (st == PPX_E_UNSUPPORTED) {
                 // an output width the MFMA tiles do not divide: one fp32 row at a time
                 st = PPX_OK;
@@ -1057,7 +1186,8 @@ int prefill_multi(ppx_model *m, const ppx_seq *seqs, int k, const ppx_prefill_pa
     };
     if (!c.tm && graphs_enabled()) {
         std::vector<long long> key = {(long long)(uintptr_t)wsb, (long long)(uintptr_t)logits, T, ub, k, prune,
-                                      nctx_max, (long long)ubs.size(), tail.nwg, tail.split.kc, tail.split.nkc};
+                                      nctx_max, (long long)ubs.size(), tail.nwg, tail.split.kc, tail.split.nkc,
+                                      c.exact};
         for (const Ub &U : ubs) {
             const long long v[] = {U.M, (long long)U.wg0, U.nwg, U.split.kc, U.split.nkc, U.pair0, U.npairs};
             key.insert(key.end(), v, v + 7);

@@ -116,7 +116,10 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, const f4 (&acc)
                 for (int j = 0; j < TN; ++j) {
                     const int col = c0 + j * 16 + lc;
                     const float P = a.ple_s * q4_raw_weight(prow, a.ple_col0 + col);
-                    a.out_f16[tiled_index(row, col, E)] = (_Float16)(gelu_tanh_f(acc[i][j][r]) * P);
+                    const float v = gelu_tanh_f(acc[i][j][r]) * P;
+                    const _Float16 hv = (_Float16)v;
+                    a.out_f16[tiled_index(row, col, E)] = hv;
+                    if (a.out_lo) a.out_lo[tiled_index(row, col, E)] = (_Float16)(v - (float)hv);
                 }
             }
     } else if (a.epi == EPI_GLU) {
@@ -168,8 +171,14 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, const f4 (&acc)
                         const float g0 = lo ? v0 : p0, u0 = lo ? p0 : v0;
                         const float g1 = lo ? v1 : p1, u1 = lo ? p1 : v1;
                         const int row = r0 + i * 16 + lr + 2 * h;
-                        if (row < a.M) a.out_f16[tiled_index(row, f, F)] = (_Float16)(act_f(a.act, g0) * u0);
-                        if (row + 1 < a.M) a.out_f16[tiled_index(row + 1, f, F)] = (_Float16)(act_f(a.act, g1) * u1);
+                        const float y0 = act_f(a.act, g0) * u0, y1 = act_f(a.act, g1) * u1;
+                        const _Float16 h0 = (_Float16)y0, h1 = (_Float16)y1;
+                        if (row < a.M) a.out_f16[tiled_index(row, f, F)] = h0;
+                        if (row + 1 < a.M) a.out_f16[tiled_index(row + 1, f, F)] = h1;
+                        if (a.out_lo) {
+                            if (row < a.M) a.out_lo[tiled_index(row, f, F)] = (_Float16)(y0 - (float)h0);
+                            if (row + 1 < a.M) a.out_lo[tiled_index(row + 1, f, F)] = (_Float16)(y1 - (float)h1);
+                        }
                     }
                 }
             }
@@ -198,7 +207,11 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, const f4 (&acc)
                         const float2 cs = a.rope[(size_t)pos * half + ii];
                         const float ra = va * cs.x - vb * cs.y;
                         const float rb = va * cs.y + vb * cs.x;
-                        if (isq) {
+                        if (isq && a.q32) {
+                            float *q = a.q32 + (size_t)row * a.qd + h * hd;
+                            q[ii] = ra;
+                            q[ii + half] = rb;
+                        } else if (isq) {
                             __half *q = a.out_f16 + (size_t)row * a.qd + h * hd;
                             q[ii] = __float2half(ra);
                             q[ii + half] = __float2half(rb);

@@ -76,7 +76,7 @@ struct ppx_model {
     // kernels' arguments depend on; token ids are read from device memory.
     struct Graph {
         const void *kv_k = nullptr, *kv_vt = nullptr, *ws = nullptr, *logits = nullptr;
-        int n_ctx = 0, n = 0, p0 = 0, ub = 0, prune = 0;
+        int n_ctx = 0, n = 0, p0 = 0, ub = 0, prune = 0, exact = 0;
         hipGraphExec_t exec = nullptr;
         unsigned long long last_use = 0;
     };
@@ -140,6 +140,11 @@ struct GemmArgs {
     int epi = EPI_F32;
     float *out_f32 = nullptr;   // EPI_F32 (ld = N), EPI_ADD residual (ld = N)
     __half *out_f16 = nullptr;  // EPI_QKV q16 [M][qd] row-major; EPI_GLU h [M][F], EPI_PLE [M][E] tiled
+    // exact-precision outputs (the exact-weight kernel only): EPI_QKV writes Q
+    // in fp32 to q32 [M][qd] row-major instead of q16; EPI_GLU / EPI_PLE also
+    // write the low part fp16(v - fp16(v)) to out_lo, tiled as out_f16
+    float *q32 = nullptr;
+    __half *out_lo = nullptr;
     // rope / cache (EPI_QKV)
     int qd = 0, kvd = 0, hd = 0;
     int pos0 = 0;               // position of row 0
@@ -252,8 +257,20 @@ struct AttnArgs {
     int nwg = 0;
     const KVRef *seq_kv = nullptr;
     const int32_t *row_pos = nullptr;
+    // exact precision: q32 fp32 [M][H][hd] replaces q; the output goes to o
+    // (high part) and o_lo (fp16(v - fp16(v))), both fragment-tiled; with
+    // rows of several sequences row r reads the cache seq_kv[row_seq[r]]
+    const float *q32 = nullptr;
+    __half *o_lo = nullptr;
+    const int32_t *row_seq = nullptr;
 };
 int launch_attn_prefill(const AttnArgs &a, hipStream_t s);
+// Causal attention of M rows at ~fp32 accuracy (exact precision): one
+// workgroup per (row, KV head) runs an online softmax over 32-key chunks with
+// both products on MFMA, every fp32 operand split into fp16 high and low parts
+// against the exact fp16 keys and values.  Needs a.q32 and a.o_lo; a.part is
+// not used.
+int launch_attn_rows_exact(const AttnArgs &a, hipStream_t s);
 
 struct Attn1Args {
     const float *q = nullptr;  // [H][hd]

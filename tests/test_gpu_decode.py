@@ -4,8 +4,10 @@ as the prefill of that one token at position n_pos (the pages' generation
 runs reuse the prefill's cache), so the checks are:
   * logits of every decoded token vs the fp64 oracle resumed one token at a
     time from the same cache (max-abs 2e-2, same top-1);
-  * the appended K/V vs the oracle's (|d| <= 1e-2 + one fp16 ulp) where the
-    cache entry depends on the row's own input (layer 0);
+  * every owning layer's K/V vs the oracle's (|d| <= 1e-2 + one fp16 ulp),
+    the appended rows and the prefilled ones (the tiny model's prefill runs
+    at exact precision: its fp16-operand path cannot hold layer 1 to the
+    bound, see test_conditioning.py);
   * at the E2B-like shape, decode == ppx_prefill of the one token from the
     same snapshot;
   * errors leave n_pos unchanged.
@@ -48,7 +50,7 @@ def test_decode_vs_oracle(ppx, cfg, n0, steps):
     oracle.prefill(om, okv, toks[:n0], prune=True)
     mm = engine_model(ppx, cfg)
     kv = ppx.KVCache(mm, n0 + steps)
-    mm.prefill(toks[:n0], kv, n_ubatch=512)
+    mm.prefill(toks[:n0], kv, n_ubatch=512, precision="exact" if cfg == "tiny" else "fast")
     for k in range(steps):
         pos = n0 + k
         ref = oracle.prefill(om, okv, toks[pos:pos + 1], prune=True).astype(np.float64)
@@ -58,10 +60,9 @@ def test_decode_vs_oracle(ppx, cfg, n0, steps):
         ok, d = logits_ok(got, ref)
         print(f"{cfg} decode at {pos}: logits max-abs {d:.3e}")
         assert ok, (pos, d)
-        # layer 0's K/V at the new position depend on the token's embedding only
         K, V = kv.kv_tensors()
-        for g, want in ((K[0, pos], okv.K[0, pos]), (V[0, pos], okv.V[0, pos])):
-            okk, dk = kv_within(g.cpu().numpy()[None], want[None])
+        for g, want in ((K[:, :pos + 1], okv.K[:, :pos + 1]), (V[:, :pos + 1], okv.V[:, :pos + 1])):
+            okk, dk = kv_within(g.cpu().numpy(), want)
             assert okk, (pos, dk)
 
 

@@ -85,8 +85,33 @@ def check_kv(ppx, cfg, n, kv, rkv, rows, unconditional_layers):
             assert okk, ("conditional", il, dk)
 
 
-@pytest.mark.parametrize("ub,prune", [(64, "auto"), (16, "auto"), (64, "off"), (7, "off")])
+TINY_RUNS = [(64, "auto"), (16, "auto"), (64, "off"), (7, "off")]
+
+
+@pytest.mark.parametrize("ub,prune", TINY_RUNS)
+def test_tiny_vs_oracle_exact(ppx, ub, prune):
+    """Exact precision: logits and every owning layer's K/V against the
+    oracle's cache, unconditionally, to the KV bound."""
+    n = 64
+    ref, rkv = run_oracle("tiny", n)
+    mm = engine_model(ppx, "tiny")
+    kv = ppx.KVCache(mm, n)
+    lg = mm.prefill(synth.prompt("tiny", n), kv, n_ubatch=ub, prune=prune, precision="exact").cpu().numpy()
+    ok, d = logits_ok(lg, ref)
+    assert ok, d
+    K, V = kv.kv_tensors()
+    for il in range(mm.info["n_layer_kv_from_start"]):
+        for got, want in ((K[il, :n], rkv.K[il, :n]), (V[il, :n], rkv.V[il, :n])):
+            okk, dk = kv_within(got.cpu().numpy(), want)
+            print(f"exact ub={ub} prune={prune} layer {il}: KV max-abs {dk:.2e}")
+            assert okk, (il, dk)
+
+
+@pytest.mark.parametrize("ub,prune", TINY_RUNS)
 def test_tiny_vs_oracle(ppx, ub, prune):
+    """Fast precision: logits against the oracle; layer 0's K/V against the
+    oracle's cache (they depend on the embedding only), every owning layer's
+    K/V against the oracle's projection of the engine's own layer inputs."""
     n = 64
     ref, rkv = run_oracle("tiny", n)
     mm = engine_model(ppx, "tiny")
@@ -95,9 +120,25 @@ def test_tiny_vs_oracle(ppx, ub, prune):
     lg = mm.prefill(synth.prompt("tiny", n), kv, n_ubatch=ub, prune=prune, debug_rows=rows).cpu().numpy()
     ok, d = logits_ok(lg, ref)
     assert ok, d
-    # layer 0's K/V depend on the embedding only; layer 1's carry layer 0's
-    # attention, where fp16 operand rounding is amplified by near-tied scores
     check_kv(ppx, "tiny", n, kv, rkv, rows.cpu().numpy().astype(np.float64), [0])
+
+
+@pytest.mark.xfail(reason="fp16 MFMA operands cannot hold the tiny model's layer-1 K/V to 1e-2: its layer-1 "
+                          "values reach |v| ~ 12 and layer 0 amplifies fp16 rounding of the query and the "
+                          "attention output alone past the bound (tests/test_conditioning.py shows it on the "
+                          "CPU); the exact precision holds every layer (test_tiny_vs_oracle_exact)",
+                   strict=True)
+def test_tiny_fast_every_layer_kv_unconditional(ppx):
+    n = 64
+    ref, rkv = run_oracle("tiny", n)
+    mm = engine_model(ppx, "tiny")
+    kv = ppx.KVCache(mm, n)
+    mm.prefill(synth.prompt("tiny", n), kv, n_ubatch=64)
+    K, V = kv.kv_tensors()
+    for il in range(mm.info["n_layer_kv_from_start"]):
+        for got, want in ((K[il, :n], rkv.K[il, :n]), (V[il, :n], rkv.V[il, :n])):
+            okk, dk = kv_within(got.cpu().numpy(), want)
+            assert okk, (il, dk)
 
 
 def test_tiny_invariants(ppx):
@@ -275,11 +316,25 @@ def load_golden(name):
 
 @pytest.mark.parametrize("name,ub,prune", GOLDEN_RUNS, ids=[f"{a}-ub{b}-{c}" for a, b, c in GOLDEN_RUNS])
 def test_full_size_vs_stored_oracle(ppx, name, ub, prune):
+    check_golden(ppx, name, ub, prune, "fast")
+
+
+EXACT_GOLDEN_RUNS = [("e2b_512", 512, "auto"), ("e4b_512", 512, "off"), ("e2b_2048", 512, "auto")]
+
+
+@pytest.mark.parametrize("name,ub,prune", EXACT_GOLDEN_RUNS, ids=[f"{a}-ub{b}-{c}" for a, b, c in EXACT_GOLDEN_RUNS])
+def test_full_size_exact_vs_stored_oracle(ppx, name, ub, prune):
+    check_golden(ppx, name, ub, prune, "exact")
+
+
+def check_golden(ppx, name, ub, prune, precision):
     g, meta = load_golden(name)
     cfg, n = meta["config"], meta["n"]
-    lg, kv = gpu_prefill(ppx, cfg, synth.prompt(cfg, n), n, ub, prune)
+    mm = engine_model(ppx, cfg)
+    kv = ppx.KVCache(mm, n)
+    lg = mm.prefill(synth.prompt(cfg, n), kv, n_ubatch=ub, prune=prune, precision=precision).cpu().numpy()
     ok, d = logits_ok(lg, g["logits"])
-    print(f"{name} ub={ub} prune={prune}: logits max-abs {d:.3e}")
+    print(f"{name} ub={ub} prune={prune} {precision}: logits max-abs {d:.3e}")
     assert ok, d
     K, V = kv.kv_tensors()
     layers = torch.from_numpy(g["kv_layers"]).cuda()

@@ -4,9 +4,9 @@ Each sequence's result is, by definition, that of its prompt run alone, and
 the pruned schedule generalises to one output row per sequence.  Checks:
   * per-sequence logits vs the fp64 oracle's multi-sequence pass (itself
     pinned to the scalar brute force per prompt): max-abs 2e-2, same top-1;
-  * K/V vs the oracle (|d| <= 1e-2 + one fp16 ulp) where the cache entry
-    depends on the row's own input (layer 0, every config; every layer of the
-    TinyLlama-shaped model, as in the single-prompt tests);
+  * K/V of every owning layer vs the oracle (|d| <= 1e-2 + one fp16 ulp);
+    the tiny model runs at exact precision (its fp16-operand path cannot
+    hold layer 1 to the bound, see test_conditioning.py);
   * rows land in their own cache only: layer 0's K/V are bit-identical to a
     single-prompt prefill of the same prompt, and positions past each
     prompt stay untouched;
@@ -61,12 +61,12 @@ def case(cfg, lens, starts, seed_off=0):
     return prompts, pre
 
 
-def engine_caches(ppx, mm, pre, n_ctx):
+def engine_caches(ppx, mm, pre, n_ctx, precision="fast"):
     kvs = []
     for t in pre:
         kv = ppx.KVCache(mm, n_ctx)
         if len(t):
-            mm.prefill(t, kv, n_ubatch=512)
+            mm.prefill(t, kv, n_ubatch=512, precision=precision)
         kvs.append(kv)
     return kvs
 
@@ -96,8 +96,8 @@ def test_tiny_multi_vs_oracle(ppx, ub, prune):
     prompts, pre = case(cfg, lens, starts)
     ref, okvs = oracle_multi(cfg, prompts, pre, n_ctx, prune != "off")
     mm = engine_model(ppx, cfg)
-    kvs = engine_caches(ppx, mm, pre, n_ctx)
-    lg = mm.prefill_multi(prompts, kvs, n_ubatch=ub, prune=prune).cpu().numpy()
+    kvs = engine_caches(ppx, mm, pre, n_ctx, "exact")
+    lg = mm.prefill_multi(prompts, kvs, n_ubatch=ub, prune=prune, precision="exact").cpu().numpy()
     torch.cuda.synchronize()
     for s in range(len(lens)):
         ok, d = logits_ok(lg[s], ref[s])
@@ -106,7 +106,7 @@ def test_tiny_multi_vs_oracle(ppx, ub, prune):
         end = starts[s] + lens[s]
         assert kvs[s].n_pos == end
         K, V = kvs[s].kv_tensors()
-        for got, want in ((K[0, :end], okvs[s].K[0, :end]), (V[0, :end], okvs[s].V[0, :end])):
+        for got, want in ((K[:, :end], okvs[s].K[:, :end]), (V[:, :end], okvs[s].V[:, :end])):
             okk, dk = kv_within(got.cpu().numpy(), want)
             assert okk, (s, dk)
         check_untouched(kvs[s], end)
@@ -152,7 +152,7 @@ def test_e2b_multi_small_vs_oracle(ppx):
         assert ok, (s, d)
         end = starts[s] + lens[s]
         K, V = kvs[s].kv_tensors()
-        for got, want in ((K[0, :end], okvs[s].K[0, :end]), (V[0, :end], okvs[s].V[0, :end])):
+        for got, want in ((K[:, :end], okvs[s].K[:, :end]), (V[:, :end], okvs[s].V[:, :end])):
             okk, dk = kv_within(got.cpu().numpy(), want)
             assert okk, (s, dk)
 
@@ -249,12 +249,11 @@ def test_multi_replay_with_new_prompts_and_caches(ppx):
 def test_tiny_multi_most_sequences(ppx, ub):
     """PPX_MAX_SEQ (64) prompts of 1-5 tokens: the gathered tail is wider than
     the ubatch (16) or every ubatch is one row (1), and 64 rows exceed the
-    head's one-tile path.  Every sequence's logits vs its own single-prompt
-    ppx_prefill (the logit bound), its layer-0 K/V vs the oracle; 65 prompts
-    fail.  (The logits are not held to the oracle here: on this model prompts
-    of two tokens are ill-conditioned for fp16 operands, see
-    test_conditioning.py, and the single-prompt path misses the bound by the
-    same amount.)"""
+    head's one-tile path.  At exact precision (prompts of two tokens are
+    ill-conditioned for fp16 operands on this model, see
+    test_conditioning.py): every sequence's logits vs the oracle and vs its
+    own single-prompt ppx_prefill, every layer's K/V vs the oracle; 65
+    prompts fail."""
     cfg, n_ctx = "tiny", 8
     rng = np.random.default_rng(64)
     lens = tuple(int(v) for v in rng.integers(1, 6, 64))
@@ -262,18 +261,20 @@ def test_tiny_multi_most_sequences(ppx, ub):
     ref, okvs = oracle_multi(cfg, prompts, pre, n_ctx, True)
     mm = engine_model(ppx, cfg)
     kvs = [ppx.KVCache(mm, n_ctx) for _ in lens]
-    lg = mm.prefill_multi(prompts, kvs, n_ubatch=ub).cpu().numpy()
+    lg = mm.prefill_multi(prompts, kvs, n_ubatch=ub, precision="exact").cpu().numpy()
     torch.cuda.synchronize()
     worst = worst_oracle = 0.0
     for s, n in enumerate(lens):
-        one = mm.prefill(prompts[s], ppx.KVCache(mm, n_ctx), n_ubatch=16).cpu().numpy()
+        one = mm.prefill(prompts[s], ppx.KVCache(mm, n_ctx), n_ubatch=16, precision="exact").cpu().numpy()
         ok, d = logits_ok(lg[s], one)
         worst = max(worst, d)
-        worst_oracle = max(worst_oracle, float(np.abs(lg[s] - ref[s]).max()))
+        assert ok, (s, d)
+        ok, d = logits_ok(lg[s], ref[s])
+        worst_oracle = max(worst_oracle, d)
         assert ok, (s, d)
         assert kvs[s].n_pos == n
         K, V = kvs[s].kv_tensors()
-        for got, want in ((K[0, :n], okvs[s].K[0, :n]), (V[0, :n], okvs[s].V[0, :n])):
+        for got, want in ((K[:, :n], okvs[s].K[:, :n]), (V[:, :n], okvs[s].V[:, :n])):
             okk, dk = kv_within(got.cpu().numpy(), want)
             assert okk, (s, dk)
     print(f"64 tiny prompts, ubatch {ub}: worst logits max-abs vs single prompts {worst:.3e}, "
