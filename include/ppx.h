@@ -300,6 +300,20 @@ int ppx_prefill_multi(ppx_model *m, const ppx_seq *seqs, int n_seq, const ppx_pr
 int ppx_decode(ppx_model *m, ppx_kv *kv, int32_t token, void *ws_dev, size_t ws_bytes, float *logits_dev,
                void *hip_stream);
 
+/* ppx_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc): the same kernels run in a scratch array of
+ * ppx_decode_static_limit() bytes (32 MiB) that the library holds on every
+ * GPU it runs on until the process ends.  The call allocates nothing.  It
+ * returns PPX_E_NOMEM when the cache's context needs more scratch than that
+ * (ppx_workspace_bytes(m, 1, n_ctx) > the limit), PPX_E_HIP if the array's
+ * address cannot be looked up, and otherwise behaves as ppx_decode.  Every
+ * call on one GPU shares that GPU's array and leaves its contents behind:
+ * calls that overlap on one GPU (other host threads, other streams) race
+ * and must be serialised by the caller. */
+int ppx_decode_static(ppx_model *m, ppx_kv *kv, int32_t token, float *logits_dev, void *hip_stream);
+size_t ppx_decode_static_limit(void);
+
 /* The prune predicate printed on the llama.cpp Gemma 4 prefill page
  * (section 1): 1 iff crop_before_nextn, 0 < n_layer_kv_from_start < n_layer,
  * !embeddings, n_seq_max == 1 and no embeddings_layer_inp[il] is set for il

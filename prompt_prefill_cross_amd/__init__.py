@@ -87,6 +87,8 @@ SIGNATURES = [
     ("ppx_prefill_multi", c_int, [c_void_p, POINTER(Seq), c_int, POINTER(PrefillParams), c_void_p, c_size_t,
                                   c_void_p, c_void_p]),
     ("ppx_decode", c_int, [c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_void_p, c_void_p]),
+    ("ppx_decode_static", c_int, [c_void_p, c_void_p, c_int, c_void_p, c_void_p]),
+    ("ppx_decode_static_limit", c_size_t, []),
     ("ppx_prefill", c_int, [c_void_p, c_void_p, c_void_p, c_int, POINTER(PrefillParams), c_void_p, c_size_t,
                             c_void_p, c_void_p]),
     ("ppx_prune_predicate", c_int, [c_int, c_int, c_int, c_int, POINTER(c_uint8), c_int]),

@@ -4,6 +4,7 @@
 #include <cstdio>
 #include <cstring>
 #include <fstream>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1525,6 +1526,53 @@ int ppx_decode(ppx_model *m, ppx_kv *kv, int32_t token, void *ws_dev, size_t ws_
                void *hip_stream) {
     return decode(m, kv, token, ws_dev, ws_bytes, logits_dev, (hipStream_t)hip_stream);
 }
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ allocation-free decode
+// The workspace of ppx_decode_static lives in a file-scope device array: each
+// GPU that loads the library holds its own copy until the process ends.  In
+// host code `scratch` names a host-side stand-in, never the device memory:
+// the device address of the current GPU's copy is looked up once per device
+// with hipGetSymbolAddress and used everywhere instead.
+constexpr size_t kStaticScratchBytes = 32ull << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The device address of the current device's scratch array (looked up on the
+// first call on that device), or null if the lookup fails.
+void *static_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+int ppx_decode_static(ppx_model *m, ppx_kv *kv, int32_t token, float *logits_dev, void *hip_stream) {
+    if (!m || !kv) return PPX_E_INVAL;
+    if (kv->m != m) return PPX_E_INVAL;
+    if (ws_layout(m, 1, kv->n_ctx).total > kStaticScratchBytes) return PPX_E_NOMEM;
+    void *ws = static_scratch();
+    if (!ws) return PPX_E_HIP;
+    return decode(m, kv, token, ws, kStaticScratchBytes, logits_dev, (hipStream_t)hip_stream);
+}
+
+size_t ppx_decode_static_limit(void) { return kStaticScratchBytes; }
 
 int ppx_prune_predicate(int n_layer, int n_layer_kv_from_start, int embeddings, int n_seq_max,
                         const uint8_t *embeddings_layer_inp, int crop_before_nextn) {
