@@ -54,8 +54,8 @@ def build(verbose=True):
 
 # ---- host-side sanitizer build of the file parsers (CPU only) ----------------
 # The host code of every source is compiled with AddressSanitizer and
-# UndefinedBehaviorSanitizer (the kernel sources keep their ordinary device
-# code, which the driver never launches; the C++ sources have none) and
+# UndefinedBehaviorSanitizer (the device code is built as usual and never
+# launched by the driver) and
 # linked with fuzz/fuzz_host.cpp into a driver that feeds mutated containers
 # and snapshots to the parsers.  Each -fsanitize= flag is scoped to the host
 # compiler with -Xarch_host.
@@ -78,7 +78,7 @@ def build_fuzz(verbose=True):
 
     def one(src):
         obj = os.path.join(SAN_BUILD, os.path.basename(src) + ".o")
-        dev = [f"--offload-arch={ARCH}"] if src.endswith(".hip") else ["--offload-host-only"]
+        dev = [f"--offload-arch={ARCH}"] if src != FUZZ_SRC else ["--offload-host-only"]
         r = subprocess.run([HIPCC, "-x", "hip", *dev, *flags, "-c", src, "-o", obj], capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc (host, sanitizers) failed for {src}:\n{r.stderr}")

@@ -68,14 +68,19 @@ struct ACfg {
     static_assert(DEPTH * STAGE_UNITS * 16 <= 160 * 1024, "LDS");
 };
 
+// Grid (column blocks, key chunks, KV heads x units): unit z / KVH of the
+// group, KV head z % KVH; a unit with fewer column blocks or key chunks than
+// the launch's largest leaves the surplus workgroups idle.
 template <class C>
-__global__ __launch_bounds__(C::NT) void k_attn_prefill(AttnArgs a) {
+__global__ __launch_bounds__(C::NT) void k_attn_prefill(const AttnGroup grp) {
     constexpr int HD = C::HD, KB = C::KB, DT = C::DT, CPW = C::CPW;
     __shared__ h8 ring[C::DEPTH * C::STAGE_UNITS];
 
+    const AttnArgs &a = grp.u[blockIdx.z / grp.u[0].KVH];
     const int tid = threadIdx.x, lane = tid & 63, wave = attn_wave_id();
     const int G = a.H / a.KVH;
-    const int ck = blockIdx.y, kvh = blockIdx.z;
+    const int ck = blockIdx.y, kvh = blockIdx.z % a.KVH;
+    if (ck >= a.nkc) return;  // the whole workgroup
     const int lc = lane & 15, lg = lane >> 4;
     // the workgroup's rows: [row0, row0 + M) of the launch, one sequence's
     // positions pos0 .. pos0 + M - 1, read against that sequence's cache
@@ -91,6 +96,8 @@ __global__ __launch_bounds__(C::NT) void k_attn_prefill(AttnArgs a) {
         kp = ref.k;
         vtp = ref.vt;
         vld = ref.vld;
+    } else if (cb * C::CB >= M * G) {
+        return;  // past this unit's query columns (the whole workgroup)
     }
 
     const int tmax = min(M - 1, (cb * C::CB + C::CB - 1) / G);
@@ -302,8 +309,9 @@ __global__ __launch_bounds__(C::NT) void k_attn_prefill(AttnArgs a) {
 // wave per (row, head): lane l owns dims 4l .. 4l+3 of each 256-dim slice;
 // the chunks are summed in chunk order.
 template <int HD>
-__global__ __launch_bounds__(256) void k_attn_prefill_merge(AttnArgs a) {
+__global__ __launch_bounds__(256) void k_attn_prefill_merge(const AttnGroup grp) {
     static_assert(ATTN_MAX_CHUNKS <= 64, "one chunk per lane");
+    const AttnArgs &a = grp.u[blockIdx.y];
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
     if (w >= a.M * a.H) return;
@@ -664,32 +672,44 @@ size_t attn_prefill_scratch_floats(int M, int H, int hd, int n_ctx) {
     return (size_t)nkc * M * H * (hd / 2 + 2);  // fp16 chunk outputs, then fp32 (max, sum) pairs
 }
 
-int launch_attn_prefill(const AttnArgs &a0, hipStream_t s) {
-    AttnArgs a = a0;
-    if (a.M <= 0) return PPX_OK;
-    const int G = a.H / a.KVH;
-    if (a.H % a.KVH || 64 % G) return PPX_E_UNSUPPORTED;
-    int nx;
-    if (a.wg) {
-        // several sequences: the caller built the workgroup table and the split
-        if (a.nwg < 1 || !a.seq_kv || !a.row_pos || a.kc < ATTN_MIN_KC || a.kc % 64 || a.nkc < 1 ||
-            a.nkc > ATTN_MAX_CHUNKS)
+int launch_attn_prefill_group(const AttnArgs *units, int n, hipStream_t s) {
+    if (n < 1 || n > kMaxUnits) return PPX_E_INVAL;
+    AttnGroup g;
+    int nx = 0, ny = 0;
+    for (int i = 0; i < n; ++i) {
+        AttnArgs a = units[i];
+        if (a.M <= 0) continue;
+        const int G = a.H / a.KVH;
+        if (a.H % a.KVH || 64 % G) return PPX_E_UNSUPPORTED;
+        if (g.n && (a.H != g.u[0].H || a.KVH != g.u[0].KVH || a.hd != g.u[0].hd || !a.wg != !g.u[0].wg))
             return PPX_E_INVAL;
-        nx = a.nwg;
-    } else {
-        if (a.vld % 64 || a.pos0 + a.M > a.vld) return PPX_E_UNSUPPORTED;
-        const AttnSplit sp = attn_split(a.M, a.H, a.KVH, a.pos0);
-        a.kc = sp.kc;
-        a.nkc = sp.nkc;
-        nx = (a.M * G + ATTN_CB - 1) / ATTN_CB;
+        int x;
+        if (a.wg) {
+            // several sequences: the caller built the workgroup table and the split
+            if (n != 1 || a.nwg < 1 || !a.seq_kv || !a.row_pos || a.kc < ATTN_MIN_KC || a.kc % 64 || a.nkc < 1 ||
+                a.nkc > ATTN_MAX_CHUNKS)
+                return PPX_E_INVAL;
+            x = a.nwg;
+        } else {
+            if (a.vld % 64 || a.pos0 + a.M > a.vld) return PPX_E_UNSUPPORTED;
+            const AttnSplit sp = attn_split(a.M, a.H, a.KVH, a.pos0);
+            a.kc = sp.kc;
+            a.nkc = sp.nkc;
+            x = (a.M * G + ATTN_CB - 1) / ATTN_CB;
+        }
+        if (a.nkc > 1 && !a.part) return PPX_E_INVAL;
+        nx = std::max(nx, x);
+        ny = std::max(ny, a.nkc);
+        g.u[g.n++] = a;
     }
-    if (a.nkc > 1 && !a.part) return PPX_E_INVAL;
-    dim3 grid(nx, a.nkc, a.KVH);
-    switch (a.hd) {
+    if (!g.n) return PPX_OK;
+    const AttnArgs &a0 = g.u[0];
+    dim3 grid(nx, ny, a0.KVH * g.n);
+    switch (a0.hd) {
 #define PPX_ATTN(hd_, np_, depth_)                                                                   \
     case hd_: {                                                                                      \
         using C = ACfg<hd_, ATTN_CPW, ATTN_NC, np_, depth_>;                                         \
-        hipLaunchKernelGGL((k_attn_prefill<C>), grid, dim3(C::NT), 0, s, a);                         \
+        hipLaunchKernelGGL((k_attn_prefill<C>), grid, dim3(C::NT), 0, s, g);                         \
         break;                                                                                       \
     }
         PPX_ATTN(64, 1, 8)
@@ -698,15 +718,26 @@ int launch_attn_prefill(const AttnArgs &a0, hipStream_t s) {
 #undef PPX_ATTN
     default: return PPX_E_UNSUPPORTED;
     }
-    if (a.nkc == 1) return ok();
     if (hipGetLastError() != hipSuccess) return PPX_E_HIP;
-    switch (a.hd) {
-    case 64: hipLaunchKernelGGL(k_attn_prefill_merge<64>, dim3((a.M * a.H + 3) / 4), dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL(k_attn_prefill_merge<128>, dim3((a.M * a.H + 3) / 4), dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL(k_attn_prefill_merge<256>, dim3((a.M * a.H + 3) / 4), dim3(256), 0, s, a); break;
+    // the key-chunk merge, for the units whose keys were split
+    AttnGroup mg;
+    int mrows = 0;
+    for (int i = 0; i < g.n; ++i)
+        if (g.u[i].nkc > 1) {
+            mg.u[mg.n++] = g.u[i];
+            mrows = std::max(mrows, g.u[i].M * g.u[i].H);
+        }
+    if (!mg.n) return PPX_OK;
+    const dim3 mgrid((mrows + 3) / 4, mg.n);
+    switch (a0.hd) {
+    case 64: hipLaunchKernelGGL(k_attn_prefill_merge<64>, mgrid, dim3(256), 0, s, mg); break;
+    case 128: hipLaunchKernelGGL(k_attn_prefill_merge<128>, mgrid, dim3(256), 0, s, mg); break;
+    default: hipLaunchKernelGGL(k_attn_prefill_merge<256>, mgrid, dim3(256), 0, s, mg); break;
     }
     return ok();
 }
+
+int launch_attn_prefill(const AttnArgs &a, hipStream_t s) { return launch_attn_prefill_group(&a, 1, s); }
 
 int launch_attn_rows_exact(const AttnArgs &a, hipStream_t s) {
     if (a.M <= 0) return PPX_OK;

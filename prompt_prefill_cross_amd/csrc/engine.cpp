@@ -27,20 +27,13 @@ namespace {
 
 inline size_t al(size_t x) { return (x + 255) / 256 * 256; }
 
-// Ubatches in flight at once: ubatch u runs on slot u % kSlots (its own
-// stream and its own activation buffers), and its attention waits only for
-// the earlier ubatches' K/V of that layer.  Measured on the E2B-like shapes
-// with two slots, kernels of the two streams overlapped in under 5% of the
-// launches (each launch already occupies every CU) and the prefill got
-// slower, so one slot is used: the schedule is then the plain serial one.
-constexpr int kSlots = 1;
-
 // Workspace layout of one prefill (offsets from the workspace base).  The
-// per-ubatch buffers (x .. ap_part) repeat once per slot, slot_stride apart.
+// per-ubatch buffers (x .. gpart) repeat once per slot, slot_stride apart:
+// a prefill keeps up to nslots ubatches in flight, each in its own slot.
 struct WsLayout {
     size_t tok;
     size_t x, a16, a16lo, q16, o16, h16, p16, ap_part, gpart;  // slot 0
-    size_t q32, o16lo, h16lo, p16lo;                           // exact precision only (slot 0)
+    size_t q32, o16lo, h16lo, p16lo;                           // exact precision only (one ubatch at a time)
     size_t gpart_floats;                                       // split-K partials of one GEMM
     size_t slot_stride;
     int nslots;
@@ -49,7 +42,7 @@ struct WsLayout {
     size_t total;
 };
 
-WsLayout ws_layout(const ppx_model *m, int ub, int n_ctx) {
+WsLayout ws_layout(const ppx_model *m, int ub, int n_ctx, int nslots) {
     const ppx_model_info &I = m->info;
     const int d = I.d_model, qd = I.n_head * I.head_dim, F = I.n_ff, E = I.ple_dim;
     WsLayout w{};
@@ -80,8 +73,8 @@ WsLayout ws_layout(const ppx_model *m, int ub, int n_ctx) {
         w.gpart = take(4 * std::max<size_t>(pf, 1));
     }
     w.slot_stride = o - s0;
-    w.nslots = kSlots;
-    o += w.slot_stride * (kSlots - 1);
+    w.nslots = std::max(1, nslots);
+    o += w.slot_stride * (w.nslots - 1);
     // exact precision: fp32 queries and the low parts of the split operands
     w.q32 = take(4ull * ub * qd);
     w.o16lo = take(2ull * ub16 * qd);
@@ -95,6 +88,13 @@ WsLayout ws_layout(const ppx_model *m, int ub, int n_ctx) {
     w.at_part = take(4 * attn1_scratch_floats(I.n_head, I.head_dim, std::max(n_ctx, 1)));
     w.total = o;
     return w;
+}
+
+// Ubatches a prefill keeps in flight: as many as the prompt has, at most one
+// per layer they run through and at most kMaxUnits.
+int prefill_slots(const ppx_model *m, int ub, int n_ctx) {
+    const long nub = ((long)std::max(n_ctx, 1) + ub - 1) / ub;
+    return (int)std::max(1L, std::min<long>({nub, (long)m->info.n_layer, (long)kMaxUnits}));
 }
 
 int predicate(int L, int Ls, int emb, int nseq, const uint8_t *inp, int crop) {
@@ -125,23 +125,20 @@ struct Ctx {
         bool gathered = false;  // the sequences' output rows, one each
     };
     const Rows *rows = nullptr;
-    // K/V ordering between ubatches on different streams: after writing layer
-    // l's K/V, kv_done[l] is recorded; before attention reads layer l's cache,
-    // kv_wait[l] (the previous ubatch's record, if on another stream) is
-    // waited for.  Null entries mean no ordering is needed.
-    std::vector<hipEvent_t> kv_done, kv_wait;
     struct Rec { int phase; hipEvent_t a, b; bool glu; };
     std::vector<Rec> recs;
     size_t next_ev = 0;
     template <typename T>
     T *at(size_t off) const { return reinterpret_cast<T *>(ws + off); }
-    // a per-ubatch buffer of the current slot
+    // a per-ubatch buffer of slot k (default: the current slot)
     template <typename T>
-    T *sl(size_t off) const { return reinterpret_cast<T *>(ws + off + (size_t)slot * L.slot_stride); }
-    // a row-batched GEMM of the current slot, with the slot's split-K partial space
-    GemmArgs gemm() const {
+    T *sl(size_t off, int k = -1) const {
+        return reinterpret_cast<T *>(ws + off + (size_t)(k < 0 ? slot : k) * L.slot_stride);
+    }
+    // a row-batched GEMM of slot k, with that slot's split-K partial space
+    GemmArgs gemm(int k = -1) const {
         GemmArgs g;
-        g.part = sl<float>(L.gpart);
+        g.part = sl<float>(L.gpart, k);
         g.part_floats = L.gpart_floats;
         g.few_rows = rows && rows->gathered;
         return g;
@@ -309,163 +306,222 @@ int layer_rows_exact(Ctx &c, int il, int M, int row0, int pos0) {
     return PPX_OK;
 }
 
-// One ubatch of M rows through layer il on the MFMA path.
-int layer_rows(Ctx &c, int il, int M, int row0, int pos0) {
-    if (c.exact) return layer_rows_exact(c, il, M, row0, pos0);
+// One ubatch in flight: rows [row0, row0 + M) of the call (token ids from
+// row0 on), positions pos0 .., running layer il with the buffers of slot.
+struct Unit {
+    int il, M, row0, pos0, slot;
+};
+
+// One step of the row-batched layers: every unit runs its own layer, and each
+// operation of the layer is one launch over all the units (the same shapes,
+// each unit with its own weights, activations and cache).
+int layer_rows_group(Ctx &c, const Unit *U, int n) {
+    if (n < 1 || n > kMaxUnits) return PPX_E_INVAL;
+    if (c.exact) {
+        if (n != 1) return PPX_E_INVAL;  // one ubatch at a time
+        return layer_rows_exact(c, U[0].il, U[0].M, U[0].row0, U[0].pos0);
+    }
     const ppx_model *m = c.m;
     const ppx_model_info &I = m->info;
-    const LayerW &w = m->layers[il];
-    const int d = I.d_model, hd = I.head_dim, qd = I.n_head * hd, kvd = I.kv_dim, F = I.n_ff;
-    float *x = c.sl<float>(c.L.x);
-    __half *a16 = c.sl<__half>(c.L.a16);
-    __half *q16 = c.sl<__half>(c.L.q16);
-    __half *o16 = c.sl<__half>(c.L.o16);
-    __half *h16 = c.sl<__half>(c.L.h16);
+    const int d = I.d_model, hd = I.head_dim, qd = I.n_head * hd, kvd = I.kv_dim;
     const Ctx::Rows *R = c.rows;
+    if (R && n != 1) return PPX_E_INVAL;
     const size_t lstride = R ? 0 : (size_t)c.kv->n_ctx * kvd;
     const size_t vstride = R ? 0 : (size_t)c.kv->vld * kvd;
+    auto W = [&](int i) -> const LayerW & { return m->layers[U[i].il]; };
+    auto X = [&](int i) { return c.sl<float>(c.L.x, U[i].slot); };
+    auto H16 = [&](int i, size_t off) { return c.sl<__half>(off, U[i].slot); };
 
-    __half *a16lo = c.sl<__half>(c.L.a16lo);
-    if (w.own)
-        PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_rmsnorm_split(x, w.attn_norm, m->eps, M, d, a16, a16lo, c.s));
-    else
-        PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_rmsnorm_f16(x, w.attn_norm, m->eps, M, d, a16, c.s));
-    GemmArgs g = c.gemm();
-    g.A = a16;
-    g.lda = d;
-    g.M = M;
-    g.W = w.wq;
-    g.epi = EPI_QKV;
-    g.out_f16 = q16;
-    g.qd = qd;
-    g.kvd = 0;
-    g.hd = hd;
-    g.pos0 = pos0;
-    g.rope = m->rope;
-    if (R) g.row_pos = R->pos;
-    PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm(g, c.s));
-    if (w.own) {
-        // K and V on the exact-weight path, straight into this layer's cache rows
-        GemmArgs gk = g;
-        gk.A2 = a16lo;
-        gk.W = w.wkv;
-        gk.qd = 0;
-        gk.kvd = kvd;
-        gk.out_f16 = nullptr;
-        if (R) {
-            gk.row_seq = R->seq;
-            gk.seq_kv = R->kv + (size_t)il * R->nseq;
-        } else {
-            gk.kc = c.kv->k + il * lstride;
-            gk.vc = c.kv->vt + il * vstride;
-            gk.vld = c.kv->vld;
+    // attention RMSNorm: owning layers also write the low part (the K|V operand)
+    {
+        NormUnit own[kMaxUnits], shr[kMaxUnits];
+        int no = 0, ns = 0;
+        for (int i = 0; i < n; ++i) {
+            NormUnit u;
+            u.x = X(i);
+            u.g = W(i).attn_norm;
+            u.hi = H16(i, c.L.a16);
+            u.M = U[i].M;
+            if (W(i).own) {
+                u.lo = H16(i, c.L.a16lo);
+                own[no++] = u;
+            } else {
+                shr[ns++] = u;
+            }
         }
-        PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm_exact(gk, c.s));
+        if (no) PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_rmsnorm_group(own, no, m->eps, d, true, c.s));
+        if (ns) PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_rmsnorm_group(shr, ns, m->eps, d, false, c.s));
     }
-    // earlier ubatches' K/V of the layer read here (owning: this layer; shared: its source)
-    if (!c.kv_wait.empty() && c.kv_wait[w.src] && hipStreamWaitEvent(c.s, c.kv_wait[w.src], 0) != hipSuccess)
-        return PPX_E_HIP;
-    if (w.own && !c.kv_done.empty() && c.kv_done[il] && hipEventRecord(c.kv_done[il], c.s) != hipSuccess)
-        return PPX_E_HIP;
-
-    AttnArgs at;
-    at.q = q16;
-    if (R) {
-        at.wg = R->wg;
-        at.nwg = R->nwg;
-        at.seq_kv = R->kv + (size_t)w.src * R->nseq;
-        at.row_pos = R->pos;
-        at.kc = R->split.kc;
-        at.nkc = R->split.nkc;
-    } else {
-        at.k = c.kv->k + (size_t)w.src * lstride;
-        at.vt = c.kv->vt + (size_t)w.src * vstride;
-        at.vld = c.kv->vld;
+    GemmArgs g[kMaxUnits];
+    for (int i = 0; i < n; ++i) {
+        g[i] = c.gemm(U[i].slot);
+        g[i].A = H16(i, c.L.a16);
+        g[i].lda = d;
+        g[i].M = U[i].M;
+        g[i].W = W(i).wq;
+        g[i].epi = EPI_QKV;
+        g[i].out_f16 = H16(i, c.L.q16);
+        g[i].qd = qd;
+        g[i].kvd = 0;
+        g[i].hd = hd;
+        g[i].pos0 = U[i].pos0;
+        g[i].rope = m->rope;
+        if (R) g[i].row_pos = R->pos;
     }
-    at.part = c.sl<float>(c.L.ap_part);
-    at.o = o16;
-    at.M = M;
-    at.H = I.n_head;
-    at.KVH = I.n_kv_head;
-    at.hd = hd;
-    at.pos0 = pos0;
-    PPX_LAUNCH(c, PPX_PHASE_ATTN, launch_attn_prefill(at, c.s));
-
-    GemmArgs go = c.gemm();
-    go.A = o16;
-    go.lda = qd;
-    go.M = M;
-    go.W = w.wo;
-    go.epi = EPI_ADD;
-    go.out_f32 = x;
-    PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm(go, c.s));
-
-    PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_rmsnorm_f16(x, w.ffn_norm, m->eps, M, d, a16, c.s));
-    GemmArgs gu = c.gemm();
-    gu.A = a16;
-    gu.lda = d;
-    gu.M = M;
-    gu.W = w.wgu;
-    gu.epi = EPI_GLU;
-    gu.out_f16 = h16;
-    gu.act = I.act;
+    PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm_group(g, n, c.s));
+    {
+        // K and V on the exact-weight path, straight into the owning layers' cache rows
+        GemmArgs gk[kMaxUnits];
+        int nk = 0;
+        for (int i = 0; i < n; ++i) {
+            if (!W(i).own) continue;
+            GemmArgs &k = gk[nk++];
+            k = g[i];
+            k.A2 = H16(i, c.L.a16lo);
+            k.W = W(i).wkv;
+            k.qd = 0;
+            k.kvd = kvd;
+            k.out_f16 = nullptr;
+            if (R) {
+                k.row_seq = R->seq;
+                k.seq_kv = R->kv + (size_t)U[i].il * R->nseq;
+            } else {
+                k.kc = c.kv->k + U[i].il * lstride;
+                k.vc = c.kv->vt + U[i].il * vstride;
+                k.vld = c.kv->vld;
+            }
+        }
+        if (nk) PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm_exact_group(gk, nk, c.s));
+    }
+    {
+        // causal attention over the cache of each unit's KV source layer
+        AttnArgs at[kMaxUnits];
+        for (int i = 0; i < n; ++i) {
+            AttnArgs &a = at[i];
+            const int src = W(i).src;
+            a.q = H16(i, c.L.q16);
+            if (R) {
+                a.wg = R->wg;
+                a.nwg = R->nwg;
+                a.seq_kv = R->kv + (size_t)src * R->nseq;
+                a.row_pos = R->pos;
+                a.kc = R->split.kc;
+                a.nkc = R->split.nkc;
+            } else {
+                a.k = c.kv->k + (size_t)src * lstride;
+                a.vt = c.kv->vt + (size_t)src * vstride;
+                a.vld = c.kv->vld;
+            }
+            a.part = c.sl<float>(c.L.ap_part, U[i].slot);
+            a.o = H16(i, c.L.o16);
+            a.M = U[i].M;
+            a.H = I.n_head;
+            a.KVH = I.n_kv_head;
+            a.hd = hd;
+            a.pos0 = U[i].pos0;
+        }
+        PPX_LAUNCH(c, PPX_PHASE_ATTN, launch_attn_prefill_group(at, n, c.s));
+    }
+    for (int i = 0; i < n; ++i) {
+        g[i] = c.gemm(U[i].slot);
+        g[i].A = H16(i, c.L.o16);
+        g[i].lda = qd;
+        g[i].M = U[i].M;
+        g[i].W = W(i).wo;
+        g[i].epi = EPI_ADD;
+        g[i].out_f32 = X(i);
+    }
+    PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm_group(g, n, c.s));
+    {
+        NormUnit nu[kMaxUnits];
+        for (int i = 0; i < n; ++i) {
+            nu[i].x = X(i);
+            nu[i].g = W(i).ffn_norm;
+            nu[i].hi = H16(i, c.L.a16);
+            nu[i].M = U[i].M;
+        }
+        PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_rmsnorm_group(nu, n, m->eps, d, false, c.s));
+    }
+    for (int i = 0; i < n; ++i) {
+        g[i] = c.gemm(U[i].slot);
+        g[i].A = H16(i, c.L.a16);
+        g[i].lda = d;
+        g[i].M = U[i].M;
+        g[i].W = W(i).wgu;
+        g[i].epi = EPI_GLU;
+        g[i].out_f16 = H16(i, c.L.h16);
+        g[i].act = I.act;
+    }
     {
         hipEvent_t ev0 = c.begin();
-        PPX_TRY(launch_gemm(gu, c.s));
+        PPX_TRY(launch_gemm_group(g, n, c.s));
         c.end(PPX_PHASE_GEMM, ev0, true);
     }
-
-    GemmArgs gd = c.gemm();
-    gd.A = h16;
-    gd.lda = F;
-    gd.M = M;
-    gd.W = w.wdown;
-    gd.epi = EPI_ADD;
-    gd.out_f32 = x;
-    if (I.ple_dim) {
-        // the per-layer-embedding block's RMSNorm of the updated rows rides on the down projection
-        gd.norm_g = w.ple_norm;
-        gd.norm_eps = m->eps;
-        gd.norm_out = a16;
+    for (int i = 0; i < n; ++i) {
+        g[i] = c.gemm(U[i].slot);
+        g[i].A = H16(i, c.L.h16);
+        g[i].lda = I.n_ff;
+        g[i].M = U[i].M;
+        g[i].W = W(i).wdown;
+        g[i].epi = EPI_ADD;
+        g[i].out_f32 = X(i);
+        if (I.ple_dim) {
+            // the per-layer-embedding block's RMSNorm of the updated rows rides on the down projection
+            g[i].norm_g = W(i).ple_norm;
+            g[i].norm_eps = m->eps;
+            g[i].norm_out = H16(i, c.L.a16);
+        }
     }
-    PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm(gd, c.s));
-
+    PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm_group(g, n, c.s));
     if (I.ple_dim) {
         const int E = I.ple_dim;
-        __half *p16 = c.sl<__half>(c.L.p16);
-        GemmArgs gp = c.gemm();
-        gp.A = a16;
-        gp.lda = d;
-        gp.M = M;
-        gp.W = w.wpg;
-        gp.epi = EPI_PLE;
-        gp.out_f16 = p16;
-        gp.ple_raw = m->ple_raw;
-        gp.tok = R ? R->tok : c.at<int32_t>(c.L.tok) + row0;
-        gp.ple_row_blocks = I.n_layer * E / 32;
-        gp.ple_col0 = il * E;
-        gp.ple_s = w.ple_s;
-        PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm(gp, c.s));
-        GemmArgs gq = c.gemm();
-        gq.A = p16;
-        gq.lda = E;
-        gq.M = M;
-        gq.W = w.wpu;
-        gq.epi = EPI_ADD;
-        gq.out_f32 = x;
-        PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm(gq, c.s));
+        for (int i = 0; i < n; ++i) {
+            g[i] = c.gemm(U[i].slot);
+            g[i].A = H16(i, c.L.a16);
+            g[i].lda = d;
+            g[i].M = U[i].M;
+            g[i].W = W(i).wpg;
+            g[i].epi = EPI_PLE;
+            g[i].out_f16 = H16(i, c.L.p16);
+            g[i].ple_raw = m->ple_raw;
+            g[i].tok = R ? R->tok : c.at<int32_t>(c.L.tok) + U[i].row0;
+            g[i].ple_row_blocks = I.n_layer * E / 32;
+            g[i].ple_col0 = U[i].il * E;
+            g[i].ple_s = W(i).ple_s;
+        }
+        PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm_group(g, n, c.s));
+        for (int i = 0; i < n; ++i) {
+            g[i] = c.gemm(U[i].slot);
+            g[i].A = H16(i, c.L.p16);
+            g[i].lda = E;
+            g[i].M = U[i].M;
+            g[i].W = W(i).wpu;
+            g[i].epi = EPI_ADD;
+            g[i].out_f32 = X(i);
+        }
+        PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm_group(g, n, c.s));
     }
     if (c.tm) {
-        double nk = (double)w.wq.N * w.wq.K + (double)w.wo.N * w.wo.K + (double)w.wgu.N * w.wgu.K +
-                    (double)w.wdown.N * w.wdown.K;
-        if (w.own) nk += (double)w.wkv.N * w.wkv.K;
-        if (I.ple_dim) nk += (double)w.wpg.N * w.wpg.K + (double)w.wpu.N * w.wpu.K;
-        c.tm->gemm_flop += 2.0 * M * nk;
-        c.tm->glu_flop += 2.0 * M * w.wgu.N * w.wgu.K;
-        const double vis = R ? R->vis : (double)M * pos0 + 0.5 * (double)M * (M + 1);  // causal (query, key) pairs
-        c.tm->attn_flop += 4.0 * I.n_head * hd * vis;
+        for (int i = 0; i < n; ++i) {
+            const LayerW &w = W(i);
+            const int M = U[i].M, pos0 = U[i].pos0;
+            double nk = (double)w.wq.N * w.wq.K + (double)w.wo.N * w.wo.K + (double)w.wgu.N * w.wgu.K +
+                        (double)w.wdown.N * w.wdown.K;
+            if (w.own) nk += (double)w.wkv.N * w.wkv.K;
+            if (I.ple_dim) nk += (double)w.wpg.N * w.wpg.K + (double)w.wpu.N * w.wpu.K;
+            c.tm->gemm_flop += 2.0 * M * nk;
+            c.tm->glu_flop += 2.0 * M * w.wgu.N * w.wgu.K;
+            const double vis = R ? R->vis : (double)M * pos0 + 0.5 * (double)M * (M + 1);  // causal (query, key) pairs
+            c.tm->attn_flop += 4.0 * I.n_head * hd * vis;
+        }
     }
     return PPX_OK;
+}
+
+// One ubatch of M rows through layer il on the MFMA path (the current slot).
+int layer_rows(Ctx &c, int il, int M, int row0, int pos0) {
+    const Unit u{il, M, row0, pos0, c.slot};
+    return layer_rows_group(c, &u, 1);
 }
 
 GemvArgs gemv_base(Ctx &c, const float *x, const Q4R &W, int epi, float *out) {
@@ -559,123 +615,108 @@ int head_row(Ctx &c, const float *x_last, float *logits) {
     return PPX_OK;
 }
 
-// Events for ordering work across streams, from a model-owned pool (reused
-// from call to call: every use is a record followed by waits in stream order).
-int sync_events(ppx_model *m, size_t n, std::vector<hipEvent_t> &out) {
-    while (m->sync_events.size() < n) {
-        hipEvent_t e;
-        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return PPX_E_HIP;
-        m->sync_events.push_back(e);
-    }
-    out.assign(m->sync_events.begin(), m->sync_events.begin() + n);
-    return PPX_OK;
-}
-
 // The launch sequence of one prefill call (all ubatches, the pruned tail and
 // the head).  Token ids are read from tok_dev, so the sequence can be recorded
-// once and replayed for any prompt of the same shape.  With several streams,
-// ubatch u runs on streams[u % S] with slot u % S's buffers; the streams fork
-// from and join back into streams[0], and attention waits for the previous
-// ubatch's K/V of the layer it reads.
+// once and replayed for any prompt of the same shape.
+//
+// Ubatches go through the row-batched layers together: up to L.nslots of them
+// are in flight, each in its own slot of buffers, and every step runs each
+// in-flight ubatch through its next layer, one launch per operation over all
+// of them (layer_rows_group).  A ubatch is admitted when a slot is free, so
+// ubatches admitted together advance in lockstep and a later one may trail.
+// Within a step the K|V launch of every unit precedes the attention launch,
+// and a ubatch is never ahead of an earlier one: when ubatch u attends at
+// layer l, every earlier ubatch's K/V of layer l is written, so each ubatch
+// sees exactly the cache of the serial order and its rows go through the same
+// kernels with the same per-ubatch launch shapes (the results are bit for bit
+// those of the serial order).  Debug outputs, extraction and exact precision
+// run one ubatch at a time.
 int enqueue_prefill(Ctx &c, const ppx_prefill_params *p, const int32_t *tok_dev, int n, int p0, int ub,
-                    bool prune, float *logits, hipStream_t *streams, int nstreams) {
+                    bool prune, float *logits) {
     ppx_model *m = c.m;
     const ppx_model_info &I = m->info;
     const int L = I.n_layer, Ls = I.n_layer_kv_from_start, d = I.d_model;
     const int nub = (n + ub - 1) / ub;
-    const int S = std::max(1, std::min({nstreams, nub, c.L.nslots}));
-    std::vector<hipEvent_t> ev;
-    if (S > 1) {
-        // [0] fork, [1..S-1] joins, then per ubatch the K/V record of every layer
-        PPX_TRY(sync_events(m, (size_t)S + (size_t)nub * L, ev));
-        if (hipEventRecord(ev[0], streams[0]) != hipSuccess) return PPX_E_HIP;
-        for (int k = 1; k < S; ++k)
-            if (hipStreamWaitEvent(streams[k], ev[0], 0) != hipSuccess) return PPX_E_HIP;
-    }
-    auto kv_ev = [&](int u, int l) { return ev[(size_t)S + (size_t)u * L + l]; };
+    const int full_layers = prune ? Ls : L;
     // extraction: the flagged layers' inputs, each in its own [n][d] slab
     std::vector<int> slab(L + 1, -1);
     int nslab = 0;
     if (p->embeddings_layer_inp)
         for (int il = 0; il <= L; ++il)
             if (p->embeddings_layer_inp[il]) slab[il] = nslab++;
-    auto extract = [&](int il, const float *x, int M, int s0, hipStream_t s) -> int {
+    auto extract = [&](int il, const float *x, int M, int s0) -> int {
         if (slab[il] < 0) return PPX_OK;
-        return launch_copy_f32(x, p->layer_inp_out + ((size_t)slab[il] * n + s0) * d, M * d, s);
+        return launch_copy_f32(x, p->layer_inp_out + ((size_t)slab[il] * n + s0) * d, M * d, c.s);
     };
+    const bool serial = c.exact || p->debug_rows || p->debug_hidden || nslab || p->embeddings;
+    const int NU = serial ? 1 : std::max(1, std::min({nub, full_layers, c.L.nslots}));
 
-    for (int u = 0; u < nub; ++u) {
-        const int s0 = u * ub;
-        const int M = std::min(ub, n - s0);
-        const bool last = s0 + M == n;
-        const int pos0 = p0 + s0;
-        c.slot = u % S;
-        c.s = streams[c.slot];
-        hipStream_t s = c.s;
-        c.kv_done.assign(S > 1 ? L : 0, nullptr);
-        c.kv_wait.assign(S > 1 ? L : 0, nullptr);
-        if (S > 1)
-            for (int l = 0; l < Ls; ++l) {
-                c.kv_done[l] = kv_ev(u, l);
-                if (u > 0) c.kv_wait[l] = kv_ev(u - 1, l);
-            }
-        float *x = c.sl<float>(c.L.x);
-        PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_embed(m->tok, tok_dev + s0, M, m->embd_scale, x, s));
-        const int full_layers = prune ? Ls : L;
-        for (int il = 0; il < full_layers; ++il) {
+    struct Flight {
+        int u, il, slot;
+    };
+    std::vector<Flight> fl;
+    std::vector<int> free_slots;
+    for (int k = NU - 1; k >= 0; --k) free_slots.push_back(k);
+    int next_u = 0;
+    while (next_u < nub || !fl.empty()) {
+        // admit ubatches into free slots: their first layer runs in this step
+        while ((int)fl.size() < NU && next_u < nub) {
+            const int slot = free_slots.back();
+            free_slots.pop_back();
+            const int s0 = next_u * ub, M = std::min(ub, n - s0);
+            PPX_LAUNCH(c, PPX_PHASE_OTHER,
+                       launch_embed(m->tok, tok_dev + s0, M, m->embd_scale, c.sl<float>(c.L.x, slot), c.s));
+            fl.push_back({next_u, 0, slot});
+            ++next_u;
+        }
+        Unit U[kMaxUnits];
+        const int nu = (int)fl.size();
+        for (int i = 0; i < nu; ++i) {
+            const int s0 = fl[i].u * ub;
+            U[i] = Unit{fl[i].il, std::min(ub, n - s0), s0, p0 + s0, fl[i].slot};
+        }
+        if (serial) {
+            const float *x = c.sl<float>(c.L.x, U[0].slot);
             if (p->debug_rows)
-                PPX_TRY(launch_copy_f32(x, p->debug_rows + ((size_t)il * n + s0) * d, M * d, s));
-            PPX_TRY(extract(il, x, M, s0, s));
-            PPX_TRY(layer_rows(c, il, M, s0, pos0));
+                PPX_TRY(launch_copy_f32(x, p->debug_rows + ((size_t)U[0].il * n + U[0].row0) * d, U[0].M * d, c.s));
+            PPX_TRY(extract(U[0].il, x, U[0].M, U[0].row0));
+        }
+        PPX_TRY(layer_rows_group(c, U, nu));
+        // advance; a ubatch past its last row-batched layer leaves its slot
+        for (int i = nu - 1; i >= 0; --i) {
+            Flight &f = fl[i];
+            const Unit &u = U[i];
+            float *x = c.sl<float>(c.L.x, f.slot);
+            const bool last = f.u == nub - 1;
             if (last && p->debug_hidden)
-                PPX_TRY(launch_copy_f32(x + (size_t)(M - 1) * d, p->debug_hidden + (size_t)il * d, d, s));
-        }
-        if (full_layers == L) {
-            // every row reached the end (the predicate keeps these off pruned runs)
-            PPX_TRY(extract(L, x, M, s0, s));
-            if (p->embeddings)
-                PPX_TRY(launch_rmsnorm_f32(x, m->out_norm, m->eps, M, d, p->embd_out + (size_t)s0 * d, s));
-        }
-        if (!last) continue;
-        const float *x_last = x + (size_t)(M - 1) * d;
-        if (prune) {
-            float *xr = c.at<float>(c.L.xr);
-            PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_copy_f32(x_last, xr, d, s));  // the one row kept
-            const int pos = p0 + n - 1;
-            for (int il = Ls; il < L; ++il) {
-                if (p->debug_rows)
-                    PPX_TRY(launch_copy_f32(xr, p->debug_rows + ((size_t)il * n + n - 1) * d, d, s));
-                PPX_TRY(layer_row(c, il, pos, tok_dev + n - 1));
-                if (p->debug_hidden) PPX_TRY(launch_copy_f32(xr, p->debug_hidden + (size_t)il * d, d, s));
+                PPX_TRY(launch_copy_f32(x + (size_t)(u.M - 1) * d, p->debug_hidden + (size_t)f.il * d, d, c.s));
+            if (++f.il < full_layers) continue;
+            if (full_layers == L) {
+                // every row reached the end (the predicate keeps these off pruned runs)
+                PPX_TRY(extract(L, x, u.M, u.row0));
+                if (p->embeddings)
+                    PPX_TRY(launch_rmsnorm_f32(x, m->out_norm, m->eps, u.M, d, p->embd_out + (size_t)u.row0 * d, c.s));
             }
-            x_last = xr;
+            if (last) {
+                const float *x_last = x + (size_t)(u.M - 1) * d;
+                if (prune) {
+                    float *xr = c.at<float>(c.L.xr);
+                    PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_copy_f32(x_last, xr, d, c.s));  // the one row kept
+                    const int pos = p0 + n - 1;
+                    for (int il = Ls; il < L; ++il) {
+                        if (p->debug_rows)
+                            PPX_TRY(launch_copy_f32(xr, p->debug_rows + ((size_t)il * n + n - 1) * d, d, c.s));
+                        PPX_TRY(layer_row(c, il, pos, tok_dev + n - 1));
+                        if (p->debug_hidden) PPX_TRY(launch_copy_f32(xr, p->debug_hidden + (size_t)il * d, d, c.s));
+                    }
+                    x_last = xr;
+                }
+                PPX_TRY(head_row(c, x_last, logits));
+            }
+            free_slots.push_back(f.slot);
+            fl.erase(fl.begin() + i);
         }
-        PPX_TRY(head_row(c, x_last, logits));
     }
-    if (S > 1) {
-        for (int k = 1; k < S; ++k) {
-            if (hipEventRecord(ev[k], streams[k]) != hipSuccess) return PPX_E_HIP;
-            if (hipStreamWaitEvent(streams[0], ev[k], 0) != hipSuccess) return PPX_E_HIP;
-        }
-    }
-    c.slot = 0;
-    c.s = streams[0];
-    c.kv_done.clear();
-    c.kv_wait.clear();
-    return PPX_OK;
-}
-
-// Streams for ubatches in flight: streams[0] is `main`, the others are
-// model-owned (separate sets for direct launches and for recording).
-int slot_streams(ppx_model *m, hipStream_t main, bool recording, hipStream_t *out) {
-    std::vector<hipStream_t> &pool = recording ? m->capture_aux : m->aux_streams;
-    while ((int)pool.size() < kSlots - 1) {
-        hipStream_t st;
-        if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return PPX_E_HIP;
-        pool.push_back(st);
-    }
-    out[0] = main;
-    for (int k = 1; k < kSlots; ++k) out[k] = pool[k - 1];
     return PPX_OK;
 }
 
@@ -717,10 +758,8 @@ int run_graph(Ctx &c, const ppx_prefill_params *p, const int32_t *tok_dev, int n
         return PPX_E_HIP;
     Ctx rc = c;
     rc.s = m->capture_stream;
-    hipStream_t streams[kSlots];
-    PPX_TRY(slot_streams(m, rc.s, true, streams));
     if (hipStreamBeginCapture(rc.s, hipStreamCaptureModeThreadLocal) != hipSuccess) return PPX_E_HIP;
-    const int st = enqueue_prefill(rc, p, tok_dev, n, p0, ub, prune, logits, streams, kSlots);
+    const int st = enqueue_prefill(rc, p, tok_dev, n, p0, ub, prune, logits);
     hipGraph_t graph = nullptr;
     const hipError_t ec = hipStreamEndCapture(rc.s, &graph);
     if (st != PPX_OK) {
@@ -805,7 +844,7 @@ int prefill(ppx_model *m, ppx_kv *kv, const int32_t *tokens, int n, const ppx_pr
     if ((long)p0 + n > kv->n_ctx) return PPX_E_CTX;
     if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return PPX_E_INVAL;
     const int ub = p->n_ubatch;
-    Ctx c{m, kv, s, static_cast<uint8_t *>(ws), ws_layout(m, ub, kv->n_ctx)};
+    Ctx c{m, kv, s, static_cast<uint8_t *>(ws), ws_layout(m, ub, kv->n_ctx, prefill_slots(m, ub, kv->n_ctx))};
     if (p->timing) {
         std::memset(p->timing, 0, sizeof(*p->timing));
         c.tm = p->timing;
@@ -835,11 +874,8 @@ int prefill(ppx_model *m, ppx_kv *kv, const int32_t *tokens, int n, const ppx_pr
         for (int il = 0; il <= L; ++il) extract = extract || p->embeddings_layer_inp[il];
     const bool graphable = !c.tm && !p->debug_rows && !p->debug_hidden && !extract && graphs_enabled();
     if (!graphable) {
-        // timing, debug and extraction outputs keep every launch on the caller's stream, in order
-        const bool serial = c.tm || p->debug_rows || p->debug_hidden || extract;
-        hipStream_t streams[kSlots];
-        PPX_TRY(slot_streams(m, s, false, streams));
-        PPX_TRY(enqueue_prefill(c, p, tok_dev, n, p0, ub, prune, logits, streams, serial ? 1 : kSlots));
+        // timing, debug and extraction outputs run the launches directly
+        PPX_TRY(enqueue_prefill(c, p, tok_dev, n, p0, ub, prune, logits));
     } else {
         PPX_TRY(run_graph(c, p, tok_dev, n, p0, ub, prune, logits));
     }
@@ -859,7 +895,7 @@ int decode(ppx_model *m, ppx_kv *kv, int32_t token, void *ws, size_t ws_bytes, f
     const int pos = kv->n_pos;
     if (pos + 1 > kv->n_ctx) return PPX_E_CTX;
     if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return PPX_E_INVAL;
-    Ctx c{m, kv, s, static_cast<uint8_t *>(ws), ws_layout(m, 1, kv->n_ctx)};
+    Ctx c{m, kv, s, static_cast<uint8_t *>(ws), ws_layout(m, 1, kv->n_ctx, 1)};
     if (ws_bytes < c.L.total) return PPX_E_NOMEM;
     int32_t *tok_dev = c.at<int32_t>(c.L.tok);
     PPX_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(tok_dev), (uint32_t)token, 1, s));  // by value: no host buffer to outlive
@@ -895,7 +931,7 @@ struct MultiLayout {
 MultiLayout multi_layout(const ppx_model *m, int ub, int k, long T, int n_ctx_max) {
     const ppx_model_info &I = m->info;
     MultiLayout L{};
-    L.w = ws_layout(m, std::max(ub, k), n_ctx_max);
+    L.w = ws_layout(m, std::max(ub, k), n_ctx_max, 1);
     size_t o = L.w.total;
     L.xk = o;
     o += al(4ull * k * I.d_model);
@@ -1503,7 +1539,7 @@ int ppx_kvfile_validate(const char *path, int n_layers, int kv_dim, int n_pos, i
 
 size_t ppx_workspace_bytes(const ppx_model *m, int n_ubatch, int n_ctx) {
     if (!m || n_ubatch < 1 || n_ctx < 1) return 0;
-    return ws_layout(m, n_ubatch, n_ctx).total;
+    return ws_layout(m, n_ubatch, n_ctx, prefill_slots(m, n_ubatch, n_ctx)).total;
 }
 
 int ppx_prefill(ppx_model *m, ppx_kv *kv, const int32_t *tokens_host, int n_tokens, const ppx_prefill_params *p,
@@ -1513,7 +1549,7 @@ int ppx_prefill(ppx_model *m, ppx_kv *kv, const int32_t *tokens_host, int n_toke
 
 size_t ppx_workspace_bytes_multi(const ppx_model *m, int n_ubatch, int n_seq, long n_tokens_total, int n_ctx_max) {
     if (!m || n_ubatch < 1 || n_seq < 1 || n_seq > PPX_MAX_SEQ || n_tokens_total < 1 || n_ctx_max < 1) return 0;
-    const size_t one = ws_layout(m, n_ubatch, n_ctx_max).total;
+    const size_t one = ws_layout(m, n_ubatch, n_ctx_max, prefill_slots(m, n_ubatch, n_ctx_max)).total;
     return std::max(one, multi_layout(m, n_ubatch, n_seq, n_tokens_total, n_ctx_max).total);
 }
 
@@ -1566,7 +1602,7 @@ extern "C" {
 int ppx_decode_static(ppx_model *m, ppx_kv *kv, int32_t token, float *logits_dev, void *hip_stream) {
     if (!m || !kv) return PPX_E_INVAL;
     if (kv->m != m) return PPX_E_INVAL;
-    if (ws_layout(m, 1, kv->n_ctx).total > kStaticScratchBytes) return PPX_E_NOMEM;
+    if (ws_layout(m, 1, kv->n_ctx, 1).total > kStaticScratchBytes) return PPX_E_NOMEM;
     void *ws = static_scratch();
     if (!ws) return PPX_E_HIP;
     return decode(m, kv, token, ws, kStaticScratchBytes, logits_dev, (hipStream_t)hip_stream);
@@ -1668,7 +1704,7 @@ int ppx_op_attention(const ppx_model *m, const void *q_dev, const void *k_dev, c
     if (!m || !q_dev || !k_dev || !vt_dev || !o_dev || !ws_dev || M < 1 || pos0 < 0 || M > PPX_MAX_UBATCH)
         return PPX_E_INVAL;
     if (vld % 64 || vld < pos0 + M) return PPX_E_INVAL;
-    const WsLayout L = ws_layout(m, M, pos0 + M);
+    const WsLayout L = ws_layout(m, M, pos0 + M, 1);
     if (ws_bytes < L.total) return PPX_E_NOMEM;
     AttnArgs a;
     a.q = static_cast<const __half *>(q_dev);
@@ -1689,7 +1725,7 @@ int ppx_op_attention_1row(const ppx_model *m, const float *q_dev, const void *k_
                           int pos, float *o_dev, void *ws_dev, size_t ws_bytes, void *hip_stream) {
     if (!m || !q_dev || !k_dev || !vt_dev || !o_dev || !ws_dev || pos < 0) return PPX_E_INVAL;
     if (vld % 64 || vld <= pos) return PPX_E_INVAL;
-    const WsLayout L = ws_layout(m, 1, pos + 1);
+    const WsLayout L = ws_layout(m, 1, pos + 1, 1);
     if (ws_bytes < L.total) return PPX_E_NOMEM;
     uint8_t *ws = static_cast<uint8_t *>(ws_dev);
     hipStream_t s = (hipStream_t)hip_stream;

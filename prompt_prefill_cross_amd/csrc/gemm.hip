@@ -279,7 +279,8 @@ struct PCfg {
 // the epilogue, or the fp32 partial of this workgroup's K range.
 template <class C, int G>
 __device__ __forceinline__ void finish_rows(const GemmArgs &a, const f4 (&acc)[C::TM][C::TN], const float *xch,
-                                            int wn, int m0, int n0, int lane, _Float16 *stage) {
+                                            int wn, int m0, int n0, int lane, _Float16 *stage, int split, int S,
+                                            int Mt) {
     f4 sum[C::TMS][C::TN];
 #pragma unroll
     for (int i = 0; i < C::TMS; ++i)
@@ -303,12 +304,12 @@ __device__ __forceinline__ void finish_rows(const GemmArgs &a, const f4 (&acc)[C
         }
     }
     const int r0 = m0 + G * C::TMS * 16, c0 = n0 + wn * C::WN;
-    if (gridDim.z == 1) {
+    if (S == 1) {
         gemm_epilogue<C::TMS, C::TN>(a, sum, r0, c0, lane, stage);
     } else {
         // partial tile layout: [split][row tile][16-column group][r][lane]
-        const int Mt = gridDim.y * C::TM, Nt = a.W.N >> 4;
-        float *dst = a.part + (size_t)blockIdx.z * Mt * Nt * 256;
+        const int Nt = a.W.N >> 4;
+        float *dst = a.part + (size_t)split * Mt * Nt * 256;
 #pragma unroll
         for (int i = 0; i < C::TMS; ++i)
 #pragma unroll
@@ -322,22 +323,29 @@ __device__ __forceinline__ void finish_rows(const GemmArgs &a, const f4 (&acc)[C
 
 template <class C, int G>
 __device__ __forceinline__ void finish_group(const GemmArgs &a, const f4 (&acc)[C::TM][C::TN], const float *xch,
-                                             int g, int wn, int m0, int n0, int lane, _Float16 *stage) {
+                                             int g, int wn, int m0, int n0, int lane, _Float16 *stage, int split,
+                                             int S, int Mt) {
     if constexpr (G < C::NFG) {
-        if (g == G) finish_rows<C, G>(a, acc, xch, wn, m0, n0, lane, stage);
-        else finish_group<C, G + 1>(a, acc, xch, g, wn, m0, n0, lane, stage);
+        if (g == G) finish_rows<C, G>(a, acc, xch, wn, m0, n0, lane, stage, split, S, Mt);
+        else finish_group<C, G + 1>(a, acc, xch, g, wn, m0, n0, lane, stage, split, S, Mt);
     }
 }
 
+// A launch covers grp.n units (the same product for different ubatches and
+// layers: same N, K and epilogue, their own operands and outputs); z =
+// unit * S + split.  Mt: row tiles of the split-K partial layout.
 template <class C>
-__global__ __launch_bounds__(C::NT) void k_q4gemm_p(GemmArgs a) {
+__global__ __launch_bounds__(C::NT) void k_q4gemm_p(const GemmGroup grp, int S, int Mt) {
     __shared__ h8 ring[C::DEPTH * C::STAGE_UNITS];
+    const int unit = blockIdx.z / S, split = blockIdx.z % S;
+    const GemmArgs &a = grp.u[unit];
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
     const int n0 = blockIdx.x * C::BN, m0 = blockIdx.y * C::BM;
+    if (m0 >= a.M) return;  // a unit with fewer rows than the launch's tallest (the whole workgroup)
     const int kch = a.W.K >> 6;
-    const int nkg = kch / ((int)gridDim.z * C::KS);  // 64-wide K steps per K group
-    const int kz = blockIdx.z * C::KS * nkg;         // first K step of this workgroup
+    const int nkg = kch / (S * C::KS);  // 64-wide K steps per K group
+    const int kz = split * C::KS * nkg;  // first K step of this workgroup
     const int ktiles = a.W.K >> 5;
 
     if (wave >= C::NCW) {
@@ -486,13 +494,14 @@ __global__ __launch_bounds__(C::NT) void k_q4gemm_p(GemmArgs a) {
     }
     // each compute wave's epilogue staging area follows the exchange space
     _Float16 *stage = reinterpret_cast<_Float16 *>(xch + C::XCH_FLOATS) + (size_t)wave * C::STAGE_HALVES;
-    finish_group<C, 0>(a, acc, xch, g, wn, m0, n0, lane, stage);
+    finish_group<C, 0>(a, acc, xch, g, wn, m0, n0, lane, stage, split, S, Mt);
 }
 
 // Sum of the S split partials in split order, then the epilogue; one wave per
 // 16 rows x (16 * TNR) columns.
 template <int TNR>
-__global__ __launch_bounds__(256) void k_gemm_reduce(GemmArgs a, int S, int Mt) {
+__global__ __launch_bounds__(256) void k_gemm_reduce(const GemmGroup grp, int S, int Mt) {
+    const GemmArgs &a = grp.u[blockIdx.y];
     const int lane = threadIdx.x & 63;
     const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int Nt = a.W.N >> 4, ncb = Nt / TNR;
@@ -517,10 +526,12 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(GemmArgs a, int S, int Mt) 
 // eight-float chunks t, t + 256, ...; every split's loads issue together.
 constexpr int RAN_MAX_CHUNKS = 2;  // d <= 2 * 8 * 256
 constexpr int RAN_MAX_SPLIT = 8;
-__global__ __launch_bounds__(256) void k_reduce_add_norm(GemmArgs a, int S, int Mt) {
+__global__ __launch_bounds__(256) void k_reduce_add_norm(const GemmGroup grp, int S, int Mt) {
     __shared__ float red[4];
+    const GemmArgs &a = grp.u[blockIdx.y];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = blockIdx.x;
+    if (row >= a.M) return;
     const int d = a.W.N, Nt = d >> 4, nch = d >> 3;
     const int rt = row >> 4, rr = row & 15;
     const int sub = (rr & 3) * 64 + (rr >> 2) * 16;  // r * 64 + lane group * 16 in the partial tile
@@ -601,11 +612,13 @@ struct Cfg {
 };
 
 template <class C>
-__global__ __launch_bounds__(C::NT) void k_q4gemm(GemmArgs a) {
+__global__ __launch_bounds__(C::NT) void k_q4gemm(const GemmGroup units) {
     __shared__ h8 ring[C::DEPTH * C::STAGE_UNITS];
+    const GemmArgs &a = units.u[blockIdx.z];
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
     const int n0 = blockIdx.x * C::BN, m0 = blockIdx.y * C::BM;
+    if (m0 >= a.M) return;  // a unit with fewer rows than the launch's tallest
     const int kch = a.W.K >> 6;
     const int nkg = kch / C::KS;  // chunks per group
     const int ktiles = a.W.K >> 5;
@@ -727,22 +740,31 @@ __global__ __launch_bounds__(C::NT) void k_q4gemm(GemmArgs a) {
 
 // ------------------------------------------------------------------ launchers
 
+// Rows of the launch: the tallest unit's (shorter units' surplus workgroups return at once).
+int max_rows(const GemmGroup &g) {
+    int M = 0;
+    for (int i = 0; i < g.n; ++i) M = std::max(M, g.u[i].M);
+    return M;
+}
+
 template <class C>
-int launch_p(const GemmArgs &a, int S, hipStream_t s) {
+int launch_p(const GemmGroup &g, int S, hipStream_t s) {
+    const GemmArgs &a = g.u[0];
     const int kch = a.W.K >> 6;
     if (S < 1 || a.W.N % C::BN || kch % (S * C::KS)) return PPX_E_UNSUPPORTED;
     if (a.epi == EPI_QKV && C::TN % 2) return PPX_E_UNSUPPORTED;
-    const int mb = (a.M + C::BM - 1) / C::BM;
+    const int mb = (max_rows(g) + C::BM - 1) / C::BM;
     const int Mt = mb * C::TM;
-    if (S > 1 && (!a.part || (size_t)S * Mt * 16 * a.W.N > a.part_floats)) return PPX_E_UNSUPPORTED;
-    hipLaunchKernelGGL((k_q4gemm_p<C>), dim3(a.W.N / C::BN, mb, S), dim3(C::NT), 0, s, a);
+    for (int i = 0; i < g.n && S > 1; ++i)
+        if (!g.u[i].part || (size_t)S * Mt * 16 * a.W.N > g.u[i].part_floats) return PPX_E_UNSUPPORTED;
+    hipLaunchKernelGGL((k_q4gemm_p<C>), dim3(a.W.N / C::BN, mb, S * g.n), dim3(C::NT), 0, s, g, S, Mt);
     if (hipGetLastError() != hipSuccess) return PPX_E_HIP;
     if (S > 1) {
         if (a.norm_out && S <= RAN_MAX_SPLIT) {
-            hipLaunchKernelGGL(k_reduce_add_norm, dim3(a.M), dim3(256), 0, s, a, S, Mt);
+            hipLaunchKernelGGL(k_reduce_add_norm, dim3(max_rows(g), g.n), dim3(256), 0, s, g, S, Mt);
         } else {
             const int waves = Mt * (a.W.N / 32);
-            hipLaunchKernelGGL((k_gemm_reduce<2>), dim3((waves + 3) / 4), dim3(256), 0, s, a, S, Mt);
+            hipLaunchKernelGGL((k_gemm_reduce<2>), dim3((waves + 3) / 4, g.n), dim3(256), 0, s, g, S, Mt);
         }
         if (hipGetLastError() != hipSuccess) return PPX_E_HIP;
     }
@@ -750,11 +772,12 @@ int launch_p(const GemmArgs &a, int S, hipStream_t s) {
 }
 
 template <class C>
-int launch_cfg(const GemmArgs &a, hipStream_t s) {
+int launch_cfg(const GemmGroup &g, hipStream_t s) {
+    const GemmArgs &a = g.u[0];
     if (a.W.N % C::BN || (a.W.K >> 6) % (C::PB * C::KS)) return PPX_E_UNSUPPORTED;
     if (a.epi == EPI_QKV && C::TN % 2) return PPX_E_UNSUPPORTED;  // RoPE pairs are adjacent groups of one wave
-    dim3 grid(a.W.N / C::BN, (a.M + C::BM - 1) / C::BM);
-    hipLaunchKernelGGL((k_q4gemm<C>), grid, dim3(C::NT), 0, s, a);
+    dim3 grid(a.W.N / C::BN, (max_rows(g) + C::BM - 1) / C::BM, g.n);
+    hipLaunchKernelGGL((k_q4gemm<C>), grid, dim3(C::NT), 0, s, g);
     return hipGetLastError() == hipSuccess ? PPX_OK : PPX_E_HIP;
 }
 
@@ -771,11 +794,11 @@ int launch_cfg(const GemmArgs &a, hipStream_t s) {
     X(7, 1, 1, 1, 4, 4, 1)  \
     X(8, 1, 2, 1, 4, 4, 1)
 
-int launch_plan(const GemmArgs &a, int cfg, int S, hipStream_t s) {
+int launch_plan(const GemmGroup &g, int cfg, int S, hipStream_t s) {
     switch (cfg) {
 #define PPX_CASE(id, tm, tn, nwn, ks, depth, np) \
     case id:                                     \
-        return launch_p<PCfg<tm, tn, nwn, ks, depth, np>>(a, S, s);
+        return launch_p<PCfg<tm, tn, nwn, ks, depth, np>>(g, S, s);
         PPX_GEMM_CONFIGS(PPX_CASE)
 #undef PPX_CASE
     default: return PPX_E_UNSUPPORTED;
@@ -828,26 +851,56 @@ size_t gemm_part_floats(int M, int N, int K) {
     return (size_t)p.S * ((M + bm - 1) / bm * bm) * N;
 }
 
-int launch_gemm(const GemmArgs &a, hipStream_t s) {
-    if (a.M <= 0) return PPX_OK;
-    if (a.W.N % 128 || a.W.K % 256 || !a.A) return PPX_E_UNSUPPORTED;
-    if (a.norm_out && (a.epi != EPI_ADD || !a.norm_g || a.W.N > RAN_MAX_CHUNKS * 8 * 256)) return PPX_E_UNSUPPORTED;
-    Plan p = plan_for(a.M, a.W.N, a.W.K, a.few_rows);
-    if (a.few_rows && a.M <= 64 && a.epi == EPI_QKV) p = {8, 1};  // RoPE pairs need two column groups per wave
-    int st = launch_plan(a, p.cfg, p.S, s);
+int launch_gemm_group(const GemmArgs *units, int n, hipStream_t s) {
+    if (n < 1 || n > kMaxUnits) return PPX_E_INVAL;
+    GemmGroup g;
+    g.n = 0;
+    for (int i = 0; i < n; ++i)
+        if (units[i].M > 0) g.u[g.n++] = units[i];
+    if (!g.n) return PPX_OK;
+    const GemmArgs &a = g.u[0];
+    for (int i = 1; i < g.n; ++i)
+        if (g.u[i].W.N != a.W.N || g.u[i].W.K != a.W.K || g.u[i].epi != a.epi || g.u[i].few_rows != a.few_rows ||
+            !g.u[i].norm_out != !a.norm_out)
+            return PPX_E_INVAL;
+    if (a.W.N % 128 || a.W.K % 256) return PPX_E_UNSUPPORTED;
+    for (int i = 0; i < g.n; ++i) {
+        const GemmArgs &u = g.u[i];
+        if (!u.A) return PPX_E_UNSUPPORTED;
+        if (u.norm_out && (u.epi != EPI_ADD || !u.norm_g || u.W.N > RAN_MAX_CHUNKS * 8 * 256)) return PPX_E_UNSUPPORTED;
+    }
+    const int M = max_rows(g);
+    Plan p = plan_for(M, a.W.N, a.W.K, a.few_rows);
+    if (a.few_rows && M <= 64 && a.epi == EPI_QKV) p = {8, 1};  // RoPE pairs need two column groups per wave
+    int st = launch_plan(g, p.cfg, p.S, s);
     bool normed = st == PPX_OK && p.S > 1 && p.S <= RAN_MAX_SPLIT && a.norm_out;  // the split's reduction normalised too
-    if (st == PPX_E_UNSUPPORTED && p.S > 1) st = launch_plan(a, p.cfg, 1, s);  // no split workspace given
-    if (st == PPX_E_UNSUPPORTED) st = launch_plan(a, 5, 1, s);                 // N % 128, K % 256: always fits
-    if (st == PPX_OK && a.norm_out && !normed)
-        st = launch_rmsnorm_f16(a.out_f32, a.norm_g, a.norm_eps, a.M, a.W.N, a.norm_out, s);
+    if (st == PPX_E_UNSUPPORTED && p.S > 1) st = launch_plan(g, p.cfg, 1, s);  // no split workspace given
+    if (st == PPX_E_UNSUPPORTED) st = launch_plan(g, 5, 1, s);                 // N % 128, K % 256: always fits
+    for (int i = 0; i < g.n && st == PPX_OK && a.norm_out && !normed; ++i)
+        st = launch_rmsnorm_f16(g.u[i].out_f32, g.u[i].norm_g, g.u[i].norm_eps, g.u[i].M, a.W.N, g.u[i].norm_out, s);
     return st;
 }
 
-int launch_gemm_exact(const GemmArgs &a, hipStream_t s) {
-    if (a.M <= 0) return PPX_OK;
-    if (a.W.N % 64 || a.W.K % 256 || !a.A || !a.A2) return PPX_E_UNSUPPORTED;
-    if ((a.W.K >> 6) % 8 == 0) return launch_cfg<Cfg<1, 2, 2, 2, 6>>(a, s);
-    return launch_cfg<Cfg<1, 2, 2, 1, 6>>(a, s);
+int launch_gemm(const GemmArgs &a, hipStream_t s) { return launch_gemm_group(&a, 1, s); }
+
+int launch_gemm_exact_group(const GemmArgs *units, int n, hipStream_t s) {
+    if (n < 1 || n > kMaxUnits) return PPX_E_INVAL;
+    GemmGroup g;
+    g.n = 0;
+    for (int i = 0; i < n; ++i)
+        if (units[i].M > 0) g.u[g.n++] = units[i];
+    if (!g.n) return PPX_OK;
+    const GemmArgs &a = g.u[0];
+    for (int i = 0; i < g.n; ++i) {
+        const GemmArgs &u = g.u[i];
+        if (u.W.N != a.W.N || u.W.K != a.W.K || u.epi != a.epi) return PPX_E_INVAL;
+        if (!u.A || !u.A2) return PPX_E_UNSUPPORTED;
+    }
+    if (a.W.N % 64 || a.W.K % 256) return PPX_E_UNSUPPORTED;
+    if ((a.W.K >> 6) % 8 == 0) return launch_cfg<Cfg<1, 2, 2, 2, 6>>(g, s);
+    return launch_cfg<Cfg<1, 2, 2, 1, 6>>(g, s);
 }
+
+int launch_gemm_exact(const GemmArgs &a, hipStream_t s) { return launch_gemm_exact_group(&a, 1, s); }
 
 }  // namespace ppx

@@ -41,13 +41,17 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float *x, const float *g,
 constexpr int NORM_MAX_CHUNKS = 2;  // d <= 2 * 8 * 256
 // One workgroup per row: thread t owns the eight-float chunks t, t + 256;
 // the gain is loaded before the row's reduction, which it does not need.
+// Grid (rows, units): unit blockIdx.y of the group.
 template <bool LO>
-__global__ __launch_bounds__(256) void k_rmsnorm_tiled(const float *x, const float *g, float eps, int M, int d,
-                                                       __half *hi, __half *lo) {
+__global__ __launch_bounds__(256) void k_rmsnorm_tiled(const NormGroup grp, float eps, int d) {
     __shared__ float red[4];
+    const NormUnit &u = grp.u[blockIdx.y];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = blockIdx.x;
-    const float *xr = x + (size_t)row * d;
+    if (row >= u.M) return;
+    const float *g = u.g;
+    __half *hi = u.hi, *lo = u.lo;
+    const float *xr = u.x + (size_t)row * d;
     const int nch = d >> 3;
     float4 v[NORM_MAX_CHUNKS][2], gv[NORM_MAX_CHUNKS][2];
     float ss = 0.f;
@@ -382,19 +386,41 @@ int launch_embed(const Q4R &tok, const int32_t *ids, int M, float scale, float *
     return ok();
 }
 
-int launch_rmsnorm_f16(const float *x, const float *g, float eps, int M, int d, __half *out, hipStream_t s) {
-    if (M <= 0) return PPX_OK;
+int launch_rmsnorm_group(const NormUnit *units, int n, float eps, int d, bool lo, hipStream_t s) {
+    if (n < 1 || n > kMaxUnits) return PPX_E_INVAL;
     if (d % 32 || d > NORM_MAX_CHUNKS * 8 * 256) return PPX_E_UNSUPPORTED;
-    hipLaunchKernelGGL((k_rmsnorm_tiled<false>), dim3(M), dim3(256), 0, s, x, g, eps, M, d, out, nullptr);
+    NormGroup g;
+    int M = 0;
+    for (int i = 0; i < n; ++i) {
+        if (units[i].M <= 0) continue;
+        if (!units[i].x || !units[i].g || !units[i].hi || (lo && !units[i].lo)) return PPX_E_INVAL;
+        g.u[g.n++] = units[i];
+        M = std::max(M, units[i].M);
+    }
+    if (!g.n) return PPX_OK;
+    if (lo) hipLaunchKernelGGL((k_rmsnorm_tiled<true>), dim3(M, g.n), dim3(256), 0, s, g, eps, d);
+    else hipLaunchKernelGGL((k_rmsnorm_tiled<false>), dim3(M, g.n), dim3(256), 0, s, g, eps, d);
     return ok();
+}
+
+int launch_rmsnorm_f16(const float *x, const float *g, float eps, int M, int d, __half *out, hipStream_t s) {
+    NormUnit u;
+    u.x = x;
+    u.g = g;
+    u.hi = out;
+    u.M = M;
+    return launch_rmsnorm_group(&u, 1, eps, d, false, s);
 }
 
 int launch_rmsnorm_split(const float *x, const float *g, float eps, int M, int d, __half *hi, __half *lo,
                          hipStream_t s) {
-    if (M <= 0) return PPX_OK;
-    if (d % 32 || d > NORM_MAX_CHUNKS * 8 * 256) return PPX_E_UNSUPPORTED;
-    hipLaunchKernelGGL((k_rmsnorm_tiled<true>), dim3(M), dim3(256), 0, s, x, g, eps, M, d, hi, lo);
-    return ok();
+    NormUnit u;
+    u.x = x;
+    u.g = g;
+    u.hi = hi;
+    u.lo = lo;
+    u.M = M;
+    return launch_rmsnorm_group(&u, 1, eps, d, true, s);
 }
 
 int launch_tile_f16(const __half *src, int M, int K, __half *dst, hipStream_t s) {

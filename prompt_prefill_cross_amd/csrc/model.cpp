@@ -404,9 +404,6 @@ void model_free(ppx_model *m) {
     for (hipEvent_t e : m->events) (void)hipEventDestroy(e);
     drop_graphs(m);
     if (m->capture_stream) (void)hipStreamDestroy(m->capture_stream);
-    for (hipStream_t st : m->aux_streams) (void)hipStreamDestroy(st);
-    for (hipStream_t st : m->capture_aux) (void)hipStreamDestroy(st);
-    for (hipEvent_t e : m->sync_events) (void)hipEventDestroy(e);
     if (m->stage_host) (void)hipHostFree(m->stage_host);
     if (m->stage_event) (void)hipEventDestroy(m->stage_event);
     delete m;

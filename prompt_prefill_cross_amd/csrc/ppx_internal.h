@@ -90,9 +90,6 @@ struct ppx_model {
     std::vector<KeyedGraph> keyed_graphs;
     unsigned long long graph_clock = 0;
     hipStream_t capture_stream = nullptr;  // recording only; graphs run on the caller's stream
-    std::vector<hipStream_t> aux_streams;  // ubatches in flight, direct launches
-    std::vector<hipStream_t> capture_aux;  // ubatches in flight, recording
-    std::vector<hipEvent_t> sync_events;   // cross-stream ordering inside one prefill
     // pinned host staging of the per-row tables of a multi-sequence prefill;
     // stage_event marks the end of the last copy out of it
     void *stage_host = nullptr;
@@ -180,6 +177,19 @@ struct GemmArgs {
     __half *norm_out = nullptr;
 };
 int launch_gemm(const GemmArgs &a, hipStream_t s);
+
+// Ubatches in flight at once in a prefill: each step runs every in-flight
+// ubatch through its next row-batched layer, and the step's identical
+// operations run as one launch over the units (ubatch, layer).
+constexpr int kMaxUnits = 8;
+struct GemmGroup {
+    int n = 0;
+    GemmArgs u[kMaxUnits];
+};
+// One launch of the same product (same N, K, epilogue) for n <= kMaxUnits
+// units with their own operands, rows (M) and outputs.
+int launch_gemm_group(const GemmArgs *units, int n, hipStream_t s);
+int launch_gemm_exact_group(const GemmArgs *units, int n, hipStream_t s);
 // fp32 words of split-K partials launch_gemm would use for an M x N x K GEMM
 // (0: that shape is not split).
 size_t gemm_part_floats(int M, int N, int K);
@@ -265,6 +275,13 @@ struct AttnArgs {
     const int32_t *row_seq = nullptr;
 };
 int launch_attn_prefill(const AttnArgs &a, hipStream_t s);
+struct AttnGroup {
+    int n = 0;
+    AttnArgs u[kMaxUnits];
+};
+// Prefill attention of n units (same H, KVH, hd; their own queries, caches,
+// positions and outputs) in one launch, each with its own key split.
+int launch_attn_prefill_group(const AttnArgs *units, int n, hipStream_t s);
 // Causal attention of M rows at ~fp32 accuracy (exact precision): one
 // workgroup per (row, KV head) runs an online softmax over 32-key chunks with
 // both products on MFMA, every fp32 operand split into fp16 high and low parts
@@ -288,6 +305,19 @@ int launch_embed(const Q4R &tok, const int32_t *ids, int M, float scale, float *
 // y = rmsnorm(x) * g -> fp16 in the fragment-tiled layout (the GEMM A operand).
 int launch_rmsnorm_f16(const float *x, const float *g, float eps, int M, int d, __half *out,
                        hipStream_t s);
+// The RMSNorm of n units' rows in one launch: unit i normalises x[i] (M[i]
+// rows of d) with gain g[i] into hi[i] (and lo[i] when lo is set).
+struct NormUnit {
+    const float *x = nullptr;
+    const float *g = nullptr;
+    __half *hi = nullptr, *lo = nullptr;
+    int M = 0;
+};
+struct NormGroup {
+    int n = 0;
+    NormUnit u[kMaxUnits];
+};
+int launch_rmsnorm_group(const NormUnit *units, int n, float eps, int d, bool lo, hipStream_t s);
 // As launch_rmsnorm_f16, also writing lo = fp16(y - fp16(y)), tiled the same way.
 int launch_rmsnorm_split(const float *x, const float *g, float eps, int M, int d, __half *hi, __half *lo,
                          hipStream_t s);

@@ -180,6 +180,25 @@ def test_recorded_launches_replay_with_new_tokens(ppx):
     assert not torch.equal(replayed[1], replayed[2])
 
 
+@pytest.mark.parametrize("cfg,n,ub,prune", [("e2b", 2048, 512, "auto"), ("e2b", 1000, 128, "off"),
+                                          ("tinyllama", 512, 64, "auto")])
+def test_pipelined_ubatches_equal_the_serial_order(ppx, cfg, n, ub, prune):
+    """Ubatches run through the row-batched layers together (one launch per
+    operation over the ubatches in flight); asking for the last row's hidden
+    states runs them one at a time instead, the serial order.  Both give the
+    same logits and the same cache, bit for bit."""
+    mm = engine_model(ppx, cfg)
+    toks = synth.prompt(cfg, n)
+    kva = ppx.KVCache(mm, n)
+    la = mm.prefill(toks, kva, n_ubatch=ub, prune=prune).clone()
+    kvb = ppx.KVCache(mm, n)
+    hid = torch.empty((mm.info["n_layer"], mm.info["d_model"]), dtype=torch.float32, device="cuda")
+    lb = mm.prefill(toks, kvb, n_ubatch=ub, prune=prune, debug_hidden=hid)
+    torch.cuda.synchronize()
+    assert torch.equal(la, lb)
+    assert torch.equal(kva.buf, kvb.buf)
+
+
 def test_replay_after_the_rope_table_grows(ppx):
     """A recorded launch sequence holds the RoPE table's address.  Creating a
     cache with a longer context replaces the table; a later prefill of a shape
