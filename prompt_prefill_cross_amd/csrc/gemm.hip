@@ -819,6 +819,8 @@ int tile_rows(int cfg) {
 struct Plan {
     int cfg, S;
 };
+#define PLAN_QO 4
+#define PLAN_KSMALL 4
 
 // Measured on the E2B-like shapes at M = 512 (one MI355X): wide outputs
 // (gate|up) take the tallest wave tiles; the long-K down projection splits K
@@ -833,13 +835,13 @@ struct Plan {
 // per 16 rows instead of a few dozen tall tiles with idle rows; measured
 // 0.4-0.5 ms faster on multi-sequence prefills of 2048 tokens in 2 to 32
 // prompts.
-Plan plan_for(int M, int N, int K, bool few = false) {
+Plan plan_for(int M, int N, int K, bool few = false, int units = 1) {
     if (few && M <= 64) return {7, K >= 4096 ? 4 : 1};  // a few gathered rows: 16-row tiles, many workgroups
     if (N >= 8192) return {N % 192 == 0 ? 0 : 1, 1};
-    if (K >= 4096) return {N % 192 == 0 ? 2 : 3, 4};
+    if (K >= 4096) return {N % 192 == 0 ? 2 : 3, units >= 4 ? 1 : units >= 2 ? 2 : 4};
     if (N <= 512) return {7, 1};
-    if (K <= 256) return {4, 1};
-    return {4, 1};
+    if (K <= 256) return {PLAN_KSMALL, 1};
+    return {PLAN_QO, 1};
 }
 
 }  // namespace
@@ -870,14 +872,22 @@ int launch_gemm_group(const GemmArgs *units, int n, hipStream_t s) {
         if (u.norm_out && (u.epi != EPI_ADD || !u.norm_g || u.W.N > RAN_MAX_CHUNKS * 8 * 256)) return PPX_E_UNSUPPORTED;
     }
     const int M = max_rows(g);
-    Plan p = plan_for(M, a.W.N, a.W.K, a.few_rows);
+    Plan p = plan_for(M, a.W.N, a.W.K, a.few_rows, g.n);
     if (a.few_rows && M <= 64 && a.epi == EPI_QKV) p = {8, 1};  // RoPE pairs need two column groups per wave
     int st = launch_plan(g, p.cfg, p.S, s);
     bool normed = st == PPX_OK && p.S > 1 && p.S <= RAN_MAX_SPLIT && a.norm_out;  // the split's reduction normalised too
     if (st == PPX_E_UNSUPPORTED && p.S > 1) st = launch_plan(g, p.cfg, 1, s);  // no split workspace given
     if (st == PPX_E_UNSUPPORTED) st = launch_plan(g, 5, 1, s);                 // N % 128, K % 256: always fits
-    for (int i = 0; i < g.n && st == PPX_OK && a.norm_out && !normed; ++i)
-        st = launch_rmsnorm_f16(g.u[i].out_f32, g.u[i].norm_g, g.u[i].norm_eps, g.u[i].M, a.W.N, g.u[i].norm_out, s);
+    if (st == PPX_OK && a.norm_out && !normed) {
+        NormUnit nu[kMaxUnits];
+        for (int i = 0; i < g.n; ++i) {
+            nu[i].x = g.u[i].out_f32;
+            nu[i].g = g.u[i].norm_g;
+            nu[i].hi = g.u[i].norm_out;
+            nu[i].M = g.u[i].M;
+        }
+        st = launch_rmsnorm_group(nu, g.n, a.norm_eps, a.W.N, false, s);
+    }
     return st;
 }
 

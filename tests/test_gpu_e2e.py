@@ -185,8 +185,10 @@ def test_recorded_launches_replay_with_new_tokens(ppx):
 def test_pipelined_ubatches_equal_the_serial_order(ppx, cfg, n, ub, prune):
     """Ubatches run through the row-batched layers together (one launch per
     operation over the ubatches in flight); asking for the last row's hidden
-    states runs them one at a time instead, the serial order.  Both give the
-    same logits and the same cache, bit for bit."""
+    states runs them one at a time instead, the serial order.  The long-K
+    down projection splits K over workgroups only when few ubatches share
+    the launch, so the two orders differ only in the order of fp32 sums:
+    logits within 1e-3 with the same top-1, the cache within the KV bound."""
     mm = engine_model(ppx, cfg)
     toks = synth.prompt(cfg, n)
     kva = ppx.KVCache(mm, n)
@@ -195,8 +197,14 @@ def test_pipelined_ubatches_equal_the_serial_order(ppx, cfg, n, ub, prune):
     hid = torch.empty((mm.info["n_layer"], mm.info["d_model"]), dtype=torch.float32, device="cuda")
     lb = mm.prefill(toks, kvb, n_ubatch=ub, prune=prune, debug_hidden=hid)
     torch.cuda.synchronize()
-    assert torch.equal(la, lb)
-    assert torch.equal(kva.buf, kvb.buf)
+    ok, d = logits_ok(la.cpu().numpy(), lb.cpu().numpy(), atol=1e-3)
+    print(f"{cfg} n={n} ub={ub} prune={prune}: grouped vs serial logits max-abs {d:.2e}")
+    assert ok, d
+    Ka, Va = kva.kv_tensors()
+    Kb, Vb = kvb.kv_tensors()
+    for got, want in ((Ka[:, :n], Kb[:, :n]), (Va[:, :n], Vb[:, :n])):
+        okk, dk = kv_within(got.cpu().numpy(), want.cpu().numpy())
+        assert okk, dk
 
 
 def test_replay_after_the_rope_table_grows(ppx):
