@@ -49,7 +49,10 @@ def parse():
     ap.add_argument("--multi", default="16x128,8x256,4x512",
                     help="multi-sequence prefills to report, KxN = K prompts of N tokens ('' = none)")
     ap.add_argument("--table", action="store_true",
-                    help="also time every config's full shapes, pruned and unpruned (builds 3 more models)")
+                    help="time every config's full shapes, pruned and unpruned (builds 3 more models)")
+    ap.add_argument("--no-matrix", dest="matrix", action="store_false",
+                    help="skip the default config matrix (E2B-like and E4B-like at 2048 tokens and the "
+                         "no-sharing control at 8192, each pruned and unpruned)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="prompt tokens of the oracle sample (0 = all)")
     ap.add_argument("--pmc-pass", action="store_true", help="one prefill + one calibration copy, then exit")
@@ -267,15 +270,20 @@ def multi_pass(ppx, mm, cfg, ub, shapes, reps=5):
     return out
 
 
-def table_pass(ppx, main_cfg, main_model):
-    """The configs' full matrix: E2B-like and E4B-like at 512/2048/8192
-    tokens pruned and unpruned, the long E2B-like prompts (16384, 32768;
-    ubatch 1024) and the no-sharing control at 8192 (pruned vs unpruned
-    should time the same there).  5 timed runs after 2 warm-ups each."""
+FULL_TABLE = [("e2b", (512, 2048, 8192), ("auto", "off")), ("e4b", (512, 2048, 8192), ("auto", "off")),
+              ("e2b_long", (16384, 32768), ("auto",)), ("e2b_ctrl", (8192,), ("auto", "off"))]
+MATRIX = [("e2b", (2048,), ("auto", "off")), ("e4b", (2048,), ("auto", "off")), ("e2b_ctrl", (8192,), ("auto", "off"))]
+
+
+def table_pass(ppx, main_cfg, main_model, plan):
+    """Configs of the plan [(config, prompt lengths, prune modes)], each from
+    an empty cache: by default E2B-like and E4B-like at 2048 tokens and the
+    no-sharing control at 8192 (pruned vs unpruned should time the same
+    there), pruned and unpruned; --table adds 512 and 8192 tokens and the long
+    E2B-like prompts (16384, 32768; ubatch 1024).  5 timed runs after 2
+    warm-ups each, and one per-launch timing pass for the phase fractions."""
     import torch
     import synth
-    plan = [("e2b", (512, 2048, 8192), ("auto", "off")), ("e4b", (512, 2048, 8192), ("auto", "off")),
-            ("e2b_long", (16384, 32768), ("auto",)), ("e2b_ctrl", (8192,), ("auto", "off"))]
     rows = []
     for name, lens, prunes in plan:
         cfg = synth.CONFIGS[name]
@@ -293,9 +301,11 @@ def table_pass(ppx, main_cfg, main_model):
                 med = float(np.median(times))
                 gemm = ph["gemm_flop"] / (ph["ms"]["gemm"] * 1e-3) / 1e12 if ph["ms"]["gemm"] else 0.0
                 attn = ph["attn_flop"] / (ph["ms"]["attn"] * 1e-3) / 1e12 if ph["ms"]["attn"] else 0.0
+                row = ph["row_bytes"] / (ph["ms"]["row"] * 1e-3) / 1e9 if ph["ms"]["row"] else 0.0
                 rows.append({"config": name, "n": n, "prune": pr, "ubatch": ub, "ms_median": med,
                              "tokens_per_s": n / med * 1e3, "gemm_frac_mfma": gemm / PEAK_FP16_TFLOPS,
-                             "attn_frac_mfma": attn / PEAK_FP16_TFLOPS, "phases_ms": ph["ms"]})
+                             "attn_frac_mfma": attn / PEAK_FP16_TFLOPS, "row_frac_hbm": row / PEAK_HBM_GBS,
+                             "phases_ms": ph["ms"]})
                 print(f"# table {name} n={n} prune={pr}: {med:.2f} ms, {n / med * 1e3:.0f} tok/s, GEMM phase "
                       f"{gemm / PEAK_FP16_TFLOPS:.2f} / attention {attn / PEAK_FP16_TFLOPS:.2f} of MFMA peak",
                       file=sys.stderr, flush=True)
@@ -387,7 +397,9 @@ def main():
         print(f"# decode after {dec['after_prompt']}: {dec['ms_per_token']:.3f} ms/token, "
               f"{dec['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
 
-    table = table_pass(ppx, cfg, mm) if a.table else None
+    table = None
+    if a.table or a.matrix:
+        table = table_pass(ppx, cfg, mm, FULL_TABLE if a.table else MATRIX)
     times, ph = results[a.n]
     glu_us, glu_reps = glu_kernel_us(mm, ub)
     ms = float(np.mean(times))
