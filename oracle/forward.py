@@ -176,9 +176,9 @@ def _layer_weights(m: OracleModel, il: int) -> dict:
     return W
 
 
-def head(m: OracleModel, x_last: np.ndarray, chunk: int = 16384) -> np.ndarray:
-    """fp32 logits of one row: W_out rms(x, g_out)."""
-    hn = rms_norm(x_last, m.f32("output_norm"), m.rms_eps)
+def head(m: OracleModel, x_last: np.ndarray, chunk: int = 16384, gain: str = "output_norm") -> np.ndarray:
+    """fp32 logits of one row: W_out rms(x, g), g the output norm's gain."""
+    hn = rms_norm(x_last, m.f32(gain), m.rms_eps)
     name = "tok_embd" if m.tied else "output"
     V = m.n_vocab
     out = np.empty(V, dtype=np.float64)
@@ -198,8 +198,25 @@ def _check_prompt(m: OracleModel, kv: KVState, tokens: np.ndarray) -> None:
         raise ValueError("context overflow")
 
 
+def nextn_head(m: OracleModel, x_prev: np.ndarray, tok_last: int) -> np.ndarray:
+    """fp32 logits of the next-n head.
+
+    The pages name a next-n (multi-token prediction) head only through the
+    prune predicate's crop_before_nextn clause (the llama.cpp Gemma 4 prefill
+    page, section 1); the definition used here is the plainest depth-1
+    multi-token predictor, sharing the model's output matrix as such heads
+    usually do: it combines the final hidden state of the row BEFORE the last
+    one with the embedding of the last token,
+        z = x_{n-2} + embd_scale * deq(tok_embd[id_{n-1}]),
+        logits = W_out rms(z, g_nextn),
+    so it needs a row that the prune drops."""
+    z = x_prev + embed_rows(m, np.array([tok_last]))[0]
+    return head(m, z, gain="nextn_norm")
+
+
 def _run(m: OracleModel, kvs: list, prompts: list, prune: bool, n_ubatch: int | None,
-         trace: dict | None, layer_inp: dict | None = None, embeddings: list | None = None) -> np.ndarray:
+         trace: dict | None, layer_inp: dict | None = None, embeddings: list | None = None,
+         nextn: list | None = None) -> np.ndarray:
     """The forward pass over the rows of all prompts, laid end to end in
     prompt order; returns the logits of each prompt's last row.
 
@@ -222,6 +239,13 @@ def _run(m: OracleModel, kvs: list, prompts: list, prune: bool, n_ubatch: int | 
         raise ValueError("layer index out of range")
     if prune and 0 < ls < L and (embeddings is not None or any(il >= ls for il in want)):
         raise ValueError("extraction from pruned layers needs every row")
+    if nextn is not None:
+        if "nextn_norm" not in m.tensors:
+            raise ValueError("the model has no next-n head")
+        if len(prompts) != 1 or len(prompts[0]) < 2:
+            raise ValueError("the next-n head reads the second-to-last row of one prompt")
+        if prune and 0 < ls < L:
+            raise ValueError("the next-n head needs a row the prune drops")
     toks = np.concatenate(prompts)
     seq = np.concatenate([np.full(len(t), s, dtype=np.int64) for s, t in enumerate(prompts)])
     pos = np.concatenate([kv.n_pos + np.arange(len(t)) for kv, t in zip(kvs, prompts)])
@@ -247,6 +271,8 @@ def _run(m: OracleModel, kvs: list, prompts: list, prune: bool, n_ubatch: int | 
         layer_inp[L] = x.copy()
     if embeddings is not None:
         embeddings.append(rms_norm(x, m.f32("output_norm"), m.rms_eps))
+    if nextn is not None:
+        nextn.append(nextn_head(m, x[last[0] - 1], int(toks[last[0]])))
     logits = np.stack([head(m, x[r]) for r in last])
     for kv, t in zip(kvs, prompts):
         kv.n_pos += len(t)
@@ -255,7 +281,8 @@ def _run(m: OracleModel, kvs: list, prompts: list, prune: bool, n_ubatch: int | 
 
 def prefill(m: OracleModel, kv: KVState, tokens, prune: bool = False,
             n_ubatch: int | None = None, trace: dict | None = None,
-            layer_inp: dict | None = None, embeddings: list | None = None) -> np.ndarray:
+            layer_inp: dict | None = None, embeddings: list | None = None,
+            nextn: list | None = None) -> np.ndarray:
     """Run the prompt `tokens` from position kv.n_pos; return last-row logits.
 
     prune=False is the plain definition: all rows through all layers.
@@ -268,9 +295,10 @@ def prefill(m: OracleModel, kv: KVState, tokens, prune: bool = False,
     writes its K/V before it attends, so it sees exactly the cache the
     ubatch-by-ubatch schedule would give it.  trace, if given, receives the
     last row's hidden state after each layer.  layer_inp / embeddings: the
-    extraction outputs described at _run.
+    extraction outputs described at _run.  nextn, if given, receives the
+    next-n head's logits (nextn_head); the prune cannot serve it.
     """
-    return _run(m, [kv], [tokens], prune, n_ubatch, trace, layer_inp, embeddings)[0]
+    return _run(m, [kv], [tokens], prune, n_ubatch, trace, layer_inp, embeddings, nextn)[0]
 
 
 def prefill_multi(m: OracleModel, kvs: list, prompts: list, prune: bool = False,

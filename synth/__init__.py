@@ -28,6 +28,8 @@ Container format "PPXM" v1 (little-endian):
   T    tensor table at T = align(128 + 8*n_layer, 64), n_tensors entries of
        96 bytes: char name[64] (NUL padded), u32 type (0 F32, 1 Q4_0),
        u32 0, u64 rows, u64 cols, u64 offset (from file start)
+  Optional tensor of a next-n head (configs with `nextn`): "nextn_norm"
+       (F32 [1][d_model]); the head shares the output matrix.
   data each tensor at a 256-byte aligned offset.  Q4_0 [rows x cols] is
        rows * cols/32 blocks of 18 bytes: fp16 d, then 16 code bytes; code j
        of a block is the low nibble of byte j (j < 16) or the high nibble of
@@ -75,6 +77,8 @@ class Config:
     # kv source layer of each shared layer; None -> alternating pair below Ls
     donors: tuple | None = None
     prompt_lens: tuple = field(default=())
+    # a next-n head: its norm gain is in the container
+    nextn: bool = False
 
     @property
     def embd_scale(self) -> float:
@@ -111,11 +115,11 @@ def _add(c: Config):
 
 
 _add(Config("tiny", 1, 4, 2, 256, 4, 1, 64, 1024, 2048, 0, "geglu", True, 64, 1001,
-            prompt_lens=(64,)))
+            prompt_lens=(64,), nextn=True))
 _add(Config("tinyllama", 2, 22, 22, 2048, 32, 4, 64, 5632, 32000, 0, "swiglu", False, 512, 1002,
             prompt_lens=(512,)))
 _add(Config("e2b", 3, 35, 15, 1536, 8, 1, 256, 6144, 262144, 256, "geglu", True, 512, 1003,
-            prompt_lens=(512, 2048, 8192)))
+            prompt_lens=(512, 2048, 8192), nextn=True))
 _add(Config("e4b", 4, 42, 24, 2560, 8, 2, 256, 10240, 262144, 256, "geglu", True, 512, 1004,
             prompt_lens=(512, 2048, 8192)))
 # long-context variant: the same model as "e2b" (same seed), ubatch 1024
@@ -154,6 +158,8 @@ def tensor_list(cfg: Config) -> list[tuple[str, int, int, int]]:
             out.append((p + "ple_norm", T_F32, 1, d))
             out.append((p + "ple_gate", T_Q4_0, E, d))
             out.append((p + "ple_up", T_Q4_0, d, E))
+    if cfg.nextn:
+        out.append(("nextn_norm", T_F32, 1, d))
     return out
 
 

@@ -150,5 +150,17 @@ def brute_prefill(M: BruteModel, tokens, n_ctx: int, hidden: dict | None = None)
     return logits, K, V
 
 
+def brute_nextn(M: BruteModel, tokens, n_ctx: int):
+    """Logits of the next-n head: the output matrix applied to the row before
+    the last one's final state plus the last token's embedding, normed with
+    the head's own gain."""
+    hb = {}
+    brute_prefill(M, tokens, n_ctx, hidden=hb)
+    x = hb["inp"][M.L][len(tokens) - 2]
+    z = [a + M.escale * w for a, w in zip(x, M.t["tok_embd"][tokens[-1]])]
+    hn = _rms(z, M.t["nextn_norm"][0], M.eps)
+    return _mv(M.t["tok_embd"] if M.tied else M.t["output"], hn)
+
+
 def as_arrays(K, n_pos: int) -> np.ndarray:
     return np.array([[K[il][p] for p in range(n_pos)] for il in range(len(K))], dtype=np.float64)

@@ -9,6 +9,7 @@ resuming after N cached positions equals a full prefill (PicoLM page,
 resume section).  Several prompts in one pass are pinned to the same brute
 force run on each prompt alone.
 """
+import dataclasses
 import json
 import math
 import os
@@ -390,6 +391,53 @@ def test_multi_sequence_identical_prompts_and_rejections(tiny):
     with pytest.raises(ValueError):
         oracle.prefill_multi(m, [kv, oracle.KVState(m, 2)], [toks[:3], toks[:3]])
     assert kv.n_pos == 0
+
+
+# ------------------------------------------------------------------ next-n head
+
+@pytest.mark.parametrize("cfg", [MICRO, MICRO_SW], ids=lambda c: c.name)
+def test_nextn_head_matches_scalar_brute_force(cfg):
+    """The head reads the second-to-last row's final state: against the
+    scalar brute force, with the two rows in different ubatches; requesting
+    it changes nothing else."""
+    c = dataclasses.replace(cfg, nextn=True)
+    buf = synth.build_model(c)
+    m = oracle.parse_model(buf)
+    toks = synth.prompt(c, 5)
+    out = []
+    kv = oracle.KVState(m, 5)
+    lg = oracle.prefill(m, kv, toks, n_ubatch=2, nextn=out)
+    ref = brute.brute_nextn(brute.BruteModel(buf.tobytes()), [int(t) for t in toks], 5)
+    np.testing.assert_allclose(out[0], np.array(ref, dtype=np.float32), rtol=2e-6, atol=1e-5)
+    kv2 = oracle.KVState(m, 5)
+    assert np.array_equal(lg, oracle.prefill(m, kv2, toks, n_ubatch=2))
+    assert np.array_equal(kv.K, kv2.K) and np.array_equal(kv.V, kv2.V)
+    assert not np.allclose(out[0], lg, atol=1e-3)
+
+
+def test_nextn_head_resumes_and_refuses_the_prune(tiny):
+    """Rows before the call come from the cache: a call after N cached
+    positions gives the head of the full prompt (its second-to-last row sees
+    the same keys).  The head needs a row the prune drops, a second row, and
+    a model that has it."""
+    m, toks = tiny
+    full = []
+    oracle.prefill(m, oracle.KVState(m, 64), toks, nextn=full)
+    for N in (1, 40, 62):
+        kv = oracle.KVState(m, 64)
+        oracle.prefill(m, kv, toks[:N])
+        got = []
+        oracle.prefill(m, kv, toks[N:], nextn=got)
+        np.testing.assert_allclose(got[0], full[0], rtol=1e-6, atol=1e-6)
+    with pytest.raises(ValueError):
+        oracle.prefill(m, oracle.KVState(m, 64), toks, prune=True, nextn=[])
+    with pytest.raises(ValueError):
+        oracle.prefill(m, oracle.KVState(m, 64), toks[:1], nextn=[])
+    plain = oracle.parse_model(synth.build_model(dataclasses.replace(MICRO, nextn=False)))
+    with pytest.raises(ValueError):
+        oracle.prefill(plain, oracle.KVState(plain, 4), synth.prompt(MICRO, 4), nextn=[])
+    assert not oracle.prune_shared(m.n_layer, m.n_layer_kv_from_start, False, 1, [0] * (m.n_layer + 1),
+                                   crop_before_nextn=False)
 
 
 # ------------------------------------------------------------------ predicate and snapshot
