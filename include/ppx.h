@@ -61,6 +61,7 @@ typedef struct {
     int ple_dim;               /* per-layer embedding width E (0 = none)      */
     int kv_dim;                /* n_kv_head * head_dim                        */
     int act;                   /* 0 GeGLU, 1 SwiGLU                           */
+    int has_nextn;             /* 1: the container holds a next-n head        */
 } ppx_model_info;
 
 enum { PPX_PRUNE_AUTO = -1, PPX_PRUNE_OFF = 0, PPX_PRUNE_ON = 1 };
@@ -113,6 +114,9 @@ typedef struct {
                             embeddings != 0                                  */
     int precision;       /* PPX_PRECISION_FAST (0, the default) or
                             PPX_PRECISION_EXACT; see below                   */
+    float *nextn_logits; /* NULL, or device fp32 [n_vocab]: the next-n head's
+                            logits (see below); requesting them makes the
+                            predicate's crop_before_nextn false            */
 } ppx_prefill_params;
 
 /* Arithmetic of the row-batched layers (the single-row path and the head
@@ -128,6 +132,20 @@ typedef struct {
  *    way).  Several times slower; for models whose activations amplify fp16
  *    rounding beyond the tolerance a comparison needs. */
 enum { PPX_PRECISION_FAST = 0, PPX_PRECISION_EXACT = 1 };
+
+/* Next-n head.  The llama.cpp Gemma 4 prefill page (section 1) lets the prune
+ * apply only when the output rows can be cropped before a next-n head, i.e.
+ * no such head reads another row.  A container may hold one (F32 tensor
+ * "nextn_norm" [1][d_model]); it is a depth-1 multi-token predictor that
+ * shares the output matrix:
+ *     z      = x_{n-2} + embd_scale * deq(tok_embd[id_{n-1}])
+ *     logits = W_out rms(z, nextn_norm)
+ * where x_{n-2} is the final hidden state (before the output norm) of the
+ * call's second-to-last row and id_{n-1} the last token.  It needs a row the
+ * prune drops, so a call that requests it runs every row through every
+ * layer (prune AUTO turns it off; ON gives PPX_E_UNSUPPORTED).  Requires
+ * n_tokens >= 2 (PPX_E_INVAL) and a model with the head (PPX_E_UNSUPPORTED);
+ * ppx_prefill_multi does not serve it (PPX_E_UNSUPPORTED). */
 
 #define PPX_MAX_UBATCH 4096
 #define PPX_MAX_SEQ 64

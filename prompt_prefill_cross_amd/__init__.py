@@ -36,7 +36,8 @@ class PPXError(RuntimeError):
 
 class ModelInfo(ctypes.Structure):
     _fields_ = [(n, c_int) for n in ("n_layer", "n_layer_kv_from_start", "d_model", "n_head", "n_kv_head",
-                                     "head_dim", "n_ff", "n_vocab", "ple_dim", "kv_dim", "act")]
+                                     "head_dim", "n_ff", "n_vocab", "ple_dim", "kv_dim", "act",
+                                     "has_nextn")]
 
 
 class Timing(ctypes.Structure):
@@ -55,7 +56,7 @@ class PrefillParams(ctypes.Structure):
     _fields_ = [("n_ubatch", c_int), ("prune", c_int), ("embeddings", c_int), ("n_seq_max", c_int),
                 ("debug_hidden", c_void_p), ("timing", POINTER(Timing)), ("debug_rows", c_void_p),
                 ("embeddings_layer_inp", c_void_p), ("layer_inp_out", c_void_p), ("embd_out", c_void_p),
-                ("precision", c_int)]
+                ("precision", c_int), ("nextn_logits", c_void_p)]
 
 
 class Seq(ctypes.Structure):
@@ -222,11 +223,13 @@ class Model:
 
     def prefill(self, tokens, kv: "KVCache", n_ubatch: int = 512, prune: str = "auto", logits=None,
                 debug_hidden=None, embeddings: int = 0, n_seq_max: int = 1, stream=None, timing=None,
-                debug_rows=None, layer_flags=None, layer_inp_out=None, embd_out=None, precision: str = "fast"):
+                debug_rows=None, layer_flags=None, layer_inp_out=None, embd_out=None, precision: str = "fast",
+                nextn_logits=None):
         """Run `tokens` (int32) from kv.n_pos; return fp32 logits [n_vocab] of the last token.
 
         layer_flags (n_layer + 1 truth values) / layer_inp_out and embeddings /
-        embd_out are the extraction outputs of ppx_prefill_params."""
+        embd_out are the extraction outputs of ppx_prefill_params;
+        nextn_logits (fp32 [n_vocab] on the device) receives the next-n head's."""
         import torch
         toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
         if logits is None:
@@ -245,7 +248,8 @@ class Model:
                           c_void_p(flags.ctypes.data) if flags is not None else None,
                           c_void_p(layer_inp_out.data_ptr()) if layer_inp_out is not None else None,
                           c_void_p(embd_out.data_ptr()) if embd_out is not None else None,
-                          PRECISION[precision])
+                          PRECISION[precision],
+                          c_void_p(nextn_logits.data_ptr()) if nextn_logits is not None else None)
         st = lib().ppx_prefill(self._h, kv.handle, c_void_p(toks.ctypes.data), toks.shape[0], ctypes.byref(p),
                                _ptr(ws), ws.numel(), _ptr(logits), _stream(stream))
         _check(st, "ppx_prefill")

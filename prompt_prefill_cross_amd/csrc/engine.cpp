@@ -605,10 +605,11 @@ int layer_row(Ctx &c, int il, int pos, const int32_t *tok, bool write_kv = false
     return PPX_OK;
 }
 
-int head_row(Ctx &c, const float *x_last, float *logits) {
+// logits = W_out rms(x, gain); gain defaults to the output norm's
+int head_row(Ctx &c, const float *x_last, float *logits, const float *gain = nullptr) {
     const ppx_model *m = c.m;
     GemvArgs gh = gemv_base(c, x_last, m->out, GV_F32, logits);
-    gh.norm_g = m->out_norm;
+    gh.norm_g = gain ? gain : m->out_norm;
     gh.eps = m->eps;
     PPX_LAUNCH(c, PPX_PHASE_ROW, launch_gemv(gh, c.s));
     if (c.tm) c.tm->row_bytes += q4_bytes(m->out);
@@ -696,6 +697,15 @@ int enqueue_prefill(Ctx &c, const ppx_prefill_params *p, const int32_t *tok_dev,
                 PPX_TRY(extract(L, x, u.M, u.row0));
                 if (p->embeddings)
                     PPX_TRY(launch_rmsnorm_f32(x, m->out_norm, m->eps, u.M, d, p->embd_out + (size_t)u.row0 * d, c.s));
+                if (p->nextn_logits && n - 2 >= u.row0 && n - 2 < u.row0 + u.M) {
+                    // next-n head: the second-to-last row's final state plus the
+                    // last token's embedding (xr is free: no pruned tail runs)
+                    float *z = c.at<float>(c.L.xr);
+                    PPX_LAUNCH(c, PPX_PHASE_OTHER,
+                               launch_embed_add(m->tok, tok_dev + n - 1, m->embd_scale,
+                                                x + (size_t)(n - 2 - u.row0) * d, z, c.s));
+                    PPX_TRY(head_row(c, z, p->nextn_logits, m->nextn_norm));
+                }
             }
             if (last) {
                 const float *x_last = x + (size_t)(u.M - 1) * d;
@@ -740,6 +750,7 @@ int run_graph(Ctx &c, const ppx_prefill_params *p, const int32_t *tok_dev, int n
     key.kv_vt = c.kv->vt;
     key.ws = c.ws;
     key.logits = logits;
+    key.nextn = p->nextn_logits;
     key.n_ctx = c.kv->n_ctx;
     key.n = n;
     key.p0 = p0;
@@ -748,7 +759,7 @@ int run_graph(Ctx &c, const ppx_prefill_params *p, const int32_t *tok_dev, int n
     key.exact = c.exact;
     for (auto &g : m->graphs) {
         if (g.kv_k == key.kv_k && g.kv_vt == key.kv_vt && g.ws == key.ws && g.logits == key.logits &&
-            g.n_ctx == key.n_ctx && g.n == key.n && g.p0 == key.p0 && g.ub == key.ub && g.prune == key.prune &&
+            g.nextn == key.nextn && g.n_ctx == key.n_ctx && g.n == key.n && g.p0 == key.p0 && g.ub == key.ub && g.prune == key.prune &&
             g.exact == key.exact) {
             g.last_use = ++m->graph_clock;
             return hipGraphLaunch(g.exec, c.s) == hipSuccess ? PPX_OK : PPX_E_HIP;
@@ -852,8 +863,13 @@ int prefill(ppx_model *m, ppx_kv *kv, const int32_t *tokens, int n, const ppx_pr
     if (ws_bytes < c.L.total) return PPX_E_NOMEM;
     if (p->precision != PPX_PRECISION_FAST && p->precision != PPX_PRECISION_EXACT) return PPX_E_INVAL;
     c.exact = p->precision == PPX_PRECISION_EXACT;
+    if (p->nextn_logits) {
+        if (!I.has_nextn) return PPX_E_UNSUPPORTED;
+        if (n < 2) return PPX_E_INVAL;
+    }
     const int L = I.n_layer, Ls = I.n_layer_kv_from_start, d = I.d_model;
-    const int can = predicate(L, Ls, p->embeddings, p->n_seq_max, p->embeddings_layer_inp, 1);
+    // a next-n head reads a row other than the output row: the rows cannot be cropped before it
+    const int can = predicate(L, Ls, p->embeddings, p->n_seq_max, p->embeddings_layer_inp, p->nextn_logits == nullptr);
     bool prune;
     if (p->prune == PPX_PRUNE_AUTO) prune = can;
     else if (p->prune == PPX_PRUNE_OFF) prune = false;
@@ -993,7 +1009,7 @@ int prefill_multi(ppx_model *m, const ppx_seq *seqs, int k, const ppx_prefill_pa
     if (k < 1 || k > PPX_MAX_SEQ) return PPX_E_INVAL;
     const ppx_model_info &I = m->info;
     if (p->embeddings != 0 || p->embeddings_layer_inp) return PPX_E_UNSUPPORTED;
-    if (p->debug_rows || p->debug_hidden) return PPX_E_UNSUPPORTED;
+    if (p->debug_rows || p->debug_hidden || p->nextn_logits) return PPX_E_UNSUPPORTED;
     if (p->n_seq_max < k) return PPX_E_INVAL;
     if (p->n_ubatch < 1 || p->n_ubatch > PPX_MAX_UBATCH) return PPX_E_INVAL;
     if (p->precision != PPX_PRECISION_FAST && p->precision != PPX_PRECISION_EXACT) return PPX_E_INVAL;

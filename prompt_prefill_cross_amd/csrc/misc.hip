@@ -12,6 +12,13 @@ __global__ __launch_bounds__(256) void k_embed(Q4R w, const int32_t *ids, float 
     for (int k = threadIdx.x; k < w.K; k += 256) x[(size_t)t * w.K + k] = scale * q4r_weight(w, id, k);
 }
 
+// x[k] = base[k] + scale * deq(w[*id])[k]: one row (the next-n head's input)
+__global__ __launch_bounds__(256) void k_embed_add(Q4R w, const int32_t *id, float scale, const float *base,
+                                                   float *x) {
+    const int t = *id;
+    for (int k = threadIdx.x; k < w.K; k += 256) x[k] = base[k] + scale * q4r_weight(w, t, k);
+}
+
 __device__ __forceinline__ float block_sum_256(float v, float *red) {
     v = wave_sum(v);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -383,6 +390,11 @@ int launch_gemv(const GemvArgs &a, hipStream_t s) {
 int launch_embed(const Q4R &tok, const int32_t *ids, int M, float scale, float *x, hipStream_t s) {
     if (M <= 0) return PPX_OK;
     hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, s, tok, ids, scale, x);
+    return ok();
+}
+
+int launch_embed_add(const Q4R &tok, const int32_t *id, float scale, const float *base, float *x, hipStream_t s) {
+    hipLaunchKernelGGL(k_embed_add, dim3(1), dim3(256), 0, s, tok, id, scale, base, x);
     return ok();
 }
 

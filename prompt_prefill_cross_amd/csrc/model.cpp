@@ -236,6 +236,10 @@ int model_load(const uint8_t *b, size_t n, hipStream_t stream, void *weights_dev
         if ((st = plain(m->out, outw))) return st;
     }
     if ((st = plan_f32(m->out_norm, need("output_norm", 0, 1, d)))) return st;
+    if (p.t.count("nextn_norm")) {
+        if ((st = plan_f32(m->nextn_norm, need("nextn_norm", 0, 1, d)))) return st;
+        I.has_nextn = 1;
+    }
     size_t ple_off = 0;
     const HostTensor *ple = nullptr;
     if (E) {

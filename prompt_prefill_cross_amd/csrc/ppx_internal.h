@@ -62,6 +62,7 @@ struct ppx_model {
     std::vector<ppx::LayerW> layers;
     ppx::Q4R tok, out;  // out == tok when tied
     const float *out_norm = nullptr;
+    const float *nextn_norm = nullptr;  // the next-n head's gain (has_nextn)
     const uint8_t *ple_raw = nullptr;  // raw Q4_0 blocks [V][L*E/32][18]
     void *dev = nullptr;               // one allocation for all weights
     size_t dev_bytes = 0;
@@ -75,7 +76,7 @@ struct ppx_model {
     // Recorded prefill launch sequences (HIP graphs), keyed by everything the
     // kernels' arguments depend on; token ids are read from device memory.
     struct Graph {
-        const void *kv_k = nullptr, *kv_vt = nullptr, *ws = nullptr, *logits = nullptr;
+        const void *kv_k = nullptr, *kv_vt = nullptr, *ws = nullptr, *logits = nullptr, *nextn = nullptr;
         int n_ctx = 0, n = 0, p0 = 0, ub = 0, prune = 0, exact = 0;
         hipGraphExec_t exec = nullptr;
         unsigned long long last_use = 0;
@@ -302,6 +303,7 @@ int launch_attn_1row(const Attn1Args &a, hipStream_t s);
 size_t attn1_scratch_floats(int H, int hd, int n_pos);
 
 int launch_embed(const Q4R &tok, const int32_t *ids, int M, float scale, float *x, hipStream_t s);
+int launch_embed_add(const Q4R &tok, const int32_t *id, float scale, const float *base, float *x, hipStream_t s);
 // y = rmsnorm(x) * g -> fp16 in the fragment-tiled layout (the GEMM A operand).
 int launch_rmsnorm_f16(const float *x, const float *g, float eps, int M, int d, __half *out,
                        hipStream_t s);

@@ -10,6 +10,7 @@ invariants on the GPU:
     section), at N = 25 and N = 500 for the TinyLlama-shaped model;
   * ubatch size does not change the result.
 """
+import dataclasses
 import os
 
 import numpy as np
@@ -264,6 +265,61 @@ def test_tiny_error_paths(ppx):
     assert kv.n_pos == 0
     mm.prefill([1, 2, 3], kv)
     assert kv.n_pos == 3
+
+
+# (config, prompt length, ubatch, precision); in the second and the last case
+# the two rows the next-n head reads sit in different ubatches
+NEXTN_RUNS = [("tiny", 64, 64, "exact"), ("tiny", 33, 16, "exact"), ("tiny", 64, 16, "fast"),
+              ("e2b", 129, 64, "fast")]
+
+
+@pytest.mark.parametrize("cfg,n,ub,precision", NEXTN_RUNS)
+def test_nextn_head_vs_oracle(ppx, cfg, n, ub, precision):
+    """A next-n head reads the second-to-last row, which makes the
+    predicate's crop_before_nextn false: prune auto runs every row through
+    every layer, and the head's logits and the last row's both match the
+    oracle -- on the recorded launch sequence and on the one-ubatch-at-a-time
+    debug path."""
+    om = oracle_model(cfg)
+    toks = synth.prompt(cfg, n)
+    want = []
+    ref = oracle.prefill(om, oracle.KVState(om, n), toks, nextn=want)
+    mm = engine_model(ppx, cfg)
+    assert mm.info["has_nextn"] == 1
+    L, d, Ls = mm.info["n_layer"], mm.info["d_model"], mm.info["n_layer_kv_from_start"]
+    rows = torch.full((L, n, d), float("nan"), dtype=torch.float32, device="cuda")
+    for debug in (False, True, False):
+        kv = ppx.KVCache(mm, n)
+        nx = torch.empty(mm.info["n_vocab"], dtype=torch.float32, device="cuda")
+        lg = mm.prefill(toks, kv, n_ubatch=ub, precision=precision, nextn_logits=nx,
+                        debug_rows=rows if debug else None)
+        torch.cuda.synchronize()
+        for what, got, r in (("last row", lg, ref), ("next-n", nx, want[0])):
+            ok, dd = logits_ok(got.cpu().numpy(), r)
+            print(f"{cfg} n={n} ub={ub} {precision} debug={debug} {what}: max-abs {dd:.2e}")
+            assert ok, (what, dd)
+    # every KV-shared layer saw every row: the prune was off
+    assert bool(torch.isfinite(rows[Ls:]).all())
+
+
+def test_nextn_head_error_paths(ppx):
+    mm = engine_model(ppx, "tiny")
+    kv = ppx.KVCache(mm, 32)
+    nx = torch.empty(mm.info["n_vocab"], dtype=torch.float32, device="cuda")
+    with pytest.raises(ppx.PPXError) as e:
+        mm.prefill([1, 2, 3], kv, prune="on", nextn_logits=nx)  # the predicate is false
+    assert e.value.status == -7
+    with pytest.raises(ppx.PPXError) as e:
+        mm.prefill([1], kv, nextn_logits=nx)  # no second-to-last row
+    assert e.value.status == -1
+    plain = ppx.Model(synth.build_model(dataclasses.replace(synth.CONFIGS["tiny"], nextn=False)))
+    assert plain.info["has_nextn"] == 0
+    kp = ppx.KVCache(plain, 32)
+    with pytest.raises(ppx.PPXError) as e:
+        plain.prefill([1, 2, 3], kp, nextn_logits=nx)
+    assert e.value.status == -7
+    assert kv.n_pos == 0 and kp.n_pos == 0
+    torch.cuda.synchronize()
 
 
 def test_tinyllama_full_and_resume(ppx, tmp_path):
