@@ -112,6 +112,66 @@ class KVState:
         return c
 
 
+class UnifiedKV:
+    """One fp16 K and V buffer shared by several sequences, [Ls][n_cells][kv_dim]
+    each; cell c holds position cell_pos[c] of sequence cell_seq[c] (-1: a
+    free cell).  The llama.cpp Gemma 4 prefill page (section 5) contrasts this
+    unified cache with one cache per sequence (split)."""
+
+    def __init__(self, m: OracleModel, n_cells: int):
+        ls = m.n_layer_kv_from_start
+        self.n_cells = n_cells
+        self.K = np.zeros((ls, n_cells, m.kv_dim), dtype=np.float16)
+        self.V = np.zeros((ls, n_cells, m.kv_dim), dtype=np.float16)
+        self.cell_seq = np.full(n_cells, -1, dtype=np.int64)
+        self.cell_pos = np.full(n_cells, -1, dtype=np.int64)
+
+    def n_pos(self, s: int) -> int:
+        return int(np.count_nonzero(self.cell_seq == s))
+
+    def cells_of(self, s: int) -> np.ndarray:
+        """The cells of sequence s in position order."""
+        c = np.nonzero(self.cell_seq == s)[0]
+        return c[np.argsort(self.cell_pos[c])]
+
+    def seq_rm(self, s: int) -> None:
+        """Free every cell of sequence s (their contents stay, never read)."""
+        free = self.cell_seq == s
+        self.cell_seq[free] = -1
+        self.cell_pos[free] = -1
+
+
+class _UnifiedSeq:
+    """Sequence s of a unified cache as _run sees a cache: its position count
+    and capacity (the cells that are free or already its own)."""
+
+    def __init__(self, u: UnifiedKV, s: int):
+        self.u, self.s = u, s
+        self.n_pos = u.n_pos(s)
+        self.n_ctx = self.n_pos + int(np.count_nonzero(u.cell_seq == -1))
+
+
+def attention_cells(q: np.ndarray, K: np.ndarray, V: np.ndarray, cell_seq: np.ndarray, cell_pos: np.ndarray,
+                    seq: np.ndarray, pos: np.ndarray) -> np.ndarray:
+    """Softmax attention over the cells of one shared buffer: row t sees
+    every cell c with cell_seq[c] == seq[t] and cell_pos[c] <= pos[t] (the
+    mask by sequence and position); other cells get weight zero.
+    q: [rows, H, hd] fp64; K, V: [n_cells, KVH, hd]; returns [rows, H*hd]."""
+    rows, H, hd = q.shape
+    grp = H // K.shape[1]
+    Kf, Vf = K.astype(np.float64), V.astype(np.float64)
+    vis = (cell_seq[None, :] == seq[:, None]) & (cell_pos[None, :] >= 0) & (cell_pos[None, :] <= pos[:, None])
+    out = np.empty((rows, H, hd), dtype=np.float64)
+    scale = 1.0 / math.sqrt(hd)
+    for h in range(H):
+        g = h // grp
+        sc = np.where(vis, (q[:, h, :] @ Kf[:, g, :].T) * scale, -np.inf)
+        sc = sc - sc.max(axis=1, keepdims=True)
+        w = np.exp(sc)
+        out[:, h, :] = (w / w.sum(axis=1, keepdims=True)) @ Vf[:, g, :]
+    return out.reshape(rows, H * hd)
+
+
 # ---------------------------------------------------------------- forward
 
 def embed_rows(m: OracleModel, tokens: np.ndarray) -> np.ndarray:
@@ -119,11 +179,13 @@ def embed_rows(m: OracleModel, tokens: np.ndarray) -> np.ndarray:
 
 
 def _layer(m: OracleModel, kvs: list, il: int, x: np.ndarray, pos: np.ndarray,
-           toks: np.ndarray, seq: np.ndarray, W: dict) -> np.ndarray:
+           toks: np.ndarray, seq: np.ndarray, W: dict, cell: np.ndarray | None = None) -> np.ndarray:
     """Layer il for rows x of sequences seq (row t belongs to kvs[seq[t]]).
 
     Every row's K/V goes into its own sequence's cache before any row
-    attends, and a row attends only to its own sequence's cache.
+    attends, and a row attends only to its own sequence's cache.  With a
+    unified cache (kvs[s] = _UnifiedSeq) row t's K/V go to cell cell[t] of
+    the one buffer and attention masks the buffer's cells by sequence.
     """
     H, KVH, hd = m.n_head, m.n_kv_head, m.head_dim
     own = il < m.n_layer_kv_from_start
@@ -133,6 +195,15 @@ def _layer(m: OracleModel, kvs: list, il: int, x: np.ndarray, pos: np.ndarray,
     a = rms_norm(x, W["attn_norm"], m.rms_eps)
     q = rope((a @ W["wq"].T).reshape(r, H, hd), pos, m.rope_base)
     groups = [(int(s), np.nonzero(seq == s)[0]) for s in np.unique(seq)]
+    if cell is not None:
+        u = kvs[0].u
+        sid = np.array([kvs[int(s)].s for s in seq])
+        if own:
+            u.K[il, cell] = rope((a @ W["wk"].T).reshape(r, KVH, hd), pos, m.rope_base).reshape(r, -1).astype(np.float16)
+            u.V[il, cell] = (a @ W["wv"].T).astype(np.float16)
+        o = attention_cells(q, u.K[src].reshape(-1, KVH, hd), u.V[src].reshape(-1, KVH, hd),
+                            u.cell_seq, u.cell_pos, sid, pos)
+        return _layer_tail(m, il, x + o @ W["wo"].T, toks, W)
     if own:
         k = rope((a @ W["wk"].T).reshape(r, KVH, hd), pos, m.rope_base).reshape(r, KVH * hd)
         v = a @ W["wv"].T
@@ -150,8 +221,11 @@ def _layer(m: OracleModel, kvs: list, il: int, x: np.ndarray, pos: np.ndarray,
             Kc.flags.writeable = False
             Vc.flags.writeable = False
         o[rows] = attention(q[rows], Kc.reshape(-1, KVH, hd), Vc.reshape(-1, KVH, hd), pos[rows])
-    x = x + o @ W["wo"].T
+    return _layer_tail(m, il, x + o @ W["wo"].T, toks, W)
 
+
+def _layer_tail(m: OracleModel, il: int, x: np.ndarray, toks: np.ndarray, W: dict) -> np.ndarray:
+    """The feed-forward block and the per-layer embedding of layer il."""
     b = rms_norm(x, W["ffn_norm"], m.rms_eps)
     gt = b @ W["ffn_gate"].T
     up = b @ W["ffn_up"].T
@@ -216,7 +290,7 @@ def nextn_head(m: OracleModel, x_prev: np.ndarray, tok_last: int) -> np.ndarray:
 
 def _run(m: OracleModel, kvs: list, prompts: list, prune: bool, n_ubatch: int | None,
          trace: dict | None, layer_inp: dict | None = None, embeddings: list | None = None,
-         nextn: list | None = None) -> np.ndarray:
+         nextn: list | None = None, unified: UnifiedKV | None = None) -> np.ndarray:
     """The forward pass over the rows of all prompts, laid end to end in
     prompt order; returns the logits of each prompt's last row.
 
@@ -250,11 +324,21 @@ def _run(m: OracleModel, kvs: list, prompts: list, prune: bool, n_ubatch: int | 
     seq = np.concatenate([np.full(len(t), s, dtype=np.int64) for s, t in enumerate(prompts)])
     pos = np.concatenate([kv.n_pos + np.arange(len(t)) for kv, t in zip(kvs, prompts)])
     last = np.cumsum([len(t) for t in prompts]) - 1  # each prompt's output row
+    cell = None
+    if unified is not None:
+        # the rows take the lowest free cells, in row order
+        free = np.nonzero(unified.cell_seq == -1)[0]
+        if free.shape[0] < toks.shape[0]:
+            raise ValueError("context overflow")
+        cell = free[:toks.shape[0]]
+        unified.cell_seq[cell] = np.array([kvs[int(q)].s for q in seq])
+        unified.cell_pos[cell] = pos
     ub = toks.shape[0] if n_ubatch is None else int(n_ubatch)
     x = embed_rows(m, toks)
     for il in range(L):
         if prune and il == ls and 0 < ls < L:
             x, pos, toks, seq = x[last], pos[last], toks[last], seq[last]
+            cell = cell[last] if cell is not None else None
             last = np.arange(len(prompts))
         if il in want:
             layer_inp[il] = x.copy()
@@ -262,7 +346,8 @@ def _run(m: OracleModel, kvs: list, prompts: list, prune: bool, n_ubatch: int | 
         parts = []
         for s in range(0, x.shape[0], ub):
             e = min(x.shape[0], s + ub)
-            parts.append(_layer(m, kvs, il, x[s:e], pos[s:e], toks[s:e], seq[s:e], W))
+            parts.append(_layer(m, kvs, il, x[s:e], pos[s:e], toks[s:e], seq[s:e], W,
+                                None if cell is None else cell[s:e]))
         x = np.concatenate(parts, axis=0)
         del W
         if trace is not None:
@@ -319,3 +404,21 @@ def prefill_multi(m: OracleModel, kvs: list, prompts: list, prune: bool = False,
     if len(prompts) < 1 or len(prompts) != len(kvs):
         raise ValueError("one cache per prompt, at least one prompt")
     return _run(m, list(kvs), list(prompts), prune, n_ubatch, None)
+
+
+def prefill_unified(m: OracleModel, u: UnifiedKV, seq_ids, prompts, prune: bool = False,
+                    n_ubatch: int | None = None) -> np.ndarray:
+    """Several prompts in one pass over ONE cache: prompt i belongs to
+    sequence seq_ids[i] and runs from that sequence's position count in u.
+    The rows take free cells of u (lowest first, in row order); each row's
+    K/V go to its cell, and it attends to the cells of its own sequence up
+    to its position (attention_cells).  Ubatching and pruning are those of
+    prefill_multi; the logits ([n_seq][n_vocab], fp32) and each sequence's
+    (position -> K/V) contents are by definition those of prefill_multi
+    with one cache per sequence, which is what the pins check."""
+    ids = [int(v) for v in seq_ids]
+    if len(prompts) < 1 or len(prompts) != len(ids) or len(set(ids)) != len(ids) or min(ids) < 0:
+        raise ValueError("one distinct sequence id per prompt, at least one prompt")
+    if sum(len(t) for t in prompts) > int(np.count_nonzero(u.cell_seq == -1)):
+        raise ValueError("context overflow")
+    return _run(m, [_UnifiedSeq(u, s) for s in ids], list(prompts), prune, n_ubatch, None, unified=u)

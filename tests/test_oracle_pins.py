@@ -393,6 +393,86 @@ def test_multi_sequence_identical_prompts_and_rejections(tiny):
     assert kv.n_pos == 0
 
 
+# ------------------------------------------------------------------ unified cache
+
+def test_masked_cell_attention_reduces_to_causal_attention():
+    """One sequence in position order is plain causal attention; shuffling
+    the cells and adding another sequence's cells (huge values) between
+    them changes nothing."""
+    rng = np.random.default_rng(21)
+    P, H, KVH, hd = 11, 4, 2, 8
+    q = rng.standard_normal((P, H, hd))
+    K = rng.standard_normal((P, KVH, hd)).astype(np.float16)
+    V = rng.standard_normal((P, KVH, hd)).astype(np.float16)
+    pos = np.arange(P)
+    ref = F.attention(q, K, V, pos)
+    got = F.attention_cells(q, K, V, np.zeros(P, np.int64), pos, np.zeros(P, np.int64), pos)
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-13)
+    n = 2 * P + 3
+    cells = rng.permutation(n)[:P]
+    Ku = np.full((n, KVH, hd), 1e4, np.float16)
+    Vu = np.full((n, KVH, hd), -1e4, np.float16)
+    cs = np.full(n, 7, np.int64)
+    cp = np.arange(n) % 5
+    cs[-1] = -1
+    Ku[cells], Vu[cells], cs[cells], cp[cells] = K, V, 3, pos
+    got = F.attention_cells(q, Ku, Vu, cs, cp, np.full(P, 3, np.int64), pos)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def _seq_kv(u, s):
+    c = u.cells_of(s)
+    return u.K[:, c], u.V[:, c]
+
+
+@pytest.mark.parametrize("prune", [False, True])
+def test_unified_cache_matches_scalar_brute_force(prune):
+    """Three prompts in one buffer, ubatches straddling them: each prompt's
+    logits and (position -> K/V) against the brute force on that prompt alone."""
+    buf = synth.build_model(MICRO)
+    m = oracle.parse_model(buf)
+    bm = brute.BruteModel(buf.tobytes())
+    prompts = [synth.prompt(MICRO, 5), synth.prompt(MICRO, 9)[4:7], synth.prompt(MICRO, 12)[8:12]]
+    u = oracle.UnifiedKV(m, 16)
+    lg = oracle.prefill_unified(m, u, [4, 0, 2], prompts, prune=prune, n_ubatch=2)
+    for i, (sid, t) in enumerate(zip([4, 0, 2], prompts)):
+        blg, bK, bV = brute.brute_prefill(bm, [int(v) for v in t], len(t))
+        np.testing.assert_allclose(lg[i], np.array(blg, dtype=np.float32), rtol=2e-6, atol=1e-5)
+        K, V = _seq_kv(u, sid)
+        np.testing.assert_array_equal(K.astype(np.float64), brute.as_arrays(bK, len(t)))
+        np.testing.assert_array_equal(V.astype(np.float64), brute.as_arrays(bV, len(t)))
+        assert u.n_pos(sid) == len(t)
+    assert np.count_nonzero(u.cell_seq == -1) == 16 - 12
+
+
+def test_unified_cache_interleaved_calls_and_reuse(tiny):
+    """Sequences that grow over several calls hold cells scattered through
+    the buffer; a removed sequence's cells are reused by a new one.  Each
+    sequence matches its own split cache, call by call."""
+    m, toks = tiny
+    a, b, c = toks[:20], toks[20:45], toks[45:64]
+    u = oracle.UnifiedKV(m, 64)
+    ka, kb, kc = oracle.KVState(m, 64), oracle.KVState(m, 64), oracle.KVState(m, 64)
+    steps = [([0, 1], [a[:7], b[:10]], [ka, kb]), ([1, 0], [b[10:], a[7:]], [kb, ka])]
+    for ids, ps, kvs in steps:
+        got = oracle.prefill_unified(m, u, ids, ps, n_ubatch=8)
+        want = oracle.prefill_multi(m, kvs, ps, n_ubatch=8)
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+    assert not np.all(np.diff(u.cells_of(0)) == 1)  # sequence 0's cells are not one run
+    u.seq_rm(1)
+    assert u.n_pos(1) == 0
+    lg = oracle.prefill_unified(m, u, [5, 0], [c, b[:3]], prune=True, n_ubatch=16)
+    np.testing.assert_allclose(lg[0], oracle.prefill(m, kc, c), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lg[1], oracle.prefill(m, ka, b[:3]), rtol=1e-12, atol=1e-12)
+    for sid, kv in ((5, kc), (0, ka)):
+        K, V = _seq_kv(u, sid)
+        assert np.array_equal(K, kv.K[:, :kv.n_pos]) and np.array_equal(V, kv.V[:, :kv.n_pos])
+    with pytest.raises(ValueError):
+        oracle.prefill_unified(m, u, [0, 0], [c[:1], c[:1]])
+    with pytest.raises(ValueError):
+        oracle.prefill_unified(m, u, [9], [toks[:u.n_cells]])
+
+
 # ------------------------------------------------------------------ next-n head
 
 @pytest.mark.parametrize("cfg", [MICRO, MICRO_SW], ids=lambda c: c.name)
