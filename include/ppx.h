@@ -303,6 +303,70 @@ size_t ppx_workspace_bytes_multi(const ppx_model *m, int n_ubatch, int n_seq, lo
 int ppx_prefill_multi(ppx_model *m, const ppx_seq *seqs, int n_seq, const ppx_prefill_params *p, void *ws_dev,
                       size_t ws_bytes, float *logits_dev, void *hip_stream);
 
+/* ---------------------------------------------------------------- unified cache
+ *
+ * One KV buffer shared by several sequences (the llama.cpp Gemma 4 prefill
+ * page, section 5, measures such a unified cache against one cache per
+ * sequence).  Every cell holds one position of one sequence; cells are handed
+ * out in pages of 64 consecutive positions of one sequence, the lowest free
+ * page first, so a sequence that grows over several calls holds pages
+ * scattered through the buffer, and a row attends only to the cells of its
+ * own sequence up to its position.  The layout per KV-owning layer is that of
+ * ppx_kv with n_cells in place of n_ctx (K [n_cells][kv_dim], V transposed
+ * [kv_dim][n_cells]). */
+typedef struct ppx_kvu ppx_kvu;
+
+/* Device bytes of a unified cache of n_cells cells (a positive multiple of
+ * 64); 0 otherwise. */
+size_t ppx_kvu_bytes(const ppx_model *m, int n_cells);
+/* Wrap caller-owned device memory (>= ppx_kvu_bytes, 256-byte aligned; the
+ * caller frees it after ppx_kvu_free) as a unified cache for sequence ids
+ * 0 .. n_seq_max - 1 (1 <= n_seq_max <= 65536), all empty.  PPX_E_INVAL,
+ * PPX_E_NOMEM (bytes too small), PPX_E_HIP. */
+int ppx_kvu_init(ppx_model *m, void *kv_dev, size_t bytes, int n_cells, int n_seq_max, ppx_kvu **out);
+void ppx_kvu_free(ppx_kvu *u);
+/* Positions held by sequence seq_id (PPX_E_INVAL for a bad id or handle). */
+int ppx_kvu_n_pos(const ppx_kvu *u, int seq_id);
+/* Cells in pages that no sequence holds. */
+int ppx_kvu_free_cells(const ppx_kvu *u);
+/* Release every cell of sequence seq_id (its n_pos becomes 0).  The cells'
+ * contents stay until a later call overwrites them; no kernel reads them.
+ * Host-only: the caller orders it after any queued call that uses them. */
+int ppx_kvu_seq_rm(ppx_kvu *u, int seq_id);
+/* The cell of each of positions 0 .. n-1 of sequence seq_id, into
+ * cells_host[0..n) (host int32); n <= ppx_kvu_n_pos.  PPX_E_INVAL. */
+int ppx_kvu_cells(const ppx_kvu *u, int seq_id, int32_t *cells_host, int n);
+
+/* One prompt of a unified-cache prefill: tokens_host[0..n_tokens) of
+ * sequence seq_id, continuing at that sequence's position count. */
+typedef struct {
+    int seq_id;
+    const int32_t *tokens_host;
+    int n_tokens;
+} ppx_useq;
+
+/* Device workspace bytes of a ppx_prefill_unified call over n_seq prompts of
+ * n_tokens_total tokens together in a cache of n_cells cells; 0 for
+ * arguments out of range. */
+size_t ppx_workspace_bytes_unified(const ppx_model *m, int n_ubatch, int n_seq, long n_tokens_total, int n_cells);
+
+/* ppx_prefill_multi over one unified cache: prompt s (distinct seq_ids)
+ * takes the free pages its new positions need, then the pass is that of
+ * ppx_prefill_multi (rows end to end in ubatches, the same generalised prune,
+ * one logits row per prompt) with every K/V write and read going to the
+ * sequence's cells.  Each sequence's result equals ppx_prefill of its prompt
+ * alone in a cache of its own; n_seq == 1 runs the same pass.  A generation
+ * step is a call with one token.  Errors are reported before any work is
+ * queued and leave every sequence and page unchanged: PPX_E_EMPTY,
+ * PPX_E_TOKEN, PPX_E_CTX (a sequence past n_cells positions, or too few free
+ * pages), PPX_E_INVAL (NULL arguments, a seq_id out of range or repeated, a
+ * cache of another model), PPX_E_UNSUPPORTED (extraction, debug outputs, the
+ * next-n head, prune ON while the predicate is false), PPX_E_NOMEM; PPX_E_HIP
+ * if a launch fails.  Asynchronous on the stream; one call in flight per
+ * cache. */
+int ppx_prefill_unified(ppx_model *m, ppx_kvu *u, const ppx_useq *seqs, int n_seq, const ppx_prefill_params *p,
+                        void *ws_dev, size_t ws_bytes, float *logits_dev, void *hip_stream);
+
 /* One generation step after a prefill: the row of `token` at position n_pos
  * runs through every layer on the single-row (GEMV) path -- KV-owning layers
  * append its fp16 K and V at n_pos, KV-shared layers read their source

@@ -13,7 +13,7 @@ from ctypes import POINTER, c_char_p, c_float, c_int, c_size_t, c_uint8, c_void_
 
 import numpy as np
 
-__all__ = ["PPXError", "lib", "Model", "KVCache", "prune_predicate", "LIB_PATH"]
+__all__ = ["PPXError", "lib", "Model", "KVCache", "UnifiedCache", "prune_predicate", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libppx.so")
 
@@ -63,6 +63,10 @@ class Seq(ctypes.Structure):
     _fields_ = [("kv", c_void_p), ("tokens_host", c_void_p), ("n_tokens", c_int)]
 
 
+class USeq(ctypes.Structure):
+    _fields_ = [("seq_id", c_int), ("tokens_host", c_void_p), ("n_tokens", c_int)]
+
+
 # (name, restype, argtypes) of every symbol declared in include/ppx.h
 SIGNATURES = [
     ("ppx_model_load", c_int, [c_void_p, c_size_t, c_void_p, POINTER(c_void_p)]),
@@ -87,6 +91,16 @@ SIGNATURES = [
     ("ppx_workspace_bytes_multi", c_size_t, [c_void_p, c_int, c_int, ctypes.c_long, c_int]),
     ("ppx_prefill_multi", c_int, [c_void_p, POINTER(Seq), c_int, POINTER(PrefillParams), c_void_p, c_size_t,
                                   c_void_p, c_void_p]),
+    ("ppx_kvu_bytes", c_size_t, [c_void_p, c_int]),
+    ("ppx_kvu_init", c_int, [c_void_p, c_void_p, c_size_t, c_int, c_int, POINTER(c_void_p)]),
+    ("ppx_kvu_free", None, [c_void_p]),
+    ("ppx_kvu_n_pos", c_int, [c_void_p, c_int]),
+    ("ppx_kvu_free_cells", c_int, [c_void_p]),
+    ("ppx_kvu_seq_rm", c_int, [c_void_p, c_int]),
+    ("ppx_kvu_cells", c_int, [c_void_p, c_int, c_void_p, c_int]),
+    ("ppx_workspace_bytes_unified", c_size_t, [c_void_p, c_int, c_int, ctypes.c_long, c_int]),
+    ("ppx_prefill_unified", c_int, [c_void_p, c_void_p, POINTER(USeq), c_int, POINTER(PrefillParams), c_void_p,
+                                    c_size_t, c_void_p, c_void_p]),
     ("ppx_decode", c_int, [c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_void_p, c_void_p]),
     ("ppx_decode_static", c_int, [c_void_p, c_void_p, c_int, c_void_p, c_void_p]),
     ("ppx_decode_static_limit", c_size_t, []),
@@ -300,6 +314,35 @@ class Model:
         _check(st, "ppx_prefill_multi")
         return logits
 
+    def prefill_unified(self, prompts, seq_ids, cache: "UnifiedCache", n_ubatch: int = 512, prune: str = "auto",
+                        logits=None, n_seq_max: int | None = None, stream=None, timing=None, precision: str = "fast"):
+        """Several prompts in one pass over one unified cache, prompt s for
+        sequence seq_ids[s]; return fp32 logits [n_seq][n_vocab]."""
+        import torch
+        toks = [np.ascontiguousarray(np.asarray(t, dtype=np.int32).reshape(-1)) for t in prompts]
+        k = len(toks)
+        if k != len(seq_ids):
+            raise ValueError("one sequence id per prompt")
+        seqs = (USeq * max(k, 1))()
+        for i, (t, sid) in enumerate(zip(toks, seq_ids)):
+            seqs[i] = USeq(int(sid), t.ctypes.data if t.size else None, int(t.shape[0]))
+        if logits is None:
+            logits = torch.empty((max(k, 1), self.info["n_vocab"]), dtype=torch.float32, device="cuda")
+        total = max(1, sum(int(t.shape[0]) for t in toks))
+        need = lib().ppx_workspace_bytes_unified(self._h, max(n_ubatch, 1), max(min(k, 64), 1), total,
+                                                 cache.n_cells)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+        ws = self._ws
+        p = PrefillParams(n_ubatch, PRUNE[prune] if isinstance(prune, str) else int(prune), 0,
+                          k if n_seq_max is None else n_seq_max, None,
+                          ctypes.pointer(timing) if timing is not None else None, None, None, None, None,
+                          PRECISION[precision])
+        st = lib().ppx_prefill_unified(self._h, cache.handle, seqs, k, ctypes.byref(p), _ptr(ws), ws.numel(),
+                                       _ptr(logits), _stream(stream))
+        _check(st, "ppx_prefill_unified")
+        return logits
+
     def decode(self, token: int, kv: "KVCache", logits=None, stream=None):
         """One generation step: `token` at kv.n_pos through every layer on the
         single-row path (owning layers append its K/V); return its fp32 logits."""
@@ -510,6 +553,74 @@ class KVCache:
     def close(self):
         if self._h:
             lib().ppx_kv_free(self._h)
+            self._h = c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class UnifiedCache:
+    """One fp16 KV buffer for several sequences (ids 0 .. n_seq_max - 1) in a
+    caller-owned (torch) device buffer; cells are handed out in pages of 64
+    positions of one sequence."""
+
+    def __init__(self, model: Model, n_cells: int, n_seq_max: int):
+        import torch
+        self.model = model
+        self.n_cells = n_cells
+        nbytes = lib().ppx_kvu_bytes(model.handle, n_cells)
+        if nbytes == 0:
+            raise ValueError("n_cells must be a positive multiple of 64")
+        self.buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        self._h = c_void_p()
+        _check(lib().ppx_kvu_init(model.handle, _ptr(self.buf), self.buf.numel(), n_cells, n_seq_max,
+                                  ctypes.byref(self._h)), "ppx_kvu_init")
+
+    @property
+    def handle(self):
+        return self._h
+
+    def n_pos(self, seq_id: int) -> int:
+        return lib().ppx_kvu_n_pos(self._h, seq_id)
+
+    def free_cells(self) -> int:
+        return lib().ppx_kvu_free_cells(self._h)
+
+    def seq_rm(self, seq_id: int):
+        _check(lib().ppx_kvu_seq_rm(self._h, seq_id), "ppx_kvu_seq_rm")
+
+    def cells(self, seq_id: int):
+        """int32 [n_pos]: the cell of each position of the sequence."""
+        n = self.n_pos(seq_id)
+        out = np.zeros(max(n, 1), np.int32)
+        _check(lib().ppx_kvu_cells(self._h, seq_id, out.ctypes.data, n), "ppx_kvu_cells")
+        return out[:n]
+
+    def kv_tensors(self):
+        """(K, V) as torch fp16 views [Ls][n_cells][kv_dim] (V is a transposed
+        view of the [Ls][kv_dim][n_cells] layout)."""
+        import torch
+        I = self.model.info
+        ls, kvd = I["n_layer_kv_from_start"], I["kv_dim"]
+        n = ls * self.n_cells * kvd
+        kbytes = (2 * n + 255) // 256 * 256
+        K = self.buf[:2 * n].view(torch.float16).view(ls, self.n_cells, kvd)
+        VT = self.buf[kbytes:kbytes + 2 * n].view(torch.float16).view(ls, kvd, self.n_cells)
+        return K, VT.transpose(1, 2)
+
+    def seq_kv(self, seq_id: int):
+        """(K, V) of one sequence in position order, torch fp16 [Ls][n_pos][kv_dim]."""
+        import torch
+        K, V = self.kv_tensors()
+        idx = torch.from_numpy(self.cells(seq_id).astype(np.int64)).to(K.device)
+        return K[:, idx], V[:, idx]
+
+    def close(self):
+        if self._h:
+            lib().ppx_kvu_free(self._h)
             self._h = c_void_p()
 
     def __del__(self):

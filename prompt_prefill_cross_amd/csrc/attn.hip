@@ -25,6 +25,7 @@ namespace ppx {
 namespace {
 
 constexpr int KT = 32;  // keys per pipeline stage
+static_assert(kKvPage % KT == 0, "a stage's keys lie in one page of a unified cache");
 
 typedef __attribute__((address_space(3))) void lds_t;
 
@@ -86,6 +87,7 @@ __global__ __launch_bounds__(C::NT) void k_attn_prefill(const AttnGroup grp) {
     // positions pos0 .. pos0 + M - 1, read against that sequence's cache
     int cb = blockIdx.x, M = a.M, pos0 = a.pos0, row0 = 0, vld = a.vld;
     const __half *kp = a.k, *vtp = a.vt;
+    const int32_t *page = nullptr;  // unified cache: the sequence's page table
     if (a.wg) {
         const AttnWg &d = a.wg[blockIdx.x];
         cb = d.cb;
@@ -96,6 +98,7 @@ __global__ __launch_bounds__(C::NT) void k_attn_prefill(const AttnGroup grp) {
         kp = ref.k;
         vtp = ref.vt;
         vld = ref.vld;
+        page = ref.page;
     } else if (cb * C::CB >= M * G) {
         return;  // past this unit's query columns (the whole workgroup)
     }
@@ -132,15 +135,19 @@ __global__ __launch_bounds__(C::NT) void k_attn_prefill(const AttnGroup grp) {
         auto issue = [&](int sb) {
             h8 *st = ring + (sb % C::DEPTH) * C::STAGE_UNITS;
             const int t0 = kbeg + min(sb, nst - 1) * KT;  // past the end: repeats keep the count uniform
+            // the stage's keys t0 .. t0 + KT - 1 (and the clamp target plast >= t0)
+            // lie in one page: cells c0 + (key - t0)
+            const int c0 = kv_cell(page, t0);
 #pragma unroll
             for (int t = 0; t < C::PER; ++t) {
                 const int e = entry(t);
                 if (e < 2 * KB) {
                     const int kb = e >> 1;
                     const int key = min(t0 + koff[t], plast);
-                    adma16(kp + ((size_t)key * a.KVH + kvh) * HD + kb * 32 + 8 * (lane >> 4), st + e * 64);
+                    adma16(kp + ((size_t)(c0 + key - t0) * a.KVH + kvh) * HD + kb * 32 + 8 * (lane >> 4),
+                           st + e * 64);
                 } else {
-                    adma16(vtp + (size_t)koff[t] + t0, st + C::K_UNITS + (e - 2 * KB) * 64);
+                    adma16(vtp + (size_t)koff[t] + c0, st + C::K_UNITS + (e - 2 * KB) * 64);
                 }
             }
         };
@@ -378,6 +385,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_merge(const AttnGroup grp)
 // Each chunk writes per head its max, exp-sum and unnormalised output;
 // k_attn_merge combines the chunks in chunk order.
 constexpr int CH = 32;
+static_assert(kKvPage % CH == 0, "a chunk's keys lie in one page of a unified cache");
 
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn_1row(Attn1Args a) {
@@ -536,12 +544,14 @@ __global__ __launch_bounds__(256) void k_attn_rows_exact(AttnArgs a) {
     const int G = a.H / a.KVH;
     const int pos = a.row_pos ? a.row_pos[r] : a.pos0 + r;
     const __half *kp = a.k, *vtp = a.vt;
+    const int32_t *page = nullptr;
     int vld = a.vld;
     if (a.seq_kv) {
         const KVRef &ref = a.seq_kv[a.row_seq[r]];
         kp = ref.k;
         vtp = ref.vt;
         vld = ref.vld;
+        page = ref.page;
     }
     const int c = lane & 15, g = c & 7, lg = lane >> 4;
     const bool lo = c >= 8;
@@ -570,10 +580,11 @@ __global__ __launch_bounds__(256) void k_attn_rows_exact(AttnArgs a) {
     const int nch = (pos + CH) / CH;
     for (int ch = 0; ch < nch; ++ch) {
         const int k0 = ch * CH, nk = min(CH, pos + 1 - k0);
+        const int c0 = kv_cell(page, k0);  // the chunk's keys lie in one page: cells c0 ..
         if (wave < CH / 16) {
             const int kt = wave * 16 + c;
-            const int kr = k0 + min(kt, nk - 1);  // masked keys re-read a valid row
-            const __half *krow = kp + ((size_t)kr * a.KVH + kvh) * HD + lg * 8;
+            const int kr = min(kt, nk - 1);  // masked keys re-read a valid row
+            const __half *krow = kp + ((size_t)(c0 + kr) * a.KVH + kvh) * HD + lg * 8;
             f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < HD / 32; ++ks)
@@ -613,7 +624,7 @@ __global__ __launch_bounds__(256) void k_attn_rows_exact(AttnArgs a) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int d = (wave + 4 * j) * 16 + c;
-            h8 av = *reinterpret_cast<const h8 *>(vtp + ((size_t)kvh * HD + d) * vld + k0 + lg * 8);
+            h8 av = *reinterpret_cast<const h8 *>(vtp + ((size_t)kvh * HD + d) * vld + c0 + lg * 8);
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 if (lg * 8 + e >= nk) av[e] = (_Float16)0.0f;

@@ -939,12 +939,13 @@ struct MultiLayout {
     size_t kv;                  // KVRef [Ls][k]
     size_t wg;                  // AttnWg [max_wg]: every ubatch's workgroups, then the tail's
     size_t pairs;               // int2 [k]: (row in its ubatch, sequence) of each output row
+    size_t pages;               // int32 [k][npg]: each sequence's page table (unified cache)
     size_t blob_bytes;
     size_t max_wg;
     size_t total;
 };
 
-MultiLayout multi_layout(const ppx_model *m, int ub, int k, long T, int n_ctx_max) {
+MultiLayout multi_layout(const ppx_model *m, int ub, int k, long T, int n_ctx_max, int npg = 0) {
     const ppx_model_info &I = m->info;
     MultiLayout L{};
     L.w = ws_layout(m, std::max(ub, k), n_ctx_max, 1);
@@ -972,9 +973,24 @@ MultiLayout multi_layout(const ppx_model *m, int ub, int k, long T, int n_ctx_ma
     L.kv = take(sizeof(KVRef) * (size_t)std::max(I.n_layer_kv_from_start, 1) * k);
     L.wg = take(sizeof(AttnWg) * L.max_wg);
     L.pairs = take(sizeof(int2) * (size_t)k);
+    L.pages = take(4ull * k * npg);
     L.blob_bytes = b;
     L.total = L.blob + b;
     return L;
+}
+
+// The prune of a multi-sequence pass: one output row per sequence, so the
+// single-sequence predicate holds per sequence.
+int multi_prune(const ppx_model *m, const ppx_prefill_params *p, bool *prune) {
+    const ppx_model_info &I = m->info;
+    const int can = predicate(I.n_layer, I.n_layer_kv_from_start, p->embeddings, 1, nullptr, 1);
+    if (p->prune == PPX_PRUNE_AUTO) *prune = can;
+    else if (p->prune == PPX_PRUNE_OFF) *prune = false;
+    else if (p->prune == PPX_PRUNE_ON) {
+        if (!can) return PPX_E_UNSUPPORTED;
+        *prune = true;
+    } else return PPX_E_INVAL;
+    return PPX_OK;
 }
 
 // Pinned staging for the tables: the previous copy out of it must be done
@@ -994,60 +1010,35 @@ int stage_tables(ppx_model *m, size_t bytes, uint8_t **out) {
     return PPX_OK;
 }
 
-// Several prompts, each in its own cache, in one pass.  Their rows are laid
-// end to end and cut into ubatches of n_ubatch rows; a ubatch row carries its
-// own position and sequence, so the K|V projection writes each row into its
-// own cache and attention reads each row's own cache.  Pruning generalises
-// the single-sequence rule to one output row per sequence: the ubatch that
-// holds a prompt's last row gathers it after the owning layers, and the k
-// gathered rows alone run the KV-shared layers (each against its own
-// sequence's source-layer cache) and the head.  Without pruning they are
-// gathered after the last layer.  logits: fp32 [k][n_vocab].
-int prefill_multi(ppx_model *m, const ppx_seq *seqs, int k, const ppx_prefill_params *p, void *ws, size_t ws_bytes,
-                  float *logits, hipStream_t s) {
-    if (!m || !seqs || !p || !logits || !ws) return PPX_E_INVAL;
-    if (k < 1 || k > PPX_MAX_SEQ) return PPX_E_INVAL;
-    const ppx_model_info &I = m->info;
-    if (p->embeddings != 0 || p->embeddings_layer_inp) return PPX_E_UNSUPPORTED;
-    if (p->debug_rows || p->debug_hidden || p->nextn_logits) return PPX_E_UNSUPPORTED;
-    if (p->n_seq_max < k) return PPX_E_INVAL;
-    if (p->n_ubatch < 1 || p->n_ubatch > PPX_MAX_UBATCH) return PPX_E_INVAL;
-    if (p->precision != PPX_PRECISION_FAST && p->precision != PPX_PRECISION_EXACT) return PPX_E_INVAL;
-    long T = 0;
-    int nctx_max = 1;
-    for (int q = 0; q < k; ++q) {
-        const ppx_seq &sq = seqs[q];
-        if (!sq.kv || sq.kv->m != m) return PPX_E_INVAL;
-        for (int r = 0; r < q; ++r)
-            if (seqs[r].kv == sq.kv) return PPX_E_INVAL;  // each sequence needs its own cache
-        if (sq.n_tokens <= 0) return PPX_E_EMPTY;
-        if (!sq.tokens_host) return PPX_E_INVAL;
-        for (int i = 0; i < sq.n_tokens; ++i)
-            if (sq.tokens_host[i] < 0 || sq.tokens_host[i] >= I.n_vocab) return PPX_E_TOKEN;
-        if ((long)sq.kv->n_pos + sq.n_tokens > sq.kv->n_ctx) return PPX_E_CTX;
-        T += sq.n_tokens;
-        nctx_max = std::max(nctx_max, sq.kv->n_ctx);
-    }
-    if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return PPX_E_INVAL;
-    if (k == 1) {
-        // one sequence: exactly the single-sequence prefill
-        ppx_prefill_params q1 = *p;
-        q1.n_seq_max = 1;
-        return prefill(m, seqs[0].kv, seqs[0].tokens_host, seqs[0].n_tokens, &q1, ws, ws_bytes, logits, s);
-    }
-    const int L = I.n_layer, Ls = I.n_layer_kv_from_start, d = I.d_model, kvd = I.kv_dim;
-    // one output row per sequence: the single-sequence predicate holds per sequence
-    const int can = predicate(L, Ls, p->embeddings, 1, nullptr, 1);
-    bool prune;
-    if (p->prune == PPX_PRUNE_AUTO) prune = can;
-    else if (p->prune == PPX_PRUNE_OFF) prune = false;
-    else if (p->prune == PPX_PRUNE_ON) {
-        if (!can) return PPX_E_UNSUPPORTED;
-        prune = true;
-    } else return PPX_E_INVAL;
+// One prompt of a multi-sequence pass: its tokens and first position, and
+// where its cache lives -- split: its own ppx_kv; unified: its page table in
+// the one buffer, covering every position the pass writes.
+struct SeqRun {
+    const int32_t *tok = nullptr;
+    int n = 0, n_pos = 0;
+    const ppx_kv *kv = nullptr;
+    const std::vector<int32_t> *pages = nullptr;
+};
 
+// Several prompts in one pass (the arguments are already checked).  Their
+// rows are laid end to end and cut into ubatches of n_ubatch rows; a ubatch
+// row carries its own position and sequence, so the K|V projection writes
+// each row into its own sequence's cache (or cells) and attention reads only
+// that sequence's keys.  Pruning generalises the single-sequence rule to one
+// output row per sequence: the ubatch that holds a prompt's last row gathers
+// it after the owning layers, and the k gathered rows alone run the
+// KV-shared layers (each against its own sequence's source-layer cache) and
+// the head.  Without pruning they are gathered after the last layer.
+// logits: fp32 [k][n_vocab].  u: the unified cache, or null (split caches).
+int multi_pass(ppx_model *m, const SeqRun *sq, int k, const ppx_kvu *u, int nctx_max, bool prune,
+               const ppx_prefill_params *p, void *ws, size_t ws_bytes, float *logits, hipStream_t s) {
+    const ppx_model_info &I = m->info;
+    const int L = I.n_layer, Ls = I.n_layer_kv_from_start, d = I.d_model, kvd = I.kv_dim;
+    long T = 0;
+    for (int q = 0; q < k; ++q) T += sq[q].n;
+    const int npg = u ? u->n_cells / kKvPage : 0;
     const int ub = p->n_ubatch;
-    const MultiLayout ML = multi_layout(m, ub, k, T, nctx_max);
+    const MultiLayout ML = multi_layout(m, ub, k, T, nctx_max, npg);
     if (ws_bytes < ML.total) return PPX_E_NOMEM;
     const int G = I.n_head / I.n_kv_head;
     const int cbw = attn_prefill_cols_per_wg(I.head_dim);
@@ -1063,26 +1054,42 @@ int prefill_multi(ppx_model *m, const ppx_seq *seqs, int k, const ppx_prefill_pa
     {
         long r = 0;
         for (int q = 0; q < k; ++q) {
-            const ppx_seq &sq = seqs[q];
-            for (int i = 0; i < sq.n_tokens; ++i, ++r) {
-                tok[r] = sq.tokens_host[i];
-                pos[r] = sq.kv->n_pos + i;
+            const SeqRun &sr = sq[q];
+            for (int i = 0; i < sr.n; ++i, ++r) {
+                tok[r] = sr.tok[i];
+                pos[r] = sr.n_pos + i;
                 seq[r] = q;
             }
             last[q] = r - 1;
-            ttok[q] = sq.tokens_host[sq.n_tokens - 1];
-            tpos[q] = sq.kv->n_pos + sq.n_tokens - 1;
+            ttok[q] = sr.tok[sr.n - 1];
+            tpos[q] = sr.n_pos + sr.n - 1;
             tseq[q] = q;
         }
+    }
+    uint8_t *wsb = static_cast<uint8_t *>(ws);
+    uint8_t *dblob = wsb + ML.blob;
+    int32_t *pgt = H32(ML.pages);
+    for (int q = 0; q < k && u; ++q) {
+        const std::vector<int32_t> &pv = *sq[q].pages;
+        std::copy(pv.begin(), pv.end(), pgt + (size_t)q * npg);
+        std::fill(pgt + (size_t)q * npg + pv.size(), pgt + (size_t)(q + 1) * npg, 0);
     }
     KVRef *kvt = reinterpret_cast<KVRef *>(hb + ML.kv);
     for (int l = 0; l < Ls; ++l)
         for (int q = 0; q < k; ++q) {
-            const ppx_kv *kv = seqs[q].kv;
             KVRef &ref = kvt[(size_t)l * k + q];
-            ref.k = kv->k + (size_t)l * kv->n_ctx * kvd;
-            ref.vt = kv->vt + (size_t)l * kv->vld * kvd;
-            ref.vld = kv->vld;
+            if (u) {
+                ref.k = u->k + (size_t)l * u->n_cells * kvd;
+                ref.vt = u->vt + (size_t)l * kvd * u->n_cells;
+                ref.vld = u->n_cells;
+                ref.page = reinterpret_cast<const int32_t *>(dblob + ML.pages) + (size_t)q * npg;
+            } else {
+                const ppx_kv *kv = sq[q].kv;
+                ref.k = kv->k + (size_t)l * kv->n_ctx * kvd;
+                ref.vt = kv->vt + (size_t)l * kv->vld * kvd;
+                ref.vld = kv->vld;
+                ref.page = nullptr;
+            }
             ref.pad = 0;
         }
     AttnWg *wgt = reinterpret_cast<AttnWg *>(hb + ML.wg);
@@ -1151,8 +1158,6 @@ int prefill_multi(ppx_model *m, const ppx_seq *seqs, int k, const ppx_prefill_pa
     }
     if (over || np != k) return PPX_E_INVAL;  // cannot happen: the layout's bounds hold for any lengths
 
-    uint8_t *wsb = static_cast<uint8_t *>(ws);
-    uint8_t *dblob = wsb + ML.blob;
     if (hipMemcpyAsync(dblob, hb, ML.blob_bytes, hipMemcpyHostToDevice, s) != hipSuccess) return PPX_E_HIP;
     if (hipEventRecord(m->stage_event, s) != hipSuccess) return PPX_E_HIP;
     auto D32 = [&](size_t off) { return reinterpret_cast<const int32_t *>(dblob + off); };
@@ -1168,8 +1173,8 @@ int prefill_multi(ppx_model *m, const ppx_seq *seqs, int k, const ppx_prefill_pa
         c.tm = p->timing;
     }
     if (log_enabled())
-        std::fprintf(stderr, "[ppx] prefill of %d sequences, %ld rows, ubatch %d, prune %s\n", k, T, ub,
-                     prune ? "on" : "off");
+        std::fprintf(stderr, "[ppx] prefill of %d sequences, %ld rows, ubatch %d, prune %s, %s cache\n", k, T,
+                     ub, prune ? "on" : "off", u ? "unified" : "split");
     // the launches (tables and tokens are already in device memory, so a
     // recorded sequence serves any prompts of the same shape)
     auto enqueue = [&](Ctx &c) -> int {
@@ -1240,7 +1245,7 @@ int prefill_multi(ppx_model *m, const ppx_seq *seqs, int k, const ppx_prefill_pa
     if (!c.tm && graphs_enabled()) {
         std::vector<long long> key = {(long long)(uintptr_t)wsb, (long long)(uintptr_t)logits, T, ub, k, prune,
                                       nctx_max, (long long)ubs.size(), tail.nwg, tail.split.kc, tail.split.nkc,
-                                      c.exact};
+                                      c.exact, npg};
         for (const Ub &U : ubs) {
             const long long v[] = {U.M, (long long)U.wg0, U.nwg, U.split.kc, U.split.nkc, U.pair0, U.npairs};
             key.insert(key.end(), v, v + 7);
@@ -1251,7 +1256,99 @@ int prefill_multi(ppx_model *m, const ppx_seq *seqs, int k, const ppx_prefill_pa
     }
     if (c.tm) c.tm->gemm_flop += 2.0 * k * (double)m->out.N * m->out.K;
     PPX_TRY(c.finish());
+    return PPX_OK;
+}
+
+int prefill_multi(ppx_model *m, const ppx_seq *seqs, int k, const ppx_prefill_params *p, void *ws, size_t ws_bytes,
+                  float *logits, hipStream_t s) {
+    if (!m || !seqs || !p || !logits || !ws) return PPX_E_INVAL;
+    if (k < 1 || k > PPX_MAX_SEQ) return PPX_E_INVAL;
+    const ppx_model_info &I = m->info;
+    if (p->embeddings != 0 || p->embeddings_layer_inp) return PPX_E_UNSUPPORTED;
+    if (p->debug_rows || p->debug_hidden || p->nextn_logits) return PPX_E_UNSUPPORTED;
+    if (p->n_seq_max < k) return PPX_E_INVAL;
+    if (p->n_ubatch < 1 || p->n_ubatch > PPX_MAX_UBATCH) return PPX_E_INVAL;
+    if (p->precision != PPX_PRECISION_FAST && p->precision != PPX_PRECISION_EXACT) return PPX_E_INVAL;
+    int nctx_max = 1;
+    for (int q = 0; q < k; ++q) {
+        const ppx_seq &sq = seqs[q];
+        if (!sq.kv || sq.kv->m != m) return PPX_E_INVAL;
+        for (int r = 0; r < q; ++r)
+            if (seqs[r].kv == sq.kv) return PPX_E_INVAL;  // each sequence needs its own cache
+        if (sq.n_tokens <= 0) return PPX_E_EMPTY;
+        if (!sq.tokens_host) return PPX_E_INVAL;
+        for (int i = 0; i < sq.n_tokens; ++i)
+            if (sq.tokens_host[i] < 0 || sq.tokens_host[i] >= I.n_vocab) return PPX_E_TOKEN;
+        if ((long)sq.kv->n_pos + sq.n_tokens > sq.kv->n_ctx) return PPX_E_CTX;
+        nctx_max = std::max(nctx_max, sq.kv->n_ctx);
+    }
+    if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return PPX_E_INVAL;
+    if (k == 1) {
+        // one sequence: exactly the single-sequence prefill
+        ppx_prefill_params q1 = *p;
+        q1.n_seq_max = 1;
+        return prefill(m, seqs[0].kv, seqs[0].tokens_host, seqs[0].n_tokens, &q1, ws, ws_bytes, logits, s);
+    }
+    bool prune;
+    PPX_TRY(multi_prune(m, p, &prune));
+    std::vector<SeqRun> sr(k);
+    for (int q = 0; q < k; ++q) sr[q] = SeqRun{seqs[q].tokens_host, seqs[q].n_tokens, seqs[q].kv->n_pos, seqs[q].kv};
+    PPX_TRY(multi_pass(m, sr.data(), k, nullptr, nctx_max, prune, p, ws, ws_bytes, logits, s));
     for (int q = 0; q < k; ++q) seqs[q].kv->n_pos += seqs[q].n_tokens;
+    return PPX_OK;
+}
+
+// Several prompts over one unified cache: each takes the pages its new
+// positions need (lowest free first); they are committed to the sequence
+// only once the pass has been queued.
+int prefill_unified(ppx_model *m, ppx_kvu *u, const ppx_useq *seqs, int k, const ppx_prefill_params *p, void *ws,
+                    size_t ws_bytes, float *logits, hipStream_t s) {
+    if (!m || !u || !seqs || !p || !logits || !ws) return PPX_E_INVAL;
+    if (u->m != m || k < 1 || k > PPX_MAX_SEQ) return PPX_E_INVAL;
+    const ppx_model_info &I = m->info;
+    if (p->embeddings != 0 || p->embeddings_layer_inp) return PPX_E_UNSUPPORTED;
+    if (p->debug_rows || p->debug_hidden || p->nextn_logits) return PPX_E_UNSUPPORTED;
+    if (p->n_seq_max < k) return PPX_E_INVAL;
+    if (p->n_ubatch < 1 || p->n_ubatch > PPX_MAX_UBATCH) return PPX_E_INVAL;
+    if (p->precision != PPX_PRECISION_FAST && p->precision != PPX_PRECISION_EXACT) return PPX_E_INVAL;
+    long need = 0;
+    for (int q = 0; q < k; ++q) {
+        const ppx_useq &sq = seqs[q];
+        if (sq.seq_id < 0 || sq.seq_id >= u->n_seq_max) return PPX_E_INVAL;
+        for (int r = 0; r < q; ++r)
+            if (seqs[r].seq_id == sq.seq_id) return PPX_E_INVAL;  // one prompt per sequence
+        if (sq.n_tokens <= 0) return PPX_E_EMPTY;
+        if (!sq.tokens_host) return PPX_E_INVAL;
+        for (int i = 0; i < sq.n_tokens; ++i)
+            if (sq.tokens_host[i] < 0 || sq.tokens_host[i] >= I.n_vocab) return PPX_E_TOKEN;
+        const long end = (long)u->n_pos[sq.seq_id] + sq.n_tokens;
+        if (end > u->n_cells) return PPX_E_CTX;
+        need += (end + kKvPage - 1) / kKvPage - (long)u->pages[sq.seq_id].size();
+    }
+    if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return PPX_E_INVAL;
+    std::vector<int32_t> freep;
+    for (int pg = 0; pg < (int)u->page_seq.size() && (long)freep.size() < need; ++pg)
+        if (u->page_seq[pg] < 0) freep.push_back(pg);
+    if ((long)freep.size() < need) return PPX_E_CTX;
+    bool prune;
+    PPX_TRY(multi_prune(m, p, &prune));
+    std::vector<std::vector<int32_t>> pv(k);
+    std::vector<SeqRun> sr(k);
+    size_t f = 0;
+    for (int q = 0; q < k; ++q) {
+        const ppx_useq &sq = seqs[q];
+        pv[q] = u->pages[sq.seq_id];
+        const int np = (u->n_pos[sq.seq_id] + sq.n_tokens + kKvPage - 1) / kKvPage;
+        while ((int)pv[q].size() < np) pv[q].push_back(freep[f++]);
+        sr[q] = SeqRun{sq.tokens_host, sq.n_tokens, u->n_pos[sq.seq_id], nullptr, &pv[q]};
+    }
+    PPX_TRY(multi_pass(m, sr.data(), k, u, u->n_cells, prune, p, ws, ws_bytes, logits, s));
+    for (int q = 0; q < k; ++q) {
+        const int sid = seqs[q].seq_id;
+        for (size_t i = u->pages[sid].size(); i < pv[q].size(); ++i) u->page_seq[pv[q][i]] = sid;
+        u->pages[sid] = std::move(pv[q]);
+        u->n_pos[sid] += seqs[q].n_tokens;
+    }
     return PPX_OK;
 }
 
@@ -1572,6 +1669,76 @@ size_t ppx_workspace_bytes_multi(const ppx_model *m, int n_ubatch, int n_seq, lo
 int ppx_prefill_multi(ppx_model *m, const ppx_seq *seqs, int n_seq, const ppx_prefill_params *p, void *ws_dev,
                       size_t ws_bytes, float *logits_dev, void *hip_stream) {
     return prefill_multi(m, seqs, n_seq, p, ws_dev, ws_bytes, logits_dev, (hipStream_t)hip_stream);
+}
+
+size_t ppx_kvu_bytes(const ppx_model *m, int n_cells) {
+    if (!m || n_cells <= 0 || n_cells % kKvPage) return 0;
+    const size_t ls = m->info.n_layer_kv_from_start, kvd = m->info.kv_dim;
+    const size_t kbytes = (ls * (size_t)n_cells * kvd * 2 + 255) / 256 * 256;
+    return kbytes + ls * kvd * (size_t)n_cells * 2;
+}
+
+int ppx_kvu_init(ppx_model *m, void *kv_dev, size_t bytes, int n_cells, int n_seq_max, ppx_kvu **out) {
+    if (!m || !out) return PPX_E_INVAL;
+    *out = nullptr;
+    if (n_cells <= 0 || n_cells % kKvPage || n_seq_max < 1 || n_seq_max > 65536) return PPX_E_INVAL;
+    const size_t need = ppx_kvu_bytes(m, n_cells);
+    if (need && !kv_dev) return PPX_E_INVAL;
+    if (bytes < need) return PPX_E_NOMEM;
+    if ((reinterpret_cast<uintptr_t>(kv_dev) & 255) != 0) return PPX_E_INVAL;
+    PPX_TRY(ensure_rope(m, n_cells));
+    if (need && hipMemset(kv_dev, 0, need) != hipSuccess) return PPX_E_HIP;
+    ppx_kvu *u = new ppx_kvu();
+    u->m = m;
+    const size_t kbytes = ((size_t)m->info.n_layer_kv_from_start * n_cells * m->info.kv_dim * 2 + 255) / 256 * 256;
+    u->k = static_cast<__half *>(kv_dev);
+    u->vt = reinterpret_cast<__half *>(static_cast<uint8_t *>(kv_dev) + kbytes);
+    u->n_cells = n_cells;
+    u->n_seq_max = n_seq_max;
+    u->page_seq.assign(n_cells / kKvPage, -1);
+    u->pages.resize(n_seq_max);
+    u->n_pos.assign(n_seq_max, 0);
+    *out = u;
+    return PPX_OK;
+}
+
+void ppx_kvu_free(ppx_kvu *u) { delete u; }
+
+int ppx_kvu_n_pos(const ppx_kvu *u, int seq_id) {
+    if (!u || seq_id < 0 || seq_id >= u->n_seq_max) return PPX_E_INVAL;
+    return u->n_pos[seq_id];
+}
+
+int ppx_kvu_free_cells(const ppx_kvu *u) {
+    if (!u) return PPX_E_INVAL;
+    return (int)std::count(u->page_seq.begin(), u->page_seq.end(), -1) * kKvPage;
+}
+
+int ppx_kvu_seq_rm(ppx_kvu *u, int seq_id) {
+    if (!u || seq_id < 0 || seq_id >= u->n_seq_max) return PPX_E_INVAL;
+    for (int32_t pg : u->pages[seq_id]) u->page_seq[pg] = -1;
+    u->pages[seq_id].clear();
+    u->n_pos[seq_id] = 0;
+    return PPX_OK;
+}
+
+int ppx_kvu_cells(const ppx_kvu *u, int seq_id, int32_t *cells_host, int n) {
+    if (!u || seq_id < 0 || seq_id >= u->n_seq_max || n < 0 || n > u->n_pos[seq_id] || (n && !cells_host))
+        return PPX_E_INVAL;
+    for (int p = 0; p < n; ++p) cells_host[p] = kv_cell(u->pages[seq_id].data(), p);
+    return PPX_OK;
+}
+
+size_t ppx_workspace_bytes_unified(const ppx_model *m, int n_ubatch, int n_seq, long n_tokens_total, int n_cells) {
+    if (!m || n_ubatch < 1 || n_seq < 1 || n_seq > PPX_MAX_SEQ || n_tokens_total < 1 || n_cells < kKvPage ||
+        n_cells % kKvPage)
+        return 0;
+    return multi_layout(m, n_ubatch, n_seq, n_tokens_total, n_cells, n_cells / kKvPage).total;
+}
+
+int ppx_prefill_unified(ppx_model *m, ppx_kvu *u, const ppx_useq *seqs, int n_seq, const ppx_prefill_params *p,
+                        void *ws_dev, size_t ws_bytes, float *logits_dev, void *hip_stream) {
+    return prefill_unified(m, u, seqs, n_seq, p, ws_dev, ws_bytes, logits_dev, (hipStream_t)hip_stream);
 }
 
 int ppx_decode(ppx_model *m, ppx_kv *kv, int32_t token, void *ws_dev, size_t ws_bytes, float *logits_dev,

@@ -216,22 +216,29 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, const f4 (&acc)
                             q[ii] = __float2half(ra);
                             q[ii + half] = __float2half(rb);
                         } else {
-                            __half *kc = a.seq_kv ? a.seq_kv[a.row_seq[row]].k : a.kc;
-                            __half *k = kc + (size_t)pos * a.kvd + h * hd;
+                            __half *kc = a.kc;
+                            int cell = pos;
+                            if (a.seq_kv) {
+                                const KVRef &ref = a.seq_kv[a.row_seq[row]];
+                                kc = ref.k;
+                                cell = kv_cell(ref.page, pos);
+                            }
+                            __half *k = kc + (size_t)cell * a.kvd + h * hd;
                             k[ii] = __float2half(ra);
                             k[ii + half] = __float2half(rb);
                         }
                     } else {
                         const int c = colA - a.qd - a.kvd;
                         __half *vc = a.vc;
-                        int vld = a.vld;
+                        int vld = a.vld, cell = pos;
                         if (a.seq_kv) {
                             const KVRef &ref = a.seq_kv[a.row_seq[row]];
                             vc = ref.vt;
                             vld = ref.vld;
+                            cell = kv_cell(ref.page, pos);
                         }
-                        vc[(size_t)c * vld + pos] = __float2half(va);  // V^T
-                        vc[(size_t)(c + 16) * vld + pos] = __float2half(vb);
+                        vc[(size_t)c * vld + cell] = __float2half(va);  // V^T
+                        vc[(size_t)(c + 16) * vld + cell] = __float2half(vb);
                     }
                 }
         }

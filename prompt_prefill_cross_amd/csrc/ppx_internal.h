@@ -98,6 +98,19 @@ struct ppx_model {
     hipEvent_t stage_event = nullptr;
 };
 
+// A unified cache: one buffer for every sequence.  Cells are handed out in
+// pages of kKvPage consecutive positions of one sequence; page_seq holds each
+// page's sequence (-1: free), pages[s] sequence s's pages in position order.
+struct ppx_kvu {
+    const ppx_model *m = nullptr;
+    __half *k = nullptr;   // [Ls][n_cells][kv_dim]
+    __half *vt = nullptr;  // [Ls][kv_dim][n_cells]: V transposed, as in ppx_kv
+    int n_cells = 0, n_seq_max = 0;
+    std::vector<int32_t> page_seq;
+    std::vector<std::vector<int32_t>> pages;
+    std::vector<int> n_pos;
+};
+
 struct ppx_kv {
     const ppx_model *m = nullptr;
     __half *k = nullptr;   // [Ls][n_ctx][kv_dim]
@@ -121,13 +134,23 @@ enum GemmEpi {
 };
 
 // One sequence's cache of one layer, for row batches that span several
-// sequences (each with its own cache).
+// sequences.  Split caches: the sequence's own buffer, position p in row p.
+// Unified cache: the one buffer of all sequences, position p in cell
+// page[p / kKvPage] * kKvPage + p % kKvPage (kv_cell).
 struct KVRef {
-    __half *k = nullptr;   // [n_ctx][kv_dim]
-    __half *vt = nullptr;  // [kv_dim][vld]
+    __half *k = nullptr;           // [n_ctx][kv_dim]  (unified: [n_cells][kv_dim])
+    __half *vt = nullptr;          // [kv_dim][vld]    (unified: vld = n_cells)
+    const int32_t *page = nullptr; // null: split; else the sequence's page table
     int vld = 0;
     int pad = 0;
 };
+
+// Cells per page of a unified cache: a page holds consecutive positions of
+// one sequence, so every 32-key stage of the attention kernels lies in one page.
+constexpr int kKvPage = 64;
+__host__ __device__ inline int kv_cell(const int32_t *page, int p) {
+    return page ? page[p / kKvPage] * kKvPage + p % kKvPage : p;
+}
 
 struct GemmArgs {
     const __half *A = nullptr;  // [M][K] fp16, fragment-tiled (the high part on the exact-weight path)
