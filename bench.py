@@ -48,6 +48,8 @@ def parse():
                     help="skip the token-verified prefix-reuse timing")
     ap.add_argument("--multi", default="16x128,8x256,4x512",
                     help="multi-sequence prefills to report, KxN = K prompts of N tokens ('' = none)")
+    ap.add_argument("--server-n", type=int, default=13789,
+                    help="one-prompt server case: unified cache, one sequence vs four slots (0 = skip)")
     ap.add_argument("--table", action="store_true",
                     help="time every config's full shapes, pruned and unpruned (builds 3 more models)")
     ap.add_argument("--no-matrix", dest="matrix", action="store_false",
@@ -224,9 +226,10 @@ def prefix_reuse_pass(mm, kv, toks, ub, keep, reps=3):
 
 
 def multi_pass(ppx, mm, cfg, ub, shapes, reps=5):
-    """k prompts of n tokens in one ppx_prefill_multi call against the same k
-    prompts run one ppx_prefill after another (same stream, one timed region
-    each way)."""
+    """k prompts of n tokens in one ppx_prefill_multi call (one cache per
+    sequence: split), in one ppx_prefill_unified call (one buffer for all
+    sequences), and run one ppx_prefill after another (same stream, one timed
+    region each way)."""
     import torch
     import synth
     V = mm.info["n_vocab"]
@@ -235,6 +238,7 @@ def multi_pass(ppx, mm, cfg, ub, shapes, reps=5):
         base = synth.prompt(cfg, k * n)
         prompts = [base[i * n:(i + 1) * n] for i in range(k)]
         kvs = [ppx.KVCache(mm, n) for _ in range(k)]
+        ucache = ppx.UnifiedCache(mm, k * ((n + 63) // 64 * 64), k)
         lg_multi = torch.empty((k, V), dtype=torch.float32, device="cuda")
         lg_one = torch.empty(V, dtype=torch.float32, device="cuda")
 
@@ -243,13 +247,18 @@ def multi_pass(ppx, mm, cfg, ub, shapes, reps=5):
                 kv.clear()
             mm.prefill_multi(prompts, kvs, n_ubatch=ub, logits=lg_multi)
 
+        def run_unified():
+            for sid in range(k):
+                ucache.seq_rm(sid)
+            mm.prefill_unified(prompts, list(range(k)), ucache, n_ubatch=ub, logits=lg_multi)
+
         def run_single():
             for kv, t in zip(kvs, prompts):
                 kv.clear()
                 mm.prefill(t, kv, n_ubatch=ub, logits=lg_one)
 
         res = {}
-        for name, fn in (("multi", run_multi), ("one_by_one", run_single)):
+        for name, fn in (("multi", run_multi), ("unified", run_unified), ("one_by_one", run_single)):
             fn()
             torch.cuda.synchronize()
             ts = []
@@ -263,11 +272,62 @@ def multi_pass(ppx, mm, cfg, ub, shapes, reps=5):
                 ts.append(e0.elapsed_time(e1))
             res[name] = float(np.median(ts))
         out[f"{k}x{n}"] = {"sequences": k, "tokens_each": n, "multi_ms": res["multi"],
-                           "one_by_one_ms": res["one_by_one"],
+                           "unified_ms": res["unified"], "one_by_one_ms": res["one_by_one"],
                            "multi_tokens_per_s": k * n / res["multi"] * 1e3,
+                           "unified_tokens_per_s": k * n / res["unified"] * 1e3,
                            "one_by_one_tokens_per_s": k * n / res["one_by_one"] * 1e3}
-        del kvs
+        del kvs, ucache
     return out
+
+
+def server_pass(ppx, mm, cfg, ub, n, reps=3):
+    """The server case of the llama.cpp Gemma 4 prefill page (section 5): one
+    long prompt (13,789 tokens there) into a unified cache as the only
+    sequence, where the predicate prunes, against the same prompt with
+    several sequence slots configured (n_seq_max 4), where the predicate's
+    single-sequence clause keeps every row through every layer; and the same
+    prompt through ppx_prefill into a cache of its own."""
+    import torch
+    import synth
+    toks = synth.prompt(cfg, n)
+    ucache = ppx.UnifiedCache(mm, (n + 63) // 64 * 64, 4)
+    lg = torch.empty((1, mm.info["n_vocab"]), dtype=torch.float32, device="cuda")
+    flags = np.zeros(mm.info["n_layer"] + 1, np.uint8)
+    slots_prune = ppx.prune_predicate(mm.info["n_layer"], mm.info["n_layer_kv_from_start"], 0, 4, flags)
+    kv = ppx.KVCache(mm, n)
+    res = {}
+
+    def unified(prune):
+        ucache.seq_rm(0)
+        mm.prefill_unified([toks], [0], ucache, n_ubatch=ub, prune=prune, logits=lg)
+
+    def own_cache():
+        kv.clear()
+        mm.prefill(toks, kv, n_ubatch=ub, logits=lg[0])
+
+    for name, fn in (("one_sequence", lambda: unified("auto")),
+                     ("four_slots", lambda: unified("auto" if slots_prune else "off")),
+                     ("own_cache", own_cache)):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        res[name] = float(np.median(ts))
+    del ucache, kv
+    torch.cuda.synchronize()
+    return {"prompt": n, "unified_one_sequence_ms": res["one_sequence"],
+            "single_sequence_cache_ms": res["own_cache"],
+            "four_slots_predicate_prunes": bool(slots_prune), "four_slots_ms": res["four_slots"],
+            "one_sequence_tokens_per_s": n / res["one_sequence"] * 1e3,
+            "four_slots_tokens_per_s": n / res["four_slots"] * 1e3,
+            "ratio": res["four_slots"] / res["one_sequence"]}
 
 
 FULL_TABLE = [("e2b", (512, 2048, 8192), ("auto", "off")), ("e4b", (512, 2048, 8192), ("auto", "off")),
@@ -388,9 +448,16 @@ def main():
         shapes = [tuple(int(v) for v in x.split("x")) for x in a.multi.split(",") if x.strip()]
         multi = multi_pass(ppx, mm, cfg, ub, shapes)
         for key, r in multi.items():
-            print(f"# multi {key}: {r['multi_ms']:.2f} ms ({r['multi_tokens_per_s']:.0f} tok/s) vs one by one "
-                  f"{r['one_by_one_ms']:.2f} ms ({r['one_by_one_tokens_per_s']:.0f} tok/s)", file=sys.stderr,
-                  flush=True)
+            print(f"# multi {key}: split {r['multi_ms']:.2f} ms ({r['multi_tokens_per_s']:.0f} tok/s), unified "
+                  f"{r['unified_ms']:.2f} ms, one by one {r['one_by_one_ms']:.2f} ms "
+                  f"({r['one_by_one_tokens_per_s']:.0f} tok/s)", file=sys.stderr, flush=True)
+    server = None
+    if a.server_n:
+        server = server_pass(ppx, mm, cfg, ub, a.server_n)
+        print(f"# server prompt {a.server_n}: unified, one sequence {server['unified_one_sequence_ms']:.1f} ms; "
+              f"four slots {server['four_slots_ms']:.1f} ms; ratio {server['ratio']:.2f}; own cache "
+              f"{server['single_sequence_cache_ms']:.1f} ms", file=sys.stderr,
+              flush=True)
     dec = None
     if a.decode:
         dec = decode_pass(mm, kv, synth.prompt(cfg, a.n + a.decode + 2), ub, a.decode)
@@ -447,6 +514,7 @@ def main():
         "decode": dec,
         "prefix_reuse": reuse,
         "multi_sequence": multi,
+        "server_unified_vs_slots": server,
         "config_table": table,
         "ms_median": float(np.median(times)),
         "ms_std": float(np.std(times)),
