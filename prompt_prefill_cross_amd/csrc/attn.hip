@@ -89,6 +89,7 @@ __global__ __launch_bounds__(C::NT) void k_attn_prefill(const AttnGroup grp) {
     const __half *kp = a.k, *vtp = a.vt;
     const int32_t *page = nullptr;  // unified cache: the sequence's page table
     if (a.wg) {
+        if ((int)blockIdx.x >= a.nwg) return;  // past this unit's workgroup table (the whole workgroup)
         const AttnWg &d = a.wg[blockIdx.x];
         cb = d.cb;
         M = d.M;
@@ -697,7 +698,7 @@ int launch_attn_prefill_group(const AttnArgs *units, int n, hipStream_t s) {
         int x;
         if (a.wg) {
             // several sequences: the caller built the workgroup table and the split
-            if (n != 1 || a.nwg < 1 || !a.seq_kv || !a.row_pos || a.kc < ATTN_MIN_KC || a.kc % 64 || a.nkc < 1 ||
+            if (a.nwg < 1 || !a.seq_kv || !a.row_pos || a.kc < ATTN_MIN_KC || a.kc % 64 || a.nkc < 1 ||
                 a.nkc > ATTN_MAX_CHUNKS)
                 return PPX_E_INVAL;
             x = a.nwg;

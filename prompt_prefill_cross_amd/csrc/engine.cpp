@@ -136,11 +136,11 @@ struct Ctx {
         return reinterpret_cast<T *>(ws + off + (size_t)(k < 0 ? slot : k) * L.slot_stride);
     }
     // a row-batched GEMM of slot k, with that slot's split-K partial space
-    GemmArgs gemm(int k = -1) const {
+    GemmArgs gemm(int k = -1, const Rows *r = nullptr) const {
         GemmArgs g;
         g.part = sl<float>(L.gpart, k);
         g.part_floats = L.gpart_floats;
-        g.few_rows = rows && rows->gathered;
+        g.few_rows = r ? r->gathered : rows && rows->gathered;
         return g;
     }
 
@@ -308,8 +308,11 @@ int layer_rows_exact(Ctx &c, int il, int M, int row0, int pos0) {
 
 // One ubatch in flight: rows [row0, row0 + M) of the call (token ids from
 // row0 on), positions pos0 .., running layer il with the buffers of slot.
+// R: the per-row tables of a batch spanning several sequences (null: one
+// sequence in c.kv).
 struct Unit {
     int il, M, row0, pos0, slot;
+    const Ctx::Rows *R = nullptr;
 };
 
 // One step of the row-batched layers: every unit runs its own layer, and each
@@ -319,15 +322,22 @@ int layer_rows_group(Ctx &c, const Unit *U, int n) {
     if (n < 1 || n > kMaxUnits) return PPX_E_INVAL;
     if (c.exact) {
         if (n != 1) return PPX_E_INVAL;  // one ubatch at a time
-        return layer_rows_exact(c, U[0].il, U[0].M, U[0].row0, U[0].pos0);
+        const Ctx::Rows *r0 = c.rows;
+        const int s0 = c.slot;
+        c.rows = U[0].R;
+        c.slot = U[0].slot;
+        const int st = layer_rows_exact(c, U[0].il, U[0].M, U[0].row0, U[0].pos0);
+        c.rows = r0;
+        c.slot = s0;
+        return st;
     }
     const ppx_model *m = c.m;
     const ppx_model_info &I = m->info;
     const int d = I.d_model, hd = I.head_dim, qd = I.n_head * hd, kvd = I.kv_dim;
-    const Ctx::Rows *R = c.rows;
-    if (R && n != 1) return PPX_E_INVAL;
-    const size_t lstride = R ? 0 : (size_t)c.kv->n_ctx * kvd;
-    const size_t vstride = R ? 0 : (size_t)c.kv->vld * kvd;
+    for (int i = 1; i < n; ++i)
+        if (!U[i].R != !U[0].R) return PPX_E_INVAL;  // one kind of cache per launch
+    const size_t lstride = U[0].R ? 0 : (size_t)c.kv->n_ctx * kvd;
+    const size_t vstride = U[0].R ? 0 : (size_t)c.kv->vld * kvd;
     auto W = [&](int i) -> const LayerW & { return m->layers[U[i].il]; };
     auto X = [&](int i) { return c.sl<float>(c.L.x, U[i].slot); };
     auto H16 = [&](int i, size_t off) { return c.sl<__half>(off, U[i].slot); };
@@ -354,7 +364,7 @@ int layer_rows_group(Ctx &c, const Unit *U, int n) {
     }
     GemmArgs g[kMaxUnits];
     for (int i = 0; i < n; ++i) {
-        g[i] = c.gemm(U[i].slot);
+        g[i] = c.gemm(U[i].slot, U[i].R);
         g[i].A = H16(i, c.L.a16);
         g[i].lda = d;
         g[i].M = U[i].M;
@@ -366,7 +376,7 @@ int layer_rows_group(Ctx &c, const Unit *U, int n) {
         g[i].hd = hd;
         g[i].pos0 = U[i].pos0;
         g[i].rope = m->rope;
-        if (R) g[i].row_pos = R->pos;
+        if (U[i].R) g[i].row_pos = U[i].R->pos;
     }
     PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm_group(g, n, c.s));
     {
@@ -382,7 +392,7 @@ int layer_rows_group(Ctx &c, const Unit *U, int n) {
             k.qd = 0;
             k.kvd = kvd;
             k.out_f16 = nullptr;
-            if (R) {
+            if (const Ctx::Rows *R = U[i].R) {
                 k.row_seq = R->seq;
                 k.seq_kv = R->kv + (size_t)U[i].il * R->nseq;
             } else {
@@ -400,7 +410,7 @@ int layer_rows_group(Ctx &c, const Unit *U, int n) {
             AttnArgs &a = at[i];
             const int src = W(i).src;
             a.q = H16(i, c.L.q16);
-            if (R) {
+            if (const Ctx::Rows *R = U[i].R) {
                 a.wg = R->wg;
                 a.nwg = R->nwg;
                 a.seq_kv = R->kv + (size_t)src * R->nseq;
@@ -423,7 +433,7 @@ int layer_rows_group(Ctx &c, const Unit *U, int n) {
         PPX_LAUNCH(c, PPX_PHASE_ATTN, launch_attn_prefill_group(at, n, c.s));
     }
     for (int i = 0; i < n; ++i) {
-        g[i] = c.gemm(U[i].slot);
+        g[i] = c.gemm(U[i].slot, U[i].R);
         g[i].A = H16(i, c.L.o16);
         g[i].lda = qd;
         g[i].M = U[i].M;
@@ -443,7 +453,7 @@ int layer_rows_group(Ctx &c, const Unit *U, int n) {
         PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_rmsnorm_group(nu, n, m->eps, d, false, c.s));
     }
     for (int i = 0; i < n; ++i) {
-        g[i] = c.gemm(U[i].slot);
+        g[i] = c.gemm(U[i].slot, U[i].R);
         g[i].A = H16(i, c.L.a16);
         g[i].lda = d;
         g[i].M = U[i].M;
@@ -458,7 +468,7 @@ int layer_rows_group(Ctx &c, const Unit *U, int n) {
         c.end(PPX_PHASE_GEMM, ev0, true);
     }
     for (int i = 0; i < n; ++i) {
-        g[i] = c.gemm(U[i].slot);
+        g[i] = c.gemm(U[i].slot, U[i].R);
         g[i].A = H16(i, c.L.h16);
         g[i].lda = I.n_ff;
         g[i].M = U[i].M;
@@ -476,7 +486,7 @@ int layer_rows_group(Ctx &c, const Unit *U, int n) {
     if (I.ple_dim) {
         const int E = I.ple_dim;
         for (int i = 0; i < n; ++i) {
-            g[i] = c.gemm(U[i].slot);
+            g[i] = c.gemm(U[i].slot, U[i].R);
             g[i].A = H16(i, c.L.a16);
             g[i].lda = d;
             g[i].M = U[i].M;
@@ -484,14 +494,14 @@ int layer_rows_group(Ctx &c, const Unit *U, int n) {
             g[i].epi = EPI_PLE;
             g[i].out_f16 = H16(i, c.L.p16);
             g[i].ple_raw = m->ple_raw;
-            g[i].tok = R ? R->tok : c.at<int32_t>(c.L.tok) + U[i].row0;
+            g[i].tok = U[i].R ? U[i].R->tok : c.at<int32_t>(c.L.tok) + U[i].row0;
             g[i].ple_row_blocks = I.n_layer * E / 32;
             g[i].ple_col0 = U[i].il * E;
             g[i].ple_s = W(i).ple_s;
         }
         PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm_group(g, n, c.s));
         for (int i = 0; i < n; ++i) {
-            g[i] = c.gemm(U[i].slot);
+            g[i] = c.gemm(U[i].slot, U[i].R);
             g[i].A = H16(i, c.L.p16);
             g[i].lda = E;
             g[i].M = U[i].M;
@@ -511,7 +521,8 @@ int layer_rows_group(Ctx &c, const Unit *U, int n) {
             if (I.ple_dim) nk += (double)w.wpg.N * w.wpg.K + (double)w.wpu.N * w.wpu.K;
             c.tm->gemm_flop += 2.0 * M * nk;
             c.tm->glu_flop += 2.0 * M * w.wgu.N * w.wgu.K;
-            const double vis = R ? R->vis : (double)M * pos0 + 0.5 * (double)M * (M + 1);  // causal (query, key) pairs
+            const double vis = U[i].R ? U[i].R->vis
+                                      : (double)M * pos0 + 0.5 * (double)M * (M + 1);  // causal (query, key) pairs
             c.tm->attn_flop += 4.0 * I.n_head * hd * vis;
         }
     }
@@ -520,7 +531,7 @@ int layer_rows_group(Ctx &c, const Unit *U, int n) {
 
 // One ubatch of M rows through layer il on the MFMA path (the current slot).
 int layer_rows(Ctx &c, int il, int M, int row0, int pos0) {
-    const Unit u{il, M, row0, pos0, c.slot};
+    const Unit u{il, M, row0, pos0, c.slot, c.rows};
     return layer_rows_group(c, &u, 1);
 }
 
@@ -948,7 +959,10 @@ struct MultiLayout {
 MultiLayout multi_layout(const ppx_model *m, int ub, int k, long T, int n_ctx_max, int npg = 0) {
     const ppx_model_info &I = m->info;
     MultiLayout L{};
-    L.w = ws_layout(m, std::max(ub, k), n_ctx_max, 1);
+    // ubatch slots as in a single-sequence prefill of T rows
+    const long nub_all = (T + ub - 1) / ub;
+    const int nslots = (int)std::max(1L, std::min<long>({nub_all, (long)I.n_layer, (long)kMaxUnits}));
+    L.w = ws_layout(m, std::max(ub, k), n_ctx_max, nslots);
     size_t o = L.w.total;
     L.xk = o;
     o += al(4ull * k * I.d_model);
@@ -1178,10 +1192,12 @@ int multi_pass(ppx_model *m, const SeqRun *sq, int k, const ppx_kvu *u, int nctx
     // the launches (tables and tokens are already in device memory, so a
     // recorded sequence serves any prompts of the same shape)
     auto enqueue = [&](Ctx &c) -> int {
-        float *x = c.sl<float>(c.L.x);
         const int full_layers = prune ? Ls : L;
-        for (const Ub &U : ubs) {
-            Ctx::Rows R;
+        const int nub = (int)ubs.size();
+        std::vector<Ctx::Rows> RU(nub);
+        for (int j = 0; j < nub; ++j) {
+            const Ub &U = ubs[j];
+            Ctx::Rows &R = RU[j];
             R.tok = D32(ML.tok) + U.u0;
             R.pos = D32(ML.pos) + U.u0;
             R.seq = D32(ML.seq) + U.u0;
@@ -1191,11 +1207,44 @@ int multi_pass(ppx_model *m, const SeqRun *sq, int k, const ppx_kvu *u, int nctx
             R.nwg = U.nwg;
             R.split = U.split;
             R.vis = U.vis;
-            c.rows = &R;
-            PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_embed(m->tok, R.tok, U.M, m->embd_scale, x, c.s));
-            for (int il = 0; il < full_layers; ++il) PPX_TRY(layer_rows(c, il, U.M, 0, 0));
-            if (U.npairs) PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_gather_rows(x, d, dpairs + U.pair0, U.npairs, xk, c.s));
         }
+        // the ubatches in lockstep, as in a single-sequence prefill: up to
+        // nslots in flight, each step runs every one through its next layer
+        // with one launch per operation; K|V of a step precede its attention,
+        // and a ubatch never runs ahead of an earlier one, so every row sees
+        // the keys of the serial order
+        const int NU = c.exact ? 1 : std::max(1, std::min({nub, full_layers, c.L.nslots}));
+        struct Flight {
+            int u, il, slot;
+        };
+        std::vector<Flight> fl;
+        std::vector<int> free_slots;
+        for (int q = NU - 1; q >= 0; --q) free_slots.push_back(q);
+        int next_u = 0;
+        while (next_u < nub || !fl.empty()) {
+            while ((int)fl.size() < NU && next_u < nub) {
+                const int slot = free_slots.back();
+                free_slots.pop_back();
+                PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_embed(m->tok, RU[next_u].tok, ubs[next_u].M, m->embd_scale,
+                                                            c.sl<float>(c.L.x, slot), c.s));
+                fl.push_back({next_u, 0, slot});
+                ++next_u;
+            }
+            Unit Us[kMaxUnits];
+            const int nu = (int)fl.size();
+            for (int i = 0; i < nu; ++i) Us[i] = Unit{fl[i].il, ubs[fl[i].u].M, 0, 0, fl[i].slot, &RU[fl[i].u]};
+            PPX_TRY(layer_rows_group(c, Us, nu));
+            for (int i = nu - 1; i >= 0; --i) {
+                if (++fl[i].il < full_layers) continue;
+                const Ub &U = ubs[fl[i].u];
+                if (U.npairs)
+                    PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_gather_rows(c.sl<float>(c.L.x, fl[i].slot), d,
+                                                                      dpairs + U.pair0, U.npairs, xk, c.s));
+                free_slots.push_back(fl[i].slot);
+                fl.erase(fl.begin() + i);
+            }
+        }
+        float *x = c.sl<float>(c.L.x, 0);
         PPX_LAUNCH(c, PPX_PHASE_OTHER, launch_copy_f32(xk, x, k * d, c.s));
         Ctx::Rows R;
         R.tok = D32(ML.ttok);
