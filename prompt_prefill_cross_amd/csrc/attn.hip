@@ -660,12 +660,24 @@ int ok() { return hipGetLastError() == hipSuccess ? PPX_OK : PPX_E_HIP; }
 constexpr int ATTN_CPW = 1, ATTN_NC = 8, ATTN_CB = 16 * ATTN_CPW * ATTN_NC;
 constexpr int ATTN_MIN_KC = 128;  // keys per chunk at least (early ubatches get more workgroups)
 
-AttnSplit attn_split(int M, int H, int KVH, int pos0) {
-    const int G = H / KVH;
-    return attn_split_cols((M * G + ATTN_CB - 1) / ATTN_CB, KVH, pos0 + M);
-}
 AttnSplit attn_split_cols(int colblocks, int KVH, int P) {
     int want = (256 + colblocks * KVH - 1) / (colblocks * KVH);
+    want = std::max(1, std::min(want, ATTN_MAX_CHUNKS));
+    int kc = (P + want - 1) / want;
+    kc = std::max(ATTN_MIN_KC, (kc + 63) / 64 * 64);
+    AttnSplit sp;
+    sp.kc = kc;
+    sp.nkc = (P + kc - 1) / kc;
+    return sp;
+}
+
+// Key split of one unit of a launch whose units hold tot_cb column blocks
+// and KV heads together: chunks enough for about ATTN_WG_TARGET workgroups
+// over the launch (fewer chunks, less partial traffic and merging, when
+// several ubatches share it).
+constexpr int ATTN_WG_TARGET = 256;
+AttnSplit attn_split_group(int P, int tot_cb) {
+    int want = (ATTN_WG_TARGET + tot_cb - 1) / tot_cb;
     want = std::max(1, std::min(want, ATTN_MAX_CHUNKS));
     int kc = (P + want - 1) / want;
     kc = std::max(ATTN_MIN_KC, (kc + 63) / 64 * 64);
@@ -687,7 +699,10 @@ size_t attn_prefill_scratch_floats(int M, int H, int hd, int n_ctx) {
 int launch_attn_prefill_group(const AttnArgs *units, int n, hipStream_t s) {
     if (n < 1 || n > kMaxUnits) return PPX_E_INVAL;
     AttnGroup g;
-    int nx = 0, ny = 0;
+    int nx = 0, ny = 0, tot_cb = 0;
+    for (int i = 0; i < n; ++i)
+        if (units[i].M > 0 && !units[i].wg && units[i].KVH > 0)
+            tot_cb += (units[i].M * (units[i].H / units[i].KVH) + ATTN_CB - 1) / ATTN_CB * units[i].KVH;
     for (int i = 0; i < n; ++i) {
         AttnArgs a = units[i];
         if (a.M <= 0) continue;
@@ -704,7 +719,7 @@ int launch_attn_prefill_group(const AttnArgs *units, int n, hipStream_t s) {
             x = a.nwg;
         } else {
             if (a.vld % 64 || a.pos0 + a.M > a.vld) return PPX_E_UNSUPPORTED;
-            const AttnSplit sp = attn_split(a.M, a.H, a.KVH, a.pos0);
+            const AttnSplit sp = attn_split_group(a.pos0 + a.M, std::max(tot_cb, 1));
             a.kc = sp.kc;
             a.nkc = sp.nkc;
             x = (a.M * G + ATTN_CB - 1) / ATTN_CB;

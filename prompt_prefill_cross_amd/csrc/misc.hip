@@ -41,14 +41,60 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float *x, const float *g,
     for (int k = threadIdx.x; k < d; k += 256) o[k] = (T)(xr[k] * r * g[k]);
 }
 
-// y = rmsnorm(x) -> fp16 in the fragment-tiled layout, one wave per row; with
-// LO, also lo = fp16(y - fp16(y)) (the split operand of the exact-weight
-// GEMM).  Lane l handles the 8-column chunks l, l+64, ... of its row, kept in
-// registers between the sum of squares and the scaling.
+// y = rmsnorm(x) -> fp16 in the fragment-tiled layout; with LO, also
+// lo = fp16(y - fp16(y)) (the split operand of the exact-weight GEMM).
 constexpr int NORM_MAX_CHUNKS = 2;  // d <= 2 * 8 * 256
-// One workgroup per row: thread t owns the eight-float chunks t, t + 256;
-// the gain is loaded before the row's reduction, which it does not need.
-// Grid (rows, units): unit blockIdx.y of the group.
+constexpr int NORM_WAVE_CHUNKS = 8;  // one wave per row: d <= 8 * 8 * 64
+
+// One wave per row, four rows per workgroup: lane l owns the eight-float
+// chunks l, l + 64, ... of its row, held in registers between the sum of
+// squares and the scaling; no workgroup barrier.  Grid (row quads, units).
+template <bool LO>
+__global__ __launch_bounds__(256) void k_rmsnorm_rows(const NormGroup grp, float eps, int d) {
+    const NormUnit &u = grp.u[blockIdx.y];
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= u.M) return;  // the whole wave
+    const float *xr = u.x + (size_t)row * d;
+    const int nch = d >> 3;
+    float4 v[NORM_WAVE_CHUNKS][2];
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < NORM_WAVE_CHUNKS; ++c) {
+        const int ch = lane + 64 * c;
+        if (ch < nch) {
+            v[c][0] = *reinterpret_cast<const float4 *>(xr + ch * 8);
+            v[c][1] = *reinterpret_cast<const float4 *>(xr + ch * 8 + 4);
+            ss += v[c][0].x * v[c][0].x + v[c][0].y * v[c][0].y + v[c][0].z * v[c][0].z + v[c][0].w * v[c][0].w;
+            ss += v[c][1].x * v[c][1].x + v[c][1].y * v[c][1].y + v[c][1].z * v[c][1].z + v[c][1].w * v[c][1].w;
+        }
+    }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+    for (int c = 0; c < NORM_WAVE_CHUNKS; ++c) {
+        const int ch = lane + 64 * c;
+        if (ch < nch) {
+            const float4 g0 = *reinterpret_cast<const float4 *>(u.g + ch * 8);
+            const float4 g1 = *reinterpret_cast<const float4 *>(u.g + ch * 8 + 4);
+            const float y[8] = {v[c][0].x * r * g0.x, v[c][0].y * r * g0.y, v[c][0].z * r * g0.z, v[c][0].w * r * g0.w,
+                                v[c][1].x * r * g1.x, v[c][1].y * r * g1.y, v[c][1].z * r * g1.z, v[c][1].w * r * g1.w};
+            h8 yh, yl;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                yh[e] = (_Float16)y[e];
+                if (LO) yl[e] = (_Float16)(y[e] - (float)yh[e]);
+            }
+            const size_t o = tiled_index(row, ch * 8, d);
+            *reinterpret_cast<h8 *>(u.hi + o) = yh;
+            if (LO) *reinterpret_cast<h8 *>(u.lo + o) = yl;
+        }
+    }
+}
+
+// One workgroup per row (rows wider than the wave kernel takes): thread t
+// owns the eight-float chunks t, t + 256; the gain is loaded before the row's
+// reduction, which it does not need.  Grid (rows, units).
 template <bool LO>
 __global__ __launch_bounds__(256) void k_rmsnorm_tiled(const NormGroup grp, float eps, int d) {
     __shared__ float red[4];
@@ -410,8 +456,14 @@ int launch_rmsnorm_group(const NormUnit *units, int n, float eps, int d, bool lo
         M = std::max(M, units[i].M);
     }
     if (!g.n) return PPX_OK;
-    if (lo) hipLaunchKernelGGL((k_rmsnorm_tiled<true>), dim3(M, g.n), dim3(256), 0, s, g, eps, d);
-    else hipLaunchKernelGGL((k_rmsnorm_tiled<false>), dim3(M, g.n), dim3(256), 0, s, g, eps, d);
+    if (d <= NORM_WAVE_CHUNKS * 8 * 64) {
+        if (lo) hipLaunchKernelGGL((k_rmsnorm_rows<true>), dim3((M + 3) / 4, g.n), dim3(256), 0, s, g, eps, d);
+        else hipLaunchKernelGGL((k_rmsnorm_rows<false>), dim3((M + 3) / 4, g.n), dim3(256), 0, s, g, eps, d);
+    } else if (lo) {
+        hipLaunchKernelGGL((k_rmsnorm_tiled<true>), dim3(M, g.n), dim3(256), 0, s, g, eps, d);
+    } else {
+        hipLaunchKernelGGL((k_rmsnorm_tiled<false>), dim3(M, g.n), dim3(256), 0, s, g, eps, d);
+    }
     return ok();
 }
 

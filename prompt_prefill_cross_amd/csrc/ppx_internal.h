@@ -258,7 +258,6 @@ constexpr int ATTN_MAX_CHUNKS = 16;
 struct AttnSplit {
     int kc = 0, nkc = 1;  // keys per chunk (multiple of 64), chunks
 };
-AttnSplit attn_split(int M, int H, int KVH, int pos0);
 // The same rule for a launch of `colblocks` workgroup column blocks per KV
 // head whose longest sequence segment ends at position P - 1.
 AttnSplit attn_split_cols(int colblocks, int KVH, int P);
