@@ -17,15 +17,18 @@
 //     A-operand order) and the repacked weight codes and block scales of the
 //     workgroup's columns, each wave an equal share.  Stage s is handed over at
 //     barrier s once every producer's outstanding-DMA count says its share of
-//     stages s and s+1 has landed.  (DMA lives in waves of its own because the
+//     stage s has landed, so DEPTH - 1 stages are in flight behind the one in
+//     use.  (DMA lives in waves of its own because the
 //     compiler makes any LDS read that follows an LDS DMA in the same wave wait
 //     for all DMA; one wave issues DMA at only a fraction of what the CU can
 //     take in, so wide tiles use several.)
 //   * Compute waves never touch global memory in the main loop: per stage they
-//     read A fragments and the NEXT stage's codes from LDS, and decode those
-//     codes (a shift, a mask, an OR with the fp16 exponent of 1024, a subtract
-//     and a multiply per pair) while the MFMAs of this stage run, so the VALU
-//     work of the decode overlaps the matrix work.
+//     read A fragments and the stage's codes from LDS and decode the codes (a
+//     shift, a mask, an OR with the fp16 exponent of 1024, a subtract and a
+//     multiply per pair); with two compute waves per SIMD one wave's decode
+//     runs beside the other's MFMAs.  (Decoding the next stage's codes during
+//     this stage's MFMAs instead kept one stage fewer in flight: measured
+//     slower, 26.7 vs 25.7 us for the E2B-like gate|up at M = 512.)
 //   * The KS partial tiles meet in LDS in slice order; the waves of up to KS
 //     groups then finish TM/KS row tiles each, spreading the epilogue.
 //   * With a K split across S workgroups, each writes its fp32 partial tile;
@@ -272,7 +275,7 @@ struct PCfg {
     static constexpr int XCH_FLOATS = (KS * NFG - NFG) * NWN * SLOT_FLOATS;
     static constexpr int STAGE_HALVES = TMS * TN * 16 * 8;  // epilogue staging per compute wave
     static_assert(NT <= 1024, "workgroup size");
-    static_assert(DEPTH >= 3 && (DEPTH - 3) * PER <= 63, "ring depth / vmcnt range");
+    static_assert(DEPTH >= 3 && (DEPTH - 2) * PER <= 63, "ring depth / vmcnt range");
     static_assert(DEPTH * STAGE_UNITS * 16 <= 160 * 1024, "LDS");
     static_assert(XCH_FLOATS * 4 + NCW * STAGE_HALVES * 2 <= DEPTH * STAGE_UNITS * 16, "exchange + staging space");
     // exchange slot of the rows K group gs hands to finishing group gd (gs != gd)
@@ -408,7 +411,7 @@ __global__ __launch_bounds__(C::NT) void k_q4gemm_p(const GemmGroup grp, int S, 
 #pragma unroll
         for (int s = 0; s < C::DEPTH - 1; ++s) issue(s);
         for (int s = 0; s < nkg; ++s) {
-            wait_vm<(C::DEPTH - 3) * C::PER>();  // this wave's share of stages <= s + 1 has landed
+            wait_vm<(C::DEPTH - 2) * C::PER>();  // this wave's share of stages <= s has landed
             lds_barrier();
             issue(s + C::DEPTH - 1);  // into the buffer of stage s - 1, which nobody reads any more
         }
@@ -443,19 +446,15 @@ __global__ __launch_bounds__(C::NT) void k_q4gemm_p(const GemmGroup grp, int S, 
             bf[1][j] = q4_word_to_h8(bw[j].y, d[1]);
         }
     };
-    // stage s: MFMAs on the codes decoded one stage earlier (bc) while the next
-    // stage's codes are decoded (bn)
-    auto step = [&](int s, const h8 (&bc)[2][C::TN], h8 (&bn)[2][C::TN]) {
+    // stage s: its codes decoded, then its MFMAs
+    auto step = [&](int s) {
         const h8 *st = ring + (s % C::DEPTH) * C::STAGE_UNITS;
-        const h8 *sn = ring + ((s + 1) % C::DEPTH) * C::STAGE_UNITS;
-        // the A fragments of the two 32-wide halves in turn: the second half's
-        // reads are in flight during the first half's MFMAs, and only one half
-        // is held at a time (with both, the 8 x 3 wave tile spills registers)
         const h8 *as = st + g * C::AFR * 64 + lane;
         h8 af[C::TM];
 #pragma unroll
         for (int i = 0; i < C::TM; ++i) af[i] = as[i * 64];
-        decode(sn, bn);
+        h8 bc[2][C::TN];
+        decode(st, bc);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             h8 an[C::TM];
@@ -474,13 +473,8 @@ __global__ __launch_bounds__(C::NT) void k_q4gemm_p(const GemmGroup grp, int S, 
         }
         if (s + 1 < nkg) lds_barrier();
     };
-    h8 bA[2][C::TN], bB[2][C::TN];
-    lds_barrier();  // stages 0 and 1 have landed
-    decode(ring, bA);
-    for (int s = 0; s < nkg; s += 2) {
-        step(s, bA, bB);
-        if (s + 1 < nkg) step(s + 1, bB, bA);
-    }
+    lds_barrier();  // stage 0 has landed
+    for (int s = 0; s < nkg; ++s) step(s);
     lds_barrier();  // matches the producer's last barrier: the ring is free
 
     float *xch = reinterpret_cast<float *>(ring);
