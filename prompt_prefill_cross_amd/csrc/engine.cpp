@@ -483,7 +483,24 @@ int layer_rows_group(Ctx &c, const Unit *U, int n) {
         }
     }
     PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_gemm_group(g, n, c.s));
-    if (I.ple_dim) {
+    if (I.ple_dim && ple_fused_supported(I.ple_dim, d)) {
+        // the whole block in one launch: p stays in LDS
+        const int E = I.ple_dim;
+        PleArgs pa[kMaxUnits];
+        for (int i = 0; i < n; ++i) {
+            pa[i].a = H16(i, c.L.a16);
+            pa[i].x = X(i);
+            pa[i].wg = W(i).wpg;
+            pa[i].wu = W(i).wpu;
+            pa[i].ple_raw = m->ple_raw;
+            pa[i].tok = U[i].R ? U[i].R->tok : c.at<int32_t>(c.L.tok) + U[i].row0;
+            pa[i].ple_row_blocks = I.n_layer * E / 32;
+            pa[i].ple_col0 = U[i].il * E;
+            pa[i].ple_s = W(i).ple_s;
+            pa[i].M = U[i].M;
+        }
+        PPX_LAUNCH(c, PPX_PHASE_GEMM, launch_ple_group(pa, n, c.s));
+    } else if (I.ple_dim) {
         const int E = I.ple_dim;
         for (int i = 0; i < n; ++i) {
             g[i] = c.gemm(U[i].slot, U[i].R);

@@ -298,6 +298,25 @@ struct AttnArgs {
     const int32_t *row_seq = nullptr;
 };
 int launch_attn_prefill(const AttnArgs &a, hipStream_t s);
+// The per-layer-embedding block of one unit (rows of one ubatch and layer):
+// x[M][d] += (gelu(a wg^T) * s * deq(ple_table[tok][ple_col0 + j])) wu^T,
+// a the fp16 fragment-tiled RMSNorm of x with the block's gain.
+struct PleArgs {
+    const __half *a = nullptr;
+    float *x = nullptr;
+    Q4R wg, wu;                    // [E][d] and [d][E]
+    const uint8_t *ple_raw = nullptr;
+    const int32_t *tok = nullptr;  // [M]
+    int ple_row_blocks = 0, ple_col0 = 0, M = 0;
+    float ple_s = 0.f;
+};
+struct PleGroup {
+    PleArgs u[kMaxUnits];
+    int n = 0;
+};
+bool ple_fused_supported(int E, int d);
+int launch_ple_group(const PleArgs *units, int n, hipStream_t s);
+
 struct AttnGroup {
     int n = 0;
     AttnArgs u[kMaxUnits];
