@@ -12,10 +12,17 @@ their own overhead; that figure is given beside it).  `phases` gives the
 whole GEMM phase, the attention phase (MFMA) and the single-row phase (HBM)
 from events around every launch in a separate, identical prefill pass.  `traffic` is read from the
 committed counter summary when it was taken on the current kernel source.
-`cpu_baseline` times the fp64 oracle on a bounded sample.
+`cpu_baseline` times the fp64 oracle on a bounded sample.  Beside the main
+line: `other_lengths`, `decode`, `prefix_reuse`, `multi_sequence` (k prompts
+in one call with split caches and with one unified cache, against k calls),
+`server_unified_vs_slots` (one long prompt as the only sequence of a unified
+cache, where the predicate prunes, against four configured slots, where it
+does not) and `config_table` (E2B-like and E4B-like at 2048 tokens and the
+no-sharing control at 8192, pruned and unpruned; --table for the full set).
 
---pmc-pass runs one prefill and one plain device copy of known size and
-exits: the command under which the HBM counters are collected.
+--pmc-pass runs the roofline's gate|up launches, an LDS-DMA read and a plain
+device copy of known sizes and exits: the command under which the HBM
+counters are collected.
 """
 import argparse
 import hashlib
@@ -57,14 +64,15 @@ def parse():
                          "no-sharing control at 8192, each pruned and unpruned)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="prompt tokens of the oracle sample (0 = all)")
-    ap.add_argument("--pmc-pass", action="store_true", help="one prefill + one calibration copy, then exit")
+    ap.add_argument("--pmc-pass", action="store_true", help="the roofline's gate|up launches and two calibration passes, then exit")
     return ap.parse_args()
 
 
 # Sources of the GEMM kernel; counter-derived traffic is reported only while they are unchanged.
 GEMM_SOURCES = ("prompt_prefill_cross_amd/csrc/gemm.hip", "prompt_prefill_cross_amd/csrc/ppx_dev.h")
 TRAFFIC_FILE = "profiles/k_q4gemm_gate_up_e2b2048_traffic.txt"
-COPY_CAL_BYTES = 1 << 29  # calibration copy: 512 MiB read + 512 MiB written
+COPY_CAL_BYTES = 1 << 29  # write calibration: a copy of 512 MiB (read and written once)
+STREAM_CAL_BYTES = 1 << 29  # fetch calibration: 512 MiB read through LDS DMA
 
 
 def gemm_source_sha():
@@ -134,13 +142,21 @@ def phase_pass(ppx, mm, kv, toks, ub, prune, reps=3):
     return tm_sum
 
 
-def glu_kernel_us(mm, ub, reps=50, warmup=5):
-    """Average duration of the gate|up GEMM (layer 0's weights, ub rows)."""
+def glu_operands(mm, ub):
+    """Inputs of the roofline's gate|up launches: a seeded tiled fp16 A of ub
+    rows and the output h."""
     import torch
     I = mm.info
     g = torch.Generator(device="cuda").manual_seed(7)
     a = mm.tile(torch.randn((ub, I["d_model"]), generator=g, device="cuda").to(torch.float16))
     h = torch.empty(((ub + 15) // 16 * 16) * I["n_ff"], dtype=torch.float16, device="cuda")
+    return a, h
+
+
+def glu_kernel_us(mm, ub, reps=50, warmup=5):
+    """Average duration of the gate|up GEMM (layer 0's weights, ub rows)."""
+    import torch
+    a, h = glu_operands(mm, ub)
     for _ in range(warmup):
         mm.op_gemm_glu("blk.0.ffn_gate", a, M=ub, out=h, raw=True)
     t0 = torch.cuda.Event(enable_timing=True)
@@ -378,15 +394,25 @@ def table_pass(ppx, main_cfg, main_model, plan):
     return rows
 
 
-def pmc_pass(mm, kv, toks, ub, prune):
+def pmc_pass(ppx, mm, ub, glu_launches=20):
+    """The dispatches the traffic counters are read on: the gate|up GEMM
+    exactly as the roofline times it (layer 0's weights, ub rows), then a read
+    of STREAM_CAL_BYTES through the same LDS DMA its producer waves use
+    (FETCH_SIZE calibration: known bytes, the GEMM's load instruction), then
+    a plain device copy of COPY_CAL_BYTES (WRITE_SIZE calibration)."""
     import torch
-    kv.clear()
-    mm.prefill(toks, kv, n_ubatch=ub, prune=prune)
+    a, h = glu_operands(mm, ub)
+    for _ in range(glu_launches):
+        mm.op_gemm_glu("blk.0.ffn_gate", a, M=ub, out=h, raw=True)
+    buf = torch.ones(STREAM_CAL_BYTES // 4, dtype=torch.int32, device="cuda")
+    ppx.stream_read(buf)
+    del buf
     src = torch.ones(COPY_CAL_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     dst.copy_(src)
     torch.cuda.synchronize()
-    print(f"# pmc pass done: one prefill of {len(toks)} tokens, one {COPY_CAL_BYTES} B copy", flush=True)
+    print(f"# pmc pass done: {glu_launches} gate|up launches (M={ub}), one {STREAM_CAL_BYTES} B LDS-DMA read, "
+          f"one {COPY_CAL_BYTES} B copy", flush=True)
 
 
 def cpu_baseline(cfg, buf, toks, sample):
@@ -426,7 +452,7 @@ def main():
     mm.workspace(ub, n_ctx)
 
     if a.pmc_pass:
-        pmc_pass(mm, kv, synth.prompt(cfg, a.n), ub, a.prune)
+        pmc_pass(ppx, mm, ub)
         return
 
     results = {}

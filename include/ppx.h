@@ -423,6 +423,16 @@ int ppx_prune_predicate(int n_layer, int n_layer_kv_from_start, int embeddings, 
  * ceil(M/16)*16 rows, of which the padding rows are left untouched. */
 int ppx_op_tile_f16(const void *src_dev, int M, int K, void *dst_dev, void *hip_stream);
 
+/* Read bytes (a positive multiple of 1024) of device memory at src_dev
+ * (16-byte aligned) through LDS DMA -- the load instruction and the 1 KB
+ * per-wave pattern with which the GEMM's producer waves fetch their operands
+ * -- over n_workgroups workgroups (1..65536) of four waves; workgroup w
+ * writes the XOR of the 32-bit words it read to xor_dev[w] (device uint32
+ * [n_workgroups]), so the XOR over all of them is that of the buffer.  For
+ * calibrating hardware byte counters against a known byte count.
+ * PPX_E_INVAL for bad arguments. */
+int ppx_op_stream_read(const void *src_dev, size_t bytes, uint32_t *xor_dev, int n_workgroups, void *hip_stream);
+
 /* Dequantise a whole Q4_0 tensor from the engine's repacked device layout
  * into fp32 [rows][cols] row-major (exact). */
 int ppx_op_dequant(const ppx_model *m, const char *tensor, float *out_dev, void *hip_stream);

@@ -109,6 +109,7 @@ SIGNATURES = [
     ("ppx_prune_predicate", c_int, [c_int, c_int, c_int, c_int, POINTER(c_uint8), c_int]),
     ("ppx_op_dequant", c_int, [c_void_p, c_char_p, c_void_p, c_void_p]),
     ("ppx_op_tile_f16", c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p]),
+    ("ppx_op_stream_read", c_int, [c_void_p, c_size_t, c_void_p, c_int, c_void_p]),
     ("ppx_op_gemm_workspace_bytes", c_size_t, [c_void_p, c_char_p, c_int]),
     ("ppx_op_gemm", c_int, [c_void_p, c_char_p, c_void_p, c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
     ("ppx_op_gemm_glu", c_int, [c_void_p, c_char_p, c_void_p, c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
@@ -153,6 +154,19 @@ def _stream(stream=None):
 
 def _ptr(t) -> c_void_p:
     return c_void_p(t.data_ptr())
+
+
+def stream_read(buf, n_workgroups: int = 2048, stream=None) -> int:
+    """XOR of the 32-bit words of a device buffer (bytes a multiple of 1024),
+    read through the GEMM producers' LDS DMA (ppx_op_stream_read)."""
+    import torch
+    out = torch.empty(n_workgroups, dtype=torch.int32, device=buf.device)
+    _check(lib().ppx_op_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out), n_workgroups,
+                                    _stream(stream)), "ppx_op_stream_read")
+    x = 0
+    for v in out.cpu().numpy().astype(np.uint32).tolist():
+        x ^= v
+    return x
 
 
 def prune_predicate(n_layer, n_layer_kv_from_start, embeddings, n_seq_max, embeddings_layer_inp=None,

@@ -1914,6 +1914,13 @@ int ppx_op_gemm_glu(const ppx_model *m, const char *tensor, const void *a_dev_f1
     return launch_gemm(g, (hipStream_t)hip_stream);
 }
 
+int ppx_op_stream_read(const void *src_dev, size_t bytes, uint32_t *xor_dev, int n_workgroups, void *hip_stream) {
+    if (!src_dev || !xor_dev || bytes == 0 || bytes % 1024 || n_workgroups < 1 || n_workgroups > 65536 ||
+        (reinterpret_cast<uintptr_t>(src_dev) & 15) != 0)
+        return PPX_E_INVAL;
+    return launch_stream_read(src_dev, bytes, xor_dev, n_workgroups, (hipStream_t)hip_stream);
+}
+
 int ppx_op_tile_f16(const void *src_dev, int M, int K, void *dst_dev, void *hip_stream) {
     if (!src_dev || !dst_dev || M < 0 || K <= 0) return PPX_E_INVAL;
     return launch_tile_f16(static_cast<const __half *>(src_dev), M, K, static_cast<__half *>(dst_dev),

@@ -19,6 +19,31 @@ __global__ __launch_bounds__(256) void k_embed_add(Q4R w, const int32_t *id, flo
     for (int k = threadIdx.x; k < w.K; k += 256) x[k] = base[k] + scale * q4r_weight(w, t, k);
 }
 
+typedef __attribute__((address_space(3))) void lds_t;
+
+// Reads nchunks 1 KB chunks through LDS DMA (global_load_lds, 16 bytes per
+// lane: the instruction and the per-wave 1 KB pattern of the GEMM's producer
+// waves) and XORs the 32-bit words read; workgroup w writes its XOR to
+// out[w].  Four waves, one 1 KB LDS slot each.
+__global__ __launch_bounds__(256) void k_stream_read(const uint8_t *src, size_t nchunks, uint32_t *out) {
+    __shared__ uint4 slot[4][64];
+    __shared__ uint32_t red[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t x = 0;
+    for (size_t c = (size_t)blockIdx.x * 4 + wave; c < nchunks; c += (size_t)gridDim.x * 4) {
+        __builtin_amdgcn_global_load_lds(src + c * 1024 + lane * 16, (lds_t *)&slot[wave][0], 16, 0, 0);
+        __builtin_amdgcn_s_waitcnt(0);  // the wave's own DMA has landed in its slot
+        const uint4 v = slot[wave][lane];
+        x ^= v.x ^ v.y ^ v.z ^ v.w;
+        __builtin_amdgcn_s_waitcnt(0);  // the read is done before the next DMA reuses the slot
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x ^= (uint32_t)__shfl_xor((int)x, o, 64);
+    if (lane == 0) red[wave] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) out[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
 __device__ __forceinline__ float block_sum_256(float v, float *red) {
     v = wave_sum(v);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -436,6 +461,12 @@ int launch_gemv(const GemvArgs &a, hipStream_t s) {
 int launch_embed(const Q4R &tok, const int32_t *ids, int M, float scale, float *x, hipStream_t s) {
     if (M <= 0) return PPX_OK;
     hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, s, tok, ids, scale, x);
+    return ok();
+}
+
+int launch_stream_read(const void *src, size_t bytes, uint32_t *out, int grid, hipStream_t s) {
+    hipLaunchKernelGGL(k_stream_read, dim3(grid), dim3(256), 0, s, static_cast<const uint8_t *>(src), bytes >> 10,
+                       out);
     return ok();
 }
 

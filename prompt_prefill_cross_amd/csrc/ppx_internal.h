@@ -344,6 +344,7 @@ int launch_attn_1row(const Attn1Args &a, hipStream_t s);
 size_t attn1_scratch_floats(int H, int hd, int n_pos);
 
 int launch_embed(const Q4R &tok, const int32_t *ids, int M, float scale, float *x, hipStream_t s);
+int launch_stream_read(const void *src, size_t bytes, uint32_t *out, int grid, hipStream_t s);
 int launch_embed_add(const Q4R &tok, const int32_t *id, float scale, const float *base, float *x, hipStream_t s);
 // y = rmsnorm(x) * g -> fp16 in the fragment-tiled layout (the GEMM A operand).
 int launch_rmsnorm_f16(const float *x, const float *g, float eps, int M, int d, __half *out,

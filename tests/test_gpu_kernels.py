@@ -221,3 +221,16 @@ def test_attention_1row_vs_oracle(ppx, cfg, pos):
                              pos).cpu().numpy().astype(np.float64)
     ref = oracle.attention(q.astype(np.float64)[None], K, V, np.array([pos]))[0]
     assert np.all(np.abs(o - ref) <= 1e-5 * np.abs(V.astype(np.float64)).max() + 1e-5 * np.abs(ref))
+
+
+@pytest.mark.parametrize("nbytes,wg", [(1024, 1), (3072, 7), (1 << 20, 64), (5 << 20, 2048)])
+def test_stream_read_reads_every_byte(ppx, nbytes, wg):
+    """The counter-calibration read: the XOR of what it read equals the
+    buffer's XOR, so it touched every word exactly once (XOR is
+    order-free)."""
+    g = torch.Generator(device="cpu").manual_seed(nbytes)
+    host = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), generator=g, dtype=torch.int32)
+    want = int(np.bitwise_xor.reduce(host.numpy().view(np.uint32)))
+    assert ppx.stream_read(host.cuda(), n_workgroups=wg) == want
+    with pytest.raises(ppx.PPXError):
+        ppx.stream_read(torch.zeros(300, dtype=torch.int32, device="cuda"))  # not a multiple of 1 KB
