@@ -69,48 +69,266 @@ struct ACfg {
     static_assert(DEPTH * STAGE_UNITS * 16 <= 160 * 1024, "LDS");
 };
 
+// The workgroup's share of one unit: its column block, rows and cache.
+struct AttnSeg {
+    int cb, M, pos0, row0, vld;
+    const __half *kp, *vtp;
+    const int32_t *page;  // unified cache: the sequence's page table (else null)
+    int pend;             // last key any column here can see
+    int plast;            // last key written before this launch reads the cache
+    int kbeg, kend;       // the key chunk, clipped to pend
+};
+
+// false: the workgroup has nothing to do (past the unit's columns, its
+// workgroup table or its keys)
+template <int CB>
+__device__ __forceinline__ bool attn_seg(const AttnArgs &a, int ck, int G, AttnSeg &s) {
+    // the workgroup's rows: [row0, row0 + M) of the launch, one sequence's
+    // positions pos0 .. pos0 + M - 1, read against that sequence's cache
+    s.cb = blockIdx.x;
+    s.M = a.M;
+    s.pos0 = a.pos0;
+    s.row0 = 0;
+    s.vld = a.vld;
+    s.kp = a.k;
+    s.vtp = a.vt;
+    s.page = nullptr;
+    if (a.wg) {
+        if ((int)blockIdx.x >= a.nwg) return false;
+        const AttnWg &d = a.wg[blockIdx.x];
+        s.cb = d.cb;
+        s.M = d.M;
+        s.pos0 = d.pos0;
+        s.row0 = d.row0;
+        const KVRef &ref = a.seq_kv[d.seq];
+        s.kp = ref.k;
+        s.vtp = ref.vt;
+        s.vld = ref.vld;
+        s.page = ref.page;
+    } else if (s.cb * CB >= s.M * G) {
+        return false;
+    }
+    const int tmax = min(s.M - 1, (s.cb * CB + CB - 1) / G);
+    s.pend = s.pos0 + tmax;
+    s.plast = s.pos0 + s.M - 1;
+    s.kbeg = ck * a.kc;
+    if (s.kbeg > s.pend) return false;
+    s.kend = min(s.kbeg + a.kc, s.pend + 1);
+    return true;
+}
+
+// Running state of a compute wave's CPW groups of 16 query columns.
+template <int HD, int CPW>
+struct AttnRun {
+    static constexpr int KB = HD / 32, DT = HD / 16;
+    h8 qf[CPW][KB];
+    f4 oacc[CPW][DT];
+    float mrun[CPW], lrun[CPW];
+    int qpos[CPW];
+};
+
+// the unit's query column of the wave's group c (row col / G, head
+// kvh * G + col % G)
+template <int CB, int CPW>
+__device__ __forceinline__ int attn_col(int cb, int wave, int c, int lc) {
+    return cb * CB + wave * 16 * CPW + c * 16 + lc;
+}
+
+template <int HD, int CB, int CPW>
+__device__ __forceinline__ void attn_begin(const AttnArgs &a, const AttnSeg &g, int wave, int kvh, int G, int lc,
+                                           int lg, AttnRun<HD, CPW> &R) {
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+        const int col = attn_col<CB, CPW>(g.cb, wave, c, lc);
+        const int t = col / G, h = kvh * G + col % G;
+        R.qpos[c] = g.pos0 + (t < g.M ? t : 0);
+#pragma unroll
+        for (int kb = 0; kb < HD / 32; ++kb)
+            R.qf[c][kb] = *reinterpret_cast<const h8 *>(a.q + ((size_t)(g.row0 + min(t, g.M - 1)) * a.H + h) * HD +
+                                                        kb * 32 + lg * 8);
+#pragma unroll
+        for (int i = 0; i < HD / 16; ++i) R.oacc[c][i] = f4{0.f, 0.f, 0.f, 0.f};
+        R.mrun[c] = -INFINITY;
+        R.lrun[c] = 0.f;
+    }
+}
+
+// One step of 32 keys t0 .. t0 + 31.  kfrag(kb, j) is the K fragment of d
+// step kb and 16-key block j, in which lane l holds the key of accumulator
+// row 8 (r / 4) + 4 j + r % 4, r = l % 16, and dims kb*32 + 8 (l / 16) ..;
+// vfrag(i) is the V^T fragment of dims 16 i .. 16 i + 15, in which lane l
+// holds dim 16 i + l % 16, keys 8 (l / 16) .. + 7.
+//
+// The kernel computes S^T = K Q^T, so a wave's 16x16 accumulator holds keys
+// down and query columns across; with the keys in that order a lane's
+// probabilities are exactly its B operand of O^T = V^T P^T.
+//
+// Online softmax in the exp2 domain against a reference max m per column
+// (mrun): p = 2^(s log2(e) / sqrt(hd) - m), l = sum p, O = sum p v.  Any m
+// gives the same O / l; m only has to keep p finite in fp16, so it moves
+// (and O and l are rescaled by 2^(m_old - m_new)) only when a score
+// exceeds it by more than ATTN_LAZY: then p <= 2^ATTN_LAZY.  The first
+// visible key of a column always sets m.
+//
+// edge (uniform): some key of the step lies past some column's position
+// (the causal mask applies) or past the last written key (stale values are
+// zeroed); other steps skip both.
+constexpr float ATTN_LAZY = 8.0f;
+
+template <int HD, int CPW, class KF, class VF>
+__device__ __forceinline__ void attn_step32(const KF &kfrag, const VF &vfrag, int t0, int plast, int lg, bool edge,
+                                            AttnRun<HD, CPW> &R) {
+    constexpr int KB = HD / 32, DT = HD / 16;
+    const float sl2 = 1.4426950408889634f / sqrtf((float)HD);
+    // S^T = K Q^T: s[c][j][r] is key t0 + 8 lg + 4 j + r, query column lc of group c
+    f4 s[CPW][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) s[c][j] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const h8 kf = kfrag(kb, j);
+#pragma unroll
+            for (int c = 0; c < CPW; ++c) s[c][j] = mfma16(kf, R.qf[c][kb], s[c][j]);
+        }
+    }
+    h8 pf[CPW];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+        // masked scores are -inf; the max is taken on the raw scores (sl2 > 0)
+        if (edge) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (t0 + 8 * lg + 4 * j + r > R.qpos[c]) s[c][j][r] = -INFINITY;
+        }
+        float tmx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tmx = fmaxf(tmx, s[c][j][r]);
+        tmx = fmaxf(tmx, __shfl_xor(tmx, 16, 64));
+        tmx = fmaxf(tmx, __shfl_xor(tmx, 32, 64));
+        tmx *= sl2;
+        // move m only past the margin (or at the first visible key); 2^-inf
+        // = 0 covers masked keys and a column with no visible key yet, whose
+        // m stays -inf and which subtracts 0 instead
+        const bool move = tmx > R.mrun[c] + ATTN_LAZY;
+        if (__builtin_amdgcn_ballot_w64(move)) {
+            const float mnew = move ? tmx : R.mrun[c];
+            const float alpha = __builtin_amdgcn_exp2f(R.mrun[c] - mnew);  // 1 where m stays
+            R.lrun[c] *= alpha;
+#pragma unroll
+            for (int i = 0; i < DT; ++i) R.oacc[c][i] *= alpha;
+            R.mrun[c] = mnew;
+        }
+        const float msub = R.mrun[c] == -INFINITY ? 0.f : R.mrun[c];
+        float psum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][j][r], sl2, -msub));
+                psum += p;
+                pf[c][4 * j + r] = (_Float16)p;
+            }
+        psum += __shfl_xor(psum, 16, 64);
+        psum += __shfl_xor(psum, 32, 64);
+        R.lrun[c] += psum;
+    }
+    // O^T += V^T P^T over the step's 32 keys (8 lg .. 8 lg + 7 in lane group lg).
+    // Values of keys past the last written position may be stale (a cache
+    // cleared or reloaded to fewer positions keeps its old contents): they
+    // are zeroed, so a non-finite stale value cannot meet a zero weight.
+    const bool tail = edge && t0 + 31 > plast;  // uniform over the workgroup
+    const int vlim = plast - (t0 + 8 * lg);     // elements e <= vlim are written keys
+#pragma unroll
+    for (int i = 0; i < DT; ++i) {
+        h8 vf = vfrag(i);
+        if (tail) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (e > vlim) vf[e] = (_Float16)0.0f;
+        }
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) R.oacc[c][i] = mfma16(vf, pf[c], R.oacc[c][i]);
+    }
+}
+
+// A step is an edge step when one of its keys may be masked for a column of
+// the workgroup (qmin: the smallest position of its columns) or lies past
+// the last written key (plast >= every column's position).
+__device__ __forceinline__ bool attn_edge(int t0, int qmin) { return t0 + 31 > qmin; }
+
+// The chunk's result of each valid column: the normalised output when the
+// keys are not split, else the chunk's own normalised output in fp16 (a
+// convex combination of value rows, so bounded by them) with its max and
+// exp-sum in fp32; a row that sees no key of the chunk writes zeros, never read.
+template <int HD, int CB, int CPW>
+__device__ __forceinline__ void attn_finish(const AttnArgs &a, const AttnSeg &g, int ck, int wave, int kvh, int G,
+                                            int lc, int lg, const AttnRun<HD, CPW> &R) {
+    constexpr int DT = HD / 16;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+        const int col = attn_col<CB, CPW>(g.cb, wave, c, lc);
+        const int t = col / G, h = kvh * G + col % G;
+        if (t >= g.M) continue;
+        if (a.nkc == 1) {
+            const float inv = 1.0f / R.lrun[c];
+            const int od = a.H * HD;
+#pragma unroll
+            for (int i = 0; i < DT; ++i) {
+                const int d = i * 16 + lg * 4;  // four consecutive columns: 8 contiguous bytes of the tiled layout
+                h4 v;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = (_Float16)(R.oacc[c][i][r] * inv);
+                *reinterpret_cast<h4 *>(a.o + tiled_index(g.row0 + t, h * HD + d, od)) = v;
+            }
+        } else {
+            const size_t slot = ((size_t)ck * a.M + g.row0 + t) * a.H + h;
+            const float inv = R.lrun[c] > 0.f ? 1.0f / R.lrun[c] : 0.f;
+            _Float16 *po = reinterpret_cast<_Float16 *>(a.part) + slot * HD;
+#pragma unroll
+            for (int i = 0; i < DT; ++i) {
+                h4 v;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = (_Float16)(R.oacc[c][i][r] * inv);
+                *reinterpret_cast<h4 *>(po + i * 16 + lg * 4) = v;
+            }
+            if (lg == 0) {
+                // (max, sum) pairs of one (row, head) are contiguous over the chunks
+                float *pm = a.part + (size_t)a.nkc * a.M * a.H * (HD / 2) +
+                            (((size_t)(g.row0 + t) * a.H + h) * a.nkc + ck) * 2;
+                pm[0] = R.mrun[c];
+                pm[1] = R.lrun[c];
+            }
+        }
+    }
+}
+
 // Grid (column blocks, key chunks, KV heads x units): unit z / KVH of the
 // group, KV head z % KVH; a unit with fewer column blocks or key chunks than
 // the launch's largest leaves the surplus workgroups idle.
+//
+// Fragment-ordered staging: every copy instruction fills one MFMA fragment
+// (16 keys x 64 bytes of K, or 16 dims x 64 bytes of V^T), so the compute
+// waves read the ring in lane order.
 template <class C>
 __global__ __launch_bounds__(C::NT) void k_attn_prefill(const AttnGroup grp) {
-    constexpr int HD = C::HD, KB = C::KB, DT = C::DT, CPW = C::CPW;
+    constexpr int HD = C::HD, KB = C::KB, CPW = C::CPW;
     __shared__ h8 ring[C::DEPTH * C::STAGE_UNITS];
 
     const AttnArgs &a = grp.u[blockIdx.z / grp.u[0].KVH];
-    const int tid = threadIdx.x, lane = tid & 63, wave = attn_wave_id();
+    const int lane = threadIdx.x & 63, wave = attn_wave_id();
     const int G = a.H / a.KVH;
     const int ck = blockIdx.y, kvh = blockIdx.z % a.KVH;
     if (ck >= a.nkc) return;  // the whole workgroup
     const int lc = lane & 15, lg = lane >> 4;
-    // the workgroup's rows: [row0, row0 + M) of the launch, one sequence's
-    // positions pos0 .. pos0 + M - 1, read against that sequence's cache
-    int cb = blockIdx.x, M = a.M, pos0 = a.pos0, row0 = 0, vld = a.vld;
-    const __half *kp = a.k, *vtp = a.vt;
-    const int32_t *page = nullptr;  // unified cache: the sequence's page table
-    if (a.wg) {
-        if ((int)blockIdx.x >= a.nwg) return;  // past this unit's workgroup table (the whole workgroup)
-        const AttnWg &d = a.wg[blockIdx.x];
-        cb = d.cb;
-        M = d.M;
-        pos0 = d.pos0;
-        row0 = d.row0;
-        const KVRef &ref = a.seq_kv[d.seq];
-        kp = ref.k;
-        vtp = ref.vt;
-        vld = ref.vld;
-        page = ref.page;
-    } else if (cb * C::CB >= M * G) {
-        return;  // past this unit's query columns (the whole workgroup)
-    }
-
-    const int tmax = min(M - 1, (cb * C::CB + C::CB - 1) / G);
-    const int pend = pos0 + tmax;  // last key any column here can see
-    const int plast = pos0 + M - 1;  // last key written before this launch reads the cache
-    const int kbeg = ck * a.kc;
-    if (kbeg > pend) return;  // the whole workgroup
-    const int kend = min(kbeg + a.kc, pend + 1);
-    const int nst = (kend - kbeg + KT - 1) / KT;
+    AttnSeg g;
+    if (!attn_seg<C::CB>(a, ck, G, g)) return;  // the whole workgroup
+    const int nst = (g.kend - g.kbeg + KT - 1) / KT;
 
     if (wave >= C::NC) {
         // ---- producers: wave NC + p issues DMAs p, p + NP, ... of every stage.
@@ -123,32 +341,30 @@ __global__ __launch_bounds__(C::NT) void k_attn_prefill(const AttnGroup grp) {
         for (int t = 0; t < C::PER; ++t) {
             const int e = entry(t);
             if (e < 2 * KB) {
-                // fragment (d step kb, key block j): lane l holds the key of accumulator row
-                // 8 (r / 4) + 4 j + r % 4, r = l % 16, and dims kb*32 + 8 (l / 16) ..
                 const int j = e & 1;
                 koff[t] = 8 * ((lane & 15) >> 2) + 4 * j + (lane & 3);
             } else {
                 // V^T subtile i: lane l holds dim 16 i + l % 16, keys 8 (l / 16) .. + 7
                 const int i = e - 2 * KB;
-                koff[t] = (kvh * HD + i * 16 + (lane & 15)) * vld + 8 * (lane >> 4);
+                koff[t] = (kvh * HD + i * 16 + (lane & 15)) * g.vld + 8 * (lane >> 4);
             }
         }
         auto issue = [&](int sb) {
             h8 *st = ring + (sb % C::DEPTH) * C::STAGE_UNITS;
-            const int t0 = kbeg + min(sb, nst - 1) * KT;  // past the end: repeats keep the count uniform
+            const int t0 = g.kbeg + min(sb, nst - 1) * KT;  // past the end: repeats keep the count uniform
             // the stage's keys t0 .. t0 + KT - 1 (and the clamp target plast >= t0)
             // lie in one page: cells c0 + (key - t0)
-            const int c0 = kv_cell(page, t0);
+            const int c0 = kv_cell(g.page, t0);
 #pragma unroll
             for (int t = 0; t < C::PER; ++t) {
                 const int e = entry(t);
                 if (e < 2 * KB) {
                     const int kb = e >> 1;
-                    const int key = min(t0 + koff[t], plast);
-                    adma16(kp + ((size_t)(c0 + key - t0) * a.KVH + kvh) * HD + kb * 32 + 8 * (lane >> 4),
+                    const int key = min(t0 + koff[t], g.plast);
+                    adma16(g.kp + ((size_t)(c0 + key - t0) * a.KVH + kvh) * HD + kb * 32 + 8 * (lane >> 4),
                            st + e * 64);
                 } else {
-                    adma16(vtp + (size_t)koff[t] + c0, st + C::K_UNITS + (e - 2 * KB) * 64);
+                    adma16(g.vtp + (size_t)koff[t] + c0, st + C::K_UNITS + (e - 2 * KB) * 64);
                 }
             }
         };
@@ -166,149 +382,19 @@ __global__ __launch_bounds__(C::NT) void k_attn_prefill(const AttnGroup grp) {
 
     // ---- compute waves: CPW groups of 16 query columns; every K / V^T
     // fragment read from LDS feeds one MFMA per group
-    int t[CPW], h[CPW], qpos[CPW];
-    bool valid[CPW];
-    h8 qf[CPW][KB];
-#pragma unroll
-    for (int c = 0; c < CPW; ++c) {
-        const int col = cb * C::CB + wave * 16 * CPW + c * 16 + lc;
-        t[c] = col / G;
-        valid[c] = t[c] < M;
-        h[c] = kvh * G + col % G;
-        qpos[c] = pos0 + (valid[c] ? t[c] : 0);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-            qf[c][kb] = *reinterpret_cast<const h8 *>(a.q + ((size_t)(row0 + min(t[c], M - 1)) * a.H + h[c]) * HD +
-                                                      kb * 32 + lg * 8);
-    }
-
-    f4 oacc[CPW][DT];
-#pragma unroll
-    for (int c = 0; c < CPW; ++c)
-#pragma unroll
-        for (int i = 0; i < DT; ++i) oacc[c][i] = f4{0.f, 0.f, 0.f, 0.f};
-    float mrun[CPW], lrun[CPW];
-#pragma unroll
-    for (int c = 0; c < CPW; ++c) {
-        mrun[c] = -INFINITY;
-        lrun[c] = 0.f;
-    }
-    const float sl2 = 1.4426950408889634f / sqrtf((float)HD);
-
+    AttnRun<HD, CPW> R;
+    attn_begin<HD, C::CB, CPW>(a, g, wave, kvh, G, lc, lg, R);
+    const int qmin = g.pos0 + g.cb * C::CB / G;
     for (int it = 0; it < nst; ++it) {
         attn_barrier();  // stage it has landed
-        const int t0 = kbeg + it * KT;
         const h8 *st = ring + (it % C::DEPTH) * C::STAGE_UNITS + lane;
-
-        // S^T = K Q^T: s[c][j][r] is key t0 + 8 lg + 4 j + r, query column lc of group c
-        f4 s[CPW][2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-#pragma unroll
-            for (int c = 0; c < CPW; ++c) s[c][j] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const h8 kf = st[(kb * 2 + j) * 64];
-#pragma unroll
-                for (int c = 0; c < CPW; ++c) s[c][j] = mfma16(kf, qf[c][kb], s[c][j]);
-            }
-        }
-        h8 pf[CPW];
-#pragma unroll
-        for (int c = 0; c < CPW; ++c) {
-            float tmx = -INFINITY;
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int kp = t0 + 8 * lg + 4 * j + r;
-                    const float v = (kp <= qpos[c]) ? s[c][j][r] * sl2 : -INFINITY;
-                    s[c][j][r] = v;
-                    tmx = fmaxf(tmx, v);
-                }
-            tmx = fmaxf(tmx, __shfl_xor(tmx, 16, 64));
-            tmx = fmaxf(tmx, __shfl_xor(tmx, 32, 64));
-            // hardware 2^x: 2^-inf = 0 covers masked keys; a column with no
-            // visible key yet keeps max -inf and subtracts 0 instead
-            const float mnew = fmaxf(mrun[c], tmx);
-            const float msub = mnew == -INFINITY ? 0.f : mnew;
-            const float alpha = __builtin_amdgcn_exp2f(mrun[c] - msub);
-            float psum = 0.f;
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(s[c][j][r] - msub);
-                    psum += p;
-                    pf[c][4 * j + r] = (_Float16)p;
-                }
-            psum += __shfl_xor(psum, 16, 64);
-            psum += __shfl_xor(psum, 32, 64);
-            lrun[c] = lrun[c] * alpha + psum;
-            mrun[c] = mnew;
-            // rescale the output only when some column's max moved this stage
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-                for (int i = 0; i < DT; ++i) oacc[c][i] *= alpha;
-            }
-        }
-        // O^T += V^T P^T over the stage's 32 keys (8 lg .. 8 lg + 7 in lane group lg).
-        // Values of keys past the last written position may be stale (a cache
-        // cleared or reloaded to fewer positions keeps its old contents): they
-        // are zeroed, so a non-finite stale value cannot meet a zero weight.
-        const int vlim = plast - (t0 + 8 * lg);  // elements e <= vlim are written keys
-        const bool tail = t0 + KT - 1 > plast;   // uniform over the workgroup
-#pragma unroll
-        for (int i = 0; i < DT; ++i) {
-            h8 vf = st[C::K_UNITS + i * 64];
-            if (tail) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (e > vlim) vf[e] = (_Float16)0.0f;
-            }
-#pragma unroll
-            for (int c = 0; c < CPW; ++c) oacc[c][i] = mfma16(vf, pf[c], oacc[c][i]);
-        }
+        const int t0 = g.kbeg + it * KT;
+        auto kfrag = [&](int kb, int j) { return st[(kb * 2 + j) * 64]; };
+        auto vfrag = [&](int i) { return st[C::K_UNITS + i * 64]; };
+        attn_step32<HD, CPW>(kfrag, vfrag, t0, g.plast, lg, attn_edge(t0, qmin), R);
     }
     attn_barrier();  // matches the producers' last barrier
-
-#pragma unroll
-    for (int c = 0; c < CPW; ++c) {
-        if (!valid[c]) continue;
-        if (a.nkc == 1) {
-            const float inv = 1.0f / lrun[c];
-            const int od = a.H * HD;
-#pragma unroll
-            for (int i = 0; i < DT; ++i) {
-                const int d = i * 16 + lg * 4;  // four consecutive columns: 8 contiguous bytes of the tiled layout
-                h4 v;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) v[r] = (_Float16)(oacc[c][i][r] * inv);
-                *reinterpret_cast<h4 *>(a.o + tiled_index(row0 + t[c], h[c] * HD + d, od)) = v;
-            }
-        } else {
-            // the chunk's own normalised output in fp16 (a convex combination of
-            // value rows, so bounded by them), its max and exp-sum in fp32; a
-            // row that sees no key of the chunk writes zeros, never read
-            const size_t slot = ((size_t)ck * a.M + row0 + t[c]) * a.H + h[c];
-            const float inv = lrun[c] > 0.f ? 1.0f / lrun[c] : 0.f;
-            _Float16 *po = reinterpret_cast<_Float16 *>(a.part) + slot * HD;
-#pragma unroll
-            for (int i = 0; i < DT; ++i) {
-                h4 v;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) v[r] = (_Float16)(oacc[c][i][r] * inv);
-                *reinterpret_cast<h4 *>(po + i * 16 + lg * 4) = v;
-            }
-            if (lg == 0) {
-                // (max, sum) pairs of one (row, head) are contiguous over the chunks
-                float *pm = a.part + (size_t)a.nkc * a.M * a.H * (HD / 2) +
-                            (((size_t)(row0 + t[c]) * a.H + h[c]) * a.nkc + ck) * 2;
-                pm[0] = mrun[c];
-                pm[1] = lrun[c];
-            }
-        }
-    }
+    attn_finish<HD, C::CB, CPW>(a, g, ck, wave, kvh, G, lc, lg, R);
 }
 
 // Combine the key chunks of row t, head h: chunks 0..floor(pos/kc) hold keys
