@@ -399,63 +399,59 @@ __global__ __launch_bounds__(C::NT) void k_attn_prefill(const AttnGroup grp) {
 
 // Combine the key chunks of row t, head h: chunks 0..floor(pos/kc) hold keys
 // the row can see.  Chunk c contributes its normalised output with weight
-// l_c 2^(m_c - M) (max-subtracted, in the exp2 domain of the kernel).  One
-// wave per (row, head): lane l owns dims 4l .. 4l+3 of each 256-dim slice;
-// the chunks are summed in chunk order.
+// l_c 2^(m_c - M), M = max_c m_c (the exp2 domain of the kernel); the chunks
+// are summed in chunk order.  One workgroup per row of a unit (grid (rows,
+// units)): thread i takes head hb + i / TPH of each pass and dims 8 (i % TPH)
+// .. + 7 (TPH = HD / 8 threads per head), so the row's whole output is one
+// pass of 16-byte reads; each thread requests the slices of its first
+// MERGE_CU chunks before it reads the chunks' (max, sum) pairs.
+constexpr int MERGE_CU = 8;
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn_prefill_merge(const AttnGroup grp) {
-    static_assert(ATTN_MAX_CHUNKS <= 64, "one chunk per lane");
+    constexpr int TPH = HD / 8, HPP = 256 / TPH;  // threads per head, heads per pass
     const AttnArgs &a = grp.u[blockIdx.y];
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
-    if (w >= a.M * a.H) return;
-    const int t = w / a.H, h = w % a.H;
+    const int t = blockIdx.x;
+    if (t >= a.M) return;  // past this unit's rows (the whole workgroup)
     const int nch = (a.row_pos ? a.row_pos[t] : a.pos0 + t) / a.kc + 1;
-    const _Float16 *po = reinterpret_cast<const _Float16 *>(a.part);
-    const float *pm = a.part + (size_t)a.nkc * a.M * a.H * (HD / 2) + (size_t)w * a.nkc * 2;
-    // lane c holds chunk c's weight l_c 2^(m_c - M)
-    const bool own = lane < nch;
-    const float mc = own ? pm[2 * lane] : -INFINITY;
-    const float lc = own ? pm[2 * lane + 1] : 0.f;
-    const float M = wave_max(mc);
-    const float wl = own ? exp2f(mc - M) * lc : 0.f;
-    constexpr int NV = (HD + 255) / 256;  // four dims per lane per slice
     const size_t cstride = (size_t)a.M * a.H * HD;  // fp16 elements per chunk
-    const _Float16 *base = po + (size_t)w * HD;
-    f4 O[NV];
+    const int dh = (threadIdx.x % TPH) * 8;
+    for (int hb = 0; hb < a.H; hb += HPP) {
+        const int h = hb + (int)threadIdx.x / TPH;
+        if (h >= a.H) break;
+        const size_t w = (size_t)t * a.H + h;
+        const float *pm = a.part + (size_t)a.nkc * a.M * a.H * (HD / 2) + w * a.nkc * 2;
+        const _Float16 *base = reinterpret_cast<const _Float16 *>(a.part) + w * HD + dh;
+        h8 x[MERGE_CU];
+        auto load = [&](int c0) {
+            // chunks past the last repeat it (weight 0 below), so every load issues at once
 #pragma unroll
-    for (int v = 0; v < NV; ++v) O[v] = f4{0.f, 0.f, 0.f, 0.f};
-    float L = 0.f;
-    // eight chunks' loads in flight at a time; the sums stay in chunk order
-    for (int c0 = 0; c0 < nch; c0 += 8) {
-        h4 x[8][NV];
+            for (int u = 0; u < MERGE_CU; ++u)
+                x[u] = *reinterpret_cast<const h8 *>(base + (size_t)min(c0 + u, nch - 1) * cstride);
+        };
+        load(0);
+        float M = -INFINITY;
+        for (int c = 0; c < nch; ++c) M = fmaxf(M, pm[2 * c]);
+        float O[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, L = 0.f;
+        for (int c0 = 0; c0 < nch; c0 += MERGE_CU) {
+            if (c0) load(c0);
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+            for (int u = 0; u < MERGE_CU; ++u) {
+                const int c = min(c0 + u, nch - 1);
+                const float wg = c0 + u < nch ? exp2f(pm[2 * c] - M) * pm[2 * c + 1] : 0.f;
+                L += wg;
 #pragma unroll
-            for (int v = 0; v < NV; ++v)
-                x[u][v] = *reinterpret_cast<const h4 *>(base + (size_t)min(c0 + u, nch - 1) * cstride +
-                                                        min(v * 256 + lane * 4, HD - 4));
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            // chunks past the last repeat it with weight 0 (no branch, so every load above issues at once)
-            const float wg = c0 + u < nch ? __shfl(wl, c0 + u, 64) : 0.f;
-            L += wg;
-#pragma unroll
-            for (int v = 0; v < NV; ++v)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) O[v][e] += wg * (float)x[u][v][e];
+                for (int e = 0; e < 8; ++e) O[e] += wg * (float)x[u][e];
+            }
         }
-    }
-    const float inv = 1.0f / L;
+        const float inv = 1.0f / L;
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-        const int d = v * 256 + lane * 4;
-        if (d >= HD) continue;
-        h4 r;
+        for (int q = 0; q < 2; ++q) {
+            h4 r;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = (_Float16)(O[v][e] * inv);
-        // four consecutive dims: 8 contiguous bytes of the tiled layout
-        *reinterpret_cast<h4 *>(a.o + tiled_index(t, h * HD + d, a.H * HD)) = r;
+            for (int e = 0; e < 4; ++e) r[e] = (_Float16)(O[4 * q + e] * inv);
+            // four consecutive dims: 8 contiguous bytes of the tiled layout
+            *reinterpret_cast<h4 *>(a.o + tiled_index(t, h * HD + dh + 4 * q, a.H * HD)) = r;
+        }
     }
 }
 
@@ -838,10 +834,10 @@ int launch_attn_prefill_group(const AttnArgs *units, int n, hipStream_t s) {
     for (int i = 0; i < g.n; ++i)
         if (g.u[i].nkc > 1) {
             mg.u[mg.n++] = g.u[i];
-            mrows = std::max(mrows, g.u[i].M * g.u[i].H);
+            mrows = std::max(mrows, g.u[i].M);
         }
     if (!mg.n) return PPX_OK;
-    const dim3 mgrid((mrows + 3) / 4, mg.n);
+    const dim3 mgrid(mrows, mg.n);  // one workgroup per row
     switch (a0.hd) {
     case 64: hipLaunchKernelGGL(k_attn_prefill_merge<64>, mgrid, dim3(256), 0, s, mg); break;
     case 128: hipLaunchKernelGGL(k_attn_prefill_merge<128>, mgrid, dim3(256), 0, s, mg); break;
