@@ -208,6 +208,43 @@ def test_attention_prefill_flat_softmax_vs_oracle(ppx, M, pos0):
     assert np.all(err <= 2e-3 * scale), float(err.max() / scale)
 
 
+@pytest.mark.parametrize("M,pos0", [(512, 4096), (64, 8128)])
+def test_attention_prefill_late_max_vs_oracle(ppx, M, pos0):
+    """Scores that jump late: q = u + noise and k ~ N(0, 0.05^2) give flat
+    scores, except two planted keys along u whose scaled scores (log2 units)
+    stand about 11 and 22 above the rest -- past the kernel's margin of 8 for
+    moving its reference max, deep in a long context and in different key
+    chunks: the first is seen by every row, the second only by the rows at or
+    after it.  Both the planted key and the thousands of flat keys carry
+    weight in the result, so a wrong rescale of either shows."""
+    mm = engine_model(ppx, "e2b")
+    I = mm.info
+    H, KVH, hd = I["n_head"], I["n_kv_head"], I["head_dim"]
+    rng = np.random.default_rng(M + pos0 + 2)
+    P = pos0 + M
+    u = np.full(hd, 0.5)
+    q = (u + 0.05 * rng.standard_normal((M, H, hd))).astype(np.float16)
+    K = (0.05 * rng.standard_normal((P, KVH, hd))).astype(np.float16)
+    V = (6 * rng.standard_normal((P, KVH, hd))).astype(np.float16)
+    # q . k / sqrt(hd) * log2(e) = alpha * |u|^2 / 16 * 1.4427 ~ 5.77 alpha
+    early, late = pos0 - 700, pos0 + M // 2
+    K[early] = (1.9 * u).astype(np.float16)
+    K[late] = (3.8 * u).astype(np.float16)
+    o = mm.op_attention(torch.from_numpy(q).cuda(), torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda(), pos0)
+    o = o.cpu().numpy().astype(np.float64)
+    ref = oracle.attention(q.astype(np.float64), K, V, pos0 + np.arange(M))
+    # the planted keys hold a share of the weight well inside (0, 1) for the rows before the late key
+    qf = q.astype(np.float64)
+    s = qf @ K.astype(np.float64)[:pos0 + 1, 0].T / np.sqrt(hd)
+    pr = np.exp(s - s.max(axis=-1, keepdims=True))
+    share = pr[..., early] / pr.sum(axis=-1)
+    assert 0.05 < share.min() and share.max() < 0.95, (share.min(), share.max())
+    bound = 2e-3 * np.abs(V.astype(np.float64)).max() + 1e-3 * np.abs(ref)
+    err = np.abs(o - ref)
+    print(f"late max M={M} keys<={P}: max err {err.max():.2e}, planted share {share.min():.2f}..{share.max():.2f}")
+    assert np.all(err <= bound), float(err.max())
+
+
 @pytest.mark.parametrize("cfg,pos", [("tiny", 0), ("tiny", 63), ("tinyllama", 511), ("e2b", 2047), ("e2b", 100)])
 def test_attention_1row_vs_oracle(ppx, cfg, pos):
     mm = engine_model(ppx, cfg)
