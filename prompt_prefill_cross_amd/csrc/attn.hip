@@ -397,6 +397,141 @@ __global__ __launch_bounds__(C::NT) void k_attn_prefill(const AttnGroup grp) {
     attn_finish<HD, C::CB, CPW>(a, g, ck, wave, kvh, G, lc, lg, R);
 }
 
+// Line-wide staging (head_dim 128 and 256).  A copy instruction that fills
+// a fragment reads 16 pieces of 64 bytes, and the vector memory path serves
+// such pieces at a quarter of the rate of whole 128-byte lines; here every
+// copy instruction reads whole lines instead: KW / 64 whole K rows (KW =
+// 2 * head_dim bytes), or 8 V^T rows of one stage's 64 keys (128 bytes each,
+// a line: cells of a stage are 64-aligned).  The ring holds the rows as they
+// are, in 16-byte slots permuted by an XOR with a function of the row, so
+// that the MFMA fragment reads (16 lanes on distinct rows at one slot) run
+// at the rate of contiguous reads -- both permutations were picked by timing
+// ds_read_b128 patterns on the chip (rows of 128 bytes at one slot, or with
+// the slot XORed by (row & 7) ^ (row >> 3 & 1), read at two thirds of it):
+//   K row k (key t0 + k), slot s holds the row's slot s ^ sigma(k),
+//       sigma(k) = (k & 3) | ((k >> 3) & 3) << 2;
+//   V^T row d (dim d), slot s holds keys t0 + 8 (s ^ tau(d)) .. + 7,
+//       tau(d) = d & 7.
+// A stage is 64 keys (two steps of 32); two stages fill the ring.  NC
+// compute waves of CPW groups of 16 query columns; NP producer waves, or
+// none (NP = 0): the compute waves then issue the copies themselves.
+template <int HD_, int NC_, int CPW_, int NP_>
+struct WCfg {
+    static constexpr int HD = HD_, NC = NC_, CPW = CPW_, NP = NP_, DEPTH = 2, KS = 64;
+    static constexpr int ROW = HD / 8;                // 16-byte slots per K row
+    static constexpr int K_UNITS = KS * ROW;          // 16-byte units
+    static constexpr int V_UNITS = HD * (KS / 8);
+    static constexpr int STAGE_UNITS = K_UNITS + V_UNITS;
+    static constexpr int K_INSTR = K_UNITS / 64, V_INSTR = V_UNITS / 64;
+    static constexpr int DMA_STAGE = K_INSTR + V_INSTR;
+    static constexpr int NI = NP ? NP : NC;  // waves that issue the copies
+    static constexpr int PER = DMA_STAGE / NI;
+    static constexpr int NT = 64 * (NC + NP);
+    static constexpr int CB = 16 * CPW * NC;
+    static_assert(ROW >= 16 && 64 % ROW == 0, "whole K rows per copy instruction; sigma < ROW");
+    static_assert(DMA_STAGE % NI == 0 && PER <= 63, "copies per issuing wave");
+    static_assert(DEPTH * STAGE_UNITS * 16 <= 160 * 1024, "LDS");
+    static_assert(kKvPage % KS == 0, "a stage's keys lie in one page of a unified cache");
+};
+
+__device__ __forceinline__ int attn_sigma(int k) { return (k & 3) | (((k >> 3) & 3) << 2); }
+__device__ __forceinline__ int attn_tau(int d) { return d & 7; }
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void k_attn_prefill_w(const AttnGroup grp) {
+    constexpr int HD = C::HD, ROW = C::ROW, KS = C::KS;
+    __shared__ h8 ring[C::DEPTH * C::STAGE_UNITS];
+
+    const AttnArgs &a = grp.u[blockIdx.z / grp.u[0].KVH];
+    const int lane = threadIdx.x & 63, wave = attn_wave_id();
+    const int G = a.H / a.KVH;
+    const int ck = blockIdx.y, kvh = blockIdx.z % a.KVH;
+    if (ck >= a.nkc) return;  // the whole workgroup
+    const int lc = lane & 15, lg = lane >> 4;
+    AttnSeg g;
+    if (!attn_seg<C::CB>(a, ck, G, g)) return;  // the whole workgroup
+    const int nst = (g.kend - g.kbeg + KS - 1) / KS;
+
+    // ---- copies: issuing wave p (producer NC + p, or compute wave p when NP
+    // = 0) issues copies p, p + NI, ... of every stage (K instructions first,
+    // then V^T).  K rows past the last written position repeat it (their
+    // scores are masked); V^T reads stay inside the row (vld is a multiple of 64).
+    const int pw = C::NP ? wave - C::NC : wave;
+    const int kx = lane / ROW, ks = lane % ROW;  // K: row within the instruction, slot
+    const int vr = lane >> 3, vs = lane & 7;     // V^T: row within the instruction, slot
+    auto issue = [&](int sb) {
+        h8 *st = ring + (sb % C::DEPTH) * C::STAGE_UNITS;
+        const int t0 = g.kbeg + min(sb, nst - 1) * KS;  // past the end: repeats keep the count uniform
+        // the stage's keys t0 .. t0 + 63 (and the clamp target plast >= t0)
+        // lie in one page: cells c0 + (key - t0)
+        const int c0 = kv_cell(g.page, t0);
+#pragma unroll
+        for (int t = 0; t < C::PER; ++t) {
+            const int e = t * C::NI + pw;
+            if (e < C::K_INSTR) {
+                const int k = e * (64 / ROW) + kx;
+                const int key = min(t0 + k, g.plast);
+                adma16(g.kp + ((size_t)(c0 + key - t0) * a.KVH + kvh) * HD + 8 * (ks ^ attn_sigma(k)), st + e * 64);
+            } else {
+                const int d = (e - C::K_INSTR) * 8 + vr;
+                adma16(g.vtp + (size_t)(kvh * HD + d) * g.vld + c0 + 8 * (vs ^ attn_tau(d)), st + e * 64);
+            }
+        }
+    };
+    if (C::NP > 0 && wave >= C::NC) {
+        // ---- producers
+#pragma unroll
+        for (int s = 0; s < C::DEPTH - 1; ++s) issue(s);
+        for (int s = 0; s < nst; ++s) {
+            attn_wait_vm<(C::DEPTH - 2) * C::PER>();  // this wave's share of stage s has landed
+            attn_barrier();
+            issue(s + C::DEPTH - 1);  // into the buffer of stage s - 1, already consumed
+        }
+        attn_wait_vm<0>();
+        attn_barrier();
+        return;
+    }
+
+    // ---- compute waves: CPW groups of 16 query columns each
+    constexpr int CPW = C::CPW;
+    AttnRun<HD, CPW> R;
+    attn_begin<HD, C::CB, CPW>(a, g, wave, kvh, G, lc, lg, R);
+    // the lane's ring offsets: K block j (keys 8 (r / 4) + 4 j + r % 4 of a
+    // step, r = lane % 16) at d step kb reads row slot (4 kb + lg) ^ sigma,
+    // = 16 (kb / 4) + kofs[j][kb % 4] within the row (sigma < 16 leaves bit 2
+    // of kb alone); V^T subtile i reads row 16 i + lc at slot (4 h + lg) ^ tau
+    // for step h, = 128 i + vofs[h] (tau(16 i + lc) = tau(lc)).  What varies
+    // with kb / 4, i and h goes into the read's immediate offset.
+    int kofs[2][4], vofs[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int k = 8 * (lc >> 2) + 4 * j + (lc & 3), sg = attn_sigma(k);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) kofs[j][b] = k * ROW + 4 * (b ^ (sg >> 2)) + (lg ^ (sg & 3));
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) vofs[h] = C::K_UNITS + lc * 8 + ((4 * h + lg) ^ attn_tau(lc));
+    const int qmin = g.pos0 + g.cb * C::CB / G;
+    static_assert(C::NP > 0 || C::DEPTH == 2, "compute waves that copy keep one stage in flight");
+    if (C::NP == 0) issue(0);
+    for (int it = 0; it < nst; ++it) {
+        if (C::NP == 0) attn_wait_vm<0>();  // this wave's copies of stage it have landed
+        attn_barrier();  // stage it has landed (and stage it - 1 is consumed)
+        if (C::NP == 0 && it + 1 < nst) issue(it + 1);  // into stage it - 1's buffer
+        const h8 *st = ring + (it % C::DEPTH) * C::STAGE_UNITS;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int t0 = g.kbeg + it * KS + 32 * h;
+            if (t0 > g.pend) break;  // every key of the step is masked for every column: no change
+            auto kfrag = [&](int kb, int j) { return st[kofs[j][kb & 3] + 16 * (kb >> 2) + 32 * h * ROW]; };
+            auto vfrag = [&](int i) { return st[vofs[h] + 128 * i]; };
+            attn_step32<HD, CPW>(kfrag, vfrag, t0, g.plast, lg, attn_edge(t0, qmin), R);
+        }
+    }
+    attn_barrier();  // matches the producers' last barrier
+    attn_finish<HD, C::CB, CPW>(a, g, ck, wave, kvh, G, lc, lg, R);
+}
+
 // Combine the key chunks of row t, head h: chunks 0..floor(pos/kc) hold keys
 // the row can see.  Chunk c contributes its normalised output with weight
 // l_c 2^(m_c - M), M = max_c m_c (the exp2 domain of the kernel); the chunks
@@ -821,10 +956,18 @@ int launch_attn_prefill_group(const AttnArgs *units, int n, hipStream_t s) {
         hipLaunchKernelGGL((k_attn_prefill<C>), grid, dim3(C::NT), 0, s, g);                         \
         break;                                                                                       \
     }
+#define PPX_ATTN_W(hd_, nc_, cpw_, np_)                                                              \
+    case hd_: {                                                                                      \
+        using C = WCfg<hd_, nc_, cpw_, np_>;                                                         \
+        static_assert(C::CB == ATTN_CB, "query columns per workgroup");                              \
+        hipLaunchKernelGGL((k_attn_prefill_w<C>), grid, dim3(C::NT), 0, s, g);                       \
+        break;                                                                                       \
+    }
         PPX_ATTN(64, 1, 8)
         PPX_ATTN(128, 2, 6)
-        PPX_ATTN(256, 2, 4)
+        PPX_ATTN_W(256, 8, 1, 4)
 #undef PPX_ATTN
+#undef PPX_ATTN_W
     default: return PPX_E_UNSUPPORTED;
     }
     if (hipGetLastError() != hipSuccess) return PPX_E_HIP;
