@@ -93,7 +93,9 @@ def test_gemm_vs_oracle(ppx, cfg, M):
 
 
 @pytest.mark.parametrize("cfg,M,layer", [("tiny", 64, 3), ("tiny", 9, 0), ("tinyllama", 512, 21), ("tinyllama", 131, 4),
-                                         ("e2b", 512, 14), ("e2b", 333, 30)])
+                                         ("e2b", 512, 14), ("e2b", 333, 30),
+                                         # more rows than a ubatch, ragged tiles
+                                         ("tiny", 600, 1), ("tinyllama", 1100, 7), ("e2b", 1300, 2)])
 def test_gemm_glu_vs_oracle(ppx, cfg, M, layer):
     """Fused gate|up GEMM + activation: g and u carry the GEMM bound
     e = 1e-3 sum|a w| each; the activation's slope is below 1.2 for both GeGLU
@@ -116,6 +118,21 @@ def test_gemm_glu_vs_oracle(ppx, cfg, M, layer):
     bound = 1.2 * np.abs(u) * eg + (np.abs(act) + 1.2 * eg) * eu + 0.5 * ulp16(ref)
     err = np.abs(h - ref)
     assert np.all(err <= bound), float((err / bound).max())
+
+
+def test_gemm_glu_rows_independent_of_launch(ppx):
+    """A row's result does not depend on the rows that share its launch (the
+    tile plan does not depend on M, and each 16-row tile is summed alone):
+    2048 and 1300 rows in one launch against launches of 512 rows, bit for
+    bit.  The lockstep ubatches of the prefill rest on this."""
+    mm = engine_model(ppx, "e2b")
+    rng = np.random.default_rng(77)
+    for M in (2048, 1300):
+        a = torch.from_numpy(rng.standard_normal((M, 1536)).astype(np.float16)).cuda()
+        whole = mm.op_gemm_glu("blk.1.ffn_gate", a)
+        for r0 in range(0, M, 512):
+            part = mm.op_gemm_glu("blk.1.ffn_gate", a[r0:r0 + 512].contiguous())
+            assert torch.equal(whole[r0:r0 + 512], part), (M, r0)
 
 
 def test_gemm_glu_rejects_plain_tensor(ppx):
