@@ -218,7 +218,8 @@ __device__ __forceinline__ void attn_step32(const KF &kfrag, const VF &vfrag, in
         const bool move = tmx > R.mrun[c] + ATTN_LAZY;
         if (__builtin_amdgcn_ballot_w64(move)) {
             const float mnew = move ? tmx : R.mrun[c];
-            const float alpha = __builtin_amdgcn_exp2f(R.mrun[c] - mnew);  // 1 where m stays
+            // 1 where m stays; against 0 while m is -inf (O and l are 0 then), never 2^(-inf + inf)
+            const float alpha = __builtin_amdgcn_exp2f(R.mrun[c] - (mnew == -INFINITY ? 0.f : mnew));
             R.lrun[c] *= alpha;
 #pragma unroll
             for (int i = 0; i < DT; ++i) R.oacc[c][i] *= alpha;
