@@ -889,10 +889,9 @@ AttnSplit attn_split_cols(int colblocks, int KVH, int P) {
     return sp;
 }
 
-// Key split of one unit of a launch whose units hold tot_cb column blocks
-// and KV heads together: chunks enough for about ATTN_WG_TARGET workgroups
-// over the launch (fewer chunks, less partial traffic and merging, when
-// several ubatches share it).
+// Key split of a launch's only unit, whose column blocks and KV heads number
+// tot_cb: chunks enough for about ATTN_WG_TARGET workgroups (a launch of
+// several units takes attn_common_kc).
 constexpr int ATTN_WG_TARGET = 256;
 AttnSplit attn_split_group(int P, int tot_cb) {
     int want = (ATTN_WG_TARGET + tot_cb - 1) / tot_cb;
@@ -903,6 +902,33 @@ AttnSplit attn_split_group(int P, int tot_cb) {
     sp.kc = kc;
     sp.nkc = (P + kc - 1) / kc;
     return sp;
+}
+
+// One key-chunk length for every unit of a launch: the shortest (a multiple
+// of 64, at least ATTN_MIN_KC) whose chunks over all the units' column
+// blocks number at most ATTN_WG_TARGET workgroups, each unit at most
+// ATTN_MAX_CHUNKS chunks.  A workgroup then never holds more keys than
+// that length, so the units further into the prompt (more keys) take more
+// workgroups rather than longer ones; splitting each unit into the same
+// number of chunks instead let the last unit's workgroups run up to four
+// times as long as the first unit's.  A launch of one unit gets the split
+// of attn_split_group.  cb[i], P[i]: column blocks (KV heads included) and
+// keys of unit i.
+int attn_common_kc(const int *cb, const int *P, int n) {
+    int pmax = ATTN_MIN_KC;
+    for (int i = 0; i < n; ++i) pmax = std::max(pmax, P[i]);
+    const int top = (pmax + 63) / 64 * 64;
+    for (int kc = ATTN_MIN_KC; kc < top; kc += 64) {
+        long wgs = 0;
+        bool fits = true;
+        for (int i = 0; i < n && fits; ++i) {
+            const int nk = (P[i] + kc - 1) / kc;
+            fits = nk <= ATTN_MAX_CHUNKS;
+            wgs += (long)cb[i] * nk;
+        }
+        if (fits && wgs <= ATTN_WG_TARGET) return kc;
+    }
+    return top;
 }
 
 int attn_prefill_cols_per_wg(int hd) {
@@ -917,10 +943,15 @@ size_t attn_prefill_scratch_floats(int M, int H, int hd, int n_ctx) {
 int launch_attn_prefill_group(const AttnArgs *units, int n, hipStream_t s) {
     if (n < 1 || n > kMaxUnits) return PPX_E_INVAL;
     AttnGroup g;
-    int nx = 0, ny = 0, tot_cb = 0;
+    int nx = 0, ny = 0;
+    // the common key-chunk length of the single-sequence units
+    int ucb[kMaxUnits], uP[kMaxUnits], nu = 0;
     for (int i = 0; i < n; ++i)
-        if (units[i].M > 0 && !units[i].wg && units[i].KVH > 0)
-            tot_cb += (units[i].M * (units[i].H / units[i].KVH) + ATTN_CB - 1) / ATTN_CB * units[i].KVH;
+        if (units[i].M > 0 && !units[i].wg && units[i].KVH > 0) {
+            ucb[nu] = (units[i].M * (units[i].H / units[i].KVH) + ATTN_CB - 1) / ATTN_CB * units[i].KVH;
+            uP[nu++] = units[i].pos0 + units[i].M;
+        }
+    const int kc_all = nu > 1 ? attn_common_kc(ucb, uP, nu) : 0;
     for (int i = 0; i < n; ++i) {
         AttnArgs a = units[i];
         if (a.M <= 0) continue;
@@ -937,9 +968,14 @@ int launch_attn_prefill_group(const AttnArgs *units, int n, hipStream_t s) {
             x = a.nwg;
         } else {
             if (a.vld % 64 || a.pos0 + a.M > a.vld) return PPX_E_UNSUPPORTED;
-            const AttnSplit sp = attn_split_group(a.pos0 + a.M, std::max(tot_cb, 1));
-            a.kc = sp.kc;
-            a.nkc = sp.nkc;
+            if (kc_all) {
+                a.kc = kc_all;
+                a.nkc = (a.pos0 + a.M + kc_all - 1) / kc_all;
+            } else {
+                const AttnSplit sp = attn_split_group(a.pos0 + a.M, std::max(nu ? ucb[0] : 1, 1));
+                a.kc = sp.kc;
+                a.nkc = sp.nkc;
+            }
             x = (a.M * G + ATTN_CB - 1) / ATTN_CB;
         }
         if (a.nkc > 1 && !a.part) return PPX_E_INVAL;
