@@ -908,6 +908,11 @@ int launch_gemm_exact_group(const GemmArgs *units, int n, hipStream_t s) {
         if (!u.A || !u.A2) return PPX_E_UNSUPPORTED;
     }
     if (a.W.N % 64 || a.W.K % 256) return PPX_E_UNSUPPORTED;
+    // 16 x 128 tiles, eight compute waves: against 16 x 64 tiles, half the
+    // workgroups stream each weight column block (same-box runs: 2 % off the
+    // 2048- and 8192-token prefills, where this is the K|V product; 32- or
+    // 64-row and 256-column tiles were slower)
+    if ((a.W.K >> 6) % 8 == 0 && a.W.N % 128 == 0) return launch_cfg<Cfg<1, 2, 4, 2, 6>>(g, s);
     if ((a.W.K >> 6) % 8 == 0) return launch_cfg<Cfg<1, 2, 2, 2, 6>>(g, s);
     return launch_cfg<Cfg<1, 2, 2, 1, 6>>(g, s);
 }
