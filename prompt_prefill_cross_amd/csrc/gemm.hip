@@ -839,7 +839,14 @@ struct Plan {
 Plan plan_for(int M, int N, int K, bool few = false, int units = 1) {
     if (few && M <= 64) return {7, K >= 4096 ? 4 : 1};  // a few gathered rows: 16-row tiles, many workgroups
     if (N >= 8192) return {N % 192 == 0 ? 0 : 1, 1};
-    if (K >= 4096) return {N % 192 == 0 ? 2 : 3, units >= 4 ? 1 : units >= 2 ? 2 : 4};
+    if (K >= 4096) {
+        // 128-row tiles once they still give every CU a workgroup (eight
+        // 512-row ubatches in a launch: 1.6 % off the 8192-token prefill;
+        // with four, half the CUs would idle: 5 % slower); both split K the
+        // same way, so a row's sums do not change
+        if (N % 192 == 0 && (long)units * ((M + 127) / 128) * (N / 192) >= 256) return {0, 1};
+        return {N % 192 == 0 ? 2 : 3, units >= 4 ? 1 : units >= 2 ? 2 : 4};
+    }
     if (N <= 512) return {7, 1};
     if (K <= 256) return {PLAN_KSMALL, 1};
     return {PLAN_QO, 1};
