@@ -408,10 +408,12 @@ __global__ __launch_bounds__(64 * KW * G) void k_q4gemv(GemvArgs a) {
 
 constexpr int kGemvMaxGrid = 2048;
 
-// waves per group: aim for ~4096 waves in flight with >= 2 chunks per wave
+// waves per group: aim for ~4096 waves in flight with >= 1 chunk per wave
+// (at least two per wave: 1.3 % slower decode, 0.3 % slower prefill;
+// 2048 or 8192 waves: slower too)
 int gemv_kw(int groups, int kch) {
     int kw = 1;
-    while (kw < 16 && groups * kw < 4096 && kch / (2 * kw) >= 2) kw *= 2;
+    while (kw < 16 && groups * kw < 4096 && kch / (2 * kw) >= 1) kw *= 2;
     return kw;
 }
 
