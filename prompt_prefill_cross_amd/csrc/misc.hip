@@ -82,14 +82,23 @@ __global__ __launch_bounds__(256) void k_rmsnorm_rows(const NormGroup grp, float
     if (row >= u.M) return;  // the whole wave
     const float *xr = u.x + (size_t)row * d;
     const int nch = d >> 3;
-    float4 v[NORM_WAVE_CHUNKS][2];
-    float ss = 0.f;
+    float4 v[NORM_WAVE_CHUNKS][2], gv[NORM_WAVE_CHUNKS][2];
+    // the row and the gain are requested together: the gain does not wait for the sum
 #pragma unroll
     for (int c = 0; c < NORM_WAVE_CHUNKS; ++c) {
         const int ch = lane + 64 * c;
         if (ch < nch) {
             v[c][0] = *reinterpret_cast<const float4 *>(xr + ch * 8);
             v[c][1] = *reinterpret_cast<const float4 *>(xr + ch * 8 + 4);
+            gv[c][0] = *reinterpret_cast<const float4 *>(u.g + ch * 8);
+            gv[c][1] = *reinterpret_cast<const float4 *>(u.g + ch * 8 + 4);
+        }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < NORM_WAVE_CHUNKS; ++c) {
+        const int ch = lane + 64 * c;
+        if (ch < nch) {
             ss += v[c][0].x * v[c][0].x + v[c][0].y * v[c][0].y + v[c][0].z * v[c][0].z + v[c][0].w * v[c][0].w;
             ss += v[c][1].x * v[c][1].x + v[c][1].y * v[c][1].y + v[c][1].z * v[c][1].z + v[c][1].w * v[c][1].w;
         }
@@ -100,8 +109,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_rows(const NormGroup grp, float
     for (int c = 0; c < NORM_WAVE_CHUNKS; ++c) {
         const int ch = lane + 64 * c;
         if (ch < nch) {
-            const float4 g0 = *reinterpret_cast<const float4 *>(u.g + ch * 8);
-            const float4 g1 = *reinterpret_cast<const float4 *>(u.g + ch * 8 + 4);
+            const float4 g0 = gv[c][0], g1 = gv[c][1];
             const float y[8] = {v[c][0].x * r * g0.x, v[c][0].y * r * g0.y, v[c][0].z * r * g0.z, v[c][0].w * r * g0.w,
                                 v[c][1].x * r * g1.x, v[c][1].y * r * g1.y, v[c][1].z * r * g1.z, v[c][1].w * r * g1.w};
             h8 yh, yl;
