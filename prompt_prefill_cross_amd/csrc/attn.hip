@@ -876,7 +876,7 @@ int ok() { return hipGetLastError() == hipSuccess ? PPX_OK : PPX_E_HIP; }
 // Eight compute waves of one group of 16 query columns: 128 columns per
 // workgroup, two compute waves per SIMD.
 constexpr int ATTN_CPW = 1, ATTN_NC = 8, ATTN_CB = 16 * ATTN_CPW * ATTN_NC;
-constexpr int ATTN_MIN_KC = 128;  // keys per chunk at least (early ubatches get more workgroups)
+constexpr int ATTN_MIN_KC = 64;  // keys per chunk at least, one 64-key stage (a 512-token prompt: 1 % faster than 128)
 
 AttnSplit attn_split_cols(int colblocks, int KVH, int P) {
     int want = (256 + colblocks * KVH - 1) / (colblocks * KVH);
