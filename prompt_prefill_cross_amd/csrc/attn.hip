@@ -398,12 +398,13 @@ __global__ __launch_bounds__(C::NT) void k_attn_prefill(const AttnGroup grp) {
     attn_finish<HD, C::CB, CPW>(a, g, ck, wave, kvh, G, lc, lg, R);
 }
 
-// Line-wide staging (head_dim 128 and 256).  A copy instruction that fills
-// a fragment reads 16 pieces of 64 bytes, and the vector memory path serves
-// such pieces at a quarter of the rate of whole 128-byte lines; here every
-// copy instruction reads whole lines instead: KW / 64 whole K rows (KW =
-// 2 * head_dim bytes), or 8 V^T rows of one stage's 64 keys (128 bytes each,
-// a line: cells of a stage are 64-aligned).  The ring holds the rows as they
+// Line-wide staging (written for head_dim 128 and 256; launched at 256).  A
+// copy instruction that fills a fragment reads 16 pieces of 64 bytes, and
+// the vector memory path serves such pieces at about a third of the rate of
+// whole 128-byte lines (16 against 44-56 bytes per clock per CU, measured);
+// here every 1 KB copy instruction reads whole lines instead: 512 / head_dim
+// whole K rows, or 8 V^T rows of one stage's 64 keys (128 bytes each, a
+// line: cells of a stage are 64-aligned).  The ring holds the rows as they
 // are, in 16-byte slots permuted by an XOR with a function of the row, so
 // that the MFMA fragment reads (16 lanes on distinct rows at one slot) run
 // at the rate of contiguous reads -- both permutations were picked by timing
@@ -415,7 +416,8 @@ __global__ __launch_bounds__(C::NT) void k_attn_prefill(const AttnGroup grp) {
 //       tau(d) = d & 7.
 // A stage is 64 keys (two steps of 32); two stages fill the ring.  NC
 // compute waves of CPW groups of 16 query columns; NP producer waves, or
-// none (NP = 0): the compute waves then issue the copies themselves.
+// none (NP = 0): the compute waves then issue the copies themselves (with
+// eight compute waves 11-15 % slower than two or four producers, measured).
 template <int HD_, int NC_, int CPW_, int NP_>
 struct WCfg {
     static constexpr int HD = HD_, NC = NC_, CPW = CPW_, NP = NP_, DEPTH = 2, KS = 64;
