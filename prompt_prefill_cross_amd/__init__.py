@@ -132,6 +132,11 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m prompt_prefill_cross_amd.build` (no CPU fallback exists)")
+        # torch bundles its own HIP runtime under the same soname as the
+        # system one libppx.so links.  Loading torch first makes the library
+        # bind to that runtime, so the two share one device context; the
+        # other order leaves torch on a runtime whose allocations fail.
+        import torch  # noqa: F401
         h = ctypes.CDLL(LIB_PATH)
         for name, res, args in SIGNATURES:
             f = getattr(h, name)
