@@ -373,10 +373,12 @@ __global__ __launch_bounds__(64 * KW * G) void k_q4gemv(GemvArgs a) {
     }
     __syncthreads();
 
-    const _Float16 *xsrc = col == 0 ? xh : xl;  // rows 0 and 1 carry v; the others stay zero
-    const bool arow = col < 2;
+    // Rows 0 and 1 of the A operand carry hi and lo; the other rows repeat
+    // them (their results, rows 2..15 of the product, are never read), so no
+    // lane masks its fragment.
+    const _Float16 *xsrc = (col & 1) ? xl : xh;
     for (; unit < nunits; unit += gridDim.x) {
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
+        float acc0 = 0.f, acc1 = 0.f;
         for (int base = kw; base < kch; base += KW * GEMV_UNR) {
             // the next batch (this unit's, else the next unit's first) while this one is used
             uint2 wn[GEMV_UNR];
@@ -391,10 +393,11 @@ __global__ __launch_bounds__(64 * KW * G) void k_q4gemv(GemvArgs a) {
                 const h2 d = __builtin_bit_cast(h2, sc[u]);
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
-                    h8 af = *reinterpret_cast<const h8 *>(xsrc + kc * 64 + s * 32 + g8);
-                    if (!arow) af = h8{0, 0, 0, 0, 0, 0, 0, 0};
+                    const h8 af = *reinterpret_cast<const h8 *>(xsrc + kc * 64 + s * 32 + g8);
                     const f4 p = mfma16(af, q4_word_codes(s ? w[u].y : w[u].x), f4{0.f, 0.f, 0.f, 0.f});
-                    acc += (float)d[s] * p;
+                    const float ds = (float)d[s];
+                    acc0 += ds * p[0];  // rows 0 and 1 of the 16 x 16 product
+                    acc1 += ds * p[1];
                 }
             }
 #pragma unroll
@@ -404,7 +407,7 @@ __global__ __launch_bounds__(64 * KW * G) void k_q4gemv(GemvArgs a) {
             }
         }
         // lanes 0..15 hold rows 0 and 1 (hi and lo parts) of column `col`
-        if (lane < 16) red[(gi * KW + kw) * 16 + lane] = acc[0] + acc[1];
+        if (lane < 16) red[(gi * KW + kw) * 16 + lane] = acc0 + acc1;
         __syncthreads();
         if (tid < 16) {
             if (unit < n1) gemv_epilogue<KW, G>(a, red, unit, tid, a.epi);
