@@ -4,9 +4,8 @@ Calls only the fp64 oracle (oracle/) on the seeded inputs of `synth`; the
 GPU parity tests compare the HIP path against these files instead of
 re-running the oracle (minutes to hours at these sizes) inside the test.
 Each file holds the last-row logits
-(fp32, all n_vocab), the fp16 K and V rows of 16 sampled positions (first
-and last included) in up to six evenly spaced KV-owning layers, and the
-run's metadata.
+(fp32, all n_vocab), the fp16 K and V rows of 32 sampled positions (first
+and last included) in every KV-owning layer, and the run's metadata.
 
     python tests/golden/make_goldens.py [name ...]      (names below)
 """
@@ -51,9 +50,8 @@ def make(name):
     logits = oracle.prefill(m, kv, toks, prune=0 < c.n_layer_kv_from_start < c.n_layer)
     dt = time.time() - t
     rng = np.random.default_rng([7, n])
-    pos = np.unique(np.concatenate([[0, n - 1], rng.choice(n, size=min(14, n), replace=False)]))
-    ls = c.n_layer_kv_from_start
-    layers = np.unique(np.linspace(0, ls - 1, num=min(6, ls)).round().astype(np.int64))
+    pos = np.unique(np.concatenate([[0, n - 1], rng.choice(n, size=min(30, n), replace=False)]))
+    layers = np.arange(c.n_layer_kv_from_start, dtype=np.int64)
     meta = {"config": cfg, "n": n, "model_seed": c.seed, "oracle_seconds": round(dt, 1),
             "numpy": np.__version__, "source": "oracle.prefill (fp64) on synth.build_model / synth.prompt"}
     np.savez(path_of(name), logits=logits.astype(np.float32), kv_pos=pos.astype(np.int64),
