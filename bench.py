@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="prompt tokens of the oracle sample (0 = all)")
     ap.add_argument("--pmc-pass", action="store_true", help="the roofline's gate|up launches and two calibration passes, then exit")
+    ap.add_argument("--pmc-attn", action="store_true",
+                    help="prefill attention launches (M = ubatch rows at the end of an 8192-token context), then exit")
     return ap.parse_args()
 
 
@@ -415,6 +417,24 @@ def pmc_pass(ppx, mm, ub, glu_launches=20):
           f"one {COPY_CAL_BYTES} B copy", flush=True)
 
 
+def pmc_attn(mm, ub, ctx=8192, launches=10):
+    """The dispatches the attention counters are read on: ub query rows at
+    positions ctx - ub .. ctx - 1 against ctx keys (seeded fp16 q, K, V of
+    the model's head shape), through ppx_op_attention."""
+    import torch
+    I = mm.info
+    g = torch.Generator(device="cuda").manual_seed(11)
+    q = torch.randn((ub, I["n_head"], I["head_dim"]), generator=g, device="cuda").to(torch.float16)
+    k = torch.randn((ctx, I["n_kv_head"], I["head_dim"]), generator=g, device="cuda").to(torch.float16)
+    v = torch.randn((ctx, I["n_kv_head"], I["head_dim"]), generator=g, device="cuda").to(torch.float16)
+    for _ in range(launches):
+        mm.op_attention(q, k, v, ctx - ub)
+    torch.cuda.synchronize()
+    flop = 4.0 * I["n_head"] * I["head_dim"] * sum(ctx - ub + t + 1 for t in range(ub))
+    print(f"# pmc attention pass done: {launches} launches, M={ub} at position {ctx - ub}, "
+          f"{flop:.4g} FLOP per launch", flush=True)
+
+
 def cpu_baseline(cfg, buf, toks, sample):
     import oracle
     m = oracle.parse_model(buf)
@@ -453,6 +473,9 @@ def main():
 
     if a.pmc_pass:
         pmc_pass(ppx, mm, ub)
+        return
+    if a.pmc_attn:
+        pmc_attn(mm, ub)
         return
 
     results = {}
