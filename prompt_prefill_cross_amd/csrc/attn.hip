@@ -42,6 +42,24 @@ __device__ __forceinline__ void attn_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Max / sum over the four lanes of one query column (l, l ^ 16, l ^ 32,
+// l ^ 48), as (x_l op x_l^16) op (same at l ^ 32), with the gfx950 lane swaps
+// (v_permlane16_swap / v_permlane32_swap: VALU, no trip through the LDS queue
+// behind the fragment reads).  Called with the same value as both operands,
+// a swap returns each lane's own value and its partner's.
+__device__ __forceinline__ float attn_col_max(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float attn_col_sum(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <int N>
 __device__ __forceinline__ void attn_wait_vm() {
     static_assert(N >= 0 && N < 64, "vmcnt");
@@ -209,9 +227,7 @@ __device__ __forceinline__ void attn_step32(const KF &kfrag, const VF &vfrag, in
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) tmx = fmaxf(tmx, s[c][j][r]);
-        tmx = fmaxf(tmx, __shfl_xor(tmx, 16, 64));
-        tmx = fmaxf(tmx, __shfl_xor(tmx, 32, 64));
-        tmx *= sl2;
+        tmx = attn_col_max(tmx) * sl2;
         // move m only past the margin (or at the first visible key); 2^-inf
         // = 0 covers masked keys and a column with no visible key yet, whose
         // m stays -inf and which subtracts 0 instead
@@ -235,9 +251,7 @@ __device__ __forceinline__ void attn_step32(const KF &kfrag, const VF &vfrag, in
                 psum += p;
                 pf[c][4 * j + r] = (_Float16)p;
             }
-        psum += __shfl_xor(psum, 16, 64);
-        psum += __shfl_xor(psum, 32, 64);
-        R.lrun[c] += psum;
+        R.lrun[c] += attn_col_sum(psum);
     }
     // O^T += V^T P^T over the step's 32 keys (8 lg .. 8 lg + 7 in lane group lg).
     // Values of keys past the last written position may be stale (a cache
