@@ -43,21 +43,17 @@ __device__ __forceinline__ void attn_barrier() {
 }
 
 // Max / sum over the four lanes of one query column (l, l ^ 16, l ^ 32,
-// l ^ 48), as (x_l op x_l^16) op (same at l ^ 32), with the gfx950 lane swaps
-// (v_permlane16_swap / v_permlane32_swap: VALU, no trip through the LDS queue
-// behind the fragment reads).  Called with the same value as both operands,
-// a swap returns each lane's own value and its partner's.
+// l ^ 48), as (x_l op x_l^16) op (the same at l ^ 32), on VALU: the step's
+// K and V^T fragment reads fill the LDS queue that a permute would wait in.
 __device__ __forceinline__ float attn_col_max(float v) {
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    LanePair p = swap16(v);
+    p = swap32(fmaxf(p.a, p.b));
+    return fmaxf(p.a, p.b);
 }
 __device__ __forceinline__ float attn_col_sum(float v) {
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+    LanePair p = swap16(v);
+    p = swap32(p.a + p.b);
+    return p.a + p.b;
 }
 
 template <int N>
@@ -658,7 +654,7 @@ __global__ __launch_bounds__(256) void k_attn_1row(Attn1Args a) {
         // acc[r] = C[key 4*lg + r of the tile][column c]; S = column g + column g + 8
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float v = acc[r] + __shfl_xor(acc[r], 8, 64);
+            const float v = acc[r] + row_ror<8>(acc[r]);
             const int kt = wave * 16 + 4 * lg + r;
             if (c < G) sl[c][kt] = kt < nk ? v * scale : -INFINITY;
         }
@@ -700,7 +696,7 @@ __global__ __launch_bounds__(256) void k_attn_1row(Attn1Args a) {
         // acc[r] = C[dimension t*16 + 4*lg + r][column c]
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float v = acc[r] + __shfl_xor(acc[r], 8, 64);
+            const float v = acc[r] + row_ror<8>(acc[r]);
             if (c < G) po[((size_t)(kvh * G + c) * nchunks + chunk) * HD + t * 16 + 4 * lg + r] = v;
         }
     }
@@ -826,7 +822,7 @@ __global__ __launch_bounds__(256) void k_attn_rows_exact(AttnArgs a) {
                 acc = mfma16(*reinterpret_cast<const h8 *>(krow + ks * 32), qb[ks], acc);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float v = acc[q] + __shfl_xor(acc[q], 8, 64);
+                const float v = acc[q] + row_ror<8>(acc[q]);
                 const int kk = wave * 16 + 4 * lg + q;
                 if (c < G) sl[c][kk] = kk < nk ? v * scale : -INFINITY;
             }
@@ -872,7 +868,7 @@ __global__ __launch_bounds__(256) void k_attn_rows_exact(AttnArgs a) {
     for (int j = 0; j < NJ; ++j) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const float v = oacc[j][q] + __shfl_xor(oacc[j][q], 8, 64);
+            const float v = oacc[j][q] + row_ror<8>(oacc[j][q]);
             if (c < G) {
                 const int h = kvh * G + c, d = (wave + 4 * j) * 16 + 4 * lg + q;
                 const float o = v / lrun[c];

@@ -111,16 +111,51 @@ __device__ __forceinline__ float act_f(int act, float g) {
     return act == ACT_GEGLU ? gelu_tanh_f(g) : silu_f(g);
 }
 
+// Cross-lane exchanges on VALU, without a trip through the LDS queue.
+// swap32 / swap16 (gfx950 v_permlane32_swap / v_permlane16_swap, both
+// operands the same register) give each lane its own value and that of lane
+// l ^ 32 / l ^ 16, in some order; row_ror<k> gives the value of lane
+// (i + k) mod 16 within each row of 16 lanes (DPP), which for k = 8 is lane i ^ 8.
+struct LanePair {
+    float a, b;
+};
+__device__ __forceinline__ LanePair swap32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ LanePair swap16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+template <int K>
+__device__ __forceinline__ float row_ror(float v) {
+    static_assert(K >= 1 && K <= 15, "row rotation");
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x120 + K, 0xf, 0xf, false));
+}
+
+// Reduction over the wave in the order of the xor butterfly (distance 32,
+// 16, 8, 4, 2, 1): after the folds at distances above 2^k every lane holds
+// the same value as the lanes that differ from it in the higher bits of its
+// row, so the rotation partner (i + 2^k) mod 16 holds what lane i ^ 2^k
+// holds, and each lane ends with the butterfly's result, bit for bit.
+template <class Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+    LanePair p = swap32(v);
+    v = op(p.a, p.b);
+    p = swap16(v);
+    v = op(p.a, p.b);
+    v = op(v, row_ror<8>(v));
+    v = op(v, row_ror<4>(v));
+    v = op(v, row_ror<2>(v));
+    return op(v, row_ror<1>(v));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    return wave_reduce(v, [](float x, float y) { return x + y; });
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+    return wave_reduce(v, [](float x, float y) { return fmaxf(x, y); });
 }
 
 }  // namespace ppx
