@@ -253,18 +253,36 @@ __device__ __forceinline__ void attn_step32(const KF &kfrag, const VF &vfrag, in
     // Values of keys past the last written position may be stale (a cache
     // cleared or reloaded to fewer positions keeps its old contents): they
     // are zeroed, so a non-finite stale value cannot meet a zero weight.
+    // Groups of four fragments: the next group's reads are issued before
+    // this group's products, so eight reads at most are in flight (more
+    // would take the registers of the wave's Q fragments), and the zeroing
+    // of a tail step is one test per group, not a branch per fragment.
     const bool tail = edge && t0 + 31 > plast;  // uniform over the workgroup
     const int vlim = plast - (t0 + 8 * lg);     // elements e <= vlim are written keys
+    static_assert(DT % 4 == 0, "fragment groups");
+    h8 va[4], vb[4];
 #pragma unroll
-    for (int i = 0; i < DT; ++i) {
-        h8 vf = vfrag(i);
+    for (int u = 0; u < 4; ++u) va[u] = vfrag(u);
+#pragma unroll
+    for (int q = 0; q < DT / 4; ++q) {
+        if (q + 1 < DT / 4) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) vb[u] = vfrag(4 * (q + 1) + u);
+        }
         if (tail) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (e > vlim) vf[e] = (_Float16)0.0f;
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (e > vlim) va[u][e] = (_Float16)0.0f;
         }
 #pragma unroll
-        for (int c = 0; c < CPW; ++c) R.oacc[c][i] = mfma16(vf, pf[c], R.oacc[c][i]);
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int c = 0; c < CPW; ++c) R.oacc[c][4 * q + u] = mfma16(va[u], pf[c], R.oacc[c][4 * q + u]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) va[u] = vb[u];
     }
 }
 
