@@ -195,17 +195,29 @@ __device__ __forceinline__ void attn_step32(const KF &kfrag, const VF &vfrag, in
     constexpr int KB = HD / 32, DT = HD / 16;
     const float sl2 = 1.4426950408889634f / sqrtf((float)HD);
     // S^T = K Q^T: s[c][j][r] is key t0 + 8 lg + 4 j + r, query column lc of group c
+    // in groups of four fragments (d steps 2q and 2q + 1 of both key
+    // blocks), the next group's reads issued before this group's products,
+    // which alternate between the two key blocks' accumulators
+    static_assert(KB % 2 == 0, "fragment groups");
     f4 s[CPW][2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int c = 0; c < CPW; ++c) s[c][0] = s[c][1] = f4{0.f, 0.f, 0.f, 0.f};
+    h8 ka[4], kn[4];
 #pragma unroll
-        for (int c = 0; c < CPW; ++c) s[c][j] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < 4; ++u) ka[u] = kfrag(u >> 1, u & 1);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const h8 kf = kfrag(kb, j);
+    for (int q = 0; q < KB / 2; ++q) {
+        if (q + 1 < KB / 2) {
 #pragma unroll
-            for (int c = 0; c < CPW; ++c) s[c][j] = mfma16(kf, R.qf[c][kb], s[c][j]);
+            for (int u = 0; u < 4; ++u) kn[u] = kfrag(2 * (q + 1) + (u >> 1), u & 1);
         }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int c = 0; c < CPW; ++c) s[c][u & 1] = mfma16(ka[u], R.qf[c][2 * q + (u >> 1)], s[c][u & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ka[u] = kn[u];
     }
     h8 pf[CPW];
 #pragma unroll
