@@ -689,6 +689,15 @@ __global__ __launch_bounds__(256) void k_attn_1row(Attn1Args a) {
             if (c < G) sl[c][kt] = kt < nk ? v * scale : -INFINITY;
         }
     }
+    // the wave's value tiles (t = wave, wave + 4, ...) do not depend on the
+    // scores: requested here, so they arrive during the softmax
+    constexpr int NTW = HD / 16 / 4;
+    h8 vpre[NTW];
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+        const int d = (wave + 4 * i) * 16 + c;
+        vpre[i] = *reinterpret_cast<const h8 *>(a.vt + ((size_t)kvh * HD + d) * a.vld + k0 + lg * 8);
+    }
     __syncthreads();
 
     // softmax of the chunk: wave w takes heads w, w+4; lane = key
@@ -716,9 +725,10 @@ __global__ __launch_bounds__(256) void k_attn_1row(Attn1Args a) {
         const _Float16 h = (_Float16)p;
         bv[e] = lo ? (_Float16)(p - (float)h) : h;
     }
-    for (int t = wave; t < HD / 16; t += 4) {
-        const int d = t * 16 + c;
-        h8 av = *reinterpret_cast<const h8 *>(a.vt + ((size_t)kvh * HD + d) * a.vld + k0 + lg * 8);
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+        const int t = wave + 4 * i;
+        h8 av = vpre[i];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             if (lg * 8 + e >= nk) av[e] = (_Float16)0.0f;
@@ -744,6 +754,19 @@ __global__ __launch_bounds__(256) void k_attn_merge(Attn1Args a, int nchunks) {
     const int hd = a.hd, nq = hd >> 2, ns = 256 / nq;
     const float *st = a.partial + (size_t)h * nchunks * 2;
     const float *po = a.partial + (size_t)a.H * nchunks * 2 + (size_t)h * nchunks * hd;
+    const int q = tid % nq, sub = tid / nq;  // ns * nq = 256: every thread has a slice
+    // the thread's first MERGE1_PRE batches of partial outputs (chunks sub +
+    // 4 ns b + ns u) do not depend on the weights: requested before the
+    // (max, sum) pass; past the last chunk the reads repeat it (weight 0)
+    constexpr int MERGE1_PRE = 4;
+    f4 xp[MERGE1_PRE][4];
+#pragma unroll
+    for (int b = 0; b < MERGE1_PRE; ++b)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = min(sub + 4 * ns * b + u * ns, nchunks - 1);
+            xp[b][u] = *reinterpret_cast<const f4 *>(po + (size_t)c * hd + 4 * q);
+        }
     float M = -INFINITY;
     for (int c = tid; c < nchunks; c += 256) M = fmaxf(M, st[2 * c]);
     M = wave_max(M);
@@ -760,21 +783,29 @@ __global__ __launch_bounds__(256) void k_attn_merge(Attn1Args a, int nchunks) {
     if (lane == 0) red[4 + wave] = L;
     __syncthreads();
     L = red[4] + red[5] + red[6] + red[7];
-    const int q = tid % nq, sub = tid / nq;
     f4 o = {0.f, 0.f, 0.f, 0.f};
-    if (sub < ns) {
-        for (int c0 = sub; c0 < nchunks; c0 += 4 * ns) {
-            f4 x[4];
-            float w[4];
+    // chunks in the order c0 = sub, sub + 4 ns, ...; u = 0..3 within each
+    auto batch = [&](int c0, const f4 (&x)[4]) {
+        float w[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int c = min(c0 + u * ns, nchunks - 1);
-                x[u] = *reinterpret_cast<const f4 *>(po + (size_t)c * hd + 4 * q);
-                w[u] = c0 + u * ns < nchunks ? (c < 1024 ? wl[c] : expf(st[2 * c] - M)) : 0.f;
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) o += w[u] * x[u];
+        for (int u = 0; u < 4; ++u) {
+            const int c = min(c0 + u * ns, nchunks - 1);
+            w[u] = c0 + u * ns < nchunks ? (c < 1024 ? wl[c] : expf(st[2 * c] - M)) : 0.f;
         }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) o += w[u] * x[u];
+    };
+#pragma unroll
+    for (int b = 0; b < MERGE1_PRE; ++b)
+        if (sub + 4 * ns * b < nchunks) batch(sub + 4 * ns * b, xp[b]);
+    for (int c0 = sub + 4 * ns * MERGE1_PRE; c0 < nchunks; c0 += 4 * ns) {
+        f4 x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = min(c0 + u * ns, nchunks - 1);
+            x[u] = *reinterpret_cast<const f4 *>(po + (size_t)c * hd + 4 * q);
+        }
+        batch(c0, x);
     }
     part[tid] = o;
     __syncthreads();
