@@ -502,22 +502,36 @@ __global__ __launch_bounds__(C::NT) void k_attn_prefill_w(const AttnGroup grp) {
     const int pw = C::NP ? wave - C::NC : wave;
     const int kx = lane / ROW, ks = lane % ROW;  // K: row within the instruction, slot
     const int vr = lane >> 3, vs = lane & 7;     // V^T: row within the instruction, slot
+    // Copy t of an issuing wave is e = t NI + pw: a K copy for t < PK (K_INSTR
+    // is a multiple of NI), known when the loop is unrolled.  What the copies
+    // read from the arguments is held in registers here: the barriers'
+    // memory clobbers would otherwise have it re-read before every copy.
+    static_assert(C::K_INSTR % C::NI == 0, "K copies per issuing wave");
+    constexpr int PK = C::K_INSTR / C::NI;
+    // Within a stage the offsets fit in 32 bits: K rows (key - t0) * KVH * HD
+    // with key - t0 < 64, V^T rows d * vld with d < HD.
+    const int kcell = a.KVH * HD;  // elements from one cell's K rows to the next's
+    const __half *const kbase = g.kp + (size_t)kvh * HD;
+    const __half *const vbase = g.vtp + (size_t)kvh * HD * g.vld;
+    const int vld = g.vld, plast = g.plast, kbeg = g.kbeg;
     auto issue = [&](int sb) {
         h8 *st = ring + (sb % C::DEPTH) * C::STAGE_UNITS;
-        const int t0 = g.kbeg + min(sb, nst - 1) * KS;  // past the end: repeats keep the count uniform
+        const int t0 = kbeg + min(sb, nst - 1) * KS;  // past the end: repeats keep the count uniform
         // the stage's keys t0 .. t0 + 63 (and the clamp target plast >= t0)
         // lie in one page: cells c0 + (key - t0)
         const int c0 = kv_cell(g.page, t0);
+        const __half *const ks0 = kbase + (size_t)c0 * kcell;
+        const __half *const vs0 = vbase + c0;
+        const int klim = plast - t0;  // keys past plast repeat it
 #pragma unroll
         for (int t = 0; t < C::PER; ++t) {
             const int e = t * C::NI + pw;
-            if (e < C::K_INSTR) {
+            if (t < PK) {
                 const int k = e * (64 / ROW) + kx;
-                const int key = min(t0 + k, g.plast);
-                adma16(g.kp + ((size_t)(c0 + key - t0) * a.KVH + kvh) * HD + 8 * (ks ^ attn_sigma(k)), st + e * 64);
+                adma16(ks0 + (unsigned)(min(k, klim) * kcell + 8 * (ks ^ attn_sigma(k))), st + e * 64);
             } else {
                 const int d = (e - C::K_INSTR) * 8 + vr;
-                adma16(g.vtp + (size_t)(kvh * HD + d) * g.vld + c0 + 8 * (vs ^ attn_tau(d)), st + e * 64);
+                adma16(vs0 + (unsigned)(d * vld + 8 * (vs ^ attn_tau(d))), st + e * 64);
             }
         }
     };
